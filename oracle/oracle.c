@@ -1,0 +1,451 @@
+/*
+ * oracle.c -- plain, slow CPU reference for interval-mask flex attention.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this code.  The GPU library never
+ * links, calls or includes it, and this file includes nothing from the GPU
+ * library: the two implementations share no code.
+ *
+ * Everything here is the plain definition, written out with loops, in double
+ * precision:
+ *   - validate  : "Flex Attention Mask Plan Design" (cuDNN frontend docs),
+ *                 §2 (endpoint order and bounds), §3.2 (Varlen prefix rules),
+ *                 §4.3 (classifier validates every endpoint).
+ *   - expand    : §2, visible(q) = [0,F0) U [F1,F2) U [F3,F4) U ...
+ *   - classify  : §4.3, exactly one of empty / full / partial per (Q tile, K
+ *                 tile); full needs the whole tile in bounds and every element
+ *                 visible; a tile that sticks out past q_len or k_len is never
+ *                 full.
+ *   - pack      : §5, one bit per score element, 1 = keep, 0 = -inf.  This
+ *                 library's consumer reads the predicate of row r, columns
+ *                 [32w, 32w+32) of a tile from word r*W + w, bit (c mod 32),
+ *                 W = T_KV/32; out-of-bounds elements are 0 bits.
+ *   - CSR       : §4.5 / §4.6, exclusive offsets off[0]=0,
+ *                 off[i+1]=off[i]+cnt[i]; partial and full lists independent,
+ *                 sample-local K-tile indices in ascending order, rows
+ *                 flattened head-major (flat = hm*rows_total + row).
+ *   - attention : FlexAttention (Dong et al.), Eq. 1,
+ *                 softmax(mod(Q K^T / sqrt(d))) V, with the mask as an additive
+ *                 0 / -inf bias (Tessera paper, "masked attention" definition);
+ *                 rows with nothing visible give O = 0 and LSE = -inf (mask
+ *                 plan design §6.1).  LSE is the natural log of the sum of
+ *                 exp(score) over visible keys, scores after score_mod.
+ *   - score_mod : softcap c*tanh(s/c) then ALiBi + slope_h*(k-q) with
+ *                 sample-local positions (optionally ALiBi first); the scale is
+ *                 applied before either.
+ *
+ * Threads: independent rows are split over POSIX threads; each thread runs the
+ * same plain loops on its own rows.  No -ffast-math.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_ERR_SEQLENS = 1, ORC_ERR_RANGE = 2, ORC_ERR_ORDER = 4 };
+enum { ORC_BSHD = 0, ORC_THD = 1 };
+
+typedef struct {
+  int32_t layout, batch, seqlen_q, seqlen_k, total_q, total_k;
+  int32_t heads_q, heads_k, head_dim, mask_heads, nfunc;
+  int32_t tile_q, tile_k;
+} orc_problem;
+
+/* ------------------------------------------------------------ geometry */
+
+static void sample_of(const orc_problem* p, const int32_t* cu_q, const int32_t* cu_k, int b,
+                      int64_t* q_off, int64_t* q_len, int64_t* k_off, int64_t* k_len) {
+  if (p->layout == ORC_BSHD) {
+    *q_off = (int64_t)b * p->seqlen_q;
+    *q_len = p->seqlen_q;
+    *k_off = (int64_t)b * p->seqlen_k;
+    *k_len = p->seqlen_k;
+  } else {
+    *q_off = cu_q[b];
+    *q_len = (int64_t)cu_q[b + 1] - cu_q[b];
+    *k_off = cu_k[b];
+    *k_len = (int64_t)cu_k[b + 1] - cu_k[b];
+  }
+}
+
+/* Sample that owns Q token t (linear search; the prefix is validated). */
+static int owner_of_token(const orc_problem* p, const int32_t* cu_q, int64_t t) {
+  if (p->layout == ORC_BSHD) return (int)(t / p->seqlen_q);
+  for (int b = 0; b < p->batch; ++b)
+    if (t >= cu_q[b] && t < cu_q[b + 1]) return b;
+  return -1;
+}
+
+static int32_t endpoint(const orc_problem* p, const int32_t* mf, int hm, int f, int64_t t) {
+  return mf[((int64_t)hm * p->nfunc + f) * p->total_q + t];
+}
+
+/* ------------------------------------------------------------ validate */
+
+/* Varlen prefix rules (§3.2): start at 0, end at the total, nondecreasing,
+ * every length <= max_seqlen. */
+static int prefix_ok(const int32_t* cu, int batch, int32_t total, int32_t max_len) {
+  if (cu[0] != 0) return 0;
+  if (cu[batch] != total) return 0;
+  for (int b = 0; b < batch; ++b) {
+    if (cu[b + 1] < cu[b]) return 0;
+    if ((int64_t)cu[b + 1] - cu[b] > max_len) return 0;
+  }
+  return 1;
+}
+
+/* Returns the OR of ORC_ERR_* bits.  When the prefixes are invalid the sample
+ * K lengths are undefined, so the per-endpoint checks are skipped. */
+uint32_t orc_validate(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                      const int32_t* cu_k) {
+  uint32_t err = 0;
+  if (p->layout == ORC_THD) {
+    if (!prefix_ok(cu_q, p->batch, p->total_q, p->seqlen_q) ||
+        !prefix_ok(cu_k, p->batch, p->total_k, p->seqlen_k))
+      return ORC_ERR_SEQLENS;
+  }
+  for (int b = 0; b < p->batch; ++b) {
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, cu_q, cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    for (int hm = 0; hm < p->mask_heads; ++hm)
+      for (int64_t q = 0; q < q_len; ++q)
+        for (int f = 0; f < p->nfunc; ++f) {
+          int32_t F = endpoint(p, mf, hm, f, q_off + q);
+          if (F < 0 || F > k_len) err |= ORC_ERR_RANGE;
+          if (f + 1 < p->nfunc && F > endpoint(p, mf, hm, f + 1, q_off + q)) err |= ORC_ERR_ORDER;
+        }
+  }
+  return err;
+}
+
+/* ------------------------------------------------------------ expand */
+
+/* visible[k] for k in [0, k_len): the union of [0,F0), [F1,F2), [F3,F4), ...
+ * Each interval's members are marked one by one. */
+void orc_expand_row(const int32_t* F, int64_t stride, int nfunc, int64_t k_len, uint8_t* vis) {
+  for (int64_t k = 0; k < k_len; ++k) vis[k] = 0;
+  for (int i = -1; i < nfunc; i += 2) {
+    int64_t a = (i < 0) ? 0 : F[(int64_t)i * stride];
+    int64_t b = F[(int64_t)(i + 1) * stride];
+    for (int64_t k = a; k < b && k < k_len; ++k)
+      if (k >= 0) vis[k] = 1;
+  }
+}
+
+/* ------------------------------------------------------------ plan */
+
+typedef struct {
+  int64_t header[8];         /* rows, pnnz, fnnz, 0, 0, 0, 0, err */
+  int32_t rows_total, nk_max, words;
+  int32_t* cu_rows;          /* [B+1] */
+  int32_t* seqdesc;          /* [B][8] */
+  int32_t* p_off;            /* [Hmask*rows+1] */
+  int32_t* f_off;
+  int32_t* p_idx;            /* [pnnz] */
+  int32_t* f_idx;            /* [fnnz] */
+  uint32_t* p_masks;         /* [pnnz * tile_q * words] */
+  uint8_t* cls;              /* [Hmask*rows*nk_max] 0 empty/nonexistent, 1 partial, 2 full */
+} orc_plan;
+
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  orc_plan* plan;
+  const int32_t* row_sample;
+  int64_t item_begin, item_end;   /* flat (hm, row) items */
+  int phase;                      /* 0 classify, 1 materialize */
+} plan_job;
+
+/* Expands rows [r0, r0+T_Q) of sample b (mask head hm) into vis[T_Q][k_len];
+ * rows past q_len stay all-zero. */
+static void expand_tile_rows(const orc_problem* p, const int32_t* mf, int hm, int64_t q_off,
+                             int64_t q_len, int64_t r0, int64_t k_len, uint8_t* vis) {
+  for (int r = 0; r < p->tile_q; ++r) {
+    uint8_t* row = vis + (int64_t)r * (k_len > 0 ? k_len : 1);
+    if (r0 + r < q_len) {
+      const int32_t* F = mf + (int64_t)hm * p->nfunc * p->total_q + q_off + r0 + r;
+      orc_expand_row(F, p->total_q, p->nfunc, k_len, row);
+    } else {
+      for (int64_t k = 0; k < k_len; ++k) row[k] = 0;
+    }
+  }
+}
+
+static void* plan_worker(void* arg) {
+  plan_job* J = (plan_job*)arg;
+  const orc_problem* p = J->p;
+  orc_plan* P = J->plan;
+  int64_t pitch = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)p->tile_q * pitch);
+  for (int64_t item = J->item_begin; item < J->item_end; ++item) {
+    int hm = (int)(item / P->rows_total);
+    int64_t row = item % P->rows_total;
+    int b = J->row_sample[row];
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t i = row - P->cu_rows[b];
+    int64_t r0 = i * p->tile_q;
+    int64_t nk = (k_len + p->tile_k - 1) / p->tile_k;
+    expand_tile_rows(p, J->mf, hm, q_off, q_len, r0, k_len, vis);
+    uint8_t* cls = P->cls + item * P->nk_max;
+    int64_t pw = P->p_off ? P->p_off[item] : 0, fw = P->f_off ? P->f_off[item] : 0;
+    for (int64_t j = 0; j < nk; ++j) {
+      int64_t c0 = j * p->tile_k;
+      if (J->phase == 0) {
+        int64_t count = 0;
+        for (int r = 0; r < p->tile_q; ++r)
+          for (int c = 0; c < p->tile_k; ++c)
+            if (r0 + r < q_len && c0 + c < k_len && vis[(int64_t)r * k_len + c0 + c]) ++count;
+        int in_bounds = (r0 + p->tile_q <= q_len) && (c0 + p->tile_k <= k_len);
+        if (count == 0) cls[j] = 0;
+        else if (in_bounds && count == (int64_t)p->tile_q * p->tile_k) cls[j] = 2;
+        else cls[j] = 1;
+      } else if (cls[j] == 1) {
+        P->p_idx[pw] = (int32_t)j;
+        uint32_t* words = P->p_masks + pw * (int64_t)p->tile_q * P->words;
+        for (int r = 0; r < p->tile_q; ++r)
+          for (int w = 0; w < P->words; ++w) {
+            uint32_t word = 0;
+            for (int bit = 0; bit < 32; ++bit) {
+              int64_t c = c0 + 32 * w + bit;
+              if (r0 + r < q_len && c < k_len && c < c0 + p->tile_k && vis[(int64_t)r * k_len + c])
+                word |= 1u << bit;
+            }
+            words[r * P->words + w] = word;
+          }
+        ++pw;
+      } else if (cls[j] == 2) {
+        P->f_idx[fw++] = (int32_t)j;
+      }
+    }
+  }
+  free(vis);
+  return NULL;
+}
+
+static void run_plan_phase(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                           const int32_t* cu_k, orc_plan* P, const int32_t* row_sample, int phase,
+                           int nthreads) {
+  int64_t items = (int64_t)p->mask_heads * P->rows_total;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > items) nthreads = items > 0 ? (int)items : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  plan_job* jobs = (plan_job*)malloc(sizeof(plan_job) * nthreads);
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (plan_job){p, mf, cu_q, cu_k, P, row_sample, items * t / nthreads,
+                         items * (t + 1) / nthreads, phase};
+    pthread_create(&th[t], NULL, plan_worker, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* Builds the whole plan by brute force.  Returns NULL on allocation failure.
+ * On a validation error the plan holds only the header (err != 0). */
+orc_plan* orc_plan_build(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                         const int32_t* cu_k, int nthreads) {
+  orc_plan* P = (orc_plan*)calloc(1, sizeof(orc_plan));
+  if (!P) return NULL;
+  uint32_t err = orc_validate(p, mf, cu_q, cu_k);
+  P->header[7] = err;
+  if (err) return P;
+  int B = p->batch;
+  P->cu_rows = (int32_t*)calloc((size_t)B + 1, sizeof(int32_t));
+  P->seqdesc = (int32_t*)calloc((size_t)B * 8 + 1, sizeof(int32_t));
+  int64_t nk_max = 0;
+  for (int b = 0; b < B; ++b) {
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, cu_q, cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t rows_b = (q_len + p->tile_q - 1) / p->tile_q;
+    int64_t nk = (k_len + p->tile_k - 1) / p->tile_k;
+    if (nk > nk_max) nk_max = nk;
+    P->cu_rows[b + 1] = P->cu_rows[b] + (int32_t)rows_b;
+    int32_t* sd = P->seqdesc + 8 * b;
+    sd[0] = (int32_t)q_off; sd[1] = (int32_t)k_off; sd[2] = (int32_t)q_len; sd[3] = (int32_t)k_len;
+    sd[4] = P->cu_rows[b]; sd[5] = (int32_t)rows_b; sd[6] = (int32_t)nk; sd[7] = 0;
+  }
+  P->rows_total = P->cu_rows[B];
+  P->nk_max = (int32_t)(nk_max > 0 ? nk_max : 1);
+  P->words = p->tile_k / 32;
+  int32_t* row_sample = (int32_t*)calloc((size_t)P->rows_total + 1, sizeof(int32_t));
+  for (int b = 0; b < B; ++b)
+    for (int32_t r = P->cu_rows[b]; r < P->cu_rows[b + 1]; ++r) row_sample[r] = b;
+  int64_t items = (int64_t)p->mask_heads * P->rows_total;
+  P->cls = (uint8_t*)calloc((size_t)(items > 0 ? items : 1) * P->nk_max, 1);
+  run_plan_phase(p, mf, cu_q, cu_k, P, row_sample, 0, nthreads);
+  /* counts and exclusive offsets */
+  P->p_off = (int32_t*)calloc((size_t)items + 1, sizeof(int32_t));
+  P->f_off = (int32_t*)calloc((size_t)items + 1, sizeof(int32_t));
+  for (int64_t it = 0; it < items; ++it) {
+    int32_t pc = 0, fc = 0;
+    for (int64_t j = 0; j < P->nk_max; ++j) {
+      pc += P->cls[it * P->nk_max + j] == 1;
+      fc += P->cls[it * P->nk_max + j] == 2;
+    }
+    P->p_off[it + 1] = P->p_off[it] + pc;
+    P->f_off[it + 1] = P->f_off[it] + fc;
+  }
+  int64_t pnnz = P->p_off[items], fnnz = P->f_off[items];
+  P->header[0] = P->rows_total;
+  P->header[1] = pnnz;
+  P->header[2] = fnnz;
+  P->p_idx = (int32_t*)calloc((size_t)pnnz + 1, sizeof(int32_t));
+  P->f_idx = (int32_t*)calloc((size_t)fnnz + 1, sizeof(int32_t));
+  P->p_masks = (uint32_t*)calloc((size_t)pnnz * p->tile_q * P->words + 1, sizeof(uint32_t));
+  run_plan_phase(p, mf, cu_q, cu_k, P, row_sample, 1, nthreads);
+  free(row_sample);
+  return P;
+}
+
+void orc_plan_sizes(const orc_plan* P, int64_t* header8, int32_t* rows_total, int32_t* nk_max) {
+  for (int i = 0; i < 8; ++i) header8[i] = P->header[i];
+  *rows_total = P->rows_total;
+  *nk_max = P->nk_max;
+}
+
+/* Copies the plan out; any pointer may be NULL. */
+void orc_plan_export(const orc_plan* P, const orc_problem* p, int32_t* cu_rows, int32_t* seqdesc,
+                     int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
+                     int32_t* f_idx, uint8_t* cls) {
+  int64_t items = (int64_t)p->mask_heads * P->rows_total;
+  if (P->header[7]) return;
+  if (cu_rows) memcpy(cu_rows, P->cu_rows, sizeof(int32_t) * (p->batch + 1));
+  if (seqdesc) memcpy(seqdesc, P->seqdesc, sizeof(int32_t) * 8 * p->batch);
+  if (p_off) memcpy(p_off, P->p_off, sizeof(int32_t) * (items + 1));
+  if (f_off) memcpy(f_off, P->f_off, sizeof(int32_t) * (items + 1));
+  if (p_idx) memcpy(p_idx, P->p_idx, sizeof(int32_t) * P->header[1]);
+  if (f_idx) memcpy(f_idx, P->f_idx, sizeof(int32_t) * P->header[2]);
+  if (p_masks) memcpy(p_masks, P->p_masks, sizeof(uint32_t) * P->header[1] * p->tile_q * P->words);
+  if (cls) memcpy(cls, P->cls, (size_t)items * P->nk_max);
+}
+
+void orc_plan_free(orc_plan* P) {
+  if (!P) return;
+  free(P->cu_rows); free(P->seqdesc); free(P->p_off); free(P->f_off);
+  free(P->p_idx); free(P->f_idx); free(P->p_masks); free(P->cls);
+  free(P);
+}
+
+/* ------------------------------------------------------------ attention */
+
+typedef struct {
+  int softcap_on;
+  double softcap;
+  int alibi_on;
+  const float* slopes;   /* [heads_q] */
+  int alibi_first;       /* 1: ALiBi before the softcap */
+} orc_mod;
+
+/* score_mod applied to one scaled score t of head h at sample-local (q, k). */
+static double apply_mod(const orc_mod* m, double t, int h, int64_t q, int64_t k) {
+  double bias = m->alibi_on ? (double)m->slopes[h] * (double)(k - q) : 0.0;
+  if (m->alibi_on && m->alibi_first) t += bias;
+  if (m->softcap_on) t = m->softcap * tanh(t / m->softcap);
+  if (m->alibi_on && !m->alibi_first) t += bias;
+  return t;
+}
+
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float *q, *k, *v;
+  double scale;
+  const orc_mod* mod;
+  const int64_t* rows;   /* pairs (token, head); NULL = all rows */
+  int64_t begin, end;
+  double* o;             /* [n][d] for selected rows; [total_q][Hq][d] for all */
+  double* lse;           /* [n] ; [Hq][total_q] for all */
+} attn_job;
+
+static void* attn_worker(void* arg) {
+  attn_job* J = (attn_job*)arg;
+  const orc_problem* p = J->p;
+  int d = p->head_dim;
+  int64_t kmax = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)kmax);
+  double* s = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* acc = (double*)malloc(sizeof(double) * (size_t)d);
+  for (int64_t n = J->begin; n < J->end; ++n) {
+    int64_t t;
+    int h;
+    if (J->rows) {
+      t = J->rows[2 * n];
+      h = (int)J->rows[2 * n + 1];
+    } else {
+      t = n / p->heads_q;
+      h = (int)(n % p->heads_q);
+    }
+    int b = owner_of_token(p, J->cu_q, t);
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t ql = t - q_off;
+    int hm = p->mask_heads == 1 ? 0 : h;
+    int g = h / (p->heads_q / p->heads_k);
+    const int32_t* F = J->mf + (int64_t)hm * p->nfunc * p->total_q + t;
+    orc_expand_row(F, p->total_q, p->nfunc, k_len, vis);
+    const float* qrow = J->q + (t * p->heads_q + h) * (int64_t)d;
+    double m = -INFINITY;
+    int any = 0;
+    for (int64_t kk = 0; kk < k_len; ++kk) {
+      if (!vis[kk]) continue;
+      const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+      double dot = 0.0;
+      for (int i = 0; i < d; ++i) dot += (double)qrow[i] * (double)krow[i];
+      s[kk] = apply_mod(J->mod, J->scale * dot, h, ql, kk);
+      if (!any || s[kk] > m) m = s[kk];
+      any = 1;
+    }
+    double* o = J->rows ? J->o + n * d : J->o + (t * p->heads_q + h) * (int64_t)d;
+    double* lse = J->rows ? J->lse + n : J->lse + (int64_t)h * p->total_q + t;
+    if (!any) {
+      for (int i = 0; i < d; ++i) o[i] = 0.0;
+      *lse = -INFINITY;
+      continue;
+    }
+    double l = 0.0;
+    for (int i = 0; i < d; ++i) acc[i] = 0.0;
+    for (int64_t kk = 0; kk < k_len; ++kk) {
+      if (!vis[kk]) continue;
+      double w = exp(s[kk] - m);
+      l += w;
+      const float* vrow = J->v + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+      for (int i = 0; i < d; ++i) acc[i] += w * (double)vrow[i];
+    }
+    for (int i = 0; i < d; ++i) o[i] = acc[i] / l;
+    *lse = m + log(l);
+  }
+  free(vis);
+  free(s);
+  free(acc);
+  return NULL;
+}
+
+/* Attention for selected rows (rows = n pairs (token, head)) or for every row
+ * (rows = NULL, n ignored).  Inputs are float32 arrays holding the exact input
+ * values ([tokens][heads][d]); everything is computed in double. */
+void orc_attention(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                   const int32_t* cu_k, const float* q, const float* k, const float* v,
+                   double scale, int softcap_on, double softcap, int alibi_on,
+                   const float* slopes, int alibi_first, int64_t n, const int64_t* rows,
+                   double* o, double* lse, int nthreads) {
+  orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
+  int64_t total = rows ? n : (int64_t)p->total_q * p->heads_q;
+  if (nthreads < 1) nthreads = 1;
+  if (total < nthreads) nthreads = total > 0 ? (int)total : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  attn_job* jobs = (attn_job*)malloc(sizeof(attn_job) * nthreads);
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (attn_job){p, mf, cu_q, cu_k, q, k, v, scale, &mod, rows,
+                         total * t / nthreads, total * (t + 1) / nthreads, o, lse};
+    pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
