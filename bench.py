@@ -1,0 +1,227 @@
+#!/usr/bin/env python3
+"""Benchmark of interval-mask flex attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: mask_plan_build (GPU planner, one header read-back)
+followed by flex_attn_fwd over the plan.  Default workload: sliding window
+256 + 64-token sink, B=2, H=16, S=2048, d=128, bf16.
+
+Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step, counting
+4*d FLOPs per visible (q, k) pair (unmasked score entries only).  The
+attention kernel alone is reported under "fwd" and "roofline" (its duration
+measured with HIP events on the launch stream inside the timed loop).  The CPU
+oracle is timed on the host cores as "cpu_baseline" (a reported baseline, not a
+target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked FLOPs) of masked attn fwd + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA (AMD published)
+PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def plan_stats(w, plan):
+    """Algorithmic counts from the plan (no oracle): visible pairs |E|,
+    executed tiles, dense-equivalent pairs."""
+    import numpy as np
+    ex = plan.export()
+    p = plan.problem
+    pop = int(np.unpackbits(ex["p_masks"].view(np.uint8)).sum()) if ex["p_masks"].size else 0
+    pnnz, fnnz = int(ex["header"][1]), int(ex["header"][2])
+    per_mask_head = pop + fnnz * p.tile_q * p.tile_k
+    rep = w.heads_q // w.mask_heads
+    visible = per_mask_head * rep
+    executed = (pnnz + fnnz) * p.tile_q * p.tile_k * rep
+    dense = sum(w.sample_bounds(b)[1] * w.sample_bounds(b)[3] for b in range(w.batch)) * w.heads_q
+    return {"visible_pairs": visible, "executed_pairs": executed, "dense_pairs": dense,
+            "partial_tiles": pnnz, "full_tiles": fnnz, "rows": int(ex["header"][0]),
+            "tasks": int(plan.info.num_tasks)}
+
+
+def cpu_baseline(w, min_seconds=10.0):
+    """The oracle, as it is, on the host cores: whole-workload passes of the
+    fp64 attention (plus the plan) until min_seconds have elapsed."""
+    import oracle
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.build_plan(w, 128 if w.dtype == 0 else 64, 64, nthreads=threads)
+        oracle.attention(w, nthreads=threads)
+        passes += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    return time.perf_counter() - t0, passes, threads
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="window_sink")
+    ap.add_argument("--tile-q", type=int, default=0)
+    ap.add_argument("--tile-k", type=int, default=0)
+    ap.add_argument("--fwd-iters", type=int, default=100,
+                    help="extra back-to-back forward launches on one plan (steady state)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also time the forward with full tiles forced through the masked path")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mask_planned_block_amd as mpb
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = W.make(args.workload)
+    d = W.to_device(w)
+    prob = mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                            w.total_k, w.heads_q, w.heads_k, w.head_dim, w.mask_heads, w.nfunc,
+                            args.tile_q, args.tile_k)
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    kw = dict(scale=w.scale, softcap=w.softcap if w.softcap > 0 else None,
+              alibi_slopes=d["slopes"], alibi_before_softcap=w.alibi_before_softcap,
+              out=out, lse=lse, workspace=ws, stream=stream)
+
+    def step():
+        plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+        return plan
+
+    # warmup (also compiles nothing: kernels are prebuilt)
+    plans = [step() for _ in range(max(args.warmup, 1))]
+    torch.cuda.synchronize()
+    stats = plan_stats(w, plans[-1])
+    tq, tk = plans[-1].problem.tile_q, plans[-1].problem.tile_k
+    del plans
+
+    # timed steps: plan build + forward; events bracket each forward launch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    keep = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        ev[i][0].record(stream)
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+        ev[i][1].record(stream)
+        keep.append(plan)          # released after the timed region
+        if len(keep) > 2:
+            keep.pop(0).close()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_s = (t1 - t0) / args.steps
+    fwd_in_step_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    # steady-state forward on one plan (back-to-back launches)
+    plan = keep[-1]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+    e0.record(stream)
+    for _ in range(args.fwd_iters):
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ss_us = e0.elapsed_time(e1) * 1e3 / args.fwd_iters
+
+    abl = None
+    if args.ablation:
+        e0.record(stream)
+        for _ in range(args.fwd_iters):
+            mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], force_partial=True, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        abl = e0.elapsed_time(e1) * 1e3 / args.fwd_iters
+
+    # plan build alone (host clock around the call, includes its one sync)
+    tb = []
+    for _ in range(10):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        p2 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        torch.cuda.synchronize()
+        tb.append(time.perf_counter() - a)
+        p2.close()
+    plan_us = float(np.median(tb)) * 1e6
+
+    d_ = w.head_dim
+    eff = 4.0 * d_ * stats["visible_pairs"]
+    exe = 4.0 * d_ * stats["executed_pairs"]
+    dense = 4.0 * d_ * stats["dense_pairs"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == W.DTYPE_BF16 else PEAK_FP32_MFMA_TFLOPS
+    fwd_s = fwd_in_step_us * 1e-6
+    achieved = eff / fwd_s / 1e12
+
+    res = {
+        "metric": METRIC,
+        "value": round(eff / step_s / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == W.DTYPE_BF16 else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V, endpoints from the workload definition)",
+        "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
+                   "heads_k": w.heads_k, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
+                   "head_dim": w.head_dim, "mask_heads": w.mask_heads, "nfunc": w.nfunc,
+                   "tile": "%dx%d" % (tq, tk), "step": "mask_plan_build + flex_attn_fwd"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
+                     "kernel": "attn_fwd_kernel", "achieved_basis": "effective flops / "
+                     "forward duration (HIP events, timed loop)"},
+        "fwd": {
+            "us_in_step": round(fwd_in_step_us, 2),
+            "us_steady": round(fwd_ss_us, 2),
+            "effective_tflops": round(eff / fwd_s / 1e12, 3),
+            "executed_tflops": round(exe / fwd_s / 1e12, 3),
+            "dense_equiv_tflops": round(dense / fwd_s / 1e12, 3),
+            "pct_peak_dense_equiv": round(100 * dense / fwd_s / 1e12 / peak, 2),
+            "pct_peak_executed": round(100 * exe / fwd_s / 1e12 / peak, 2),
+            "effective_gflop": round(eff / 1e9, 4), "executed_gflop": round(exe / 1e9, 4),
+            "dense_gflop": round(dense / 1e9, 4),
+            "force_partial_us": None if abl is None else round(abl, 2),
+        },
+        "plan": {"build_us_host": round(plan_us, 1), **stats},
+    }
+    if not args.no_cpu_baseline:
+        secs, passes, threads = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = {
+            "value": round(eff * passes / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d whole-workload pass(es) of the fp64 oracle (plan + attention, every "
+                      "row) in %.1f s" % (passes, secs)}
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,220 @@
+/*
+ * mpb.h -- C ABI of the interval-mask flex attention library (libmpb.so).
+ *
+ * Two operations, both hand-written HIP kernels for gfx950 (MI355X):
+ *
+ *   mask_plan_build  turns per-Q-row interval endpoints into a MaskPlan: per
+ *                    (mask head, Q tile) the K tiles classed partial or full
+ *                    (empty tiles are absent), a packed predicate for every
+ *                    partial tile, and a forward task schedule.
+ *   flex_attn_fwd    consumes a plan: S = Q K^T * scale, optional score_mod
+ *                    (tanh softcap, ALiBi), online softmax over the listed K
+ *                    tiles, O = P V and a per-row log-sum-exp.
+ *
+ * Sources (cited by page title and section):
+ *   [MPD]  "Flex Attention Mask Plan Design", cuDNN frontend documentation.
+ *   [FLEX] "FlexAttention" (Dong et al.), Eq. 1 and the BlockMask section.
+ *   [TESS] "Decoupling Logical Masks from GPU Execution for Dynamic
+ *          Block-Sparse Attention" (Tessera), physical tile vs logical block.
+ *   [PYG]  cuDNN "pygraph and execution backends" page, sections "Handle,
+ *          stream, and device" and "Accept means run".
+ *
+ * Conventions for every entry point:
+ *   - Every call returns an mpb_status; nothing throws across the ABI.  On
+ *     failure mpb_last_error_detail() (thread-local) names the violated rule.
+ *   - Device pointers are plain HIP device addresses (e.g. torch tensor
+ *     data_ptr()).  `stream` is a hipStream_t passed as void*; NULL is the
+ *     null stream.  There is no ambient stream or device state [PYG].
+ *   - The caller owns every buffer it passes in; the plan owns every array it
+ *     creates (including device copies of cu_seqlens) [MPD §3.2, §8].
+ */
+#ifndef MPB_H_
+#define MPB_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MPB_OK = 0,
+  MPB_ERR_INVALID_ARGUMENT = 1,   /* host-decidable shape/pointer/enum error */
+  MPB_ERR_ENDPOINT_RANGE = 2,     /* an endpoint < 0 or > its sample's k_len [MPD §2, §4.3] */
+  MPB_ERR_ENDPOINT_ORDER = 3,     /* F(i) > F(i+1) for some row [MPD §2, §4.3] */
+  MPB_ERR_SEQLENS = 4,            /* cu_seqlens not 0..total, decreasing, or > max_seqlen [MPD §3.2] */
+  MPB_ERR_SIGNATURE_MISMATCH = 5, /* plan used with another geometry/consumer/device [MPD §7] */
+  MPB_ERR_WORKSPACE = 6,          /* workspace missing or too small */
+  MPB_ERR_UNSUPPORTED = 7,        /* legal but not implemented (head_dim, tile, nfunc > 4095) */
+  MPB_ERR_OUT_OF_MEMORY = 8,
+  MPB_ERR_DEVICE = 9              /* a HIP runtime call failed */
+} mpb_status;
+
+enum { MPB_LAYOUT_BSHD = 0, MPB_LAYOUT_THD = 1 };
+enum { MPB_DTYPE_BF16 = 0, MPB_DTYPE_FP32 = 1 };
+
+/* Device error bits, OR-ed into header[7] by the planner kernels. */
+enum { MPB_DEVERR_SEQLENS = 1, MPB_DEVERR_RANGE = 2, MPB_DEVERR_ORDER = 4 };
+
+/* Problem geometry = the plan binding [MPD §8].
+ *   BSHD: Q is [batch, seqlen_q, heads_q, head_dim], K/V [batch, seqlen_k,
+ *         heads_k, head_dim], contiguous; total_q = batch*seqlen_q,
+ *         total_k = batch*seqlen_k.
+ *   THD : Q is [total_q, heads_q, head_dim], K/V [total_k, heads_k, head_dim];
+ *         seqlen_q/seqlen_k are max_seqlen_q/k; sample b owns tokens
+ *         [cu_seqlens[b], cu_seqlens[b+1]).
+ *   mask_heads (Hmask) is 1 (one mask shared by all Q heads) or heads_q
+ *   [MPD §2].  nfunc is odd, 1 <= nfunc <= 4095.  heads_q % heads_k == 0; the
+ *   K/V head of Q head h is h / (heads_q / heads_k).  tile_q/tile_k are the
+ *   physical tile (0 = library default), chosen independently of any logical
+ *   block size [TESS "logical blocks and physical tiles"]. */
+typedef struct mpb_problem {
+  int32_t layout;
+  int32_t dtype;
+  int32_t batch;
+  int32_t seqlen_q, seqlen_k;
+  int32_t total_q, total_k;
+  int32_t heads_q, heads_k, head_dim;
+  int32_t mask_heads, nfunc;
+  int32_t tile_q, tile_k;
+} mpb_problem;
+
+typedef struct mpb_plan mpb_plan; /* opaque, immutable after build [MPD §8] */
+
+/* Consumer signature recorded in a plan and compared field by field before
+ * every launch; a mismatch is an error, never a fallback [MPD §7, §9.9]. */
+typedef struct mpb_signature {
+  int32_t arch;            /* 950 = gfx950 */
+  int32_t direction;       /* 0 = forward */
+  int32_t kernel_family;   /* 1 = bf16 MFMA 32x32x16, 2 = fp32 MFMA 32x32x2 */
+  int32_t tile_q, tile_k, head_dim, dtype;
+  int32_t payload_layout;  /* 1 = row-major, 32-column uint32 words (see below) */
+  int32_t scheduler;       /* 1 = per-section work queues, atomic counters in workspace */
+} mpb_signature;
+
+typedef struct mpb_plan_info {
+  int64_t header[8];       /* fwd Q rows, fwd partial nnz, fwd full nnz, 0, 0, 0, 0, error bits */
+  int32_t rows_total;      /* Q plan rows over all samples */
+  int32_t nk_max;          /* K tiles of the longest sample */
+  int32_t words_per_row;   /* tile_k / 32 */
+  int32_t num_tasks;       /* rows_total * heads_q */
+  int32_t num_sections;    /* schedule sections (work queues) */
+  int32_t device;
+  mpb_problem problem;
+  mpb_signature signature;
+  int64_t device_bytes;    /* bytes of device memory the plan holds */
+} mpb_plan_info;
+
+/* score_mod of [FLEX] Eq. 1, applied to t = scale * (q . k):
+ *   softcap:  t <- softcap * tanh(t / softcap)
+ *   ALiBi:    t <- t + alibi_slopes[h] * (k - q), sample-local positions
+ * Default order is softcap, then ALiBi; alibi_before_softcap = 1 swaps it.
+ * alibi_slopes is a device float array [heads_q]. */
+typedef struct mpb_score_mod {
+  int32_t softcap_enabled;
+  float softcap;
+  int32_t alibi_enabled;
+  const float* alibi_slopes;
+  int32_t alibi_before_softcap;
+} mpb_score_mod;
+
+/* mask_plan_build [MPD §4]: host structural validation and consumer
+ * resolution (§4.1), then GPU stages: Varlen geometry (§4.2), Q2K
+ * classification with endpoint validation (§4.3), count scan and header
+ * (§4.5), one 8-value header read-back with a single stream synchronisation,
+ * exact allocation, Q2K materialisation of the partial/full CSR and the packed
+ * predicates (§4.6, §5) and the forward schedule (§4.8).
+ *
+ *   mask_func    device int32 [mask_heads][nfunc][total_q]; column t holds the
+ *                endpoints F0..F(nfunc-1) of Q token t, sample-local K
+ *                positions; row t sees [0,F0) U [F1,F2) U ... [MPD §2].
+ *                It may be freed once the call returns.
+ *   cu_seqlens_q/k  device int32 [batch+1] for THD; ignored (may be NULL) for
+ *                BSHD.  Validated on the GPU [MPD §3.2].
+ *   stream       work is enqueued here; the call synchronises on it once.
+ *   out          receives the plan, or NULL on any failure (nothing leaks).
+ * Errors: host-decidable problems return MPB_ERR_INVALID_ARGUMENT or
+ * MPB_ERR_UNSUPPORTED before any launch; endpoint and prefix violations found
+ * on the GPU return MPB_ERR_SEQLENS, then MPB_ERR_ENDPOINT_RANGE, then
+ * MPB_ERR_ENDPOINT_ORDER (first set bit in that order).
+ *
+ * Plan layout (device, read with mask_plan_export):
+ *   rows are Q tiles of T_Q tokens per sample; row r of sample b is global row
+ *   cu_rows[b] + r; CSR rows are flattened head-major, flat = hm*rows_total +
+ *   row.  p_off/f_off [mask_heads*rows_total + 1] are exclusive offsets into
+ *   p_idx/f_idx (sample-local K-tile indices, ascending).  Partial tile n
+ *   owns payload words p_masks[n][T_Q][tile_k/32]: bit c%32 of word
+ *   [r][c/32] is 1 iff score (row r, column c) of the tile is visible and in
+ *   bounds [MPD §5].  In the attention kernel each lane owns one Q row and 16
+ *   K columns of every 32-column block, all in one such word, so it reads its
+ *   predicate with a single dword load (the packed-bit select of [MPD §5.1]). */
+mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           void* stream, mpb_plan** out);
+
+/* Releases the plan's device memory in stream order on its build stream.
+ * The caller must order every use of the plan on other streams before this
+ * call (e.g. synchronise them).  NULL is accepted. */
+mpb_status mask_plan_destroy(mpb_plan* plan);
+
+/* Header, geometry and signature of a plan (host struct, no device access). */
+mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info);
+
+/* Copies plan arrays to host memory [MPD §8 debug_snapshot]; any pointer may
+ * be NULL.  Sizes: cu_rows [batch+1], seqdesc [batch][8] = {q_offset,
+ * k_offset, q_len, k_len, row_begin, row_count, k_tiles, 0}, p_off/f_off
+ * [mask_heads*rows_total+1], p_idx [header[1]], f_idx [header[2]], p_masks
+ * [header[1]*tile_q*tile_k/32], work_desc [num_tasks][4] = {m_block, head,
+ * batch, q_valid_rows} in schedule order, section_off [num_sections+1].
+ * Synchronises the plan's build stream. */
+mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seqdesc,
+                            int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
+                            int32_t* f_idx, int32_t* work_desc, int32_t* section_off);
+
+/* Bytes of caller-provided device workspace flex_attn_fwd needs (the work
+ * queue counters [MPD §4.8]).  One workspace per concurrently running call. */
+size_t flex_attn_fwd_workspace_size(const mpb_plan* plan);
+
+/* flex_attn_fwd [MPD §6.1; FLEX Eq. 1]: block-sparse attention forward.
+ *   problem   geometry of q/k/v/o as the caller sees it; must equal the plan's
+ *             binding field by field (tile_q/tile_k may be 0) and the current
+ *             device must be the plan's, else MPB_ERR_SIGNATURE_MISMATCH.
+ *   q,k,v     device, layout per `problem` (bf16 or fp32 per dtype).
+ *   o         device, same layout and dtype as q.
+ *   lse       device float32 [heads_q][total_q], natural log of the sum of
+ *             exp(score) over visible keys (scores after score_mod).  A row
+ *             with nothing visible gets O = 0 and LSE = -inf [MPD §6.1].
+ *   scale     multiplies q.k before score_mod (usually 1/sqrt(head_dim)).
+ *   mod       NULL for no score_mod.
+ *   workspace device, >= flex_attn_fwd_workspace_size(plan) bytes, any
+ *             contents; reset by the call.
+ * Partial tiles apply their predicate; full tiles skip it; empty tiles are
+ * never touched.  Enqueue only; no synchronisation.  Every refusal happens
+ * before the launch [PYG "Accept means run"]. */
+mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                         const void* k, const void* v, void* o, float* lse, float scale,
+                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* Ablation hook: same contract as flex_attn_fwd.  With force_partial = 1
+ * every full tile runs through the partial-tile code path with an all-ones
+ * predicate, which measures what the full-tile fast path saves ([FLEX] "full
+ * block optimization"; [MPD §6.1]).  Results equal flex_attn_fwd's. */
+mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
+                                  const void* q, const void* k, const void* v, void* o,
+                                  float* lse, float scale, const mpb_score_mod* mod,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t force_partial);
+
+const char* mpb_status_string(mpb_status status);
+const char* mpb_last_error_detail(void);
+
+/* Library ABI version (major*100 + minor). */
+int32_t mpb_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MPB_H_ */

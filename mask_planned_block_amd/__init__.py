@@ -1,0 +1,281 @@
+"""Python binding of libmpb: interval-mask flex attention on MI355X (gfx950).
+
+Argument marshalling only.  Every step of the path -- plan building and the
+attention forward -- runs in the HIP kernels of ``libmpb.so`` behind the C ABI
+of ``include/mpb.h``; torch tensors provide device memory and streams.  There
+is no CPU fallback: importing this package fails if the library is missing.
+
+    plan = mask_plan_build(problem, mask_func, cu_seqlens_q, cu_seqlens_k)
+    o, lse = flex_attn_fwd(plan, q, k, v, scale=..., softcap=..., alibi_slopes=...)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "MPBError", "Problem", "MaskPlan",
+    "make_problem", "mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
+    "flex_attn_fwd", "flex_attn_fwd_workspace_size", "library_path",
+]
+
+LAYOUT_BSHD = 0
+LAYOUT_THD = 1
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+NUM_QUEUES = 9
+
+STATUS = {0: "MPB_OK", 1: "MPB_ERR_INVALID_ARGUMENT", 2: "MPB_ERR_ENDPOINT_RANGE",
+          3: "MPB_ERR_ENDPOINT_ORDER", 4: "MPB_ERR_SEQLENS", 5: "MPB_ERR_SIGNATURE_MISMATCH",
+          6: "MPB_ERR_WORKSPACE", 7: "MPB_ERR_UNSUPPORTED", 8: "MPB_ERR_OUT_OF_MEMORY",
+          9: "MPB_ERR_DEVICE"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libmpb.so")
+
+
+class MPBError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, "MPB_ERR_%d" % status)
+        super().__init__("%s: %s" % (self.name, detail))
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layout", "dtype", "batch", "seqlen_q", "seqlen_k", "total_q", "total_k", "heads_q",
+        "heads_k", "head_dim", "mask_heads", "nfunc", "tile_q", "tile_k")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class Signature(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "arch", "direction", "kernel_family", "tile_q", "tile_k", "head_dim", "dtype",
+        "payload_layout", "scheduler")]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("header", ctypes.c_int64 * 8), ("rows_total", ctypes.c_int32),
+                ("nk_max", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
+                ("num_tasks", ctypes.c_int32), ("num_sections", ctypes.c_int32),
+                ("device", ctypes.c_int32), ("problem", Problem), ("signature", Signature),
+                ("device_bytes", ctypes.c_int64)]
+
+
+class ScoreMod(ctypes.Structure):
+    _fields_ = [("softcap_enabled", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("alibi_enabled", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p),
+                ("alibi_before_softcap", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError("libmpb.so is not built (%s); run __graft_entry__.build() or "
+                          "python mask_planned_block_amd/build.py" % library_path)
+    lib = ctypes.CDLL(library_path)
+    vp, P = ctypes.c_void_p, ctypes.POINTER
+    lib.mask_plan_build.argtypes = [P(Problem), vp, vp, vp, vp, P(vp)]
+    lib.mask_plan_destroy.argtypes = [vp]
+    lib.mask_plan_info.argtypes = [vp, P(PlanInfo)]
+    lib.mask_plan_export.argtypes = [vp] + [vp] * 9
+    lib.flex_attn_fwd_workspace_size.argtypes = [vp]
+    lib.flex_attn_fwd_workspace_size.restype = ctypes.c_size_t
+    fwd_args = [vp, P(Problem), vp, vp, vp, vp, vp, ctypes.c_float, P(ScoreMod), vp,
+                ctypes.c_size_t, vp]
+    lib.flex_attn_fwd.argtypes = fwd_args
+    lib.flex_attn_fwd_ablation.argtypes = fwd_args + [ctypes.c_int32]
+    lib.mpb_status_string.restype = ctypes.c_char_p
+    lib.mpb_status_string.argtypes = [ctypes.c_int]
+    lib.mpb_last_error_detail.restype = ctypes.c_char_p
+    lib.mpb_version.restype = ctypes.c_int32
+    for name in ("mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
+                 "flex_attn_fwd", "flex_attn_fwd_ablation"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MPBError(status, _lib.mpb_last_error_detail().decode())
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dev_ptr(t: Optional[torch.Tensor], what: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (what, dtype, t.dtype))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_problem(layout, dtype, batch, seqlen_q, seqlen_k, total_q, total_k, heads_q, heads_k,
+                 head_dim, mask_heads, nfunc, tile_q=0, tile_k=0) -> Problem:
+    return Problem(layout, dtype, batch, seqlen_q, seqlen_k, total_q, total_k, heads_q, heads_k,
+                   head_dim, mask_heads, nfunc, tile_q, tile_k)
+
+
+class MaskPlan:
+    """Owner of an opaque mpb_plan handle (immutable device plan)."""
+
+    def __init__(self, handle: int, stream_handle: int):
+        self._h = ctypes.c_void_p(handle)
+        self._stream = stream_handle
+        self.info = mask_plan_info(self)
+        self.problem = self.info.problem
+
+    @property
+    def handle(self):
+        return self._h
+
+    def header(self):
+        return list(self.info.header)
+
+    def export(self):
+        return mask_plan_export(self)
+
+    def close(self):
+        if self._h and self._h.value:
+            _lib.mask_plan_destroy(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mask_plan_build(problem: Problem, mask_func: torch.Tensor,
+                    cu_seqlens_q: Optional[torch.Tensor] = None,
+                    cu_seqlens_k: Optional[torch.Tensor] = None, stream=None) -> MaskPlan:
+    """Builds a MaskPlan on the GPU (one header read-back; see include/mpb.h)."""
+    mf = _dev_ptr(mask_func, "mask_func", torch.int32)
+    cq = _dev_ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    ck = _dev_ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32)
+    s = _stream_handle(stream)
+    out = ctypes.c_void_p()
+    _check(_lib.mask_plan_build(ctypes.byref(problem), mf, cq, ck, ctypes.c_void_p(s),
+                                ctypes.byref(out)))
+    return MaskPlan(out.value, s)
+
+
+def mask_plan_destroy(plan: MaskPlan):
+    plan.close()
+
+
+def mask_plan_info(plan: MaskPlan) -> PlanInfo:
+    info = PlanInfo()
+    _check(_lib.mask_plan_info(plan.handle, ctypes.byref(info)))
+    return info
+
+
+def mask_plan_export(plan: MaskPlan) -> dict:
+    """Host copies of every plan array (numpy)."""
+    info = plan.info
+    p = info.problem
+    n_off = p.mask_heads * info.rows_total + 1
+    pnnz, fnnz = int(info.header[1]), int(info.header[2])
+    W = p.tile_k // 32
+    a = {
+        "cu_rows": np.zeros(p.batch + 1, np.int32),
+        "seqdesc": np.zeros((p.batch, 8), np.int32),
+        "p_off": np.zeros(n_off, np.int32),
+        "p_idx": np.zeros(max(pnnz, 1), np.int32),
+        "p_masks": np.zeros(max(pnnz * p.tile_q * W, 1), np.uint32),
+        "f_off": np.zeros(n_off, np.int32),
+        "f_idx": np.zeros(max(fnnz, 1), np.int32),
+        "work_desc": np.zeros((max(info.num_tasks, 1), 4), np.int32),
+        "section_off": np.zeros(NUM_QUEUES + 1, np.int32),
+    }
+    ptrs = [ctypes.c_void_p(a[k].ctypes.data) for k in
+            ("cu_rows", "seqdesc", "p_off", "p_idx", "p_masks", "f_off", "f_idx", "work_desc",
+             "section_off")]
+    _check(_lib.mask_plan_export(plan.handle, *ptrs))
+    a["p_idx"] = a["p_idx"][:pnnz]
+    a["f_idx"] = a["f_idx"][:fnnz]
+    a["p_masks"] = a["p_masks"][:pnnz * p.tile_q * W].reshape(pnnz, p.tile_q, W)
+    a["work_desc"] = a["work_desc"][:info.num_tasks]
+    a["header"] = np.asarray(list(info.header), np.int64)
+    return a
+
+
+def flex_attn_fwd_workspace_size(plan: MaskPlan) -> int:
+    return int(_lib.flex_attn_fwd_workspace_size(plan.handle))
+
+
+def _call_problem(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor) -> Problem:
+    """Geometry of the call as the tensors show it (checked against the plan
+    binding by the library)."""
+    p = plan.problem
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else (DTYPE_FP32 if q.dtype == torch.float32
+                                                     else -1)
+    if p.layout == LAYOUT_BSHD:
+        if q.dim() != 4 or k.dim() != 4:
+            raise ValueError("BSHD q/k/v must be 4-D [B, S, H, D]")
+        B, Sq, Hq, D = q.shape
+        _, Sk, Hk, _ = k.shape
+        return Problem(LAYOUT_BSHD, dt, B, Sq, Sk, B * Sq, B * Sk, Hq, Hk, D, p.mask_heads,
+                       p.nfunc, 0, 0)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("THD q/k/v must be 3-D [T, H, D]")
+    Tq, Hq, D = q.shape
+    Tk, Hk, _ = k.shape
+    return Problem(LAYOUT_THD, dt, p.batch, p.seqlen_q, p.seqlen_k, Tq, Tk, Hq, Hk, D,
+                   p.mask_heads, p.nfunc, 0, 0)
+
+
+def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  scale: Optional[float] = None, softcap: Optional[float] = None,
+                  alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
+                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  force_partial: bool = False):
+    """Block-sparse attention forward over a plan.  Returns (O, LSE[Hq, total_q]).
+
+    Allocates O/LSE/workspace with torch when not given (device memory only)."""
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    prob = _call_problem(plan, q, k)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
+    need = flex_attn_fwd_workspace_size(plan)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    mod = None
+    if softcap or alibi_slopes is not None:
+        mod = ScoreMod(1 if softcap else 0, float(softcap or 0.0),
+                       1 if alibi_slopes is not None else 0,
+                       _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
+                       1 if alibi_before_softcap else 0)
+    sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
+    args = (plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
+            _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
+            ctypes.byref(mod) if mod is not None else None, _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream_handle(stream)))
+    if force_partial:
+        _check(_lib.flex_attn_fwd_ablation(*args, 1))
+    else:
+        _check(_lib.flex_attn_fwd(*args))
+    return out, lse

@@ -1,0 +1,114 @@
+// Internal declarations shared by the host runtime and the HIP kernels of
+// libmpb.  Nothing here is part of the public ABI (include/mpb.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mpb {
+
+// Forward schedule: positive-cost tasks are split into kNumSections sections,
+// one per XCD of the MI355X (8 XCDs with a private L2 each).  Tasks of one
+// (batch, K/V head) pair share a section, so the work queue of XCD x keeps
+// that pair's K/V tiles in x's L2 (this library's reading of the "L2 section"
+// of the mask plan design page, §4.8).  Zero-cost tasks (rows with nothing
+// visible) form one more queue that is drained last.
+constexpr int kNumSections = 8;
+constexpr int kNumQueues = kNumSections + 1;
+
+// Planner geometry, passed by value to every planner kernel.
+struct PlanGeo {
+  int32_t layout;       // 0 BSHD, 1 THD
+  int32_t batch;
+  int32_t seqlen_q, seqlen_k;   // BSHD: Sq, Sk ; THD: max lengths
+  int32_t total_q, total_k;
+  int32_t heads_q, heads_k, mask_heads, nfunc;
+  int32_t tile_q, tile_k;
+  int32_t upper_rows;   // upper bound of Q plan rows (exact for BSHD)
+  int32_t nk_max;       // upper bound of K tiles per sample
+  int32_t words_k;      // ceil(nk_max / 32): bitset words per (hm, row)
+  int32_t words_tile;   // tile_k / 32: payload words per tile row
+};
+
+// Device arrays of a plan.
+struct PlanDev {
+  int32_t* header;       // [8]
+  int32_t* seqdesc;      // [B][8]
+  int32_t* cu_rows;      // [B+1]
+  int32_t* cu_q;         // [B+1] clone (THD) or nullptr
+  int32_t* cu_k;
+  int32_t* work_desc;    // [upper_rows*Hq][4]
+  int32_t* section_off;  // [kNumQueues+1]
+  int32_t* p_off;        // [Hmask*rows+1]
+  int32_t* f_off;
+  int32_t* p_idx;
+  int32_t* f_idx;
+  uint32_t* p_masks;
+};
+
+// Build-time workspace (freed when the build finishes).
+struct PlanWork {
+  uint32_t* vis_bits;    // [Hmask][upper_rows][words_k]
+  uint32_t* full_bits;
+  int32_t* pcnt;         // [Hmask][upper_rows]
+  int32_t* fcnt;
+  int32_t* p_off_tmp;    // [Hmask*upper_rows+1] (compact head-major order)
+  int32_t* f_off_tmp;
+  int32_t* bins;         // [kNumQueues][nk_max+1] histogram, then cursors
+};
+
+// ---- planner launchers (plan_kernels.hip) ----
+hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
+                                const PlanDev& d, hipStream_t s);
+hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                                const PlanWork& w, hipStream_t s);
+hipError_t launch_plan_scan(const PlanGeo& g, const PlanDev& d, const PlanWork& w, hipStream_t s);
+hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                int32_t rows_upper_tasks, hipStream_t s);
+hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                                   const PlanWork& w, int32_t rows_total, hipStream_t s);
+
+// ---- attention ----
+enum ModKind : int32_t {
+  kModNone = 0,
+  kModSoftcap = 1,
+  kModAlibi = 2,
+  kModSoftcapAlibi = 3,   // softcap, then ALiBi
+  kModAlibiSoftcap = 4,   // ALiBi, then softcap
+};
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* seqdesc;
+  const int32_t* cu_rows;
+  const int32_t* p_off;
+  const int32_t* p_idx;
+  const int32_t* f_off;
+  const int32_t* f_idx;
+  const uint32_t* p_masks;
+  const int32_t* work_desc;
+  const int32_t* section_off;
+  int32_t* counters;        // [kNumQueues + 1] in caller workspace
+  const float* slopes;
+  int32_t heads_q, heads_k, group, mask_heads, rows_total, total_q;
+  int32_t force_partial;
+  float scale_log2;         // scale * log2(e)
+  float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
+  float softcap_c2;         // c * log2(e)
+  float alibi_k;            // ALiBi-first: 2*log2(e)/c multiplier of slope*(k-q)
+};
+
+// Attention kernel variants known to this build (the consumers a plan can be
+// resolved to).  Returns false if (dtype, head_dim, tile_q, tile_k) has none.
+bool attn_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k);
+hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
+                           int32_t mod_kind, int32_t grid, const AttnParams& p, hipStream_t s);
+int32_t attn_grid_size(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
+                       int32_t num_tasks, int device);
+hipError_t launch_reset_counters(int32_t* counters, hipStream_t s);
+
+}  // namespace mpb

@@ -1,0 +1,585 @@
+// Host runtime of libmpb: the C ABI declared in include/mpb.h.
+//
+// mask_plan_build follows the stage order of "Flex Attention Mask Plan
+// Design" §4: host structural validation and consumer resolution (§4.1) with
+// no elementwise work on the host; GPU geometry, classification and scan; one
+// 8-value header read-back (§4.5) that both sizes the exact allocation and
+// reports device-side validation errors; then materialisation (§4.6) and the
+// forward schedule (§4.8).  The schedule kernels are enqueued right after the
+// header copy so they overlap the host's wait and allocation.
+//
+// Device memory comes from a per-device stream-ordered pool owned by the
+// library (allocation and release are enqueued on the caller's stream), so a
+// build costs no device-wide synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+
+#include "../../include/mpb.h"
+#include "mpb_internal.h"
+
+using namespace mpb;
+
+struct mpb_plan {
+  int device;
+  mpb_problem prob;        // binding, with the resolved tile
+  mpb_signature sig;
+  PlanGeo geo;
+  PlanDev dev;
+  int32_t rows_total;
+  int32_t num_tasks;
+  int64_t header[8];
+  void* geo_block;
+  void* exact_block;
+  size_t geo_bytes;
+  size_t exact_bytes;
+  hipStream_t stream;
+};
+
+namespace {
+
+thread_local std::string g_detail;
+
+mpb_status fail(mpb_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+mpb_status ok() {
+  g_detail.clear();
+  return MPB_OK;
+}
+
+// ---- per-device stream-ordered memory pool
+
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[64];
+
+hipError_t device_pool(int dev, hipMemPool_t* out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool = nullptr;
+    hipError_t e = hipMemPoolCreate(&pool, &props);
+    if (e != hipSuccess) return e;
+    uint64_t keep = ~0ull;  // keep freed blocks cached for the next build
+    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    if (e != hipSuccess) return e;
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return hipSuccess;
+}
+
+// ---- per-thread pinned header slot and completion event
+
+struct ThreadSlot {
+  int32_t* pinned = nullptr;
+  hipEvent_t ev[64] = {};
+};
+thread_local ThreadSlot g_slot;
+
+hipError_t thread_slot(int dev, int32_t** pinned, hipEvent_t* ev) {
+  if (!g_slot.pinned) {
+    hipError_t e = hipHostMalloc((void**)&g_slot.pinned, 8 * sizeof(int32_t), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      g_slot.pinned = nullptr;
+      return e;
+    }
+  }
+  if (!g_slot.ev[dev]) {
+    hipError_t e = hipEventCreateWithFlags(&g_slot.ev[dev], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      g_slot.ev[dev] = nullptr;
+      return e;
+    }
+  }
+  *pinned = g_slot.pinned;
+  *ev = g_slot.ev[dev];
+  return hipSuccess;
+}
+
+// ---- layout of a device block carved into 256-byte aligned arrays
+
+struct Carver {
+  size_t off = 0;
+  template <class T>
+  size_t take(int64_t count) {
+    const size_t o = off;
+    const size_t bytes = (size_t)(count > 0 ? count : 1) * sizeof(T);
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 128 : 64; }
+int default_tile_k(const mpb_problem& p) {
+  return (p.dtype == MPB_DTYPE_FP32 && p.head_dim > 64) ? 32 : 64;
+}
+
+mpb_signature consumer_signature(const mpb_problem& p, int tq, int tk) {
+  mpb_signature s;
+  s.arch = 950;
+  s.direction = 0;
+  s.kernel_family = p.dtype == MPB_DTYPE_BF16 ? 1 : 2;
+  s.tile_q = tq;
+  s.tile_k = tk;
+  s.head_dim = p.head_dim;
+  s.dtype = p.dtype;
+  s.payload_layout = 1;
+  s.scheduler = 1;
+  return s;
+}
+
+// §4.1: structural validation only (no element is read on the host).
+mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out) {
+  if (!p) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
+  if (p->layout != MPB_LAYOUT_BSHD && p->layout != MPB_LAYOUT_THD)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "layout %d is neither BSHD (0) nor THD (1)", p->layout);
+  if (p->dtype != MPB_DTYPE_BF16 && p->dtype != MPB_DTYPE_FP32)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "dtype %d is neither bf16 (0) nor fp32 (1)", p->dtype);
+  if (p->batch < 1) return fail(MPB_ERR_INVALID_ARGUMENT, "batch %d < 1", p->batch);
+  if (p->seqlen_q < 0 || p->seqlen_k < 0)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "negative sequence length");
+  if (p->total_q < 0 || p->total_k < 0)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "negative token total");
+  if (p->layout == MPB_LAYOUT_BSHD) {
+    if ((int64_t)p->batch * p->seqlen_q != p->total_q)
+      return fail(MPB_ERR_INVALID_ARGUMENT, "BSHD total_q %d != batch*seqlen_q", p->total_q);
+    if ((int64_t)p->batch * p->seqlen_k != p->total_k)
+      return fail(MPB_ERR_INVALID_ARGUMENT, "BSHD total_k %d != batch*seqlen_k", p->total_k);
+  }
+  if (p->heads_q < 1 || p->heads_k < 1)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "heads_q/heads_k must be >= 1");
+  if (p->heads_q % p->heads_k != 0)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "heads_q %d is not a multiple of heads_k %d", p->heads_q,
+                p->heads_k);
+  if (p->head_dim < 1) return fail(MPB_ERR_INVALID_ARGUMENT, "head_dim %d < 1", p->head_dim);
+  if (p->mask_heads != 1 && p->mask_heads != p->heads_q)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "mask_heads %d is neither 1 nor heads_q %d",
+                p->mask_heads, p->heads_q);
+  if (p->nfunc < 1 || (p->nfunc % 2) == 0)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "nfunc %d is not a positive odd integer", p->nfunc);
+  if (p->nfunc > 4095) return fail(MPB_ERR_UNSUPPORTED, "nfunc %d > 4095", p->nfunc);
+  const int tq = p->tile_q ? p->tile_q : default_tile_q(*p);
+  const int tk = p->tile_k ? p->tile_k : default_tile_k(*p);
+  if (tq != 32 && tq != 64 && tq != 128 && tq != 256)
+    return fail(MPB_ERR_UNSUPPORTED, "tile_q %d not in {32,64,128,256}", tq);
+  if (tk < 32 || tk % 32 != 0 || tk > 256)
+    return fail(MPB_ERR_UNSUPPORTED, "tile_k %d is not a multiple of 32 in [32,256]", tk);
+  if (!attn_variant_exists(p->dtype, p->head_dim, tq, tk))
+    return fail(MPB_ERR_UNSUPPORTED,
+                "no gfx950 forward consumer for dtype %d, head_dim %d, tile %dx%d", p->dtype,
+                p->head_dim, tq, tk);
+  const int64_t elems = (int64_t)p->total_q * p->heads_q * p->head_dim;
+  if (elems > ((int64_t)1 << 40)) return fail(MPB_ERR_UNSUPPORTED, "problem too large");
+  *tq_out = tq;
+  *tk_out = tk;
+  return MPB_OK;
+}
+
+mpb_status device_status(hipError_t e, const char* what) {
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+    return fail(MPB_ERR_OUT_OF_MEMORY, "%s: %s", what, hipGetErrorString(e));
+  return fail(MPB_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mpb_version(void) { return 100; }
+
+const char* mpb_status_string(mpb_status s) {
+  switch (s) {
+    case MPB_OK: return "MPB_OK";
+    case MPB_ERR_INVALID_ARGUMENT: return "MPB_ERR_INVALID_ARGUMENT";
+    case MPB_ERR_ENDPOINT_RANGE: return "MPB_ERR_ENDPOINT_RANGE";
+    case MPB_ERR_ENDPOINT_ORDER: return "MPB_ERR_ENDPOINT_ORDER";
+    case MPB_ERR_SEQLENS: return "MPB_ERR_SEQLENS";
+    case MPB_ERR_SIGNATURE_MISMATCH: return "MPB_ERR_SIGNATURE_MISMATCH";
+    case MPB_ERR_WORKSPACE: return "MPB_ERR_WORKSPACE";
+    case MPB_ERR_UNSUPPORTED: return "MPB_ERR_UNSUPPORTED";
+    case MPB_ERR_OUT_OF_MEMORY: return "MPB_ERR_OUT_OF_MEMORY";
+    case MPB_ERR_DEVICE: return "MPB_ERR_DEVICE";
+  }
+  return "MPB_ERR_UNKNOWN";
+}
+
+const char* mpb_last_error_detail(void) { return g_detail.c_str(); }
+
+mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* stream,
+                           mpb_plan** out) {
+  if (!out) return fail(MPB_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  int tq = 0, tk = 0;
+  mpb_status st = validate_problem(problem, &tq, &tk);
+  if (st != MPB_OK) return st;
+  const mpb_problem& p = *problem;
+  if (!mask_func && p.total_q > 0) return fail(MPB_ERR_INVALID_ARGUMENT, "mask_func is NULL");
+  if (p.layout == MPB_LAYOUT_THD && (!cu_seqlens_q || !cu_seqlens_k))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "THD layout needs cu_seqlens_q and cu_seqlens_k");
+
+  PlanGeo g;
+  g.layout = p.layout;
+  g.batch = p.batch;
+  g.seqlen_q = p.seqlen_q;
+  g.seqlen_k = p.seqlen_k;
+  g.total_q = p.total_q;
+  g.total_k = p.total_k;
+  g.heads_q = p.heads_q;
+  g.heads_k = p.heads_k;
+  g.mask_heads = p.mask_heads;
+  g.nfunc = p.nfunc;
+  g.tile_q = tq;
+  g.tile_k = tk;
+  const int64_t upper = p.layout == MPB_LAYOUT_BSHD
+                            ? (int64_t)p.batch * ((p.seqlen_q + tq - 1) / tq)
+                            : ((int64_t)p.total_q + (int64_t)p.batch * (tq - 1)) / tq;
+  const int64_t nk_max = ((int64_t)p.seqlen_k + tk - 1) / tk;
+  const int64_t words_k = nk_max > 0 ? (nk_max + 31) / 32 : 1;
+  if (upper * p.mask_heads >= ((int64_t)1 << 31) || upper * p.heads_q >= ((int64_t)1 << 31) ||
+      upper * p.mask_heads * words_k >= ((int64_t)1 << 31))
+    return fail(MPB_ERR_UNSUPPORTED, "too many plan rows");
+  g.upper_rows = (int32_t)upper;
+  g.nk_max = (int32_t)nk_max;
+  g.words_k = (int32_t)words_k;
+  g.words_tile = tk / 32;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  hipMemPool_t pool;
+  if ((e = device_pool(dev, &pool)) != hipSuccess) return device_status(e, "memory pool");
+  int32_t* pinned = nullptr;
+  hipEvent_t ev;
+  if ((e = thread_slot(dev, &pinned, &ev)) != hipSuccess) return device_status(e, "host slot");
+
+  const int64_t items_upper = upper * p.mask_heads;
+  Carver cg;
+  const size_t o_header = cg.take<int32_t>(8);
+  const size_t o_seqdesc = cg.take<int32_t>(8 * (int64_t)p.batch);
+  const size_t o_cu_rows = cg.take<int32_t>(p.batch + 1);
+  const size_t o_cu_q = cg.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 1);
+  const size_t o_cu_k = cg.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 1);
+  const size_t o_work_desc = cg.take<int32_t>(4 * upper * p.heads_q);
+  const size_t o_sec = cg.take<int32_t>(kNumQueues + 1);
+  Carver cw;
+  const size_t o_vis = cw.take<uint32_t>(items_upper * words_k);
+  const size_t o_full = cw.take<uint32_t>(items_upper * words_k);
+  const size_t o_pcnt = cw.take<int32_t>(items_upper);
+  const size_t o_fcnt = cw.take<int32_t>(items_upper);
+  const size_t o_poff = cw.take<int32_t>(items_upper + 1);
+  const size_t o_foff = cw.take<int32_t>(items_upper + 1);
+  const size_t o_bins = cw.take<int32_t>(kNumQueues * (nk_max + 1));
+
+  void* geo_block = nullptr;
+  void* work_block = nullptr;
+  auto release = [&]() {
+    if (work_block) hipFreeAsync(work_block, s);
+    if (geo_block) hipFreeAsync(geo_block, s);
+    work_block = geo_block = nullptr;
+  };
+  if ((e = hipMallocFromPoolAsync(&geo_block, cg.off, pool, s)) != hipSuccess)
+    return device_status(e, "plan allocation");
+  if ((e = hipMallocFromPoolAsync(&work_block, cw.off, pool, s)) != hipSuccess) {
+    release();
+    return device_status(e, "planner workspace allocation");
+  }
+
+  PlanDev d;
+  std::memset(&d, 0, sizeof(d));
+  d.header = at<int32_t>(geo_block, o_header);
+  d.seqdesc = at<int32_t>(geo_block, o_seqdesc);
+  d.cu_rows = at<int32_t>(geo_block, o_cu_rows);
+  d.cu_q = p.layout == MPB_LAYOUT_THD ? at<int32_t>(geo_block, o_cu_q) : nullptr;
+  d.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(geo_block, o_cu_k) : nullptr;
+  d.work_desc = at<int32_t>(geo_block, o_work_desc);
+  d.section_off = at<int32_t>(geo_block, o_sec);
+  PlanWork w;
+  w.vis_bits = at<uint32_t>(work_block, o_vis);
+  w.full_bits = at<uint32_t>(work_block, o_full);
+  w.pcnt = at<int32_t>(work_block, o_pcnt);
+  w.fcnt = at<int32_t>(work_block, o_fcnt);
+  w.p_off_tmp = at<int32_t>(work_block, o_poff);
+  w.f_off_tmp = at<int32_t>(work_block, o_foff);
+  w.bins = at<int32_t>(work_block, o_bins);
+
+  const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
+  const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
+  if ((e = launch_plan_geometry(g, cq, ck, d, s)) != hipSuccess ||
+      (e = launch_plan_classify(g, mask_func, d, w, s)) != hipSuccess ||
+      (e = launch_plan_scan(g, d, w, s)) != hipSuccess ||
+      (e = hipMemcpyAsync(pinned, d.header, 8 * sizeof(int32_t), hipMemcpyDeviceToHost, s)) !=
+          hipSuccess ||
+      (e = hipEventRecord(ev, s)) != hipSuccess ||
+      (e = launch_plan_schedule(g, d, w, (int32_t)(upper * p.heads_q), s)) != hipSuccess) {
+    release();
+    return device_status(e, "planner launch");
+  }
+  // §4.5: the single header read-back of the build.
+  if ((e = hipEventSynchronize(ev)) != hipSuccess) {
+    release();
+    return device_status(e, "header read-back");
+  }
+  int64_t header[8];
+  for (int i = 0; i < 8; ++i) header[i] = pinned[i];
+  const uint32_t err = (uint32_t)header[7];
+  if (err) {
+    release();
+    if (err & MPB_DEVERR_SEQLENS)
+      return fail(MPB_ERR_SEQLENS,
+                  "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
+                  "respect max_seqlen");
+    if (err & MPB_DEVERR_RANGE)
+      return fail(MPB_ERR_ENDPOINT_RANGE, "an endpoint is < 0 or > its sample's k_len");
+    return fail(MPB_ERR_ENDPOINT_ORDER, "endpoints of some row are not nondecreasing");
+  }
+  const int64_t rows_total = header[0], pnnz = header[1], fnnz = header[2];
+  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0) {
+    release();
+    return fail(MPB_ERR_DEVICE, "inconsistent plan header");
+  }
+
+  // Exact allocation: no capacity padding of the retained CSR (§4.5).
+  const int64_t n_off = p.mask_heads * rows_total + 1;
+  Carver ce;
+  const size_t o_p_off = ce.take<int32_t>(n_off);
+  const size_t o_f_off = ce.take<int32_t>(n_off);
+  const size_t o_p_idx = ce.take<int32_t>(pnnz);
+  const size_t o_f_idx = ce.take<int32_t>(fnnz);
+  const size_t o_masks = ce.take<uint32_t>(pnnz * tq * (tk / 32));
+  void* exact_block = nullptr;
+  if ((e = hipMallocFromPoolAsync(&exact_block, ce.off, pool, s)) != hipSuccess) {
+    release();
+    return device_status(e, "exact plan allocation");
+  }
+  d.p_off = at<int32_t>(exact_block, o_p_off);
+  d.f_off = at<int32_t>(exact_block, o_f_off);
+  d.p_idx = at<int32_t>(exact_block, o_p_idx);
+  d.f_idx = at<int32_t>(exact_block, o_f_idx);
+  d.p_masks = at<uint32_t>(exact_block, o_masks);
+  if ((e = launch_plan_materialize(g, mask_func, d, w, (int32_t)rows_total, s)) != hipSuccess) {
+    hipFreeAsync(exact_block, s);
+    release();
+    return device_status(e, "materialize launch");
+  }
+  hipFreeAsync(work_block, s);
+  work_block = nullptr;
+
+  mpb_plan* plan = new (std::nothrow) mpb_plan;
+  if (!plan) {
+    hipFreeAsync(exact_block, s);
+    release();
+    return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
+  }
+  plan->device = dev;
+  plan->prob = p;
+  plan->prob.tile_q = tq;
+  plan->prob.tile_k = tk;
+  plan->sig = consumer_signature(p, tq, tk);
+  plan->geo = g;
+  plan->dev = d;
+  plan->rows_total = (int32_t)rows_total;
+  plan->num_tasks = (int32_t)(rows_total * p.heads_q);
+  for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
+  plan->geo_block = geo_block;
+  plan->exact_block = exact_block;
+  plan->geo_bytes = cg.off;
+  plan->exact_bytes = ce.off;
+  plan->stream = s;
+  *out = plan;
+  return ok();
+}
+
+mpb_status mask_plan_destroy(mpb_plan* plan) {
+  if (!plan) return ok();
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipFreeAsync(plan->exact_block, plan->stream);
+  hipFreeAsync(plan->geo_block, plan->stream);
+  if (cur != plan->device) hipSetDevice(cur);
+  delete plan;
+  return ok();
+}
+
+mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info) {
+  if (!plan || !info) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or info is NULL");
+  for (int i = 0; i < 8; ++i) info->header[i] = plan->header[i];
+  info->rows_total = plan->rows_total;
+  info->nk_max = plan->geo.nk_max;
+  info->words_per_row = plan->geo.words_tile;
+  info->num_tasks = plan->num_tasks;
+  info->num_sections = kNumQueues;
+  info->device = plan->device;
+  info->problem = plan->prob;
+  info->signature = plan->sig;
+  info->device_bytes = (int64_t)(plan->geo_bytes + plan->exact_bytes);
+  return ok();
+}
+
+mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seqdesc,
+                            int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
+                            int32_t* f_idx, int32_t* work_desc, int32_t* section_off) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipError_t e = hipStreamSynchronize(plan->stream);
+  const int64_t B = plan->prob.batch;
+  const int64_t n_off = (int64_t)plan->prob.mask_heads * plan->rows_total + 1;
+  const int64_t words = plan->header[1] * plan->prob.tile_q * (plan->prob.tile_k / 32);
+  struct Copy { void* dst; const void* src; size_t bytes; } copies[] = {
+      {cu_rows, plan->dev.cu_rows, (size_t)(B + 1) * 4},
+      {seqdesc, plan->dev.seqdesc, (size_t)B * 32},
+      {p_off, plan->dev.p_off, (size_t)n_off * 4},
+      {p_idx, plan->dev.p_idx, (size_t)plan->header[1] * 4},
+      {p_masks, plan->dev.p_masks, (size_t)words * 4},
+      {f_off, plan->dev.f_off, (size_t)n_off * 4},
+      {f_idx, plan->dev.f_idx, (size_t)plan->header[2] * 4},
+      {work_desc, plan->dev.work_desc, (size_t)plan->num_tasks * 16},
+      {section_off, plan->dev.section_off, (size_t)(kNumQueues + 1) * 4},
+  };
+  for (const Copy& c : copies) {
+    if (e != hipSuccess) break;
+    if (c.dst && c.bytes) e = hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyDeviceToHost);
+  }
+  if (cur != plan->device) hipSetDevice(cur);
+  if (e != hipSuccess) return device_status(e, "plan export");
+  return ok();
+}
+
+size_t flex_attn_fwd_workspace_size(const mpb_plan* plan) {
+  (void)plan;
+  return 256;  // kNumQueues + 1 counters, padded
+}
+
+static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                              const void* k, const void* v, void* o, float* lse, float scale,
+                              const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                              void* stream, int32_t force_partial) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan built on device %d used on device %d",
+                plan->device, dev);
+  // §7 / §8: the call's geometry must equal the plan binding field by field.
+  const mpb_problem& a = *problem;
+  const mpb_problem& b = plan->prob;
+#define MPB_CMP(f)                                                                           \
+  if (a.f != b.f)                                                                            \
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "field " #f ": call has %d, plan has %d", a.f, b.f);
+  MPB_CMP(layout) MPB_CMP(dtype) MPB_CMP(batch) MPB_CMP(seqlen_q) MPB_CMP(seqlen_k)
+  MPB_CMP(total_q) MPB_CMP(total_k) MPB_CMP(heads_q) MPB_CMP(heads_k) MPB_CMP(head_dim)
+  MPB_CMP(mask_heads) MPB_CMP(nfunc)
+#undef MPB_CMP
+  if ((a.tile_q && a.tile_q != b.tile_q) || (a.tile_k && a.tile_k != b.tile_k))
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "tile %dx%d requested, plan has %dx%d", a.tile_q,
+                a.tile_k, b.tile_q, b.tile_k);
+  const mpb_signature want = consumer_signature(b, b.tile_q, b.tile_k);
+  if (std::memcmp(&want, &plan->sig, sizeof(want)) != 0 ||
+      !attn_variant_exists(b.dtype, b.head_dim, b.tile_q, b.tile_k))
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan payload/scheduler signature does not match "
+                                            "this forward consumer");
+  if (plan->num_tasks > 0 && (!q || !k || !v || !o || !lse))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
+  if (!workspace || workspace_bytes < flex_attn_fwd_workspace_size(plan))
+    return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed",
+                flex_attn_fwd_workspace_size(plan));
+  if (!std::isfinite(scale)) return fail(MPB_ERR_INVALID_ARGUMENT, "scale is not finite");
+  const bool sc = mod && mod->softcap_enabled;
+  const bool al = mod && mod->alibi_enabled;
+  if (sc && !(std::isfinite(mod->softcap) && mod->softcap > 0.0f))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "softcap must be finite and > 0");
+  if (al && !mod->alibi_slopes) return fail(MPB_ERR_INVALID_ARGUMENT, "alibi_slopes is NULL");
+  int32_t kind = kModNone;
+  if (sc && al) kind = mod->alibi_before_softcap ? kModAlibiSoftcap : kModSoftcapAlibi;
+  else if (sc) kind = kModSoftcap;
+  else if (al) kind = kModAlibi;
+
+  AttnParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.o = o;
+  prm.lse = lse;
+  prm.seqdesc = plan->dev.seqdesc;
+  prm.cu_rows = plan->dev.cu_rows;
+  prm.p_off = plan->dev.p_off;
+  prm.p_idx = plan->dev.p_idx;
+  prm.f_off = plan->dev.f_off;
+  prm.f_idx = plan->dev.f_idx;
+  prm.p_masks = plan->dev.p_masks;
+  prm.work_desc = plan->dev.work_desc;
+  prm.section_off = plan->dev.section_off;
+  prm.counters = static_cast<int32_t*>(workspace);
+  prm.slopes = al ? mod->alibi_slopes : nullptr;
+  prm.heads_q = b.heads_q;
+  prm.heads_k = b.heads_k;
+  prm.group = b.heads_q / b.heads_k;
+  prm.mask_heads = b.mask_heads;
+  prm.rows_total = plan->rows_total;
+  prm.total_q = b.total_q;
+  prm.force_partial = force_partial ? 1 : 0;
+  const float log2e = 1.4426950408889634f;
+  prm.scale_log2 = scale * log2e;
+  prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
+  prm.softcap_c2 = sc ? mod->softcap * log2e : 0.0f;
+  prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
+  if (plan->num_tasks == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = attn_grid_size(b.dtype, b.head_dim, b.tile_q, b.tile_k, plan->num_tasks, dev);
+  if (grid < 1) return fail(MPB_ERR_DEVICE, "could not size the persistent grid");
+  if ((e = launch_reset_counters(prm.counters, s)) != hipSuccess ||
+      (e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, grid, prm, s)) !=
+          hipSuccess)
+    return device_status(e, "attention launch");
+  return ok();
+}
+
+mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                         const void* k, const void* v, void* o, float* lse, float scale,
+                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
+                     stream, 0);
+}
+
+mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
+                                  const void* q, const void* k, const void* v, void* o,
+                                  float* lse, float scale, const mpb_score_mod* mod,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t force_partial) {
+  return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
+                     stream, force_partial);
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+"""Helpers for the GPU tests: move a seeded workload to the device, run the HIP
+path through the C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import mask_planned_block_amd as mpb
+import workloads as W
+
+TOL = {W.DTYPE_FP32: (1e-4, 1e-4), W.DTYPE_BF16: (2e-2, 1e-2)}   # (O, LSE) max-abs
+
+
+def torch_dtype(w):
+    return torch.bfloat16 if w.dtype == W.DTYPE_BF16 else torch.float32
+
+
+def device_inputs(w, device="cuda"):
+    return W.to_device(w, device)
+
+
+def problem(w, tile_q=0, tile_k=0):
+    return mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                            w.total_k, w.heads_q, w.heads_k, w.head_dim, w.mask_heads, w.nfunc,
+                            tile_q, tile_k)
+
+
+def build_plan(w, d, tile_q=0, tile_k=0, stream=None):
+    return mpb.mask_plan_build(problem(w, tile_q, tile_k), d["mask_func"], d["cu_q"], d["cu_k"],
+                               stream=stream)
+
+
+def run_attention(w, d, plan, **kw):
+    o, lse = mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], scale=w.scale,
+                               softcap=w.softcap if w.softcap > 0 else None,
+                               alibi_slopes=d["slopes"],
+                               alibi_before_softcap=w.alibi_before_softcap, **kw)
+    return o, lse
+
+
+def flat_o(w, o):
+    """O as [total_q, Hq, d] float64 numpy."""
+    return o.float().reshape(w.total_q, w.heads_q, w.head_dim).cpu().numpy().astype(np.float64)
+
+
+def compare_plan(gp, op):
+    """Bit-exact comparison of a GPU plan export with the oracle's plan."""
+    assert gp["header"][7] == 0
+    assert list(gp["header"][:3]) == [int(x) for x in op.header[:3]], (gp["header"], op.header)
+    assert all(int(x) == 0 for x in gp["header"][3:7])
+    for key in ("cu_rows", "seqdesc", "p_off", "f_off", "p_idx", "f_idx"):
+        a, b = np.asarray(gp[key]), np.asarray(getattr(op, key))
+        assert a.shape == b.shape and np.array_equal(a, b), key
+    assert gp["p_masks"].shape == op.p_masks.shape
+    assert np.array_equal(gp["p_masks"], op.p_masks), "payload words differ"
+
+
+def check_schedule(w, gp, tile_q, num_sections=8):
+    """The forward schedule is a permutation of all (row, head) tasks with the
+    right q_valid_rows; positive-cost tasks sit in their (batch, kv-head)
+    section in descending cost with canonical ties; zero-cost tasks last."""
+    wd, so = gp["work_desc"], gp["section_off"]
+    cu_rows, sd = gp["cu_rows"], gp["seqdesc"]
+    rows_total = int(cu_rows[-1])
+    n = rows_total * w.heads_q
+    assert wd.shape == (n, 4) and so[0] == 0 and so[-1] == n
+    assert np.all(np.diff(so) >= 0)
+    p_off, f_off = gp["p_off"], gp["f_off"]
+    group = w.heads_q // w.heads_k
+
+    def cost(b, h, i):
+        hm = 0 if w.mask_heads == 1 else h
+        flat = hm * rows_total + int(cu_rows[b]) + i
+        return int(p_off[flat + 1] - p_off[flat] + f_off[flat + 1] - f_off[flat])
+
+    seen = set()
+    for s in range(num_sections + 1):
+        prev = None
+        for t in range(so[s], so[s + 1]):
+            i, h, b, qv = (int(x) for x in wd[t])
+            assert (b, h, i) not in seen
+            seen.add((b, h, i))
+            q_len = int(sd[b][2])
+            assert qv == min(tile_q, q_len - i * tile_q)
+            c = cost(b, h, i)
+            if s < num_sections:
+                assert c > 0 and (b * w.heads_k + h // group) % num_sections == s
+                key = (-c, b, h, i)
+            else:
+                assert c == 0
+                key = (b, h, i)
+            assert prev is None or key > prev, (s, prev, key)
+            prev = key
+    assert len(seen) == n
+
+
+def compare_attention(w, o_ref, lse_ref, o_gpu, lse_gpu, what=""):
+    """Max-abs comparison at the stated tolerance; empty rows must be exactly
+    O = 0 and LSE = -inf on both sides."""
+    tol_o, tol_l = TOL[w.dtype]
+    empty = ~np.isfinite(lse_ref)
+    assert np.array_equal(~np.isfinite(lse_gpu), empty), what + " non-finite LSE pattern differs"
+    assert np.all(lse_gpu[empty] == -np.inf)
+    if empty.any():
+        # LSE is [Hq, T] (or [n]); O is [T, Hq, d] (or [n, d])
+        empty_o = empty.T if empty.ndim == 2 else empty
+        assert np.all(o_gpu[empty_o] == 0.0), what + " empty rows must be O = 0"
+    fin = ~empty
+    assert not np.isnan(o_gpu).any(), what + " NaN in O"
+    do = float(np.max(np.abs(o_gpu - o_ref))) if o_ref.size else 0.0
+    dl = float(np.max(np.abs(lse_gpu[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    assert do <= tol_o, "%s max|dO| = %.3g > %.3g" % (what, do, tol_o)
+    assert dl <= tol_l, "%s max|dLSE| = %.3g > %.3g" % (what, dl, tol_l)
+    return do, dl
+
+
+def sample_rows(w, n_random=1500, seed=0, tile_q=128):
+    """(token, head) pairs: random ones plus the edges of every sample and of
+    Q tiles (first/last rows, rows on both sides of a tile boundary)."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for _ in range(n_random):
+        rows.add((int(rng.integers(0, w.total_q)), int(rng.integers(0, w.heads_q))))
+    heads = sorted({0, w.heads_q - 1, w.heads_q // 2})
+    for b in range(w.batch):
+        qo, ql, _, _ = w.sample_bounds(b)
+        cand = [0, 1, ql - 1, ql - 2, tile_q - 1, tile_q, ql // 2]
+        for q in cand:
+            if 0 <= q < ql:
+                for h in heads:
+                    rows.add((qo + q, h))
+    return np.asarray(sorted(rows), dtype=np.int64)

@@ -1,0 +1,118 @@
+"""C-ABI checks that need no GPU.
+
+The library must load and export every function include/mpb.h declares, and
+every host-decidable refusal must happen before any device call (so these run
+on a machine without a GPU).  Loaded with ctypes directly; no compute call is
+made.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpb.h")
+LIB = os.path.join(ROOT, "mask_planned_block_amd", "libmpb.so")
+
+
+def _ensure_built():
+    if not os.path.exists(LIB):
+        subprocess.check_call(["python", os.path.join(ROOT, "mask_planned_block_amd", "build.py")])
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("__")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ("mask_plan_build", "flex_attn_fwd", "mask_plan_destroy", "mask_plan_info",
+                 "mask_plan_export", "flex_attn_fwd_workspace_size", "mpb_status_string",
+                 "mpb_last_error_detail"):
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "layout", "dtype", "batch", "seqlen_q", "seqlen_k", "total_q", "total_k", "heads_q",
+        "heads_k", "head_dim", "mask_heads", "nfunc", "tile_q", "tile_k")]
+
+
+def _good(**kw):
+    base = dict(layout=0, dtype=0, batch=2, seqlen_q=256, seqlen_k=256, total_q=512, total_k=512,
+                heads_q=4, heads_k=4, head_dim=128, mask_heads=1, nfunc=1, tile_q=0, tile_k=0)
+    base.update(kw)
+    return Problem(**base)
+
+
+def _build(lib, prob, mask_ptr=1, cu_q=None, cu_k=None):
+    lib.mask_plan_build.restype = ctypes.c_int
+    lib.mask_plan_build.argtypes = [ctypes.POINTER(Problem)] + [ctypes.c_void_p] * 4 + \
+        [ctypes.POINTER(ctypes.c_void_p)]
+    out = ctypes.c_void_p(12345)
+    st = lib.mask_plan_build(ctypes.byref(prob) if prob is not None else None,
+                             ctypes.c_void_p(mask_ptr) if mask_ptr else None,
+                             ctypes.c_void_p(cu_q) if cu_q else None,
+                             ctypes.c_void_p(cu_k) if cu_k else None, None, ctypes.byref(out))
+    return st, out.value
+
+
+INVALID, UNSUPPORTED = 1, 7
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(layout=2), INVALID), (dict(dtype=5), INVALID), (dict(batch=0), INVALID),
+    (dict(total_q=511), INVALID), (dict(total_k=100), INVALID), (dict(heads_q=0), INVALID),
+    (dict(heads_q=6, heads_k=4), INVALID), (dict(mask_heads=2), INVALID),
+    (dict(nfunc=2), INVALID), (dict(nfunc=0), INVALID), (dict(nfunc=4097), UNSUPPORTED),
+    (dict(head_dim=96), UNSUPPORTED), (dict(tile_q=48), UNSUPPORTED),
+    (dict(tile_k=48), UNSUPPORTED), (dict(tile_q=256, tile_k=256), UNSUPPORTED),
+    (dict(seqlen_q=-1), INVALID),
+])
+def test_host_refusals_before_any_launch(lib, kw, status):
+    st, out = _build(lib, _good(**kw))
+    assert st == status
+    assert out is None  # *out is NULL on failure
+    lib.mpb_last_error_detail.restype = ctypes.c_char_p
+    assert lib.mpb_last_error_detail()  # names the violated rule
+
+
+def test_null_arguments(lib):
+    st, out = _build(lib, None)
+    assert st == INVALID and out is None
+    st, out = _build(lib, _good(), mask_ptr=0)
+    assert st == INVALID
+    st, out = _build(lib, _good(layout=1, total_q=300, total_k=300))  # THD without prefixes
+    assert st == INVALID
+
+
+def test_fwd_refuses_null_plan_and_workspace_size(lib):
+    lib.flex_attn_fwd.restype = ctypes.c_int
+    lib.flex_attn_fwd.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_float] + \
+        [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    st = lib.flex_attn_fwd(None, None, None, None, None, None, None, 1.0, None, None, 0, None)
+    assert st == INVALID
+    lib.mpb_status_string.restype = ctypes.c_char_p
+    assert lib.mpb_status_string(5) == b"MPB_ERR_SIGNATURE_MISMATCH"
+    lib.mask_plan_destroy.restype = ctypes.c_int
+    assert lib.mask_plan_destroy(None) == 0

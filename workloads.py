@@ -312,3 +312,30 @@ def custom(mask_func, layout=LAYOUT_BSHD, batch=1, seqlen_q=None, seqlen_k=None,
                     heads_k, head_dim, mf.shape[0], mf.shape[1], mf, cq, ck, q, k, v,
                     scale if scale is not None else 1.0 / math.sqrt(head_dim), softcap=softcap,
                     alibi_slopes=slopes, alibi_before_softcap=alibi_before_softcap, seed=seed)
+
+
+def to_device(w: Workload, device="cuda") -> dict:
+    """Copy a workload's input arrays into torch device tensors (exact: bf16
+    values are bf16-representable).  BSHD tensors are [B, S, H, d], THD
+    [T, H, d]."""
+    import torch
+
+    dt = torch.bfloat16 if w.dtype == DTYPE_BF16 else torch.float32
+
+    def qkv(x, total):
+        t = torch.from_numpy(x).to(dt)
+        if w.layout == LAYOUT_BSHD:
+            t = t.reshape(w.batch, total // w.batch, x.shape[1], x.shape[2])
+        return t.contiguous().to(device)
+
+    d = {
+        "mask_func": torch.from_numpy(np.ascontiguousarray(w.mask_func)).to(device),
+        "cu_q": None if w.cu_seqlens_q is None else torch.from_numpy(w.cu_seqlens_q).to(device),
+        "cu_k": None if w.cu_seqlens_k is None else torch.from_numpy(w.cu_seqlens_k).to(device),
+        "slopes": None if w.alibi_slopes is None else torch.from_numpy(w.alibi_slopes).to(device),
+    }
+    if w.q is not None:
+        d["q"] = qkv(w.q, w.total_q)
+        d["k"] = qkv(w.k, w.total_k)
+        d["v"] = qkv(w.v, w.total_k)
+    return d
