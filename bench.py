@@ -102,7 +102,7 @@ def main():
     stream = torch.cuda.current_stream()
     out = torch.empty_like(d["q"])
     lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    ws = None
     kw = dict(scale=w.scale, softcap=w.softcap if w.softcap > 0 else None,
               alibi_slopes=d["slopes"], alibi_before_softcap=w.alibi_before_softcap,
               out=out, lse=lse, workspace=ws, stream=stream)

@@ -90,7 +90,7 @@ typedef struct mpb_signature {
   int32_t kernel_family;   /* 1 = bf16 MFMA 32x32x16, 2 = fp32 MFMA 32x32x2 */
   int32_t tile_q, tile_k, head_dim, dtype;
   int32_t payload_layout;  /* 1 = row-major, 32-column uint32 words (see below) */
-  int32_t scheduler;       /* 1 = per-section work queues, atomic counters in workspace */
+  int32_t scheduler;       /* 2 = one workgroup per task, section-interleaved launch order */
 } mpb_signature;
 
 typedef struct mpb_plan_info {
@@ -99,7 +99,7 @@ typedef struct mpb_plan_info {
   int32_t nk_max;          /* K tiles of the longest sample */
   int32_t words_per_row;   /* tile_k / 32 */
   int32_t num_tasks;       /* rows_total * heads_q */
-  int32_t num_sections;    /* schedule sections (work queues) */
+  int32_t num_sections;    /* schedule sections (8 XCD sections + the zero-cost tail) */
   int32_t device;
   mpb_problem problem;
   mpb_signature signature;
@@ -172,8 +172,20 @@ mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seq
                             int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
                             int32_t* f_idx, int32_t* work_desc, int32_t* section_off);
 
-/* Bytes of caller-provided device workspace flex_attn_fwd needs (the work
- * queue counters [MPD §4.8]).  One workspace per concurrently running call. */
+/* Launch order of the forward tasks: records [num_tasks][16] int32, record i
+ * run by workgroup i: {m_block, head, batch, q_valid_rows, q_offset, k_offset,
+ * q_len, k_len, partial_begin, partial_count, full_begin, full_count,
+ * first_k_tile (-1 if none), mask_head, kv_head, section}.  The order
+ * interleaves the schedule's sections (one per XCD): while every section has
+ * tasks left, slot 8r+x holds the r-th task of section x [MPD §4.8, read for
+ * MI355X's round-robin workgroup-to-XCD dispatch].  Synchronises the plan's
+ * build stream. */
+mpb_status mask_plan_export_launch_order(const mpb_plan* plan, int32_t* records);
+
+/* Bytes of caller-provided device workspace flex_attn_fwd needs.  The
+ * forward launches one workgroup per task in the plan's launch order, so no
+ * scheduler state is needed and this returns 0; the argument is kept for
+ * consumers that need call-local state [MPD §4.8]. */
 size_t flex_attn_fwd_workspace_size(const mpb_plan* plan);
 
 /* flex_attn_fwd [MPD §6.1; FLEX Eq. 1]: block-sparse attention forward.
@@ -185,10 +197,11 @@ size_t flex_attn_fwd_workspace_size(const mpb_plan* plan);
  *   lse       device float32 [heads_q][total_q], natural log of the sum of
  *             exp(score) over visible keys (scores after score_mod).  A row
  *             with nothing visible gets O = 0 and LSE = -inf [MPD §6.1].
- *   scale     multiplies q.k before score_mod (usually 1/sqrt(head_dim)).
+ *   scale     multiplies q.k before score_mod; finite and > 0 (usually
+ *             1/sqrt(head_dim)), else MPB_ERR_INVALID_ARGUMENT.
  *   mod       NULL for no score_mod.
- *   workspace device, >= flex_attn_fwd_workspace_size(plan) bytes, any
- *             contents; reset by the call.
+ *   workspace device, >= flex_attn_fwd_workspace_size(plan) bytes (may be
+ *             NULL when that is 0).
  * Partial tiles apply their predicate; full tiles skip it; empty tiles are
  * never touched.  Enqueue only; no synchronisation.  Every refusal happens
  * before the launch [PYG "Accept means run"]. */

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "MPBError", "Problem", "MaskPlan",
     "make_problem", "mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
-    "flex_attn_fwd", "flex_attn_fwd_workspace_size", "library_path",
+    "flex_attn_fwd", "flex_attn_fwd_workspace_size", "library_path", "TASK_REC_FIELDS",
 ]
 
 LAYOUT_BSHD = 0
@@ -28,6 +28,10 @@ LAYOUT_THD = 1
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
 NUM_QUEUES = 9
+TASK_REC_INTS = 16
+TASK_REC_FIELDS = ("m_block", "head", "batch", "q_valid_rows", "q_offset", "k_offset", "q_len",
+                   "k_len", "partial_begin", "partial_count", "full_begin", "full_count",
+                   "first_k_tile", "mask_head", "kv_head", "section")
 
 STATUS = {0: "MPB_OK", 1: "MPB_ERR_INVALID_ARGUMENT", 2: "MPB_ERR_ENDPOINT_RANGE",
           3: "MPB_ERR_ENDPOINT_ORDER", 4: "MPB_ERR_SEQLENS", 5: "MPB_ERR_SIGNATURE_MISMATCH",
@@ -84,6 +88,7 @@ def _load():
     lib.mask_plan_destroy.argtypes = [vp]
     lib.mask_plan_info.argtypes = [vp, P(PlanInfo)]
     lib.mask_plan_export.argtypes = [vp] + [vp] * 9
+    lib.mask_plan_export_launch_order.argtypes = [vp, vp]
     lib.flex_attn_fwd_workspace_size.argtypes = [vp]
     lib.flex_attn_fwd_workspace_size.restype = ctypes.c_size_t
     fwd_args = [vp, P(Problem), vp, vp, vp, vp, vp, ctypes.c_float, P(ScoreMod), vp,
@@ -95,7 +100,7 @@ def _load():
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
     lib.mpb_version.restype = ctypes.c_int32
     for name in ("mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
-                 "flex_attn_fwd", "flex_attn_fwd_ablation"):
+                 "mask_plan_export_launch_order", "flex_attn_fwd", "flex_attn_fwd_ablation"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -216,6 +221,9 @@ def mask_plan_export(plan: MaskPlan) -> dict:
     a["p_masks"] = a["p_masks"][:pnnz * p.tile_q * W].reshape(pnnz, p.tile_q, W)
     a["work_desc"] = a["work_desc"][:info.num_tasks]
     a["header"] = np.asarray(list(info.header), np.int64)
+    rec = np.zeros((max(info.num_tasks, 1), TASK_REC_INTS), np.int32)
+    _check(_lib.mask_plan_export_launch_order(plan.handle, ctypes.c_void_p(rec.ctypes.data)))
+    a["launch"] = rec[:info.num_tasks]
     return a
 
 
@@ -261,7 +269,7 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     if lse is None:
         lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
     need = flex_attn_fwd_workspace_size(plan)
-    if workspace is None:
+    if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     mod = None
     if softcap or alibi_slopes is not None:
@@ -273,7 +281,8 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     args = (plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
             _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
             ctypes.byref(mod) if mod is not None else None, _dev_ptr(workspace, "workspace"),
-            workspace.numel() * workspace.element_size(), ctypes.c_void_p(_stream_handle(stream)))
+            0 if workspace is None else workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(_stream_handle(stream)))
     if force_partial:
         _check(_lib.flex_attn_fwd_ablation(*args, 1))
     else:

@@ -6,9 +6,12 @@
 // tiles are never touched; a row with nothing visible gets O = 0, LSE = -inf.
 //
 // Design (gfx950 native, not a port of any CUDA kernel):
-//  * One workgroup = NW wavefronts = one Q tile of 32*NW rows; a persistent
-//    grid pulls tasks from per-section work queues (one per XCD) through
-//    atomic counters held in caller workspace (§4.8 dynamic scheduler).
+//  * One workgroup = NW wavefronts = one Q tile of 32*NW rows = one task of
+//    the plan's launch order (§4.8): workgroup i reads record i, which holds
+//    the task's geometry, CSR ranges and first K tile, so its Q and first K/V
+//    loads issue after one record read.  Sections are interleaved in the
+//    launch order because workgroups reach the XCDs round-robin; the hardware
+//    dispatcher balances the load (cost-descending order within a section).
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: in the 32x32 accumulator a lane holds one Q
 //    column (q = lane%32) and 16 K rows {8a + 4*(lane/32) + c}.  So the
@@ -17,10 +20,16 @@
 //    feeds the P.V MFMA straight from registers: O^T = V^T P^T, where the V
 //    operand is read from an LDS copy of V stored transposed with its K order
 //    permuted (bits 2 and 3 swapped) so each lane reads 8 contiguous values.
+//  * Q, K, V and O are addressed through buffer resources bounded by the
+//    task's sample: loads past k_len/q_len return zero and stores past q_len
+//    are dropped by the hardware range check, so the tail protection of the
+//    plan design (§4.3, §4.8) costs no branch; offsets are 32-bit.
 //  * K and V^T tiles are staged in LDS (double buffered, padded rows) from
 //    coalesced 16-byte HBM loads issued one tile ahead.
-//  * Online softmax in base 2 (scale*log2e folded into one multiply), fp32
-//    statistics, P rounded to bf16 for the second MFMA.
+//  * Online softmax in base 2 with lazy rescaling: the running max used for
+//    the exponent only moves when a row's max grows by more than 2^8, and the
+//    O rescale is skipped by the whole wavefront when no lane moved.
+//    Statistics in fp32, P rounded to bf16 for the second MFMA.
 //  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout
 //    and keep P in fp32.
 #include "mpb_internal.h"
@@ -35,13 +44,26 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Lazy rescale threshold in log2 units: P values stay <= 2^8.
+constexpr float kRescaleSlack = 8.0f;
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Raw (stride 0) buffer descriptor over [base, base + bytes); gfx9 word 3.
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
 
 // Position of K index k inside a permuted V^T row: bits 2 and 3 swapped.
 __device__ constexpr int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
@@ -53,6 +75,7 @@ struct Bf16Ops {
   using T = __bf16;
   static constexpr int D = D_, NW = NW_, TKV = TKV_;
   static constexpr int NT = NW * 64, TQ = 32 * NW, NKB = TKV / 32;
+  static constexpr int ESZ = 2;
   static constexpr int KP = D + 8;    // K row pitch (elements): 16 B pad, conflict-free b128 reads
   static constexpr int VP = TKV + 8;  // V^T row pitch (elements)
   static constexpr int KCH = TKV * D / 8 / NT;          // 16-byte K chunks per thread
@@ -69,24 +92,22 @@ struct Bf16Ops {
   struct Stage { u32x4 k[KCH]; u32x4 v0[VCH]; u32x4 v1[VCH]; };
   struct PFrag { bf16x8 p[NKB][2]; };
 
-  // Tile rows >= rows_valid (past the sample's k_len) are zero-filled, so
-  // no stale or foreign value can reach P.V.
-  static __device__ inline void load(Stage& st, const __bf16* kg, const __bf16* vg, int64_t rs,
-                                     int rows_valid, int tid) {
+  // tile_off = byte offset of the tile's first row; rs = bytes per token row.
+  static __device__ inline void load(Stage& st, rsrc_t rk, rsrc_t rv, uint32_t tile_off,
+                                     uint32_t rs, int tid) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
       const int r = idx / (D / 8), c8 = idx % (D / 8);
-      st.k[c] = r < rows_valid ? *(const u32x4*)(kg + r * rs + c8 * 8) : u32x4{0, 0, 0, 0};
+      st.k[c] = bload16(rk, tile_off + r * rs + c8 * 16);
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = tid + c * NT;
       const int pr = idx % (TKV / 2), c8 = idx / (TKV / 2);
-      const int r0 = 2 * pr;
-      st.v0[c] = r0 < rows_valid ? *(const u32x4*)(vg + r0 * rs + c8 * 8) : u32x4{0, 0, 0, 0};
-      st.v1[c] = r0 + 1 < rows_valid ? *(const u32x4*)(vg + (r0 + 1) * rs + c8 * 8)
-                                     : u32x4{0, 0, 0, 0};
+      const uint32_t off = tile_off + (2 * pr) * rs + c8 * 16;
+      st.v0[c] = bload16(rv, off);
+      st.v1[c] = bload16(rv, off + rs);
     }
   }
 
@@ -106,22 +127,16 @@ struct Bf16Ops {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         const uint32_t a = st.v0[c][w], b = st.v1[c][w];
-        *(uint32_t*)(dst + (2 * w) * VP) = (a & 0xFFFFu) | (b << 16);
-        *(uint32_t*)(dst + (2 * w + 1) * VP) = (a >> 16) | (b & 0xFFFF0000u);
+        *(uint32_t*)(dst + (2 * w) * VP) = __builtin_amdgcn_perm(b, a, 0x05040100u);
+        *(uint32_t*)(dst + (2 * w + 1) * VP) = __builtin_amdgcn_perm(b, a, 0x07060302u);
       }
     }
   }
 
-  static __device__ inline void load_q(QFrag& qf, const __bf16* qrow, int b2) {
+  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, uint32_t row_off, int b2) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      if (qrow) {
-        qf.q[s] = *(const bf16x8*)(qrow + 16 * s + 8 * b2);
-      } else {
-        u32x4 z = {0, 0, 0, 0};
-        qf.q[s] = __builtin_bit_cast(bf16x8, z);
-      }
-    }
+    for (int s = 0; s < D / 16; ++s)
+      qf.q[s] = __builtin_bit_cast(bf16x8, bload16(rq, row_off + (16 * s + 8 * b2) * ESZ));
   }
 
   static __device__ inline void qk(f32x16 (&acc)[NKB], const QFrag& qf, const Smem& sm, int stage,
@@ -148,6 +163,24 @@ struct Bf16Ops {
         for (int e = 0; e < 8; ++e) pf.p[kk][m][e] = (__bf16)acc[kk][8 * m + e];
   }
 
+  // Sum of the bf16-rounded weights (the values P.V uses), two per
+  // v_dot2_f32_bf16 against (1, 1).
+  static __device__ inline float row_sum(const PFrag& pf, const f32x16 (&)[NKB]) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    float s = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pr = {pf.p[kk][m][e], pf.p[kk][m][e + 1]};
+          s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
+        }
+    return s;
+  }
+
   static __device__ inline void pv(f32x16 (&o)[D / 32], const PFrag& pf, const Smem& sm,
                                    int stage, int lane) {
     const __bf16* vb = &sm.vt[stage][(lane & 31) * VP + 8 * (lane >> 5)];
@@ -162,8 +195,8 @@ struct Bf16Ops {
         }
   }
 
-  static __device__ inline void store_o(__bf16* orow, const f32x16 (&o)[D / 32], float inv,
-                                        int b2) {
+  static __device__ inline void store_o(rsrc_t ro, uint32_t row_off, const f32x16 (&o)[D / 32],
+                                        float inv, int b2) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -171,7 +204,9 @@ struct Bf16Ops {
         bf16x4 v;
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = (__bf16)(o[db][4 * a + c] * inv);
-        *(bf16x4*)(orow + db * 32 + 8 * a + 4 * b2) = v;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro,
+                                              (int)(row_off + (db * 32 + 8 * a + 4 * b2) * ESZ),
+                                              0, 0);
       }
   }
 };
@@ -183,10 +218,10 @@ struct F32Ops {
   using T = float;
   static constexpr int D = D_, NW = NW_, TKV = TKV_;
   static constexpr int NT = NW * 64, TQ = 32 * NW, NKB = TKV / 32;
+  static constexpr int ESZ = 4;
   static constexpr int KP = D + 4;   // 16-byte reads of 32 rows: banks 4r, conflict-free
   static constexpr int VP = D + 8;   // lanes 32..63 read row k+4: +32 banks
   static constexpr int KCH = TKV * D / 4 / NT;
-  static constexpr int VCH = TKV * D / 4 / NT;
   static_assert(KCH * NT * 4 == TKV * D, "tile must split evenly over threads");
 
   struct Smem {
@@ -194,17 +229,17 @@ struct F32Ops {
     float v[2][TKV * VP];
   };
   struct QFrag { float q[D / 2]; };
-  struct Stage { f32x4 k[KCH]; f32x4 v[VCH]; };
+  struct Stage { u32x4 k[KCH]; u32x4 v[KCH]; };
   struct PFrag { f32x16 p[NKB]; };
 
-  static __device__ inline void load(Stage& st, const float* kg, const float* vg, int64_t rs,
-                                     int rows_valid, int tid) {
+  static __device__ inline void load(Stage& st, rsrc_t rk, rsrc_t rv, uint32_t tile_off,
+                                     uint32_t rs, int tid) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
       const int r = idx / (D / 4), c4 = idx % (D / 4);
-      st.k[c] = r < rows_valid ? *(const f32x4*)(kg + r * rs + c4 * 4) : f32x4{};
-      st.v[c] = r < rows_valid ? *(const f32x4*)(vg + r * rs + c4 * 4) : f32x4{};
+      st.k[c] = bload16(rk, tile_off + r * rs + c4 * 16);
+      st.v[c] = bload16(rv, tile_off + r * rs + c4 * 16);
     }
   }
 
@@ -213,15 +248,15 @@ struct F32Ops {
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
       const int r = idx / (D / 4), c4 = idx % (D / 4);
-      *(f32x4*)&sm.k[stage][r * KP + c4 * 4] = st.k[c];
-      *(f32x4*)&sm.v[stage][r * VP + c4 * 4] = st.v[c];
+      *(u32x4*)&sm.k[stage][r * KP + c4 * 4] = st.k[c];
+      *(u32x4*)&sm.v[stage][r * VP + c4 * 4] = st.v[c];
     }
   }
 
-  static __device__ inline void load_q(QFrag& qf, const float* qrow, int b2) {
+  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, uint32_t row_off, int b2) {
 #pragma unroll
     for (int s = 0; s < D / 2; s += 4) {
-      const f32x4 x = qrow ? *(const f32x4*)(qrow + b2 * (D / 2) + s) : f32x4{};
+      const f32x4 x = __builtin_bit_cast(f32x4, bload16(rq, row_off + (b2 * (D / 2) + s) * ESZ));
 #pragma unroll
       for (int e = 0; e < 4; ++e) qf.q[s + e] = x[e];
     }
@@ -249,6 +284,15 @@ struct F32Ops {
     for (int kk = 0; kk < NKB; ++kk) pf.p[kk] = acc[kk];
   }
 
+  static __device__ inline float row_sum(const PFrag&, const f32x16 (&acc)[NKB]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[kk][v];
+    return s;
+  }
+
   static __device__ inline void pv(f32x16 (&o)[D / 32], const PFrag& pf, const Smem& sm,
                                    int stage, int lane) {
     const int b2 = lane >> 5;
@@ -264,7 +308,8 @@ struct F32Ops {
         }
   }
 
-  static __device__ inline void store_o(float* orow, const f32x16 (&o)[D / 32], float inv, int b2) {
+  static __device__ inline void store_o(rsrc_t ro, uint32_t row_off, const f32x16 (&o)[D / 32],
+                                        float inv, int b2) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -272,36 +317,39 @@ struct F32Ops {
         f32x4 v;
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[c] = o[db][4 * a + c] * inv;
-        *(f32x4*)(orow + db * 32 + 8 * a + 4 * b2) = v;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                               (int)(row_off + (db * 32 + 8 * a + 4 * b2) * ESZ),
+                                               0, 0);
       }
   }
 };
 
-// ----------------------------------------------------------------- scheduling
+// ----------------------------------------------------------------- helpers
 
-__device__ inline int fetch_task(const AttnParams& p, int home, int& qpos) {
-  // Home section first, then the others in rotation, then the zero-cost
-  // queue.  Every counter only grows, so each workgroup leaves after at most
-  // (tasks it ran + kNumQueues) atomics.
-  while (qpos < kNumQueues) {
-    const int q = qpos < kNumSections ? (home + qpos) % kNumSections : kNumSections;
-    const int beg = p.section_off[q];
-    const int size = p.section_off[q + 1] - beg;
-    if (size > 0) {
-      const int idx = atomicAdd(&p.counters[q], 1);
-      if (idx < size) return beg + idx;
-    }
-    ++qpos;
-  }
-  return -1;
+// Reduction over the two lanes that own one Q row (lane and lane ^ 32):
+// v_permlane32_swap exchanges the wavefront halves in one VALU op.
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Packed predicate select (§5.1): bit `pos` of the lane's word keeps the
+// score, a 0 bit turns it into -inf.  sbfe yields 0 or all-ones.
+__device__ inline float keep_or_neginf(float u, uint32_t word, int pos) {
+  const uint32_t m = (uint32_t)__builtin_amdgcn_sbfe((int)word, pos, 1);
+  return __uint_as_float((__float_as_uint(u) & m) | (~m & 0xFF800000u));
 }
 
 // score_mod in log2 units: returns log2(e) * mod(s * scale).  kq = k - q.
 template <int MOD>
 __device__ inline float mod_score(float s, float kq, const AttnParams& p, float slope) {
-  if constexpr (MOD == kModNone) {
-    return s * p.scale_log2;
-  } else if constexpr (MOD == kModAlibi) {
+  if constexpr (MOD == kModAlibi) {
     return fmaf(s, p.scale_log2, slope * kq);            // slope = slope_h * log2e
   } else if constexpr (MOD == kModSoftcap || MOD == kModSoftcapAlibi) {
     // c*tanh(x) = c - 2c / (1 + e^{2x}),  e^{2x} = exp2(s * 2*scale*log2e/c)
@@ -315,169 +363,211 @@ __device__ inline float mod_score(float s, float kq, const AttnParams& p, float 
   }
 }
 
+// Running softmax state of one lane (one Q row, shared with lane ^ 32).
+struct RowState {
+  float m;   // reference max (log2 units) used by the exponents so far
+  float l;   // this lane's partial sum of the weights
+};
+
+// One K tile: scores on MFMA, score_mod and (MASKED) the predicate, online
+// softmax, P.V on MFMA.
+template <class Ops, int MOD, bool MASKED>
+__device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
+                                 const typename Ops::Smem& sm, int stage, int lane,
+                                 const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
+                                 f32x16 (&o)[Ops::D / 32], RowState& rs) {
+  constexpr int NKB = Ops::NKB, D = Ops::D;
+  f32x16 acc[NKB];
+  Ops::qk(acc, qf, sm, stage, lane);
+  // Without a score_mod the max is taken on the raw dot products (scale > 0)
+  // and scaled once; the exponent is then one FMA per element.
+  float mt = kNegInf;
+  if constexpr (MOD == kModNone) {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if constexpr (MASKED) acc[kk][v] = keep_or_neginf(acc[kk][v], mw[kk], 8 * (v / 4) + v % 4);
+        mt = fmaxf(mt, acc[kk][v]);
+      }
+    mt = pair_max(mt) * p.scale_log2;
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float kq = kq0 + (float)(kk * 32 + 8 * (v / 4) + (v % 4));
+        float u = mod_score<MOD>(acc[kk][v], kq, p, slope);
+        if constexpr (MASKED) u = keep_or_neginf(u, mw[kk], 8 * (v / 4) + v % 4);
+        acc[kk][v] = u;
+        mt = fmaxf(mt, u);
+      }
+    mt = pair_max(mt);
+  }
+  // Lazy rescale: the reference max only moves when the row max grows by more
+  // than kRescaleSlack, and the wavefront skips the O rescale if no lane
+  // moved.  Both lanes of a row see the same mt, so they stay in step.
+  const bool bump = mt > rs.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(bump)) {
+    const float alpha = bump ? exp2_fast(rs.m - mt) : 1.0f;
+    rs.m = bump ? mt : rs.m;
+    rs.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+  const float m_use = rs.m == kNegInf ? 0.0f : rs.m;
+  if constexpr (MOD == kModNone) {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kk][v] = exp2_fast(fmaf(acc[kk][v], p.scale_log2, -m_use));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kk][v] = exp2_fast(acc[kk][v] - m_use);
+  }
+  typename Ops::PFrag pf;
+  Ops::to_p(pf, acc);
+  rs.l += Ops::row_sum(pf, acc);
+  Ops::pv(o, pf, sm, stage, lane);
+}
+
+// One workgroup per task, in the plan's launch order (record blockIdx.x).
 template <class Ops, int MOD>
-__global__ __launch_bounds__(Ops::NT) void attn_fwd_kernel(AttnParams p) {
-  using T = typename Ops::T;
-  constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB;
+__global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(AttnParams p) {
+  constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
   __shared__ typename Ops::Smem sm;
-  __shared__ int s_task;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int b2 = lane >> 5;
   const int lq = lane & 31;
-  const int home = blockIdx.x % kNumSections;
-  int qpos = 0;
 
-  const T* __restrict__ Qg = (const T*)p.q;
-  const T* __restrict__ Kg = (const T*)p.k;
-  const T* __restrict__ Vg = (const T*)p.v;
-  T* __restrict__ Og = (T*)p.o;
-  const int64_t q_rs = (int64_t)p.heads_q * D;
-  const int64_t kv_rs = (int64_t)p.heads_k * D;
+  const int32_t* rec = p.task_rec + (int64_t)blockIdx.x * kTaskRecInts;
+  const int m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);
+  const int h = __builtin_amdgcn_readfirstlane(rec[kRecHead]);
+  const int q_off = __builtin_amdgcn_readfirstlane(rec[kRecQOff]);
+  const int k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
+  const int q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
+  const int k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
+  const int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
+  const int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
+  const int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
+  const int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
+  const int j_first = __builtin_amdgcn_readfirstlane(rec[kRecFirstTile]);
+  const int g = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
 
-  while (true) {
-    if (tid == 0) s_task = fetch_task(p, home, qpos);
-    __syncthreads();
-    const int task = s_task;
-    __syncthreads();
-    if (task < 0) break;
+  const uint32_t q_rs = (uint32_t)p.heads_q * D * ESZ;   // bytes per Q/O token row
+  const uint32_t kv_rs = (uint32_t)p.heads_k * D * ESZ;  // bytes per K/V token row
+  // Sample-bounded views: [q_off, q_off+q_len) rows of head h in Q and O,
+  // [k_off, k_off+k_len) rows of K/V head g.
+  const char* qbase = (const char*)p.q + (int64_t)q_off * q_rs + (int64_t)h * D * ESZ;
+  char* obase = (char*)p.o + (int64_t)q_off * q_rs + (int64_t)h * D * ESZ;
+  const char* kbase = (const char*)p.k + (int64_t)k_off * kv_rs + (int64_t)g * D * ESZ;
+  const char* vbase = (const char*)p.v + (int64_t)k_off * kv_rs + (int64_t)g * D * ESZ;
+  const rsrc_t rq = make_rsrc(qbase, (uint32_t)q_len * q_rs);
+  const rsrc_t ro = make_rsrc(obase, (uint32_t)q_len * q_rs);
+  const rsrc_t rk = make_rsrc(kbase, (uint32_t)k_len * kv_rs);
+  const rsrc_t rv = make_rsrc(vbase, (uint32_t)k_len * kv_rs);
 
-    const int32_t* wd = p.work_desc + 4 * (int64_t)task;
-    const int m_block = wd[0], h = wd[1], b = wd[2];
-    const int32_t* sd = p.seqdesc + 8 * b;
-    const int q_off = sd[0], k_off = sd[1], q_len = sd[2], k_len = sd[3];
-    const int g = h / p.group;
-    const int hm = p.mask_heads == 1 ? 0 : h;
-    const int64_t flat = (int64_t)hm * p.rows_total + sd[4] + m_block;
-    const int p_beg = p.p_off[flat];
-    const int np = p.p_off[flat + 1] - p_beg;
-    const int f_beg = p.f_off[flat];
-    const int ntiles = np + (p.f_off[flat + 1] - f_beg);
+  const int qloc = m_block * TQ + 32 * wave + lq;  // sample-local Q row of this lane
+  const uint32_t q_row_off = (uint32_t)qloc * q_rs;
 
-    const int qloc = m_block * TQ + 32 * wave + lq;  // sample-local Q row of this lane
-    const bool qvalid = qloc < q_len;
-    typename Ops::QFrag qf;
-    Ops::load_q(qf, qvalid ? Qg + (q_off + (int64_t)qloc) * q_rs + (int64_t)h * D : nullptr, b2);
-
-    float slope = 0.0f;
-    if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) slope = p.slopes[h] * kLog2e;
-    if constexpr (MOD == kModAlibiSoftcap) slope = p.slopes[h] * p.alibi_k;
-
-    f32x16 o[D / 32];
+  // tile t of the task: partial list first, then full list (§6.1)
+  auto tile_j = [&](int t) {
+    return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
+  };
+  auto load_masks = [&](int t, uint32_t (&mw)[NKB]) {
+    if (t < np) {
+      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-    float m_run = kNegInf, l_run = 0.0f;
-
-    const T* kbase = Kg + (int64_t)k_off * kv_rs + (int64_t)g * D;
-    const T* vbase = Vg + (int64_t)k_off * kv_rs + (int64_t)g * D;
-    // tile t of the task: partial list first, then full list (§6.1)
-    auto tile_j = [&](int t) { return t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]; };
-    auto load_masks = [&](int t, uint32_t (&mw)[NKB]) {
-      if (t < np) {
-        const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk] >> (4 * b2);
+    } else {
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk] >> (4 * b2);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
-      }
-    };
-
-    if (ntiles > 0) {
-      typename Ops::Stage st;
-      uint32_t mw_cur[NKB], mw_next[NKB];
-      int j_cur = tile_j(0);
-      Ops::load(st, kbase + (int64_t)j_cur * TKV * kv_rs, vbase + (int64_t)j_cur * TKV * kv_rs,
-                kv_rs, min(TKV, k_len - j_cur * TKV), tid);
-      load_masks(0, mw_cur);
-      Ops::store(st, sm, 0, tid);
-      __syncthreads();
-
-      for (int t = 0; t < ntiles; ++t) {
-        const int stage = t & 1;
-        const bool partial = t < np || p.force_partial;
-        const bool more = t + 1 < ntiles;
-        int j_next = 0;
-        if (more) {
-          j_next = tile_j(t + 1);
-          Ops::load(st, kbase + (int64_t)j_next * TKV * kv_rs,
-                    vbase + (int64_t)j_next * TKV * kv_rs, kv_rs,
-                    min(TKV, k_len - j_next * TKV), tid);
-          load_masks(t + 1, mw_next);
-        }
-
-        f32x16 acc[NKB];
-        Ops::qk(acc, qf, sm, stage, lane);
-
-        // score_mod, predicate, running max
-        const float kq0 = (float)(j_cur * TKV + 4 * b2 - qloc);
-        float mt = kNegInf;
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float kq = kq0 + (float)(kk * 32 + 8 * (v / 4) + (v % 4));
-            float u = mod_score<MOD>(acc[kk][v], kq, p, slope);
-            if (partial && !((mw_cur[kk] >> (8 * (v / 4) + (v % 4))) & 1u)) u = kNegInf;
-            acc[kk][v] = u;
-            mt = fmaxf(mt, u);
-          }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run, mt);
-        const float m_use = m_new == kNegInf ? 0.0f : m_new;
-        const float alpha = exp2_fast(m_run - m_use);
-        float rs = 0.0f;
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const float e = exp2_fast(acc[kk][v] - m_use);
-            acc[kk][v] = e;
-            rs += e;
-          }
-        l_run = fmaf(l_run, alpha, rs);
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-
-        typename Ops::PFrag pf;
-        Ops::to_p(pf, acc);
-        Ops::pv(o, pf, sm, stage, lane);
-
-        if (more) {
-          Ops::store(st, sm, stage ^ 1, tid);
-#pragma unroll
-          for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
-          j_cur = j_next;
-        }
-        __syncthreads();
-      }
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
     }
+  };
 
-    // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (qvalid) {
-      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-      Ops::store_o(Og + (q_off + (int64_t)qloc) * q_rs + (int64_t)h * D, o, inv, b2);
-      if (b2 == 0) {
-        p.lse[(int64_t)h * p.total_q + q_off + qloc] =
-            l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
-      }
+  typename Ops::Stage st;
+  uint32_t mw_cur[NKB], mw_next[NKB];
+  int j_cur = j_first;
+  if (ntiles > 0) {
+    Ops::load(st, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
+    load_masks(0, mw_cur);
+  }
+  typename Ops::QFrag qf;
+  Ops::load_q(qf, rq, q_row_off, b2);
+
+  float slope = 0.0f;
+  if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) slope = p.slopes[h] * kLog2e;
+  if constexpr (MOD == kModAlibiSoftcap) slope = p.slopes[h] * p.alibi_k;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
+  RowState rs{kNegInf, 0.0f};
+
+  // Two loops, as in §6.1: the partial list with its predicate, then the full
+  // list without one.  The K/V prefetch runs one tile ahead across both.
+  int t = 0;
+  auto advance = [&](int stage) {
+    const bool more = t + 1 < ntiles;
+    int j_next = 0;
+    if (more) {
+      j_next = tile_j(t + 1);
+      Ops::load(st, rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
+      load_masks(t + 1, mw_next);
+    }
+    return j_next;
+  };
+  auto retire = [&](int stage, int j_next) {
+    if (t + 1 < ntiles) {
+      Ops::store(st, sm, stage ^ 1, tid);
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
+      j_cur = j_next;
+    }
+    __syncthreads();
+  };
+  if (ntiles > 0) {
+    Ops::store(st, sm, 0, tid);
+    __syncthreads();
+    const int n_masked = p.force_partial ? ntiles : np;
+    for (; t < n_masked; ++t) {
+      const int stage = t & 1;
+      const int j_next = advance(stage);
+      const float kq0 = (float)(j_cur * TKV + 4 * b2 - qloc);
+      tile_step<Ops, MOD, true>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
+      retire(stage, j_next);
+    }
+    for (; t < ntiles; ++t) {
+      const int stage = t & 1;
+      const int j_next = advance(stage);
+      const float kq0 = (float)(j_cur * TKV + 4 * b2 - qloc);
+      tile_step<Ops, MOD, false>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
+      retire(stage, j_next);
     }
   }
-}
 
-__global__ void reset_counters_kernel(int32_t* c) {
-  if (threadIdx.x <= kNumQueues) c[threadIdx.x] = 0;
+  // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf.
+  // Rows past q_len are dropped by the O descriptor's range check.
+  const float l_tot = pair_sum(rs.l);
+  const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
+  Ops::store_o(ro, q_row_off, o, inv, b2);
+  if (b2 == 0 && qloc < q_len) {
+    p.lse[(int64_t)h * p.total_q + q_off + qloc] =
+        l_tot > 0.0f ? (rs.m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+  }
 }
 
 // ----------------------------------------------------------------- dispatch
 
 template <class Ops>
-hipError_t launch_ops(int mod, int grid, const AttnParams& p, hipStream_t s) {
-  const dim3 g(grid), blk(Ops::NT);
+hipError_t launch_ops(int mod, int num_tasks, const AttnParams& p, hipStream_t s) {
+  const dim3 g(num_tasks), blk(Ops::NT);
   switch (mod) {
     case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone>), g, blk, 0, s, p); break;
     case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap>), g, blk, 0, s, p); break;
@@ -487,25 +577,6 @@ hipError_t launch_ops(int mod, int grid, const AttnParams& p, hipStream_t s) {
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
-}
-
-template <class Ops>
-int occupancy_grid(int num_tasks, int device) {
-  static int cached[16] = {0};
-  int& per_cu = cached[device & 15];
-  if (per_cu == 0) {
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, attn_fwd_kernel<Ops, kModNone>,
-                                                     Ops::NT, 0) != hipSuccess || blocks < 1)
-      blocks = 1;
-    per_cu = blocks;
-  }
-  int cus = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      cus < 1)
-    cus = 256;
-  const int g = per_cu * cus;
-  return num_tasks < g ? num_tasks : g;
 }
 
 // The consumer table: (dtype, head_dim, tile_q, tile_k) -> kernel family.
@@ -531,26 +602,13 @@ bool attn_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_
 }
 
 hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
-                           int32_t mod_kind, int32_t grid, const AttnParams& p, hipStream_t s) {
+                           int32_t mod_kind, int32_t num_tasks, const AttnParams& p,
+                           hipStream_t s) {
 #define X(DT, HD, TQ_, TK_, ...) \
-  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return launch_ops<__VA_ARGS__>(mod_kind, grid, p, s);
+  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return launch_ops<__VA_ARGS__>(mod_kind, num_tasks, p, s);
   MPB_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
-}
-
-int32_t attn_grid_size(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
-                       int32_t num_tasks, int device) {
-#define X(DT, HD, TQ_, TK_, ...) \
-  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return occupancy_grid<__VA_ARGS__>(num_tasks, device);
-  MPB_VARIANTS(X)
-#undef X
-  return 0;
-}
-
-hipError_t launch_reset_counters(int32_t* counters, hipStream_t s) {
-  hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, counters);
-  return hipGetLastError();
 }
 
 }  // namespace mpb

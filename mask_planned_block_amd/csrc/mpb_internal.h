@@ -8,13 +8,27 @@
 namespace mpb {
 
 // Forward schedule: positive-cost tasks are split into kNumSections sections,
-// one per XCD of the MI355X (8 XCDs with a private L2 each).  Tasks of one
-// (batch, K/V head) pair share a section, so the work queue of XCD x keeps
-// that pair's K/V tiles in x's L2 (this library's reading of the "L2 section"
-// of the mask plan design page, §4.8).  Zero-cost tasks (rows with nothing
-// visible) form one more queue that is drained last.
+// one per XCD of the MI355X (8 XCDs, each with its own L2).  Tasks of one
+// (batch, K/V head) pair share a section.  Workgroups are handed to the XCDs
+// round-robin in launch order, so the launch order interleaves the sections
+// (launch slot 8r+x holds the r-th task of section x while every section still
+// has tasks): each XCD then runs one section's tasks in descending cost and
+// keeps that section's K/V in its L2.  This is this library's reading of the
+// "L2 section" of the mask plan design page, §4.8.  Zero-cost tasks (rows
+// with nothing visible) come last.
 constexpr int kNumSections = 8;
 constexpr int kNumQueues = kNumSections + 1;
+
+// One 64-byte record per forward task, in launch order: workgroup i runs
+// record i.  Fields (int32):
+enum TaskRecField {
+  kRecMBlock = 0, kRecHead, kRecBatch, kRecQValid,
+  kRecQOff, kRecKOff, kRecQLen, kRecKLen,
+  kRecPBeg, kRecPCnt, kRecFBeg, kRecFCnt,
+  kRecFirstTile,   // K tile of the first listed block, -1 if none
+  kRecMaskHead, kRecKvHead, kRecSection,
+  kTaskRecInts
+};
 
 // Planner geometry, passed by value to every planner kernel.
 struct PlanGeo {
@@ -37,8 +51,9 @@ struct PlanDev {
   int32_t* cu_rows;      // [B+1]
   int32_t* cu_q;         // [B+1] clone (THD) or nullptr
   int32_t* cu_k;
-  int32_t* work_desc;    // [upper_rows*Hq][4]
+  int32_t* work_desc;    // [upper_rows*Hq][4] section-major schedule
   int32_t* section_off;  // [kNumQueues+1]
+  int32_t* task_rec;     // [upper_rows*Hq][kTaskRecInts] launch order (sections interleaved)
   int32_t* p_off;        // [Hmask*rows+1]
   int32_t* f_off;
   int32_t* p_idx;
@@ -90,9 +105,7 @@ struct AttnParams {
   const int32_t* f_off;
   const int32_t* f_idx;
   const uint32_t* p_masks;
-  const int32_t* work_desc;
-  const int32_t* section_off;
-  int32_t* counters;        // [kNumQueues + 1] in caller workspace
+  const int32_t* task_rec;  // [num_tasks][kTaskRecInts]
   const float* slopes;
   int32_t heads_q, heads_k, group, mask_heads, rows_total, total_q;
   int32_t force_partial;
@@ -106,9 +119,7 @@ struct AttnParams {
 // resolved to).  Returns false if (dtype, head_dim, tile_q, tile_k) has none.
 bool attn_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k);
 hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
-                           int32_t mod_kind, int32_t grid, const AttnParams& p, hipStream_t s);
-int32_t attn_grid_size(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
-                       int32_t num_tasks, int device);
-hipError_t launch_reset_counters(int32_t* counters, hipStream_t s);
+                           int32_t mod_kind, int32_t num_tasks, const AttnParams& p,
+                           hipStream_t s);
 
 }  // namespace mpb

@@ -14,7 +14,9 @@
 //   plan_sched_*_kernel     §4.8 forward schedule by bounded counting:
 //                           histogram over (section, cost), one-workgroup
 //                           scan of bucket offsets, one wavefront per section
-//                           scattering its tasks in tie order.
+//                           scattering its tasks in tie order, then the
+//                           section-interleaved launch order with one record
+//                           per task.
 //   plan_materialize_kernel §4.6 / §5 Q2K materialisation: ascending partial
 //                           and full K-tile indices plus one packed predicate
 //                           per partial tile.
@@ -459,6 +461,69 @@ __global__ __launch_bounds__(64) void plan_sched_scatter_kernel(PlanGeo g, PlanD
   }
 }
 
+// Launch order and task records.  Task t of the section-major schedule has
+// rank r in its section s; its launch slot interleaves the sections:
+// slot = sum_s' min(r, n_s') + #{s' < s : n_s' > r}; zero-cost tasks follow
+// all positive-cost ones.  Each record carries everything a forward
+// workgroup needs (see TaskRecField), so the attention kernel starts its
+// Q and first K/V loads after a single record read.
+__global__ __launch_bounds__(256) void plan_sched_records_kernel(PlanGeo g, PlanDev d,
+                                                                 PlanWork w) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rows_total = d.cu_rows[g.batch];
+  const int ntasks = rows_total * g.heads_q;
+  if (t >= ntasks) return;
+  int s = 0;
+  while (s < kNumSections && t >= d.section_off[s + 1]) ++s;
+  const int r = t - d.section_off[s];
+  int slot;
+  if (s < kNumSections) {
+    slot = 0;
+    for (int s2 = 0; s2 < kNumSections; ++s2) {
+      const int n2 = d.section_off[s2 + 1] - d.section_off[s2];
+      slot += min(r, n2) + ((s2 < s && n2 > r) ? 1 : 0);
+    }
+  } else {
+    slot = d.section_off[kNumSections] + r;
+  }
+  const int32_t* wd = d.work_desc + 4 * (int64_t)t;
+  const int m_block = wd[0], h = wd[1], b = wd[2];
+  const int32_t* sd = d.seqdesc + 8 * b;
+  const int row = sd[4] + m_block;
+  const int hm = g.mask_heads == 1 ? 0 : h;
+  const int64_t flat = (int64_t)hm * rows_total + row;
+  const int64_t src = (int64_t)hm * g.upper_rows + row;
+  const int p_beg = w.p_off_tmp[flat], np = w.p_off_tmp[flat + 1] - p_beg;
+  const int f_beg = w.f_off_tmp[flat], nf = w.f_off_tmp[flat + 1] - f_beg;
+  int first = -1;
+  if (np + nf > 0) {
+    const int nwords = (sd[6] + 31) >> 5;
+    for (int ww = 0; ww < nwords && first < 0; ++ww) {
+      const uint32_t vw = w.vis_bits[src * g.words_k + ww];
+      const uint32_t fw = w.full_bits[src * g.words_k + ww];
+      const uint32_t pick = np > 0 ? (vw & ~fw) : fw;  // partial list first (§6.1)
+      if (pick) first = 32 * ww + __ffs(pick) - 1;
+    }
+  }
+  int32_t* rec = d.task_rec + (int64_t)slot * kTaskRecInts;
+  rec[kRecMBlock] = m_block;
+  rec[kRecHead] = h;
+  rec[kRecBatch] = b;
+  rec[kRecQValid] = wd[3];
+  rec[kRecQOff] = sd[0];
+  rec[kRecKOff] = sd[1];
+  rec[kRecQLen] = sd[2];
+  rec[kRecKLen] = sd[3];
+  rec[kRecPBeg] = p_beg;
+  rec[kRecPCnt] = np;
+  rec[kRecFBeg] = f_beg;
+  rec[kRecFCnt] = nf;
+  rec[kRecFirstTile] = first;
+  rec[kRecMaskHead] = hm;
+  rec[kRecKvHead] = h / (g.heads_q / g.heads_k);
+  rec[kRecSection] = s;
+}
+
 // ---------------------------------------------------------------- materialize
 
 namespace {
@@ -606,6 +671,10 @@ hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWo
   }
   hipLaunchKernelGGL(plan_sched_offsets_kernel, dim3(1), dim3(1024), 0, s, g, d, w);
   hipLaunchKernelGGL(plan_sched_scatter_kernel, dim3(kNumQueues), dim3(64), 0, s, g, d, w);
+  if (upper_tasks > 0) {
+    hipLaunchKernelGGL(plan_sched_records_kernel, dim3((upper_tasks + 255) / 256), dim3(256), 0,
+                       s, g, d, w);
+  }
   return hipGetLastError();
 }
 

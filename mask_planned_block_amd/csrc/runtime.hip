@@ -149,7 +149,7 @@ mpb_signature consumer_signature(const mpb_problem& p, int tq, int tk) {
   s.head_dim = p.head_dim;
   s.dtype = p.dtype;
   s.payload_layout = 1;
-  s.scheduler = 1;
+  s.scheduler = 2;
   return s;
 }
 
@@ -288,6 +288,7 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   const size_t o_cu_k = cg.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 1);
   const size_t o_work_desc = cg.take<int32_t>(4 * upper * p.heads_q);
   const size_t o_sec = cg.take<int32_t>(kNumQueues + 1);
+  const size_t o_rec = cg.take<int32_t>(kTaskRecInts * upper * p.heads_q);
   Carver cw;
   const size_t o_vis = cw.take<uint32_t>(items_upper * words_k);
   const size_t o_full = cw.take<uint32_t>(items_upper * words_k);
@@ -320,6 +321,7 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   d.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(geo_block, o_cu_k) : nullptr;
   d.work_desc = at<int32_t>(geo_block, o_work_desc);
   d.section_off = at<int32_t>(geo_block, o_sec);
+  d.task_rec = at<int32_t>(geo_block, o_rec);
   PlanWork w;
   w.vis_bits = at<uint32_t>(work_block, o_vis);
   w.full_bits = at<uint32_t>(work_block, o_full);
@@ -474,9 +476,23 @@ mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seq
   return ok();
 }
 
+mpb_status mask_plan_export_launch_order(const mpb_plan* plan, int32_t* records) {
+  if (!plan || !records) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or records is NULL");
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipError_t e = hipStreamSynchronize(plan->stream);
+  if (e == hipSuccess && plan->num_tasks > 0)
+    e = hipMemcpy(records, plan->dev.task_rec, (size_t)plan->num_tasks * kTaskRecInts * 4,
+                  hipMemcpyDeviceToHost);
+  if (cur != plan->device) hipSetDevice(cur);
+  if (e != hipSuccess) return device_status(e, "launch order export");
+  return ok();
+}
+
 size_t flex_attn_fwd_workspace_size(const mpb_plan* plan) {
   (void)plan;
-  return 256;  // kNumQueues + 1 counters, padded
+  return 0;  // the forward launches one workgroup per task: no scheduler state
 }
 
 static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
@@ -511,10 +527,19 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
                                             "this forward consumer");
   if (plan->num_tasks > 0 && (!q || !k || !v || !o || !lse))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
-  if (!workspace || workspace_bytes < flex_attn_fwd_workspace_size(plan))
+  if (workspace_bytes < flex_attn_fwd_workspace_size(plan) ||
+      (workspace_bytes > 0 && !workspace))
     return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed",
                 flex_attn_fwd_workspace_size(plan));
-  if (!std::isfinite(scale)) return fail(MPB_ERR_INVALID_ARGUMENT, "scale is not finite");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  // The kernel addresses one sample's rows of one head through 32-bit buffer
+  // offsets (including one tile of overshoot past the sample end).
+  const int64_t esz = b.dtype == MPB_DTYPE_BF16 ? 2 : 4;
+  const int64_t qspan = ((int64_t)b.seqlen_q + b.tile_q) * b.heads_q * b.head_dim * esz;
+  const int64_t kspan = ((int64_t)b.seqlen_k + b.tile_k) * b.heads_k * b.head_dim * esz;
+  if (qspan >= ((int64_t)1 << 31) || kspan >= ((int64_t)1 << 31))
+    return fail(MPB_ERR_UNSUPPORTED, "one sample spans >= 2 GiB of Q/K/V; not supported");
   const bool sc = mod && mod->softcap_enabled;
   const bool al = mod && mod->alibi_enabled;
   if (sc && !(std::isfinite(mod->softcap) && mod->softcap > 0.0f))
@@ -538,9 +563,7 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.f_off = plan->dev.f_off;
   prm.f_idx = plan->dev.f_idx;
   prm.p_masks = plan->dev.p_masks;
-  prm.work_desc = plan->dev.work_desc;
-  prm.section_off = plan->dev.section_off;
-  prm.counters = static_cast<int32_t*>(workspace);
+  prm.task_rec = plan->dev.task_rec;
   prm.slopes = al ? mod->alibi_slopes : nullptr;
   prm.heads_q = b.heads_q;
   prm.heads_k = b.heads_k;
@@ -556,11 +579,8 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
   if (plan->num_tasks == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = attn_grid_size(b.dtype, b.head_dim, b.tile_q, b.tile_k, plan->num_tasks, dev);
-  if (grid < 1) return fail(MPB_ERR_DEVICE, "could not size the persistent grid");
-  if ((e = launch_reset_counters(prm.counters, s)) != hipSuccess ||
-      (e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, grid, prm, s)) !=
-          hipSuccess)
+  if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks, prm,
+                           s)) != hipSuccess)
     return device_status(e, "attention launch");
   return ok();
 }

@@ -94,6 +94,45 @@ def check_schedule(w, gp, tile_q, num_sections=8):
     assert len(seen) == n
 
 
+def check_launch_order(w, gp, tile_q, num_sections=8):
+    """Launch records: a permutation of the schedule with the sections
+    interleaved (slot = sum_s' min(r, n_s') + #{s' < s : n_s' > r} for the
+    r-th task of section s; zero-cost tasks last in schedule order), each
+    record carrying the task's geometry, CSR ranges and first K tile."""
+    wd, so, rec = gp["work_desc"], gp["section_off"], gp["launch"]
+    n = wd.shape[0]
+    assert rec.shape == (n, 16)
+    sizes = np.diff(so)
+    rows_total = int(gp["cu_rows"][-1])
+    want = np.full(n, -1, np.int64)
+    for s in range(num_sections + 1):
+        for r in range(int(sizes[s])):
+            t = int(so[s]) + r
+            if s < num_sections:
+                slot = sum(min(r, int(sizes[x])) for x in range(num_sections)) + \
+                    sum(1 for x in range(s) if sizes[x] > r)
+            else:
+                slot = int(so[num_sections]) + r
+            assert want[slot] == -1
+            want[slot] = t
+    for slot in range(n):
+        t = want[slot]
+        m_block, h, b, qv = (int(x) for x in wd[t])
+        R = rec[slot]
+        assert list(R[:4]) == [m_block, h, b, qv]
+        sd = gp["seqdesc"][b]
+        assert list(R[4:8]) == [int(sd[0]), int(sd[1]), int(sd[2]), int(sd[3])]
+        hm = 0 if w.mask_heads == 1 else h
+        flat = hm * rows_total + int(sd[4]) + m_block
+        pb, pe = int(gp["p_off"][flat]), int(gp["p_off"][flat + 1])
+        fb, fe = int(gp["f_off"][flat]), int(gp["f_off"][flat + 1])
+        assert list(R[8:12]) == [pb, pe - pb, fb, fe - fb]
+        first = int(gp["p_idx"][pb]) if pe > pb else (int(gp["f_idx"][fb]) if fe > fb else -1)
+        assert int(R[12]) == first
+        assert int(R[13]) == hm and int(R[14]) == h // (w.heads_q // w.heads_k)
+        assert 0 <= int(R[15]) <= num_sections
+
+
 def compare_attention(w, o_ref, lse_ref, o_gpu, lse_gpu, what=""):
     """Max-abs comparison at the stated tolerance; empty rows must be exactly
     O = 0 and LSE = -inf on both sides."""

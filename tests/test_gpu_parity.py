@@ -50,6 +50,7 @@ def test_plan_bit_exact_small(name, tiles):
     op = oracle.build_plan(w, tq, tk)
     G.compare_plan(gp, op)
     G.check_schedule(w, gp, tq)
+    G.check_launch_order(w, gp, tq)
 
 
 @pytest.mark.parametrize("name", CONFIGS)
@@ -63,6 +64,7 @@ def test_plan_bit_exact_full(name):
     op = oracle.build_plan(w, tq, tk)
     G.compare_plan(gp, op)
     G.check_schedule(w, gp, tq)
+    G.check_launch_order(w, gp, tq)
 
 
 # ------------------------------------------------------------------ attention
@@ -162,6 +164,7 @@ def test_empty_samples_empty_rows_gqa_hmask():
     plan = G.build_plan(w, d)
     G.compare_plan(plan.export(), oracle.build_plan(w, 128, 64))
     G.check_schedule(w, plan.export(), 128)
+    G.check_launch_order(w, plan.export(), 128)
     o, lse = G.run_attention(w, d, plan)
     torch.cuda.synchronize()
     O, L = oracle.attention(w)
@@ -273,6 +276,6 @@ def test_signature_and_workspace_errors():
         plan, q2, d["k"][:, :, :1].contiguous(), d["v"][:, :, :1].contiguous()))
     _expect("MPB_ERR_SIGNATURE_MISMATCH", lambda: mpb.flex_attn_fwd(
         plan, d["q"].float(), d["k"].float(), d["v"].float()))
-    ws = torch.empty(4, dtype=torch.uint8, device="cuda")
-    _expect("MPB_ERR_WORKSPACE", lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"],
-                                                            workspace=ws))
+    assert mpb.flex_attn_fwd_workspace_size(plan) == 0
+    _expect("MPB_ERR_INVALID_ARGUMENT", lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"],
+                                                                   scale=-1.0))
