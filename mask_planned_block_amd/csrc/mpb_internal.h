@@ -69,17 +69,26 @@ struct PlanWork {
   int32_t* fcnt;
   int32_t* p_off_tmp;    // [Hmask*upper_rows+1] (compact head-major order)
   int32_t* f_off_tmp;
-  int32_t* bins;         // [kNumQueues][nk_max+1] histogram, then cursors
+  int32_t* item_err;     // [Hmask][upper_rows] endpoint error bits per classified row
+  int32_t* geo_err;      // [1] cu_seqlens error bit (THD)
+  int32_t* keys;         // [upper_rows*Hq] schedule bucket of each task
+  int32_t* lrank;        // [upper_rows*Hq] rank among equal keys of its 64-task chunk
+  int32_t* chunk_cnt;    // [buckets][nchunks] counts, then first positions
+  int64_t chunk_cnt_len; // buckets * nchunks, buckets = kNumQueues * (nk_max + 1)
+  int32_t nchunks;       // ceil(upper_rows*Hq / 64)
 };
+
+// Longest sample the planner handles, in K tiles: bounds the schedule's
+// (section, cost) bucket count, which sizes the count matrix of its sort.
+constexpr int kMaxKTiles = 8191;
 
 // ---- planner launchers (plan_kernels.hip) ----
 hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
-                                const PlanDev& d, hipStream_t s);
+                                const PlanDev& d, const PlanWork& w, hipStream_t s);
 hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
                                 const PlanWork& w, hipStream_t s);
-hipError_t launch_plan_scan(const PlanGeo& g, const PlanDev& d, const PlanWork& w, hipStream_t s);
-hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                int32_t rows_upper_tasks, hipStream_t s);
+hipError_t launch_plan_index(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                             int32_t* host_header, hipStream_t s);
 hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
                                    const PlanWork& w, int32_t rows_total, hipStream_t s);
 

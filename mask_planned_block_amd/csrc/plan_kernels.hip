@@ -1,25 +1,32 @@
 // MaskPlan builder kernels for gfx950.
 //
 // Stages follow "Flex Attention Mask Plan Design" (cuDNN frontend docs):
-//   plan_geometry_kernel    §4.2 Varlen geometry: validates cu_seqlens, builds
-//                           the per-sample descriptor and the compact Q plan
-//                           row prefix; fixed-length geometry is closed form.
+//   plan_geometry_kernel    §4.2 Varlen geometry (THD only): validates
+//                           cu_seqlens, builds the per-sample descriptor and
+//                           the compact Q plan-row prefix.  Fixed-length
+//                           geometry is closed form (written by the scan).
 //   plan_classify_kernel    §4.3 Q2K classification: one wavefront per
-//                           (mask head, Q plan row); each lane owns Q rows and
-//                           sweeps that row's sorted intervals; the per-tile
-//                           any/all reduction is a wavefront ballot.  Also
-//                           validates every endpoint (§2 order and bounds).
-//   plan_scan_kernel        §4.5 count scan into exact exclusive offsets plus
-//                           the 8-value allocation header.
-//   plan_sched_*_kernel     §4.8 forward schedule by bounded counting:
-//                           histogram over (section, cost), one-workgroup
-//                           scan of bucket offsets, one wavefront per section
-//                           scattering its tasks in tie order, then the
-//                           section-interleaved launch order with one record
-//                           per task.
+//                           (mask head, Q plan row).  Each lane reads its
+//                           row's intervals once (coalesced across lanes),
+//                           validates them (§2 order and bounds), merges
+//                           touching intervals and records the K tiles each
+//                           run touches / fully covers in LDS difference
+//                           arrays; a wavefront prefix scan then gives, per
+//                           tile, how many rows see it at all and how many see
+//                           all of it: any > 0 is visible, all == T_Q is full.
+//   plan_index_kernel       one workgroup: §4.5 exact exclusive CSR offsets
+//                           and the 8-value allocation header (device errors
+//                           OR-ed in, published to host-mapped memory), then
+//                           §4.8 the forward schedule as a stable counting sort
+//                           and the section-interleaved launch records.
 //   plan_materialize_kernel §4.6 / §5 Q2K materialisation: ascending partial
-//                           and full K-tile indices plus one packed predicate
-//                           per partial tile.
+//                           and full K-tile indices, and one predicate word per
+//                           (row, 32 columns) of each partial tile.
+//
+// Visibility used throughout: with sorted endpoints F, column k is visible iff
+// an even number of endpoints are <= k (k < F0: none; F0 <= k < F1: one, ...),
+// which is the union [0,F0) U [F1,F2) U ... of §2; columns >= F(nfunc-1)
+// (hence >= k_len) see an odd count and are masked.
 #include "mpb_internal.h"
 #include "../../include/mpb.h"
 
@@ -40,82 +47,86 @@ __device__ inline int sample_of_row(const int32_t* cu_rows, int batch, int row) 
 
 __device__ inline int wave_lane() { return threadIdx.x & 63; }
 
-__device__ inline uint32_t range_bits(int lo, int hi) {
-  // bits [lo, hi) of a 32-bit word, 0 <= lo < hi <= 32
-  uint32_t upto = hi >= 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u);
-  return upto & ~((1u << lo) - 1u);
+__device__ inline uint64_t lanes_below(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-// Reads interval p of one row: p = 0 is [0, F0); p >= 1 is [F(2p-1), F(2p)).
-struct RowIntervals {
-  const int32_t* col;   // &mask_func[hm][0][token]
-  int64_t stride;       // total_q
-  __device__ inline void get(int p, int& s, int& e) const {
-    if (p == 0) {
-      s = 0;
-      e = col[0];
-    } else {
-      s = col[(int64_t)(2 * p - 1) * stride];
-      e = col[(int64_t)(2 * p) * stride];
-    }
-  }
+// Geometry of one Q plan row: sample, tile row within the sample, bounds.
+struct RowGeo {
+  int b, i, q_off, q_len, k_off, k_len, nk, row_begin;
 };
 
-// Monotone sweep over one row's intervals: count(x) = number of visible k < x.
-struct CountSweep {
-  int p, cum, s, e;
-  __device__ inline void init(const RowIntervals& r, int nint) {
-    p = 0;
-    cum = 0;
-    r.get(0, s, e);
-    (void)nint;
+__device__ inline RowGeo row_geometry(const PlanGeo& g, const PlanDev& d, int row) {
+  RowGeo r;
+  if (g.layout == MPB_LAYOUT_BSHD) {
+    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+    r.b = row / rps;
+    r.i = row - r.b * rps;
+    r.q_off = r.b * g.seqlen_q;
+    r.q_len = g.seqlen_q;
+    r.k_off = r.b * g.seqlen_k;
+    r.k_len = g.seqlen_k;
+    r.row_begin = r.b * rps;
+  } else {
+    r.b = sample_of_row(d.cu_rows, g.batch, row);
+    const int32_t* sd = d.seqdesc + 8 * r.b;
+    r.q_off = sd[0];
+    r.k_off = sd[1];
+    r.q_len = sd[2];
+    r.k_len = sd[3];
+    r.row_begin = sd[4];
+    r.i = row - r.row_begin;
   }
-  __device__ inline int count_below(const RowIntervals& r, int nint, int x) {
-    while (p < nint && e <= x) {
-      cum += max(0, e - s);
-      ++p;
-      if (p < nint) r.get(p, s, e);
-    }
-    int v = cum;
-    if (p < nint) v += min(max(x - s, 0), max(0, e - s));
-    return v;
+  r.nk = (r.k_len + g.tile_k - 1) / g.tile_k;
+  return r;
+}
+
+__device__ inline int rows_total_of(const PlanGeo& g, const PlanDev& d) {
+  return g.layout == MPB_LAYOUT_BSHD ? g.upper_rows : d.cu_rows[g.batch];
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ inline int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
-};
+  return v;
+}
 
 }  // namespace
 
 // ---------------------------------------------------------------- geometry
 
 __global__ __launch_bounds__(1024) void plan_geometry_kernel(PlanGeo g, const int32_t* cu_q,
-                                                             const int32_t* cu_k, PlanDev d) {
+                                                             const int32_t* cu_k, PlanDev d,
+                                                             PlanWork w) {
   __shared__ int s_bad;
   __shared__ int s_carry;
   __shared__ int s_scan[1024];
   const int tid = threadIdx.x;
   const int B = g.batch;
-  if (tid < 8) d.header[tid] = 0;
   if (tid == 0) {
     s_bad = 0;
     s_carry = 0;
   }
   __syncthreads();
-  if (g.layout == MPB_LAYOUT_THD) {
-    // §3.2: prefixes start at 0, end at the totals, never decrease and no
-    // sample exceeds max_seqlen.  The plan keeps its own copy of both.
-    for (int b = tid; b <= B; b += blockDim.x) {
-      int bad = 0;
-      const int q1 = cu_q[b], k1 = cu_k[b];
-      if (b == 0 && (q1 != 0 || k1 != 0)) bad = 1;
-      if (b == B && (q1 != g.total_q || k1 != g.total_k)) bad = 1;
-      if (b < B) {
-        const int q2 = cu_q[b + 1], k2 = cu_k[b + 1];
-        if (q2 < q1 || k2 < k1) bad = 1;
-        if ((int64_t)q2 - q1 > g.seqlen_q || (int64_t)k2 - k1 > g.seqlen_k) bad = 1;
-      }
-      d.cu_q[b] = q1;
-      d.cu_k[b] = k1;
-      if (bad) atomicOr(&s_bad, 1);
+  // §3.2: prefixes start at 0, end at the totals, never decrease and no
+  // sample exceeds max_seqlen.  The plan keeps its own copy of both.
+  for (int b = tid; b <= B; b += blockDim.x) {
+    int bad = 0;
+    const int q1 = cu_q[b], k1 = cu_k[b];
+    if (b == 0 && (q1 != 0 || k1 != 0)) bad = 1;
+    if (b == B && (q1 != g.total_q || k1 != g.total_k)) bad = 1;
+    if (b < B) {
+      const int q2 = cu_q[b + 1], k2 = cu_k[b + 1];
+      if (q2 < q1 || k2 < k1) bad = 1;
+      if ((int64_t)q2 - q1 > g.seqlen_q || (int64_t)k2 - k1 > g.seqlen_k) bad = 1;
     }
+    d.cu_q[b] = q1;
+    d.cu_k[b] = k1;
+    if (bad) atomicOr(&s_bad, 1);
   }
   __syncthreads();
   const bool bad = s_bad != 0;
@@ -125,17 +136,10 @@ __global__ __launch_bounds__(1024) void plan_geometry_kernel(PlanGeo g, const in
     const int b = base + tid;
     int q_off = 0, q_len = 0, k_off = 0, k_len = 0;
     if (b < B && !bad) {
-      if (g.layout == MPB_LAYOUT_BSHD) {
-        q_off = b * g.seqlen_q;
-        q_len = g.seqlen_q;
-        k_off = b * g.seqlen_k;
-        k_len = g.seqlen_k;
-      } else {
-        q_off = cu_q[b];
-        q_len = cu_q[b + 1] - q_off;
-        k_off = cu_k[b];
-        k_len = cu_k[b + 1] - k_off;
-      }
+      q_off = cu_q[b];
+      q_len = cu_q[b + 1] - q_off;
+      k_off = cu_k[b];
+      k_len = cu_k[b + 1] - k_off;
     }
     const int rows_b = (q_len + g.tile_q - 1) / g.tile_q;
     s_scan[tid] = rows_b;
@@ -165,108 +169,182 @@ __global__ __launch_bounds__(1024) void plan_geometry_kernel(PlanGeo g, const in
   }
   if (tid == 0) {
     d.cu_rows[0] = 0;
-    if (bad) d.header[7] = MPB_DEVERR_SEQLENS;
+    w.geo_err[0] = bad ? MPB_DEVERR_SEQLENS : 0;
   }
 }
 
 // ---------------------------------------------------------------- classify
 
+namespace {
+
+// bits [lo, hi) of a 32-bit word, 0 <= lo < hi <= 32
+__device__ inline uint32_t range_bits(int lo, int hi) {
+  const uint32_t upto = hi >= 32 ? 0xFFFFFFFFu : ((1u << hi) - 1u);
+  return upto & ~((1u << lo) - 1u);
+}
+
+// OR tiles [t0, t1) into a 128-tile window starting at tile tg.
+__device__ inline void set_tiles(uint32_t (&m)[4], int t0, int t1, int tg) {
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int w0 = tg + 32 * x;
+    const int lo = max(t0, w0), hi = min(t1, w0 + 32);
+    if (hi > lo) m[x] |= range_bits(lo - w0, hi - w0);
+  }
+}
+
+__device__ inline uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x |= (uint32_t)__shfl_xor((int)x, off);
+  return x;
+}
+__device__ inline uint32_t wave_and(uint32_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x &= (uint32_t)__shfl_xor((int)x, off);
+  return x;
+}
+
+}  // namespace
+
+// One wavefront per (mask head, Q plan row); lanes own rows lane + 64t.
+// Tiles are handled in windows of 128 (four 32-bit words): for each window a
+// lane walks its row's intervals (read 8 at a time, coalesced across lanes),
+// merges touching intervals into runs, and ORs the tiles each run touches
+// ("any") or fully covers ("full") into its words.  Across the wavefront the
+// "any" words are OR-ed and the "full" words AND-ed: a tile is visible if any
+// row sees part of it and full if every one of the T_Q rows covers it, which
+// needs every row in bounds (rows past q_len contribute nothing) and the tile
+// inside k_len (no run extends past k_len).  §2 order and bounds of every
+// endpoint are checked on the way.
 template <int RPL>
 __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
                                                             const int32_t* __restrict__ mf,
                                                             PlanDev d, PlanWork w) {
   const int lane = wave_lane();
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // Side job: clear the schedule's [bucket][chunk] count matrix (read only
+  // by the schedule kernels, which run after this kernel).
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < w.chunk_cnt_len;
+       x += (int64_t)gridDim.x * blockDim.x)
+    w.chunk_cnt[x] = 0;
   const int hm = item / g.upper_rows;
   const int row = item - hm * g.upper_rows;
   if (hm >= g.mask_heads) return;
-  const int rows_total = d.cu_rows[g.batch];
-  if (row >= rows_total) return;
-  const int b = sample_of_row(d.cu_rows, g.batch, row);
-  const int32_t* sd = d.seqdesc + 8 * b;
-  const int q_off = sd[0], q_len = sd[2], k_len = sd[3], nk = sd[6];
-  const int i = row - sd[4];
+  if (row >= rows_total_of(g, d)) return;
+  const RowGeo rg = row_geometry(g, d, row);
+  const int nk = rg.nk;
+  const int T = g.tile_k;
   const int nint = (g.nfunc + 1) >> 1;
 
-  bool valid[RPL];
-  RowIntervals ri[RPL];
+  bool valid[RPL], exists[RPL];
+  const int32_t* col[RPL];
+#pragma unroll
   for (int t = 0; t < RPL; ++t) {
     const int rho = lane + 64 * t;
-    valid[t] = rho < g.tile_q && i * g.tile_q + rho < q_len;
-    const int64_t tok = (int64_t)q_off + (int64_t)i * g.tile_q + rho;
-    ri[t].col = mf + (int64_t)hm * g.nfunc * g.total_q + (valid[t] ? tok : 0);
-    ri[t].stride = g.total_q;
+    exists[t] = rho < g.tile_q;
+    valid[t] = exists[t] && rg.i * g.tile_q + rho < rg.q_len;
+    col[t] = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off + (int64_t)rg.i * g.tile_q +
+             (valid[t] ? rho : 0);
   }
 
-  // §2 / §4.3: every endpoint in [0, k_len] and nondecreasing.  Loads are
-  // coalesced: all lanes read endpoint f of consecutive tokens.
   uint32_t err = 0;
-  {
-    int prev[RPL];
-    for (int f = 0; f < g.nfunc; ++f) {
-      for (int t = 0; t < RPL; ++t) {
-        if (!valid[t]) continue;
-        const int F = ri[t].col[(int64_t)f * g.total_q];
-        if (F < 0 || F > k_len) err |= MPB_DEVERR_RANGE;
-        if (f > 0 && F < prev[t]) err |= MPB_DEVERR_ORDER;
-        prev[t] = F;
-      }
-    }
-  }
-  const uint64_t any_range = __ballot((err & MPB_DEVERR_RANGE) != 0);
-  const uint64_t any_order = __ballot((err & MPB_DEVERR_ORDER) != 0);
-  if (lane == 0 && (any_range | any_order)) {
-    atomicOr(&d.header[7], (any_range ? MPB_DEVERR_RANGE : 0) | (any_order ? MPB_DEVERR_ORDER : 0));
-  }
-
-  // §4.3 three states per (row tile, K tile).  A lane's visible count in
-  // tile j is count(c1) - count(c0) of its row; a tile is full only if the
-  // whole T_Q x T_KV tile is in bounds and every element is visible.
-  CountSweep sw[RPL];
-  int prevc[RPL];
-  for (int t = 0; t < RPL; ++t) {
-    if (valid[t]) sw[t].init(ri[t], nint);
-    prevc[t] = 0;
-  }
-  const bool rows_in_bounds = (i + 1) * g.tile_q <= q_len;
-  uint32_t vword = 0, fword = 0;
   int pc = 0, fc = 0;
   const int64_t wbase = ((int64_t)hm * g.upper_rows + row) * g.words_k;
-  for (int j = 0; j < nk; ++j) {
-    const int c0 = j * g.tile_k;
-    const int c1 = min(c0 + g.tile_k, k_len);
-    bool any_vis = false, all_vis = true;
+  for (int tg = 0; tg < nk; tg += 128) {
+    uint32_t any_m[4] = {0u, 0u, 0u, 0u};
+    uint32_t full_m[4] = {~0u, ~0u, ~0u, ~0u};   // AND identity
+#pragma unroll
     for (int t = 0; t < RPL; ++t) {
-      if (!valid[t]) continue;
-      const int c = sw[t].count_below(ri[t], nint, c1);
-      const int cnt = c - prevc[t];
-      prevc[t] = c;
-      any_vis |= cnt > 0;
-      all_vis &= cnt == g.tile_k;
-    }
-    const bool tile_any = __ballot(any_vis) != 0;
-    const bool tile_full = tile_any && rows_in_bounds && (c0 + g.tile_k <= k_len) &&
-                           __ballot(!all_vis) == 0;
-    vword |= (uint32_t)tile_any << (j & 31);
-    fword |= (uint32_t)tile_full << (j & 31);
-    pc += (tile_any && !tile_full) ? 1 : 0;
-    fc += tile_full ? 1 : 0;
-    if ((j & 31) == 31 || j == nk - 1) {
-      if (lane == 0) {
-        w.vis_bits[wbase + (j >> 5)] = vword;
-        w.full_bits[wbase + (j >> 5)] = fword;
+      if (!exists[t]) continue;                    // not a row of the tile
+      uint32_t rf[4] = {0u, 0u, 0u, 0u};
+      if (valid[t]) {
+        // A run [a, b) touches tiles a/T .. (b-1)/T and fully covers
+        // ceil(a/T) .. b/T - 1 (clamped to [0, nk] for malformed input).
+        auto flush = [&](int a, int b) {
+          if (b <= a) return;
+          const int t0 = min(max(a / T, 0), nk), t1 = min(max((b - 1) / T + 1, 0), nk);
+          set_tiles(any_m, t0, t1, tg);
+          const int f0 = min(max((a + T - 1) / T, 0), nk), f1 = min(max(b / T, 0), nk);
+          set_tiles(rf, f0, f1, tg);
+        };
+        int run_a = 0, run_b = 0;  // open run, empty when run_b <= run_a
+        int prev = 0;
+        constexpr int kBatch = 8;
+        for (int p0 = 0; p0 < nint; p0 += kBatch) {
+          int sv[kBatch], ev[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u;
+            sv[u] = 0;
+            ev[u] = 0;
+            if (p < nint) {
+              if (p > 0) sv[u] = col[t][(int64_t)(2 * p - 1) * g.total_q];
+              ev[u] = col[t][(int64_t)(2 * p) * g.total_q];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int p = p0 + u;
+            if (p >= nint) break;
+            const int s = sv[u], e = ev[u];
+            if (tg == 0) {
+              if (p > 0) {
+                if (s < prev) err |= MPB_DEVERR_ORDER;
+                if (s < 0 || s > rg.k_len) err |= MPB_DEVERR_RANGE;
+              }
+              if (e < s) err |= MPB_DEVERR_ORDER;
+              if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
+            }
+            prev = e;
+            if (e <= s) continue;                 // empty interval
+            if (run_b > run_a && s == run_b) {
+              run_b = e;                          // touching: extend the run
+            } else {
+              flush(run_a, run_b);
+              run_a = s;
+              run_b = e;
+            }
+          }
+        }
+        flush(run_a, run_b);
       }
-      vword = 0;
-      fword = 0;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) full_m[x] &= rf[x];
+    }
+    uint32_t vis_w[4], full_w[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      vis_w[x] = wave_or(any_m[x]);
+      full_w[x] = wave_and(full_m[x]);
+      const int w0 = tg + 32 * x;
+      const uint32_t live = w0 >= nk ? 0u : (nk - w0 >= 32 ? ~0u : ((1u << (nk - w0)) - 1u));
+      vis_w[x] &= live;
+      full_w[x] &= vis_w[x];
+      pc += __popc(vis_w[x] & ~full_w[x]);
+      fc += __popc(full_w[x]);
+    }
+    if (lane < 4) {
+      const int x = lane;
+      const int w0 = tg + 32 * x;
+      if (w0 < nk) {
+        w.vis_bits[wbase + (w0 >> 5)] = x == 0 ? vis_w[0] : x == 1 ? vis_w[1] : x == 2 ? vis_w[2] : vis_w[3];
+        w.full_bits[wbase + (w0 >> 5)] = x == 0 ? full_w[0] : x == 1 ? full_w[1] : x == 2 ? full_w[2] : full_w[3];
+      }
     }
   }
+  const uint64_t er = __ballot((err & MPB_DEVERR_RANGE) != 0);
+  const uint64_t eo = __ballot((err & MPB_DEVERR_ORDER) != 0);
   if (lane == 0) {
-    w.pcnt[(int64_t)hm * g.upper_rows + row] = pc;
-    w.fcnt[(int64_t)hm * g.upper_rows + row] = fc;
+    const int64_t it = (int64_t)hm * g.upper_rows + row;
+    w.pcnt[it] = pc;
+    w.fcnt[it] = fc;
+    w.item_err[it] = (er ? MPB_DEVERR_RANGE : 0) | (eo ? MPB_DEVERR_ORDER : 0);
   }
 }
 
-// ---------------------------------------------------------------- scan + header
+// ---------------------------------------------------------------- scan, header, schedule
+
+namespace {
 
 __device__ inline void block_incl_scan2(int* sa, int* sb, int tid, int n) {
   for (int off = 1; off < n; off <<= 1) {
@@ -279,27 +357,192 @@ __device__ inline void block_incl_scan2(int* sa, int* sb, int tid, int n) {
   }
 }
 
-__global__ __launch_bounds__(1024) void plan_scan_kernel(PlanGeo g, PlanDev d, PlanWork w) {
+// In-place exclusive scan of n ints (LDS or global) by one workgroup of 1024
+// threads: four consecutive values per thread, a wavefront shuffle scan of
+// the thread sums and one scan of the 16 wavefront totals -- two barriers per
+// 4096 values.  Returns the total (valid in every thread).
+__device__ inline int block_exclusive_scan_inplace(int32_t* a, int64_t n, int* s_wave,
+                                                   int* s_carry) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) *s_carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < n; base += 4096) {
+    const int64_t i0 = base + 4 * (int64_t)tid;
+    int v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = i0 + u < n ? a[i0 + u] : 0;
+    const int tsum = v[0] + v[1] + v[2] + v[3];
+    const int incl = wave_incl_scan(tsum, lane);
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    if (wv == 0) {
+      const int t = lane < 16 ? s_wave[lane] : 0;
+      const int ti = wave_incl_scan(t, lane);
+      if (lane < 16) s_wave[16 + lane] = ti - t;   // exclusive prefix of wave totals
+      if (lane == 15) s_wave[32] = ti;             // block total
+    }
+    __syncthreads();
+    int run = *s_carry + s_wave[16 + wv] + incl - tsum;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u < n) a[i0 + u] = run;
+      run += v[u];
+    }
+    __syncthreads();
+    if (tid == 0) *s_carry += s_wave[32];
+    __syncthreads();
+  }
+  return *s_carry;
+}
+
+struct TaskInfo {
+  int b, h, i, rows_b, row;
+};
+
+__device__ inline TaskInfo decode_task(const PlanGeo& g, const PlanDev& d, int t) {
+  // Canonical tie order: t = Hq*cu_rows[b] + h*rows_b + i.
+  TaskInfo r;
+  r.b = sample_of_row(d.cu_rows, g.batch, t / g.heads_q);
+  const int r0 = d.cu_rows[r.b];
+  r.rows_b = d.cu_rows[r.b + 1] - r0;
+  const int rel = t - g.heads_q * r0;
+  r.h = rel / r.rows_b;
+  r.i = rel - r.h * r.rows_b;
+  r.row = r0 + r.i;
+  return r;
+}
+
+__device__ inline int task_cost(const PlanGeo& g, const PlanWork& w, int h, int row) {
+  const int hm = g.mask_heads == 1 ? 0 : h;
+  const int64_t src = (int64_t)hm * g.upper_rows + row;
+  return w.pcnt[src] + w.fcnt[src];
+}
+
+__device__ inline int task_section(const PlanGeo& g, int b, int h, int cost) {
+  if (cost == 0) return kNumSections;
+  const int group = g.heads_q / g.heads_k;
+  return (b * g.heads_k + h / group) % kNumSections;
+}
+
+// Launch slot of the r-th task of section s: sections interleaved while they
+// last; zero-cost tasks after all positive-cost ones.
+__device__ inline int launch_slot(const PlanDev& d, int s, int r) {
+  if (s >= kNumSections) return d.section_off[kNumSections] + r;
+  int slot = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < kNumSections; ++s2) {
+    const int n2 = d.section_off[s2 + 1] - d.section_off[s2];
+    slot += min(r, n2) + ((s2 < s && n2 > r) ? 1 : 0);
+  }
+  return slot;
+}
+
+__device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                  const TaskInfo& ti, int s, int pos, int rows_total) {
+  const int32_t* sd = d.seqdesc + 8 * ti.b;
+  const int qvalid = min(g.tile_q, sd[2] - ti.i * g.tile_q);
+  int32_t* wd = d.work_desc + 4 * (int64_t)pos;
+  wd[0] = ti.i;
+  wd[1] = ti.h;
+  wd[2] = ti.b;
+  wd[3] = qvalid;
+  const int hm = g.mask_heads == 1 ? 0 : ti.h;
+  const int64_t flat = (int64_t)hm * rows_total + ti.row;
+  const int64_t src = (int64_t)hm * g.upper_rows + ti.row;
+  const int p_beg = w.p_off_tmp[flat], np = w.p_off_tmp[flat + 1] - p_beg;
+  const int f_beg = w.f_off_tmp[flat], nf = w.f_off_tmp[flat + 1] - f_beg;
+  int first = -1;
+  if (np + nf > 0) {
+    const int nwords = (sd[6] + 31) >> 5;
+    for (int ww = 0; ww < nwords && first < 0; ++ww) {
+      const uint32_t vw = w.vis_bits[src * g.words_k + ww];
+      const uint32_t fw = w.full_bits[src * g.words_k + ww];
+      const uint32_t pick = np > 0 ? (vw & ~fw) : fw;  // partial list first (§6.1)
+      if (pick) first = 32 * ww + __ffs(pick) - 1;
+    }
+  }
+  int32_t* rec = d.task_rec + (int64_t)launch_slot(d, s, pos - d.section_off[s]) * kTaskRecInts;
+  rec[kRecMBlock] = ti.i;
+  rec[kRecHead] = ti.h;
+  rec[kRecBatch] = ti.b;
+  rec[kRecQValid] = qvalid;
+  rec[kRecQOff] = sd[0];
+  rec[kRecKOff] = sd[1];
+  rec[kRecQLen] = sd[2];
+  rec[kRecKLen] = sd[3];
+  rec[kRecPBeg] = p_beg;
+  rec[kRecPCnt] = np;
+  rec[kRecFBeg] = f_beg;
+  rec[kRecFCnt] = nf;
+  rec[kRecFirstTile] = first;
+  rec[kRecMaskHead] = hm;
+  rec[kRecKvHead] = ti.h / (g.heads_q / g.heads_k);
+  rec[kRecSection] = s;
+}
+
+}  // namespace
+
+// One workgroup after classification:
+//  1. §4.5 exact exclusive CSR offsets over rows flattened head-major
+//     (flat = hm * rows_total + row), off[0] = 0, off[i+1] = off[i] + cnt[i];
+//     the fixed-length geometry in closed form; the 8-value header with the
+//     OR of every device error bit, published to host-mapped memory so the
+//     host reads it with no copy command.
+//  2. §4.8 the forward schedule: section ascending, cost descending, ties in
+//     canonical order t = Hq*cu_rows[b] + h*rows_b + i; zero-cost tasks form
+//     the last section.  A stable counting sort: tasks are cut into chunks
+//     of 64 (one wavefront each) that yield each task's bucket key, its rank
+//     among equal keys of the chunk and the chunk's bucket counts; one
+//     exclusive scan of the counts laid out [bucket][chunk] gives, per
+//     (bucket, chunk), the position of the chunk's first task of that bucket.
+//     Each task is then written to the section-major schedule and, as a
+//     launch record, at its section-interleaved launch slot.
+__global__ __launch_bounds__(1024) void plan_index_kernel(PlanGeo g, PlanDev d, PlanWork w,
+                                                          int32_t* host_header, int cnt_in_lds) {
+  extern __shared__ int dyn[];
   __shared__ int sa[1024], sb[1024];
   __shared__ int carry_p, carry_f;
+  __shared__ uint32_t s_err;
+  __shared__ int s_wave[33];
+  __shared__ int s_carry;
   const int tid = threadIdx.x;
-  const int rows_total = d.cu_rows[g.batch];
+  const int lane = tid & 63, wv = tid >> 6;
+  const int rows_total = rows_total_of(g, d);
   const int n = g.mask_heads * rows_total;
   if (tid == 0) {
     carry_p = 0;
     carry_f = 0;
+    s_err = g.layout == MPB_LAYOUT_THD ? (uint32_t)w.geo_err[0] : 0u;
+  }
+  // Fixed-length geometry in closed form (§4.2: rectangular upper bound).
+  if (g.layout == MPB_LAYOUT_BSHD) {
+    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+    for (int b = tid; b < g.batch; b += 1024) {
+      int32_t* sd = d.seqdesc + 8 * b;
+      sd[0] = b * g.seqlen_q;
+      sd[1] = b * g.seqlen_k;
+      sd[2] = g.seqlen_q;
+      sd[3] = g.seqlen_k;
+      sd[4] = b * rps;
+      sd[5] = rps;
+      sd[6] = (g.seqlen_k + g.tile_k - 1) / g.tile_k;
+      sd[7] = 0;
+      d.cu_rows[b + 1] = (b + 1) * rps;
+    }
+    if (tid == 0) d.cu_rows[0] = 0;
   }
   __syncthreads();
-  // §4.5: off[0] = 0, off[i+1] = off[i] + cnt[i], over rows flattened
-  // head-major (flat = hm * rows_total + row).
+  uint32_t err = 0;
   for (int base = 0; base < n; base += 1024) {
     const int idx = base + tid;
     int a = 0, c = 0;
     if (idx < n) {
       const int hm = idx / rows_total;
       const int r = idx - hm * rows_total;
-      a = w.pcnt[(int64_t)hm * g.upper_rows + r];
-      c = w.fcnt[(int64_t)hm * g.upper_rows + r];
+      const int64_t it = (int64_t)hm * g.upper_rows + r;
+      a = w.pcnt[it];
+      c = w.fcnt[it];
+      err |= (uint32_t)w.item_err[it];
     }
     sa[tid] = a;
     sb[tid] = c;
@@ -316,320 +559,156 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(PlanGeo g, PlanDev d, P
     }
     __syncthreads();
   }
+  if (err) atomicOr(&s_err, err);
+  __syncthreads();
   if (tid == 0) {
     w.p_off_tmp[n] = carry_p;
     w.f_off_tmp[n] = carry_f;
-    d.header[0] = rows_total;
-    d.header[1] = carry_p;
-    d.header[2] = carry_f;
-  }
-  const int nbins = kNumQueues * (g.nk_max + 1);
-  for (int x = tid; x < nbins; x += 1024) w.bins[x] = 0;
-}
-
-// ---------------------------------------------------------------- schedule
-
-namespace {
-
-struct TaskInfo {
-  int b, h, i, rows_b, cost;
-};
-
-__device__ inline TaskInfo decode_task(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                       int t) {
-  // Canonical tie order: t = Hq*cu_rows[b] + h*rows_b + i.
-  TaskInfo r;
-  r.b = sample_of_row(d.cu_rows, g.batch, t / g.heads_q);
-  const int r0 = d.cu_rows[r.b];
-  r.rows_b = d.cu_rows[r.b + 1] - r0;
-  const int rel = t - g.heads_q * r0;
-  r.h = rel / r.rows_b;
-  r.i = rel - r.h * r.rows_b;
-  const int hm = g.mask_heads == 1 ? 0 : r.h;
-  const int64_t src = (int64_t)hm * g.upper_rows + r0 + r.i;
-  r.cost = w.pcnt[src] + w.fcnt[src];
-  return r;
-}
-
-__device__ inline int task_section(const PlanGeo& g, int b, int h, int cost) {
-  if (cost == 0) return kNumSections;
-  const int group = g.heads_q / g.heads_k;
-  return (b * g.heads_k + h / group) % kNumSections;
-}
-
-__device__ inline int task_bin(const PlanGeo& g, int sec, int cost) {
-  // Buckets in final order: section ascending, then cost descending.
-  return sec * (g.nk_max + 1) + (g.nk_max - cost);
-}
-
-}  // namespace
-
-__global__ __launch_bounds__(256) void plan_sched_hist_kernel(PlanGeo g, PlanDev d, PlanWork w) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int ntasks = d.cu_rows[g.batch] * g.heads_q;
-  if (t >= ntasks) return;
-  const TaskInfo ti = decode_task(g, d, w, t);
-  atomicAdd(&w.bins[task_bin(g, task_section(g, ti.b, ti.h, ti.cost), ti.cost)], 1);
-}
-
-__global__ __launch_bounds__(1024) void plan_sched_offsets_kernel(PlanGeo g, PlanDev d,
-                                                                  PlanWork w) {
-  __shared__ int sa[1024], sb[1024];
-  __shared__ int carry;
-  const int tid = threadIdx.x;
-  const int per = g.nk_max + 1;
-  const int nbins = kNumQueues * per;
-  if (tid == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < nbins; base += 1024) {
-    const int x = base + tid;
-    const int c = x < nbins ? w.bins[x] : 0;
-    sa[tid] = c;
-    sb[tid] = 0;
-    __syncthreads();
-    block_incl_scan2(sa, sb, tid, 1024);
-    const int excl = carry + sa[tid] - c;
-    if (x < nbins) {
-      w.bins[x] = excl;  // becomes the bucket's write cursor
-      if (x % per == 0) d.section_off[x / per] = excl;
+    const int32_t hdr[8] = {rows_total, carry_p, carry_f, 0, 0, 0, 0, (int32_t)s_err};
+    for (int i = 0; i < 8; ++i) {
+      d.header[i] = hdr[i];
+      __hip_atomic_store(&host_header[i], hdr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     }
-    __syncthreads();
-    if (tid == 1023) carry += sa[1023];
-    __syncthreads();
+    __threadfence_system();
   }
-  if (tid == 0) d.section_off[kNumQueues] = carry;
-}
+  if (s_err) return;  // no plan will be built (uniform: read after the barrier)
 
-// One wavefront per queue.  Section s walks the (batch, head) pairs that map
-// to it in canonical order and scatters each 64-task chunk: lanes with equal
-// buckets are grouped by ballot, ranked by lane order, and reserve their slots
-// with one atomic on the bucket cursor, so each bucket keeps tie order.
-__global__ __launch_bounds__(64) void plan_sched_scatter_kernel(PlanGeo g, PlanDev d,
-                                                                PlanWork w) {
-  const int s = blockIdx.x;
-  const int lane = threadIdx.x;
-  const int group = g.heads_q / g.heads_k;
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int zero_cursor = (s == kNumSections) ? d.section_off[kNumSections] : 0;
-  for (int b = 0; b < g.batch; ++b) {
-    const int r0 = d.cu_rows[b];
-    const int rows_b = d.cu_rows[b + 1] - r0;
-    if (rows_b == 0) continue;
-    const int32_t* sd = d.seqdesc + 8 * b;
-    const int q_len = sd[2];
-    for (int h = 0; h < g.heads_q; ++h) {
-      if (s < kNumSections && (b * g.heads_k + h / group) % kNumSections != s) continue;
-      const int hm = g.mask_heads == 1 ? 0 : h;
-      for (int i0 = 0; i0 < rows_b; i0 += 64) {
-        const int i = i0 + lane;
-        int cost = 0;
-        if (i < rows_b) {
-          const int64_t src = (int64_t)hm * g.upper_rows + r0 + i;
-          cost = w.pcnt[src] + w.fcnt[src];
-        }
-        const int qvalid = min(g.tile_q, q_len - i * g.tile_q);
-        if (s == kNumSections) {
-          const bool mine = i < rows_b && cost == 0;
-          const uint64_t m = __ballot(mine);
-          if (mine) {
-            int32_t* wd = d.work_desc + 4 * (int64_t)(zero_cursor + __popcll(m & lt));
-            wd[0] = i; wd[1] = h; wd[2] = b; wd[3] = qvalid;
-          }
-          zero_cursor += __popcll(m);
-        } else {
-          bool mine = i < rows_b && cost > 0;
-          const int key = task_bin(g, s, cost);
-          while (true) {
-            const uint64_t m = __ballot(mine);
-            if (m == 0) break;
-            const int leader = __ffsll((unsigned long long)m) - 1;
-            const int k0 = __shfl(key, leader);
-            const bool same = mine && key == k0;
-            const uint64_t match = __ballot(same);
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&w.bins[k0], __popcll(match));
-            base = __shfl(base, leader);
-            if (same) {
-              int32_t* wd = d.work_desc + 4 * (int64_t)(base + __popcll(match & lt));
-              wd[0] = i; wd[1] = h; wd[2] = b; wd[3] = qvalid;
-              mine = false;
-            }
-          }
-        }
-      }
-    }
-  }
-}
-
-// Launch order and task records.  Task t of the section-major schedule has
-// rank r in its section s; its launch slot interleaves the sections:
-// slot = sum_s' min(r, n_s') + #{s' < s : n_s' > r}; zero-cost tasks follow
-// all positive-cost ones.  Each record carries everything a forward
-// workgroup needs (see TaskRecField), so the attention kernel starts its
-// Q and first K/V loads after a single record read.
-__global__ __launch_bounds__(256) void plan_sched_records_kernel(PlanGeo g, PlanDev d,
-                                                                 PlanWork w) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  const int rows_total = d.cu_rows[g.batch];
+  // ---- schedule
   const int ntasks = rows_total * g.heads_q;
-  if (t >= ntasks) return;
-  int s = 0;
-  while (s < kNumSections && t >= d.section_off[s + 1]) ++s;
-  const int r = t - d.section_off[s];
-  int slot;
-  if (s < kNumSections) {
-    slot = 0;
-    for (int s2 = 0; s2 < kNumSections; ++s2) {
-      const int n2 = d.section_off[s2 + 1] - d.section_off[s2];
-      slot += min(r, n2) + ((s2 < s && n2 > r) ? 1 : 0);
+  const int per = g.nk_max + 1;
+  const int nc = w.nchunks;
+  int32_t* cnt = cnt_in_lds ? dyn : w.chunk_cnt;
+  if (cnt_in_lds)
+    for (int64_t x = tid; x < w.chunk_cnt_len; x += 1024) cnt[x] = 0;  // global copy: zeroed by classify
+  __syncthreads();
+  const uint64_t lt = lanes_below(lane);
+  for (int chunk = wv; chunk * 64 < ntasks; chunk += 16) {
+    const int t = chunk * 64 + lane;
+    int key = -1;
+    if (t < ntasks) {
+      const TaskInfo ti = decode_task(g, d, t);
+      const int cost = task_cost(g, w, ti.h, ti.row);
+      key = task_section(g, ti.b, ti.h, cost) * per + (g.nk_max - cost);
+      w.keys[t] = key;
     }
-  } else {
-    slot = d.section_off[kNumSections] + r;
-  }
-  const int32_t* wd = d.work_desc + 4 * (int64_t)t;
-  const int m_block = wd[0], h = wd[1], b = wd[2];
-  const int32_t* sd = d.seqdesc + 8 * b;
-  const int row = sd[4] + m_block;
-  const int hm = g.mask_heads == 1 ? 0 : h;
-  const int64_t flat = (int64_t)hm * rows_total + row;
-  const int64_t src = (int64_t)hm * g.upper_rows + row;
-  const int p_beg = w.p_off_tmp[flat], np = w.p_off_tmp[flat + 1] - p_beg;
-  const int f_beg = w.f_off_tmp[flat], nf = w.f_off_tmp[flat + 1] - f_beg;
-  int first = -1;
-  if (np + nf > 0) {
-    const int nwords = (sd[6] + 31) >> 5;
-    for (int ww = 0; ww < nwords && first < 0; ++ww) {
-      const uint32_t vw = w.vis_bits[src * g.words_k + ww];
-      const uint32_t fw = w.full_bits[src * g.words_k + ww];
-      const uint32_t pick = np > 0 ? (vw & ~fw) : fw;  // partial list first (§6.1)
-      if (pick) first = 32 * ww + __ffs(pick) - 1;
+    bool todo = t < ntasks;
+    while (true) {  // one pass per distinct key of the chunk
+      const uint64_t m = __ballot(todo);
+      if (m == 0) break;
+      const int leader = __ffsll((unsigned long long)m) - 1;
+      const int k0 = __shfl(key, leader);
+      const bool same = todo && key == k0;
+      const uint64_t match = __ballot(same);
+      if (same) {
+        w.lrank[t] = __popcll(match & lt);
+        todo = false;
+      }
+      if (lane == leader) cnt[(int64_t)k0 * nc + chunk] = __popcll(match);
     }
   }
-  int32_t* rec = d.task_rec + (int64_t)slot * kTaskRecInts;
-  rec[kRecMBlock] = m_block;
-  rec[kRecHead] = h;
-  rec[kRecBatch] = b;
-  rec[kRecQValid] = wd[3];
-  rec[kRecQOff] = sd[0];
-  rec[kRecKOff] = sd[1];
-  rec[kRecQLen] = sd[2];
-  rec[kRecKLen] = sd[3];
-  rec[kRecPBeg] = p_beg;
-  rec[kRecPCnt] = np;
-  rec[kRecFBeg] = f_beg;
-  rec[kRecFCnt] = nf;
-  rec[kRecFirstTile] = first;
-  rec[kRecMaskHead] = hm;
-  rec[kRecKvHead] = h / (g.heads_q / g.heads_k);
-  rec[kRecSection] = s;
+  __syncthreads();
+  const int total = block_exclusive_scan_inplace(cnt, w.chunk_cnt_len, s_wave, &s_carry);
+  const int64_t per_section = (int64_t)per * nc;
+  if (tid < kNumQueues) d.section_off[tid] = cnt[(int64_t)tid * per_section];
+  if (tid == 0) d.section_off[kNumQueues] = total;
+  __syncthreads();
+  for (int t = tid; t < ntasks; t += 1024) {
+    const int key = w.keys[t];
+    const int pos = cnt[(int64_t)key * nc + t / 64] + w.lrank[t];
+    write_task(g, d, w, decode_task(g, d, t), key / per, pos, rows_total);
+  }
 }
 
 // ---------------------------------------------------------------- materialize
 
-namespace {
-
-// Predicate word of one row for columns [x0, x0+32): OR over the row's
-// intervals of their overlap with the window; columns >= k_len stay 0.
-struct WordSweep {
-  int p, s, e;
-  __device__ inline void init(const RowIntervals& r) {
-    p = 0;
-    r.get(0, s, e);
-  }
-  __device__ inline uint32_t word(const RowIntervals& r, int nint, int x0, int k_len) {
-    const int x1 = min(x0 + 32, k_len);
-    if (x1 <= x0) return 0u;
-    while (p < nint && e <= x0) {
-      ++p;
-      if (p < nint) r.get(p, s, e);
-    }
-    uint32_t wbits = 0u;
-    int q = p, qs = s, qe = e;
-    while (q < nint && qs < x1) {
-      const int lo = max(qs, x0), hi = min(qe, x1);
-      if (hi > lo) wbits |= range_bits(lo - x0, hi - x0);
-      ++q;
-      if (q < nint) r.get(q, qs, qe);
-    }
-    return wbits;
-  }
-};
-
-}  // namespace
-
-template <int RPL>
+// One workgroup per (mask head, Q plan row), one thread per Q row of the
+// tile.
+//  * §4.6: exact offsets and the ascending partial and full K-tile indices
+//    (sample-local), partial and full kept apart; the partial list is also
+//    staged in LDS for the payload loop.
+//  * §5: payload word [r][c/32] bit c%32 is 1 iff column c is visible for row
+//    r.  A column is visible iff an even number of the row's endpoints are
+//    <= it, so a word starts from that parity at its first column and each
+//    endpoint inside the word flips the bits from its column on.  The
+//    thread's endpoints are staged in LDS (when [nfunc][T_Q] ints fit) and
+//    its pointer (endpoints <= current column) only moves forward, because
+//    partial tiles are listed in ascending order.  Rows past q_len write 0.
 __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
                                                                const int32_t* __restrict__ mf,
                                                                PlanDev d, PlanWork w,
-                                                               int rows_total) {
-  const int lane = wave_lane();
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+                                                               int rows_total, int stage_ep) {
+  extern __shared__ int lds[];
+  int* tiles = lds;                     // [nk_max] partial K tiles of this row
+  int* ep = lds + g.nk_max;             // [nfunc][T_Q] endpoints when staged
+  const int item = blockIdx.x;
+  const int tid = threadIdx.x;
   const int n = g.mask_heads * rows_total;
-  if (item == 0 && lane == 0) {
+  if (item == 0 && tid == 0) {
     d.p_off[n] = w.p_off_tmp[n];
     d.f_off[n] = w.f_off_tmp[n];
   }
   if (item >= n) return;
   const int hm = item / rows_total;
   const int row = item - hm * rows_total;
-  const int b = sample_of_row(d.cu_rows, g.batch, row);
-  const int32_t* sd = d.seqdesc + 8 * b;
-  const int q_off = sd[0], q_len = sd[2], k_len = sd[3], nk = sd[6];
-  const int i = row - sd[4];
-  const int nint = (g.nfunc + 1) >> 1;
   const int64_t src = (int64_t)hm * g.upper_rows + row;
   const int p_begin = w.p_off_tmp[item];
   const int f_begin = w.f_off_tmp[item];
-  if (lane == 0) {
+  const int np = w.p_off_tmp[item + 1] - p_begin;
+  const RowGeo rg = row_geometry(g, d, row);
+  if (tid == 0) {
     d.p_off[item] = p_begin;
     d.f_off[item] = f_begin;
   }
-  // §4.6: sample-local K-tile indices, ascending, partial and full apart.
-  const int nwords = (nk + 31) >> 5;
-  int pb = p_begin, fb = f_begin;
-  for (int ww = 0; ww < nwords; ++ww) {
-    const uint32_t vw = w.vis_bits[src * g.words_k + ww];
-    const uint32_t fw = w.full_bits[src * g.words_k + ww];
-    const uint32_t pw = vw & ~fw;
-    if (lane < 32) {
-      const uint32_t bit = 1u << lane;
-      const uint32_t below = bit - 1u;
-      if (pw & bit) d.p_idx[pb + __popc(pw & below)] = 32 * ww + lane;
-      if (fw & bit) d.f_idx[fb + __popc(fw & below)] = 32 * ww + lane;
+  if (tid < 64) {
+    const int nwords = (rg.nk + 31) >> 5;
+    int pb = 0, fb = f_begin;
+    for (int ww = 0; ww < nwords; ++ww) {
+      const uint32_t vw = w.vis_bits[src * g.words_k + ww];
+      const uint32_t fw = w.full_bits[src * g.words_k + ww];
+      const uint32_t pw = vw & ~fw;
+      if (tid < 32) {
+        const uint32_t bit = 1u << tid;
+        const uint32_t below = bit - 1u;
+        if (pw & bit) {
+          const int k = pb + __popc(pw & below);
+          d.p_idx[p_begin + k] = 32 * ww + tid;
+          tiles[k] = 32 * ww + tid;
+        }
+        if (fw & bit) d.f_idx[fb + __popc(fw & below)] = 32 * ww + tid;
+      }
+      pb += __popc(pw);
+      fb += __popc(fw);
     }
-    pb += __popc(pw);
-    fb += __popc(fw);
   }
-  // §5: one predicate bit per score element of each partial tile; word
-  // [r][c/32], bit c%32; rows past q_len and columns past k_len are 0.
-  bool valid[RPL];
-  RowIntervals ri[RPL];
-  WordSweep sw[RPL];
-  for (int t = 0; t < RPL; ++t) {
-    const int rho = lane + 64 * t;
-    valid[t] = rho < g.tile_q && i * g.tile_q + rho < q_len;
-    const int64_t tok = (int64_t)q_off + (int64_t)i * g.tile_q + rho;
-    ri[t].col = mf + (int64_t)hm * g.nfunc * g.total_q + (valid[t] ? tok : 0);
-    ri[t].stride = g.total_q;
-    if (valid[t]) sw[t].init(ri[t]);
-  }
-  int pos = p_begin;
-  for (int ww = 0; ww < nwords; ++ww) {
-    uint32_t pw = w.vis_bits[src * g.words_k + ww] & ~w.full_bits[src * g.words_k + ww];
-    while (pw) {
-      const int jb = __ffs(pw) - 1;
-      pw &= pw - 1u;
-      const int c0 = (32 * ww + jb) * g.tile_k;
-      uint32_t* dst = d.p_masks + (int64_t)pos * g.tile_q * g.words_tile;
-      for (int t = 0; t < RPL; ++t) {
-        const int rho = lane + 64 * t;
-        if (rho >= g.tile_q) continue;
-        for (int x = 0; x < g.words_tile; ++x) {
-          const uint32_t word = valid[t] ? sw[t].word(ri[t], nint, c0 + 32 * x, k_len) : 0u;
-          dst[(int64_t)rho * g.words_tile + x] = word;
+  if (np == 0) return;  // uniform; no payload
+  const int rho = tid;
+  const bool is_row = rho < g.tile_q;
+  const bool valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
+  const int32_t* col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off +
+                       (int64_t)rg.i * g.tile_q + (valid ? rho : 0);
+  if (stage_ep && valid)
+    for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
+  __syncthreads();  // the partial tile list is complete
+  auto E = [&](int f) -> int {
+    return stage_ep ? ep[f * g.tile_q + rho] : col[(int64_t)f * g.total_q];
+  };
+  int ptr = 0;
+  for (int k = 0; k < np; ++k) {
+    const int c0 = tiles[k] * g.tile_k;
+    uint32_t* dst = d.p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
+    for (int x = 0; x < g.words_tile; ++x) {
+      uint32_t word = 0u;
+      if (valid) {
+        const int c = c0 + 32 * x;
+        while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
+        word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
+        for (int f = ptr; f < g.nfunc; ++f) {
+          const int e = E(f);
+          if (e >= c + 32) break;
+          word ^= 0xFFFFFFFFu << (e - c);
         }
       }
-      ++pos;
+      if (is_row) dst[x] = word;
     }
   }
 }
@@ -639,8 +718,9 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
 static inline int rows_per_lane(int tile_q) { return tile_q <= 64 ? 1 : tile_q / 64; }
 
 hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
-                                const PlanDev& d, hipStream_t s) {
-  hipLaunchKernelGGL(plan_geometry_kernel, dim3(1), dim3(1024), 0, s, g, cu_q_in, cu_k_in, d);
+                                const PlanDev& d, const PlanWork& w, hipStream_t s) {
+  if (g.layout != MPB_LAYOUT_THD) return hipSuccess;
+  hipLaunchKernelGGL(plan_geometry_kernel, dim3(1), dim3(1024), 0, s, g, cu_q_in, cu_k_in, d, w);
   return hipGetLastError();
 }
 
@@ -648,46 +728,38 @@ hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, cons
                                 const PlanWork& w, hipStream_t s) {
   const int64_t items = (int64_t)g.mask_heads * g.upper_rows;
   if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((items + 3) / 4));
+  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
   switch (rows_per_lane(g.tile_q)) {
-    case 1: hipLaunchKernelGGL(plan_classify_kernel<1>, grid, dim3(256), 0, s, g, mask_func, d, w); break;
-    case 2: hipLaunchKernelGGL(plan_classify_kernel<2>, grid, dim3(256), 0, s, g, mask_func, d, w); break;
-    case 4: hipLaunchKernelGGL(plan_classify_kernel<4>, grid, dim3(256), 0, s, g, mask_func, d, w); break;
+    case 1: hipLaunchKernelGGL(plan_classify_kernel<1>, grid, block, 0, s, g, mask_func, d, w); break;
+    case 2: hipLaunchKernelGGL(plan_classify_kernel<2>, grid, block, 0, s, g, mask_func, d, w); break;
+    case 4: hipLaunchKernelGGL(plan_classify_kernel<4>, grid, block, 0, s, g, mask_func, d, w); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_plan_scan(const PlanGeo& g, const PlanDev& d, const PlanWork& w, hipStream_t s) {
-  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, s, g, d, w);
-  return hipGetLastError();
+size_t index_kernel_lds(const PlanWork& w) {
+  const size_t bytes = (size_t)w.chunk_cnt_len * 4;
+  return bytes <= 40 * 1024 ? bytes : 0;
 }
 
-hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                int32_t upper_tasks, hipStream_t s) {
-  if (upper_tasks > 0) {
-    hipLaunchKernelGGL(plan_sched_hist_kernel, dim3((upper_tasks + 255) / 256), dim3(256), 0, s,
-                       g, d, w);
-  }
-  hipLaunchKernelGGL(plan_sched_offsets_kernel, dim3(1), dim3(1024), 0, s, g, d, w);
-  hipLaunchKernelGGL(plan_sched_scatter_kernel, dim3(kNumQueues), dim3(64), 0, s, g, d, w);
-  if (upper_tasks > 0) {
-    hipLaunchKernelGGL(plan_sched_records_kernel, dim3((upper_tasks + 255) / 256), dim3(256), 0,
-                       s, g, d, w);
-  }
+hipError_t launch_plan_index(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                             int32_t* host_header, hipStream_t s) {
+  const size_t lds = index_kernel_lds(w);
+  hipLaunchKernelGGL(plan_index_kernel, dim3(1), dim3(1024), lds, s, g, d, w, host_header,
+                     lds > 0 ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
                                    const PlanWork& w, int32_t rows_total, hipStream_t s) {
   const int64_t items = (int64_t)g.mask_heads * rows_total;
-  const dim3 grid((unsigned)((items > 0 ? items + 3 : 4) / 4));
-  switch (rows_per_lane(g.tile_q)) {
-    case 1: hipLaunchKernelGGL(plan_materialize_kernel<1>, grid, dim3(256), 0, s, g, mask_func, d, w, rows_total); break;
-    case 2: hipLaunchKernelGGL(plan_materialize_kernel<2>, grid, dim3(256), 0, s, g, mask_func, d, w, rows_total); break;
-    case 4: hipLaunchKernelGGL(plan_materialize_kernel<4>, grid, dim3(256), 0, s, g, mask_func, d, w, rows_total); break;
-    default: return hipErrorInvalidValue;
-  }
+  const int threads = g.tile_q < 64 ? 64 : g.tile_q;
+  const size_t ep_bytes = (size_t)g.nfunc * g.tile_q * 4;
+  const int stage = ep_bytes <= 32 * 1024 ? 1 : 0;
+  const size_t lds = (size_t)g.nk_max * 4 + (stage ? ep_bytes : 0);
+  hipLaunchKernelGGL(plan_materialize_kernel, dim3((unsigned)(items > 0 ? items : 1)),
+                     dim3(threads), lds, s, g, mask_func, d, w, rows_total, stage);
   return hipGetLastError();
 }
 

@@ -2,11 +2,11 @@
 //
 // mask_plan_build follows the stage order of "Flex Attention Mask Plan
 // Design" §4: host structural validation and consumer resolution (§4.1) with
-// no elementwise work on the host; GPU geometry, classification and scan; one
-// 8-value header read-back (§4.5) that both sizes the exact allocation and
-// reports device-side validation errors; then materialisation (§4.6) and the
-// forward schedule (§4.8).  The schedule kernels are enqueued right after the
-// header copy so they overlap the host's wait and allocation.
+// no elementwise work on the host; on the GPU the Varlen geometry, the Q2K
+// classification, and one kernel for the count scan, the header and the
+// forward schedule (§4.5, §4.8); one 8-value header read-back (through
+// host-mapped memory, no copy command) that both sizes the exact allocation
+// and reports device-side validation errors; then materialisation (§4.6).
 //
 // Device memory comes from a per-device stream-ordered pool owned by the
 // library (allocation and release are enqueued on the caller's stream), so a
@@ -88,19 +88,28 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// ---- per-thread pinned header slot and completion event
+// ---- per-thread host-mapped header slot and completion event
+//
+// The index kernel writes the 8-value header straight into this pinned,
+// coherent, device-mapped host memory; the host reads it after the kernel's
+// completion event, so the header read-back needs no copy command.
 
 struct ThreadSlot {
   int32_t* pinned = nullptr;
+  int32_t* pinned_dev = nullptr;
   hipEvent_t ev[64] = {};
 };
 thread_local ThreadSlot g_slot;
 
-hipError_t thread_slot(int dev, int32_t** pinned, hipEvent_t* ev) {
+hipError_t thread_slot(int dev, volatile int32_t** pinned, int32_t** pinned_dev, hipEvent_t* ev) {
   if (!g_slot.pinned) {
-    hipError_t e = hipHostMalloc((void**)&g_slot.pinned, 8 * sizeof(int32_t), hipHostMallocDefault);
+    hipError_t e = hipHostMalloc((void**)&g_slot.pinned, 8 * sizeof(int32_t),
+                                 hipHostMallocMapped | hipHostMallocCoherent);
+    if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&g_slot.pinned_dev, g_slot.pinned, 0);
     if (e != hipSuccess) {
+      if (g_slot.pinned) hipHostFree(g_slot.pinned);
       g_slot.pinned = nullptr;
+      g_slot.pinned_dev = nullptr;
       return e;
     }
   }
@@ -112,6 +121,7 @@ hipError_t thread_slot(int dev, int32_t** pinned, hipEvent_t* ev) {
     }
   }
   *pinned = g_slot.pinned;
+  *pinned_dev = g_slot.pinned_dev;
   *ev = g_slot.ev[dev];
   return hipSuccess;
 }
@@ -261,6 +271,9 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
                             : ((int64_t)p.total_q + (int64_t)p.batch * (tq - 1)) / tq;
   const int64_t nk_max = ((int64_t)p.seqlen_k + tk - 1) / tk;
   const int64_t words_k = nk_max > 0 ? (nk_max + 31) / 32 : 1;
+  if (nk_max > kMaxKTiles)
+    return fail(MPB_ERR_UNSUPPORTED, "seqlen_k %d spans more than %d K tiles of %d", p.seqlen_k,
+                kMaxKTiles, tk);
   if (upper * p.mask_heads >= ((int64_t)1 << 31) || upper * p.heads_q >= ((int64_t)1 << 31) ||
       upper * p.mask_heads * words_k >= ((int64_t)1 << 31))
     return fail(MPB_ERR_UNSUPPORTED, "too many plan rows");
@@ -275,9 +288,11 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   if (e != hipSuccess) return device_status(e, "hipGetDevice");
   hipMemPool_t pool;
   if ((e = device_pool(dev, &pool)) != hipSuccess) return device_status(e, "memory pool");
-  int32_t* pinned = nullptr;
+  volatile int32_t* pinned = nullptr;
+  int32_t* pinned_dev = nullptr;
   hipEvent_t ev;
-  if ((e = thread_slot(dev, &pinned, &ev)) != hipSuccess) return device_status(e, "host slot");
+  if ((e = thread_slot(dev, &pinned, &pinned_dev, &ev)) != hipSuccess)
+    return device_status(e, "host slot");
 
   const int64_t items_upper = upper * p.mask_heads;
   Carver cg;
@@ -296,7 +311,14 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   const size_t o_fcnt = cw.take<int32_t>(items_upper);
   const size_t o_poff = cw.take<int32_t>(items_upper + 1);
   const size_t o_foff = cw.take<int32_t>(items_upper + 1);
-  const size_t o_bins = cw.take<int32_t>(kNumQueues * (nk_max + 1));
+  const int64_t upper_tasks = upper * p.heads_q;
+  const int64_t nchunks = (upper_tasks + 63) / 64;
+  const int64_t cnt_len = (int64_t)kNumQueues * (nk_max + 1) * nchunks;
+  const size_t o_cnt = cw.take<int32_t>(cnt_len);
+  const size_t o_lrank = cw.take<int32_t>(upper_tasks);
+  const size_t o_ierr = cw.take<int32_t>(items_upper);
+  const size_t o_gerr = cw.take<int32_t>(1);
+  const size_t o_keys = cw.take<int32_t>(upper * p.heads_q);
 
   void* geo_block = nullptr;
   void* work_block = nullptr;
@@ -329,17 +351,20 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   w.fcnt = at<int32_t>(work_block, o_fcnt);
   w.p_off_tmp = at<int32_t>(work_block, o_poff);
   w.f_off_tmp = at<int32_t>(work_block, o_foff);
-  w.bins = at<int32_t>(work_block, o_bins);
+  w.chunk_cnt = at<int32_t>(work_block, o_cnt);
+  w.chunk_cnt_len = cnt_len;
+  w.nchunks = (int32_t)nchunks;
+  w.lrank = at<int32_t>(work_block, o_lrank);
+  w.item_err = at<int32_t>(work_block, o_ierr);
+  w.geo_err = at<int32_t>(work_block, o_gerr);
+  w.keys = at<int32_t>(work_block, o_keys);
 
   const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
   const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
-  if ((e = launch_plan_geometry(g, cq, ck, d, s)) != hipSuccess ||
+  if ((e = launch_plan_geometry(g, cq, ck, d, w, s)) != hipSuccess ||
       (e = launch_plan_classify(g, mask_func, d, w, s)) != hipSuccess ||
-      (e = launch_plan_scan(g, d, w, s)) != hipSuccess ||
-      (e = hipMemcpyAsync(pinned, d.header, 8 * sizeof(int32_t), hipMemcpyDeviceToHost, s)) !=
-          hipSuccess ||
-      (e = hipEventRecord(ev, s)) != hipSuccess ||
-      (e = launch_plan_schedule(g, d, w, (int32_t)(upper * p.heads_q), s)) != hipSuccess) {
+      (e = launch_plan_index(g, d, w, pinned_dev, s)) != hipSuccess ||
+      (e = hipEventRecord(ev, s)) != hipSuccess) {
     release();
     return device_status(e, "planner launch");
   }

@@ -88,6 +88,7 @@ INVALID, UNSUPPORTED = 1, 7
     (dict(head_dim=96), UNSUPPORTED), (dict(tile_q=48), UNSUPPORTED),
     (dict(tile_k=48), UNSUPPORTED), (dict(tile_q=256, tile_k=256), UNSUPPORTED),
     (dict(seqlen_q=-1), INVALID),
+    (dict(seqlen_k=8192 * 64, total_k=2 * 8192 * 64), UNSUPPORTED),   # > 8191 K tiles
 ])
 def test_host_refusals_before_any_launch(lib, kw, status):
     st, out = _build(lib, _good(**kw))
