@@ -123,13 +123,20 @@ def main():
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     keep = []
+    host_build = host_fwd = 0.0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        ta = time.perf_counter()
         plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        tb = time.perf_counter()
         ev[i][0].record(stream)
+        tc = time.perf_counter()
         mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+        td = time.perf_counter()
         ev[i][1].record(stream)
+        host_build += tb - ta
+        host_fwd += td - tc
         keep.append(plan)          # released after the timed region
         if len(keep) > 2:
             keep.pop(0).close()
@@ -212,6 +219,8 @@ def main():
             "force_partial_us": None if abl is None else round(abl, 2),
         },
         "plan": {"build_us_host": round(plan_us, 1), **stats},
+        "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
+                 "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }
     if not args.no_cpu_baseline:
         secs, passes, threads = cpu_baseline(w, args.cpu_seconds)

@@ -122,17 +122,24 @@ typedef struct mpb_score_mod {
 /* mask_plan_build [MPD §4]: host structural validation and consumer
  * resolution (§4.1), then GPU stages: Varlen geometry (§4.2), Q2K
  * classification with endpoint validation (§4.3), count scan and header
- * (§4.5), one 8-value header read-back with a single stream synchronisation,
- * exact allocation, Q2K materialisation of the partial/full CSR and the packed
- * predicates (§4.6, §5) and the forward schedule (§4.8).
+ * (§4.5), the forward schedule (§4.8), one 8-value header read-back (the
+ * call waits on the host until the header has landed in host-mapped memory,
+ * not for the stream to drain), exact allocation, and Q2K materialisation of
+ * the partial/full CSR and the packed predicates (§4.6, §5).
  *
  *   mask_func    device int32 [mask_heads][nfunc][total_q]; column t holds the
  *                endpoints F0..F(nfunc-1) of Q token t, sample-local K
  *                positions; row t sees [0,F0) U [F1,F2) U ... [MPD §2].
- *                It may be freed once the call returns.
+ *                Work enqueued on `stream` still reads it after the call
+ *                returns: release it in stream order (as torch's caching
+ *                allocator does) or after synchronising the stream.
  *   cu_seqlens_q/k  device int32 [batch+1] for THD; ignored (may be NULL) for
- *                BSHD.  Validated on the GPU [MPD §3.2].
- *   stream       work is enqueued here; the call synchronises on it once.
+ *                BSHD.  Validated on the GPU [MPD §3.2].  Same lifetime rule.
+ *   stream       work is enqueued here.  The plan's arrays are complete in
+ *                this stream's order: a forward on another stream must be
+ *                ordered after it (event or synchronisation).  Builds of one
+ *                host thread share a device workspace; a build on a stream
+ *                other than the previous build's first waits for that stream.
  *   out          receives the plan, or NULL on any failure (nothing leaks).
  * Errors: host-decidable problems return MPB_ERR_INVALID_ARGUMENT or
  * MPB_ERR_UNSUPPORTED before any launch; endpoint and prefix violations found

@@ -124,13 +124,11 @@ def _stream_handle(stream) -> int:
 def _dev_ptr(t: Optional[torch.Tensor], what: str, dtype=None):
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError("%s must be a device tensor" % what)
-    if not t.is_contiguous():
-        raise ValueError("%s must be contiguous" % what)
-    if dtype is not None and t.dtype != dtype:
-        raise ValueError("%s must be %s, got %s" % (what, dtype, t.dtype))
-    return ctypes.c_void_p(t.data_ptr())
+    if not (t.is_cuda and t.is_contiguous()) or (dtype is not None and t.dtype != dtype):
+        raise ValueError("%s must be a contiguous device tensor%s (got %s, %s, contiguous=%s)"
+                         % (what, "" if dtype is None else " of " + str(dtype), t.device,
+                            t.dtype, t.is_contiguous()))
+    return t.data_ptr()
 
 
 def make_problem(layout, dtype, batch, seqlen_q, seqlen_k, total_q, total_k, heads_q, heads_k,
@@ -142,15 +140,33 @@ def make_problem(layout, dtype, batch, seqlen_q, seqlen_k, total_q, total_k, hea
 class MaskPlan:
     """Owner of an opaque mpb_plan handle (immutable device plan)."""
 
-    def __init__(self, handle: int, stream_handle: int):
+    def __init__(self, handle: int, stream_handle: int, problem: Problem):
         self._h = ctypes.c_void_p(handle)
         self._stream = stream_handle
-        self.info = mask_plan_info(self)
-        self.problem = self.info.problem
+        self._bound = Problem.from_buffer_copy(problem)   # geometry the plan was built for
+        self._info = None
+        self._ws = None
 
     @property
     def handle(self):
         return self._h
+
+    @property
+    def info(self) -> "PlanInfo":
+        if self._info is None:
+            self._info = mask_plan_info(self)
+        return self._info
+
+    @property
+    def problem(self) -> Problem:
+        """The plan binding, with the physical tile resolved."""
+        return self.info.problem
+
+    @property
+    def workspace_bytes(self) -> int:
+        if self._ws is None:
+            self._ws = int(_lib.flex_attn_fwd_workspace_size(self._h))
+        return self._ws
 
     def header(self):
         return list(self.info.header)
@@ -179,9 +195,8 @@ def mask_plan_build(problem: Problem, mask_func: torch.Tensor,
     ck = _dev_ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32)
     s = _stream_handle(stream)
     out = ctypes.c_void_p()
-    _check(_lib.mask_plan_build(ctypes.byref(problem), mf, cq, ck, ctypes.c_void_p(s),
-                                ctypes.byref(out)))
-    return MaskPlan(out.value, s)
+    _check(_lib.mask_plan_build(ctypes.byref(problem), mf, cq, ck, s, ctypes.byref(out)))
+    return MaskPlan(out.value, s, problem)
 
 
 def mask_plan_destroy(plan: MaskPlan):
@@ -234,7 +249,7 @@ def flex_attn_fwd_workspace_size(plan: MaskPlan) -> int:
 def _call_problem(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor) -> Problem:
     """Geometry of the call as the tensors show it (checked against the plan
     binding by the library)."""
-    p = plan.problem
+    p = plan._bound
     dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else (DTYPE_FP32 if q.dtype == torch.float32
                                                      else -1)
     if p.layout == LAYOUT_BSHD:
@@ -268,7 +283,7 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
-    need = flex_attn_fwd_workspace_size(plan)
+    need = plan.workspace_bytes
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     mod = None
@@ -282,7 +297,7 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
             _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
             ctypes.byref(mod) if mod is not None else None, _dev_ptr(workspace, "workspace"),
             0 if workspace is None else workspace.numel() * workspace.element_size(),
-            ctypes.c_void_p(_stream_handle(stream)))
+            _stream_handle(stream))
     if force_partial:
         _check(_lib.flex_attn_fwd_ablation(*args, 1))
     else:

@@ -67,30 +67,50 @@ struct PlanWork {
   uint32_t* full_bits;
   int32_t* pcnt;         // [Hmask][upper_rows]
   int32_t* fcnt;
+  int32_t* first_tile;   // [Hmask][upper_rows] first listed K tile (partial list first), -1 if none
   int32_t* p_off_tmp;    // [Hmask*upper_rows+1] (compact head-major order)
   int32_t* f_off_tmp;
   int32_t* item_err;     // [Hmask][upper_rows] endpoint error bits per classified row
   int32_t* geo_err;      // [1] cu_seqlens error bit (THD)
-  int32_t* keys;         // [upper_rows*Hq] schedule bucket of each task
-  int32_t* lrank;        // [upper_rows*Hq] rank among equal keys of its 64-task chunk
-  int32_t* chunk_cnt;    // [buckets][nchunks] counts, then first positions
-  int64_t chunk_cnt_len; // buckets * nchunks, buckets = kNumQueues * (nk_max + 1)
-  int32_t nchunks;       // ceil(upper_rows*Hq / 64)
+  int32_t* lrank;        // [Hmask*upper_rows] rank among equal costs within its 64-row chunk
+  int32_t* order;        // [Hmask*upper_rows] rows sorted by descending cost
+  int32_t* row_base;     // [Hmask*upper_rows][kNumQueues] first in-section position of each row's tasks
+  int32_t* chunk_cnt;    // [nk_max+1][nchunks] counts, then first positions (when not in LDS)
+  int32_t nchunks;       // ceil(Hmask*upper_rows / 64)
 };
 
-// Longest sample the planner handles, in K tiles: bounds the schedule's
-// (section, cost) bucket count, which sizes the count matrix of its sort.
+// Longest sample the planner handles, in K tiles: bounds the cost range of
+// the schedule's counting sort.
 constexpr int kMaxKTiles = 8191;
+
+// Host-mapped slot the classify kernel publishes the header into: values
+// [0, 8) and, last, the build's sequence number at kHeaderSeq.
+constexpr int kHeaderSeq = 8;
+constexpr int kHostSlotInts = 16;
 
 // ---- planner launchers (plan_kernels.hip) ----
 hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
                                 const PlanDev& d, const PlanWork& w, hipStream_t s);
+// `arrive` is a device counter that is 0 on entry and left 0 on exit; the last
+// workgroup to finish computes the offsets and publishes the header (with
+// `seq`) to `host_slot` (host-mapped).
 hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
-                                const PlanWork& w, hipStream_t s);
-hipError_t launch_plan_index(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                             int32_t* host_header, hipStream_t s);
-hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
-                                   const PlanWork& w, int32_t rows_total, hipStream_t s);
+                                const PlanWork& w, int32_t* arrive, int32_t* host_slot,
+                                int32_t seq, hipStream_t s);
+hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                hipStream_t s);
+// Segments of plan metadata copied from the staging arrays into the plan
+// block by the materialize launch: segment i covers flat elements
+// [end[i-1], end[i]).
+struct MetaCopy {
+  const int32_t* src[8];
+  int32_t* dst[8];
+  int64_t end[8];
+  int64_t total;
+};
+hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& st,
+                                   const PlanDev& d, const PlanWork& w, int32_t rows_total,
+                                   hipStream_t s);
 
 // ---- attention ----
 enum ModKind : int32_t {

@@ -9,16 +9,18 @@
 //                           (mask head, Q plan row).  Each lane reads its
 //                           row's intervals once (coalesced across lanes),
 //                           validates them (§2 order and bounds), merges
-//                           touching intervals and records the K tiles each
-//                           run touches / fully covers in LDS difference
-//                           arrays; a wavefront prefix scan then gives, per
-//                           tile, how many rows see it at all and how many see
-//                           all of it: any > 0 is visible, all == T_Q is full.
-//   plan_index_kernel       one workgroup: §4.5 exact exclusive CSR offsets
-//                           and the 8-value allocation header (device errors
-//                           OR-ed in, published to host-mapped memory), then
-//                           §4.8 the forward schedule as a stable counting sort
-//                           and the section-interleaved launch records.
+//                           touching intervals and ORs / ANDs the K tiles each
+//                           run touches / fully covers across the wavefront:
+//                           any row touching a tile makes it visible, all T_Q
+//                           rows covering it make it full.  The workgroup
+//                           that finishes last then computes the §4.5 exact
+//                           CSR offsets and the 8-value allocation header
+//                           (device errors OR-ed in) and publishes the header
+//                           to host-mapped memory.
+//   plan_schedule_kernel    one workgroup: §4.8 the forward schedule by
+//                           bounded counting (cost ranks, per-section scans)
+//                           and the section-interleaved launch records; runs
+//                           while the host reads the header and allocates.
 //   plan_materialize_kernel §4.6 / §5 Q2K materialisation: ascending partial
 //                           and full K-tile indices, and one predicate word per
 //                           (row, 32 columns) of each partial tile.
@@ -204,33 +206,20 @@ __device__ inline uint32_t wave_and(uint32_t x) {
   return x;
 }
 
-}  // namespace
-
-// One wavefront per (mask head, Q plan row); lanes own rows lane + 64t.
-// Tiles are handled in windows of 128 (four 32-bit words): for each window a
-// lane walks its row's intervals (read 8 at a time, coalesced across lanes),
-// merges touching intervals into runs, and ORs the tiles each run touches
-// ("any") or fully covers ("full") into its words.  Across the wavefront the
-// "any" words are OR-ed and the "full" words AND-ed: a tile is visible if any
-// row sees part of it and full if every one of the T_Q rows covers it, which
-// needs every row in bounds (rows past q_len contribute nothing) and the tile
-// inside k_len (no run extends past k_len).  §2 order and bounds of every
-// endpoint are checked on the way.
+// Classification of one (mask head, Q plan row): one wavefront, lanes own rows
+// lane + 64t.  Tiles are handled in windows of 128 (four 32-bit words): for
+// each window a lane walks its row's intervals (read 8 at a time, coalesced
+// across lanes), merges touching intervals into runs, and ORs the tiles each
+// run touches ("any") or fully covers ("full") into its words.  Across the
+// wavefront the "any" words are OR-ed and the "full" words AND-ed: a tile is
+// visible if any row sees part of it and full if every one of the T_Q rows
+// covers it, which needs every row in bounds (rows past q_len contribute
+// nothing) and the tile inside k_len (no run extends past k_len).  §2 order
+// and bounds of every endpoint are checked on the way.
 template <int RPL>
-__global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
-                                                            const int32_t* __restrict__ mf,
-                                                            PlanDev d, PlanWork w) {
-  const int lane = wave_lane();
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  // Side job: clear the schedule's [bucket][chunk] count matrix (read only
-  // by the schedule kernels, which run after this kernel).
-  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < w.chunk_cnt_len;
-       x += (int64_t)gridDim.x * blockDim.x)
-    w.chunk_cnt[x] = 0;
-  const int hm = item / g.upper_rows;
-  const int row = item - hm * g.upper_rows;
-  if (hm >= g.mask_heads) return;
-  if (row >= rows_total_of(g, d)) return;
+__device__ inline void classify_row(const PlanGeo& g, const int32_t* __restrict__ mf,
+                                    const PlanDev& d, const PlanWork& w, int hm, int row,
+                                    int lane) {
   const RowGeo rg = row_geometry(g, d, row);
   const int nk = rg.nk;
   const int T = g.tile_k;
@@ -248,7 +237,7 @@ __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
   }
 
   uint32_t err = 0;
-  int pc = 0, fc = 0;
+  int pc = 0, fc = 0, first_p = -1, first_f = -1;
   const int64_t wbase = ((int64_t)hm * g.upper_rows + row) * g.words_k;
   for (int tg = 0; tg < nk; tg += 128) {
     uint32_t any_m[4] = {0u, 0u, 0u, 0u};
@@ -320,8 +309,11 @@ __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
       const uint32_t live = w0 >= nk ? 0u : (nk - w0 >= 32 ? ~0u : ((1u << (nk - w0)) - 1u));
       vis_w[x] &= live;
       full_w[x] &= vis_w[x];
-      pc += __popc(vis_w[x] & ~full_w[x]);
+      const uint32_t part = vis_w[x] & ~full_w[x];
+      pc += __popc(part);
       fc += __popc(full_w[x]);
+      if (first_p < 0 && part) first_p = w0 + __ffs(part) - 1;
+      if (first_f < 0 && full_w[x]) first_f = w0 + __ffs(full_w[x]) - 1;
     }
     if (lane < 4) {
       const int x = lane;
@@ -338,24 +330,140 @@ __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
     const int64_t it = (int64_t)hm * g.upper_rows + row;
     w.pcnt[it] = pc;
     w.fcnt[it] = fc;
+    w.first_tile[it] = pc > 0 ? first_p : first_f;   // the partial list is traversed first
     w.item_err[it] = (er ? MPB_DEVERR_RANGE : 0) | (eo ? MPB_DEVERR_ORDER : 0);
   }
 }
 
-// ---------------------------------------------------------------- scan, header, schedule
-
-namespace {
-
-__device__ inline void block_incl_scan2(int* sa, int* sb, int tid, int n) {
-  for (int off = 1; off < n; off <<= 1) {
-    const int va = tid >= off ? sa[tid - off] : 0;
-    const int vb = tid >= off ? sb[tid - off] : 0;
+// §4.5 after classification, by the last workgroup of the classify launch:
+// exact exclusive CSR offsets over rows flattened head-major
+// (flat = hm * rows_total + row; off[0] = 0, off[i+1] = off[i] + cnt[i]) and
+// the 8-value allocation header {rows, partial blocks, full blocks, 0, 0, 0,
+// 0, OR of every device error bit}.  The header goes to the plan and to the
+// host-mapped slot, its values first and the build's sequence number last,
+// so the host can read it the moment it lands.  Four values per thread, a
+// wavefront scan of the thread sums and a pass over the NT/64 wavefront
+// totals in LDS.
+template <int NT>
+__device__ inline void publish_offsets(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                       int32_t* host_slot, int32_t seq, int* s_wp, int* s_wf,
+                                       uint32_t* s_err) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int rows_total = rows_total_of(g, d);
+  const int n = g.mask_heads * rows_total;
+  uint32_t err = 0;
+  int carry_p = 0, carry_f = 0;
+  for (int base = 0; base < n; base += 4 * NT) {
+    const int i0 = base + 4 * tid;
+    int vp[4], vf[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u;
+      vp[u] = 0;
+      vf[u] = 0;
+      if (i < n) {
+        const int hm = i / rows_total;
+        const int64_t src = (int64_t)hm * g.upper_rows + (i - hm * rows_total);
+        vp[u] = w.pcnt[src];
+        vf[u] = w.fcnt[src];
+        err |= (uint32_t)w.item_err[src];
+      }
+    }
+    const int tp = vp[0] + vp[1] + vp[2] + vp[3];
+    const int tf = vf[0] + vf[1] + vf[2] + vf[3];
+    const int ip = wave_incl_scan(tp, lane);
+    const int jf = wave_incl_scan(tf, lane);
+    if (lane == 63) {
+      s_wp[wv] = ip;
+      s_wf[wv] = jf;
+    }
     __syncthreads();
-    sa[tid] += va;
-    sb[tid] += vb;
-    __syncthreads();
+    int pre_p = 0, pre_f = 0, tot_p = 0, tot_f = 0;
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+      const int a = s_wp[x], c = s_wf[x];
+      if (x < wv) {
+        pre_p += a;
+        pre_f += c;
+      }
+      tot_p += a;
+      tot_f += c;
+    }
+    int run_p = carry_p + pre_p + ip - tp, run_f = carry_f + pre_f + jf - tf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u < n) {
+        w.p_off_tmp[i0 + u] = run_p;
+        w.f_off_tmp[i0 + u] = run_f;
+      }
+      run_p += vp[u];
+      run_f += vf[u];
+    }
+    carry_p += tot_p;
+    carry_f += tot_f;
+    __syncthreads();  // s_wp / s_wf are reused
+  }
+  if (tid == 0 && g.layout == MPB_LAYOUT_THD) err |= (uint32_t)w.geo_err[0];
+  if (err) atomicOr(s_err, err);
+  __syncthreads();
+  if (tid == 0) {
+    w.p_off_tmp[n] = carry_p;
+    w.f_off_tmp[n] = carry_f;
+    const int32_t hdr[8] = {rows_total, carry_p, carry_f, 0, 0, 0, 0, (int32_t)*s_err};
+    for (int i = 0; i < 8; ++i) {
+      d.header[i] = hdr[i];
+      __hip_atomic_store(&host_slot[i], hdr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    __hip_atomic_store(&host_slot[kHeaderSeq], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
 }
+
+}  // namespace
+
+// §4.3 Q2K classification, one wavefront per (mask head, Q plan row), then
+// §4.5 offsets and header by whichever workgroup finishes last: every
+// workgroup makes its results visible device-wide and takes a ticket from
+// `arrive`; the one that draws the last ticket resets the counter, sees
+// every other workgroup's results and runs publish_offsets.  No workgroup
+// waits for another, so the grid always drains.
+template <int RPL>
+__global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
+                                                            const int32_t* __restrict__ mf,
+                                                            PlanDev d, PlanWork w, int32_t* arrive,
+                                                            int32_t* host_slot, int32_t seq) {
+  __shared__ int s_last;
+  __shared__ int s_wp[4], s_wf[4];
+  __shared__ uint32_t s_err;
+  const int lane = wave_lane();
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (g.upper_rows > 0) {
+    const int hm = item / g.upper_rows;
+    const int row = item - hm * g.upper_rows;
+    if (hm < g.mask_heads && row < rows_total_of(g, d))
+      classify_row<RPL>(g, mf, d, w, hm, row, lane);
+  }
+
+  // Every wavefront waits for its stores to complete; the workgroup's ticket
+  // is then taken with release semantics (writing the device caches back
+  // once per workgroup), and only the last workgroup acquires.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (int)gridDim.x - 1 ? 1 : 0;
+    s_err = 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);   // agent scope: sees every workgroup's results
+  if (threadIdx.x == 0) __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  publish_offsets<256>(g, d, w, host_slot, seq, s_wp, s_wf, &s_err);
+}
+
+// ---------------------------------------------------------------- schedule
+
+namespace {
 
 // In-place exclusive scan of n ints (LDS or global) by one workgroup of 1024
 // threads: four consecutive values per thread, a wavefront shuffle scan of
@@ -395,227 +503,333 @@ __device__ inline int block_exclusive_scan_inplace(int32_t* a, int64_t n, int* s
   return *s_carry;
 }
 
-struct TaskInfo {
-  int b, h, i, rows_b, row;
+struct SampleGeo {
+  int b, row_begin, q_off, k_off, q_len, k_len;
 };
 
-__device__ inline TaskInfo decode_task(const PlanGeo& g, const PlanDev& d, int t) {
-  // Canonical tie order: t = Hq*cu_rows[b] + h*rows_b + i.
-  TaskInfo r;
-  r.b = sample_of_row(d.cu_rows, g.batch, t / g.heads_q);
-  const int r0 = d.cu_rows[r.b];
-  r.rows_b = d.cu_rows[r.b + 1] - r0;
-  const int rel = t - g.heads_q * r0;
-  r.h = rel / r.rows_b;
-  r.i = rel - r.h * r.rows_b;
-  r.row = r0 + r.i;
+// Sample of a plan row; `s_cu` is an LDS copy of cu_rows (THD) or nullptr.
+__device__ inline SampleGeo sample_geo(const PlanGeo& g, const PlanDev& d, const int* s_cu,
+                                       int row) {
+  SampleGeo r;
+  if (g.layout == MPB_LAYOUT_BSHD) {
+    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+    r.b = row / rps;
+    r.row_begin = r.b * rps;
+    r.q_off = r.b * g.seqlen_q;
+    r.k_off = r.b * g.seqlen_k;
+    r.q_len = g.seqlen_q;
+    r.k_len = g.seqlen_k;
+  } else {
+    r.b = sample_of_row(s_cu ? s_cu : d.cu_rows, g.batch, row);
+    const int32_t* sd = d.seqdesc + 8 * r.b;
+    r.q_off = sd[0];
+    r.k_off = sd[1];
+    r.q_len = sd[2];
+    r.k_len = sd[3];
+    r.row_begin = sd[4];
+  }
   return r;
 }
 
-__device__ inline int task_cost(const PlanGeo& g, const PlanWork& w, int h, int row) {
-  const int hm = g.mask_heads == 1 ? 0 : h;
-  const int64_t src = (int64_t)hm * g.upper_rows + row;
-  return w.pcnt[src] + w.fcnt[src];
+__device__ inline int row_cost(const PlanWork& w, int i) {
+  return (w.p_off_tmp[i + 1] - w.p_off_tmp[i]) + (w.f_off_tmp[i + 1] - w.f_off_tmp[i]);
 }
 
-__device__ inline int task_section(const PlanGeo& g, int b, int h, int cost) {
-  if (cost == 0) return kNumSections;
-  const int group = g.heads_q / g.heads_k;
-  return (b * g.heads_k + h / group) % kNumSections;
+// Number of KV heads hk in [0, Hk) with (b*Hk + hk) % 8 == s; they are
+// r, r+8, ... with r = (s - b*Hk) mod 8.
+__device__ inline int kv_heads_in_section(int b, int heads_k, int s, int* r_out) {
+  const int r = (int)(((int64_t)s - (int64_t)b * heads_k) % kNumSections + kNumSections) %
+                kNumSections;
+  *r_out = r;
+  return r < heads_k ? (heads_k - 1 - r) / kNumSections + 1 : 0;
 }
 
 // Launch slot of the r-th task of section s: sections interleaved while they
 // last; zero-cost tasks after all positive-cost ones.
-__device__ inline int launch_slot(const PlanDev& d, int s, int r) {
-  if (s >= kNumSections) return d.section_off[kNumSections] + r;
+__device__ inline int launch_slot(const int* secoff, int s, int r) {
+  if (s >= kNumSections) return secoff[kNumSections] + r;
   int slot = 0;
 #pragma unroll
   for (int s2 = 0; s2 < kNumSections; ++s2) {
-    const int n2 = d.section_off[s2 + 1] - d.section_off[s2];
+    const int n2 = secoff[s2 + 1] - secoff[s2];
     slot += min(r, n2) + ((s2 < s && n2 > r) ? 1 : 0);
   }
   return slot;
 }
 
-__device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                  const TaskInfo& ti, int s, int pos, int rows_total) {
-  const int32_t* sd = d.seqdesc + 8 * ti.b;
-  const int qvalid = min(g.tile_q, sd[2] - ti.i * g.tile_q);
-  int32_t* wd = d.work_desc + 4 * (int64_t)pos;
-  wd[0] = ti.i;
-  wd[1] = ti.h;
-  wd[2] = ti.b;
-  wd[3] = qvalid;
-  const int hm = g.mask_heads == 1 ? 0 : ti.h;
-  const int64_t flat = (int64_t)hm * rows_total + ti.row;
-  const int64_t src = (int64_t)hm * g.upper_rows + ti.row;
-  const int p_beg = w.p_off_tmp[flat], np = w.p_off_tmp[flat + 1] - p_beg;
-  const int f_beg = w.f_off_tmp[flat], nf = w.f_off_tmp[flat + 1] - f_beg;
-  int first = -1;
-  if (np + nf > 0) {
-    const int nwords = (sd[6] + 31) >> 5;
-    for (int ww = 0; ww < nwords && first < 0; ++ww) {
-      const uint32_t vw = w.vis_bits[src * g.words_k + ww];
-      const uint32_t fw = w.full_bits[src * g.words_k + ww];
-      const uint32_t pick = np > 0 ? (vw & ~fw) : fw;  // partial list first (§6.1)
-      if (pick) first = 32 * ww + __ffs(pick) - 1;
+}  // namespace
+
+// §4.8 the forward schedule, one workgroup, after the header is known.
+// Tasks are (plan row, Q head).  Order: section ascending (section of
+// (b, h) = (b*Hk + h/group) % 8, zero-cost tasks last), then the cost of the
+// task's mask row descending, ties by flat row index then head.  Bounded
+// counting, no general sort:
+//  1. rows (flat, head-major) are ranked by descending cost with a stable
+//     counting sort: per 64-row chunk (one wavefront) the rows with an equal
+//     cost are found with one ballot per cost bit, giving each row its rank
+//     among them and the chunk's per-cost counts; one exclusive scan of the
+//     counts laid out [cost][chunk] gives every row its sorted position.  The
+//     same pass totals the tasks of each section.
+//  2. over the sorted rows, an exclusive scan of each row's per-section task
+//     counts (eight sections and the zero-cost queue) gives the in-section
+//     position of the row's first task in each queue.
+//  3. every task is written to the section-major schedule and, as a launch
+//     record, at its section-interleaved launch slot (slot 8r+x holds the r-th
+//     task of section x while every section still has tasks).
+// Up to kSchedLdsRows rows, the row data (offsets, first tiles, the sorted
+// order) live in LDS, and up to kSchedLdsBaseRows rows their nine first
+// positions too; past that in the build workspace.
+constexpr int kSchedLdsRows = 4096;
+constexpr int kSchedLdsBaseRows = 1024;   // rows whose first positions also fit in LDS
+
+namespace {
+
+// Tasks of one row in each of the nine queues.
+__device__ inline void row_queue_counts(const PlanGeo& g, int b, int hm, int cost,
+                                        int (&v)[kNumQueues]) {
+  const int group = g.heads_q / g.heads_k;
+#pragma unroll
+  for (int s = 0; s < kNumQueues; ++s) v[s] = 0;
+  if (cost == 0) {
+    v[kNumSections] = g.mask_heads == 1 ? g.heads_q : 1;
+  } else if (g.mask_heads == 1) {
+#pragma unroll
+    for (int s = 0; s < kNumSections; ++s) {
+      int r;
+      v[s] = group * kv_heads_in_section(b, g.heads_k, s, &r);
     }
+  } else {
+    const int sec = (int)(((int64_t)b * g.heads_k + hm / group) % kNumSections);
+#pragma unroll
+    for (int s = 0; s < kNumSections; ++s) v[s] = s == sec ? 1 : 0;
   }
-  int32_t* rec = d.task_rec + (int64_t)launch_slot(d, s, pos - d.section_off[s]) * kTaskRecInts;
-  rec[kRecMBlock] = ti.i;
-  rec[kRecHead] = ti.h;
-  rec[kRecBatch] = ti.b;
-  rec[kRecQValid] = qvalid;
-  rec[kRecQOff] = sd[0];
-  rec[kRecKOff] = sd[1];
-  rec[kRecQLen] = sd[2];
-  rec[kRecKLen] = sd[3];
-  rec[kRecPBeg] = p_beg;
-  rec[kRecPCnt] = np;
-  rec[kRecFBeg] = f_beg;
-  rec[kRecFCnt] = nf;
-  rec[kRecFirstTile] = first;
-  rec[kRecMaskHead] = hm;
-  rec[kRecKvHead] = ti.h / (g.heads_q / g.heads_k);
-  rec[kRecSection] = s;
+}
+
+__device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int* secoff,
+                                  const SampleGeo& sg, int il, int h, int hm, int s, int pos_s,
+                                  int p_beg, int np, int f_beg, int nf, int first) {
+  const int qvalid = min(g.tile_q, sg.q_len - il * g.tile_q);
+  *reinterpret_cast<int4*>(d.work_desc + 4 * (int64_t)(secoff[s] + pos_s)) =
+      make_int4(il, h, sg.b, qvalid);
+  int4* rec = reinterpret_cast<int4*>(d.task_rec +
+                                      (int64_t)launch_slot(secoff, s, pos_s) * kTaskRecInts);
+  rec[0] = make_int4(il, h, sg.b, qvalid);                         // kRecMBlock ..
+  rec[1] = make_int4(sg.q_off, sg.k_off, sg.q_len, sg.k_len);      // kRecQOff ..
+  rec[2] = make_int4(p_beg, np, f_beg, nf);                        // kRecPBeg ..
+  rec[3] = make_int4(first, hm, h / (g.heads_q / g.heads_k), s);   // kRecFirstTile ..
 }
 
 }  // namespace
 
-// One workgroup after classification:
-//  1. §4.5 exact exclusive CSR offsets over rows flattened head-major
-//     (flat = hm * rows_total + row), off[0] = 0, off[i+1] = off[i] + cnt[i];
-//     the fixed-length geometry in closed form; the 8-value header with the
-//     OR of every device error bit, published to host-mapped memory so the
-//     host reads it with no copy command.
-//  2. §4.8 the forward schedule: section ascending, cost descending, ties in
-//     canonical order t = Hq*cu_rows[b] + h*rows_b + i; zero-cost tasks form
-//     the last section.  A stable counting sort: tasks are cut into chunks
-//     of 64 (one wavefront each) that yield each task's bucket key, its rank
-//     among equal keys of the chunk and the chunk's bucket counts; one
-//     exclusive scan of the counts laid out [bucket][chunk] gives, per
-//     (bucket, chunk), the position of the chunk's first task of that bucket.
-//     Each task is then written to the section-major schedule and, as a
-//     launch record, at its section-interleaved launch slot.
-__global__ __launch_bounds__(1024) void plan_index_kernel(PlanGeo g, PlanDev d, PlanWork w,
-                                                          int32_t* host_header, int cnt_in_lds) {
+__global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev d, PlanWork w,
+                                                             int cnt_in_lds, int rows_in_lds) {
   extern __shared__ int dyn[];
-  __shared__ int sa[1024], sb[1024];
-  __shared__ int carry_p, carry_f;
-  __shared__ uint32_t s_err;
+  __shared__ int s_secoff[kNumQueues + 1];
+  __shared__ int s_run[kNumQueues];
+  __shared__ int s_tot[kNumQueues];
+  __shared__ int s_vec[16][kNumQueues];
   __shared__ int s_wave[33];
   __shared__ int s_carry;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wv = tid >> 6;
-  const int rows_total = rows_total_of(g, d);
+  __shared__ int s_cu[1025];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (d.header[7] != 0) return;  // the build failed: no plan is made
+  const int rows_total = d.header[0];
   const int n = g.mask_heads * rows_total;
-  if (tid == 0) {
-    carry_p = 0;
-    carry_f = 0;
-    s_err = g.layout == MPB_LAYOUT_THD ? (uint32_t)w.geo_err[0] : 0u;
+  const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
+  const int nc = (n + 63) >> 6;
+  const int64_t cnt_len = (int64_t)(g.nk_max + 1) * nc;
+
+  // LDS carve: [count matrix][p_off n+1][f_off n+1][first n][order n]
+  int32_t* cnt = cnt_in_lds ? dyn : w.chunk_cnt;
+  int* lds_rows = dyn + (cnt_in_lds ? (int64_t)(g.nk_max + 1) * w.nchunks : 0);
+  const int32_t* P = w.p_off_tmp;
+  const int32_t* F = w.f_off_tmp;
+  int32_t* FT = nullptr;
+  int32_t* order = w.order;
+  if (rows_in_lds) {
+    int* lp = lds_rows;
+    int* lf = lp + n + 1;
+    FT = lf + n + 1;
+    order = FT + n;
+    for (int i = tid; i <= n; i += 1024) {
+      lp[i] = w.p_off_tmp[i];
+      lf[i] = w.f_off_tmp[i];
+      if (i < n) {
+        const int hm = i / rows_total;
+        FT[i] = w.first_tile[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
+      }
+    }
+    P = lp;
+    F = lf;
   }
-  // Fixed-length geometry in closed form (§4.2: rectangular upper bound).
+  auto first_of = [&](int i) -> int {
+    if (FT) return FT[i];
+    const int hm = i / rows_total;
+    return w.first_tile[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
+  };
+  auto cost_of = [&](int i) -> int { return (P[i + 1] - P[i]) + (F[i + 1] - F[i]); };
+
+  const int* cu = nullptr;
   if (g.layout == MPB_LAYOUT_BSHD) {
+    // Fixed-length geometry in closed form (§4.2: rectangular upper bound).
     const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
     for (int b = tid; b < g.batch; b += 1024) {
-      int32_t* sd = d.seqdesc + 8 * b;
-      sd[0] = b * g.seqlen_q;
-      sd[1] = b * g.seqlen_k;
-      sd[2] = g.seqlen_q;
-      sd[3] = g.seqlen_k;
-      sd[4] = b * rps;
-      sd[5] = rps;
-      sd[6] = (g.seqlen_k + g.tile_k - 1) / g.tile_k;
-      sd[7] = 0;
+      int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
+      sd[0] = make_int4(b * g.seqlen_q, b * g.seqlen_k, g.seqlen_q, g.seqlen_k);
+      sd[1] = make_int4(b * rps, rps, (g.seqlen_k + g.tile_k - 1) / g.tile_k, 0);
       d.cu_rows[b + 1] = (b + 1) * rps;
     }
     if (tid == 0) d.cu_rows[0] = 0;
+  } else if (g.batch < 1025) {
+    for (int b = tid; b <= g.batch; b += 1024) s_cu[b] = d.cu_rows[b];
+    cu = s_cu;
   }
+  if (tid < kNumQueues) {
+    s_run[tid] = 0;
+    s_tot[tid] = 0;
+  }
+  for (int64_t x = tid; x < cnt_len; x += 1024) cnt[x] = 0;
   __syncthreads();
-  uint32_t err = 0;
-  for (int base = 0; base < n; base += 1024) {
-    const int idx = base + tid;
-    int a = 0, c = 0;
-    if (idx < n) {
-      const int hm = idx / rows_total;
-      const int r = idx - hm * rows_total;
-      const int64_t it = (int64_t)hm * g.upper_rows + r;
-      a = w.pcnt[it];
-      c = w.fcnt[it];
-      err |= (uint32_t)w.item_err[it];
-    }
-    sa[tid] = a;
-    sb[tid] = c;
-    __syncthreads();
-    block_incl_scan2(sa, sb, tid, 1024);
-    if (idx < n) {
-      w.p_off_tmp[idx] = carry_p + sa[tid] - a;
-      w.f_off_tmp[idx] = carry_f + sb[tid] - c;
-    }
-    __syncthreads();
-    if (tid == 1023) {
-      carry_p += sa[1023];
-      carry_f += sb[1023];
-    }
-    __syncthreads();
-  }
-  if (err) atomicOr(&s_err, err);
-  __syncthreads();
-  if (tid == 0) {
-    w.p_off_tmp[n] = carry_p;
-    w.f_off_tmp[n] = carry_f;
-    const int32_t hdr[8] = {rows_total, carry_p, carry_f, 0, 0, 0, 0, (int32_t)s_err};
-    for (int i = 0; i < 8; ++i) {
-      d.header[i] = hdr[i];
-      __hip_atomic_store(&host_header[i], hdr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    __threadfence_system();
-  }
-  if (s_err) return;  // no plan will be built (uniform: read after the barrier)
 
-  // ---- schedule
-  const int ntasks = rows_total * g.heads_q;
-  const int per = g.nk_max + 1;
-  const int nc = w.nchunks;
-  int32_t* cnt = cnt_in_lds ? dyn : w.chunk_cnt;
-  if (cnt_in_lds)
-    for (int64_t x = tid; x < w.chunk_cnt_len; x += 1024) cnt[x] = 0;  // global copy: zeroed by classify
-  __syncthreads();
-  const uint64_t lt = lanes_below(lane);
-  for (int chunk = wv; chunk * 64 < ntasks; chunk += 16) {
-    const int t = chunk * 64 + lane;
-    int key = -1;
-    if (t < ntasks) {
-      const TaskInfo ti = decode_task(g, d, t);
-      const int cost = task_cost(g, w, ti.h, ti.row);
-      key = task_section(g, ti.b, ti.h, cost) * per + (g.nk_max - cost);
-      w.keys[t] = key;
+  // 1. stable counting sort of the rows by descending cost; queue totals
+  const int nbits = 32 - __clz(g.nk_max);
+  const uint64_t below = lanes_below(lane);
+  int lr[kSchedLdsRows / 1024];
+  int tot[kNumQueues];
+#pragma unroll
+  for (int s = 0; s < kNumQueues; ++s) tot[s] = 0;
+  for (int c = wv, k = 0; c < nc; c += 16, ++k) {
+    const int i = c * 64 + lane;
+    const bool live = i < n;
+    int key = 0;
+    if (live) {
+      const int cost = cost_of(i);
+      key = g.nk_max - cost;
+      const int hm = i / rows_total;
+      int v[kNumQueues];
+      row_queue_counts(g, sample_geo(g, d, cu, i - hm * rows_total).b, hm, cost, v);
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s) tot[s] += v[s];
     }
-    bool todo = t < ntasks;
-    while (true) {  // one pass per distinct key of the chunk
-      const uint64_t m = __ballot(todo);
-      if (m == 0) break;
-      const int leader = __ffsll((unsigned long long)m) - 1;
-      const int k0 = __shfl(key, leader);
-      const bool same = todo && key == k0;
-      const uint64_t match = __ballot(same);
-      if (same) {
-        w.lrank[t] = __popcll(match & lt);
-        todo = false;
+    uint64_t eq = __ballot(live);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool on = (key >> bit) & 1;
+      const uint64_t m = __ballot(on);
+      eq &= on ? m : ~m;
+    }
+    if (live) {
+      const int rank = __popcll(eq & below);
+      if (rows_in_lds) {
+#pragma unroll
+        for (int u = 0; u < kSchedLdsRows / 1024; ++u)
+          if (u == k) lr[u] = rank;
+      } else {
+        w.lrank[i] = rank;
       }
-      if (lane == leader) cnt[(int64_t)k0 * nc + chunk] = __popcll(match);
+      if ((eq & below) == 0) cnt[(int64_t)key * nc + c] = __popcll(eq);
     }
   }
+#pragma unroll
+  for (int s = 0; s < kNumQueues; ++s) {
+    int t = tot[s];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    if (lane == 0 && t) atomicAdd(&s_tot[s], t);
+  }
   __syncthreads();
-  const int total = block_exclusive_scan_inplace(cnt, w.chunk_cnt_len, s_wave, &s_carry);
-  const int64_t per_section = (int64_t)per * nc;
-  if (tid < kNumQueues) d.section_off[tid] = cnt[(int64_t)tid * per_section];
-  if (tid == 0) d.section_off[kNumQueues] = total;
+  block_exclusive_scan_inplace(cnt, cnt_len, s_wave, &s_carry);
+  for (int c = wv, k = 0; c < nc; c += 16, ++k) {   // same row-to-thread map as above
+    const int i = c * 64 + lane;
+    if (i >= n) continue;
+    int rank = 0;
+    if (rows_in_lds) {
+#pragma unroll
+      for (int u = 0; u < kSchedLdsRows / 1024; ++u)
+        if (u == k) rank = lr[u];
+    } else {
+      rank = w.lrank[i];
+    }
+    order[cnt[(int64_t)(g.nk_max - cost_of(i)) * nc + c] + rank] = i;
+  }
+  if (tid == 0) {
+    s_secoff[0] = 0;
+    for (int s = 0; s < kNumQueues; ++s) s_secoff[s + 1] = s_secoff[s] + s_tot[s];
+    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_secoff[s];
+  }
   __syncthreads();
+
+  // 2. in-section position of each row's first task, over the sorted rows
+  int32_t* rbase = rows_in_lds == 2 ? order + n : w.row_base;
+  for (int base = 0; base < n; base += 1024) {
+    const int pos = base + tid;
+    int v[kNumQueues];
+    int i = 0;
+    if (pos < n) {
+      i = order[pos];
+      const int hm = i / rows_total;
+      row_queue_counts(g, sample_geo(g, d, cu, i - hm * rows_total).b, hm, cost_of(i), v);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s) v[s] = 0;
+    }
+    int first_pos[kNumQueues];
+#pragma unroll
+    for (int s = 0; s < kNumQueues; ++s) {
+      const int incl = wave_incl_scan(v[s], lane);
+      first_pos[s] = incl - v[s];
+      if (lane == 63) s_vec[wv][s] = incl;
+    }
+    __syncthreads();
+    if (pos < n) {
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s) {
+        int pre = s_run[s];
+        for (int x = 0; x < wv; ++x) pre += s_vec[x][s];
+        rbase[(int64_t)i * kNumQueues + s] = pre + first_pos[s];
+      }
+    }
+    __syncthreads();
+    if (tid < kNumQueues)
+      for (int x = 0; x < 16; ++x) s_run[tid] += s_vec[x][tid];
+    __syncthreads();
+  }
+
+  // 3. every task, one per thread
+  int so[kNumQueues + 1];
+#pragma unroll
+  for (int s = 0; s <= kNumQueues; ++s) so[s] = s_secoff[s];
+  const int ntasks = rows_total * Hq;
   for (int t = tid; t < ntasks; t += 1024) {
-    const int key = w.keys[t];
-    const int pos = cnt[(int64_t)key * nc + t / 64] + w.lrank[t];
-    write_task(g, d, w, decode_task(g, d, t), key / per, pos, rows_total);
+    int i, h;
+    if (g.mask_heads == 1) {
+      i = t / Hq;
+      h = t - i * Hq;
+    } else {
+      i = t;
+      h = t / rows_total;
+    }
+    const int hm = g.mask_heads == 1 ? 0 : h;
+    const int row = i - hm * rows_total;
+    const SampleGeo sg = sample_geo(g, d, cu, row);
+    const int p_beg = P[i], np = P[i + 1] - p_beg;
+    const int f_beg = F[i], nf = F[i + 1] - f_beg;
+    int s, rank;
+    if (np + nf == 0) {
+      s = kNumSections;
+      rank = g.mask_heads == 1 ? h : 0;
+    } else {
+      const int hk = h / group;
+      s = (int)(((int64_t)sg.b * g.heads_k + hk) % kNumSections);
+      if (g.mask_heads == 1) {
+        int r;
+        kv_heads_in_section(sg.b, g.heads_k, s, &r);
+        rank = ((hk - r) / kNumSections) * group + (h - hk * group);
+      } else {
+        rank = 0;
+      }
+    }
+    write_task(g, d, so, sg, row - sg.row_begin, h, hm, s,
+               rbase[(int64_t)i * kNumQueues + s] + rank, p_beg, np, f_beg, nf, first_of(i));
   }
 }
 
@@ -635,14 +849,27 @@ __global__ __launch_bounds__(1024) void plan_index_kernel(PlanGeo g, PlanDev d, 
 //    partial tiles are listed in ascending order.  Rows past q_len write 0.
 __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
                                                                const int32_t* __restrict__ mf,
-                                                               PlanDev d, PlanWork w,
-                                                               int rows_total, int stage_ep) {
+                                                               PlanDev st, PlanDev d, PlanWork w,
+                                                               int rows_total, int stage_ep,
+                                                               MetaCopy mc) {
   extern __shared__ int lds[];
   int* tiles = lds;                     // [nk_max] partial K tiles of this row
   int* ep = lds + g.nk_max;             // [nfunc][T_Q] endpoints when staged
   const int item = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = g.mask_heads * rows_total;
+  // Plan metadata staged in the workspace (header, geometry, schedule and
+  // launch records), copied into the plan block a slice per workgroup.
+  {
+    const int64_t per = (mc.total + gridDim.x - 1) / gridDim.x;
+    const int64_t lo = per * blockIdx.x, hi = min(mc.total, lo + per);
+    for (int64_t x = lo + tid; x < hi; x += blockDim.x) {
+      int seg = 0;
+      while (x >= mc.end[seg]) ++seg;
+      const int64_t off = x - (seg ? mc.end[seg - 1] : 0);
+      mc.dst[seg][off] = mc.src[seg][off];
+    }
+  }
   if (item == 0 && tid == 0) {
     d.p_off[n] = w.p_off_tmp[n];
     d.f_off[n] = w.f_off_tmp[n];
@@ -654,7 +881,7 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
   const int p_begin = w.p_off_tmp[item];
   const int f_begin = w.f_off_tmp[item];
   const int np = w.p_off_tmp[item + 1] - p_begin;
-  const RowGeo rg = row_geometry(g, d, row);
+  const RowGeo rg = row_geometry(g, st, row);
   if (tid == 0) {
     d.p_off[item] = p_begin;
     d.f_off[item] = f_begin;
@@ -725,41 +952,62 @@ hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const 
 }
 
 hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
-                                const PlanWork& w, hipStream_t s) {
+                                const PlanWork& w, int32_t* arrive, int32_t* host_slot,
+                                int32_t seq, hipStream_t s) {
   const int64_t items = (int64_t)g.mask_heads * g.upper_rows;
-  if (items == 0) return hipSuccess;
-  const dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  // At least one workgroup, so the header is always published.
+  const dim3 grid((unsigned)(items > 0 ? (items + 3) / 4 : 1)), block(256);
   switch (rows_per_lane(g.tile_q)) {
-    case 1: hipLaunchKernelGGL(plan_classify_kernel<1>, grid, block, 0, s, g, mask_func, d, w); break;
-    case 2: hipLaunchKernelGGL(plan_classify_kernel<2>, grid, block, 0, s, g, mask_func, d, w); break;
-    case 4: hipLaunchKernelGGL(plan_classify_kernel<4>, grid, block, 0, s, g, mask_func, d, w); break;
+    case 1: hipLaunchKernelGGL(plan_classify_kernel<1>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
+    case 2: hipLaunchKernelGGL(plan_classify_kernel<2>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
+    case 4: hipLaunchKernelGGL(plan_classify_kernel<4>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-size_t index_kernel_lds(const PlanWork& w) {
-  const size_t bytes = (size_t)w.chunk_cnt_len * 4;
-  return bytes <= 40 * 1024 ? bytes : 0;
-}
-
-hipError_t launch_plan_index(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                             int32_t* host_header, hipStream_t s) {
-  const size_t lds = index_kernel_lds(w);
-  hipLaunchKernelGGL(plan_index_kernel, dim3(1), dim3(1024), lds, s, g, d, w, host_header,
-                     lds > 0 ? 1 : 0);
+hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                hipStream_t s) {
+  const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
+  const size_t cnt_bytes = w.chunk_cnt ? 0 : (size_t)(g.nk_max + 1) * w.nchunks * 4;
+  // 0: row data in the workspace; 1: in LDS; 2: their first positions too
+  const int rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  const size_t row_bytes =
+      rows_in_lds ? (size_t)(4 * rows + 2 + (rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4 : 0;
+  hipLaunchKernelGGL(plan_schedule_kernel, dim3(1), dim3(1024), cnt_bytes + row_bytes, s, g, d,
+                     w, w.chunk_cnt ? 0 : 1, rows_in_lds);
   return hipGetLastError();
 }
 
-hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
-                                   const PlanWork& w, int32_t rows_total, hipStream_t s) {
+hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& st,
+                                   const PlanDev& d, const PlanWork& w, int32_t rows_total,
+                                   hipStream_t s) {
   const int64_t items = (int64_t)g.mask_heads * rows_total;
+  const int64_t tasks = (int64_t)rows_total * g.heads_q;
+  MetaCopy mc;
+  int nseg = 0;
+  int64_t run = 0;
+  auto seg = [&](const int32_t* src, int32_t* dst, int64_t count) {
+    mc.src[nseg] = src;
+    mc.dst[nseg] = dst;
+    run += count;
+    mc.end[nseg++] = run;
+  };
+  seg(st.header, d.header, 8);
+  seg(st.seqdesc, d.seqdesc, 8 * (int64_t)g.batch);
+  seg(st.cu_rows, d.cu_rows, g.batch + 1);
+  seg(st.cu_q, d.cu_q, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
+  seg(st.cu_k, d.cu_k, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
+  seg(st.work_desc, d.work_desc, 4 * tasks);
+  seg(st.section_off, d.section_off, kNumQueues + 1);
+  seg(st.task_rec, d.task_rec, kTaskRecInts * tasks);
+  mc.total = run;
   const int threads = g.tile_q < 64 ? 64 : g.tile_q;
   const size_t ep_bytes = (size_t)g.nfunc * g.tile_q * 4;
   const int stage = ep_bytes <= 32 * 1024 ? 1 : 0;
   const size_t lds = (size_t)g.nk_max * 4 + (stage ? ep_bytes : 0);
   hipLaunchKernelGGL(plan_materialize_kernel, dim3((unsigned)(items > 0 ? items : 1)),
-                     dim3(threads), lds, s, g, mask_func, d, w, rows_total, stage);
+                     dim3(threads), lds, s, g, mask_func, st, d, w, rows_total, stage, mc);
   return hipGetLastError();
 }
 

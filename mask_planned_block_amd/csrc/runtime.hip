@@ -13,6 +13,8 @@
 // build costs no device-wide synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -35,10 +37,8 @@ struct mpb_plan {
   int32_t rows_total;
   int32_t num_tasks;
   int64_t header[8];
-  void* geo_block;
-  void* exact_block;
-  size_t geo_bytes;
-  size_t exact_bytes;
+  void* block;             // every device array of the plan, one allocation
+  size_t bytes;
   hipStream_t stream;
 };
 
@@ -88,22 +88,40 @@ hipError_t device_pool(int dev, hipMemPool_t* out) {
   return hipSuccess;
 }
 
-// ---- per-thread host-mapped header slot and completion event
+// ---- per-thread host-mapped header slot and arrival counters
 //
-// The index kernel writes the 8-value header straight into this pinned,
-// coherent, device-mapped host memory; the host reads it after the kernel's
-// completion event, so the header read-back needs no copy command.
+// The classify kernel's last workgroup writes the 8-value header straight
+// into this pinned, coherent, device-mapped host memory and then the build's
+// sequence number; the host spins on the sequence number, so the header
+// read-back needs neither a copy command nor a wait for the kernel to retire.
+// Builds issued from one host thread are sequential (each returns only after
+// its header arrived), so one slot and one arrival counter per (thread,
+// device) are never shared by two builds in flight.
+
+// The build workspace of a (thread, device) is one arena reused by every
+// build: the previous build's kernels that still read it are ordered before
+// the next build's by the stream, and a build on another stream first waits
+// for the stream of the previous one.
+struct Arena {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipStream_t last = nullptr;
+  bool used = false;
+};
 
 struct ThreadSlot {
   int32_t* pinned = nullptr;
   int32_t* pinned_dev = nullptr;
-  hipEvent_t ev[64] = {};
+  uint32_t seq = 0;
+  int32_t* arrive[64] = {};
+  Arena arena[64];
 };
 thread_local ThreadSlot g_slot;
 
-hipError_t thread_slot(int dev, volatile int32_t** pinned, int32_t** pinned_dev, hipEvent_t* ev) {
+hipError_t thread_slot(int dev, ThreadSlot** out) {
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   if (!g_slot.pinned) {
-    hipError_t e = hipHostMalloc((void**)&g_slot.pinned, 8 * sizeof(int32_t),
+    hipError_t e = hipHostMalloc((void**)&g_slot.pinned, kHostSlotInts * sizeof(int32_t),
                                  hipHostMallocMapped | hipHostMallocCoherent);
     if (e == hipSuccess) e = hipHostGetDevicePointer((void**)&g_slot.pinned_dev, g_slot.pinned, 0);
     if (e != hipSuccess) {
@@ -112,17 +130,61 @@ hipError_t thread_slot(int dev, volatile int32_t** pinned, int32_t** pinned_dev,
       g_slot.pinned_dev = nullptr;
       return e;
     }
+    for (int i = 0; i < kHostSlotInts; ++i) g_slot.pinned[i] = 0;
   }
-  if (!g_slot.ev[dev]) {
-    hipError_t e = hipEventCreateWithFlags(&g_slot.ev[dev], hipEventDisableTiming);
+  if (!g_slot.arrive[dev]) {
+    int32_t* a = nullptr;
+    hipError_t e = hipMalloc((void**)&a, 256);
+    if (e == hipSuccess) e = hipMemset(a, 0, 256);
     if (e != hipSuccess) {
-      g_slot.ev[dev] = nullptr;
+      if (a) hipFree(a);
       return e;
     }
+    g_slot.arrive[dev] = a;
   }
-  *pinned = g_slot.pinned;
-  *pinned_dev = g_slot.pinned_dev;
-  *ev = g_slot.ev[dev];
+  *out = &g_slot;
+  return hipSuccess;
+}
+
+// An arena of at least `bytes` that no earlier build's kernels still read.
+hipError_t arena_acquire(Arena& a, size_t bytes, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (a.used && a.last != stream && (e = hipStreamSynchronize(a.last)) != hipSuccess) return e;
+  if (a.bytes < bytes) {
+    if (a.ptr && ((e = hipDeviceSynchronize()) != hipSuccess || (e = hipFree(a.ptr)) != hipSuccess))
+      return e;
+    a.ptr = nullptr;
+    a.bytes = 0;
+    const size_t want = std::max(bytes + bytes / 2, (size_t)1 << 20);
+    if ((e = hipMalloc(&a.ptr, want)) != hipSuccess) return e;
+    a.bytes = want;
+  }
+  a.last = stream;
+  a.used = true;
+  return hipSuccess;
+}
+
+// Wait until the header of build `seq` has landed in the slot.  Now and then
+// (every few hundred microseconds) the stream is queried: if all its work has
+// completed and the sequence number is still not there, the header was never
+// written.
+hipError_t wait_header(ThreadSlot* slot, hipStream_t stream, uint32_t seq, bool* published) {
+  volatile int32_t* sq = slot->pinned + kHeaderSeq;
+  *published = false;
+  for (uint32_t spin = 1;; ++spin) {
+    if ((uint32_t)*sq == seq) break;
+    if ((spin & 4095u) == 0) {
+      const hipError_t e = hipStreamQuery(stream);
+      if (e == hipSuccess) {
+        if ((uint32_t)*sq == seq) break;
+        return hipSuccess;   // the stream drained without publishing
+      }
+      if (e != hipErrorNotReady) return e;
+    }
+    __builtin_ia32_pause();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  *published = true;
   return hipSuccess;
 }
 
@@ -275,7 +337,8 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
     return fail(MPB_ERR_UNSUPPORTED, "seqlen_k %d spans more than %d K tiles of %d", p.seqlen_k,
                 kMaxKTiles, tk);
   if (upper * p.mask_heads >= ((int64_t)1 << 31) || upper * p.heads_q >= ((int64_t)1 << 31) ||
-      upper * p.mask_heads * words_k >= ((int64_t)1 << 31))
+      upper * p.mask_heads * words_k >= ((int64_t)1 << 31) ||
+      upper * p.mask_heads * nk_max >= ((int64_t)1 << 31))
     return fail(MPB_ERR_UNSUPPORTED, "too many plan rows");
   g.upper_rows = (int32_t)upper;
   g.nk_max = (int32_t)nk_max;
@@ -288,96 +351,87 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   if (e != hipSuccess) return device_status(e, "hipGetDevice");
   hipMemPool_t pool;
   if ((e = device_pool(dev, &pool)) != hipSuccess) return device_status(e, "memory pool");
-  volatile int32_t* pinned = nullptr;
-  int32_t* pinned_dev = nullptr;
-  hipEvent_t ev;
-  if ((e = thread_slot(dev, &pinned, &pinned_dev, &ev)) != hipSuccess)
-    return device_status(e, "host slot");
+  ThreadSlot* slot = nullptr;
+  if ((e = thread_slot(dev, &slot)) != hipSuccess) return device_status(e, "host slot");
 
+  // Build workspace and the staged plan metadata, in the thread's arena.
   const int64_t items_upper = upper * p.mask_heads;
-  Carver cg;
-  const size_t o_header = cg.take<int32_t>(8);
-  const size_t o_seqdesc = cg.take<int32_t>(8 * (int64_t)p.batch);
-  const size_t o_cu_rows = cg.take<int32_t>(p.batch + 1);
-  const size_t o_cu_q = cg.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 1);
-  const size_t o_cu_k = cg.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 1);
-  const size_t o_work_desc = cg.take<int32_t>(4 * upper * p.heads_q);
-  const size_t o_sec = cg.take<int32_t>(kNumQueues + 1);
-  const size_t o_rec = cg.take<int32_t>(kTaskRecInts * upper * p.heads_q);
+  const int64_t tasks_upper = upper * p.heads_q;
+  const int64_t nchunks = (items_upper + 63) / 64;
+  const int64_t cnt_len = (nk_max + 1) * nchunks;
+  // The schedule's [cost][chunk] count matrix lives in LDS when it fits.
+  const bool cnt_in_lds = cnt_len * 4 <= 60 * 1024;
   Carver cw;
   const size_t o_vis = cw.take<uint32_t>(items_upper * words_k);
   const size_t o_full = cw.take<uint32_t>(items_upper * words_k);
   const size_t o_pcnt = cw.take<int32_t>(items_upper);
   const size_t o_fcnt = cw.take<int32_t>(items_upper);
+  const size_t o_first = cw.take<int32_t>(items_upper);
   const size_t o_poff = cw.take<int32_t>(items_upper + 1);
   const size_t o_foff = cw.take<int32_t>(items_upper + 1);
-  const int64_t upper_tasks = upper * p.heads_q;
-  const int64_t nchunks = (upper_tasks + 63) / 64;
-  const int64_t cnt_len = (int64_t)kNumQueues * (nk_max + 1) * nchunks;
-  const size_t o_cnt = cw.take<int32_t>(cnt_len);
-  const size_t o_lrank = cw.take<int32_t>(upper_tasks);
   const size_t o_ierr = cw.take<int32_t>(items_upper);
   const size_t o_gerr = cw.take<int32_t>(1);
-  const size_t o_keys = cw.take<int32_t>(upper * p.heads_q);
+  const size_t o_lrank = cw.take<int32_t>(items_upper);
+  const size_t o_order = cw.take<int32_t>(items_upper);
+  const size_t o_base = cw.take<int32_t>(items_upper * kNumQueues);
+  const size_t o_cnt = cw.take<int32_t>(cnt_in_lds ? 1 : cnt_len);
+  const size_t o_header = cw.take<int32_t>(8);
+  const size_t o_seqdesc = cw.take<int32_t>(8 * (int64_t)p.batch);
+  const size_t o_cu_rows = cw.take<int32_t>(p.batch + 1);
+  const size_t o_cu_q = cw.take<int32_t>(p.batch + 1);
+  const size_t o_cu_k = cw.take<int32_t>(p.batch + 1);
+  const size_t o_work_desc = cw.take<int32_t>(4 * tasks_upper);
+  const size_t o_sec = cw.take<int32_t>(kNumQueues + 1);
+  const size_t o_rec = cw.take<int32_t>(kTaskRecInts * tasks_upper);
+  Arena& arena = slot->arena[dev];
+  if ((e = arena_acquire(arena, cw.off, s)) != hipSuccess)
+    return device_status(e, "planner workspace");
+  void* wb = arena.ptr;
 
-  void* geo_block = nullptr;
-  void* work_block = nullptr;
-  auto release = [&]() {
-    if (work_block) hipFreeAsync(work_block, s);
-    if (geo_block) hipFreeAsync(geo_block, s);
-    work_block = geo_block = nullptr;
-  };
-  if ((e = hipMallocFromPoolAsync(&geo_block, cg.off, pool, s)) != hipSuccess)
-    return device_status(e, "plan allocation");
-  if ((e = hipMallocFromPoolAsync(&work_block, cw.off, pool, s)) != hipSuccess) {
-    release();
-    return device_status(e, "planner workspace allocation");
-  }
-
-  PlanDev d;
-  std::memset(&d, 0, sizeof(d));
-  d.header = at<int32_t>(geo_block, o_header);
-  d.seqdesc = at<int32_t>(geo_block, o_seqdesc);
-  d.cu_rows = at<int32_t>(geo_block, o_cu_rows);
-  d.cu_q = p.layout == MPB_LAYOUT_THD ? at<int32_t>(geo_block, o_cu_q) : nullptr;
-  d.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(geo_block, o_cu_k) : nullptr;
-  d.work_desc = at<int32_t>(geo_block, o_work_desc);
-  d.section_off = at<int32_t>(geo_block, o_sec);
-  d.task_rec = at<int32_t>(geo_block, o_rec);
+  PlanDev sg;   // staged: geometry, header and schedule before the exact allocation
+  std::memset(&sg, 0, sizeof(sg));
+  sg.header = at<int32_t>(wb, o_header);
+  sg.seqdesc = at<int32_t>(wb, o_seqdesc);
+  sg.cu_rows = at<int32_t>(wb, o_cu_rows);
+  sg.cu_q = p.layout == MPB_LAYOUT_THD ? at<int32_t>(wb, o_cu_q) : nullptr;
+  sg.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(wb, o_cu_k) : nullptr;
+  sg.work_desc = at<int32_t>(wb, o_work_desc);
+  sg.section_off = at<int32_t>(wb, o_sec);
+  sg.task_rec = at<int32_t>(wb, o_rec);
   PlanWork w;
-  w.vis_bits = at<uint32_t>(work_block, o_vis);
-  w.full_bits = at<uint32_t>(work_block, o_full);
-  w.pcnt = at<int32_t>(work_block, o_pcnt);
-  w.fcnt = at<int32_t>(work_block, o_fcnt);
-  w.p_off_tmp = at<int32_t>(work_block, o_poff);
-  w.f_off_tmp = at<int32_t>(work_block, o_foff);
-  w.chunk_cnt = at<int32_t>(work_block, o_cnt);
-  w.chunk_cnt_len = cnt_len;
+  w.vis_bits = at<uint32_t>(wb, o_vis);
+  w.full_bits = at<uint32_t>(wb, o_full);
+  w.pcnt = at<int32_t>(wb, o_pcnt);
+  w.fcnt = at<int32_t>(wb, o_fcnt);
+  w.first_tile = at<int32_t>(wb, o_first);
+  w.p_off_tmp = at<int32_t>(wb, o_poff);
+  w.f_off_tmp = at<int32_t>(wb, o_foff);
+  w.item_err = at<int32_t>(wb, o_ierr);
+  w.geo_err = at<int32_t>(wb, o_gerr);
+  w.lrank = at<int32_t>(wb, o_lrank);
+  w.order = at<int32_t>(wb, o_order);
+  w.row_base = at<int32_t>(wb, o_base);
+  w.chunk_cnt = cnt_in_lds ? nullptr : at<int32_t>(wb, o_cnt);
   w.nchunks = (int32_t)nchunks;
-  w.lrank = at<int32_t>(work_block, o_lrank);
-  w.item_err = at<int32_t>(work_block, o_ierr);
-  w.geo_err = at<int32_t>(work_block, o_gerr);
-  w.keys = at<int32_t>(work_block, o_keys);
 
   const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
   const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
-  if ((e = launch_plan_geometry(g, cq, ck, d, w, s)) != hipSuccess ||
-      (e = launch_plan_classify(g, mask_func, d, w, s)) != hipSuccess ||
-      (e = launch_plan_index(g, d, w, pinned_dev, s)) != hipSuccess ||
-      (e = hipEventRecord(ev, s)) != hipSuccess) {
-    release();
+  uint32_t seq = ++slot->seq;
+  if (seq == 0) seq = ++slot->seq;   // 0 is the slot's initial value
+  if ((e = launch_plan_geometry(g, cq, ck, sg, w, s)) != hipSuccess ||
+      (e = launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
+                                (int32_t)seq, s)) != hipSuccess ||
+      (e = launch_plan_schedule(g, sg, w, s)) != hipSuccess)
     return device_status(e, "planner launch");
-  }
   // §4.5: the single header read-back of the build.
-  if ((e = hipEventSynchronize(ev)) != hipSuccess) {
-    release();
+  bool published = false;
+  if ((e = wait_header(slot, s, seq, &published)) != hipSuccess)
     return device_status(e, "header read-back");
-  }
+  if (!published) return fail(MPB_ERR_DEVICE, "the planner did not publish its header");
   int64_t header[8];
-  for (int i = 0; i < 8; ++i) header[i] = pinned[i];
+  for (int i = 0; i < 8; ++i) header[i] = ((volatile int32_t*)slot->pinned)[i];
   const uint32_t err = (uint32_t)header[7];
   if (err) {
-    release();
     if (err & MPB_DEVERR_SEQLENS)
       return fail(MPB_ERR_SEQLENS,
                   "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
@@ -387,41 +441,53 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
     return fail(MPB_ERR_ENDPOINT_ORDER, "endpoints of some row are not nondecreasing");
   }
   const int64_t rows_total = header[0], pnnz = header[1], fnnz = header[2];
-  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0) {
-    release();
+  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0)
     return fail(MPB_ERR_DEVICE, "inconsistent plan header");
-  }
 
-  // Exact allocation: no capacity padding of the retained CSR (§4.5).
+  // Exact allocation: every retained array sized by the header, no capacity
+  // padding (§4.5); one block per plan.
   const int64_t n_off = p.mask_heads * rows_total + 1;
+  const int64_t tasks = rows_total * p.heads_q;
   Carver ce;
-  const size_t o_p_off = ce.take<int32_t>(n_off);
-  const size_t o_f_off = ce.take<int32_t>(n_off);
-  const size_t o_p_idx = ce.take<int32_t>(pnnz);
-  const size_t o_f_idx = ce.take<int32_t>(fnnz);
-  const size_t o_masks = ce.take<uint32_t>(pnnz * tq * (tk / 32));
-  void* exact_block = nullptr;
-  if ((e = hipMallocFromPoolAsync(&exact_block, ce.off, pool, s)) != hipSuccess) {
-    release();
-    return device_status(e, "exact plan allocation");
-  }
-  d.p_off = at<int32_t>(exact_block, o_p_off);
-  d.f_off = at<int32_t>(exact_block, o_f_off);
-  d.p_idx = at<int32_t>(exact_block, o_p_idx);
-  d.f_idx = at<int32_t>(exact_block, o_f_idx);
-  d.p_masks = at<uint32_t>(exact_block, o_masks);
-  if ((e = launch_plan_materialize(g, mask_func, d, w, (int32_t)rows_total, s)) != hipSuccess) {
-    hipFreeAsync(exact_block, s);
-    release();
+  const size_t e_header = ce.take<int32_t>(8);
+  const size_t e_seqdesc = ce.take<int32_t>(8 * (int64_t)p.batch);
+  const size_t e_cu_rows = ce.take<int32_t>(p.batch + 1);
+  const size_t e_cu_q = ce.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 0);
+  const size_t e_cu_k = ce.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 0);
+  const size_t e_work_desc = ce.take<int32_t>(4 * tasks);
+  const size_t e_sec = ce.take<int32_t>(kNumQueues + 1);
+  const size_t e_rec = ce.take<int32_t>(kTaskRecInts * tasks);
+  const size_t e_p_off = ce.take<int32_t>(n_off);
+  const size_t e_f_off = ce.take<int32_t>(n_off);
+  const size_t e_p_idx = ce.take<int32_t>(pnnz);
+  const size_t e_f_idx = ce.take<int32_t>(fnnz);
+  const size_t e_masks = ce.take<uint32_t>(pnnz * tq * (tk / 32));
+  void* block = nullptr;
+  if ((e = hipMallocFromPoolAsync(&block, ce.off, pool, s)) != hipSuccess)
+    return device_status(e, "plan allocation");
+  PlanDev d;
+  d.header = at<int32_t>(block, e_header);
+  d.seqdesc = at<int32_t>(block, e_seqdesc);
+  d.cu_rows = at<int32_t>(block, e_cu_rows);
+  d.cu_q = p.layout == MPB_LAYOUT_THD ? at<int32_t>(block, e_cu_q) : nullptr;
+  d.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(block, e_cu_k) : nullptr;
+  d.work_desc = at<int32_t>(block, e_work_desc);
+  d.section_off = at<int32_t>(block, e_sec);
+  d.task_rec = at<int32_t>(block, e_rec);
+  d.p_off = at<int32_t>(block, e_p_off);
+  d.f_off = at<int32_t>(block, e_f_off);
+  d.p_idx = at<int32_t>(block, e_p_idx);
+  d.f_idx = at<int32_t>(block, e_f_idx);
+  d.p_masks = at<uint32_t>(block, e_masks);
+  if ((e = launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s)) !=
+      hipSuccess) {
+    hipFreeAsync(block, s);
     return device_status(e, "materialize launch");
   }
-  hipFreeAsync(work_block, s);
-  work_block = nullptr;
 
   mpb_plan* plan = new (std::nothrow) mpb_plan;
   if (!plan) {
-    hipFreeAsync(exact_block, s);
-    release();
+    hipFreeAsync(block, s);
     return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
   }
   plan->device = dev;
@@ -432,12 +498,10 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   plan->geo = g;
   plan->dev = d;
   plan->rows_total = (int32_t)rows_total;
-  plan->num_tasks = (int32_t)(rows_total * p.heads_q);
+  plan->num_tasks = (int32_t)tasks;
   for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
-  plan->geo_block = geo_block;
-  plan->exact_block = exact_block;
-  plan->geo_bytes = cg.off;
-  plan->exact_bytes = ce.off;
+  plan->block = block;
+  plan->bytes = ce.off;
   plan->stream = s;
   *out = plan;
   return ok();
@@ -448,8 +512,7 @@ mpb_status mask_plan_destroy(mpb_plan* plan) {
   int cur = 0;
   hipGetDevice(&cur);
   if (cur != plan->device) hipSetDevice(plan->device);
-  hipFreeAsync(plan->exact_block, plan->stream);
-  hipFreeAsync(plan->geo_block, plan->stream);
+  hipFreeAsync(plan->block, plan->stream);
   if (cur != plan->device) hipSetDevice(cur);
   delete plan;
   return ok();
@@ -466,7 +529,7 @@ mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info) {
   info->device = plan->device;
   info->problem = plan->prob;
   info->signature = plan->sig;
-  info->device_bytes = (int64_t)(plan->geo_bytes + plan->exact_bytes);
+  info->device_bytes = (int64_t)plan->bytes;
   return ok();
 }
 

@@ -58,7 +58,8 @@ def compare_plan(gp, op):
 def check_schedule(w, gp, tile_q, num_sections=8):
     """The forward schedule is a permutation of all (row, head) tasks with the
     right q_valid_rows; positive-cost tasks sit in their (batch, kv-head)
-    section in descending cost with canonical ties; zero-cost tasks last."""
+    section in descending cost, ties by flat mask row (head-major) and then
+    head; zero-cost tasks last, in the same tie order."""
     wd, so = gp["work_desc"], gp["section_off"]
     cu_rows, sd = gp["cu_rows"], gp["seqdesc"]
     rows_total = int(cu_rows[-1])
@@ -83,12 +84,13 @@ def check_schedule(w, gp, tile_q, num_sections=8):
             q_len = int(sd[b][2])
             assert qv == min(tile_q, q_len - i * tile_q)
             c = cost(b, h, i)
+            tie = (b, i, h) if w.mask_heads == 1 else (h, b, i)
             if s < num_sections:
                 assert c > 0 and (b * w.heads_k + h // group) % num_sections == s
-                key = (-c, b, h, i)
+                key = (-c,) + tie
             else:
                 assert c == 0
-                key = (b, h, i)
+                key = tie
             assert prev is None or key > prev, (s, prev, key)
             prev = key
     assert len(seen) == n

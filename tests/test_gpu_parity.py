@@ -221,6 +221,24 @@ def test_one_plan_two_streams():
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_builds_alternating_streams():
+    """Consecutive builds on different streams (the build workspace is shared
+    by one host thread's builds) give the oracle's plans."""
+    ws = [W.make("varlen_doc", small=True), W.make("block_sparse", small=True)]
+    _print_case("alternating_streams")
+    ds = [G.device_inputs(w) for w in ws]
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    plans = []
+    for r in range(2):
+        for w, d, s in ((ws[0], ds[0], s1), (ws[1], ds[1], s2)):
+            plans.append((w, G.build_plan(w, d, stream=s)))
+    torch.cuda.synchronize()
+    for w, plan in plans:
+        pl = plan.problem
+        G.compare_plan(plan.export(), oracle.build_plan(w, pl.tile_q, pl.tile_k))
+
+
 # ------------------------------------------------------------------ errors
 
 def _expect(status_name, fn):
