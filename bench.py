@@ -8,10 +8,16 @@ followed by flex_attn_fwd over the plan.  Default workload: sliding window
 
 Prints ONE JSON line.  `value` is effective TFLOP/s of the whole step, counting
 4*d FLOPs per visible (q, k) pair (unmasked score entries only).  The
-attention kernel alone is reported under "fwd" and "roofline" (its duration
-measured with HIP events on the launch stream inside the timed loop).  The CPU
-oracle is timed on the host cores as "cpu_baseline" (a reported baseline, not a
-target).
+attention kernel alone is reported under "fwd" and "roofline": its average
+launch duration is measured with HIP events on the launch stream, around each
+forward of the timed steps and around back-to-back launches on one plan; the
+roofline uses the latter (the per-step spans also hold host launch latency).
+"roofline.traffic" is the kernel's HBM bytes per launch from the committed
+counter summary, when that summary was taken on the current kernel source.
+The CPU oracle is timed on the host cores as "cpu_baseline" (a reported
+baseline, not a target).
+
+  --summarize stats|pmc DIRS  digests rocprofv3 csv output instead.
 """
 from __future__ import annotations
 
@@ -65,6 +71,92 @@ def cpu_baseline(w, min_seconds=10.0):
     return time.perf_counter() - t0, passes, threads
 
 
+ATTN_SOURCE = os.path.join(ROOT, "mask_planned_block_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_window_sink_pmc.txt")
+
+
+def source_digest(path=ATTN_SOURCE):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _kernel_group(name):
+    for key in ("attn_fwd_kernel", "plan_classify_kernel", "plan_schedule_kernel",
+                "plan_materialize_kernel", "plan_geometry_kernel", "elementwise"):
+        if key in name:
+            return key
+    return None
+
+
+def summarize(kind, dirs, copy_mb=0):
+    """Digest of rocprofv3 csv output under the comma-separated `dirs`:
+    per-kernel duration statistics (kind "stats") or per-dispatch counter
+    averages (kind "pmc": FETCH_SIZE and WRITE_SIZE, in KiB as read).  For
+    pmc, the calibration pass (a streaming elementwise kernel that reads and
+    writes copy_mb MiB: the largest elementwise dispatch) gives the factor
+    between each counter and the bytes it moved; the attention kernel's
+    averages scaled by it give its HBM traffic per launch."""
+    import csv
+    import glob
+    paths = lambda pat: sorted(p for d in dirs.split(",") for p in glob.glob(os.path.join(d, pat)))
+    if kind == "stats":
+        for path in paths("*kernel_stats.csv"):
+            print("# %s" % os.path.basename(path))
+            print("%-44s %7s %10s %10s %10s" % ("kernel", "calls", "avg_us", "min_us", "max_us"))
+            for r in csv.DictReader(open(path)):
+                tmpl = r["Name"].replace("(anonymous namespace)::", "").replace(
+                    "mpb::", "").replace("void ", "").split("(")[0]
+                print("%-44s %7s %10.2f %10.2f %10.2f" % (
+                    tmpl[:44], r["Calls"], float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+        return
+    per = {}
+    for path in paths("*counter_collection.csv"):
+        for r in csv.DictReader(open(path)):
+            g = _kernel_group(r["Kernel_Name"])
+            if g is not None:
+                per.setdefault((g, r["Counter_Name"]), []).append(
+                    (int(r["Grid_Size"]), float(r["Counter_Value"])))
+    total = 0.0
+    complete = True
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        cal = per.get(("elementwise", c))
+        att = per.get(("attn_fwd_kernel", c))
+        if not cal or not att or copy_mb <= 0:
+            print("# %s: missing calibration or attention dispatches" % c)
+            complete = False
+            continue
+        grid, v = max(cal)
+        factor = copy_mb * 1024.0 / v
+        avg = sum(x for _, x in att) / len(att)
+        print("calibration %s grid=%d read_kib=%.1f known_kib=%d factor=%.4f"
+              % (c, grid, v, copy_mb * 1024, factor))
+        print("attn_fwd_kernel %s dispatches=%d avg_kib=%.1f scaled_bytes=%.0f"
+              % (c, len(att), avg, avg * 1024 * factor))
+        total += avg * 1024 * factor
+        for (g, cc), vals in sorted(per.items()):
+            if cc == c and g not in ("elementwise", "attn_fwd_kernel"):
+                xs = [x for _, x in vals]
+                print("%s %s dispatches=%d avg_kib=%.1f scaled_bytes=%.0f"
+                      % (g, c, len(xs), sum(xs) / len(xs), sum(xs) / len(xs) * 1024 * factor))
+    if complete:
+        print("attn_source_sha256_16=%s" % source_digest())
+        print("traffic_bytes_per_launch=%.0f" % total)
+
+
+def load_traffic(expected_digest):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when it is missing or was taken on another version of the kernel."""
+    try:
+        kv = dict(line.strip().split("=", 1) for line in open(TRAFFIC_FILE)
+                  if "=" in line and not line.startswith("#"))
+        if kv.get("attn_source_sha256_16") != expected_digest:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,7 +171,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--ablation", action="store_true",
                     help="also time the forward with full tiles forced through the masked path")
+    ap.add_argument("--dense-reference", action="store_true",
+                    help="also time the all-visible forward at the same shape")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="end with plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
+                    help="print a summary of rocprofv3 csv output under comma-separated DIRS "
+                         "(KIND: stats or pmc) and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize[0], args.summarize[1], args.copy_calibration_mb)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -144,6 +246,7 @@ def main():
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
     fwd_in_step_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    fwd_in_step_med_us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
 
     # steady-state forward on one plan (back-to-back launches)
     plan = keep[-1]
@@ -177,13 +280,48 @@ def main():
         p2.close()
     plan_us = float(np.median(tb)) * 1e6
 
+    # all-visible forward at the same shape (nfunc = 1, F0 = k_len): the
+    # dense attention this mask skips most of
+    dense_ref = None
+    if args.dense_reference and w.layout == W.LAYOUT_BSHD:
+        mf_all = torch.full((1, 1, w.total_q), w.seqlen_k, dtype=torch.int32, device="cuda")
+        prob_all = mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                                    w.total_k, w.heads_q, w.heads_k, w.head_dim, 1, 1,
+                                    args.tile_q, args.tile_k)
+        plan_all = mpb.mask_plan_build(prob_all, mf_all, None, None, stream=stream)
+        kw_all = dict(kw, softcap=None, alibi_slopes=None)
+        for _ in range(3):
+            mpb.flex_attn_fwd(plan_all, d["q"], d["k"], d["v"], **kw_all)
+        e0.record(stream)
+        for _ in range(args.fwd_iters):
+            mpb.flex_attn_fwd(plan_all, d["q"], d["k"], d["v"], **kw_all)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_all = e0.elapsed_time(e1) * 1e3 / args.fwd_iters
+        fl_all = 4.0 * w.head_dim * w.total_q * w.seqlen_k * w.heads_q
+        peak_all = PEAK_BF16_TFLOPS if w.dtype == W.DTYPE_BF16 else PEAK_FP32_MFMA_TFLOPS
+        dense_ref = {"us": round(us_all, 2), "tflops": round(fl_all / us_all / 1e6, 2),
+                     "pct_peak": round(100 * fl_all / us_all / 1e6 / peak_all, 2)}
+        plan_all.close()
+
+    if args.copy_calibration_mb > 0:
+        # streaming calibration: reads and writes exactly copy_calibration_mb MiB
+        src = torch.ones((args.copy_calibration_mb << 20) // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+
     d_ = w.head_dim
     eff = 4.0 * d_ * stats["visible_pairs"]
     exe = 4.0 * d_ * stats["executed_pairs"]
     dense = 4.0 * d_ * stats["dense_pairs"]
     peak = PEAK_BF16_TFLOPS if w.dtype == W.DTYPE_BF16 else PEAK_FP32_MFMA_TFLOPS
     fwd_s = fwd_in_step_us * 1e-6
-    achieved = eff / fwd_s / 1e12
+    # roofline: the kernel's average launch duration from the back-to-back
+    # launches on one plan (HIP events on the launch stream); the per-step
+    # event spans also hold the host's launch latency
+    achieved = eff / (fwd_ss_us * 1e-6) / 1e12
+    traffic = load_traffic(source_digest()) if args.workload == "window_sink" else None
 
     res = {
         "metric": METRIC,
@@ -203,9 +341,10 @@ def main():
                    "head_dim": w.head_dim, "mask_heads": w.mask_heads, "nfunc": w.nfunc,
                    "tile": "%dx%d" % (tq, tk), "step": "mask_plan_build + flex_attn_fwd"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": None,
-                     "kernel": "attn_fwd_kernel", "achieved_basis": "effective flops / "
-                     "forward duration (HIP events, timed loop)"},
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic,
+                     "kernel": "attn_fwd_kernel", "achieved_basis": "effective flops per launch / "
+                     "average launch duration (HIP events around %d back-to-back launches on "
+                     "the launch stream)" % args.fwd_iters},
         "fwd": {
             "us_in_step": round(fwd_in_step_us, 2),
             "us_steady": round(fwd_ss_us, 2),
@@ -217,6 +356,8 @@ def main():
             "effective_gflop": round(eff / 1e9, 4), "executed_gflop": round(exe / 1e9, 4),
             "dense_gflop": round(dense / 1e9, 4),
             "force_partial_us": None if abl is None else round(abl, 2),
+            "us_in_step_median": round(fwd_in_step_med_us, 2),
+            "dense_all_visible": dense_ref,
         },
         "plan": {"build_us_host": round(plan_us, 1), **stats},
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
