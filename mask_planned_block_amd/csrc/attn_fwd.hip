@@ -70,36 +70,54 @@ __device__ constexpr int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k
 
 // ----------------------------------------------------------------- bf16 tiles
 
-template <int D_, int NW_, int TKV_>
+// QB 32-row Q blocks per wavefront: every K or V^T fragment read from LDS
+// feeds QB MFMAs, and one block's softmax can run while the other block's
+// MFMAs are in flight.  QB = 2 needs one wavefront per SIMD.
+//
+// K goes straight from HBM into LDS (buffer_load ... lds: lane l of a
+// wavefront writes LDS bytes [16 l, 16 l + 16) of the instruction's 1 KiB),
+// rows unpadded, the 16-byte chunk c of row r stored at chunk position
+// c ^ (r % CH): 8 or 16 consecutive lanes reading one logical chunk of
+// consecutive rows then hit distinct banks.  V passes through registers to be
+// stored transposed.
+template <int D_, int NW_, int TKV_, int QB_>
 struct Bf16Ops {
   using T = __bf16;
-  static constexpr int D = D_, NW = NW_, TKV = TKV_;
-  static constexpr int NT = NW * 64, TQ = 32 * NW, NKB = TKV / 32;
+  static constexpr int D = D_, NW = NW_, TKV = TKV_, QB = QB_;
+  static constexpr int NT = NW * 64, TQ = 32 * QB * NW, NKB = TKV / 32;
+  static constexpr int WPE = QB == 1 ? 2 : 1;   // wavefronts per SIMD
   static constexpr int ESZ = 2;
-  static constexpr int KP = D + 8;    // K row pitch (elements): 16 B pad, conflict-free b128 reads
+  static constexpr int CH = D / 8;              // 16-byte chunks per K row
+  static constexpr int RPI = 1024 / (D * 2);    // K rows per wavefront load instruction
+  static constexpr int KI = TKV / RPI / NW;     // K load instructions per wavefront per tile
   static constexpr int VP = TKV + 8;  // V^T row pitch (elements)
-  static constexpr int KCH = TKV * D / 8 / NT;          // 16-byte K chunks per thread
   static constexpr int VCH = (TKV / 2) * (D / 8) / NT;  // V row-pair chunks per thread
-  static_assert(KCH * NT * 8 == TKV * D, "K tile must split evenly over threads");
+  static_assert(KI * RPI * NW == TKV, "K tile must split evenly over wavefronts");
   static_assert(VCH * NT * 16 == TKV * D, "V tile must split evenly over threads");
-  static_assert(D % 32 == 0 && TKV % 32 == 0, "tile shape");
+  static_assert(D % 32 == 0 && TKV % 32 == 0 && CH <= 16, "tile shape");
 
   struct Smem {
-    __bf16 k[2][TKV * KP];
+    __bf16 k[2][TKV * D];
     __bf16 vt[2][D * VP];
   };
-  struct QFrag { bf16x8 q[D / 16]; };
-  struct Stage { u32x4 k[KCH]; u32x4 v0[VCH]; u32x4 v1[VCH]; };
-  struct PFrag { bf16x8 p[NKB][2]; };
+  struct QFrag { bf16x8 q[QB][D / 16]; };
+  struct Stage { u32x4 v0[VCH]; u32x4 v1[VCH]; };
+  typedef bf16x8 PBlock[NKB][2];
+  struct PFrag { PBlock p[QB]; };
 
   // tile_off = byte offset of the tile's first row; rs = bytes per token row.
-  static __device__ inline void load(Stage& st, rsrc_t rk, rsrc_t rv, uint32_t tile_off,
-                                     uint32_t rs, int tid) {
+  // K lands in sm.k[stage] when the issuing wavefront's loads complete.
+  static __device__ inline void load(Stage& st, Smem& sm, int stage, rsrc_t rk, rsrc_t rv,
+                                     uint32_t tile_off, uint32_t rs, int tid) {
+    const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      st.k[c] = bload16(rk, tile_off + r * rs + c8 * 16);
+    for (int c = 0; c < KI; ++c) {
+      const int r0 = (c * NW + wave) * RPI;
+      const int r = r0 + lane / CH;
+      const int lc = (lane % CH) ^ (r % CH);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rk, (__attribute__((address_space(3))) void*)&sm.k[stage][r0 * D], 16,
+          (int)(tile_off + r * rs + lc * 16), 0, 0, 0);
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
@@ -112,12 +130,6 @@ struct Bf16Ops {
   }
 
   static __device__ inline void store(const Stage& st, Smem& sm, int stage, int tid) {
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = tid + c * NT;
-      const int r = idx / (D / 8), c8 = idx % (D / 8);
-      *(u32x4*)&sm.k[stage][r * KP + c8 * 8] = st.k[c];
-    }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = tid + c * NT;
@@ -133,39 +145,59 @@ struct Bf16Ops {
     }
   }
 
-  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, uint32_t row_off, int b2) {
+  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, const uint32_t (&row_off)[QB],
+                                       int b2) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf.q[s] = __builtin_bit_cast(bf16x8, bload16(rq, row_off + (16 * s + 8 * b2) * ESZ));
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s)
+        qf.q[qb][s] =
+            __builtin_bit_cast(bf16x8, bload16(rq, row_off[qb] + (16 * s + 8 * b2) * ESZ));
   }
 
-  static __device__ inline void qk(f32x16 (&acc)[NKB], const QFrag& qf, const Smem& sm, int stage,
-                                   int lane) {
-    const __bf16* kb = &sm.k[stage][(lane & 31) * KP + 8 * (lane >> 5)];
+  // K fragments are read from LDS one k-step ahead of the MFMAs using them.
+  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const Smem& sm,
+                                   int stage, int lane) {
+    // row kk*32 + lane%32, logical chunk 2s + lane/32, at chunk (2s) ^ x
+    const __bf16* kb = &sm.k[stage][(lane & 31) * D];
+    const int x = (lane >> 5) ^ (lane & (CH - 1));
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) acc[kk] = f32x16{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) acc[qb][kk] = f32x16{};
+    bf16x8 a[2][NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) a[0][kk] = *(const bf16x8*)(kb + kk * 32 * D + x * 8);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < D / 16) {
+        const int off = ((2 * (s + 1)) ^ x) * 8;
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(kb + kk * 32 * KP + 16 * s);
-        acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[s], acc[kk], 0, 0, 0);
+        for (int kk = 0; kk < NKB; ++kk)
+          a[cur ^ 1][kk] = *(const bf16x8*)(kb + kk * 32 * D + off);
       }
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][kk] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][kk], qf.q[qb][s], acc[qb][kk], 0, 0, 0);
     }
   }
 
-  static __device__ inline void to_p(PFrag& pf, const f32x16 (&acc)[NKB]) {
+  static __device__ inline void to_p(PBlock& pb, const f32x16 (&acc)[NKB]) {
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pf.p[kk][m][e] = (__bf16)acc[kk][8 * m + e];
+        for (int e = 0; e < 8; ++e) pb[kk][m][e] = (__bf16)acc[kk][8 * m + e];
   }
 
   // Sum of the bf16-rounded weights (the values P.V uses), two per
   // v_dot2_f32_bf16 against (1, 1).
-  static __device__ inline float row_sum(const PFrag& pf, const f32x16 (&)[NKB]) {
+  static __device__ inline float row_sum(const PBlock& pb, const f32x16 (&)[NKB]) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float s = 0.0f;
@@ -175,24 +207,32 @@ struct Bf16Ops {
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const bf16x2 pr = {pf.p[kk][m][e], pf.p[kk][m][e + 1]};
+          const bf16x2 pr = {pb[kk][m][e], pb[kk][m][e + 1]};
           s = __builtin_amdgcn_fdot2_f32_bf16(pr, one, s, false);
         }
     return s;
   }
 
-  static __device__ inline void pv(f32x16 (&o)[D / 32], const PFrag& pf, const Smem& sm,
+  // V^T fragments in the order (db, kk, m), each read one step ahead.
+  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const Smem& sm,
                                    int stage, int lane) {
     const __bf16* vb = &sm.vt[stage][(lane & 31) * VP + 8 * (lane >> 5)];
+    constexpr int NS = (D / 32) * NKB * 2;
+    auto frag = [&](int i) {
+      const int db = i / (NKB * 2), kk = (i / 2) % NKB, m = i % 2;
+      return *(const bf16x8*)(vb + db * 32 * VP + kk * 32 + 16 * m);
+    };
+    bf16x8 a[2];
+    a[0] = frag(0);
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int i = 0; i < NS; ++i) {
+      const int cur = i & 1;
+      if (i + 1 < NS) a[cur ^ 1] = frag(i + 1);
+      const int db = i / (NKB * 2), kk = (i / 2) % NKB, m = i % 2;
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const bf16x8 a = *(const bf16x8*)(vb + db * 32 * VP + kk * 32 + 16 * m);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf.p[kk][m], o[db], 0, 0, 0);
-        }
+      for (int qb = 0; qb < QB; ++qb)
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur], pf.p[qb][kk][m], o[qb][db], 0, 0, 0);
+    }
   }
 
   static __device__ inline void store_o(rsrc_t ro, uint32_t row_off, const f32x16 (&o)[D / 32],
@@ -217,7 +257,9 @@ template <int D_, int NW_, int TKV_>
 struct F32Ops {
   using T = float;
   static constexpr int D = D_, NW = NW_, TKV = TKV_;
+  static constexpr int QB = 1;
   static constexpr int NT = NW * 64, TQ = 32 * NW, NKB = TKV / 32;
+  static constexpr int WPE = 2;
   static constexpr int ESZ = 4;
   static constexpr int KP = D + 4;   // 16-byte reads of 32 rows: banks 4r, conflict-free
   static constexpr int VP = D + 8;   // lanes 32..63 read row k+4: +32 banks
@@ -228,12 +270,13 @@ struct F32Ops {
     float k[2][TKV * KP];
     float v[2][TKV * VP];
   };
-  struct QFrag { float q[D / 2]; };
+  struct QFrag { float q[QB][D / 2]; };
   struct Stage { u32x4 k[KCH]; u32x4 v[KCH]; };
-  struct PFrag { f32x16 p[NKB]; };
+  typedef f32x16 PBlock[NKB];
+  struct PFrag { PBlock p[QB]; };
 
-  static __device__ inline void load(Stage& st, rsrc_t rk, rsrc_t rv, uint32_t tile_off,
-                                     uint32_t rs, int tid) {
+  static __device__ inline void load(Stage& st, Smem&, int, rsrc_t rk, rsrc_t rv,
+                                     uint32_t tile_off, uint32_t rs, int tid) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
@@ -253,20 +296,22 @@ struct F32Ops {
     }
   }
 
-  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, uint32_t row_off, int b2) {
+  static __device__ inline void load_q(QFrag& qf, rsrc_t rq, const uint32_t (&row_off)[QB],
+                                       int b2) {
 #pragma unroll
     for (int s = 0; s < D / 2; s += 4) {
-      const f32x4 x = __builtin_bit_cast(f32x4, bload16(rq, row_off + (b2 * (D / 2) + s) * ESZ));
+      const f32x4 x =
+          __builtin_bit_cast(f32x4, bload16(rq, row_off[0] + (b2 * (D / 2) + s) * ESZ));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qf.q[s + e] = x[e];
+      for (int e = 0; e < 4; ++e) qf.q[0][s + e] = x[e];
     }
   }
 
-  static __device__ inline void qk(f32x16 (&acc)[NKB], const QFrag& qf, const Smem& sm, int stage,
-                                   int lane) {
+  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const Smem& sm,
+                                   int stage, int lane) {
     const float* kb = &sm.k[stage][(lane & 31) * KP + (lane >> 5) * (D / 2)];
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) acc[kk] = f32x16{};
+    for (int kk = 0; kk < NKB; ++kk) acc[0][kk] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 2; s += 4) {
 #pragma unroll
@@ -274,17 +319,18 @@ struct F32Ops {
         const f32x4 a = *(const f32x4*)(kb + kk * 32 * KP + s);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          acc[kk] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf.q[s + e], acc[kk], 0, 0, 0);
+          acc[0][kk] =
+              __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf.q[0][s + e], acc[0][kk], 0, 0, 0);
       }
     }
   }
 
-  static __device__ inline void to_p(PFrag& pf, const f32x16 (&acc)[NKB]) {
+  static __device__ inline void to_p(PBlock& pb, const f32x16 (&acc)[NKB]) {
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) pf.p[kk] = acc[kk];
+    for (int kk = 0; kk < NKB; ++kk) pb[kk] = acc[kk];
   }
 
-  static __device__ inline float row_sum(const PFrag&, const f32x16 (&acc)[NKB]) {
+  static __device__ inline float row_sum(const PBlock&, const f32x16 (&acc)[NKB]) {
     float s = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk)
@@ -293,7 +339,7 @@ struct F32Ops {
     return s;
   }
 
-  static __device__ inline void pv(f32x16 (&o)[D / 32], const PFrag& pf, const Smem& sm,
+  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const Smem& sm,
                                    int stage, int lane) {
     const int b2 = lane >> 5;
 #pragma unroll
@@ -304,7 +350,7 @@ struct F32Ops {
         for (int v = 0; v < 16; ++v) {
           const int k = kk * 32 + 8 * (v / 4) + 4 * b2 + (v % 4);
           const float a = sm.v[stage][k * VP + db * 32 + (lane & 31)];
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.p[kk][v], o[db], 0, 0, 0);
+          o[0][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.p[0][kk][v], o[0][db], 0, 0, 0);
         }
   }
 
@@ -369,16 +415,15 @@ struct RowState {
   float l;   // this lane's partial sum of the weights
 };
 
-// One K tile: scores on MFMA, score_mod and (MASKED) the predicate, online
-// softmax, P.V on MFMA.
+// Softmax of one 32-row Q block over one K tile: score_mod and (MASKED) the
+// predicate, online max with lazy rescale of the block's O, exponentials,
+// P in the MFMA operand type and the row sum.
 template <class Ops, int MOD, bool MASKED>
-__device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
-                                 const typename Ops::Smem& sm, int stage, int lane,
-                                 const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
-                                 f32x16 (&o)[Ops::D / 32], RowState& rs) {
+__device__ inline void softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
+                                     const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
+                                     f32x16 (&o)[Ops::D / 32], RowState& rs,
+                                     typename Ops::PBlock& pb) {
   constexpr int NKB = Ops::NKB, D = Ops::D;
-  f32x16 acc[NKB];
-  Ops::qk(acc, qf, sm, stage, lane);
   // Without a score_mod the max is taken on the raw dot products (scale > 0)
   // and scaled once; the exponent is then one FMA per element.
   float mt = kNegInf;
@@ -427,17 +472,34 @@ __device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag&
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[kk][v] = exp2_fast(acc[kk][v] - m_use);
   }
+  Ops::to_p(pb, acc);
+  rs.l += Ops::row_sum(pb, acc);
+}
+
+// One K tile for the wavefront's QB Q blocks: scores on MFMA, softmax per
+// block, P.V on MFMA.
+template <class Ops, int MOD, bool MASKED>
+__device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
+                                 const typename Ops::Smem& sm, int stage, int lane,
+                                 const uint32_t (&mw)[Ops::QB][Ops::NKB],
+                                 const float (&kq0)[Ops::QB], float slope,
+                                 f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
+  constexpr int QB = Ops::QB, NKB = Ops::NKB;
+  f32x16 acc[QB][NKB];
+  Ops::qk(acc, qf, sm, stage, lane);
   typename Ops::PFrag pf;
-  Ops::to_p(pf, acc);
-  rs.l += Ops::row_sum(pf, acc);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+    softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb], pf.p[qb]);
   Ops::pv(o, pf, sm, stage, lane);
 }
 
 // One workgroup per task, in the plan's launch order (record blockIdx.x).
 template <class Ops, int MOD>
-__global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(Ops::WPE, Ops::WPE)))
 void attn_fwd_kernel(AttnParams p) {
   constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
+  constexpr int QB = Ops::QB;
   __shared__ typename Ops::Smem sm;
 
   const int tid = threadIdx.x;
@@ -473,30 +535,44 @@ void attn_fwd_kernel(AttnParams p) {
   const rsrc_t rk = make_rsrc(kbase, (uint32_t)k_len * kv_rs);
   const rsrc_t rv = make_rsrc(vbase, (uint32_t)k_len * kv_rs);
 
-  const int qloc = m_block * TQ + 32 * wave + lq;  // sample-local Q row of this lane
-  const uint32_t q_row_off = (uint32_t)qloc * q_rs;
+  // Sample-local Q row of this lane in each of the wavefront's blocks.
+  int qloc[QB];
+  uint32_t q_row_off[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    qloc[qb] = m_block * TQ + 32 * (QB * wave + qb) + lq;
+    q_row_off[qb] = (uint32_t)qloc[qb] * q_rs;
+  }
 
   // tile t of the task: partial list first, then full list (§6.1)
   auto tile_j = [&](int t) {
     return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
   };
-  auto load_masks = [&](int t, uint32_t (&mw)[NKB]) {
-    if (t < np) {
-      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
+  auto load_masks = [&](int t, uint32_t (&mw)[QB][NKB]) {
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk] >> (4 * b2);
-    } else {
+    for (int qb = 0; qb < QB; ++qb) {
+      if (t < np) {
+        const uint32_t* src =
+            p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * (QB * wave + qb) + lq) * NKB;
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
+        for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = src[kk] >> (4 * b2);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = 0xFFFFFFFFu;
+      }
     }
   };
 
   typename Ops::Stage st;
-  uint32_t mw_cur[NKB], mw_next[NKB];
+  uint32_t mw_cur[QB][NKB], mw_next[QB][NKB];
   int j_cur = j_first;
+  // K-tile index of tile t+1, read one tile ahead of its use so that no
+  // tile waits on the index load before issuing its prefetch.
+  int j_ahead = 0;
   if (ntiles > 0) {
-    Ops::load(st, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
+    Ops::load(st, sm, 0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
     load_masks(0, mw_cur);
+    if (ntiles > 1) j_ahead = tile_j(1);
   }
   typename Ops::QFrag qf;
   Ops::load_q(qf, rq, q_row_off, b2);
@@ -505,48 +581,67 @@ void attn_fwd_kernel(AttnParams p) {
   if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) slope = p.slopes[h] * kLog2e;
   if constexpr (MOD == kModAlibiSoftcap) slope = p.slopes[h] * p.alibi_k;
 
-  f32x16 o[D / 32];
+  f32x16 o[QB][D / 32];
+  RowState rs[QB];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = f32x16{};
-  RowState rs{kNegInf, 0.0f};
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[qb][db] = f32x16{};
+    rs[qb] = RowState{kNegInf, 0.0f};
+  }
 
   // Two loops, as in §6.1: the partial list with its predicate, then the full
-  // list without one.  The K/V prefetch runs one tile ahead across both.
+  // list without one.  The K/V prefetch runs one tile ahead across both, the
+  // tile-index read two tiles ahead.
   int t = 0;
+  int j_pending = 0;   // index of tile t+2, in flight during tile t
   auto advance = [&](int stage) {
     const bool more = t + 1 < ntiles;
-    int j_next = 0;
+    const int j_next = j_ahead;
     if (more) {
-      j_next = tile_j(t + 1);
-      Ops::load(st, rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
+      Ops::load(st, sm, stage ^ 1, rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
       load_masks(t + 1, mw_next);
     }
+    if (t + 2 < ntiles) j_pending = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
     return j_next;
   };
   auto retire = [&](int stage, int j_next) {
     if (t + 1 < ntiles) {
       Ops::store(st, sm, stage ^ 1, tid);
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) mw_cur[qb][kk] = mw_next[qb][kk];
       j_cur = j_next;
     }
+    // this wavefront's loads straight into LDS have landed; the barrier
+    // publishes them and the stores above to the whole workgroup
+    __builtin_amdgcn_s_waitcnt(0);
+    if (t + 2 < ntiles) j_ahead = __builtin_amdgcn_readfirstlane(j_pending);
     __syncthreads();
+  };
+  auto kq_of = [&](float (&kq0)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) kq0[qb] = (float)(j_cur * TKV + 4 * b2 - qloc[qb]);
   };
   if (ntiles > 0) {
     Ops::store(st, sm, 0, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int n_masked = p.force_partial ? ntiles : np;
     for (; t < n_masked; ++t) {
       const int stage = t & 1;
       const int j_next = advance(stage);
-      const float kq0 = (float)(j_cur * TKV + 4 * b2 - qloc);
+      float kq0[QB];
+      kq_of(kq0);
       tile_step<Ops, MOD, true>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
       retire(stage, j_next);
     }
     for (; t < ntiles; ++t) {
       const int stage = t & 1;
       const int j_next = advance(stage);
-      const float kq0 = (float)(j_cur * TKV + 4 * b2 - qloc);
+      float kq0[QB];
+      kq_of(kq0);
       tile_step<Ops, MOD, false>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
       retire(stage, j_next);
     }
@@ -554,12 +649,15 @@ void attn_fwd_kernel(AttnParams p) {
 
   // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf.
   // Rows past q_len are dropped by the O descriptor's range check.
-  const float l_tot = pair_sum(rs.l);
-  const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
-  Ops::store_o(ro, q_row_off, o, inv, b2);
-  if (b2 == 0 && qloc < q_len) {
-    p.lse[(int64_t)h * p.total_q + q_off + qloc] =
-        l_tot > 0.0f ? (rs.m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l_tot = pair_sum(rs[qb].l);
+    const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
+    Ops::store_o(ro, q_row_off[qb], o[qb], inv, b2);
+    if (b2 == 0 && qloc[qb] < q_len) {
+      p.lse[(int64_t)h * p.total_q + q_off + qloc[qb]] =
+          l_tot > 0.0f ? (rs[qb].m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+    }
   }
 }
 
@@ -581,12 +679,12 @@ hipError_t launch_ops(int mod, int num_tasks, const AttnParams& p, hipStream_t s
 
 // The consumer table: (dtype, head_dim, tile_q, tile_k) -> kernel family.
 #define MPB_VARIANTS(X)                         \
-  X(MPB_DTYPE_BF16, 128, 128, 64, Bf16Ops<128, 4, 64>) \
-  X(MPB_DTYPE_BF16, 128, 64, 64, Bf16Ops<128, 2, 64>)  \
-  X(MPB_DTYPE_BF16, 128, 128, 32, Bf16Ops<128, 4, 32>) \
-  X(MPB_DTYPE_BF16, 128, 64, 32, Bf16Ops<128, 2, 32>)  \
-  X(MPB_DTYPE_BF16, 64, 128, 64, Bf16Ops<64, 4, 64>)   \
-  X(MPB_DTYPE_BF16, 64, 64, 64, Bf16Ops<64, 2, 64>)    \
+  X(MPB_DTYPE_BF16, 128, 128, 64, Bf16Ops<128, 4, 64, 1>) \
+  X(MPB_DTYPE_BF16, 128, 64, 64, Bf16Ops<128, 2, 64, 1>)  \
+  X(MPB_DTYPE_BF16, 128, 128, 32, Bf16Ops<128, 4, 32, 1>) \
+  X(MPB_DTYPE_BF16, 128, 64, 32, Bf16Ops<128, 2, 32, 1>)  \
+  X(MPB_DTYPE_BF16, 64, 128, 64, Bf16Ops<64, 4, 64, 1>)   \
+  X(MPB_DTYPE_BF16, 64, 64, 64, Bf16Ops<64, 2, 64, 1>)    \
   X(MPB_DTYPE_FP32, 64, 64, 64, F32Ops<64, 2, 64>)     \
   X(MPB_DTYPE_FP32, 64, 64, 32, F32Ops<64, 2, 32>)     \
   X(MPB_DTYPE_FP32, 128, 64, 32, F32Ops<128, 2, 32>)
