@@ -486,12 +486,19 @@ __device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag&
                                  f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
   constexpr int QB = Ops::QB, NKB = Ops::NKB;
   f32x16 acc[QB][NKB];
+  // Wavefront priority: high while issuing MFMAs, low during the softmax, so
+  // that of the wavefronts sharing a SIMD the one with matrix work issues
+  // first and the other fills the VALU meanwhile.
+  __builtin_amdgcn_s_setprio(1);
   Ops::qk(acc, qf, sm, stage, lane);
+  __builtin_amdgcn_s_setprio(0);
   typename Ops::PFrag pf;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
     softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb], pf.p[qb]);
+  __builtin_amdgcn_s_setprio(1);
   Ops::pv(o, pf, sm, stage, lane);
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // One workgroup per task, in the plan's launch order (record blockIdx.x).
