@@ -87,14 +87,23 @@ __device__ inline int rows_total_of(const PlanGeo& g, const PlanDev& d) {
   return g.layout == MPB_LAYOUT_BSHD ? g.upper_rows : d.cu_rows[g.batch];
 }
 
-// Inclusive prefix sum over the 64 lanes of a wavefront.
-__device__ inline int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off);
-    if (lane >= off) v += u;
-  }
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP moves:
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's last lane
+// is broadcast into row 1 and row 2's into row 3, then lane 31 into rows 2
+// and 3.  Lanes a move has no source for receive 0.
+__device__ inline int wave_incl_scan(int v, int /*lane*/) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
+}
+
+// Sum over the wavefront, in every lane.
+__device__ inline int wave_sum(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_scan(v, 0), 63);
 }
 
 }  // namespace
@@ -195,15 +204,27 @@ __device__ inline void set_tiles(uint32_t (&m)[4], int t0, int t1, int tg) {
   }
 }
 
+// OR / AND over the wavefront (same DPP pattern as the scan; lanes without a
+// source receive the identity), in every lane.
 __device__ inline uint32_t wave_or(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x |= (uint32_t)__shfl_xor((int)x, off);
-  return x;
+  int v = (int)x;
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);
+  v |= __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 __device__ inline uint32_t wave_and(uint32_t x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x &= (uint32_t)__shfl_xor((int)x, off);
-  return x;
+  int v = (int)x;
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false);
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x112, 0xf, 0xf, false);
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x114, 0xf, 0xf, false);
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x118, 0xf, 0xf, false);
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x142, 0xa, 0xf, false);
+  v &= __builtin_amdgcn_update_dpp(-1, v, 0x143, 0xc, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
 
 // Classification of one (mask head, Q plan row): one wavefront, lanes own rows
@@ -731,9 +752,7 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
   }
 #pragma unroll
   for (int s = 0; s < kNumQueues; ++s) {
-    int t = tot[s];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+    const int t = wave_sum(tot[s]);
     if (lane == 0 && t) atomicAdd(&s_tot[s], t);
   }
   __syncthreads();
