@@ -36,6 +36,8 @@ namespace mpb {
 
 namespace {
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
 __device__ inline int sample_of_row(const int32_t* cu_rows, int batch, int row) {
   // Largest b with cu_rows[b] <= row; empty samples share their prefix value
   // with the next sample and are skipped by taking the largest such b.
@@ -558,9 +560,14 @@ __device__ inline int row_cost(const PlanWork& w, int i) {
 
 // Number of KV heads hk in [0, Hk) with (b*Hk + hk) % 8 == s; they are
 // r, r+8, ... with r = (s - b*Hk) mod 8.
+// Section of KV head hk of sample b: (b*Hk + hk) mod 8, from the low bits
+// (unsigned arithmetic, exact modulo 8 whatever the product's size).
+__device__ inline int section_of(int b, int heads_k, int hk) {
+  return (int)(((uint32_t)b * (uint32_t)heads_k + (uint32_t)hk) & (kNumSections - 1));
+}
+
 __device__ inline int kv_heads_in_section(int b, int heads_k, int s, int* r_out) {
-  const int r = (int)(((int64_t)s - (int64_t)b * heads_k) % kNumSections + kNumSections) %
-                kNumSections;
+  const int r = (int)(((uint32_t)s - (uint32_t)b * (uint32_t)heads_k) & (kNumSections - 1));
   *r_out = r;
   return r < heads_k ? (heads_k - 1 - r) / kNumSections + 1 : 0;
 }
@@ -620,7 +627,7 @@ __device__ inline void row_queue_counts(const PlanGeo& g, int b, int hm, int cos
       v[s] = group * kv_heads_in_section(b, g.heads_k, s, &r);
     }
   } else {
-    const int sec = (int)(((int64_t)b * g.heads_k + hm / group) % kNumSections);
+    const int sec = section_of(b, g.heads_k, hm / group);
 #pragma unroll
     for (int s = 0; s < kNumSections; ++s) v[s] = s == sec ? 1 : 0;
   }
@@ -653,40 +660,40 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
   __shared__ int s_carry;
   __shared__ int s_cu[1025];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_up = g.mask_heads * g.upper_rows;
+
+  // LDS carve, sized for the upper bound of rows so the row data can be
+  // fetched in the same round trip as the header:
+  // [count matrix][p_off n_up+1][f_off n_up+1][first n_up][order n_up][bases]
+  int32_t* cnt = cnt_in_lds ? dyn : w.chunk_cnt;
+  int* lds_rows = dyn + (cnt_in_lds ? (int64_t)(g.nk_max + 1) * w.nchunks : 0);
+  const int32_t* P = w.p_off_tmp;
+  const int32_t* F = w.f_off_tmp;
+  const int32_t* FT = w.first_tile;   // indexed hm * upper_rows + row
+  int32_t* order = w.order;
+  if (rows_in_lds) {
+    int* lp = lds_rows;
+    int* lf = lp + n_up + 1;
+    int* lt = lf + n_up + 1;
+    order = lt + n_up;
+    for (int i = tid; i <= n_up; i += 1024) {
+      lp[i] = w.p_off_tmp[i];
+      lf[i] = w.f_off_tmp[i];
+      if (i < n_up) lt[i] = w.first_tile[i];
+    }
+    P = lp;
+    F = lf;
+    FT = lt;
+  }
   if (d.header[7] != 0) return;  // the build failed: no plan is made
   const int rows_total = d.header[0];
   const int n = g.mask_heads * rows_total;
   const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
   const int nc = (n + 63) >> 6;
   const int64_t cnt_len = (int64_t)(g.nk_max + 1) * nc;
-
-  // LDS carve: [count matrix][p_off n+1][f_off n+1][first n][order n]
-  int32_t* cnt = cnt_in_lds ? dyn : w.chunk_cnt;
-  int* lds_rows = dyn + (cnt_in_lds ? (int64_t)(g.nk_max + 1) * w.nchunks : 0);
-  const int32_t* P = w.p_off_tmp;
-  const int32_t* F = w.f_off_tmp;
-  int32_t* FT = nullptr;
-  int32_t* order = w.order;
-  if (rows_in_lds) {
-    int* lp = lds_rows;
-    int* lf = lp + n + 1;
-    FT = lf + n + 1;
-    order = FT + n;
-    for (int i = tid; i <= n; i += 1024) {
-      lp[i] = w.p_off_tmp[i];
-      lf[i] = w.f_off_tmp[i];
-      if (i < n) {
-        const int hm = i / rows_total;
-        FT[i] = w.first_tile[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
-      }
-    }
-    P = lp;
-    F = lf;
-  }
   auto first_of = [&](int i) -> int {
-    if (FT) return FT[i];
     const int hm = i / rows_total;
-    return w.first_tile[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
+    return FT[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
   };
   auto cost_of = [&](int i) -> int { return (P[i + 1] - P[i]) + (F[i + 1] - F[i]); };
 
@@ -750,10 +757,12 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
       if ((eq & below) == 0) cnt[(int64_t)key * nc + c] = __popcll(eq);
     }
   }
+  if (wv < nc) {   // wavefronts that classified rows
 #pragma unroll
-  for (int s = 0; s < kNumQueues; ++s) {
-    const int t = wave_sum(tot[s]);
-    if (lane == 0 && t) atomicAdd(&s_tot[s], t);
+    for (int s = 0; s < kNumQueues; ++s) {
+      const int t = wave_sum(tot[s]);
+      if (lane == 0 && t) atomicAdd(&s_tot[s], t);
+    }
   }
   __syncthreads();
   block_exclusive_scan_inplace(cnt, cnt_len, s_wave, &s_carry);
@@ -778,7 +787,7 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
   __syncthreads();
 
   // 2. in-section position of each row's first task, over the sorted rows
-  int32_t* rbase = rows_in_lds == 2 ? order + n : w.row_base;
+  int32_t* rbase = rows_in_lds == 2 ? order + n_up : w.row_base;
   for (int base = 0; base < n; base += 1024) {
     const int pos = base + tid;
     int v[kNumQueues];
@@ -838,7 +847,7 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
       rank = g.mask_heads == 1 ? h : 0;
     } else {
       const int hk = h / group;
-      s = (int)(((int64_t)sg.b * g.heads_k + hk) % kNumSections);
+      s = section_of(sg.b, g.heads_k, hk);
       if (g.mask_heads == 1) {
         int r;
         kv_heads_in_section(sg.b, g.heads_k, s, &r);
@@ -877,6 +886,44 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
   const int item = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = g.mask_heads * rows_total;
+  const bool has_row = item < n;
+  // This row's loads are issued first; the metadata copy below runs while
+  // they are in flight.
+  const int hm = has_row ? item / rows_total : 0;
+  const int row = has_row ? item - hm * rows_total : 0;
+  const int64_t src = (int64_t)hm * g.upper_rows + row;
+  int p_begin = 0, f_begin = 0, np = 0;
+  RowGeo rg = {};
+  bool valid = false;
+  const bool is_row = tid < g.tile_q;
+  const int rho = tid;
+  const int32_t* col = mf;
+  if (has_row) {
+    p_begin = w.p_off_tmp[item];
+    f_begin = w.f_off_tmp[item];
+    np = w.p_off_tmp[item + 1] - p_begin;
+    rg = row_geometry(g, st, row);
+    valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
+    col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off + (int64_t)rg.i * g.tile_q +
+          (valid ? rho : 0);
+    if (stage_ep == 2) {
+      // straight into LDS: lane l of wavefront v loads row 64v + l of every
+      // endpoint column (rows past q_len load values nobody reads)
+      const int wv = tid >> 6, ln = tid & 63;
+      if (64 * wv < g.tile_q) {
+        const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(mf + (int64_t)hm * g.nfunc * g.total_q), (short)0,
+            (int)((int64_t)g.nfunc * g.total_q * 4), 0x00020000);
+        const uint32_t base = (uint32_t)(rg.q_off + rg.i * g.tile_q + 64 * wv + ln) * 4u;
+        for (int f = 0; f < g.nfunc; ++f)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rm, (__attribute__((address_space(3))) void*)&ep[f * g.tile_q + 64 * wv], 4,
+              (int)(base + (uint32_t)f * (uint32_t)g.total_q * 4u), 0, 0, 0);
+      }
+    } else if (stage_ep && valid) {
+      for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
+    }
+  }
   // Plan metadata staged in the workspace (header, geometry, schedule and
   // launch records), copied into the plan block a slice per workgroup.
   {
@@ -893,14 +940,7 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
     d.p_off[n] = w.p_off_tmp[n];
     d.f_off[n] = w.f_off_tmp[n];
   }
-  if (item >= n) return;
-  const int hm = item / rows_total;
-  const int row = item - hm * rows_total;
-  const int64_t src = (int64_t)hm * g.upper_rows + row;
-  const int p_begin = w.p_off_tmp[item];
-  const int f_begin = w.f_off_tmp[item];
-  const int np = w.p_off_tmp[item + 1] - p_begin;
-  const RowGeo rg = row_geometry(g, st, row);
+  if (!has_row) return;
   if (tid == 0) {
     d.p_off[item] = p_begin;
     d.f_off[item] = f_begin;
@@ -927,34 +967,37 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
     }
   }
   if (np == 0) return;  // uniform; no payload
-  const int rho = tid;
-  const bool is_row = rho < g.tile_q;
-  const bool valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
-  const int32_t* col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off +
-                       (int64_t)rg.i * g.tile_q + (valid ? rho : 0);
-  if (stage_ep && valid)
-    for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
-  __syncthreads();  // the partial tile list is complete
+  __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads into LDS have landed
+  __syncthreads();  // the partial tile list and the staged endpoints are complete
   auto E = [&](int f) -> int {
     return stage_ep ? ep[f * g.tile_q + rho] : col[(int64_t)f * g.total_q];
   };
+  // Word of columns [c, c + 32): the parity of endpoints <= c, then a flip at
+  // each endpoint inside the word.
   int ptr = 0;
+  auto word_at = [&](int c) -> uint32_t {
+    if (!valid) return 0u;
+    while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
+    uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
+    for (int f = ptr; f < g.nfunc; ++f) {
+      const int e = E(f);
+      if (e >= c + 32) break;
+      word ^= 0xFFFFFFFFu << (e - c);
+    }
+    return word;
+  };
   for (int k = 0; k < np; ++k) {
     const int c0 = tiles[k] * g.tile_k;
     uint32_t* dst = d.p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
-    for (int x = 0; x < g.words_tile; ++x) {
-      uint32_t word = 0u;
-      if (valid) {
-        const int c = c0 + 32 * x;
-        while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
-        word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
-        for (int f = ptr; f < g.nfunc; ++f) {
-          const int e = E(f);
-          if (e >= c + 32) break;
-          word ^= 0xFFFFFFFFu << (e - c);
-        }
+    if (g.words_tile == 2) {
+      const uint32_t w0 = word_at(c0);
+      const uint32_t w1 = word_at(c0 + 32);
+      if (is_row) *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else {
+      for (int x = 0; x < g.words_tile; ++x) {
+        const uint32_t wd = word_at(c0 + 32 * x);
+        if (is_row) dst[x] = wd;
       }
-      if (is_row) dst[x] = word;
     }
   }
 }
@@ -1023,7 +1066,11 @@ hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, c
   mc.total = run;
   const int threads = g.tile_q < 64 ? 64 : g.tile_q;
   const size_t ep_bytes = (size_t)g.nfunc * g.tile_q * 4;
-  const int stage = ep_bytes <= 32 * 1024 ? 1 : 0;
+  // 0: endpoints read from HBM as needed; 1: staged in LDS through registers;
+  // 2: staged with loads straight into LDS (whole wavefronts of rows, and a
+  // mask head's endpoints addressable with 32-bit offsets)
+  int stage = ep_bytes <= 32 * 1024 ? 1 : 0;
+  if (stage && g.tile_q >= 64 && (int64_t)g.nfunc * g.total_q * 4 < ((int64_t)1 << 31)) stage = 2;
   const size_t lds = (size_t)g.nk_max * 4 + (stage ? ep_bytes : 0);
   hipLaunchKernelGGL(plan_materialize_kernel, dim3((unsigned)(items > 0 ? items : 1)),
                      dim3(threads), lds, s, g, mask_func, st, d, w, rows_total, stage, mc);

@@ -3,14 +3,18 @@
 // mask_plan_build follows the stage order of "Flex Attention Mask Plan
 // Design" §4: host structural validation and consumer resolution (§4.1) with
 // no elementwise work on the host; on the GPU the Varlen geometry, the Q2K
-// classification, and one kernel for the count scan, the header and the
-// forward schedule (§4.5, §4.8); one 8-value header read-back (through
-// host-mapped memory, no copy command) that both sizes the exact allocation
-// and reports device-side validation errors; then materialisation (§4.6).
+// classification whose last workgroup computes the offsets and publishes the
+// 8-value header (§4.3, §4.5), and the forward schedule (§4.8); one header
+// read-back (host-mapped memory, no copy command, no stream wait) that both
+// sizes the exact allocation and reports device-side validation errors; then
+// materialisation (§4.6), which also moves the staged plan metadata into the
+// plan's block.
 //
-// Device memory comes from a per-device stream-ordered pool owned by the
-// library (allocation and release are enqueued on the caller's stream), so a
-// build costs no device-wide synchronisation.
+// Memory: the build workspace is a per-(host thread, device) arena reused by
+// every build; each plan owns one exactly sized block carved from device
+// chunks the library keeps, released in its build stream's order.  A build
+// therefore makes no device allocation in the steady state and no
+// device-wide synchronisation.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -19,7 +23,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
+#include <vector>
 #include <new>
 #include <string>
 
@@ -39,6 +45,8 @@ struct mpb_plan {
   int64_t header[8];
   void* block;             // every device array of the plan, one allocation
   size_t bytes;
+  int blk_chunk;           // where the block sits in the device's plan heap
+  size_t blk_off;
   hipStream_t stream;
 };
 
@@ -61,31 +69,119 @@ mpb_status ok() {
   return MPB_OK;
 }
 
-// ---- per-device stream-ordered memory pool
+// ---- per-device plan memory
+//
+// Plan blocks are carved from device chunks the library keeps (never
+// returned while the process runs), best fit with coalescing, so a build
+// pays no allocator call on the device.  A destroyed plan's block is reused
+// only after an event recorded on its build stream has completed, which
+// gives the same ordering as a stream-ordered free on that stream.
 
-std::mutex g_pool_mu;
-hipMemPool_t g_pools[64];
+struct PlanHeap {
+  struct Chunk { char* base; size_t size; };
+  struct Pending { int chunk; size_t off, size; hipEvent_t ev; };
+  std::mutex mu;
+  std::vector<Chunk> chunks;
+  std::map<std::pair<int, size_t>, size_t> free_at;    // (chunk, offset) -> size
+  std::multimap<size_t, std::pair<int, size_t>> by_size; // size -> (chunk, offset)
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> idle_events;
 
-hipError_t device_pool(int dev, hipMemPool_t* out) {
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lk(g_pool_mu);
-  if (!g_pools[dev]) {
-    hipMemPoolProps props;
-    std::memset(&props, 0, sizeof(props));
-    props.allocType = hipMemAllocationTypePinned;
-    props.handleTypes = hipMemHandleTypeNone;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = dev;
-    hipMemPool_t pool = nullptr;
-    hipError_t e = hipMemPoolCreate(&pool, &props);
-    if (e != hipSuccess) return e;
-    uint64_t keep = ~0ull;  // keep freed blocks cached for the next build
-    e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-    if (e != hipSuccess) return e;
-    g_pools[dev] = pool;
+  void insert_free(int c, size_t off, size_t size) {
+    // coalesce with the neighbours in the same chunk
+    auto next = free_at.lower_bound({c, off});
+    if (next != free_at.end() && next->first.first == c && next->first.second == off + size) {
+      size += next->second;
+      erase_by_size(c, next->first.second, next->second);
+      next = free_at.erase(next);
+    }
+    if (next != free_at.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first.first == c && prev->first.second + prev->second == off) {
+        off = prev->first.second;
+        size += prev->second;
+        erase_by_size(c, prev->first.second, prev->second);
+        free_at.erase(prev);
+      }
+    }
+    free_at[{c, off}] = size;
+    by_size.insert({size, {c, off}});
   }
-  *out = g_pools[dev];
-  return hipSuccess;
+  void erase_by_size(int c, size_t off, size_t size) {
+    auto range = by_size.equal_range(size);
+    for (auto it = range.first; it != range.second; ++it)
+      if (it->second.first == c && it->second.second == off) {
+        by_size.erase(it);
+        return;
+      }
+  }
+  void reap() {
+    size_t k = 0;
+    for (size_t i = 0; i < pending.size(); ++i) {
+      Pending& q = pending[i];
+      if (hipEventQuery(q.ev) == hipSuccess) {
+        insert_free(q.chunk, q.off, q.size);
+        idle_events.push_back(q.ev);
+      } else {
+        pending[k++] = q;
+      }
+    }
+    pending.resize(k);
+  }
+  hipError_t alloc(size_t bytes, void** out, int* chunk_out, size_t* off_out) {
+    std::lock_guard<std::mutex> lk(mu);
+    bytes = (bytes + 255) & ~(size_t)255;
+    if (!pending.empty()) reap();
+    auto it = by_size.lower_bound(bytes);
+    if (it == by_size.end()) {
+      const size_t want = std::max(bytes, (size_t)64 << 20);
+      void* p = nullptr;
+      hipError_t e = hipMalloc(&p, want);
+      if (e != hipSuccess) return e;
+      chunks.push_back({(char*)p, want});
+      insert_free((int)chunks.size() - 1, 0, want);
+      it = by_size.lower_bound(bytes);
+    }
+    const int c = it->second.first;
+    const size_t off = it->second.second, size = it->first;
+    by_size.erase(it);
+    free_at.erase({c, off});
+    if (size > bytes) insert_free(c, off + bytes, size - bytes);
+    *out = chunks[c].base + off;
+    *chunk_out = c;
+    *off_out = off;
+    return hipSuccess;
+  }
+  // Returns the block once everything enqueued on `stream` so far is done.
+  hipError_t release(int c, size_t off, size_t bytes, hipStream_t stream) {
+    std::lock_guard<std::mutex> lk(mu);
+    bytes = (bytes + 255) & ~(size_t)255;
+    hipEvent_t ev = nullptr;
+    if (!idle_events.empty()) {
+      ev = idle_events.back();
+      idle_events.pop_back();
+    } else {
+      hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e = hipEventRecord(ev, stream);
+    if (e != hipSuccess) {
+      idle_events.push_back(ev);
+      return e;
+    }
+    pending.push_back({c, off, bytes, ev});
+    return hipSuccess;
+  }
+};
+
+std::mutex g_heap_mu;
+PlanHeap* g_heaps[64];
+
+PlanHeap* plan_heap(int dev) {
+  if (dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(g_heap_mu);
+  if (!g_heaps[dev]) g_heaps[dev] = new (std::nothrow) PlanHeap;
+  return g_heaps[dev];
 }
 
 // ---- per-thread host-mapped header slot and arrival counters
@@ -349,8 +445,8 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return device_status(e, "hipGetDevice");
-  hipMemPool_t pool;
-  if ((e = device_pool(dev, &pool)) != hipSuccess) return device_status(e, "memory pool");
+  PlanHeap* heap = plan_heap(dev);
+  if (!heap) return fail(MPB_ERR_OUT_OF_MEMORY, "plan heap");
   ThreadSlot* slot = nullptr;
   if ((e = thread_slot(dev, &slot)) != hipSuccess) return device_status(e, "host slot");
 
@@ -463,7 +559,9 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   const size_t e_f_idx = ce.take<int32_t>(fnnz);
   const size_t e_masks = ce.take<uint32_t>(pnnz * tq * (tk / 32));
   void* block = nullptr;
-  if ((e = hipMallocFromPoolAsync(&block, ce.off, pool, s)) != hipSuccess)
+  int blk_chunk = 0;
+  size_t blk_off = 0;
+  if ((e = heap->alloc(ce.off, &block, &blk_chunk, &blk_off)) != hipSuccess)
     return device_status(e, "plan allocation");
   PlanDev d;
   d.header = at<int32_t>(block, e_header);
@@ -481,13 +579,13 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   d.p_masks = at<uint32_t>(block, e_masks);
   if ((e = launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s)) !=
       hipSuccess) {
-    hipFreeAsync(block, s);
+    heap->release(blk_chunk, blk_off, ce.off, s);
     return device_status(e, "materialize launch");
   }
 
   mpb_plan* plan = new (std::nothrow) mpb_plan;
   if (!plan) {
-    hipFreeAsync(block, s);
+    heap->release(blk_chunk, blk_off, ce.off, s);
     return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
   }
   plan->device = dev;
@@ -502,6 +600,8 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
   plan->block = block;
   plan->bytes = ce.off;
+  plan->blk_chunk = blk_chunk;
+  plan->blk_off = blk_off;
   plan->stream = s;
   *out = plan;
   return ok();
@@ -512,7 +612,8 @@ mpb_status mask_plan_destroy(mpb_plan* plan) {
   int cur = 0;
   hipGetDevice(&cur);
   if (cur != plan->device) hipSetDevice(plan->device);
-  hipFreeAsync(plan->block, plan->stream);
+  if (PlanHeap* heap = plan_heap(plan->device))
+    heap->release(plan->blk_chunk, plan->blk_off, plan->bytes, plan->stream);
   if (cur != plan->device) hipSetDevice(cur);
   delete plan;
   return ok();
