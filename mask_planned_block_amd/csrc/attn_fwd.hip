@@ -85,65 +85,51 @@ struct Bf16Ops {
   using T = __bf16;
   static constexpr int D = D_, NW = NW_, TKV = TKV_, QB = QB_;
   static constexpr int NT = NW * 64, TQ = 32 * QB * NW, NKB = TKV / 32;
-  static constexpr int WPE = QB == 1 ? 2 : 1;   // wavefronts per SIMD
+  static constexpr int WPE = QB == 1 ? (TKV == 32 ? 3 : 2) : 1;   // wavefronts per SIMD
   static constexpr int ESZ = 2;
   static constexpr int CH = D / 8;              // 16-byte chunks per K row
   static constexpr int RPI = 1024 / (D * 2);    // K rows per wavefront load instruction
   static constexpr int KI = TKV / RPI / NW;     // K load instructions per wavefront per tile
-  static constexpr int VP = TKV + 8;  // V^T row pitch (elements)
-  static constexpr int VCH = (TKV / 2) * (D / 8) / NT;  // V row-pair chunks per thread
   static_assert(KI * RPI * NW == TKV, "K tile must split evenly over wavefronts");
-  static_assert(VCH * NT * 16 == TKV * D, "V tile must split evenly over threads");
-  static_assert(D % 32 == 0 && TKV % 32 == 0 && CH <= 16, "tile shape");
+  static_assert(D % 32 == 0 && TKV % 32 == 0 && CH <= 16 && CH >= 8, "tile shape");
 
   struct Smem {
     __bf16 k[2][TKV * D];
-    __bf16 vt[2][D * VP];
+    __bf16 v[2][TKV * D];
   };
   struct QFrag { bf16x8 q[QB][D / 16]; };
-  struct Stage { u32x4 v0[VCH]; u32x4 v1[VCH]; };
+  struct Stage {};
   typedef bf16x8 PBlock[NKB][2];
   struct PFrag { PBlock p[QB]; };
 
+  // Swizzles of the 16-byte chunk positions inside a row: K is read as MFMA
+  // operands by 32 lanes holding 32 consecutive rows (chunk c of row r at
+  // c ^ (r % CH)); V by transposing reads whose 16-lane groups hold 4
+  // consecutive rows and 2 neighbouring chunks (chunk c of row r at
+  // c ^ 2 (r % 4)).  Either way the lanes serviced together hit distinct banks.
+  static __device__ constexpr int kswz(int r) { return r % CH; }
+  static __device__ constexpr int vswz(int r) { return 2 * (r % 4); }
+
   // tile_off = byte offset of the tile's first row; rs = bytes per token row.
-  // K lands in sm.k[stage] when the issuing wavefront's loads complete.
-  static __device__ inline void load(Stage& st, Smem& sm, int stage, rsrc_t rk, rsrc_t rv,
+  // K and V land in sm.k[stage] / sm.v[stage] when the issuing wavefront's
+  // loads complete.
+  static __device__ inline void load(Stage&, Smem& sm, int stage, rsrc_t rk, rsrc_t rv,
                                      uint32_t tile_off, uint32_t rs, int tid) {
     const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
     for (int c = 0; c < KI; ++c) {
       const int r0 = (c * NW + wave) * RPI;
       const int r = r0 + lane / CH;
-      const int lc = (lane % CH) ^ (r % CH);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rk, (__attribute__((address_space(3))) void*)&sm.k[stage][r0 * D], 16,
-          (int)(tile_off + r * rs + lc * 16), 0, 0, 0);
-    }
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * NT;
-      const int pr = idx % (TKV / 2), c8 = idx / (TKV / 2);
-      const uint32_t off = tile_off + (2 * pr) * rs + c8 * 16;
-      st.v0[c] = bload16(rv, off);
-      st.v1[c] = bload16(rv, off + rs);
+          (int)(tile_off + r * rs + ((lane % CH) ^ kswz(r)) * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)&sm.v[stage][r0 * D], 16,
+          (int)(tile_off + r * rs + ((lane % CH) ^ vswz(r)) * 16), 0, 0, 0);
     }
   }
 
-  static __device__ inline void store(const Stage& st, Smem& sm, int stage, int tid) {
-#pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = tid + c * NT;
-      const int pr = idx % (TKV / 2), c8 = idx / (TKV / 2);
-      const int pos = vt_pos(2 * pr);  // rows 2pr, 2pr+1 stay adjacent
-      __bf16* dst = &sm.vt[stage][(c8 * 8) * VP + pos];
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a = st.v0[c][w], b = st.v1[c][w];
-        *(uint32_t*)(dst + (2 * w) * VP) = __builtin_amdgcn_perm(b, a, 0x05040100u);
-        *(uint32_t*)(dst + (2 * w + 1) * VP) = __builtin_amdgcn_perm(b, a, 0x07060302u);
-      }
-    }
-  }
+  static __device__ inline void store(const Stage&, Smem&, int, int) {}
 
   static __device__ inline void load_q(QFrag& qf, rsrc_t rq, const uint32_t (&row_off)[QB],
                                        int b2) {
@@ -160,7 +146,7 @@ struct Bf16Ops {
                                    int stage, int lane) {
     // row kk*32 + lane%32, logical chunk 2s + lane/32, at chunk (2s) ^ x
     const __bf16* kb = &sm.k[stage][(lane & 31) * D];
-    const int x = (lane >> 5) ^ (lane & (CH - 1));
+    const int x = (lane >> 5) ^ kswz(lane & 31);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -213,14 +199,36 @@ struct Bf16Ops {
     return s;
   }
 
-  // V^T fragments in the order (db, kk, m), each read one step ahead.
+  // O^T += V^T P^T.  The V^T operand of MFMA (db, kk, m) is read from the
+  // row-major V tile with two ds_read_b64_tr_b16: in each 16-lane group, lane
+  // i receives element i % 4 of the rows addressed by lanes i/4 + 4j
+  // (j = 0..3).  Lane r of the group addresses row kb + 4 kg + r/4 at
+  // columns 32 db + 16 ((lane/16) % 2) + 4 (r % 4), so lane L receives
+  // V[kb + 4 kg + j][32 db + L % 32] for j = 0..3: the 4 K slots of one
+  // MFMA operand half, in the K order of the P registers (kb = 32 kk +
+  // 16 m, then + 8 for slots 4..7).  Reads run one MFMA ahead.
   static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const Smem& sm,
                                    int stage, int lane) {
-    const __bf16* vb = &sm.vt[stage][(lane & 31) * VP + 8 * (lane >> 5)];
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int r = lane & 15, g2 = (lane >> 4) & 1, kg = lane >> 5;
+    const int krow = 4 * kg + (r >> 2);            // lane part of the row
+    const __bf16* vb = &sm.v[stage][krow * D];
+    int coff[D / 32];                              // lane part of the column, per db
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int dcol = 32 * db + 16 * g2 + 4 * (r & 3);
+      coff[db] = (((dcol >> 3) ^ vswz(krow)) << 3) + (dcol & 7);
+    }
     constexpr int NS = (D / 32) * NKB * 2;
     auto frag = [&](int i) {
       const int db = i / (NKB * 2), kk = (i / 2) % NKB, m = i % 2;
-      return *(const bf16x8*)(vb + db * 32 * VP + kk * 32 + 16 * m);
+      const __bf16* p0 = vb + (32 * kk + 16 * m) * D + coff[db];
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)p0);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16*)(p0 + 8 * D));
+      const v4i16 both[2] = {lo, hi};
+      return __builtin_bit_cast(bf16x8, both);
     };
     bf16x8 a[2];
     a[0] = frag(0);
