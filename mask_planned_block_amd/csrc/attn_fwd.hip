@@ -17,21 +17,23 @@
 //    column (q = lane%32) and 16 K rows {8a + 4*(lane/32) + c}.  So the
 //    softmax row max/sum is 16 in-lane values plus one exchange with lane^32,
 //    the packed predicate of a 32-column block is one dword per lane, and P
-//    feeds the P.V MFMA straight from registers: O^T = V^T P^T, where the V
-//    operand is read from an LDS copy of V stored transposed with its K order
-//    permuted (bits 2 and 3 swapped) so each lane reads 8 contiguous values.
+//    feeds the P.V MFMA straight from registers: O^T = V^T P^T, where the
+//    V^T operand is read from the row-major V tile with ds_read_b64_tr_b16.
 //  * Q, K, V and O are addressed through buffer resources bounded by the
 //    task's sample: loads past k_len/q_len return zero and stores past q_len
 //    are dropped by the hardware range check, so the tail protection of the
 //    plan design (§4.3, §4.8) costs no branch; offsets are 32-bit.
-//  * K and V^T tiles are staged in LDS (double buffered, padded rows) from
-//    coalesced 16-byte HBM loads issued one tile ahead.
+//  * bf16 K and V tiles go straight from HBM into LDS (16-byte buffer loads
+//    with the LDS flag, swizzled rows), double buffered in separate LDS
+//    arrays and fetched one tile ahead; fp32 tiles pass through registers.
 //  * Online softmax in base 2 with lazy rescaling: the running max used for
 //    the exponent only moves when a row's max grows by more than 2^8, and the
 //    O rescale is skipped by the whole wavefront when no lane moved.
 //    Statistics in fp32, P rounded to bf16 for the second MFMA.
 //  * fp32 inputs use v_mfma_f32_32x32x2_f32 with the same accumulator layout
 //    and keep P in fp32.
+#include <type_traits>
+
 #include "mpb_internal.h"
 #include "../../include/mpb.h"
 
@@ -65,8 +67,6 @@ __device__ inline u32x4 bload16(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
-// Position of K index k inside a permuted V^T row: bits 2 and 3 swapped.
-__device__ constexpr int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // ----------------------------------------------------------------- bf16 tiles
 
@@ -93,10 +93,8 @@ struct Bf16Ops {
   static_assert(KI * RPI * NW == TKV, "K tile must split evenly over wavefronts");
   static_assert(D % 32 == 0 && TKV % 32 == 0 && CH <= 16 && CH >= 8, "tile shape");
 
-  struct Smem {
-    __bf16 k[2][TKV * D];
-    __bf16 v[2][TKV * D];
-  };
+  static constexpr int KELEMS = TKV * D, VELEMS = TKV * D;   // LDS elements per stage
+  static constexpr bool kDirectLds = true;   // tiles land in LDS without registers
   struct QFrag { bf16x8 q[QB][D / 16]; };
   struct Stage {};
   typedef bf16x8 PBlock[NKB][2];
@@ -111,9 +109,9 @@ struct Bf16Ops {
   static __device__ constexpr int vswz(int r) { return 2 * (r % 4); }
 
   // tile_off = byte offset of the tile's first row; rs = bytes per token row.
-  // K and V land in sm.k[stage] / sm.v[stage] when the issuing wavefront's
-  // loads complete.
-  static __device__ inline void load(Stage&, Smem& sm, int stage, rsrc_t rk, rsrc_t rv,
+  // K and V land in kdst / vdst (one stage's LDS buffers) when the issuing
+  // wavefront's loads complete.
+  static __device__ inline void load(Stage&, T* kdst, T* vdst, rsrc_t rk, rsrc_t rv,
                                      uint32_t tile_off, uint32_t rs, int tid) {
     const int wave = tid >> 6, lane = tid & 63;
 #pragma unroll
@@ -121,15 +119,15 @@ struct Bf16Ops {
       const int r0 = (c * NW + wave) * RPI;
       const int r = r0 + lane / CH;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (__attribute__((address_space(3))) void*)&sm.k[stage][r0 * D], 16,
+          rk, (__attribute__((address_space(3))) void*)&kdst[r0 * D], 16,
           (int)(tile_off + r * rs + ((lane % CH) ^ kswz(r)) * 16), 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (__attribute__((address_space(3))) void*)&sm.v[stage][r0 * D], 16,
+          rv, (__attribute__((address_space(3))) void*)&vdst[r0 * D], 16,
           (int)(tile_off + r * rs + ((lane % CH) ^ vswz(r)) * 16), 0, 0, 0);
     }
   }
 
-  static __device__ inline void store(const Stage&, Smem&, int, int) {}
+  static __device__ inline void store(const Stage&, T*, T*, int) {}
 
   static __device__ inline void load_q(QFrag& qf, rsrc_t rq, const uint32_t (&row_off)[QB],
                                        int b2) {
@@ -142,10 +140,10 @@ struct Bf16Ops {
   }
 
   // K fragments are read from LDS one k-step ahead of the MFMAs using them.
-  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const Smem& sm,
-                                   int stage, int lane) {
+  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const T* kst,
+                                   int lane) {
     // row kk*32 + lane%32, logical chunk 2s + lane/32, at chunk (2s) ^ x
-    const __bf16* kb = &sm.k[stage][(lane & 31) * D];
+    const __bf16* kb = &kst[(lane & 31) * D];
     const int x = (lane >> 5) ^ kswz(lane & 31);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -207,12 +205,12 @@ struct Bf16Ops {
   // V[kb + 4 kg + j][32 db + L % 32] for j = 0..3: the 4 K slots of one
   // MFMA operand half, in the K order of the P registers (kb = 32 kk +
   // 16 m, then + 8 for slots 4..7).  Reads run one MFMA ahead.
-  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const Smem& sm,
-                                   int stage, int lane) {
+  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const T* vst,
+                                   int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int r = lane & 15, g2 = (lane >> 4) & 1, kg = lane >> 5;
     const int krow = 4 * kg + (r >> 2);            // lane part of the row
-    const __bf16* vb = &sm.v[stage][krow * D];
+    const __bf16* vb = &vst[krow * D];
     int coff[D / 32];                              // lane part of the column, per db
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
@@ -274,16 +272,14 @@ struct F32Ops {
   static constexpr int KCH = TKV * D / 4 / NT;
   static_assert(KCH * NT * 4 == TKV * D, "tile must split evenly over threads");
 
-  struct Smem {
-    float k[2][TKV * KP];
-    float v[2][TKV * VP];
-  };
+  static constexpr int KELEMS = TKV * KP, VELEMS = TKV * VP;   // LDS elements per stage
+  static constexpr bool kDirectLds = false;  // tiles pass through registers
   struct QFrag { float q[QB][D / 2]; };
   struct Stage { u32x4 k[KCH]; u32x4 v[KCH]; };
   typedef f32x16 PBlock[NKB];
   struct PFrag { PBlock p[QB]; };
 
-  static __device__ inline void load(Stage& st, Smem&, int, rsrc_t rk, rsrc_t rv,
+  static __device__ inline void load(Stage& st, T*, T*, rsrc_t rk, rsrc_t rv,
                                      uint32_t tile_off, uint32_t rs, int tid) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
@@ -294,13 +290,13 @@ struct F32Ops {
     }
   }
 
-  static __device__ inline void store(const Stage& st, Smem& sm, int stage, int tid) {
+  static __device__ inline void store(const Stage& st, T* kdst, T* vdst, int tid) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
       const int r = idx / (D / 4), c4 = idx % (D / 4);
-      *(u32x4*)&sm.k[stage][r * KP + c4 * 4] = st.k[c];
-      *(u32x4*)&sm.v[stage][r * VP + c4 * 4] = st.v[c];
+      *(u32x4*)&kdst[r * KP + c4 * 4] = st.k[c];
+      *(u32x4*)&vdst[r * VP + c4 * 4] = st.v[c];
     }
   }
 
@@ -315,9 +311,9 @@ struct F32Ops {
     }
   }
 
-  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const Smem& sm,
-                                   int stage, int lane) {
-    const float* kb = &sm.k[stage][(lane & 31) * KP + (lane >> 5) * (D / 2)];
+  static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const T* kst,
+                                   int lane) {
+    const float* kb = &kst[(lane & 31) * KP + (lane >> 5) * (D / 2)];
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) acc[0][kk] = f32x16{};
 #pragma unroll
@@ -347,8 +343,8 @@ struct F32Ops {
     return s;
   }
 
-  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const Smem& sm,
-                                   int stage, int lane) {
+  static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const T* vst,
+                                   int lane) {
     const int b2 = lane >> 5;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -357,7 +353,7 @@ struct F32Ops {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int k = kk * 32 + 8 * (v / 4) + 4 * b2 + (v % 4);
-          const float a = sm.v[stage][k * VP + db * 32 + (lane & 31)];
+          const float a = vst[k * VP + db * 32 + (lane & 31)];
           o[0][db] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, pf.p[0][kk][v], o[0][db], 0, 0, 0);
         }
   }
@@ -427,7 +423,7 @@ struct RowState {
 // predicate, online max with lazy rescale of the block's O, exponentials,
 // P in the MFMA operand type and the row sum.
 template <class Ops, int MOD, bool MASKED>
-__device__ inline void softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
+__device__ __attribute__((always_inline)) inline void softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
                                      const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
                                      f32x16 (&o)[Ops::D / 32], RowState& rs,
                                      typename Ops::PBlock& pb) {
@@ -487,8 +483,9 @@ __device__ inline void softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB
 // One K tile for the wavefront's QB Q blocks: scores on MFMA, softmax per
 // block, P.V on MFMA.
 template <class Ops, int MOD, bool MASKED>
-__device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
-                                 const typename Ops::Smem& sm, int stage, int lane,
+__device__ __attribute__((always_inline)) inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
+                                 const typename Ops::T* kst, const typename Ops::T* vst,
+                                 int lane,
                                  const uint32_t (&mw)[Ops::QB][Ops::NKB],
                                  const float (&kq0)[Ops::QB], float slope,
                                  f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
@@ -498,14 +495,14 @@ __device__ inline void tile_step(const AttnParams& p, const typename Ops::QFrag&
   // that of the wavefronts sharing a SIMD the one with matrix work issues
   // first and the other fills the VALU meanwhile.
   __builtin_amdgcn_s_setprio(1);
-  Ops::qk(acc, qf, sm, stage, lane);
+  Ops::qk(acc, qf, kst, lane);
   __builtin_amdgcn_s_setprio(0);
   typename Ops::PFrag pf;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
     softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb], pf.p[qb]);
   __builtin_amdgcn_s_setprio(1);
-  Ops::pv(o, pf, sm, stage, lane);
+  Ops::pv(o, pf, vst, lane);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -515,7 +512,31 @@ __global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(Ops::WP
 void attn_fwd_kernel(AttnParams p) {
   constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
   constexpr int QB = Ops::QB;
-  __shared__ typename Ops::Smem sm;
+  using T = typename Ops::T;
+  // One LDS array per stage and operand, each a separate object: the compiler
+  // then knows that the loads landing in the next stage's buffers cannot
+  // alias this stage's operand reads and does not wait for them.
+  __shared__ __attribute__((aligned(16))) T k_s0[Ops::KELEMS];
+  __shared__ __attribute__((aligned(16))) T k_s1[Ops::KELEMS];
+  __shared__ __attribute__((aligned(16))) T v_s0[Ops::VELEMS];
+  __shared__ __attribute__((aligned(16))) T v_s1[Ops::VELEMS];
+  // A stage is an int or, where the loop is unrolled, a compile-time constant.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  auto kbuf = [&](auto st) -> T* {
+    if constexpr (std::is_integral_v<decltype(st)>) return st ? k_s1 : k_s0;
+    else if constexpr (decltype(st)::value == 0) return k_s0;
+    else return k_s1;
+  };
+  auto vbuf = [&](auto st) -> T* {
+    if constexpr (std::is_integral_v<decltype(st)>) return st ? v_s1 : v_s0;
+    else if constexpr (decltype(st)::value == 0) return v_s0;
+    else return v_s1;
+  };
+  auto flip = [](auto st) {
+    if constexpr (std::is_integral_v<decltype(st)>) return st ^ 1;
+    else return std::integral_constant<int, decltype(st)::value ^ 1>{};
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -570,7 +591,7 @@ void attn_fwd_kernel(AttnParams p) {
         const uint32_t* src =
             p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * (QB * wave + qb) + lq) * NKB;
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = src[kk] >> (4 * b2);
+        for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = src[kk];
       } else {
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = 0xFFFFFFFFu;
@@ -585,7 +606,7 @@ void attn_fwd_kernel(AttnParams p) {
   // tile waits on the index load before issuing its prefetch.
   int j_ahead = 0;
   if (ntiles > 0) {
-    Ops::load(st, sm, 0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
+    Ops::load(st, k_s0, v_s0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
     load_masks(0, mw_cur);
     if (ntiles > 1) j_ahead = tile_j(1);
   }
@@ -607,26 +628,31 @@ void attn_fwd_kernel(AttnParams p) {
 
   // Two loops, as in §6.1: the partial list with its predicate, then the full
   // list without one.  The K/V prefetch runs one tile ahead across both, the
-  // tile-index read two tiles ahead.
+  // tile-index read two tiles ahead.  Tile t uses stage t % 2; with tiles
+  // loaded straight into LDS the stage is a compile-time constant in every
+  // step (the loops step two tiles at a time).
   int t = 0;
   int j_pending = 0;   // index of tile t+2, in flight during tile t
-  auto advance = [&](int stage) {
+  auto step = [&](auto masked, auto stage) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const auto next = flip(stage);
     const bool more = t + 1 < ntiles;
     const int j_next = j_ahead;
     if (more) {
-      Ops::load(st, sm, stage ^ 1, rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
+      Ops::load(st, kbuf(next), vbuf(next), rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
       load_masks(t + 1, mw_next);
     }
     if (t + 2 < ntiles) j_pending = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
-    return j_next;
-  };
-  auto retire = [&](int stage, int j_next) {
-    if (t + 1 < ntiles) {
-      Ops::store(st, sm, stage ^ 1, tid);
+    float kq0[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) kq0[qb] = (float)(j_cur * TKV + 4 * b2 - qloc[qb]);
+    tile_step<Ops, MOD, kMasked>(p, qf, kbuf(stage), vbuf(stage), lane, mw_cur, kq0, slope, o, rs);
+    if (more) {
+      Ops::store(st, kbuf(next), vbuf(next), tid);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) mw_cur[qb][kk] = mw_next[qb][kk];
+        for (int kk = 0; kk < NKB; ++kk) mw_cur[qb][kk] = mw_next[qb][kk] >> (4 * b2);
       j_cur = j_next;
     }
     // this wavefront's loads straight into LDS have landed; the barrier
@@ -634,32 +660,34 @@ void attn_fwd_kernel(AttnParams p) {
     __builtin_amdgcn_s_waitcnt(0);
     if (t + 2 < ntiles) j_ahead = __builtin_amdgcn_readfirstlane(j_pending);
     __syncthreads();
+    ++t;
   };
-  auto kq_of = [&](float (&kq0)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) kq0[qb] = (float)(j_cur * TKV + 4 * b2 - qloc[qb]);
+  // tiles [t, t_end) with the predicate or without it
+  auto run = [&](auto masked, int t_end) __attribute__((always_inline)) {
+    if constexpr (Ops::kDirectLds) {
+      if (t < t_end && (t & 1)) step(masked, S1{});
+      while (t + 1 < t_end) {
+        step(masked, S0{});
+        step(masked, S1{});
+      }
+      if (t < t_end) step(masked, S0{});
+    } else {
+      while (t < t_end) step(masked, t & 1);
+    }
   };
   if (ntiles > 0) {
-    Ops::store(st, sm, 0, tid);
+    Ops::store(st, k_s0, v_s0, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const int n_masked = p.force_partial ? ntiles : np;
-    for (; t < n_masked; ++t) {
-      const int stage = t & 1;
-      const int j_next = advance(stage);
-      float kq0[QB];
-      kq_of(kq0);
-      tile_step<Ops, MOD, true>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
-      retire(stage, j_next);
-    }
-    for (; t < ntiles; ++t) {
-      const int stage = t & 1;
-      const int j_next = advance(stage);
-      float kq0[QB];
-      kq_of(kq0);
-      tile_step<Ops, MOD, false>(p, qf, sm, stage, lane, mw_cur, kq0, slope, o, rs);
-      retire(stage, j_next);
-    }
+    // mask words are kept as loaded until their tile starts (a shift right at
+    // the load would make it wait for every load in flight); lanes 32..63 hold
+    // the columns 4 above those of lanes 0..31
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw_cur[qb][kk] >>= 4 * b2;
+    run(std::true_type{}, p.force_partial ? ntiles : np);
+    run(std::false_type{}, ntiles);
   }
 
   // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf.
