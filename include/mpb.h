@@ -124,8 +124,12 @@ typedef struct mpb_score_mod {
  * classification with endpoint validation (§4.3), count scan and header
  * (§4.5), the forward schedule (§4.8), one 8-value header read-back (the
  * call waits on the host until the header has landed in host-mapped memory,
- * not for the stream to drain), exact allocation, and Q2K materialisation of
- * the partial/full CSR and the packed predicates (§4.6, §5).
+ * not for the stream to drain), allocation, and Q2K materialisation of the
+ * partial/full CSR and the packed predicates (§4.6, §5).  Allocation is
+ * exact (sized by the header) unless the plan's block at the upper bound of
+ * every count is at most 32 MiB: then that block is allocated before the
+ * launches, every stage writes the plan in place and the schedule and the
+ * materialisation run in one launch (mask_plan_info reports the bytes held).
  *
  *   mask_func    device int32 [mask_heads][nfunc][total_q]; column t holds the
  *                endpoints F0..F(nfunc-1) of Q token t, sample-local K

@@ -112,6 +112,13 @@ hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, c
                                    const PlanDev& d, const PlanWork& w, int32_t rows_total,
                                    hipStream_t s);
 
+// In-place builds: the schedule and the rows' lists and payload in one launch
+// on the plan block itself (rows_total < 0: read from the device header).
+hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                              const PlanWork& w, int32_t rows_total, hipStream_t s);
+// Whether that launch's LDS fits (count matrix in LDS or not, its chunks).
+bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks);
+
 // ---- attention ----
 enum ModKind : int32_t {
   kModNone = 0,

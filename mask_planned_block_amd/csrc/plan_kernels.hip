@@ -29,6 +29,8 @@
 // an even number of endpoints are <= k (k < F0: none; F0 <= k < F1: one, ...),
 // which is the union [0,F0) U [F1,F2) U ... of §2; columns >= F(nfunc-1)
 // (hence >= k_len) see an odd count and are masked.
+#include <algorithm>
+
 #include "mpb_internal.h"
 #include "../../include/mpb.h"
 
@@ -649,9 +651,10 @@ __device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int*
 
 }  // namespace
 
-__global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev d, PlanWork w,
-                                                             int cnt_in_lds, int rows_in_lds) {
-  extern __shared__ int dyn[];
+// The schedule, run by one workgroup of 1024 threads; `dyn` is its dynamic
+// LDS.
+__device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                      int cnt_in_lds, int rows_in_lds, int* dyn) {
   __shared__ int s_secoff[kNumQueues + 1];
   __shared__ int s_run[kNumQueues];
   __shared__ int s_tot[kNumQueues];
@@ -861,6 +864,12 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
   }
 }
 
+__global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev d, PlanWork w,
+                                                             int cnt_in_lds, int rows_in_lds) {
+  extern __shared__ int dyn[];
+  schedule_block(g, d, w, cnt_in_lds, rows_in_lds, dyn);
+}
+
 // ---------------------------------------------------------------- materialize
 
 // One workgroup per (mask head, Q plan row), one thread per Q row of the
@@ -885,6 +894,12 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
   int* ep = lds + g.nk_max;             // [nfunc][T_Q] endpoints when staged
   const int item = blockIdx.x;
   const int tid = threadIdx.x;
+  if (rows_total < 0) {
+    // launched before the header was read back (Varlen rows counted on the
+    // device): nothing to do for a failed build
+    if (d.header[7] != 0) return;
+    rows_total = d.header[0];
+  }
   const int n = g.mask_heads * rows_total;
   const bool has_row = item < n;
   // This row's loads are issued first; the metadata copy below runs while
@@ -1002,6 +1017,131 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
   }
 }
 
+
+// In-place builds: the schedule (workgroup 0) and every row's lists and
+// payload (the other workgroups, 1024 / SG rows each with SG = max(64, T_Q)
+// threads per row) in one launch -- both follow from the classification and
+// its offsets, neither needs the other.  The per-row work is the one of
+// plan_materialize_kernel; the metadata is already in place.
+__global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
+                                                           const int32_t* __restrict__ mf,
+                                                           PlanDev d, PlanWork w, int rows_total,
+                                                           int stage_ep, int cnt_in_lds,
+                                                           int rows_in_lds) {
+  extern __shared__ int dyn[];
+  if (blockIdx.x == 0) {
+    schedule_block(g, d, w, cnt_in_lds, rows_in_lds, dyn);
+    return;
+  }
+  if (rows_total < 0) {   // Varlen: rows counted on the device; nothing for a failed build
+    if (d.header[7] != 0) return;
+    rows_total = d.header[0];
+  }
+  const int SG = g.tile_q < 64 ? 64 : g.tile_q;
+  const int G = 1024 / SG;
+  const int sub = threadIdx.x / SG;
+  const int tid = threadIdx.x - sub * SG;
+  int* tiles = dyn + sub * (g.nk_max + (stage_ep ? g.nfunc * g.tile_q : 0));
+  int* ep = tiles + g.nk_max;
+  const int item = (blockIdx.x - 1) * G + sub;
+  const int n = g.mask_heads * rows_total;
+  const bool has_row = item < n;
+  const int hm = has_row ? item / rows_total : 0;
+  const int row = has_row ? item - hm * rows_total : 0;
+  const int64_t src = (int64_t)hm * g.upper_rows + row;
+  int p_begin = 0, f_begin = 0, np = 0;
+  RowGeo rg = {};
+  bool valid = false;
+  const bool is_row = tid < g.tile_q;
+  const int rho = tid;
+  const int32_t* col = mf;
+  if (has_row) {
+    p_begin = w.p_off_tmp[item];
+    f_begin = w.f_off_tmp[item];
+    np = w.p_off_tmp[item + 1] - p_begin;
+    rg = row_geometry(g, d, row);
+    valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
+    col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off + (int64_t)rg.i * g.tile_q +
+          (valid ? rho : 0);
+    if (stage_ep == 2) {
+      const int wv = tid >> 6, ln = tid & 63;
+      if (64 * wv < g.tile_q) {
+        const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t*>(mf + (int64_t)hm * g.nfunc * g.total_q), (short)0,
+            (int)((int64_t)g.nfunc * g.total_q * 4), 0x00020000);
+        const uint32_t base = (uint32_t)(rg.q_off + rg.i * g.tile_q + 64 * wv + ln) * 4u;
+        for (int f = 0; f < g.nfunc; ++f)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rm, (__attribute__((address_space(3))) void*)&ep[f * g.tile_q + 64 * wv], 4,
+              (int)(base + (uint32_t)f * (uint32_t)g.total_q * 4u), 0, 0, 0);
+      }
+    } else if (stage_ep && valid) {
+      for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
+    }
+    if (item == 0 && tid == 0) {
+      d.p_off[n] = w.p_off_tmp[n];
+      d.f_off[n] = w.f_off_tmp[n];
+    }
+    if (tid == 0) {
+      d.p_off[item] = p_begin;
+      d.f_off[item] = f_begin;
+    }
+    if (tid < 64) {
+      const int nwords = (rg.nk + 31) >> 5;
+      int pb = 0, fb = f_begin;
+      for (int ww = 0; ww < nwords; ++ww) {
+        const uint32_t vw = w.vis_bits[src * g.words_k + ww];
+        const uint32_t fw = w.full_bits[src * g.words_k + ww];
+        const uint32_t pw = vw & ~fw;
+        if (tid < 32) {
+          const uint32_t bit = 1u << tid;
+          const uint32_t below = bit - 1u;
+          if (pw & bit) {
+            const int k = pb + __popc(pw & below);
+            d.p_idx[p_begin + k] = 32 * ww + tid;
+            tiles[k] = 32 * ww + tid;
+          }
+          if (fw & bit) d.f_idx[fb + __popc(fw & below)] = 32 * ww + tid;
+        }
+        pb += __popc(pw);
+        fb += __popc(fw);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads into LDS have landed
+  __syncthreads();  // every row's partial tile list and staged endpoints are complete
+  if (!has_row || np == 0) return;
+  auto E = [&](int f) -> int {
+    return stage_ep ? ep[f * g.tile_q + rho] : col[(int64_t)f * g.total_q];
+  };
+  int ptr = 0;
+  auto word_at = [&](int c) -> uint32_t {
+    if (!valid) return 0u;
+    while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
+    uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
+    for (int f = ptr; f < g.nfunc; ++f) {
+      const int e = E(f);
+      if (e >= c + 32) break;
+      word ^= 0xFFFFFFFFu << (e - c);
+    }
+    return word;
+  };
+  for (int k = 0; k < np; ++k) {
+    const int c0 = tiles[k] * g.tile_k;
+    uint32_t* dst = d.p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
+    if (g.words_tile == 2) {
+      const uint32_t w0 = word_at(c0);
+      const uint32_t w1 = word_at(c0 + 32);
+      if (is_row) *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else {
+      for (int x = 0; x < g.words_tile; ++x) {
+        const uint32_t wd = word_at(c0 + 32 * x);
+        if (is_row) dst[x] = wd;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline int rows_per_lane(int tile_q) { return tile_q <= 64 ? 1 : tile_q / 64; }
@@ -1044,8 +1184,10 @@ hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWo
 hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, const PlanDev& st,
                                    const PlanDev& d, const PlanWork& w, int32_t rows_total,
                                    hipStream_t s) {
-  const int64_t items = (int64_t)g.mask_heads * rows_total;
-  const int64_t tasks = (int64_t)rows_total * g.heads_q;
+  // rows_total < 0: rows counted on the device, one workgroup per row of the
+  // upper bound; st == d: the metadata is already in place, nothing to copy
+  const int64_t items = (int64_t)g.mask_heads * (rows_total >= 0 ? rows_total : g.upper_rows);
+  const int64_t tasks = (int64_t)(rows_total >= 0 ? rows_total : 0) * g.heads_q;
   MetaCopy mc;
   int nseg = 0;
   int64_t run = 0;
@@ -1055,14 +1197,16 @@ hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, c
     run += count;
     mc.end[nseg++] = run;
   };
-  seg(st.header, d.header, 8);
-  seg(st.seqdesc, d.seqdesc, 8 * (int64_t)g.batch);
-  seg(st.cu_rows, d.cu_rows, g.batch + 1);
-  seg(st.cu_q, d.cu_q, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
-  seg(st.cu_k, d.cu_k, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
-  seg(st.work_desc, d.work_desc, 4 * tasks);
-  seg(st.section_off, d.section_off, kNumQueues + 1);
-  seg(st.task_rec, d.task_rec, kTaskRecInts * tasks);
+  if (st.header != d.header) {
+    seg(st.header, d.header, 8);
+    seg(st.seqdesc, d.seqdesc, 8 * (int64_t)g.batch);
+    seg(st.cu_rows, d.cu_rows, g.batch + 1);
+    seg(st.cu_q, d.cu_q, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
+    seg(st.cu_k, d.cu_k, g.layout == MPB_LAYOUT_THD ? g.batch + 1 : 0);
+    seg(st.work_desc, d.work_desc, 4 * tasks);
+    seg(st.section_off, d.section_off, kNumQueues + 1);
+    seg(st.task_rec, d.task_rec, kTaskRecInts * tasks);
+  }
   mc.total = run;
   const int threads = g.tile_q < 64 ? 64 : g.tile_q;
   const size_t ep_bytes = (size_t)g.nfunc * g.tile_q * 4;
@@ -1074,6 +1218,49 @@ hipError_t launch_plan_materialize(const PlanGeo& g, const int32_t* mask_func, c
   const size_t lds = (size_t)g.nk_max * 4 + (stage ? ep_bytes : 0);
   hipLaunchKernelGGL(plan_materialize_kernel, dim3((unsigned)(items > 0 ? items : 1)),
                      dim3(threads), lds, s, g, mask_func, st, d, w, rows_total, stage, mc);
+  return hipGetLastError();
+}
+
+
+namespace {
+struct FinishShape {
+  int rows_in_lds, stage, per_wg;
+  size_t lds;
+};
+FinishShape finish_shape(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks) {
+  FinishShape f;
+  const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
+  const size_t cnt_bytes = cnt_in_lds ? (size_t)(g.nk_max + 1) * nchunks * 4 : 0;
+  f.rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  const size_t row_bytes =
+      f.rows_in_lds ? (size_t)(4 * rows + 2 + (f.rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4
+                    : 0;
+  const int sg = g.tile_q < 64 ? 64 : g.tile_q;
+  f.per_wg = 1024 / sg;
+  const size_t ep_bytes = (size_t)g.nfunc * g.tile_q * 4;
+  // endpoints staged in LDS when every row of a workgroup fits in 96 KiB
+  f.stage = (size_t)f.per_wg * ((size_t)g.nk_max * 4 + ep_bytes) <= 96 * 1024 ? 1 : 0;
+  if (f.stage && g.tile_q >= 64 && (int64_t)g.nfunc * g.total_q * 4 < ((int64_t)1 << 31))
+    f.stage = 2;
+  const size_t mat_bytes = (size_t)f.per_wg * ((size_t)g.nk_max * 4 + (f.stage ? ep_bytes : 0));
+  f.lds = std::max(cnt_bytes + row_bytes, mat_bytes);
+  return f;
+}
+}  // namespace
+
+bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks) {
+  return finish_shape(g, cnt_in_lds, nchunks).lds <= 120 * 1024;
+}
+
+hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                              const PlanWork& w, int32_t rows_total, hipStream_t s) {
+  const FinishShape f = finish_shape(g, w.chunk_cnt == nullptr, w.nchunks);
+  const int rows_in_lds = f.rows_in_lds, stage = f.stage, per_wg = f.per_wg;
+  const size_t lds = f.lds;
+  const int64_t items = (int64_t)g.mask_heads * (rows_total >= 0 ? rows_total : g.upper_rows);
+  const unsigned grid = (unsigned)(1 + (items + per_wg - 1) / per_wg);
+  hipLaunchKernelGGL(plan_finish_kernel, dim3(grid), dim3(1024), lds, s, g, mask_func, d, w,
+                     rows_total, stage, w.chunk_cnt ? 0 : 1, rows_in_lds);
   return hipGetLastError();
 }
 

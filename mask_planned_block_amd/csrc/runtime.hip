@@ -302,6 +302,60 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// Arrays of one plan block for `rows` plan rows, `pnnz` partial and `fnnz`
+// full tiles (exact counts, or upper bounds for a block allocated before the
+// header is known).
+struct BlockLayout {
+  size_t header, seqdesc, cu_rows, cu_q, cu_k, work_desc, sec, rec, p_off, f_off, p_idx, f_idx,
+      masks, bytes;
+};
+BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int64_t pnnz,
+                         int64_t fnnz) {
+  const int64_t n_off = p.mask_heads * rows + 1;
+  const int64_t tasks = rows * p.heads_q;
+  const bool thd = p.layout == MPB_LAYOUT_THD;
+  Carver c;
+  BlockLayout L;
+  L.header = c.take<int32_t>(8);
+  L.seqdesc = c.take<int32_t>(8 * (int64_t)p.batch);
+  L.cu_rows = c.take<int32_t>(p.batch + 1);
+  L.cu_q = c.take<int32_t>(thd ? p.batch + 1 : 0);
+  L.cu_k = c.take<int32_t>(thd ? p.batch + 1 : 0);
+  L.work_desc = c.take<int32_t>(4 * tasks);
+  L.sec = c.take<int32_t>(kNumQueues + 1);
+  L.rec = c.take<int32_t>(kTaskRecInts * tasks);
+  L.p_off = c.take<int32_t>(n_off);
+  L.f_off = c.take<int32_t>(n_off);
+  L.p_idx = c.take<int32_t>(pnnz);
+  L.f_idx = c.take<int32_t>(fnnz);
+  L.masks = c.take<uint32_t>(pnnz * tq * (tk / 32));
+  L.bytes = c.off;
+  return L;
+}
+PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
+  PlanDev d;
+  d.header = at<int32_t>(block, L.header);
+  d.seqdesc = at<int32_t>(block, L.seqdesc);
+  d.cu_rows = at<int32_t>(block, L.cu_rows);
+  d.cu_q = thd ? at<int32_t>(block, L.cu_q) : nullptr;
+  d.cu_k = thd ? at<int32_t>(block, L.cu_k) : nullptr;
+  d.work_desc = at<int32_t>(block, L.work_desc);
+  d.section_off = at<int32_t>(block, L.sec);
+  d.task_rec = at<int32_t>(block, L.rec);
+  d.p_off = at<int32_t>(block, L.p_off);
+  d.f_off = at<int32_t>(block, L.f_off);
+  d.p_idx = at<int32_t>(block, L.p_idx);
+  d.f_idx = at<int32_t>(block, L.f_idx);
+  d.p_masks = at<uint32_t>(block, L.masks);
+  return d;
+}
+
+// Plans whose block at the upper bound of every count stays under this size
+// are built in one pass: the block is allocated before the header is known
+// and every planner kernel writes its part in place, so the launches follow
+// each other with no host round trip and no staging copy.
+constexpr size_t kInPlaceBlockBytes = (size_t)32 << 20;
+
 int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 128 : 64; }
 int default_tile_k(const mpb_problem& p) {
   return (p.dtype == MPB_DTYPE_FP32 && p.head_dim > 64) ? 32 : 64;
@@ -512,22 +566,59 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
 
   const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
   const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
+  const bool thd = p.layout == MPB_LAYOUT_THD;
   uint32_t seq = ++slot->seq;
   if (seq == 0) seq = ++slot->seq;   // 0 is the slot's initial value
-  if ((e = launch_plan_geometry(g, cq, ck, sg, w, s)) != hipSuccess ||
-      (e = launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
-                                (int32_t)seq, s)) != hipSuccess ||
-      (e = launch_plan_schedule(g, sg, w, s)) != hipSuccess)
-    return device_status(e, "planner launch");
+
+  // In place (small plans): the block at the upper bound of every count,
+  // allocated now; every kernel writes the plan directly and the header is
+  // read back only to report errors and the exact counts.
+  const int64_t tiles_upper = items_upper * nk_max;
+  const BlockLayout L_up = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper);
+  const bool in_place = L_up.bytes <= kInPlaceBlockBytes && plan_finish_fits(g, cnt_in_lds, nchunks);
+  void* block = nullptr;
+  int blk_chunk = 0;
+  size_t blk_off = 0, blk_bytes = 0;
+  PlanDev d;
+  std::memset(&d, 0, sizeof(d));
+  if (in_place) {
+    if ((e = heap->alloc(L_up.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
+      return device_status(e, "plan allocation");
+    blk_bytes = L_up.bytes;
+    d = bind_block(block, L_up, thd);
+    if ((e = launch_plan_geometry(g, cq, ck, d, w, s)) != hipSuccess ||
+        (e = launch_plan_classify(g, mask_func, d, w, slot->arrive[dev], slot->pinned_dev,
+                                  (int32_t)seq, s)) != hipSuccess ||
+        (e = launch_plan_finish(g, mask_func, d, w, thd ? -1 : (int32_t)upper, s)) !=
+            hipSuccess) {
+      heap->release(blk_chunk, blk_off, blk_bytes, s);
+      return device_status(e, "planner launch");
+    }
+  } else {
+    if ((e = launch_plan_geometry(g, cq, ck, sg, w, s)) != hipSuccess ||
+        (e = launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
+                                  (int32_t)seq, s)) != hipSuccess ||
+        (e = launch_plan_schedule(g, sg, w, s)) != hipSuccess)
+      return device_status(e, "planner launch");
+  }
+  auto drop_block = [&]() {
+    if (block) heap->release(blk_chunk, blk_off, blk_bytes, s);
+  };
   // §4.5: the single header read-back of the build.
   bool published = false;
-  if ((e = wait_header(slot, s, seq, &published)) != hipSuccess)
+  if ((e = wait_header(slot, s, seq, &published)) != hipSuccess) {
+    drop_block();
     return device_status(e, "header read-back");
-  if (!published) return fail(MPB_ERR_DEVICE, "the planner did not publish its header");
+  }
+  if (!published) {
+    drop_block();
+    return fail(MPB_ERR_DEVICE, "the planner did not publish its header");
+  }
   int64_t header[8];
   for (int i = 0; i < 8; ++i) header[i] = ((volatile int32_t*)slot->pinned)[i];
   const uint32_t err = (uint32_t)header[7];
   if (err) {
+    drop_block();
     if (err & MPB_DEVERR_SEQLENS)
       return fail(MPB_ERR_SEQLENS,
                   "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
@@ -537,55 +628,31 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
     return fail(MPB_ERR_ENDPOINT_ORDER, "endpoints of some row are not nondecreasing");
   }
   const int64_t rows_total = header[0], pnnz = header[1], fnnz = header[2];
-  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0)
+  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0 || pnnz > tiles_upper ||
+      fnnz > tiles_upper) {
+    drop_block();
     return fail(MPB_ERR_DEVICE, "inconsistent plan header");
-
-  // Exact allocation: every retained array sized by the header, no capacity
-  // padding (§4.5); one block per plan.
-  const int64_t n_off = p.mask_heads * rows_total + 1;
+  }
   const int64_t tasks = rows_total * p.heads_q;
-  Carver ce;
-  const size_t e_header = ce.take<int32_t>(8);
-  const size_t e_seqdesc = ce.take<int32_t>(8 * (int64_t)p.batch);
-  const size_t e_cu_rows = ce.take<int32_t>(p.batch + 1);
-  const size_t e_cu_q = ce.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 0);
-  const size_t e_cu_k = ce.take<int32_t>(p.layout == MPB_LAYOUT_THD ? p.batch + 1 : 0);
-  const size_t e_work_desc = ce.take<int32_t>(4 * tasks);
-  const size_t e_sec = ce.take<int32_t>(kNumQueues + 1);
-  const size_t e_rec = ce.take<int32_t>(kTaskRecInts * tasks);
-  const size_t e_p_off = ce.take<int32_t>(n_off);
-  const size_t e_f_off = ce.take<int32_t>(n_off);
-  const size_t e_p_idx = ce.take<int32_t>(pnnz);
-  const size_t e_f_idx = ce.take<int32_t>(fnnz);
-  const size_t e_masks = ce.take<uint32_t>(pnnz * tq * (tk / 32));
-  void* block = nullptr;
-  int blk_chunk = 0;
-  size_t blk_off = 0;
-  if ((e = heap->alloc(ce.off, &block, &blk_chunk, &blk_off)) != hipSuccess)
-    return device_status(e, "plan allocation");
-  PlanDev d;
-  d.header = at<int32_t>(block, e_header);
-  d.seqdesc = at<int32_t>(block, e_seqdesc);
-  d.cu_rows = at<int32_t>(block, e_cu_rows);
-  d.cu_q = p.layout == MPB_LAYOUT_THD ? at<int32_t>(block, e_cu_q) : nullptr;
-  d.cu_k = p.layout == MPB_LAYOUT_THD ? at<int32_t>(block, e_cu_k) : nullptr;
-  d.work_desc = at<int32_t>(block, e_work_desc);
-  d.section_off = at<int32_t>(block, e_sec);
-  d.task_rec = at<int32_t>(block, e_rec);
-  d.p_off = at<int32_t>(block, e_p_off);
-  d.f_off = at<int32_t>(block, e_f_off);
-  d.p_idx = at<int32_t>(block, e_p_idx);
-  d.f_idx = at<int32_t>(block, e_f_idx);
-  d.p_masks = at<uint32_t>(block, e_masks);
-  if ((e = launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s)) !=
-      hipSuccess) {
-    heap->release(blk_chunk, blk_off, ce.off, s);
-    return device_status(e, "materialize launch");
+
+  if (!in_place) {
+    // Exact allocation: every retained array sized by the header, no
+    // capacity padding (§4.5); one block per plan.
+    const BlockLayout L = block_layout(p, tq, tk, rows_total, pnnz, fnnz);
+    if ((e = heap->alloc(L.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
+      return device_status(e, "plan allocation");
+    blk_bytes = L.bytes;
+    d = bind_block(block, L, thd);
+    if ((e = launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s)) !=
+        hipSuccess) {
+      drop_block();
+      return device_status(e, "materialize launch");
+    }
   }
 
   mpb_plan* plan = new (std::nothrow) mpb_plan;
   if (!plan) {
-    heap->release(blk_chunk, blk_off, ce.off, s);
+    drop_block();
     return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
   }
   plan->device = dev;
@@ -599,7 +666,7 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   plan->num_tasks = (int32_t)tasks;
   for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
   plan->block = block;
-  plan->bytes = ce.off;
+  plan->bytes = blk_bytes;
   plan->blk_chunk = blk_chunk;
   plan->blk_off = blk_off;
   plan->stream = s;
