@@ -635,6 +635,18 @@ __device__ inline void row_queue_counts(const PlanGeo& g, int b, int hm, int cos
   }
 }
 
+// Tasks of one row in queue q alone.
+__device__ inline int row_queue_count(const PlanGeo& g, int b, int hm, int cost, int q) {
+  const int group = g.heads_q / g.heads_k;
+  if (cost == 0) return q == kNumSections ? (g.mask_heads == 1 ? g.heads_q : 1) : 0;
+  if (q == kNumSections) return 0;
+  if (g.mask_heads == 1) {
+    int r;
+    return group * kv_heads_in_section(b, g.heads_k, q, &r);
+  }
+  return q == section_of(b, g.heads_k, hm / group) ? 1 : 0;
+}
+
 __device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int* secoff,
                                   const SampleGeo& sg, int il, int h, int hm, int s, int pos_s,
                                   int p_beg, int np, int f_beg, int nf, int first) {
@@ -674,6 +686,9 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
   const int32_t* F = w.f_off_tmp;
   const int32_t* FT = w.first_tile;   // indexed hm * upper_rows + row
   int32_t* order = w.order;
+  // header first, so that its load and the row loads are in flight together
+  const int hdr_err = d.header[7];
+  const int hdr_rows = d.header[0];
   if (rows_in_lds) {
     int* lp = lds_rows;
     int* lf = lp + n_up + 1;
@@ -688,8 +703,8 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     F = lf;
     FT = lt;
   }
-  if (d.header[7] != 0) return;  // the build failed: no plan is made
-  const int rows_total = d.header[0];
+  if (hdr_err != 0) return;  // the build failed: no plan is made
+  const int rows_total = hdr_rows;
   const int n = g.mask_heads * rows_total;
   const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
   const int nc = (n + 63) >> 6;
@@ -729,18 +744,33 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
   int tot[kNumQueues];
 #pragma unroll
   for (int s = 0; s < kNumQueues; ++s) tot[s] = 0;
-  for (int c = wv, k = 0; c < nc; c += 16, ++k) {
+  // With one chunk of rows, wavefront 0 ranks them while wavefronts 1..9 each
+  // total one queue; otherwise every wavefront does both for its chunks.
+  const bool one_chunk = nc == 1;
+  if (one_chunk && wv >= 1 && wv <= kNumQueues) {
+    const int q = wv - 1;
+    int v = 0;
+    if (lane < n) {
+      const int hm = lane / rows_total;
+      v = row_queue_count(g, sample_geo(g, d, cu, lane - hm * rows_total).b, hm, cost_of(lane), q);
+    }
+    const int t = wave_sum(v);
+    if (lane == 0) s_tot[q] = t;
+  }
+  for (int c = wv, k = 0; c < nc && !(one_chunk && wv > 0); c += 16, ++k) {
     const int i = c * 64 + lane;
     const bool live = i < n;
     int key = 0;
     if (live) {
       const int cost = cost_of(i);
       key = g.nk_max - cost;
-      const int hm = i / rows_total;
-      int v[kNumQueues];
-      row_queue_counts(g, sample_geo(g, d, cu, i - hm * rows_total).b, hm, cost, v);
+      if (!one_chunk) {
+        const int hm = i / rows_total;
+        int v[kNumQueues];
+        row_queue_counts(g, sample_geo(g, d, cu, i - hm * rows_total).b, hm, cost, v);
 #pragma unroll
-      for (int s = 0; s < kNumQueues; ++s) tot[s] += v[s];
+        for (int s = 0; s < kNumQueues; ++s) tot[s] += v[s];
+      }
     }
     uint64_t eq = __ballot(live);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -760,7 +790,7 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
       if ((eq & below) == 0) cnt[(int64_t)key * nc + c] = __popcll(eq);
     }
   }
-  if (wv < nc) {   // wavefronts that classified rows
+  if (!one_chunk && wv < nc) {   // wavefronts that classified rows
 #pragma unroll
     for (int s = 0; s < kNumQueues; ++s) {
       const int t = wave_sum(tot[s]);
@@ -768,7 +798,16 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     }
   }
   __syncthreads();
-  block_exclusive_scan_inplace(cnt, cnt_len, s_wave, &s_carry);
+  if (cnt_len <= 64) {   // one wavefront scans the whole count matrix
+    if (wv == 0) {
+      const int v = lane < cnt_len ? cnt[lane] : 0;
+      const int incl = wave_incl_scan(v, lane);
+      if (lane < cnt_len) cnt[lane] = incl - v;
+    }
+    __syncthreads();
+  } else {
+    block_exclusive_scan_inplace(cnt, cnt_len, s_wave, &s_carry);
+  }
   for (int c = wv, k = 0; c < nc; c += 16, ++k) {   // same row-to-thread map as above
     const int i = c * 64 + lane;
     if (i >= n) continue;
@@ -790,8 +829,22 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
   __syncthreads();
 
   // 2. in-section position of each row's first task, over the sorted rows
+  // (one chunk: wavefront q scans queue q)
   int32_t* rbase = rows_in_lds == 2 ? order + n_up : w.row_base;
-  for (int base = 0; base < n; base += 1024) {
+  if (one_chunk) {
+    if (wv < kNumQueues) {
+      int v = 0, i = 0;
+      if (lane < n) {
+        i = order[lane];
+        const int hm = i / rows_total;
+        v = row_queue_count(g, sample_geo(g, d, cu, i - hm * rows_total).b, hm, cost_of(i), wv);
+      }
+      const int incl = wave_incl_scan(v, lane);
+      if (lane < n) rbase[(int64_t)i * kNumQueues + wv] = incl - v;
+    }
+    __syncthreads();
+  }
+  for (int base = 0; base < n && !one_chunk; base += 1024) {
     const int pos = base + tid;
     int v[kNumQueues];
     int i = 0;
