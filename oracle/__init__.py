@@ -66,6 +66,11 @@ def _load():
         lib.orc_plan_sizes.argtypes = [vp, vp, vp, vp]
         lib.orc_plan_export.argtypes = [vp, P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.orc_plan_free.argtypes = [vp]
+        lib.orc_k2q_build.argtypes = [P, vp, vp, vp, ctypes.c_int]
+        lib.orc_k2q_build.restype = vp
+        lib.orc_k2q_sizes.argtypes = [vp, vp]
+        lib.orc_k2q_export.argtypes = [vp, P, vp, vp, vp, vp, vp, vp]
+        lib.orc_k2q_free.argtypes = [vp]
         lib.orc_attention.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_double, ctypes.c_int,
                                       ctypes.c_double, ctypes.c_int, vp, ctypes.c_int,
                                       ctypes.c_int64, vp, vp, vp, ctypes.c_int]
@@ -162,6 +167,50 @@ def build_plan(w, tile_q: int, tile_k: int, nthreads: Optional[int] = None) -> P
                     cls[:items * nkm].reshape(w.mask_heads, R, nkm))
     finally:
         lib.orc_plan_free(h)
+
+
+class K2Q:
+    """Host copy of the oracle's backward K2Q view (all arrays numpy).
+
+    header = (Q rows, K rows, partial nnz, full nnz); K rows flattened
+    head-major; p_masks [pnnz][tile_k][tile_q/32] (K-major predicate)."""
+
+    def __init__(self, header, tile_q, tile_k, cu_krows, p_off, p_idx, p_masks, f_off, f_idx):
+        self.header = header
+        self.tile_q, self.tile_k = tile_q, tile_k
+        self.cu_krows = cu_krows
+        self.p_off, self.p_idx, self.p_masks = p_off, p_idx, p_masks
+        self.f_off, self.f_idx = f_off, f_idx
+
+
+def build_k2q(w, tile_q: int, tile_k: int, nthreads: Optional[int] = None) -> Optional[K2Q]:
+    """Brute-force K2Q view ("Flex Attention Mask Plan Design" §4.4, §4.7);
+    None when the workload fails validation."""
+    lib = _load()
+    p = _problem(w, tile_q, tile_k)
+    mf, cq, ck = _i32(w.mask_func), _i32(w.cu_seqlens_q), _i32(w.cu_seqlens_k)
+    h = lib.orc_k2q_build(ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck),
+                          nthreads or default_threads())
+    if not h:
+        return None
+    try:
+        header = np.zeros(4, dtype=np.int64)
+        lib.orc_k2q_sizes(h, _ptr(header))
+        kitems = w.mask_heads * int(header[1])
+        pn, fn = int(header[2]), int(header[3])
+        wq = tile_q // 32
+        cu_krows = np.zeros(w.batch + 1, np.int32)
+        p_off = np.zeros(kitems + 1, np.int32)
+        f_off = np.zeros(kitems + 1, np.int32)
+        p_idx = np.zeros(max(pn, 1), np.int32)
+        f_idx = np.zeros(max(fn, 1), np.int32)
+        p_masks = np.zeros(max(pn * tile_k * wq, 1), np.uint32)
+        lib.orc_k2q_export(h, ctypes.byref(p), _ptr(cu_krows), _ptr(p_off), _ptr(p_idx),
+                           _ptr(p_masks), _ptr(f_off), _ptr(f_idx))
+        return K2Q(header, tile_q, tile_k, cu_krows, p_off, p_idx[:pn],
+                   p_masks[:pn * tile_k * wq].reshape(pn, tile_k, wq), f_off, f_idx[:fn])
+    finally:
+        lib.orc_k2q_free(h)
 
 
 def attention(w, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = None):

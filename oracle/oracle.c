@@ -30,6 +30,8 @@
  *                 rows with nothing visible give O = 0 and LSE = -inf (mask
  *                 plan design §6.1).  LSE is the natural log of the sum of
  *                 exp(score) over visible keys, scores after score_mod.
+ *   - K2Q view  : §4.4 / §4.7, the same pair classes read K-major, with a
+ *                 K-major predicate per partial pair (see orc_k2q_build).
  *   - score_mod : softcap c*tanh(s/c) then ALiBi + slope_h*(k-q) with
  *                 sample-local positions (optionally ALiBi first); the scale is
  *                 applied before either.
@@ -321,6 +323,195 @@ void orc_plan_export(const orc_plan* P, const orc_problem* p, int32_t* cu_rows, 
   if (f_idx) memcpy(f_idx, P->f_idx, sizeof(int32_t) * P->header[2]);
   if (p_masks) memcpy(p_masks, P->p_masks, sizeof(uint32_t) * P->header[1] * p->tile_q * P->words);
   if (cls) memcpy(cls, P->cls, (size_t)items * P->nk_max);
+}
+
+/* ------------------------------------------------------------ K2Q view */
+
+/* Backward K-major view ("Flex Attention Mask Plan Design" §4.4 counting,
+ * §4.7 materialization): for every mask head and K plan row (one K tile of
+ * one sample; K rows flattened head-major, flat = hm*krows_total + krow,
+ * krow = cu_krows[b] + j), the sample-local Q tiles i whose pair (i, j) is
+ * partial and, independently, full -- the same three-way class as §4.3 --
+ * in ascending i.  Each partial pair carries a K-major predicate:
+ * word [r][c/32], bit c%32, is 1 iff score (Q row i*T_Q + c, K column
+ * j*T_KV + r) is in bounds and visible.  Computed here from the dense
+ * expansion of every Q tile, in two passes (classes and counts, then lists
+ * and payload). */
+typedef struct {
+  int64_t header[4];          /* Q rows, K rows, partial nnz, full nnz */
+  int32_t krows_total, qrows_total;
+  int32_t* cu_krows;          /* [B+1] */
+  int32_t* cu_qrows;          /* [B+1] */
+  uint8_t* cls;               /* [Hmask][krows_total][max Q rows per sample] */
+  int32_t qrows_max;
+  int32_t* p_off;             /* [Hmask*krows+1] */
+  int32_t* f_off;
+  int32_t* p_idx;
+  int32_t* f_idx;
+  uint32_t* p_masks;          /* [pnnz][tile_k][tile_q/32] */
+} orc_k2q;
+
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  orc_k2q* V;
+  int64_t item_begin, item_end;   /* (hm, b, i) items, i over the sample's Q tiles */
+  int64_t* item_tab;              /* [items][3] */
+  int phase;
+} k2q_job;
+
+static void* k2q_worker(void* arg) {
+  k2q_job* J = (k2q_job*)arg;
+  const orc_problem* p = J->p;
+  orc_k2q* V = J->V;
+  int64_t pitch = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)p->tile_q * pitch);
+  int wq = p->tile_q / 32;
+  for (int64_t it = J->item_begin; it < J->item_end; ++it) {
+    int hm = (int)J->item_tab[3 * it], b = (int)J->item_tab[3 * it + 1];
+    int64_t i = J->item_tab[3 * it + 2];
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t r0 = i * p->tile_q;
+    int64_t nk = (k_len + p->tile_k - 1) / p->tile_k;
+    expand_tile_rows(p, J->mf, hm, q_off, q_len, r0, k_len, vis);
+    for (int64_t j = 0; j < nk; ++j) {
+      int64_t c0 = j * p->tile_k;
+      int64_t flat = (int64_t)hm * V->krows_total + V->cu_krows[b] + j;
+      uint8_t* cls = V->cls + flat * V->qrows_max;
+      if (J->phase == 0) {
+        int64_t count = 0;
+        for (int r = 0; r < p->tile_q; ++r)
+          for (int c = 0; c < p->tile_k; ++c)
+            if (r0 + r < q_len && c0 + c < k_len && vis[(int64_t)r * k_len + c0 + c]) ++count;
+        int in_bounds = (r0 + p->tile_q <= q_len) && (c0 + p->tile_k <= k_len);
+        if (count == 0) cls[i] = 0;
+        else if (in_bounds && count == (int64_t)p->tile_q * p->tile_k) cls[i] = 2;
+        else cls[i] = 1;
+      } else if (cls[i] != 0) {
+        /* rank of i among this K row's Q tiles of the same class */
+        int64_t rank = 0;
+        for (int64_t i2 = 0; i2 < i; ++i2) rank += cls[i2] == cls[i];
+        if (cls[i] == 2) {
+          V->f_idx[V->f_off[flat] + rank] = (int32_t)i;
+          continue;
+        }
+        int64_t n = V->p_off[flat] + rank;
+        V->p_idx[n] = (int32_t)i;
+        uint32_t* words = V->p_masks + n * (int64_t)p->tile_k * wq;
+        for (int r = 0; r < p->tile_k; ++r)          /* K row of the tile */
+          for (int w = 0; w < wq; ++w) {
+            uint32_t word = 0;
+            for (int bit = 0; bit < 32; ++bit) {
+              int64_t c = 32 * w + bit;                /* Q row of the tile */
+              if (r0 + c < q_len && c0 + r < k_len && vis[c * k_len + c0 + r]) word |= 1u << bit;
+            }
+            words[r * wq + w] = word;
+          }
+      }
+    }
+  }
+  free(vis);
+  return NULL;
+}
+
+static void run_k2q_phase(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                          const int32_t* cu_k, orc_k2q* V, int64_t* tab, int64_t items, int phase,
+                          int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > items) nthreads = items > 0 ? (int)items : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  k2q_job* jobs = (k2q_job*)malloc(sizeof(k2q_job) * nthreads);
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (k2q_job){p, mf, cu_q, cu_k, V, items * t / nthreads, items * (t + 1) / nthreads, tab,
+                        phase};
+    pthread_create(&th[t], NULL, k2q_worker, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* Returns NULL on allocation failure or invalid input (the forward plan's
+ * validation decides that). */
+orc_k2q* orc_k2q_build(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                       const int32_t* cu_k, int nthreads) {
+  if (orc_validate(p, mf, cu_q, cu_k)) return NULL;
+  orc_k2q* V = (orc_k2q*)calloc(1, sizeof(orc_k2q));
+  if (!V) return NULL;
+  int B = p->batch;
+  V->cu_krows = (int32_t*)calloc((size_t)B + 1, sizeof(int32_t));
+  V->cu_qrows = (int32_t*)calloc((size_t)B + 1, sizeof(int32_t));
+  int64_t qmax = 1;
+  for (int b = 0; b < B; ++b) {
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, cu_q, cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t qr = (q_len + p->tile_q - 1) / p->tile_q;
+    if (qr > qmax) qmax = qr;
+    V->cu_qrows[b + 1] = V->cu_qrows[b] + (int32_t)qr;
+    V->cu_krows[b + 1] = V->cu_krows[b] + (int32_t)((k_len + p->tile_k - 1) / p->tile_k);
+  }
+  V->qrows_total = V->cu_qrows[B];
+  V->krows_total = V->cu_krows[B];
+  V->qrows_max = (int32_t)qmax;
+  int64_t kitems = (int64_t)p->mask_heads * V->krows_total;
+  V->cls = (uint8_t*)calloc((size_t)(kitems > 0 ? kitems : 1) * qmax, 1);
+  int64_t items = (int64_t)p->mask_heads * V->qrows_total;
+  int64_t* tab = (int64_t*)malloc(sizeof(int64_t) * 3 * (size_t)(items > 0 ? items : 1));
+  int64_t n = 0;
+  for (int hm = 0; hm < p->mask_heads; ++hm)
+    for (int b = 0; b < B; ++b)
+      for (int64_t i = 0; i < V->cu_qrows[b + 1] - V->cu_qrows[b]; ++i) {
+        tab[3 * n] = hm; tab[3 * n + 1] = b; tab[3 * n + 2] = i; ++n;
+      }
+  run_k2q_phase(p, mf, cu_q, cu_k, V, tab, items, 0, nthreads);
+  V->p_off = (int32_t*)calloc((size_t)kitems + 1, sizeof(int32_t));
+  V->f_off = (int32_t*)calloc((size_t)kitems + 1, sizeof(int32_t));
+  for (int64_t f = 0; f < kitems; ++f) {
+    int32_t pc = 0, fc = 0;
+    for (int64_t i = 0; i < qmax; ++i) {
+      pc += V->cls[f * qmax + i] == 1;
+      fc += V->cls[f * qmax + i] == 2;
+    }
+    V->p_off[f + 1] = V->p_off[f] + pc;
+    V->f_off[f + 1] = V->f_off[f] + fc;
+  }
+  V->header[0] = V->qrows_total;
+  V->header[1] = V->krows_total;
+  V->header[2] = V->p_off[kitems];
+  V->header[3] = V->f_off[kitems];
+  V->p_idx = (int32_t*)calloc((size_t)V->header[2] + 1, sizeof(int32_t));
+  V->f_idx = (int32_t*)calloc((size_t)V->header[3] + 1, sizeof(int32_t));
+  V->p_masks = (uint32_t*)calloc((size_t)V->header[2] * p->tile_k * (p->tile_q / 32) + 1,
+                                 sizeof(uint32_t));
+  run_k2q_phase(p, mf, cu_q, cu_k, V, tab, items, 1, nthreads);
+  free(tab);
+  return V;
+}
+
+void orc_k2q_sizes(const orc_k2q* V, int64_t* header4) {
+  for (int i = 0; i < 4; ++i) header4[i] = V->header[i];
+}
+
+void orc_k2q_export(const orc_k2q* V, const orc_problem* p, int32_t* cu_krows, int32_t* p_off,
+                    int32_t* p_idx, uint32_t* p_masks, int32_t* f_off, int32_t* f_idx) {
+  int64_t kitems = (int64_t)p->mask_heads * V->krows_total;
+  if (cu_krows) memcpy(cu_krows, V->cu_krows, sizeof(int32_t) * (p->batch + 1));
+  if (p_off) memcpy(p_off, V->p_off, sizeof(int32_t) * (kitems + 1));
+  if (f_off) memcpy(f_off, V->f_off, sizeof(int32_t) * (kitems + 1));
+  if (p_idx) memcpy(p_idx, V->p_idx, sizeof(int32_t) * V->header[2]);
+  if (f_idx) memcpy(f_idx, V->f_idx, sizeof(int32_t) * V->header[3]);
+  if (p_masks)
+    memcpy(p_masks, V->p_masks, sizeof(uint32_t) * V->header[2] * p->tile_k * (p->tile_q / 32));
+}
+
+void orc_k2q_free(orc_k2q* V) {
+  if (!V) return;
+  free(V->cu_krows); free(V->cu_qrows); free(V->cls); free(V->p_off); free(V->f_off);
+  free(V->p_idx); free(V->f_idx); free(V->p_masks);
+  free(V);
 }
 
 void orc_plan_free(orc_plan* P) {

@@ -249,6 +249,123 @@ def test_causal_closed_form():
     assert int((P.cls == 0).sum()) == 6
 
 
+# ------------------------------------------------------------------ K2Q view
+
+def _check_k2q_against_brute_force(w, tq, tk):
+    """Backward K2Q view (mask plan design §4.4, §4.7) against tile classes
+    and visibility taken from the dense boolean matrix."""
+    V = oracle.build_k2q(w, tq, tk, nthreads=2)
+    assert V is not None
+    bf = brute_force_classes(w, tq, tk)
+    mask = dense_mask(w)
+    wq = tq // 32
+    nks = [-(-w.sample_bounds(b)[3] // tk) for b in range(w.batch)]
+    nqs = [-(-w.sample_bounds(b)[1] // tq) for b in range(w.batch)]
+    assert V.cu_krows.tolist() == np.concatenate([[0], np.cumsum(nks)]).tolist()
+    K = int(V.cu_krows[-1])
+    assert int(V.header[0]) == sum(nqs) and int(V.header[1]) == K
+    tot_p = tot_f = 0
+    for hm in range(w.mask_heads):
+        for b in range(w.batch):
+            qo, ql, ko, kl = w.sample_bounds(b)
+            rows = [row for (bb, i, row) in bf[hm] if bb == b]
+            for j in range(nks[b]):
+                flat = hm * K + int(V.cu_krows[b]) + j
+                col = [row[j] for row in rows]
+                pidx = V.p_idx[V.p_off[flat]:V.p_off[flat + 1]].tolist()
+                fidx = V.f_idx[V.f_off[flat]:V.f_off[flat + 1]].tolist()
+                assert pidx == [i for i, c in enumerate(col) if c == 1], (hm, b, j)
+                assert fidx == [i for i, c in enumerate(col) if c == 2], (hm, b, j)
+                tot_p += len(pidx)
+                tot_f += len(fidx)
+                for n, i in enumerate(pidx):
+                    words = V.p_masks[V.p_off[flat] + n]
+                    for r in range(tk):
+                        for c in range(tq):
+                            bit = (int(words[r, c // 32]) >> (c % 32)) & 1
+                            q, kk = i * tq + c, j * tk + r
+                            want = q < ql and kk < kl and bool(mask[(hm, qo + q)][kk])
+                            assert bit == int(want), (hm, b, i, j, r, c)
+    assert (int(V.header[2]), int(V.header[3])) == (tot_p, tot_f)
+    assert V.p_masks.shape[1:] == (tk, wq)
+    return V
+
+
+@pytest.mark.parametrize("tq,tk", [(32, 32), (64, 32), (32, 64)])
+def test_k2q_brute_force_random_intervals(tq, tk):
+    rng = np.random.default_rng(7)
+    B, Sq, Sk, nfunc = 2, 75, 101, 5
+    mf = np.sort(rng.integers(0, Sk + 1, size=(2, nfunc, B * Sq)), axis=1).astype(np.int32)
+    w = W.custom(mf, batch=B, seqlen_q=Sq, seqlen_k=Sk, heads_q=2, head_dim=32, with_values=False)
+    _check_k2q_against_brute_force(w, tq, tk)
+
+
+def test_k2q_brute_force_varlen():
+    rng = np.random.default_rng(13)
+    lq, lk = [40, 0, 97, 33], [50, 20, 0, 70]
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    mf = np.zeros((1, 3, int(cq[-1])), np.int32)
+    for b, L in enumerate(lq):
+        if L:
+            mf[0, :, cq[b]:cq[b + 1]] = np.sort(rng.integers(0, lk[b] + 1, size=(3, L)), axis=0)
+    w = W.custom(mf, layout=W.LAYOUT_THD, cu_seqlens_q=cq, cu_seqlens_k=ck, head_dim=32,
+                 with_values=False)
+    V = _check_k2q_against_brute_force(w, 32, 32)
+    assert V.cu_krows.tolist() == [0, 2, 3, 3, 6]
+
+
+def test_k2q_is_the_q2k_relation_transposed():
+    # Design invariant 7: Q2K and K2Q describe the same block relation, and a
+    # partial pair's K-major word bits are its Q-major bits transposed.
+    rng = np.random.default_rng(17)
+    B, S, nfunc, T = 2, 130, 7, 32
+    mf = np.sort(rng.integers(0, S + 1, size=(1, nfunc, B * S)), axis=1).astype(np.int32)
+    w = W.custom(mf, batch=B, seqlen_q=S, seqlen_k=S, heads_q=1, head_dim=32, with_values=False)
+    P = oracle.build_plan(w, 64, T, nthreads=2)
+    V = oracle.build_k2q(w, 64, T, nthreads=2)
+    assert (int(P.header[1]), int(P.header[2])) == (int(V.header[2]), int(V.header[3]))
+    K = int(V.cu_krows[-1])
+    for b in range(B):
+        for i in range(int(P.cu_rows[b + 1] - P.cu_rows[b])):
+            qflat = int(P.cu_rows[b]) + i
+            plist = P.p_idx[P.p_off[qflat]:P.p_off[qflat + 1]].tolist()
+            for n, j in enumerate(plist):
+                kflat = int(V.cu_krows[b]) + j
+                kp = V.p_idx[V.p_off[kflat]:V.p_off[kflat + 1]].tolist()
+                assert i in kp
+                m = kp.index(i)
+                qm = P.p_masks[P.p_off[qflat] + n]        # [64][1]
+                km = V.p_masks[V.p_off[kflat] + m]        # [32][2]
+                for r in range(64):
+                    for c in range(T):
+                        assert ((int(qm[r, c // 32]) >> (c % 32)) & 1) == \
+                            ((int(km[c, r // 32]) >> (r % 32)) & 1)
+            flist = P.f_idx[P.f_off[qflat]:P.f_off[qflat + 1]].tolist()
+            for j in flist:
+                kflat = int(V.cu_krows[b]) + j
+                assert i in V.f_idx[V.f_off[kflat]:V.f_off[kflat + 1]].tolist()
+    assert K == B * (-(-S // T))
+
+
+def test_k2q_causal_closed_form():
+    # Square causal mask, T_Q = T_KV = T, S a multiple of T: K row j is
+    # partial for Q tile j alone and full for every Q tile after it.
+    for S, T in [(256, 64), (256, 32)]:
+        w = W.tiny_causal(seqlen=S, heads=1, with_values=False)
+        V = oracle.build_k2q(w, T, T, nthreads=2)
+        n = S // T
+        for j in range(n):
+            assert V.p_idx[V.p_off[j]:V.p_off[j + 1]].tolist() == [j]
+            assert V.f_idx[V.f_off[j]:V.f_off[j + 1]].tolist() == list(range(j + 1, n))
+        # the diagonal tile's K-major predicate: column (Q row) c sees K row r iff r <= c
+        for j in range(n):
+            km = V.p_masks[V.p_off[j]]
+            for r in range(T):
+                bits = [(int(km[r, c // 32]) >> (c % 32)) & 1 for c in range(T)]
+                assert bits == [int(r <= c) for c in range(T)]
+
+
 def test_tail_tile_never_full():
     # Every in-bound element visible, but the tile sticks out past k_len: partial.
     w = W.custom(np.full((1, 1, 64), 40, np.int32), batch=1, seqlen_q=64, seqlen_k=40,
