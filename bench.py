@@ -56,6 +56,24 @@ def plan_stats(w, plan):
             "tasks": int(plan.info.num_tasks)}
 
 
+def k2q_bytes(w, plan):
+    """Algorithmic bytes of the K2Q view's materialization: the endpoints
+    read once, then the lists, offsets, K-row prefixes and the K-major
+    payload (T_Q*T_KV/8 bytes per partial pair) written once."""
+    h = plan.info.header
+    p = plan.problem
+    krows, pn, fn = int(h[4]), int(h[5]), int(h[6])
+    read = 4 * w.mask_heads * w.nfunc * w.total_q
+    write = 4 * (pn + fn) + pn * p.tile_q * p.tile_k // 8 + 8 * (w.mask_heads * krows + 1) + \
+        4 * (w.batch + 1)
+    return read + write
+
+
+def _median_stages(runs):
+    import numpy as np
+    return {k: round(float(np.median([r[k] for r in runs])), 2) for k in runs[0]}
+
+
 def cpu_baseline(w, min_seconds=10.0):
     """The oracle, as it is, on the host cores: whole-workload passes of the
     fp64 attention (plus the plan) until min_seconds have elapsed."""
@@ -83,7 +101,8 @@ def source_digest(path=ATTN_SOURCE):
 
 def _kernel_group(name):
     for key in ("attn_fwd_kernel", "plan_classify_kernel", "plan_schedule_kernel",
-                "plan_materialize_kernel", "plan_geometry_kernel", "elementwise"):
+                "plan_materialize_kernel", "plan_geometry_kernel", "plan_finish_kernel",
+                "plan_k2q_count_kernel", "plan_k2q_materialize_kernel", "elementwise"):
         if key in name:
             return key
     return None
@@ -290,6 +309,40 @@ def main():
         p2.close()
     plan_us = float(np.median(tb)) * 1e6
 
+    def build_runs(bwd, timed, n=10):
+        """n builds, each alone on the stream: host clock around the call
+        (with its one sync), or the GPU stage times from its HIP events."""
+        out = []
+        for _ in range(n):
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            p3 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream,
+                                     build_backward=bwd, time_stages=timed)
+            torch.cuda.synchronize()
+            out.append(p3.stage_times() if timed else time.perf_counter() - a)
+            if len(out) < n:
+                p3.close()
+        return out, p3
+
+    stage_runs, p3 = build_runs(False, True)
+    p3.close()
+    plan_stages = _median_stages(stage_runs)
+    # the backward K2Q view added to the same build
+    tbk, p3 = build_runs(True, False)
+    p3.close()
+    k2q_runs, pk = build_runs(True, True)
+    k2q_stages = _median_stages(k2q_runs)
+    kb = k2q_bytes(w, pk)
+    kmat = k2q_stages["k2q_materialize"]
+    kh = pk.info.header
+    plan_k2q = {"build_us_host": round(float(np.median(tbk)) * 1e6, 1), "stages_us": k2q_stages,
+                "k_rows": int(kh[4]), "partial": int(kh[5]), "full": int(kh[6]),
+                "materialize_algorithmic_bytes": kb,
+                "materialize_gbs": round(kb / (kmat * 1e-6) / 1e9, 1) if kmat > 0 else None,
+                "materialize_frac_hbm": round(kb / (kmat * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                if kmat > 0 else None}
+    pk.close()
+
     # all-visible forward at the same shape (nfunc = 1, F0 = k_len): the
     # dense attention this mask skips most of
     dense_ref = None
@@ -369,7 +422,8 @@ def main():
             "us_in_step_median": round(fwd_in_step_med_us, 2),
             "dense_all_visible": dense_ref,
         },
-        "plan": {"build_us_host": round(plan_us, 1), **stats},
+        "plan": {"build_us_host": round(plan_us, 1), "stages_us": plan_stages, **stats},
+        "plan_k2q": plan_k2q,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }

@@ -94,7 +94,8 @@ typedef struct mpb_signature {
 } mpb_signature;
 
 typedef struct mpb_plan_info {
-  int64_t header[8];       /* fwd Q rows, fwd partial nnz, fwd full nnz, 0, 0, 0, 0, error bits */
+  int64_t header[8];       /* fwd Q rows, fwd partial nnz, fwd full nnz, then (K2Q view only,
+                            * else 0) Q rows, K rows, K2Q partial nnz, K2Q full nnz; error bits */
   int32_t rows_total;      /* Q plan rows over all samples */
   int32_t nk_max;          /* K tiles of the longest sample */
   int32_t words_per_row;   /* tile_k / 32 */
@@ -192,6 +193,51 @@ mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seq
  * MI355X's round-robin workgroup-to-XCD dispatch].  Synchronises the plan's
  * build stream. */
 mpb_status mask_plan_export_launch_order(const mpb_plan* plan, int32_t* records);
+
+/* Build options.  build_backward = 1 adds the backward K2Q view [MPD §4.4
+ * K2Q counting, §4.7 K2Q materialization] at the plan's own tile geometry
+ * (read from the forward classification; a different backward geometry is
+ * not built).  For every mask head and K plan row (one T_KV tile of one
+ * sample's K; K rows flattened head-major, flat = hm*krows_total + krow,
+ * krow = cu_krows[b] + j) it holds the sample-local Q tiles whose pair with
+ * that K tile is partial and, independently, full, each list ascending, and
+ * for every partial pair a K-major predicate: word [r][c/32], bit c%32, is 1
+ * iff score (Q row c, K row r) of the pair is in bounds and visible
+ * (consumer layout chosen for a K-major backward: one word row per K row).
+ * The header then also holds {Q rows, K rows, K2Q partial nnz, K2Q full nnz}
+ * in slots 3..6, read back like the forward values.  NULL options = all
+ * zero. */
+typedef struct {
+  int32_t build_backward;  /* 0 or 1: also build the K2Q view */
+  int32_t time_stages;     /* 0 or 1: record HIP events around each planner launch
+                            * (mask_plan_stage_times); adds event records to the
+                            * build stream, for measurement only */
+} mpb_build_options;
+
+/* mask_plan_build with options; same arguments, errors and lifetime rules. */
+mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_options* options,
+                              const int32_t* mask_func, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* stream, mpb_plan** out);
+
+/* Copies the K2Q view to host memory; any pointer may be NULL.  Sizes:
+ * cu_krows [batch+1], p_off/f_off [mask_heads*header[4]+1], p_idx
+ * [header[5]], f_idx [header[6]], p_masks [header[5]*tile_k*tile_q/32].
+ * MPB_ERR_INVALID_ARGUMENT if the plan was built without it.  Synchronises
+ * the plan's build stream. */
+mpb_status mask_plan_export_k2q(const mpb_plan* plan, int32_t* cu_krows, int32_t* p_off,
+                                int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
+                                int32_t* f_idx);
+
+/* GPU time of each planner stage of a build made with time_stages = 1, in
+ * microseconds, from the HIP events around its launches [MPD §4.2-§4.7
+ * stages]; us must hold 7 floats: us[0] THD geometry (an empty span for
+ * BSHD), us[1] classify, us[2] schedule (for a plan built in place, schedule
+ * and materialization in one launch), us[3] materialization (-1 when fused),
+ * us[4] K2Q count, us[5] K2Q materialization (-1 without the view), us[6]
+ * first event to last (when the plan is not built in place this includes the
+ * host's header wait).  Waits for the build's last event.
+ * MPB_ERR_INVALID_ARGUMENT if the plan was built without time_stages. */
+mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us);
 
 /* Bytes of caller-provided device workspace flex_attn_fwd needs.  The
  * forward launches one workgroup per task in the plan's launch order, so no

@@ -72,6 +72,10 @@ class PlanInfo(ctypes.Structure):
                 ("device_bytes", ctypes.c_int64)]
 
 
+class BuildOptions(ctypes.Structure):
+    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32)]
+
+
 class ScoreMod(ctypes.Structure):
     _fields_ = [("softcap_enabled", ctypes.c_int32), ("softcap", ctypes.c_float),
                 ("alibi_enabled", ctypes.c_int32), ("alibi_slopes", ctypes.c_void_p),
@@ -85,6 +89,9 @@ def _load():
     lib = ctypes.CDLL(library_path)
     vp, P = ctypes.c_void_p, ctypes.POINTER
     lib.mask_plan_build.argtypes = [P(Problem), vp, vp, vp, vp, P(vp)]
+    lib.mask_plan_build_ex.argtypes = [P(Problem), P(BuildOptions), vp, vp, vp, vp, P(vp)]
+    lib.mask_plan_export_k2q.argtypes = [vp] + [vp] * 6
+    lib.mask_plan_stage_times.argtypes = [vp, vp]
     lib.mask_plan_destroy.argtypes = [vp]
     lib.mask_plan_info.argtypes = [vp, P(PlanInfo)]
     lib.mask_plan_export.argtypes = [vp] + [vp] * 9
@@ -99,8 +106,10 @@ def _load():
     lib.mpb_status_string.argtypes = [ctypes.c_int]
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
     lib.mpb_version.restype = ctypes.c_int32
-    for name in ("mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
-                 "mask_plan_export_launch_order", "flex_attn_fwd", "flex_attn_fwd_ablation"):
+    for name in ("mask_plan_build", "mask_plan_build_ex", "mask_plan_destroy", "mask_plan_info",
+                 "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times",
+                 "mask_plan_export_launch_order",
+                 "flex_attn_fwd", "flex_attn_fwd_ablation"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -174,6 +183,12 @@ class MaskPlan:
     def export(self):
         return mask_plan_export(self)
 
+    def export_k2q(self):
+        return mask_plan_export_k2q(self)
+
+    def stage_times(self):
+        return mask_plan_stage_times(self)
+
     def close(self):
         if self._h and self._h.value:
             _lib.mask_plan_destroy(self._h)
@@ -188,14 +203,22 @@ class MaskPlan:
 
 def mask_plan_build(problem: Problem, mask_func: torch.Tensor,
                     cu_seqlens_q: Optional[torch.Tensor] = None,
-                    cu_seqlens_k: Optional[torch.Tensor] = None, stream=None) -> MaskPlan:
-    """Builds a MaskPlan on the GPU (one header read-back; see include/mpb.h)."""
+                    cu_seqlens_k: Optional[torch.Tensor] = None, stream=None,
+                    build_backward: bool = False, time_stages: bool = False) -> MaskPlan:
+    """Builds a MaskPlan on the GPU (one header read-back; see include/mpb.h);
+    build_backward adds the K2Q view, time_stages records HIP events around the
+    planner launches (both through mask_plan_build_ex)."""
     mf = _dev_ptr(mask_func, "mask_func", torch.int32)
     cq = _dev_ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     ck = _dev_ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32)
     s = _stream_handle(stream)
     out = ctypes.c_void_p()
-    _check(_lib.mask_plan_build(ctypes.byref(problem), mf, cq, ck, s, ctypes.byref(out)))
+    if build_backward or time_stages:
+        opt = BuildOptions(int(build_backward), int(time_stages))
+        _check(_lib.mask_plan_build_ex(ctypes.byref(problem), ctypes.byref(opt), mf, cq, ck, s,
+                                       ctypes.byref(out)))
+    else:
+        _check(_lib.mask_plan_build(ctypes.byref(problem), mf, cq, ck, s, ctypes.byref(out)))
     return MaskPlan(out.value, s, problem)
 
 
@@ -240,6 +263,44 @@ def mask_plan_export(plan: MaskPlan) -> dict:
     _check(_lib.mask_plan_export_launch_order(plan.handle, ctypes.c_void_p(rec.ctypes.data)))
     a["launch"] = rec[:info.num_tasks]
     return a
+
+
+def mask_plan_export_k2q(plan: MaskPlan) -> dict:
+    """Host copies of the backward K2Q view (numpy); header slots 3..6 are
+    (Q rows, K rows, partial nnz, full nnz)."""
+    info = plan.info
+    p = info.problem
+    krows, pn, fn = int(info.header[4]), int(info.header[5]), int(info.header[6])
+    n_off = p.mask_heads * krows + 1
+    wq = p.tile_q // 32
+    a = {
+        "cu_krows": np.zeros(p.batch + 1, np.int32),
+        "p_off": np.zeros(n_off, np.int32),
+        "p_idx": np.zeros(max(pn, 1), np.int32),
+        "p_masks": np.zeros(max(pn * p.tile_k * wq, 1), np.uint32),
+        "f_off": np.zeros(n_off, np.int32),
+        "f_idx": np.zeros(max(fn, 1), np.int32),
+    }
+    ptrs = [ctypes.c_void_p(a[k].ctypes.data) for k in
+            ("cu_krows", "p_off", "p_idx", "p_masks", "f_off", "f_idx")]
+    _check(_lib.mask_plan_export_k2q(plan.handle, *ptrs))
+    a["p_idx"] = a["p_idx"][:pn]
+    a["f_idx"] = a["f_idx"][:fn]
+    a["p_masks"] = a["p_masks"][:pn * p.tile_k * wq].reshape(pn, p.tile_k, wq)
+    a["header"] = np.asarray(list(info.header), np.int64)
+    return a
+
+
+STAGE_NAMES = ("geometry", "classify", "schedule", "materialize", "k2q_count",
+               "k2q_materialize", "span")
+
+
+def mask_plan_stage_times(plan: MaskPlan) -> dict:
+    """GPU microseconds of each planner stage of a build made with
+    time_stages=True (-1 for a stage that did not run on its own)."""
+    us = (ctypes.c_float * len(STAGE_NAMES))()
+    _check(_lib.mask_plan_stage_times(plan.handle, ctypes.cast(us, ctypes.c_void_p)))
+    return {n: float(v) for n, v in zip(STAGE_NAMES, us)}
 
 
 def flex_attn_fwd_workspace_size(plan: MaskPlan) -> int:

@@ -88,6 +88,25 @@ constexpr int kMaxKTiles = 8191;
 constexpr int kHeaderSeq = 8;
 constexpr int kHostSlotInts = 16;
 
+// Backward K2Q view: plan arrays and build workspace.
+struct K2QDev {
+  int32_t* cu_krows;   // [B+1] K plan rows per sample, prefix
+  int32_t* p_off;      // [Hmask*krows+1]
+  int32_t* f_off;
+  int32_t* p_idx;      // sample-local Q tiles, ascending per K row
+  int32_t* f_idx;
+  uint32_t* p_masks;   // [pnnz][tile_k][tile_q/32]
+};
+struct K2QWork {
+  int32_t* pcnt;       // [Hmask][B][nk_max] (padded by sample)
+  int32_t* fcnt;
+  int32_t* cu_krows;   // [B+1]
+  int32_t* p_off;      // [Hmask*B*nk_max+1] compact exclusive offsets
+  int32_t* f_off;
+  int32_t* info;       // [4]: K rows total, partial nnz, full nnz, 0
+};
+constexpr int kHeaderSeq2 = 9;   // host slot index of the K2Q header's sequence number
+
 // ---- planner launchers (plan_kernels.hip) ----
 hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
                                 const PlanDev& d, const PlanWork& w, hipStream_t s);
@@ -118,6 +137,18 @@ hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const 
                               const PlanWork& w, int32_t rows_total, hipStream_t s);
 // Whether that launch's LDS fits (count matrix in LDS or not, its chunks).
 bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks);
+
+// Backward K2Q view (same tile geometry as the forward plan): count from the
+// classifier's bitsets, then (last workgroup) offsets and header values 3..6
+// published with `seq` at kHeaderSeq2; materialize lists and K-major payload
+// (the transpose of the Q2K payload: d is the finished forward plan).
+hipError_t launch_plan_k2q_count(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                 const K2QWork& kw, int32_t* arrive, int32_t* host_slot,
+                                 int32_t seq, hipStream_t s);
+// krows_total < 0: read from kw.info (launch before the header is back).
+hipError_t launch_plan_k2q_materialize(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                       const K2QWork& kw, const K2QDev& kd, int32_t krows_total,
+                                       hipStream_t s);
 
 // ---- attention ----
 enum ModKind : int32_t {

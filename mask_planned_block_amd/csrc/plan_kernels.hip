@@ -1195,6 +1195,352 @@ __global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
   }
 }
 
+
+// ---------------------------------------------------------------- backward K2Q view
+
+namespace {
+
+// Q rows [row_begin, row_begin + nrows) and K tiles nk of sample b.
+struct SampleRows {
+  int row_begin, nrows, nk, q_off, q_len, k_len;
+};
+__device__ inline SampleRows sample_rows(const PlanGeo& g, const PlanDev& d, int b) {
+  SampleRows r;
+  if (g.layout == MPB_LAYOUT_BSHD) {
+    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+    r.row_begin = b * rps;
+    r.nrows = rps;
+    r.nk = (g.seqlen_k + g.tile_k - 1) / g.tile_k;
+    r.q_off = b * g.seqlen_q;
+    r.q_len = g.seqlen_q;
+    r.k_len = g.seqlen_k;
+  } else {
+    const int32_t* sd = d.seqdesc + 8 * b;
+    r.q_off = sd[0];
+    r.q_len = sd[2];
+    r.k_len = sd[3];
+    r.row_begin = sd[4];
+    r.nrows = sd[5];
+    r.nk = sd[6];
+  }
+  return r;
+}
+
+}  // namespace
+
+// §4.4 K2Q counting, the count phase of a sparse transpose of the
+// classifier's bitsets: one wavefront per (mask head, sample, 32-tile word
+// of K tiles).  For every 64 Q rows of the sample the lanes load their row's
+// word; one ballot per K tile and class counts the partial and full Q
+// contributors, kept by lane j for K tile 32w + j.  The last workgroup (same
+// ticket protocol as the classifier) lays the K rows out per sample
+// (cu_krows), scans the counts into compact head-major exclusive offsets and
+// publishes the header's backward values {Q rows, K rows, partial nnz, full
+// nnz} (slots 3..6) with its own sequence number.
+__global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev d, PlanWork w,
+                                                             K2QWork kw, int32_t* arrive,
+                                                             int32_t* host_slot, int32_t seq) {
+  __shared__ int s_last;
+  __shared__ int s_wp[4], s_wf[4];
+  __shared__ int s_cu[1025];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t items = (int64_t)g.mask_heads * g.batch * g.words_k;
+  const int64_t item = (int64_t)blockIdx.x * 4 + wv;
+  // a failed classification (bad endpoints or prefixes) leaves the geometry
+  // and bitsets meaningless: count nothing, publish zeros
+  const bool failed = d.header[7] != 0;
+  if (item < items && !failed) {
+    const int wi = (int)(item % g.words_k);
+    const int64_t hb = item / g.words_k;
+    const int b = (int)(hb % g.batch);
+    const int hm = (int)(hb / g.batch);
+    const SampleRows sr = sample_rows(g, d, b);
+    int mp = 0, mf = 0;
+    for (int r0 = 0; r0 < sr.nrows; r0 += 64) {
+      uint32_t vis = 0u, full = 0u;
+      if (r0 + lane < sr.nrows && sr.row_begin + r0 + lane < g.upper_rows) {
+        const int64_t src = ((int64_t)hm * g.upper_rows + sr.row_begin + r0 + lane) * g.words_k + wi;
+        vis = w.vis_bits[src];
+        full = w.full_bits[src];
+      }
+      const uint32_t part = vis & ~full;
+#pragma unroll 4
+      for (int j = 0; j < 32; ++j) {
+        const int cp = __popcll(__ballot((part >> j) & 1u));
+        const int cf = __popcll(__ballot((full >> j) & 1u));
+        if (lane == j) {
+          mp += cp;
+          mf += cf;
+        }
+      }
+    }
+    const int kt = 32 * wi + lane;
+    if (lane < 32 && kt < sr.nk) {
+      const int64_t dst = ((int64_t)hm * g.batch + b) * g.nk_max + kt;
+      kw.pcnt[dst] = mp;
+      kw.fcnt[dst] = mf;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = prev == (int)gridDim.x - 1 ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __atomic_thread_fence(__ATOMIC_ACQUIRE);
+  if (threadIdx.x == 0) __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // K rows per sample: cu_krows (one thread per sample, then a serial pass
+  // over the wavefront totals; B <= 1024 samples are kept in LDS)
+  const int tid = threadIdx.x;
+  int* cu = g.batch < 1025 ? s_cu : kw.cu_krows;
+  for (int b = tid; b < g.batch; b += 256) cu[b + 1] = failed ? 0 : sample_rows(g, d, b).nk;
+  __syncthreads();
+  if (tid == 0) {
+    cu[0] = 0;
+    for (int b = 0; b < g.batch; ++b) cu[b + 1] += cu[b];
+  }
+  __syncthreads();
+  const int krows = cu[g.batch];
+  for (int b = tid; b <= g.batch; b += 256) kw.cu_krows[b] = cu[b];
+  const int n = g.mask_heads * krows;
+  // compact exclusive offsets over flat = hm * krows + krow
+  int carry_p = 0, carry_f = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int f = base + tid;
+    int vp = 0, vf = 0;
+    if (f < n) {
+      const int hm = f / krows, kr = f - hm * krows;
+      const int b = sample_of_row(cu, g.batch, kr);
+      const int64_t src = ((int64_t)hm * g.batch + b) * g.nk_max + (kr - cu[b]);
+      vp = kw.pcnt[src];
+      vf = kw.fcnt[src];
+    }
+    const int ip = wave_incl_scan(vp, lane);
+    const int jf = wave_incl_scan(vf, lane);
+    if (lane == 63) {
+      s_wp[wv] = ip;
+      s_wf[wv] = jf;
+    }
+    __syncthreads();
+    int pre_p = 0, pre_f = 0, tot_p = 0, tot_f = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      if (x < wv) {
+        pre_p += s_wp[x];
+        pre_f += s_wf[x];
+      }
+      tot_p += s_wp[x];
+      tot_f += s_wf[x];
+    }
+    if (f < n) {
+      kw.p_off[f] = carry_p + pre_p + ip - vp;
+      kw.f_off[f] = carry_f + pre_f + jf - vf;
+    }
+    carry_p += tot_p;
+    carry_f += tot_f;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    kw.p_off[n] = carry_p;
+    kw.f_off[n] = carry_f;
+    kw.info[0] = krows;
+    kw.info[1] = carry_p;
+    kw.info[2] = carry_f;
+    kw.info[3] = 0;
+    const int32_t vals[4] = {d.header[0], krows, carry_p, carry_f};
+    for (int i = 0; i < 4; ++i) {
+      d.header[3 + i] = vals[i];
+      __hip_atomic_store(&host_slot[3 + i], vals[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    __hip_atomic_store(&host_slot[kHeaderSeq2], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
+namespace {
+
+// Lanes L and L ^ J of a wavefront swap one dword: DPP quad permutes for
+// J = 1, 2, a swizzle within 32 lanes for J = 4, 8, 16, a lane permute
+// across the halves for J = 32.
+template <int J>
+__device__ inline uint32_t xor_lane(uint32_t v) {
+  if constexpr (J == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (J == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (J < 32) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (J << 10));
+  else return (uint32_t)__shfl_xor((int)v, 32);
+}
+
+// One butterfly stage of a 64 x 64 bit transpose: between lanes L and L ^ J
+// swap the bits b with (b & J) != 0 of the lower lane and (b & J) == 0 of
+// the upper one (M: the bits with (b & J) == 0 of a dword).
+template <int J, uint32_t M>
+__device__ inline void butterfly(uint32_t& lo, uint32_t& hi, int lane) {
+  const uint32_t plo = xor_lane<J>(lo), phi = xor_lane<J>(hi);
+  if ((lane & J) == 0) {
+    lo = (lo & M) | ((plo & M) << J);
+    hi = (hi & M) | ((phi & M) << J);
+  } else {
+    lo = (lo & ~M) | ((plo & ~M) >> J);
+    hi = (hi & ~M) | ((phi & ~M) >> J);
+  }
+}
+
+// Transposes the 64 x 64 bit matrix whose row c is lane c's (lo, hi): on
+// return lane r holds column r, bit c = old bit r of lane c (recursive
+// block transpose: swap the off-diagonal halves, then recurse in place).
+__device__ inline void transpose_bits64(uint32_t& lo, uint32_t& hi, int lane) {
+  const bool top = lane < 32;
+  const uint32_t got = xor_lane<32>(top ? hi : lo);
+  if (top) hi = got; else lo = got;
+  butterfly<16, 0x0000FFFFu>(lo, hi, lane);
+  butterfly<8, 0x00FF00FFu>(lo, hi, lane);
+  butterfly<4, 0x0F0F0F0Fu>(lo, hi, lane);
+  butterfly<2, 0x33333333u>(lo, hi, lane);
+  butterfly<1, 0x55555555u>(lo, hi, lane);
+}
+
+}  // namespace
+
+// §4.7 K2Q materialization, one workgroup of 256 threads per (mask head, K
+// plan row).  The Q tiles of the K row's sample are read from the bitsets in
+// ascending order, ranked with one ballot per wavefront and written to the
+// partial and full lists.  The K-major predicate of a partial pair is the
+// transpose of the same pair's Q2K payload, already in the plan: the thread
+// that found pair (i, j) also locates it in row i's Q2K list (row offset plus
+// the partial tiles of the row before j, counted in the bitsets) and keeps
+// the list and that position in LDS (lds_list = 1: the longest sample's Q
+// tiles fit; otherwise both are read back or recounted).  Then the
+// wavefronts take the pairs in turn: a lane per Q row loads its row's
+// T_KV-bit word(s), each 64-row half is transposed across the wavefront and
+// lane r writes K row r's T_Q/32 words with one store.
+__global__ __launch_bounds__(256) void plan_k2q_materialize_kernel(
+    PlanGeo g, PlanDev d, PlanWork w, K2QWork kw, K2QDev kd, int krows_total, int lds_list) {
+  extern __shared__ int qlds[];   // [rps_max] partial Q tiles, then [rps_max] Q2K positions
+  __shared__ int s_wp[4], s_wf[4];
+  __shared__ int s_cu[1025];
+  if (krows_total < 0) {   // launched before the header was read back
+    if (d.header[7] != 0) return;
+    krows_total = kw.info[0];
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int item = blockIdx.x;
+  const int n = g.mask_heads * krows_total;
+  if (item == 0) {   // also when there are no K rows at all
+    for (int x = tid; x <= g.batch; x += 256) kd.cu_krows[x] = kw.cu_krows[x];
+    if (tid == 0) {
+      kd.p_off[n] = kw.p_off[n];
+      kd.f_off[n] = kw.f_off[n];
+    }
+  }
+  if (item >= n) return;
+  const int* cu = kw.cu_krows;
+  if (g.batch < 1025) {
+    for (int b = tid; b <= g.batch; b += 256) s_cu[b] = kw.cu_krows[b];
+    __syncthreads();
+    cu = s_cu;
+  }
+  const int hm = item / krows_total, kr = item - hm * krows_total;
+  const int b = sample_of_row(cu, g.batch, kr);
+  const int j = kr - cu[b];
+  const SampleRows sr = sample_rows(g, d, b);
+  const int p_begin = kw.p_off[item], f_begin = kw.f_off[item];
+  const int rows_total = d.header[0];
+  if (tid == 0) {
+    kd.p_off[item] = p_begin;
+    kd.f_off[item] = f_begin;
+  }
+  const int rps_max = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+  int* qlist = qlds;
+  int* qpos = qlds + rps_max;
+  const int jw = j >> 5;
+  const uint32_t jbit = 1u << (j & 31);
+  // position of pair (i, j) in Q row i's partial list
+  auto q2k_pos = [&](int i, uint32_t part_j) -> int {
+    const int64_t rs = ((int64_t)hm * g.upper_rows + sr.row_begin + i) * g.words_k;
+    int below = __popc(part_j & (jbit - 1u));
+    for (int x = 0; x < jw; ++x) below += __popc(w.vis_bits[rs + x] & ~w.full_bits[rs + x]);
+    return d.p_off[(int64_t)hm * rows_total + sr.row_begin + i] + below;
+  };
+
+  // lists, ascending Q tile
+  const uint64_t below = lanes_below(lane);
+  int base_p = 0, base_f = 0;
+  for (int i0 = 0; i0 < sr.nrows; i0 += 256) {
+    const int i = i0 + tid;
+    bool isp = false, isf = false;
+    uint32_t part = 0u;
+    if (i < sr.nrows) {
+      const int64_t src = ((int64_t)hm * g.upper_rows + sr.row_begin + i) * g.words_k + jw;
+      const uint32_t vis = w.vis_bits[src], full = w.full_bits[src];
+      part = vis & ~full;
+      isf = (full & jbit) != 0u;
+      isp = (part & jbit) != 0u;
+    }
+    const uint64_t bp = __ballot(isp), bf = __ballot(isf);
+    if (lane == 0) {
+      s_wp[wv] = __popcll(bp);
+      s_wf[wv] = __popcll(bf);
+    }
+    __syncthreads();
+    int pre_p = base_p, pre_f = base_f;
+    for (int x = 0; x < wv; ++x) {
+      pre_p += s_wp[x];
+      pre_f += s_wf[x];
+    }
+    if (isp) {
+      const int rk = pre_p + __popcll(bp & below);
+      kd.p_idx[p_begin + rk] = i;
+      if (lds_list) {
+        qlist[rk] = i;
+        qpos[rk] = q2k_pos(i, part);
+      }
+    }
+    if (isf) kd.f_idx[f_begin + pre_f + __popcll(bf & below)] = i;
+    for (int x = 0; x < 4; ++x) {
+      base_p += s_wp[x];
+      base_f += s_wf[x];
+    }
+    __syncthreads();
+  }
+  const int np = base_p;
+
+  // payload, K-major: [pair][T_KV][T_Q/32]; wavefront wv takes pairs wv, wv + 4, ...
+  const int wt = g.tile_k >> 5;     // words of a Q2K row (1 or 2)
+  const int wq = g.tile_q >> 5;     // words of a K2Q row
+  const int halves = (g.tile_q + 63) >> 6;
+  auto pos_of = [&](int x) -> int {
+    if (lds_list) return qpos[x];
+    const int i = kd.p_idx[p_begin + x];   // written above by this workgroup
+    const int64_t src = ((int64_t)hm * g.upper_rows + sr.row_begin + i) * g.words_k + jw;
+    return q2k_pos(i, w.vis_bits[src] & ~w.full_bits[src]);
+  };
+  for (int x = wv; x < np; x += 4) {
+    const int64_t pos = pos_of(x);
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      lo[h] = hi[h] = 0u;
+      const int c = 64 * h + lane;   // Q row of the tile
+      if (h < halves && c < g.tile_q) {
+        const uint32_t* src = d.p_masks + (pos * g.tile_q + c) * wt;
+        lo[h] = src[0];
+        if (wt == 2) hi[h] = src[1];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (h < halves) transpose_bits64(lo[h], hi[h], lane);
+    if (lane < g.tile_k) {
+      uint32_t* dst = kd.p_masks + ((int64_t)(p_begin + x) * g.tile_k + lane) * wq;
+      if (wq == 4) *reinterpret_cast<uint4*>(dst) = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+      else if (wq == 2) *reinterpret_cast<uint2*>(dst) = make_uint2(lo[0], hi[0]);
+      else dst[0] = lo[0];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 
 static inline int rows_per_lane(int tile_q) { return tile_q <= 64 ? 1 : tile_q / 64; }
@@ -1314,6 +1660,30 @@ hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const 
   const unsigned grid = (unsigned)(1 + (items + per_wg - 1) / per_wg);
   hipLaunchKernelGGL(plan_finish_kernel, dim3(grid), dim3(1024), lds, s, g, mask_func, d, w,
                      rows_total, stage, w.chunk_cnt ? 0 : 1, rows_in_lds);
+  return hipGetLastError();
+}
+
+
+hipError_t launch_plan_k2q_count(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                 const K2QWork& kw, int32_t* arrive, int32_t* host_slot,
+                                 int32_t seq, hipStream_t s) {
+  const int64_t items = (int64_t)g.mask_heads * g.batch * g.words_k;
+  const dim3 grid((unsigned)(items > 0 ? (items + 3) / 4 : 1)), block(256);
+  hipLaunchKernelGGL(plan_k2q_count_kernel, grid, block, 0, s, g, d, w, kw, arrive, host_slot,
+                     seq);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_k2q_materialize(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                       const K2QWork& kw, const K2QDev& kd, int32_t krows_total,
+                                       hipStream_t s) {
+  const int64_t upper = (int64_t)g.mask_heads * g.batch * g.nk_max;
+  const int64_t items = krows_total >= 0 ? (int64_t)g.mask_heads * krows_total : upper;
+  const int64_t rps_max = (g.seqlen_q + (int64_t)g.tile_q - 1) / g.tile_q;   // longest sample
+  const int lds_list = rps_max <= 4096 ? 1 : 0;
+  const size_t lds = lds_list ? (size_t)(rps_max > 0 ? rps_max : 1) * 8 : 0;
+  hipLaunchKernelGGL(plan_k2q_materialize_kernel, dim3((unsigned)(items > 0 ? items : 1)),
+                     dim3(256), lds, s, g, d, w, kw, kd, krows_total, lds_list);
   return hipGetLastError();
 }
 

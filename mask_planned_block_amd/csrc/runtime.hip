@@ -34,12 +34,51 @@
 
 using namespace mpb;
 
+// HIP events recorded on the build stream around each planner launch when
+// the build asks for stage times: stage k between ev[2k] and ev[2k+1].
+struct StageEvents {
+  static constexpr int kStages = 6;   // geometry, classify, schedule, materialize, K2Q x2
+  hipEvent_t ev[2 * kStages] = {};
+  bool used[kStages] = {};
+  int last = -1;                      // stage launched last
+  bool on = false;
+  hipError_t create() {
+    on = true;
+    for (hipEvent_t& e : ev) {
+      const hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+  }
+  void destroy() {
+    for (hipEvent_t& e : ev)
+      if (e) {
+        hipEventDestroy(e);
+        e = nullptr;
+      }
+    on = false;
+  }
+  template <class F>
+  hipError_t timed(int stage, hipStream_t s, F&& launch) {
+    hipError_t r = on ? hipEventRecord(ev[2 * stage], s) : hipSuccess;
+    if (r == hipSuccess) r = launch();
+    if (r == hipSuccess && on) {
+      r = hipEventRecord(ev[2 * stage + 1], s);
+      used[stage] = true;
+      last = stage;
+    }
+    return r;
+  }
+};
+
 struct mpb_plan {
   int device;
   mpb_problem prob;        // binding, with the resolved tile
   mpb_signature sig;
   PlanGeo geo;
   PlanDev dev;
+  K2QDev kdev;             // backward view (has_k2q)
+  bool has_k2q;
   int32_t rows_total;
   int32_t num_tasks;
   int64_t header[8];
@@ -48,6 +87,8 @@ struct mpb_plan {
   int blk_chunk;           // where the block sits in the device's plan heap
   size_t blk_off;
   hipStream_t stream;
+  StageEvents tev;         // build stage events (time_stages)
+  bool fused_finish;       // in-place build: schedule and materialize in one launch
 };
 
 namespace {
@@ -264,8 +305,9 @@ hipError_t arena_acquire(Arena& a, size_t bytes, hipStream_t stream) {
 // (every few hundred microseconds) the stream is queried: if all its work has
 // completed and the sequence number is still not there, the header was never
 // written.
-hipError_t wait_header(ThreadSlot* slot, hipStream_t stream, uint32_t seq, bool* published) {
-  volatile int32_t* sq = slot->pinned + kHeaderSeq;
+hipError_t wait_header(ThreadSlot* slot, hipStream_t stream, uint32_t seq, bool* published,
+                       int seq_index = kHeaderSeq) {
+  volatile int32_t* sq = slot->pinned + seq_index;
   *published = false;
   for (uint32_t spin = 1;; ++spin) {
     if ((uint32_t)*sq == seq) break;
@@ -307,10 +349,15 @@ T* at(void* base, size_t off) {
 // header is known).
 struct BlockLayout {
   size_t header, seqdesc, cu_rows, cu_q, cu_k, work_desc, sec, rec, p_off, f_off, p_idx, f_idx,
-      masks, bytes;
+      masks, k_cu, k_p_off, k_f_off, k_p_idx, k_f_idx, k_masks, bytes;
+};
+// Counts of the backward K2Q view (all zero: none).
+struct K2QCounts {
+  int64_t krows = 0, pnnz = 0, fnnz = 0;
+  bool on = false;
 };
 BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int64_t pnnz,
-                         int64_t fnnz) {
+                         int64_t fnnz, const K2QCounts& kc = K2QCounts()) {
   const int64_t n_off = p.mask_heads * rows + 1;
   const int64_t tasks = rows * p.heads_q;
   const bool thd = p.layout == MPB_LAYOUT_THD;
@@ -329,8 +376,31 @@ BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int
   L.p_idx = c.take<int32_t>(pnnz);
   L.f_idx = c.take<int32_t>(fnnz);
   L.masks = c.take<uint32_t>(pnnz * tq * (tk / 32));
+  if (kc.on) {
+    const int64_t nk_off = p.mask_heads * kc.krows + 1;
+    L.k_cu = c.take<int32_t>(p.batch + 1);
+    L.k_p_off = c.take<int32_t>(nk_off);
+    L.k_f_off = c.take<int32_t>(nk_off);
+    L.k_p_idx = c.take<int32_t>(kc.pnnz);
+    L.k_f_idx = c.take<int32_t>(kc.fnnz);
+    L.k_masks = c.take<uint32_t>(kc.pnnz * tk * (tq / 32));
+  } else {
+    L.k_cu = L.k_p_off = L.k_f_off = L.k_p_idx = L.k_f_idx = L.k_masks = 0;
+  }
   L.bytes = c.off;
   return L;
+}
+K2QDev bind_k2q(void* block, const BlockLayout& L, bool on) {
+  K2QDev k;
+  std::memset(&k, 0, sizeof(k));
+  if (!on) return k;
+  k.cu_krows = at<int32_t>(block, L.k_cu);
+  k.p_off = at<int32_t>(block, L.k_p_off);
+  k.f_off = at<int32_t>(block, L.k_f_off);
+  k.p_idx = at<int32_t>(block, L.k_p_idx);
+  k.f_idx = at<int32_t>(block, L.k_f_idx);
+  k.p_masks = at<uint32_t>(block, L.k_masks);
+  return k;
 }
 PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
   PlanDev d;
@@ -455,8 +525,20 @@ const char* mpb_last_error_detail(void) { return g_detail.c_str(); }
 mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* stream,
                            mpb_plan** out) {
+  return mask_plan_build_ex(problem, nullptr, mask_func, cu_seqlens_q, cu_seqlens_k, stream, out);
+}
+
+mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_options* options,
+                              const int32_t* mask_func, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, void* stream, mpb_plan** out) {
   if (!out) return fail(MPB_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
+  const bool bwd = options && options->build_backward;
+  if (options && (options->build_backward != 0 && options->build_backward != 1))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "build_backward must be 0 or 1");
+  if (options && (options->time_stages != 0 && options->time_stages != 1))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "time_stages must be 0 or 1");
+  const bool time_stages = options && options->time_stages;
   int tq = 0, tk = 0;
   mpb_status st = validate_problem(problem, &tq, &tk);
   if (st != MPB_OK) return st;
@@ -533,6 +615,14 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   const size_t o_work_desc = cw.take<int32_t>(4 * tasks_upper);
   const size_t o_sec = cw.take<int32_t>(kNumQueues + 1);
   const size_t o_rec = cw.take<int32_t>(kTaskRecInts * tasks_upper);
+  // backward K2Q view: counts padded per sample, compact offsets, K rows
+  const int64_t kpad = bwd ? (int64_t)p.mask_heads * p.batch * nk_max : 0;
+  const size_t o_kpc = cw.take<int32_t>(kpad);
+  const size_t o_kfc = cw.take<int32_t>(kpad);
+  const size_t o_kcu = cw.take<int32_t>(bwd ? p.batch + 1 : 0);
+  const size_t o_kpo = cw.take<int32_t>(bwd ? kpad + 1 : 0);
+  const size_t o_kfo = cw.take<int32_t>(bwd ? kpad + 1 : 0);
+  const size_t o_kin = cw.take<int32_t>(4);
   Arena& arena = slot->arena[dev];
   if ((e = arena_acquire(arena, cw.off, s)) != hipSuccess)
     return device_status(e, "planner workspace");
@@ -563,10 +653,25 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   w.row_base = at<int32_t>(wb, o_base);
   w.chunk_cnt = cnt_in_lds ? nullptr : at<int32_t>(wb, o_cnt);
   w.nchunks = (int32_t)nchunks;
+  K2QWork kw;
+  kw.pcnt = at<int32_t>(wb, o_kpc);
+  kw.fcnt = at<int32_t>(wb, o_kfc);
+  kw.cu_krows = at<int32_t>(wb, o_kcu);
+  kw.p_off = at<int32_t>(wb, o_kpo);
+  kw.f_off = at<int32_t>(wb, o_kfo);
+  kw.info = at<int32_t>(wb, o_kin);
 
   const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
   const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
   const bool thd = p.layout == MPB_LAYOUT_THD;
+  StageEvents tev;
+  struct EventGuard {
+    StageEvents* t;
+    ~EventGuard() {
+      if (t) t->destroy();
+    }
+  } tev_guard{&tev};
+  if (time_stages && (e = tev.create()) != hipSuccess) return device_status(e, "stage events");
   uint32_t seq = ++slot->seq;
   if (seq == 0) seq = ++slot->seq;   // 0 is the slot's initial value
 
@@ -574,31 +679,58 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   // allocated now; every kernel writes the plan directly and the header is
   // read back only to report errors and the exact counts.
   const int64_t tiles_upper = items_upper * nk_max;
-  const BlockLayout L_up = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper);
+  K2QCounts kc_up;
+  kc_up.on = bwd;
+  if (bwd) {
+    kc_up.krows = (int64_t)p.batch * nk_max;
+    kc_up.pnnz = kc_up.fnnz = tiles_upper;
+  }
+  const BlockLayout L_up = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper, kc_up);
   const bool in_place = L_up.bytes <= kInPlaceBlockBytes && plan_finish_fits(g, cnt_in_lds, nchunks);
   void* block = nullptr;
   int blk_chunk = 0;
   size_t blk_off = 0, blk_bytes = 0;
   PlanDev d;
   std::memset(&d, 0, sizeof(d));
+  K2QDev kd;
+  std::memset(&kd, 0, sizeof(kd));
   if (in_place) {
     if ((e = heap->alloc(L_up.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
       return device_status(e, "plan allocation");
     blk_bytes = L_up.bytes;
     d = bind_block(block, L_up, thd);
-    if ((e = launch_plan_geometry(g, cq, ck, d, w, s)) != hipSuccess ||
-        (e = launch_plan_classify(g, mask_func, d, w, slot->arrive[dev], slot->pinned_dev,
-                                  (int32_t)seq, s)) != hipSuccess ||
-        (e = launch_plan_finish(g, mask_func, d, w, thd ? -1 : (int32_t)upper, s)) !=
-            hipSuccess) {
+    kd = bind_k2q(block, L_up, bwd);
+    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, d, w, s); })) !=
+            hipSuccess ||
+        (e = tev.timed(1, s, [&] {
+           return launch_plan_classify(g, mask_func, d, w, slot->arrive[dev], slot->pinned_dev,
+                                       (int32_t)seq, s);
+         })) != hipSuccess ||
+        (e = tev.timed(2, s, [&] {
+           return launch_plan_finish(g, mask_func, d, w, thd ? -1 : (int32_t)upper, s);
+         })) != hipSuccess ||
+        (bwd && ((e = tev.timed(4, s, [&] {
+                    return launch_plan_k2q_count(g, d, w, kw, slot->arrive[dev] + 16,
+                                                 slot->pinned_dev, (int32_t)seq, s);
+                  })) != hipSuccess ||
+                 (e = tev.timed(5, s, [&] {
+                    return launch_plan_k2q_materialize(g, d, w, kw, kd, -1, s);
+                  })) != hipSuccess))) {
       heap->release(blk_chunk, blk_off, blk_bytes, s);
       return device_status(e, "planner launch");
     }
   } else {
-    if ((e = launch_plan_geometry(g, cq, ck, sg, w, s)) != hipSuccess ||
-        (e = launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
-                                  (int32_t)seq, s)) != hipSuccess ||
-        (e = launch_plan_schedule(g, sg, w, s)) != hipSuccess)
+    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, sg, w, s); })) !=
+            hipSuccess ||
+        (e = tev.timed(1, s, [&] {
+           return launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
+                                       (int32_t)seq, s);
+         })) != hipSuccess ||
+        (e = tev.timed(2, s, [&] { return launch_plan_schedule(g, sg, w, s); })) != hipSuccess ||
+        (bwd && (e = tev.timed(4, s, [&] {
+                   return launch_plan_k2q_count(g, sg, w, kw, slot->arrive[dev] + 16,
+                                                slot->pinned_dev, (int32_t)seq, s);
+                 })) != hipSuccess))
       return device_status(e, "planner launch");
   }
   auto drop_block = [&]() {
@@ -614,8 +746,20 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
     drop_block();
     return fail(MPB_ERR_DEVICE, "the planner did not publish its header");
   }
+  if (bwd) {   // the K2Q count publishes slots 3..6 with its own sequence number
+    if ((e = wait_header(slot, s, seq, &published, kHeaderSeq2)) != hipSuccess) {
+      drop_block();
+      return device_status(e, "header read-back");
+    }
+    if (!published) {
+      drop_block();
+      return fail(MPB_ERR_DEVICE, "the K2Q count did not publish its header");
+    }
+  }
   int64_t header[8];
   for (int i = 0; i < 8; ++i) header[i] = ((volatile int32_t*)slot->pinned)[i];
+  if (!bwd)
+    for (int i = 3; i < 7; ++i) header[i] = 0;
   const uint32_t err = (uint32_t)header[7];
   if (err) {
     drop_block();
@@ -634,17 +778,35 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
     return fail(MPB_ERR_DEVICE, "inconsistent plan header");
   }
   const int64_t tasks = rows_total * p.heads_q;
+  K2QCounts kc;
+  kc.on = bwd;
+  if (bwd) {
+    kc.krows = header[4];
+    kc.pnnz = header[5];
+    kc.fnnz = header[6];
+    if (header[3] != rows_total || kc.krows < 0 || kc.krows > (int64_t)p.batch * nk_max ||
+        kc.pnnz != pnnz || kc.fnnz != fnnz) {
+      // the same block relation read K-major: its totals equal the Q2K ones
+      drop_block();
+      return fail(MPB_ERR_DEVICE, "inconsistent K2Q header");
+    }
+  }
 
   if (!in_place) {
     // Exact allocation: every retained array sized by the header, no
     // capacity padding (§4.5); one block per plan.
-    const BlockLayout L = block_layout(p, tq, tk, rows_total, pnnz, fnnz);
+    const BlockLayout L = block_layout(p, tq, tk, rows_total, pnnz, fnnz, kc);
     if ((e = heap->alloc(L.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
       return device_status(e, "plan allocation");
     blk_bytes = L.bytes;
     d = bind_block(block, L, thd);
-    if ((e = launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s)) !=
-        hipSuccess) {
+    kd = bind_k2q(block, L, bwd);
+    if ((e = tev.timed(3, s, [&] {
+           return launch_plan_materialize(g, mask_func, sg, d, w, (int32_t)rows_total, s);
+         })) != hipSuccess ||
+        (bwd && (e = tev.timed(5, s, [&] {
+                   return launch_plan_k2q_materialize(g, d, w, kw, kd, (int32_t)kc.krows, s);
+                 })) != hipSuccess)) {
       drop_block();
       return device_status(e, "materialize launch");
     }
@@ -662,6 +824,8 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   plan->sig = consumer_signature(p, tq, tk);
   plan->geo = g;
   plan->dev = d;
+  plan->kdev = kd;
+  plan->has_k2q = bwd;
   plan->rows_total = (int32_t)rows_total;
   plan->num_tasks = (int32_t)tasks;
   for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
@@ -670,6 +834,9 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
   plan->blk_chunk = blk_chunk;
   plan->blk_off = blk_off;
   plan->stream = s;
+  plan->tev = tev;
+  plan->fused_finish = in_place;
+  tev_guard.t = nullptr;   // the plan owns the events now
   *out = plan;
   return ok();
 }
@@ -681,6 +848,7 @@ mpb_status mask_plan_destroy(mpb_plan* plan) {
   if (cur != plan->device) hipSetDevice(plan->device);
   if (PlanHeap* heap = plan_heap(plan->device))
     heap->release(plan->blk_chunk, plan->blk_off, plan->bytes, plan->stream);
+  plan->tev.destroy();
   if (cur != plan->device) hipSetDevice(cur);
   delete plan;
   return ok();
@@ -729,6 +897,58 @@ mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seq
   }
   if (cur != plan->device) hipSetDevice(cur);
   if (e != hipSuccess) return device_status(e, "plan export");
+  return ok();
+}
+
+mpb_status mask_plan_export_k2q(const mpb_plan* plan, int32_t* cu_krows, int32_t* p_off,
+                                int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
+                                int32_t* f_idx) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!plan->has_k2q) return fail(MPB_ERR_INVALID_ARGUMENT, "the plan has no K2Q view");
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipError_t e = hipStreamSynchronize(plan->stream);
+  const int64_t B = plan->prob.batch;
+  const int64_t n_off = (int64_t)plan->prob.mask_heads * plan->header[4] + 1;
+  const int64_t words = plan->header[5] * plan->prob.tile_k * (plan->prob.tile_q / 32);
+  struct Copy { void* dst; const void* src; size_t bytes; } copies[] = {
+      {cu_krows, plan->kdev.cu_krows, (size_t)(B + 1) * 4},
+      {p_off, plan->kdev.p_off, (size_t)n_off * 4},
+      {p_idx, plan->kdev.p_idx, (size_t)plan->header[5] * 4},
+      {p_masks, plan->kdev.p_masks, (size_t)words * 4},
+      {f_off, plan->kdev.f_off, (size_t)n_off * 4},
+      {f_idx, plan->kdev.f_idx, (size_t)plan->header[6] * 4},
+  };
+  for (const Copy& c : copies) {
+    if (e != hipSuccess) break;
+    if (c.dst && c.bytes) e = hipMemcpy(c.dst, c.src, c.bytes, hipMemcpyDeviceToHost);
+  }
+  if (cur != plan->device) hipSetDevice(cur);
+  if (e != hipSuccess) return device_status(e, "K2Q export");
+  return ok();
+}
+
+mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us) {
+  if (!plan || !us) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or us is NULL");
+  const StageEvents& t = plan->tev;
+  if (!t.on || t.last < 0)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "the plan was built without time_stages");
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipError_t e = hipEventSynchronize(t.ev[2 * t.last + 1]);
+  for (int k = 0; k < StageEvents::kStages && e == hipSuccess; ++k) {
+    us[k] = -1.0f;
+    float ms = 0.0f;
+    if (t.used[k] && (e = hipEventElapsedTime(&ms, t.ev[2 * k], t.ev[2 * k + 1])) == hipSuccess)
+      us[k] = ms * 1e3f;
+  }
+  float span = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&span, t.ev[0], t.ev[2 * t.last + 1]);
+  if (e == hipSuccess) us[StageEvents::kStages] = span * 1e3f;
+  if (cur != plan->device) hipSetDevice(cur);
+  if (e != hipSuccess) return device_status(e, "stage times");
   return ok();
 }
 

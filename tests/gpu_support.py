@@ -25,9 +25,10 @@ def problem(w, tile_q=0, tile_k=0):
                             tile_q, tile_k)
 
 
-def build_plan(w, d, tile_q=0, tile_k=0, stream=None):
+def build_plan(w, d, tile_q=0, tile_k=0, stream=None, build_backward=False, time_stages=False):
     return mpb.mask_plan_build(problem(w, tile_q, tile_k), d["mask_func"], d["cu_q"], d["cu_k"],
-                               stream=stream)
+                               stream=stream, build_backward=build_backward,
+                               time_stages=time_stages)
 
 
 def run_attention(w, d, plan, **kw):
@@ -43,11 +44,13 @@ def flat_o(w, o):
     return o.float().reshape(w.total_q, w.heads_q, w.head_dim).cpu().numpy().astype(np.float64)
 
 
-def compare_plan(gp, op):
-    """Bit-exact comparison of a GPU plan export with the oracle's plan."""
+def compare_plan(gp, op, with_k2q=False):
+    """Bit-exact comparison of a GPU plan export with the oracle's plan
+    (header slots 3..6 are zero unless the plan holds the K2Q view)."""
     assert gp["header"][7] == 0
     assert list(gp["header"][:3]) == [int(x) for x in op.header[:3]], (gp["header"], op.header)
-    assert all(int(x) == 0 for x in gp["header"][3:7])
+    if not with_k2q:
+        assert all(int(x) == 0 for x in gp["header"][3:7])
     for key in ("cu_rows", "seqdesc", "p_off", "f_off", "p_idx", "f_idx"):
         a, b = np.asarray(gp[key]), np.asarray(getattr(op, key))
         assert a.shape == b.shape and np.array_equal(a, b), key
@@ -171,3 +174,13 @@ def sample_rows(w, n_random=1500, seed=0, tile_q=128):
                 for h in heads:
                     rows.add((qo + q, h))
     return np.asarray(sorted(rows), dtype=np.int64)
+
+
+def compare_k2q(gk, ok):
+    """Bit-exact comparison of a GPU K2Q export with the oracle's K2Q view."""
+    assert list(gk["header"][3:7]) == [int(x) for x in ok.header], (gk["header"], ok.header)
+    for key in ("cu_krows", "p_off", "f_off", "p_idx", "f_idx"):
+        a, b = np.asarray(gk[key]), np.asarray(getattr(ok, key))
+        assert a.shape == b.shape and np.array_equal(a, b), key
+    assert gk["p_masks"].shape == ok.p_masks.shape
+    assert np.array_equal(gk["p_masks"], ok.p_masks), "K2Q payload words differ"

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     fns = declared_functions()
     for name in ("mask_plan_build", "flex_attn_fwd", "mask_plan_destroy", "mask_plan_info",
                  "mask_plan_export", "flex_attn_fwd_workspace_size", "mpb_status_string",
-                 "mpb_last_error_detail"):
+                 "mpb_last_error_detail", "mask_plan_build_ex", "mask_plan_export_k2q",
+                 "mask_plan_stage_times"):
         assert name in fns
 
 
@@ -117,3 +118,31 @@ def test_fwd_refuses_null_plan_and_workspace_size(lib):
     assert lib.mpb_status_string(5) == b"MPB_ERR_SIGNATURE_MISMATCH"
     lib.mask_plan_destroy.restype = ctypes.c_int
     assert lib.mask_plan_destroy(None) == 0
+
+
+class BuildOptions(ctypes.Structure):
+    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32)]
+
+
+def test_build_options_and_k2q_export_refusals(lib):
+    lib.mask_plan_build_ex.restype = ctypes.c_int
+    lib.mask_plan_build_ex.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(BuildOptions)] + \
+        [ctypes.c_void_p] * 4 + [ctypes.POINTER(ctypes.c_void_p)]
+    out = ctypes.c_void_p(12345)
+    prob = _good()
+    for opt in (BuildOptions(2, 0), BuildOptions(0, -1)):
+        out = ctypes.c_void_p(12345)
+        st = lib.mask_plan_build_ex(ctypes.byref(prob), ctypes.byref(opt),
+                                    ctypes.c_void_p(1), None, None, None, ctypes.byref(out))
+        assert st == INVALID and out.value is None
+    # options are checked with the problem: a bad problem still names its own rule
+    bad = _good(head_dim=96)
+    st = lib.mask_plan_build_ex(ctypes.byref(bad), ctypes.byref(BuildOptions(1)),
+                                ctypes.c_void_p(1), None, None, None, ctypes.byref(out))
+    assert st == UNSUPPORTED and out.value is None
+    lib.mask_plan_export_k2q.restype = ctypes.c_int
+    lib.mask_plan_export_k2q.argtypes = [ctypes.c_void_p] * 7
+    assert lib.mask_plan_export_k2q(None, None, None, None, None, None, None) == INVALID
+    lib.mask_plan_stage_times.restype = ctypes.c_int
+    lib.mask_plan_stage_times.argtypes = [ctypes.c_void_p] * 2
+    assert lib.mask_plan_stage_times(None, None) == INVALID
