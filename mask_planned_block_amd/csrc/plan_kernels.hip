@@ -30,6 +30,7 @@
 // which is the union [0,F0) U [F1,F2) U ... of §2; columns >= F(nfunc-1)
 // (hence >= k_len) see an odd count and are masked.
 #include <algorithm>
+#include <climits>
 
 #include "mpb_internal.h"
 #include "../../include/mpb.h"
@@ -40,7 +41,14 @@ namespace {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-__device__ inline int sample_of_row(const int32_t* cu_rows, int batch, int row) {
+// LDS-typed pointers: code that chooses between an LDS copy and the HBM
+// original at run time takes one branch per type, so neither becomes a flat
+// access.
+typedef __attribute__((address_space(3))) int32_t* lds_ptr;
+typedef __attribute__((address_space(3))) const int32_t* lds_cptr;
+
+template <class P>
+__device__ inline int sample_of_row(P cu_rows, int batch, int row) {
   // Largest b with cu_rows[b] <= row; empty samples share their prefix value
   // with the next sample and are skipped by taking the largest such b.
   int lo = 0, hi = batch - 1;
@@ -545,7 +553,8 @@ __device__ inline SampleGeo sample_geo(const PlanGeo& g, const PlanDev& d, const
     r.q_len = g.seqlen_q;
     r.k_len = g.seqlen_k;
   } else {
-    r.b = sample_of_row(s_cu ? s_cu : d.cu_rows, g.batch, row);
+    r.b = s_cu ? sample_of_row((lds_cptr)s_cu, g.batch, row)
+               : sample_of_row(d.cu_rows, g.batch, row);
     const int32_t* sd = d.seqdesc + 8 * r.b;
     r.q_off = sd[0];
     r.k_off = sd[1];
@@ -664,16 +673,25 @@ __device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int*
 }  // namespace
 
 // The schedule, run by one workgroup of 1024 threads; `dyn` is its dynamic
-// LDS.
-__device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                      int cnt_in_lds, int rows_in_lds, int* dyn) {
-  __shared__ int s_secoff[kNumQueues + 1];
-  __shared__ int s_run[kNumQueues];
-  __shared__ int s_tot[kNumQueues];
-  __shared__ int s_vec[16][kNumQueues];
-  __shared__ int s_wave[33];
-  __shared__ int s_carry;
-  __shared__ int s_cu[1025];
+// LDS.  CNT_LDS: the count matrix is in LDS; ROWS: 0 row data read from the
+// workspace, 1 in LDS, 2 their first positions in LDS too.  (Compile-time, so
+// that every access is ds_* or global_*: a pointer that may point to either
+// memory becomes a flat access.)
+struct SchedShared {
+  int secoff[kNumQueues + 1];
+  int run[kNumQueues];
+  int tot[kNumQueues];
+  int vec[16][kNumQueues];
+  int wave[33];
+  int carry;
+  int cu[1025];
+};
+
+template <bool CNT_LDS, int ROWS>
+__device__ __attribute__((always_inline)) inline void schedule_block(
+    const PlanGeo& g, const PlanDev& d, const PlanWork& w, int* dyn, SchedShared& sh) {
+  constexpr bool cnt_in_lds = CNT_LDS;
+  constexpr int rows_in_lds = ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_up = g.mask_heads * g.upper_rows;
 
@@ -689,7 +707,7 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
   // header first, so that its load and the row loads are in flight together
   const int hdr_err = d.header[7];
   const int hdr_rows = d.header[0];
-  if (rows_in_lds) {
+  if constexpr (rows_in_lds != 0) {
     int* lp = lds_rows;
     int* lf = lp + n_up + 1;
     int* lt = lf + n_up + 1;
@@ -727,12 +745,12 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     }
     if (tid == 0) d.cu_rows[0] = 0;
   } else if (g.batch < 1025) {
-    for (int b = tid; b <= g.batch; b += 1024) s_cu[b] = d.cu_rows[b];
-    cu = s_cu;
+    for (int b = tid; b <= g.batch; b += 1024) sh.cu[b] = d.cu_rows[b];
+    cu = sh.cu;
   }
   if (tid < kNumQueues) {
-    s_run[tid] = 0;
-    s_tot[tid] = 0;
+    sh.run[tid] = 0;
+    sh.tot[tid] = 0;
   }
   for (int64_t x = tid; x < cnt_len; x += 1024) cnt[x] = 0;
   __syncthreads();
@@ -755,7 +773,7 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
       v = row_queue_count(g, sample_geo(g, d, cu, lane - hm * rows_total).b, hm, cost_of(lane), q);
     }
     const int t = wave_sum(v);
-    if (lane == 0) s_tot[q] = t;
+    if (lane == 0) sh.tot[q] = t;
   }
   for (int c = wv, k = 0; c < nc && !(one_chunk && wv > 0); c += 16, ++k) {
     const int i = c * 64 + lane;
@@ -780,7 +798,7 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     }
     if (live) {
       const int rank = __popcll(eq & below);
-      if (rows_in_lds) {
+      if constexpr (rows_in_lds != 0) {
 #pragma unroll
         for (int u = 0; u < kSchedLdsRows / 1024; ++u)
           if (u == k) lr[u] = rank;
@@ -794,7 +812,7 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
 #pragma unroll
     for (int s = 0; s < kNumQueues; ++s) {
       const int t = wave_sum(tot[s]);
-      if (lane == 0 && t) atomicAdd(&s_tot[s], t);
+      if (lane == 0 && t) atomicAdd(&sh.tot[s], t);
     }
   }
   __syncthreads();
@@ -806,13 +824,13 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     }
     __syncthreads();
   } else {
-    block_exclusive_scan_inplace(cnt, cnt_len, s_wave, &s_carry);
+    block_exclusive_scan_inplace(cnt, cnt_len, sh.wave, &sh.carry);
   }
   for (int c = wv, k = 0; c < nc; c += 16, ++k) {   // same row-to-thread map as above
     const int i = c * 64 + lane;
     if (i >= n) continue;
     int rank = 0;
-    if (rows_in_lds) {
+    if constexpr (rows_in_lds != 0) {
 #pragma unroll
       for (int u = 0; u < kSchedLdsRows / 1024; ++u)
         if (u == k) rank = lr[u];
@@ -822,9 +840,9 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     order[cnt[(int64_t)(g.nk_max - cost_of(i)) * nc + c] + rank] = i;
   }
   if (tid == 0) {
-    s_secoff[0] = 0;
-    for (int s = 0; s < kNumQueues; ++s) s_secoff[s + 1] = s_secoff[s] + s_tot[s];
-    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_secoff[s];
+    sh.secoff[0] = 0;
+    for (int s = 0; s < kNumQueues; ++s) sh.secoff[s + 1] = sh.secoff[s] + sh.tot[s];
+    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = sh.secoff[s];
   }
   __syncthreads();
 
@@ -861,27 +879,27 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
     for (int s = 0; s < kNumQueues; ++s) {
       const int incl = wave_incl_scan(v[s], lane);
       first_pos[s] = incl - v[s];
-      if (lane == 63) s_vec[wv][s] = incl;
+      if (lane == 63) sh.vec[wv][s] = incl;
     }
     __syncthreads();
     if (pos < n) {
 #pragma unroll
       for (int s = 0; s < kNumQueues; ++s) {
-        int pre = s_run[s];
-        for (int x = 0; x < wv; ++x) pre += s_vec[x][s];
+        int pre = sh.run[s];
+        for (int x = 0; x < wv; ++x) pre += sh.vec[x][s];
         rbase[(int64_t)i * kNumQueues + s] = pre + first_pos[s];
       }
     }
     __syncthreads();
     if (tid < kNumQueues)
-      for (int x = 0; x < 16; ++x) s_run[tid] += s_vec[x][tid];
+      for (int x = 0; x < 16; ++x) sh.run[tid] += sh.vec[x][tid];
     __syncthreads();
   }
 
   // 3. every task, one per thread
   int so[kNumQueues + 1];
 #pragma unroll
-  for (int s = 0; s <= kNumQueues; ++s) so[s] = s_secoff[s];
+  for (int s = 0; s <= kNumQueues; ++s) so[s] = sh.secoff[s];
   const int ntasks = rows_total * Hq;
   for (int t = tid; t < ntasks; t += 1024) {
     int i, h;
@@ -917,13 +935,74 @@ __device__ inline void schedule_block(const PlanGeo& g, const PlanDev& d, const 
   }
 }
 
+__device__ __attribute__((always_inline)) inline void schedule_any(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                    int cnt_in_lds, int rows_in_lds, int* dyn) {
+  __shared__ SchedShared sh;
+  if (cnt_in_lds) {
+    if (rows_in_lds == 2) schedule_block<true, 2>(g, d, w, dyn, sh);
+    else if (rows_in_lds == 1) schedule_block<true, 1>(g, d, w, dyn, sh);
+    else schedule_block<true, 0>(g, d, w, dyn, sh);
+  } else {
+    if (rows_in_lds == 2) schedule_block<false, 2>(g, d, w, dyn, sh);
+    else if (rows_in_lds == 1) schedule_block<false, 1>(g, d, w, dyn, sh);
+    else schedule_block<false, 0>(g, d, w, dyn, sh);
+  }
+}
+
 __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev d, PlanWork w,
                                                              int cnt_in_lds, int rows_in_lds) {
   extern __shared__ int dyn[];
-  schedule_block(g, d, w, cnt_in_lds, rows_in_lds, dyn);
+  schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn);
 }
 
 // ---------------------------------------------------------------- materialize
+
+// Payload words of one row for its np partial K tiles (ascending, in
+// `tiles`), written from pair p_begin on.  Word [r][c/32] of a pair starts
+// from the parity of the row's endpoints < c and flips at each endpoint
+// inside the word.  Words come in ascending column order, so every endpoint
+// is read once: `ptr` counts the endpoints below the current word and `nxt`
+// holds the next one (INT_MAX past the last), and a word with no endpoint
+// inside costs one compare.  STAGED: the endpoints were staged in LDS as
+// [nfunc][T_Q]; else read from HBM through `col`.  (One instance per source
+// keeps LDS reads ds_read: a pointer that may point to either memory would
+// become a flat load.)
+template <bool STAGED>
+__device__ __attribute__((always_inline)) inline void row_payload(
+    const PlanGeo& g, const int* tiles, int np, const int* ep, const int32_t* col, int rho,
+    bool valid, bool is_row, uint32_t* p_masks, int p_begin) {
+  auto E = [&](int f) -> int {
+    if (f >= g.nfunc) return INT_MAX;
+    if constexpr (STAGED) return ep[f * g.tile_q + rho];
+    else return col[(int64_t)f * g.total_q];
+  };
+  int ptr = 0;
+  int nxt = valid ? E(0) : INT_MAX;
+  auto word_at = [&](int c) -> uint32_t {
+    if (!valid) return 0u;
+    while (nxt < c) nxt = E(++ptr);
+    uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
+    while (nxt < c + 32) {
+      word ^= 0xFFFFFFFFu << (nxt - c);
+      nxt = E(++ptr);
+    }
+    return word;
+  };
+  for (int k = 0; k < np; ++k) {
+    const int c0 = tiles[k] * g.tile_k;
+    uint32_t* dst = p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
+    if (g.words_tile == 2) {
+      const uint32_t w0 = word_at(c0);
+      const uint32_t w1 = word_at(c0 + 32);
+      if (is_row) *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
+    } else {
+      for (int x = 0; x < g.words_tile; ++x) {
+        const uint32_t wd = word_at(c0 + 32 * x);
+        if (is_row) dst[x] = wd;
+      }
+    }
+  }
+}
 
 // One workgroup per (mask head, Q plan row), one thread per Q row of the
 // tile.
@@ -1037,37 +1116,10 @@ __global__ __launch_bounds__(256) void plan_materialize_kernel(PlanGeo g,
   if (np == 0) return;  // uniform; no payload
   __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads into LDS have landed
   __syncthreads();  // the partial tile list and the staged endpoints are complete
-  auto E = [&](int f) -> int {
-    return stage_ep ? ep[f * g.tile_q + rho] : col[(int64_t)f * g.total_q];
-  };
-  // Word of columns [c, c + 32): the parity of endpoints <= c, then a flip at
-  // each endpoint inside the word.
-  int ptr = 0;
-  auto word_at = [&](int c) -> uint32_t {
-    if (!valid) return 0u;
-    while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
-    uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
-    for (int f = ptr; f < g.nfunc; ++f) {
-      const int e = E(f);
-      if (e >= c + 32) break;
-      word ^= 0xFFFFFFFFu << (e - c);
-    }
-    return word;
-  };
-  for (int k = 0; k < np; ++k) {
-    const int c0 = tiles[k] * g.tile_k;
-    uint32_t* dst = d.p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
-    if (g.words_tile == 2) {
-      const uint32_t w0 = word_at(c0);
-      const uint32_t w1 = word_at(c0 + 32);
-      if (is_row) *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-    } else {
-      for (int x = 0; x < g.words_tile; ++x) {
-        const uint32_t wd = word_at(c0 + 32 * x);
-        if (is_row) dst[x] = wd;
-      }
-    }
-  }
+  if (stage_ep)
+    row_payload<true>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
+  else
+    row_payload<false>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
 }
 
 
@@ -1083,7 +1135,7 @@ __global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
                                                            int rows_in_lds) {
   extern __shared__ int dyn[];
   if (blockIdx.x == 0) {
-    schedule_block(g, d, w, cnt_in_lds, rows_in_lds, dyn);
+    schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn);
     return;
   }
   if (rows_total < 0) {   // Varlen: rows counted on the device; nothing for a failed build
@@ -1164,35 +1216,10 @@ __global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
   __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads into LDS have landed
   __syncthreads();  // every row's partial tile list and staged endpoints are complete
   if (!has_row || np == 0) return;
-  auto E = [&](int f) -> int {
-    return stage_ep ? ep[f * g.tile_q + rho] : col[(int64_t)f * g.total_q];
-  };
-  int ptr = 0;
-  auto word_at = [&](int c) -> uint32_t {
-    if (!valid) return 0u;
-    while (ptr < g.nfunc && E(ptr) <= c) ++ptr;
-    uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
-    for (int f = ptr; f < g.nfunc; ++f) {
-      const int e = E(f);
-      if (e >= c + 32) break;
-      word ^= 0xFFFFFFFFu << (e - c);
-    }
-    return word;
-  };
-  for (int k = 0; k < np; ++k) {
-    const int c0 = tiles[k] * g.tile_k;
-    uint32_t* dst = d.p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
-    if (g.words_tile == 2) {
-      const uint32_t w0 = word_at(c0);
-      const uint32_t w1 = word_at(c0 + 32);
-      if (is_row) *reinterpret_cast<uint2*>(dst) = make_uint2(w0, w1);
-    } else {
-      for (int x = 0; x < g.words_tile; ++x) {
-        const uint32_t wd = word_at(c0 + 32 * x);
-        if (is_row) dst[x] = wd;
-      }
-    }
-  }
+  if (stage_ep)
+    row_payload<true>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
+  else
+    row_payload<false>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
 }
 
 
@@ -1295,7 +1322,7 @@ __global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev 
   // K rows per sample: cu_krows (one thread per sample, then a serial pass
   // over the wavefront totals; B <= 1024 samples are kept in LDS)
   const int tid = threadIdx.x;
-  int* cu = g.batch < 1025 ? s_cu : kw.cu_krows;
+  auto offsets = [&](auto cu) {
   for (int b = tid; b < g.batch; b += 256) cu[b + 1] = failed ? 0 : sample_rows(g, d, b).nk;
   __syncthreads();
   if (tid == 0) {
@@ -1357,6 +1384,9 @@ __global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev 
     }
     __hip_atomic_store(&host_slot[kHeaderSeq2], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
   }
+  };
+  if (g.batch < 1025) offsets((lds_ptr)s_cu);
+  else offsets(kw.cu_krows);
 }
 
 namespace {
@@ -1435,15 +1465,17 @@ __global__ __launch_bounds__(256) void plan_k2q_materialize_kernel(
     }
   }
   if (item >= n) return;
-  const int* cu = kw.cu_krows;
-  if (g.batch < 1025) {
-    for (int b = tid; b <= g.batch; b += 256) s_cu[b] = kw.cu_krows[b];
-    __syncthreads();
-    cu = s_cu;
-  }
   const int hm = item / krows_total, kr = item - hm * krows_total;
-  const int b = sample_of_row(cu, g.batch, kr);
-  const int j = kr - cu[b];
+  int b, j;
+  if (g.batch < 1025) {
+    for (int x = tid; x <= g.batch; x += 256) s_cu[x] = kw.cu_krows[x];
+    __syncthreads();
+    b = sample_of_row((lds_cptr)s_cu, g.batch, kr);
+    j = kr - ((lds_cptr)s_cu)[b];
+  } else {
+    b = sample_of_row(kw.cu_krows, g.batch, kr);
+    j = kr - kw.cu_krows[b];
+  }
   const SampleRows sr = sample_rows(g, d, b);
   const int p_begin = kw.p_off[item], f_begin = kw.f_off[item];
   const int rows_total = d.header[0];
