@@ -56,6 +56,19 @@ def plan_stats(w, plan):
             "tasks": int(plan.info.num_tasks)}
 
 
+def plan_bytes(w, plan):
+    """Algorithmic bytes of the forward plan build: the endpoints read once;
+    the lists, payload (T_Q*T_KV/8 bytes per partial tile), offsets and
+    16 bytes per task written once."""
+    h = plan.info.header
+    p = plan.problem
+    rows, pn, fn = int(h[0]), int(h[1]), int(h[2])
+    read = 4 * w.mask_heads * w.nfunc * w.total_q
+    write = 4 * (pn + fn) + pn * p.tile_q * p.tile_k // 8 + 8 * (w.mask_heads * rows + 1) + \
+        16 * int(plan.info.num_tasks)
+    return read + write
+
+
 def k2q_bytes(w, plan):
     """Algorithmic bytes of the K2Q view's materialization: the endpoints
     read once, then the lists, offsets, K-row prefixes and the K-major
@@ -325,8 +338,10 @@ def main():
         return out, p3
 
     stage_runs, p3 = build_runs(False, True)
+    pb = plan_bytes(w, p3)
     p3.close()
     plan_stages = _median_stages(stage_runs)
+    gpu_us = sum(v for k, v in plan_stages.items() if k != "span" and v > 0)
     # the backward K2Q view added to the same build
     tbk, p3 = build_runs(True, False)
     p3.close()
@@ -422,7 +437,9 @@ def main():
             "us_in_step_median": round(fwd_in_step_med_us, 2),
             "dense_all_visible": dense_ref,
         },
-        "plan": {"build_us_host": round(plan_us, 1), "stages_us": plan_stages, **stats},
+        "plan": {"build_us_host": round(plan_us, 1), "stages_us": plan_stages,
+                 "algorithmic_bytes": pb, "gbs_over_stages": round(pb / (gpu_us * 1e-6) / 1e9, 1),
+                 **stats},
         "plan_k2q": plan_k2q,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},

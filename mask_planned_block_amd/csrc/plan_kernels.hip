@@ -1333,43 +1333,56 @@ __global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev 
   const int krows = cu[g.batch];
   for (int b = tid; b <= g.batch; b += 256) kw.cu_krows[b] = cu[b];
   const int n = g.mask_heads * krows;
-  // compact exclusive offsets over flat = hm * krows + krow
-  int carry_p = 0, carry_f = 0;
-  for (int base = 0; base < n; base += 256) {
-    const int f = base + tid;
-    int vp = 0, vf = 0;
-    if (f < n) {
-      const int hm = f / krows, kr = f - hm * krows;
-      const int b = sample_of_row(cu, g.batch, kr);
-      const int64_t src = ((int64_t)hm * g.batch + b) * g.nk_max + (kr - cu[b]);
-      vp = kw.pcnt[src];
-      vf = kw.fcnt[src];
-    }
-    const int ip = wave_incl_scan(vp, lane);
-    const int jf = wave_incl_scan(vf, lane);
-    if (lane == 63) {
-      s_wp[wv] = ip;
-      s_wf[wv] = jf;
-    }
-    __syncthreads();
-    int pre_p = 0, pre_f = 0, tot_p = 0, tot_f = 0;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      if (x < wv) {
-        pre_p += s_wp[x];
-        pre_f += s_wf[x];
+  // compact exclusive offsets over flat = hm * krows + krow: thread t scans
+  // the contiguous segment [t*per, (t+1)*per) (its loads all in flight, the
+  // sample advanced along the segment instead of searched per element),
+  // then the 256 segment totals are scanned
+  const int per = (n + 255) / 256;
+  const int f0 = min(n, tid * per), f1 = min(n, f0 + per);
+  auto walk = [&](auto&& visit) {
+    if (f0 >= f1) return;
+    int hm = f0 / krows, kr = f0 - hm * krows;
+    int b = sample_of_row(cu, g.batch, kr);
+    for (int f = f0; f < f1; ++f) {
+      while (kr >= cu[b + 1]) ++b;
+      visit(f, ((int64_t)hm * g.batch + b) * g.nk_max + (kr - cu[b]));
+      if (++kr == krows) {
+        kr = 0;
+        b = 0;
+        ++hm;
       }
-      tot_p += s_wp[x];
-      tot_f += s_wf[x];
     }
-    if (f < n) {
-      kw.p_off[f] = carry_p + pre_p + ip - vp;
-      kw.f_off[f] = carry_f + pre_f + jf - vf;
-    }
-    carry_p += tot_p;
-    carry_f += tot_f;
-    __syncthreads();
+  };
+  int sp = 0, sf = 0;
+  walk([&](int, int64_t src) {
+    sp += kw.pcnt[src];
+    sf += kw.fcnt[src];
+  });
+  const int ip = wave_incl_scan(sp, lane);
+  const int jf = wave_incl_scan(sf, lane);
+  if (lane == 63) {
+    s_wp[wv] = ip;
+    s_wf[wv] = jf;
   }
+  __syncthreads();
+  int carry_p = ip - sp, carry_f = jf - sf, tot_p = 0, tot_f = 0;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    if (x < wv) {
+      carry_p += s_wp[x];
+      carry_f += s_wf[x];
+    }
+    tot_p += s_wp[x];
+    tot_f += s_wf[x];
+  }
+  walk([&](int f, int64_t src) {
+    kw.p_off[f] = carry_p;
+    kw.f_off[f] = carry_f;
+    carry_p += kw.pcnt[src];
+    carry_f += kw.fcnt[src];
+  });
+  carry_p = tot_p;
+  carry_f = tot_f;
   if (tid == 0) {
     kw.p_off[n] = carry_p;
     kw.f_off[n] = carry_f;
