@@ -75,6 +75,10 @@ def _load():
                                       ctypes.c_double, ctypes.c_int, vp, ctypes.c_int,
                                       ctypes.c_int64, vp, vp, vp, ctypes.c_int]
         lib.orc_attention.restype = None
+        lib.orc_attention_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_double,
+                                          ctypes.c_int, ctypes.c_double, ctypes.c_int, vp,
+                                          ctypes.c_int, vp, vp, vp, ctypes.c_int]
+        lib.orc_attention_bwd.restype = None
         _lib = lib
     return _lib
 
@@ -241,3 +245,28 @@ def attention(w, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = No
                       int(slopes is not None), _ptr(slopes), int(bool(w.alibi_before_softcap)),
                       n, _ptr(rp), _ptr(o), _ptr(lse), nthreads or default_threads())
     return o, lse
+
+
+def attention_bwd(w, dout: np.ndarray, nthreads: Optional[int] = None):
+    """fp64 gradients (dQ, dK, dV) of the workload's attention output for the
+    incoming gradient dout [total_q, Hq, d] (the chain rule of FlexAttention
+    Eq. 1 with the score_mod's derivative; see orc_attention_bwd).  Returns
+    dQ [total_q, Hq, d], dK and dV [total_k, Hk, d]."""
+    lib = _load()
+    p = _problem(w)
+    mf, cq, ck = _i32(w.mask_func), _i32(w.cu_seqlens_q), _i32(w.cu_seqlens_k)
+    q = np.ascontiguousarray(w.q, dtype=np.float32)
+    k = np.ascontiguousarray(w.k, dtype=np.float32)
+    v = np.ascontiguousarray(w.v, dtype=np.float32)
+    do = np.ascontiguousarray(dout, dtype=np.float32)
+    assert do.shape == q.shape
+    slopes = None if w.alibi_slopes is None else np.ascontiguousarray(w.alibi_slopes, np.float32)
+    dq = np.zeros((w.total_q, w.heads_q, w.head_dim), np.float64)
+    dk = np.zeros((w.total_k, w.heads_k, w.head_dim), np.float64)
+    dv = np.zeros((w.total_k, w.heads_k, w.head_dim), np.float64)
+    lib.orc_attention_bwd(ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck), _ptr(q), _ptr(k),
+                          _ptr(v), _ptr(do), float(w.scale), int(w.softcap > 0),
+                          float(w.softcap), int(slopes is not None), _ptr(slopes),
+                          int(bool(w.alibi_before_softcap)), _ptr(dq), _ptr(dk), _ptr(dv),
+                          nthreads or default_threads())
+    return dq, dk, dv

@@ -35,6 +35,10 @@
  *   - score_mod : softcap c*tanh(s/c) then ALiBi + slope_h*(k-q) with
  *                 sample-local positions (optionally ALiBi first); the scale is
  *                 applied before either.
+ *   - backward  : the gradient of Eq. 1 for a given dO, by the chain rule
+ *                 written out per row (see orc_attention_bwd); the softcap's
+ *                 derivative is 1 - tanh^2, ALiBi's is 1 (FlexAttention,
+ *                 "automatic backward of score_mod").
  *
  * Threads: independent rows are split over POSIX threads; each thread runs the
  * same plain loops on its own rows.  No -ffast-math.
@@ -637,6 +641,143 @@ void orc_attention(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
     pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
   }
   for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
+
+/* ------------------------------------------------------------ backward */
+
+/* d(score_mod)/d(scaled score) at scaled score t: the softcap's derivative at
+ * its own input, 1 - tanh^2(u/c); ALiBi adds a constant. */
+static double mod_slope(const orc_mod* m, double t, int h, int64_t q, int64_t k) {
+  if (!m->softcap_on) return 1.0;
+  double u = t;
+  if (m->alibi_on && m->alibi_first) u += (double)m->slopes[h] * (double)(k - q);
+  double th = tanh(u / m->softcap);
+  return 1.0 - th * th;
+}
+
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float *q, *k, *v, *dout;
+  double scale;
+  const orc_mod* mod;
+  int64_t begin, end;    /* items (sample, kv head) */
+  double *dq, *dk, *dv;
+} bwd_job;
+
+/* One item = (sample b, kv head g): every Q row of b for every Q head of the
+ * group.  For a row with visible keys k (scaled score x_k, modded t_k):
+ *   P_k  = exp(t_k - LSE),              LSE = log sum_k exp(t_k)
+ *   dP_k = dO . V_k
+ *   dT_k = P_k (dP_k - sum_j P_j dP_j)  (softmax backward)
+ *   dX_k = dT_k * dt/dx_k               (score_mod backward)
+ *   dQ  += scale * dX_k * K_k,  dK_k += scale * dX_k * Q,  dV_k += P_k * dO.
+ * dK and dV of the item's K rows receive only this item's contributions. */
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  const orc_problem* p = J->p;
+  int d = p->head_dim;
+  int group = p->heads_q / p->heads_k;
+  int64_t kmax = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)kmax);
+  double* x = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* t = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* P = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)kmax);
+  for (int64_t it = J->begin; it < J->end; ++it) {
+    int b = (int)(it / p->heads_k);
+    int g = (int)(it % p->heads_k);
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    for (int h = g * group; h < (g + 1) * group; ++h) {
+      int hm = p->mask_heads == 1 ? 0 : h;
+      for (int64_t ql = 0; ql < q_len; ++ql) {
+        int64_t tok = q_off + ql;
+        const int32_t* F = J->mf + (int64_t)hm * p->nfunc * p->total_q + tok;
+        orc_expand_row(F, p->total_q, p->nfunc, k_len, vis);
+        const float* qrow = J->q + (tok * p->heads_q + h) * (int64_t)d;
+        const float* dorow = J->dout + (tok * p->heads_q + h) * (int64_t)d;
+        double m = -INFINITY;
+        int any = 0;
+        for (int64_t kk = 0; kk < k_len; ++kk) {
+          if (!vis[kk]) continue;
+          const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += (double)qrow[i] * (double)krow[i];
+          x[kk] = J->scale * dot;
+          t[kk] = apply_mod(J->mod, x[kk], h, ql, kk);
+          if (!any || t[kk] > m) m = t[kk];
+          any = 1;
+        }
+        if (!any) continue;   /* nothing visible: no gradient flows */
+        double l = 0.0;
+        for (int64_t kk = 0; kk < k_len; ++kk)
+          if (vis[kk]) l += exp(t[kk] - m);
+        double lse = m + log(l);
+        double Dsum = 0.0;
+        for (int64_t kk = 0; kk < k_len; ++kk) {
+          if (!vis[kk]) continue;
+          const float* vrow = J->v + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          P[kk] = exp(t[kk] - lse);
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += (double)dorow[i] * (double)vrow[i];
+          dP[kk] = dot;
+          Dsum += P[kk] * dP[kk];
+        }
+        double* dqrow = J->dq + (tok * p->heads_q + h) * (int64_t)d;
+        for (int64_t kk = 0; kk < k_len; ++kk) {
+          if (!vis[kk]) continue;
+          double dT = P[kk] * (dP[kk] - Dsum);
+          double dX = dT * mod_slope(J->mod, x[kk], h, ql, kk);
+          const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          double* dkrow = J->dk + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          double* dvrow = J->dv + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          for (int i = 0; i < d; ++i) {
+            dqrow[i] += J->scale * dX * (double)krow[i];
+            dkrow[i] += J->scale * dX * (double)qrow[i];
+            dvrow[i] += P[kk] * (double)dorow[i];
+          }
+        }
+      }
+    }
+  }
+  free(vis);
+  free(x);
+  free(t);
+  free(P);
+  free(dP);
+  return NULL;
+}
+
+/* Gradients of the attention output O with respect to Q, K and V for the
+ * incoming gradient dout ([total_q][Hq][d]).  dq is [total_q][Hq][d], dk and
+ * dv [total_k][Hk][d]; all three are overwritten.  Same inputs as
+ * orc_attention; the forward quantities are recomputed here. */
+void orc_attention_bwd(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                       const int32_t* cu_k, const float* q, const float* k, const float* v,
+                       const float* dout, double scale, int softcap_on, double softcap,
+                       int alibi_on, const float* slopes, int alibi_first, double* dq,
+                       double* dk, double* dv, int nthreads) {
+  orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
+  int d = p->head_dim;
+  memset(dq, 0, sizeof(double) * (size_t)p->total_q * p->heads_q * d);
+  memset(dk, 0, sizeof(double) * (size_t)p->total_k * p->heads_k * d);
+  memset(dv, 0, sizeof(double) * (size_t)p->total_k * p->heads_k * d);
+  int64_t items = (int64_t)p->batch * p->heads_k;
+  if (nthreads < 1) nthreads = 1;
+  if (items < nthreads) nthreads = items > 0 ? (int)items : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  bwd_job* jobs = (bwd_job*)malloc(sizeof(bwd_job) * nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (bwd_job){p, mf, cu_q, cu_k, q, k, v, dout, scale, &mod,
+                        items * i / nthreads, items * (i + 1) / nthreads, dq, dk, dv};
+    pthread_create(&th[i], NULL, bwd_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
   free(th);
   free(jobs);
 }

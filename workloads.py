@@ -99,6 +99,15 @@ def _draw_qkv(rng, total_q, total_k, hq, hk, d, dtype, with_values=True):
     return q, k, v
 
 
+def grad_output(w: "Workload") -> np.ndarray:
+    """Seeded incoming gradient dO [total_q, Hq, d] for a backward pass: N(0,1)
+    from its own generator (seeded with (seed, 1), so the forward inputs are
+    unchanged), bf16-rounded for bf16 workloads."""
+    rng = np.random.default_rng([w.seed, 1])
+    do = rng.standard_normal((w.total_q, w.heads_q, w.head_dim), dtype=np.float32)
+    return round_to_bf16(do) if w.dtype == DTYPE_BF16 else do
+
+
 def alibi_slopes(heads: int) -> np.ndarray:
     """slope_h = 2^(-8(h+1)/H) as float32."""
     h = np.arange(heads, dtype=np.float64)
