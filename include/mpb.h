@@ -277,6 +277,36 @@ mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* probl
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t force_partial);
 
+/* Bytes of caller-provided device workspace flex_attn_bwd needs: one fp32
+ * per (Q row, head) for dO . O, rounded up to 256. */
+size_t flex_attn_bwd_workspace_size(const mpb_plan* plan);
+
+/* flex_attn_bwd [MPD §6.3, §8; FLEX Eq. 1 and its automatic backward]:
+ * gradients of O = softmax(mod(Q K^T * scale)) V for an incoming dO.
+ *   plan      built with build_backward = 1 (else MPB_ERR_INVALID_ARGUMENT:
+ *             a training call needs the backward view [MPD §8]); problem,
+ *             device and tile checked as for flex_attn_fwd.  bf16 only, at
+ *             the forward's bf16 tile geometries (else MPB_ERR_UNSUPPORTED).
+ *   q,k,v     device bf16, the forward's inputs, layout per `problem`.
+ *   o, lse    the forward's outputs for these inputs (flex_attn_fwd).
+ *   dout      device bf16, layout of o: the gradient of the loss w.r.t. O.
+ *   dq        device bf16, layout of q (overwritten).
+ *   dk, dv    device bf16, layout of k and v (overwritten): for grouped
+ *             heads, summed over the Q heads of each KV head.
+ *   scale,mod exactly as given to the forward; the score_mod contributes its
+ *             derivative (softcap: 1 - tanh^2 of its argument; ALiBi: 1).
+ *   workspace device, >= flex_attn_bwd_workspace_size(plan) bytes.
+ * The dQ consumer walks the Q2K view, the dK/dV consumer the K2Q view;
+ * partial entries apply their predicate, full entries none, empty pairs are
+ * never touched [MPD §6.3].  A row with nothing visible contributes nothing;
+ * a K row that no Q row sees gets dK = dV = 0.  Every buffer must be 16-byte
+ * aligned.  Enqueue only; every refusal happens before any launch. */
+mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float scale,
+                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 const char* mpb_status_string(mpb_status status);
 const char* mpb_last_error_detail(void);
 

@@ -102,6 +102,10 @@ def _load():
                 ctypes.c_size_t, vp]
     lib.flex_attn_fwd.argtypes = fwd_args
     lib.flex_attn_fwd_ablation.argtypes = fwd_args + [ctypes.c_int32]
+    lib.flex_attn_bwd_workspace_size.argtypes = [vp]
+    lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
+                                                              ctypes.c_size_t, vp]
     lib.mpb_status_string.restype = ctypes.c_char_p
     lib.mpb_status_string.argtypes = [ctypes.c_int]
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
@@ -109,7 +113,7 @@ def _load():
     for name in ("mask_plan_build", "mask_plan_build_ex", "mask_plan_destroy", "mask_plan_info",
                  "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times",
                  "mask_plan_export_launch_order",
-                 "flex_attn_fwd", "flex_attn_fwd_ablation"):
+                 "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -364,3 +368,44 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
     else:
         _check(_lib.flex_attn_fwd(*args))
     return out, lse
+
+
+def flex_attn_bwd_workspace_size(plan: MaskPlan) -> int:
+    return int(_lib.flex_attn_bwd_workspace_size(plan.handle))
+
+
+def flex_attn_bwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                  o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                  scale: Optional[float] = None, softcap: Optional[float] = None,
+                  alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
+                  dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                  dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Backward of flex_attn_fwd over a plan built with build_backward=True:
+    returns (dQ, dK, dV) for the incoming gradient dout (see include/mpb.h).
+
+    Allocates the outputs and the workspace with torch when not given."""
+    if k.shape != v.shape or dout.shape != q.shape or o.shape != q.shape:
+        raise ValueError("k/v, and q/o/dout must have matching shapes")
+    prob = _call_problem(plan, q, k)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(flex_attn_bwd_workspace_size(plan), dtype=torch.uint8,
+                                device=q.device)
+    mod = None
+    if softcap or alibi_slopes is not None:
+        mod = ScoreMod(1 if softcap else 0, float(softcap or 0.0),
+                       1 if alibi_slopes is not None else 0,
+                       _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
+                       1 if alibi_before_softcap else 0)
+    sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
+    _check(_lib.flex_attn_bwd(
+        plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype),
+        _dev_ptr(v, "v", q.dtype), _dev_ptr(o, "o", q.dtype), _dev_ptr(lse, "lse", torch.float32),
+        _dev_ptr(dout, "dout", q.dtype), _dev_ptr(dq, "dq", q.dtype), _dev_ptr(dk, "dk", q.dtype),
+        _dev_ptr(dv, "dv", q.dtype), sc, ctypes.byref(mod) if mod is not None else None,
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream)))
+    return dq, dk, dv

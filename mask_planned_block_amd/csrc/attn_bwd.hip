@@ -1,0 +1,515 @@
+// Block-sparse flex attention backward for gfx950 (MI355X).
+//
+// Gradients of FlexAttention's Eq. 1 (O = softmax(mod(Q K^T * scale)) V)
+// for an incoming dO, consuming the plan as "Flex Attention Mask Plan
+// Design" §6.3 prescribes: the Q-major dQ kernel walks the Q2K view and the
+// K-major dK/dV kernel walks the K2Q view; partial entries apply their packed
+// predicate, full entries none; empty pairs are never touched.  Softmax
+// weights are recomputed from the forward's LSE (FlexAttention: the backward
+// recomputes the forward softmax from saved statistics), and the score_mod
+// contributes its derivative (softcap: 1 - tanh^2 of its argument; ALiBi: 1).
+//
+// With x = scale * q.k, t = mod(x), P = exp(t - LSE) and Dq = dO . O:
+//   dP = dO . V,  dS = P (dP - Dq) dt/dx,
+//   dQ = scale * sum_k dS K,  dK = scale * sum_q dS Q,  dV = sum_q P dO.
+//
+// Three launches:
+//  * attn_bwd_dot_kernel: Dq per (row, head), fp32 [Hq][total_q].
+//  * attn_bwd_dq_kernel: one workgroup per task of the plan's launch order
+//    (as the forward), a wavefront per 32 Q rows.  S^T = K Q^T and
+//    dP^T = V dO^T put one Q row in each lane (its LSE and Dq are scalars),
+//    dS^T feeds dQ^T += K^T dS^T from registers; K^T is read from the
+//    row-major K tile with ds_read_b64_tr_b16.  K and V are double buffered
+//    in LDS and fetched one tile ahead straight from HBM.
+//  * attn_bwd_dkdv_kernel: one workgroup per (KV head, K plan row), a
+//    wavefront per 32 K rows, looping over the heads of the KV group and the
+//    Q tiles that the K2Q view lists for the K row.  S = Q K^T and
+//    dP = dO V^T put one K row in each lane, with K and V held in registers
+//    for the whole workgroup; P and dS feed dV^T += dO^T P and dK^T += Q^T dS
+//    from registers, dO^T and Q^T read transposed from the Q/dO tiles in LDS.
+//    dK and dV of the K row are summed over the group in registers, so no
+//    atomics and a deterministic result.
+// All products on v_mfma_f32_32x32x16_bf16 (P and dS rounded to bf16),
+// statistics and accumulators in fp32; outputs in bf16.
+#include "mpb_internal.h"
+#include "../../include/mpb.h"
+
+namespace mpb {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kPosInf = __builtin_huge_valf();
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ inline u32x4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// MFMA 32x32x16 bf16 operand layouts used below (D = A B, 32x32 outputs):
+//   A: lane l holds A[l % 32][8 (l / 32) + i], i = 0..7
+//   B: lane l holds B[8 (l / 32) + i][l % 32]
+//   D: lane l holds D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32], v = 0..15
+// A 32-row tile in LDS is row-major with D bf16 per row, its 16-byte chunk c
+// of row r stored at position c ^ (r % (D / 8)).
+
+// 16 bytes of row `row`, logical chunk `c`.
+template <int D>
+__device__ inline bf16x8 lds_chunk(const __bf16* tile, int row, int c) {
+  constexpr int CH = D / 8;
+  return *(const bf16x8*)(tile + row * D + ((c ^ (row % CH)) << 3));
+}
+
+// A operand X^T (rows of the LDS tile X are the MFMA k index, its columns the
+// m index) for the k-step over X rows [kb, kb + 16) and columns [32 db, +32):
+// two ds_read_b64_tr_b16, each giving lane L the column 32 db + L % 32 of
+// four consecutive rows, in the k-slot order of the D layout above (slots
+// 0..3: rows kb + 4 (L / 32) + j, slots 4..7: the same + 8).
+template <int D>
+__device__ inline bf16x8 lds_tr_frag(const __bf16* tile, int kb, int db, int lane) {
+  constexpr int CH = D / 8;
+  const int r = lane & 15, g2 = (lane >> 4) & 1, kg = lane >> 5;
+  const int row = kb + 4 * kg + (r >> 2);
+  const int dcol = 32 * db + 16 * g2 + 4 * (r & 3);
+  const int c = dcol >> 3, e = dcol & 7;
+  const __bf16* p0 = tile + row * D + (((c ^ (row % CH)) << 3) + e);
+  const __bf16* p1 = tile + (row + 8) * D + (((c ^ ((row + 8) % CH)) << 3) + e);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
+  const v4i16 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// Rows [0, R) of a row-major bf16 tile at byte tile_off of `src` (rs bytes
+// per row) straight into LDS `dst` with the chunk swizzle above; NWAVES
+// wavefronts share the rows.  Rows past the resource's range land as zeros.
+template <int D, int R, int NWAVES>
+__device__ inline void dma_tile(__bf16* dst, rsrc_t src, uint32_t tile_off, uint32_t rs,
+                                int wave, int lane) {
+  constexpr int CH = D / 8, RPI = 1024 / (D * 2);
+  static_assert(R % (RPI * NWAVES) == 0, "tile rows must split evenly over wavefronts");
+#pragma unroll
+  for (int c = 0; c < R / RPI / NWAVES; ++c) {
+    const int r0 = (c * NWAVES + wave) * RPI;
+    const int r = r0 + lane / CH;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        src, (lds_vptr)&dst[r0 * D], 16, (int)(tile_off + r * rs + ((lane % CH) ^ (r % CH)) * 16),
+        0, 0, 0);
+  }
+}
+
+// B operand fragments of one token row (d = 16 s + 8 (lane / 32) + i).
+template <int D>
+__device__ inline void load_row_frags(bf16x8 (&f)[D / 16], rsrc_t r, uint32_t row_off, int g) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    f[s] = __builtin_bit_cast(bf16x8, bload16(r, row_off + (16 * s + 8 * g) * 2));
+}
+
+// Stores a D^T accumulator set (lane: one token row, d = 32 db + 8 a + 4 g + c)
+// times `mul` as bf16; stores past the resource's range are dropped.
+template <int D>
+__device__ inline void store_rows(rsrc_t r, uint32_t row_off, const f32x16 (&acc)[D / 32],
+                                  float mul, int g) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      bf16x4 v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = (__bf16)(acc[db][4 * a + c] * mul);
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r,
+                                            (int)(row_off + (db * 32 + 8 * a + 4 * g) * 2), 0, 0);
+    }
+}
+
+// score_mod of a raw dot product s in log2 units, log2(e) * mod(s * scale),
+// and its derivative with respect to x = s * scale.  kq = k - q.
+// softcap: c tanh(u / c) = c (1 - 2 r) with r = 1 / (1 + e^{2u/c}), whose
+// derivative 1 - tanh^2 is 4 r (1 - r).
+template <int MOD>
+__device__ inline float mod_fwd_bwd(float s, float kq, const BwdParams& p, float slope,
+                                    float& grad) {
+  if constexpr (MOD == kModNone) {
+    grad = 1.0f;
+    return s * p.scale_log2;
+  } else if constexpr (MOD == kModAlibi) {
+    grad = 1.0f;
+    return fmaf(s, p.scale_log2, slope * kq);          // slope = slope_h * log2e
+  } else if constexpr (MOD == kModSoftcap || MOD == kModSoftcapAlibi) {
+    const float r = rcp_fast(1.0f + exp2_fast(s * p.softcap_k));
+    grad = 4.0f * r * (1.0f - r);
+    float u = fmaf(-2.0f * p.softcap_c2, r, p.softcap_c2);
+    if constexpr (MOD == kModSoftcapAlibi) u = fmaf(slope, kq, u);
+    return u;
+  } else {   // kModAlibiSoftcap: slope = slope_h * 2 log2e / c
+    const float r = rcp_fast(1.0f + exp2_fast(fmaf(s, p.softcap_k, slope * kq)));
+    grad = 4.0f * r * (1.0f - r);
+    return fmaf(-2.0f * p.softcap_c2, r, p.softcap_c2);
+  }
+}
+
+template <int MOD>
+__device__ inline float head_slope(const BwdParams& p, int h) {
+  if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) return p.slopes[h] * kLog2e;
+  else if constexpr (MOD == kModAlibiSoftcap) return p.slopes[h] * p.alibi_k;
+  else return 0.0f;
+}
+
+// LSE in log2 units for the exponent; +inf for a row with nothing visible
+// (its weights are then exactly 0) and for rows past the sample.
+__device__ inline float lse_log2(float lse) { return lse == -kPosInf ? kPosInf : lse * kLog2e; }
+
+// Weight and dS of one score element.
+template <int MOD>
+__device__ inline void weight_and_ds(float s, float dp, float kq, bool keep, float lse2, float dq,
+                                     const BwdParams& p, float slope, float& P, float& dS) {
+  float grad;
+  const float t = mod_fwd_bwd<MOD>(s, kq, p, slope, grad);
+  P = keep ? exp2_fast(t - lse2) : 0.0f;
+  dS = P * (dp - dq) * grad;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ Dq
+
+// Dq[h][t] = dO[t][h] . O[t][h] in fp32; D / 8 lanes per (token, head) row.
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(BwdParams p) {
+  constexpr int L = D / 8;
+  const int64_t rows = (int64_t)p.total_q * p.heads_q;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / L;
+  const int part = (int)(gid % L);
+  float s = 0.0f;
+  if (row < rows) {
+    const bf16x8 a = *(const bf16x8*)((const __bf16*)p.o + row * D + part * 8);
+    const bf16x8 b = *(const bf16x8*)((const __bf16*)p.dout + row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = fmaf((float)a[i], (float)b[i], s);
+  }
+#pragma unroll
+  for (int off = L / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+  if (row < rows && part == 0) {
+    const int64_t t = row / p.heads_q;
+    const int h = (int)(row % p.heads_q);
+    p.dvec[(int64_t)h * p.total_q + t] = s;
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+
+template <int D, int TQ, int TKV, int MOD>
+__global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
+  constexpr int NW = TQ / 32, NKB = TKV / 32, DS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 k_s0[TKV * D];
+  __shared__ __attribute__((aligned(16))) __bf16 k_s1[TKV * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_s0[TKV * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_s1[TKV * D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lq = lane & 31;
+
+  const int32_t* rec = p.task_rec + (int64_t)blockIdx.x * kTaskRecInts;
+  const int m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);
+  const int h = __builtin_amdgcn_readfirstlane(rec[kRecHead]);
+  const int q_off = __builtin_amdgcn_readfirstlane(rec[kRecQOff]);
+  const int k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
+  const int q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
+  const int k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
+  const int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
+  const int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
+  const int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
+  const int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
+  const int kvh = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
+
+  const uint32_t q_rs = (uint32_t)p.heads_q * D * 2;
+  const uint32_t kv_rs = (uint32_t)p.heads_k * D * 2;
+  const int64_t qh = (int64_t)q_off * q_rs + (int64_t)h * D * 2;
+  const int64_t kh = (int64_t)k_off * kv_rs + (int64_t)kvh * D * 2;
+  const rsrc_t rq = make_rsrc((const char*)p.q + qh, (uint32_t)q_len * q_rs);
+  const rsrc_t rdo = make_rsrc((const char*)p.dout + qh, (uint32_t)q_len * q_rs);
+  const rsrc_t rdq = make_rsrc((char*)p.dq + qh, (uint32_t)q_len * q_rs);
+  const rsrc_t rk = make_rsrc((const char*)p.k + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rv = make_rsrc((const char*)p.v + kh, (uint32_t)k_len * kv_rs);
+
+  const int qloc = m_block * TQ + 32 * wave + lq;   // this lane's sample-local Q row
+  const uint32_t q_row_off = (uint32_t)qloc * q_rs;
+  auto tile_j = [&](int t) {
+    return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
+  };
+  auto load_kv = [&](int t, __bf16* kd, __bf16* vd) {
+    const uint32_t off = (uint32_t)tile_j(t) * TKV * kv_rs;
+    dma_tile<D, TKV, NW>(kd, rk, off, kv_rs, wave, lane);
+    dma_tile<D, TKV, NW>(vd, rv, off, kv_rs, wave, lane);
+  };
+  if (ntiles > 0) load_kv(0, k_s0, v_s0);
+
+  bf16x8 qf[DS], df[DS];
+  load_row_frags<D>(qf, rq, q_row_off, g);
+  load_row_frags<D>(df, rdo, q_row_off, g);
+  const bool row_in = qloc < q_len;
+  const int64_t stat = (int64_t)h * p.total_q + q_off + qloc;
+  const float lse2 = row_in ? lse_log2(p.lse[stat]) : kPosInf;
+  const float dqv = row_in ? p.dvec[stat] : 0.0f;
+  const float slope = head_slope<MOD>(p, h);
+
+  f32x16 acc_dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_dq[db] = f32x16{};
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int st = t & 1;
+    __bf16* ks = st ? k_s1 : k_s0;
+    __bf16* vs = st ? v_s1 : v_s0;
+    const int j = tile_j(t);
+    uint32_t mw[NKB];
+    if (t < np) {
+      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk] >> (4 * g);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's tile loads have landed
+    __syncthreads();                 // ... and everyone's
+    if (t + 1 < ntiles) load_kv(t + 1, st ? k_s0 : k_s1, st ? v_s0 : v_s1);
+
+    // S^T = K Q^T and dP^T = V dO^T: lane holds Q row lq, K rows 8(v/4)+4g+v%4
+    f32x16 s_acc[NKB], dp_acc[NKB];
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) s_acc[kk] = dp_acc[kk] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < DS; ++s)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) {
+        const bf16x8 a = lds_chunk<D>(ks, 32 * kk + lq, 2 * s + g);
+        const bf16x8 b = lds_chunk<D>(vs, 32 * kk + lq, 2 * s + g);
+        s_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s_acc[kk], 0, 0, 0);
+        dp_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, df[s], dp_acc[kk], 0, 0, 0);
+      }
+    // dS^T in the B operand order of the next product
+    bf16x8 dsb[NKB][2];
+    const float kq0 = (float)(j * TKV + 4 * g - qloc);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int pos = 8 * (v / 4) + v % 4;
+        const bool keep = (mw[kk] >> pos) & 1u;
+        float P, dS;
+        weight_and_ds<MOD>(s_acc[kk][v], dp_acc[kk][v], kq0 + (float)(32 * kk + pos), keep, lse2,
+                           dqv, p, slope, P, dS);
+        dsb[kk][v / 8][v % 8] = (__bf16)dS;
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_tr_frag<D>(ks, 32 * kk + 16 * m, db, lane), dsb[kk][m], acc_dq[db], 0, 0, 0);
+  }
+  store_rows<D>(rdq, q_row_off, acc_dq, p.scale, g);
+}
+
+// ------------------------------------------------------------------ dK, dV
+
+template <int D, int TQ, int TKV, int MOD>
+__global__ __launch_bounds__(TKV * 2) void attn_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NWK = TKV / 32, NQB = TQ / 32, DS = D / 16, DB = D / 32;
+  __shared__ __attribute__((aligned(16))) __bf16 q_s[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s[TQ * D];
+  __shared__ float lse_s[TQ];
+  __shared__ float dq_s[TQ];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lq = lane & 31;
+
+  const int item = blockIdx.x;
+  const int kvh = item / p.krows_total;
+  const int kr = item - kvh * p.krows_total;
+  // sample of the K row (largest b with cu_krows[b] <= kr)
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.k_cu[mid] <= kr) lo = mid; else hi = mid - 1;
+  }
+  const int b = __builtin_amdgcn_readfirstlane(lo);
+  const int j = kr - p.k_cu[b];
+  const int32_t* sd = p.seqdesc + 8 * b;
+  const int q_off = __builtin_amdgcn_readfirstlane(sd[0]);
+  const int k_off = __builtin_amdgcn_readfirstlane(sd[1]);
+  const int q_len = __builtin_amdgcn_readfirstlane(sd[2]);
+  const int k_len = __builtin_amdgcn_readfirstlane(sd[3]);
+
+  const uint32_t q_rs = (uint32_t)p.heads_q * D * 2;
+  const uint32_t kv_rs = (uint32_t)p.heads_k * D * 2;
+  const int64_t kh = (int64_t)k_off * kv_rs + (int64_t)kvh * D * 2;
+  const rsrc_t rk = make_rsrc((const char*)p.k + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rv = make_rsrc((const char*)p.v + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rdk = make_rsrc((char*)p.dk + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rdv = make_rsrc((char*)p.dv + kh, (uint32_t)k_len * kv_rs);
+
+  const int kloc = j * TKV + 32 * wave + lq;   // this lane's sample-local K row
+  const uint32_t k_row_off = (uint32_t)kloc * kv_rs;
+  bf16x8 kf[DS], vf[DS];
+  load_row_frags<D>(kf, rk, k_row_off, g);
+  load_row_frags<D>(vf, rv, k_row_off, g);
+
+  f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_dk[db] = acc_dv[db] = f32x16{};
+
+  for (int hh = 0; hh < p.group; ++hh) {
+    const int h = kvh * p.group + hh;
+    const int hm = p.mask_heads == 1 ? 0 : h;
+    const int64_t flat = (int64_t)hm * p.krows_total + kr;
+    const int pb = __builtin_amdgcn_readfirstlane(p.k_p_off[flat]);
+    const int np = __builtin_amdgcn_readfirstlane(p.k_p_off[flat + 1]) - pb;
+    const int fb = __builtin_amdgcn_readfirstlane(p.k_f_off[flat]);
+    const int ntiles = np + __builtin_amdgcn_readfirstlane(p.k_f_off[flat + 1]) - fb;
+    const int64_t qh = (int64_t)q_off * q_rs + (int64_t)h * D * 2;
+    const rsrc_t rq = make_rsrc((const char*)p.q + qh, (uint32_t)q_len * q_rs);
+    const rsrc_t rdo = make_rsrc((const char*)p.dout + qh, (uint32_t)q_len * q_rs);
+    const float slope = head_slope<MOD>(p, h);
+    const int64_t stat = (int64_t)h * p.total_q + q_off;
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int i = __builtin_amdgcn_readfirstlane(t < np ? p.k_p_idx[pb + t]
+                                                          : p.k_f_idx[fb + t - np]);
+      __syncthreads();   // the previous tile's LDS reads are done
+      dma_tile<D, TQ, NWK>(q_s, rq, (uint32_t)i * TQ * q_rs, q_rs, wave, lane);
+      dma_tile<D, TQ, NWK>(do_s, rdo, (uint32_t)i * TQ * q_rs, q_rs, wave, lane);
+      for (int r = tid; r < TQ; r += TKV * 2) {
+        const int q = i * TQ + r;
+        lse_s[r] = q < q_len ? lse_log2(p.lse[stat + q]) : kPosInf;
+        dq_s[r] = q < q_len ? p.dvec[stat + q] : 0.0f;
+      }
+      uint32_t mw[NQB];
+      if (t < np) {
+        const uint32_t* src = p.k_masks + ((int64_t)(pb + t) * TKV + 32 * wave + lq) * NQB;
+#pragma unroll
+        for (int w = 0; w < NQB; ++w) mw[w] = src[w] >> (4 * g);
+      } else {
+#pragma unroll
+        for (int w = 0; w < NQB; ++w) mw[w] = 0xFFFFFFFFu;
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+
+      const float kq0 = (float)(kloc - i * TQ - 4 * g);
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb) {
+        // S = Q K^T and dP = dO V^T: lane holds K row lq, Q rows 32qb+8(v/4)+4g+v%4
+        f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < DS; ++s) {
+          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_chunk<D>(q_s, 32 * qb + lq, 2 * s + g),
+                                                          kf[s], s_acc, 0, 0, 0);
+          dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              lds_chunk<D>(do_s, 32 * qb + lq, 2 * s + g), vf[s], dp_acc, 0, 0, 0);
+        }
+        bf16x8 pb8[2], dsb[2];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int pos = 8 * (v / 4) + v % 4;
+          const int qr = 32 * qb + pos + 4 * g;   // tile-local Q row
+          const bool keep = (mw[qb] >> pos) & 1u;
+          float P, dS;
+          weight_and_ds<MOD>(s_acc[v], dp_acc[v], kq0 - (float)(32 * qb + pos), keep, lse_s[qr],
+                             dq_s[qr], p, slope, P, dS);
+          pb8[v / 8][v % 8] = (__bf16)P;
+          dsb[v / 8][v % 8] = (__bf16)dS;
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                lds_tr_frag<D>(do_s, 32 * qb + 16 * m, db, lane), pb8[m], acc_dv[db], 0, 0, 0);
+            acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                lds_tr_frag<D>(q_s, 32 * qb + 16 * m, db, lane), dsb[m], acc_dk[db], 0, 0, 0);
+          }
+      }
+    }
+  }
+  store_rows<D>(rdk, k_row_off, acc_dk, p.scale, g);
+  store_rows<D>(rdv, k_row_off, acc_dv, 1.0f, g);
+}
+
+// ------------------------------------------------------------------ dispatch
+
+namespace {
+
+template <int D, int TQ, int TKV, int MOD>
+hipError_t launch_bwd_mod(int num_tasks, const BwdParams& p, hipStream_t s) {
+  if (num_tasks > 0)
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, TQ, TKV, MOD>), dim3(num_tasks), dim3(TQ * 2), 0, s,
+                       p);
+  const int64_t items = (int64_t)p.heads_k * p.krows_total;
+  if (items > 0)
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, TQ, TKV, MOD>), dim3((unsigned)items),
+                       dim3(TKV * 2), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int D, int TQ, int TKV>
+hipError_t launch_bwd(int mod, int num_tasks, const BwdParams& p, hipStream_t s) {
+  const int64_t rows = (int64_t)p.total_q * p.heads_q;
+  if (rows > 0)
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<D>), dim3((unsigned)((rows * (D / 8) + 255) / 256)),
+                       dim3(256), 0, s, p);
+  switch (mod) {
+    case kModNone: return launch_bwd_mod<D, TQ, TKV, kModNone>(num_tasks, p, s);
+    case kModSoftcap: return launch_bwd_mod<D, TQ, TKV, kModSoftcap>(num_tasks, p, s);
+    case kModAlibi: return launch_bwd_mod<D, TQ, TKV, kModAlibi>(num_tasks, p, s);
+    case kModSoftcapAlibi: return launch_bwd_mod<D, TQ, TKV, kModSoftcapAlibi>(num_tasks, p, s);
+    case kModAlibiSoftcap: return launch_bwd_mod<D, TQ, TKV, kModAlibiSoftcap>(num_tasks, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// The backward consumers: bf16 at the forward's bf16 tile geometries.
+#define MPB_BWD_VARIANTS(X) \
+  X(128, 128, 64) X(128, 64, 64) X(128, 128, 32) X(128, 64, 32) X(64, 128, 64) X(64, 64, 64)
+
+bool attn_bwd_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k) {
+  if (dtype != MPB_DTYPE_BF16) return false;
+#define X(D_, TQ_, TKV_) \
+  if (head_dim == D_ && tile_q == TQ_ && tile_k == TKV_) return true;
+  MPB_BWD_VARIANTS(X)
+#undef X
+  return false;
+}
+
+hipError_t launch_attn_bwd(int32_t head_dim, int32_t tile_q, int32_t tile_k, int32_t mod_kind,
+                           int32_t num_tasks, const BwdParams& p, hipStream_t s) {
+#define X(D_, TQ_, TKV_) \
+  if (head_dim == D_ && tile_q == TQ_ && tile_k == TKV_) return launch_bwd<D_, TQ_, TKV_>(mod_kind, num_tasks, p, s);
+  MPB_BWD_VARIANTS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mpb

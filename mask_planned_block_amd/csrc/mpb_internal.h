@@ -182,6 +182,40 @@ struct AttnParams {
   float alibi_k;            // ALiBi-first: 2*log2(e)/c multiplier of slope*(k-q)
 };
 
+// Backward: Q2K launch records and payload (dQ), K2Q lists and payload
+// (dK, dV), the forward's O and LSE, the incoming dO and a Dq workspace.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* lse;          // [heads_q][total_q], natural log
+  float* dvec;               // workspace [heads_q][total_q]: dO . O per row
+  const int32_t* seqdesc;
+  const int32_t* task_rec;
+  const int32_t* p_idx;
+  const int32_t* f_idx;
+  const uint32_t* p_masks;
+  const int32_t* k_cu;       // K2Q: cu_krows [batch+1]
+  const int32_t* k_p_off;
+  const int32_t* k_f_off;
+  const int32_t* k_p_idx;
+  const int32_t* k_f_idx;
+  const uint32_t* k_masks;
+  const float* slopes;
+  int32_t batch, heads_q, heads_k, group, mask_heads, total_q, krows_total;
+  float scale;
+  float scale_log2, softcap_k, softcap_c2, alibi_k;   // as in AttnParams
+};
+
+bool attn_bwd_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k);
+hipError_t launch_attn_bwd(int32_t head_dim, int32_t tile_q, int32_t tile_k, int32_t mod_kind,
+                           int32_t num_tasks, const BwdParams& p, hipStream_t s);
+
 // Attention kernel variants known to this build (the consumers a plan can be
 // resolved to).  Returns false if (dtype, head_dim, tile_q, tile_k) has none.
 bool attn_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k);

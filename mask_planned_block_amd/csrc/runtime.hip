@@ -1061,6 +1061,107 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   return ok();
 }
 
+size_t flex_attn_bwd_workspace_size(const mpb_plan* plan) {
+  if (!plan) return 0;
+  const size_t bytes = (size_t)plan->prob.heads_q * plan->prob.total_q * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float scale,
+                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_status(e, "hipGetDevice");
+  if (dev != plan->device)
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan built on device %d used on device %d",
+                plan->device, dev);
+  const mpb_problem& a = *problem;
+  const mpb_problem& b = plan->prob;
+#define MPB_CMP(f)                                                                           \
+  if (a.f != b.f)                                                                            \
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "field " #f ": call has %d, plan has %d", a.f, b.f);
+  MPB_CMP(layout) MPB_CMP(dtype) MPB_CMP(batch) MPB_CMP(seqlen_q) MPB_CMP(seqlen_k)
+  MPB_CMP(total_q) MPB_CMP(total_k) MPB_CMP(heads_q) MPB_CMP(heads_k) MPB_CMP(head_dim)
+  MPB_CMP(mask_heads) MPB_CMP(nfunc)
+#undef MPB_CMP
+  if ((a.tile_q && a.tile_q != b.tile_q) || (a.tile_k && a.tile_k != b.tile_k))
+    return fail(MPB_ERR_SIGNATURE_MISMATCH, "tile %dx%d requested, plan has %dx%d", a.tile_q,
+                a.tile_k, b.tile_q, b.tile_k);
+  // §8: a training call needs a plan built with its backward view.
+  if (!plan->has_k2q)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "the plan was built without the backward K2Q view");
+  if (!attn_bwd_variant_exists(b.dtype, b.head_dim, b.tile_q, b.tile_k))
+    return fail(MPB_ERR_UNSUPPORTED, "no gfx950 backward consumer for dtype %d, head_dim %d, "
+                "tile %dx%d", b.dtype, b.head_dim, b.tile_q, b.tile_k);
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
+  if (workspace_bytes < flex_attn_bwd_workspace_size(plan) || !workspace)
+    return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed",
+                flex_attn_bwd_workspace_size(plan));
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+  const int64_t qspan = ((int64_t)b.seqlen_q + b.tile_q) * b.heads_q * b.head_dim * 2;
+  const int64_t kspan = ((int64_t)b.seqlen_k + b.tile_k) * b.heads_k * b.head_dim * 2;
+  if (qspan >= ((int64_t)1 << 31) || kspan >= ((int64_t)1 << 31))
+    return fail(MPB_ERR_UNSUPPORTED, "one sample spans >= 2 GiB of Q/K/V; not supported");
+  const bool sc = mod && mod->softcap_enabled;
+  const bool al = mod && mod->alibi_enabled;
+  if (sc && !(std::isfinite(mod->softcap) && mod->softcap > 0.0f))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "softcap must be finite and > 0");
+  if (al && !mod->alibi_slopes) return fail(MPB_ERR_INVALID_ARGUMENT, "alibi_slopes is NULL");
+  int32_t kind = kModNone;
+  if (sc && al) kind = mod->alibi_before_softcap ? kModAlibiSoftcap : kModSoftcapAlibi;
+  else if (sc) kind = kModSoftcap;
+  else if (al) kind = kModAlibi;
+
+  BwdParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.o = o;
+  prm.dout = dout;
+  prm.dq = dq;
+  prm.dk = dk;
+  prm.dv = dv;
+  prm.lse = lse;
+  prm.dvec = static_cast<float*>(workspace);
+  prm.seqdesc = plan->dev.seqdesc;
+  prm.task_rec = plan->dev.task_rec;
+  prm.p_idx = plan->dev.p_idx;
+  prm.f_idx = plan->dev.f_idx;
+  prm.p_masks = plan->dev.p_masks;
+  prm.k_cu = plan->kdev.cu_krows;
+  prm.k_p_off = plan->kdev.p_off;
+  prm.k_f_off = plan->kdev.f_off;
+  prm.k_p_idx = plan->kdev.p_idx;
+  prm.k_f_idx = plan->kdev.f_idx;
+  prm.k_masks = plan->kdev.p_masks;
+  prm.slopes = al ? mod->alibi_slopes : nullptr;
+  prm.batch = b.batch;
+  prm.heads_q = b.heads_q;
+  prm.heads_k = b.heads_k;
+  prm.group = b.heads_q / b.heads_k;
+  prm.mask_heads = b.mask_heads;
+  prm.total_q = b.total_q;
+  prm.krows_total = (int32_t)plan->header[4];
+  prm.scale = scale;
+  const float log2e = 1.4426950408889634f;
+  prm.scale_log2 = scale * log2e;
+  prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
+  prm.softcap_c2 = sc ? mod->softcap * log2e : 0.0f;
+  prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((e = launch_attn_bwd(b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks, prm, s)) !=
+      hipSuccess)
+    return device_status(e, "backward launch");
+  return ok();
+}
+
 mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
                          const void* k, const void* v, void* o, float* lse, float scale,
                          const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,

@@ -1,0 +1,162 @@
+"""GPU parity of the attention backward (flex_attn_bwd through the C ABI)
+against the oracle's fp64 backward.
+
+Tolerance: the GPU rounds O (the forward's output, which Dq = dO . O uses),
+the MFMA operands P and dS, and dQ/dK/dV themselves to bf16.  Emulating
+exactly those roundings in float64 on the four bf16 reduced workloads gives
+max|err| / max|ref| between 2.5e-3 and 4.2e-3 per tensor; the test allows
+1e-2 of max|ref| (the fp32 accumulation order and the hardware exp2/rcp add
+far less).  Exact zeros are required where the method fixes them: dQ of a
+row that sees nothing, dK and dV of a key that no row sees.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests import gpu_support as G
+
+pytestmark = pytest.mark.gpu
+
+NORM_TOL = 1e-2
+BF16_CONFIGS = ["window_sink", "varlen_doc", "block_sparse", "prefix_softcap"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def require_gpu():
+    assert torch.cuda.is_available(), "no GPU visible to a GPU test"
+
+
+def _case(case, **kw):
+    print("CASE", case, kw, flush=True)
+
+
+def run_backward(w, d, plan, do_np):
+    import mask_planned_block_amd as mpb
+    o, lse = G.run_attention(w, d, plan)
+    dout = torch.from_numpy(do_np).to(torch.bfloat16).reshape(d["q"].shape).cuda()
+    dq, dk, dv = mpb.flex_attn_bwd(plan, d["q"], d["k"], d["v"], o, lse, dout, scale=w.scale,
+                                   softcap=w.softcap if w.softcap > 0 else None,
+                                   alibi_slopes=d["slopes"],
+                                   alibi_before_softcap=w.alibi_before_softcap)
+    torch.cuda.synchronize()
+    f = lambda x, T, H: x.float().reshape(T, H, w.head_dim).cpu().numpy().astype(np.float64)
+    return (f(dq, w.total_q, w.heads_q), f(dk, w.total_k, w.heads_k),
+            f(dv, w.total_k, w.heads_k))
+
+
+def compare_grads(w, ref, got, what=""):
+    for name, r, g in zip(("dQ", "dK", "dV"), ref, got):
+        assert not np.isnan(g).any(), "%s %s has NaN" % (what, name)
+        scale = float(np.max(np.abs(r))) if r.size else 0.0
+        err = float(np.max(np.abs(r - g))) if r.size else 0.0
+        print("  %s %s max|err|/max|ref| = %.3g" % (what, name, err / max(scale, 1e-30)),
+              flush=True)
+        assert err <= NORM_TOL * max(scale, 1e-30), "%s %s: max|err| %.3g vs max|ref| %.3g" % (
+            what, name, err, scale)
+
+
+def _check(w, tiles=None):
+    d = G.device_inputs(w)
+    tq, tk = tiles if tiles else (0, 0)
+    plan = G.build_plan(w, d, tq, tk, build_backward=True)
+    do = W.grad_output(w)
+    got = run_backward(w, d, plan, do)
+    ref = oracle.attention_bwd(w, do)
+    compare_grads(w, ref, got, w.name)
+    return ref, got
+
+
+@pytest.mark.parametrize("name", BF16_CONFIGS)
+def test_backward_small(name):
+    w = W.make(name, small=True)
+    _case("bwd_small", name=name)
+    _check(w)
+
+
+@pytest.mark.parametrize("tq,tk", [(64, 64), (128, 32), (64, 32)])
+@pytest.mark.parametrize("name", ["window_sink", "varlen_doc", "block_sparse"])
+def test_backward_other_tiles(name, tq, tk):
+    w = W.make(name, small=True)
+    _case("bwd_tiles", name=name, tq=tq, tk=tk)
+    _check(w, (tq, tk))
+
+
+@pytest.mark.parametrize("variant", ["softcap", "alibi", "alibi_first", "both"])
+def test_backward_score_mods(variant):
+    B, S = 2, 300
+    q_local = np.tile(np.arange(S), B)
+    mf = np.stack([np.minimum(q_local + 1, 32), np.maximum(np.minimum(q_local + 1, 32),
+                                                           q_local - 100), q_local + 1])[None]
+    kw = dict(batch=B, seqlen_q=S, seqlen_k=S, heads_q=4, heads_k=2, head_dim=128,
+              dtype=W.DTYPE_BF16, seed=4)
+    if variant in ("softcap", "both", "alibi_first"):
+        kw["softcap"] = 5.0
+    if variant in ("alibi", "both", "alibi_first"):
+        kw["alibi"] = True
+    if variant == "alibi_first":
+        kw["alibi_before_softcap"] = True
+    w = W.custom(mf.astype(np.int32), **kw)
+    _case("bwd_mod", variant=variant)
+    _check(w)
+
+
+def test_backward_head_dim_64():
+    B, S = 2, 333
+    q_local = np.tile(np.arange(S), B)
+    mf = (q_local + 1).reshape(1, 1, -1).astype(np.int32)
+    w = W.custom(mf, batch=B, seqlen_q=S, seqlen_k=S, heads_q=3, head_dim=64,
+                 dtype=W.DTYPE_BF16, seed=6)
+    _case("bwd_d64")
+    _check(w)
+    _check(w, (64, 64))
+
+
+def test_backward_empty_samples_rows_gqa_hmask():
+    lens_q = [130, 0, 77, 1, 256]
+    lens_k = [100, 5, 0, 64, 300]
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    rng = np.random.default_rng(3)
+    Hq = 4
+    mf = np.zeros((Hq, 5, int(cq[-1])), np.int32)
+    for b in range(5):
+        for t in range(cq[b], cq[b + 1]):
+            mf[:, :, t] = np.sort(rng.integers(0, lens_k[b] + 1, size=(Hq, 5)), axis=1)
+    mf[:, :, 0:3] = 0          # fully masked rows
+    w = W.custom(mf, layout=W.LAYOUT_THD, cu_seqlens_q=cq, cu_seqlens_k=ck, heads_q=Hq,
+                 heads_k=2, head_dim=128, dtype=W.DTYPE_BF16, seed=8)
+    _case("bwd_edge_thd")
+    ref, got = _check(w)
+    dq_ref, dk_ref, dv_ref = ref
+    dq, dk, dv = got
+    # rows that see nothing: dQ exactly 0; keys that nothing sees: dK = dV = 0
+    assert np.all(dq[0:3] == 0.0)
+    unseen = np.all(dv_ref == 0.0, axis=2)
+    assert np.all(dk[unseen] == 0.0) and np.all(dv[unseen] == 0.0)
+
+
+def test_backward_refusals():
+    import mask_planned_block_amd as mpb
+    w = W.make("window_sink", small=True)
+    d = G.device_inputs(w)
+    plan = G.build_plan(w, d)                    # no backward view
+    o, lse = G.run_attention(w, d, plan)
+    with pytest.raises(mpb.MPBError) as ei:
+        mpb.flex_attn_bwd(plan, d["q"], d["k"], d["v"], o, lse, torch.zeros_like(o),
+                          scale=w.scale)
+    assert ei.value.name == "MPB_ERR_INVALID_ARGUMENT"
+    plan2 = G.build_plan(w, d, build_backward=True)
+    with pytest.raises(mpb.MPBError) as ei:
+        mpb.flex_attn_bwd(plan2, d["q"], d["k"], d["v"], o, lse, torch.zeros_like(o),
+                          scale=w.scale, workspace=torch.empty(16, dtype=torch.uint8,
+                                                                device="cuda"))
+    assert ei.value.name == "MPB_ERR_WORKSPACE"
+    wf = W.make("tiny_causal")                   # fp32: no backward consumer
+    df = G.device_inputs(wf)
+    pf = G.build_plan(wf, df, build_backward=True)
+    of, lf = G.run_attention(wf, df, pf)
+    with pytest.raises(mpb.MPBError) as ei:
+        mpb.flex_attn_bwd(pf, df["q"], df["k"], df["v"], of, lf, torch.zeros_like(of))
+    assert ei.value.name == "MPB_ERR_UNSUPPORTED"
