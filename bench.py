@@ -206,6 +206,9 @@ def main():
                     help="also time the forward with full tiles forced through the masked path")
     ap.add_argument("--dense-reference", action="store_true",
                     help="also time the all-visible forward at the same shape")
+    ap.add_argument("--bwd-iters", type=int, default=20,
+                    help="back-to-back backward launches timed on a plan with the K2Q view "
+                         "(bf16 workloads; 0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="end with plain device copies of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
@@ -382,6 +385,38 @@ def main():
                      "pct_peak": round(100 * fl_all / us_all / 1e6 / peak_all, 2)}
         plan_all.close()
 
+    # backward (not part of the step): a plan with the K2Q view, the forward's
+    # O and LSE, a seeded dO; HIP events around back-to-back launches
+    bwd = None
+    if args.bwd_iters > 0 and w.dtype == W.DTYPE_BF16:
+        pbw = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream,
+                                  build_backward=True)
+        ob, lb = mpb.flex_attn_fwd(pbw, d["q"], d["k"], d["v"], **dict(kw, out=None, lse=None))
+        dout = torch.from_numpy(W.grad_output(w)).to(torch.bfloat16).reshape(d["q"].shape).cuda()
+        dq_b, dk_b, dv_b = (torch.empty_like(d["q"]), torch.empty_like(d["k"]),
+                            torch.empty_like(d["v"]))
+        ws_b = torch.empty(mpb.flex_attn_bwd_workspace_size(pbw), dtype=torch.uint8, device="cuda")
+        kw_b = dict(scale=w.scale, softcap=w.softcap if w.softcap > 0 else None,
+                    alibi_slopes=d["slopes"], alibi_before_softcap=w.alibi_before_softcap,
+                    dq=dq_b, dk=dk_b, dv=dv_b, workspace=ws_b, stream=stream)
+        for _ in range(3):
+            mpb.flex_attn_bwd(pbw, d["q"], d["k"], d["v"], ob, lb, dout, **kw_b)
+        e0.record(stream)
+        for _ in range(args.bwd_iters):
+            mpb.flex_attn_bwd(pbw, d["q"], d["k"], d["v"], ob, lb, dout, **kw_b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_us = e0.elapsed_time(e1) * 1e3 / args.bwd_iters
+        # algorithmic work: five products per visible pair (S, dP, dV, dQ, dK)
+        eff_b = 10.0 * w.head_dim * stats["visible_pairs"]
+        dense_b = 10.0 * w.head_dim * stats["dense_pairs"]
+        bwd = {"us": round(bwd_us, 2), "effective_tflops": round(eff_b / bwd_us / 1e6, 3),
+               "dense_equiv_tflops": round(dense_b / bwd_us / 1e6, 3),
+               "pct_peak_dense_equiv": round(100 * dense_b / bwd_us / 1e6 / PEAK_BF16_TFLOPS, 2),
+               "flops_basis": "10*d per visible pair (S, dP, dV, dQ, dK); the kernels also "
+                              "recompute S and dP in both the dQ and the dK/dV launch"}
+        pbw.close()
+
     if args.copy_calibration_mb > 0:
         # streaming calibration: reads and writes exactly copy_calibration_mb MiB
         src = torch.ones((args.copy_calibration_mb << 20) // 4, dtype=torch.float32, device="cuda")
@@ -441,6 +476,7 @@ def main():
                  "algorithmic_bytes": pb, "gbs_over_stages": round(pb / (gpu_us * 1e-6) / 1e9, 1),
                  **stats},
         "plan_k2q": plan_k2q,
+        "bwd": bwd,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }

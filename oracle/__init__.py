@@ -79,6 +79,11 @@ def _load():
                                           ctypes.c_int, ctypes.c_double, ctypes.c_int, vp,
                                           ctypes.c_int, vp, vp, vp, ctypes.c_int]
         lib.orc_attention_bwd.restype = None
+        lib.orc_attention_bwd_dq_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_double,
+                                                  ctypes.c_int, ctypes.c_double, ctypes.c_int,
+                                                  vp, ctypes.c_int, ctypes.c_int64, vp, vp,
+                                                  ctypes.c_int]
+        lib.orc_attention_bwd_dq_rows.restype = None
         _lib = lib
     return _lib
 
@@ -270,3 +275,25 @@ def attention_bwd(w, dout: np.ndarray, nthreads: Optional[int] = None):
                           int(bool(w.alibi_before_softcap)), _ptr(dq), _ptr(dk), _ptr(dv),
                           nthreads or default_threads())
     return dq, dk, dv
+
+
+def attention_bwd_dq_rows(w, dout: np.ndarray, rows: np.ndarray,
+                          nthreads: Optional[int] = None) -> np.ndarray:
+    """dQ [n, d] of the selected (token, head) rows (same chain rule as
+    attention_bwd, one row at a time)."""
+    lib = _load()
+    p = _problem(w)
+    mf, cq, ck = _i32(w.mask_func), _i32(w.cu_seqlens_q), _i32(w.cu_seqlens_k)
+    q = np.ascontiguousarray(w.q, dtype=np.float32)
+    k = np.ascontiguousarray(w.k, dtype=np.float32)
+    v = np.ascontiguousarray(w.v, dtype=np.float32)
+    do = np.ascontiguousarray(dout, dtype=np.float32)
+    rp = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    slopes = None if w.alibi_slopes is None else np.ascontiguousarray(w.alibi_slopes, np.float32)
+    dq = np.zeros((rp.shape[0], w.head_dim), np.float64)
+    lib.orc_attention_bwd_dq_rows(ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck), _ptr(q),
+                                  _ptr(k), _ptr(v), _ptr(do), float(w.scale),
+                                  int(w.softcap > 0), float(w.softcap), int(slopes is not None),
+                                  _ptr(slopes), int(bool(w.alibi_before_softcap)),
+                                  rp.shape[0], _ptr(rp), _ptr(dq), nthreads or default_threads())
+    return dq

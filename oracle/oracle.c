@@ -781,3 +781,106 @@ void orc_attention_bwd(const orc_problem* p, const int32_t* mf, const int32_t* c
   free(th);
   free(jobs);
 }
+
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float *q, *k, *v, *dout;
+  double scale;
+  const orc_mod* mod;
+  const int64_t* rows;   /* pairs (token, head) */
+  int64_t begin, end;
+  double* dq;            /* [n][d] */
+} bwd_rows_job;
+
+/* dQ of selected rows only: the same per-row chain rule as bwd_worker (a
+ * row's dQ depends on that row alone). */
+static void* bwd_rows_worker(void* arg) {
+  bwd_rows_job* J = (bwd_rows_job*)arg;
+  const orc_problem* p = J->p;
+  int d = p->head_dim;
+  int group = p->heads_q / p->heads_k;
+  int64_t kmax = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)kmax);
+  double* x = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* t = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)kmax);
+  for (int64_t n = J->begin; n < J->end; ++n) {
+    int64_t tok = J->rows[2 * n];
+    int h = (int)J->rows[2 * n + 1];
+    double* dqrow = J->dq + n * d;
+    for (int i = 0; i < d; ++i) dqrow[i] = 0.0;
+    int b = owner_of_token(p, J->cu_q, tok);
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    int64_t ql = tok - q_off;
+    int hm = p->mask_heads == 1 ? 0 : h;
+    int g = h / group;
+    const int32_t* F = J->mf + (int64_t)hm * p->nfunc * p->total_q + tok;
+    orc_expand_row(F, p->total_q, p->nfunc, k_len, vis);
+    const float* qrow = J->q + (tok * p->heads_q + h) * (int64_t)d;
+    const float* dorow = J->dout + (tok * p->heads_q + h) * (int64_t)d;
+    double m = -INFINITY;
+    int any = 0;
+    for (int64_t kk = 0; kk < k_len; ++kk) {
+      if (!vis[kk]) continue;
+      const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+      double dot = 0.0;
+      for (int i = 0; i < d; ++i) dot += (double)qrow[i] * (double)krow[i];
+      x[kk] = J->scale * dot;
+      t[kk] = apply_mod(J->mod, x[kk], h, ql, kk);
+      if (!any || t[kk] > m) m = t[kk];
+      any = 1;
+    }
+    if (!any) continue;
+    double l = 0.0;
+    for (int64_t kk = 0; kk < k_len; ++kk)
+      if (vis[kk]) l += exp(t[kk] - m);
+    double lse = m + log(l);
+    double Dsum = 0.0;
+    for (int64_t kk = 0; kk < k_len; ++kk) {
+      if (!vis[kk]) continue;
+      const float* vrow = J->v + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+      double dot = 0.0;
+      for (int i = 0; i < d; ++i) dot += (double)dorow[i] * (double)vrow[i];
+      dP[kk] = dot;
+      Dsum += exp(t[kk] - lse) * dot;
+    }
+    for (int64_t kk = 0; kk < k_len; ++kk) {
+      if (!vis[kk]) continue;
+      double P = exp(t[kk] - lse);
+      double dX = P * (dP[kk] - Dsum) * mod_slope(J->mod, x[kk], h, ql, kk);
+      const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+      for (int i = 0; i < d; ++i) dqrow[i] += J->scale * dX * (double)krow[i];
+    }
+  }
+  free(vis);
+  free(x);
+  free(t);
+  free(dP);
+  return NULL;
+}
+
+/* dQ [n][d] of the n selected (token, head) rows. */
+void orc_attention_bwd_dq_rows(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                               const int32_t* cu_k, const float* q, const float* k,
+                               const float* v, const float* dout, double scale, int softcap_on,
+                               double softcap, int alibi_on, const float* slopes,
+                               int alibi_first, int64_t n, const int64_t* rows, double* dq,
+                               int nthreads) {
+  orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
+  if (nthreads < 1) nthreads = 1;
+  if (n < nthreads) nthreads = n > 0 ? (int)n : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  bwd_rows_job* jobs = (bwd_rows_job*)malloc(sizeof(bwd_rows_job) * nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (bwd_rows_job){p, mf, cu_q, cu_k, q, k, v, dout, scale, &mod, rows,
+                             n * i / nthreads, n * (i + 1) / nthreads, dq};
+    pthread_create(&th[i], NULL, bwd_rows_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+}

@@ -160,3 +160,51 @@ def test_backward_refusals():
     with pytest.raises(mpb.MPBError) as ei:
         mpb.flex_attn_bwd(pf, df["q"], df["k"], df["v"], of, lf, torch.zeros_like(of))
     assert ei.value.name == "MPB_ERR_UNSUPPORTED"
+
+
+def test_backward_full_window_sink():
+    w = W.make("window_sink")
+    _case("bwd_full", name="window_sink")
+    _check(w)
+
+
+@pytest.mark.parametrize("name", ["varlen_doc", "block_sparse", "prefix_softcap"])
+def test_backward_full_sampled_and_sums(name):
+    """Full benchmark shapes: dQ on sampled rows (random rows plus sample and
+    tile edges) against the oracle; dK and dV through identities that hold
+    at any size: summed over a sample's keys, dV of KV head g equals the sum
+    of dO over the sample's rows (of g's Q heads) that see anything (each
+    row's weights sum to 1), and without a score_mod dK sums to zero (each
+    row's softmax gradient sums to zero)."""
+    w = W.make(name)
+    _case("bwd_full", name=name)
+    d = G.device_inputs(w)
+    plan = G.build_plan(w, d, build_backward=True)
+    do = W.grad_output(w)
+    dq, dk, dv = run_backward(w, d, plan, do)
+    assert not (np.isnan(dq).any() or np.isnan(dk).any() or np.isnan(dv).any())
+    rows = G.sample_rows(w, n_random=400, seed=1)
+    ref = oracle.attention_bwd_dq_rows(w, do, rows)
+    got = dq[rows[:, 0], rows[:, 1]]
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(ref - got)))
+    print("  %s dQ sampled max|err|/max|ref| = %.3g" % (name, err / scale), flush=True)
+    assert err <= NORM_TOL * scale
+    # rows that see anything: those with a finite LSE in the forward
+    _, lse = G.run_attention(w, d, plan)
+    torch.cuda.synchronize()
+    seen = np.isfinite(lse.cpu().numpy()).T          # [total_q, Hq]
+    grp = w.heads_q // w.heads_k
+    for b in range(w.batch):
+        qo, ql, ko, kl = w.sample_bounds(b)
+        if kl == 0:
+            continue
+        for g in range(w.heads_k):
+            hs = slice(g * grp, (g + 1) * grp)
+            want = (do[qo:qo + ql, hs].astype(np.float64) * seen[qo:qo + ql, hs, None]).sum(axis=(0, 1))
+            have = dv[ko:ko + kl, g].sum(axis=0)
+            bound = 1e-2 * np.abs(dv[ko:ko + kl, g]).sum(axis=0) + 1e-6
+            assert np.all(np.abs(have - want) <= bound), (b, g)
+            if w.softcap == 0 and w.alibi_slopes is None:
+                ksum = dk[ko:ko + kl, g].sum(axis=0)
+                assert np.all(np.abs(ksum) <= 1e-2 * np.abs(dk[ko:ko + kl, g]).sum(axis=0) + 1e-6)

@@ -160,3 +160,14 @@ def test_single_visible_key_and_zero_row_sums():
     # summed over the keys of a sample
     for b in range(B):
         np.testing.assert_allclose(dk[b * S:(b + 1) * S].sum(axis=0), 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("variant", ["none", "both_first"])
+def test_selected_dq_rows_match_full_backward(variant):
+    w, do = _tiny(variant)
+    _, _, _ = oracle.attention_bwd(w, do, nthreads=1)
+    dq = oracle.attention_bwd(w, do, nthreads=2)[0]
+    rows = np.array([[t, h] for t in range(w.total_q) for h in range(w.heads_q)][::-1])
+    got = oracle.attention_bwd_dq_rows(w, do, rows, nthreads=3)
+    for n, (t, h) in enumerate(rows):
+        assert np.array_equal(got[n], dq[t, h])
