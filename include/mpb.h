@@ -228,6 +228,13 @@ mpb_status mask_plan_export_k2q(const mpb_plan* plan, int32_t* cu_krows, int32_t
                                 int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
                                 int32_t* f_idx);
 
+/* Copies the K2Q view's launch order to host memory: order[header[4]], the
+ * K rows sorted by descending cost (partial + full Q tiles summed over mask
+ * heads), ties by K row (the backward dK/dV consumer starts the heaviest K
+ * rows first).  MPB_ERR_INVALID_ARGUMENT if the plan was built without the
+ * view.  Synchronises the plan's build stream. */
+mpb_status mask_plan_export_k2q_order(const mpb_plan* plan, int32_t* order);
+
 /* GPU time of each planner stage of a build made with time_stages = 1, in
  * microseconds, from the HIP events around its launches [MPD §4.2-§4.7
  * stages]; us must hold 7 floats: us[0] THD geometry (an empty span for

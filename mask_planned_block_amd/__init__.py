@@ -92,6 +92,7 @@ def _load():
     lib.mask_plan_build_ex.argtypes = [P(Problem), P(BuildOptions), vp, vp, vp, vp, P(vp)]
     lib.mask_plan_export_k2q.argtypes = [vp] + [vp] * 6
     lib.mask_plan_stage_times.argtypes = [vp, vp]
+    lib.mask_plan_export_k2q_order.argtypes = [vp, vp]
     lib.mask_plan_destroy.argtypes = [vp]
     lib.mask_plan_info.argtypes = [vp, P(PlanInfo)]
     lib.mask_plan_export.argtypes = [vp] + [vp] * 9
@@ -111,7 +112,7 @@ def _load():
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
     lib.mpb_version.restype = ctypes.c_int32
     for name in ("mask_plan_build", "mask_plan_build_ex", "mask_plan_destroy", "mask_plan_info",
-                 "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times",
+                 "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times", "mask_plan_export_k2q_order",
                  "mask_plan_export_launch_order",
                  "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
@@ -292,6 +293,9 @@ def mask_plan_export_k2q(plan: MaskPlan) -> dict:
     a["f_idx"] = a["f_idx"][:fn]
     a["p_masks"] = a["p_masks"][:pn * p.tile_k * wq].reshape(pn, p.tile_k, wq)
     a["header"] = np.asarray(list(info.header), np.int64)
+    order = np.zeros(max(krows, 1), np.int32)
+    _check(_lib.mask_plan_export_k2q_order(plan.handle, ctypes.c_void_p(order.ctypes.data)))
+    a["order"] = order[:krows]
     return a
 
 

@@ -31,6 +31,8 @@
 //    atomics and a deterministic result.
 // All products on v_mfma_f32_32x32x16_bf16 (P and dS rounded to bf16),
 // statistics and accumulators in fp32; outputs in bf16.
+#include <type_traits>
+
 #include "mpb_internal.h"
 #include "../../include/mpb.h"
 
@@ -65,14 +67,22 @@ __device__ inline u32x4 bload16(rsrc_t r, uint32_t off) {
 //   A: lane l holds A[l % 32][8 (l / 32) + i], i = 0..7
 //   B: lane l holds B[8 (l / 32) + i][l % 32]
 //   D: lane l holds D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32], v = 0..15
-// A 32-row tile in LDS is row-major with D bf16 per row, its 16-byte chunk c
-// of row r stored at position c ^ (r % (D / 8)).
+// A tile in LDS is row-major with D bf16 per row, its 16-byte chunk c of row
+// r stored at position c ^ swz(r).  Every tile here is read both ways: as
+// rows (8 lanes reading one chunk of 8 consecutive rows) and transposed (16
+// lanes reading two neighbouring chunks of 4 consecutive rows), and
+// swz(r) = 2 ((r / rp) % (CH / 2)), rp = rows per 256 bytes, puts both
+// groups on distinct banks (the forward's K-only swizzle serves one pattern).
+template <int D>
+__device__ constexpr int swz(int r) {
+  constexpr int CH = D / 8, RP = 256 / (2 * D);
+  return 2 * ((r / RP) % (CH / 2));
+}
 
 // 16 bytes of row `row`, logical chunk `c`.
 template <int D>
 __device__ inline bf16x8 lds_chunk(const __bf16* tile, int row, int c) {
-  constexpr int CH = D / 8;
-  return *(const bf16x8*)(tile + row * D + ((c ^ (row % CH)) << 3));
+  return *(const bf16x8*)(tile + row * D + ((c ^ swz<D>(row)) << 3));
 }
 
 // A operand X^T (rows of the LDS tile X are the MFMA k index, its columns the
@@ -82,13 +92,12 @@ __device__ inline bf16x8 lds_chunk(const __bf16* tile, int row, int c) {
 // 0..3: rows kb + 4 (L / 32) + j, slots 4..7: the same + 8).
 template <int D>
 __device__ inline bf16x8 lds_tr_frag(const __bf16* tile, int kb, int db, int lane) {
-  constexpr int CH = D / 8;
   const int r = lane & 15, g2 = (lane >> 4) & 1, kg = lane >> 5;
   const int row = kb + 4 * kg + (r >> 2);
   const int dcol = 32 * db + 16 * g2 + 4 * (r & 3);
   const int c = dcol >> 3, e = dcol & 7;
-  const __bf16* p0 = tile + row * D + (((c ^ (row % CH)) << 3) + e);
-  const __bf16* p1 = tile + (row + 8) * D + (((c ^ ((row + 8) % CH)) << 3) + e);
+  const __bf16* p0 = tile + row * D + (((c ^ swz<D>(row)) << 3) + e);
+  const __bf16* p1 = tile + (row + 8) * D + (((c ^ swz<D>(row + 8)) << 3) + e);
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p0);
   const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p1);
   const v4i16 both[2] = {lo, hi};
@@ -108,7 +117,7 @@ __device__ inline void dma_tile(__bf16* dst, rsrc_t src, uint32_t tile_off, uint
     const int r0 = (c * NWAVES + wave) * RPI;
     const int r = r0 + lane / CH;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src, (lds_vptr)&dst[r0 * D], 16, (int)(tile_off + r * rs + ((lane % CH) ^ (r % CH)) * 16),
+        src, (lds_vptr)&dst[r0 * D], 16, (int)(tile_off + r * rs + ((lane % CH) ^ swz<D>(r)) * 16),
         0, 0, 0);
   }
 }
@@ -215,6 +224,17 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dQ
 
+// Stage index of a double buffer: an int, or a compile-time constant where
+// the loop is unrolled by two.  With one LDS array per stage and compile-time
+// stages, the compiler sees that the loads landing in the next stage cannot
+// alias this stage's reads and does not wait for them.
+using S0 = std::integral_constant<int, 0>;
+using S1 = std::integral_constant<int, 1>;
+template <class St>
+__device__ constexpr auto flip(St) {
+  return std::integral_constant<int, St::value ^ 1>{};
+}
+
 template <int D, int TQ, int TKV, int MOD>
 __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NW = TQ / 32, NKB = TKV / 32, DS = D / 16, DB = D / 32;
@@ -222,6 +242,12 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) __bf16 k_s1[TKV * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_s0[TKV * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_s1[TKV * D];
+  auto kbuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return k_s0; else return k_s1;
+  };
+  auto vbuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return v_s0; else return v_s1;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lq = lane & 31;
 
@@ -253,13 +279,30 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
   auto tile_j = [&](int t) {
     return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
   };
-  auto load_kv = [&](int t, __bf16* kd, __bf16* vd) {
-    const uint32_t off = (uint32_t)tile_j(t) * TKV * kv_rs;
+  auto load_masks = [&](int t, uint32_t (&mw)[NKB]) {
+    if (t < np) {
+      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk];
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
+    }
+  };
+  auto load_kv = [&](int j, __bf16* kd, __bf16* vd) {
+    const uint32_t off = (uint32_t)j * TKV * kv_rs;
     dma_tile<D, TKV, NW>(kd, rk, off, kv_rs, wave, lane);
     dma_tile<D, TKV, NW>(vd, rv, off, kv_rs, wave, lane);
   };
-  if (ntiles > 0) load_kv(0, k_s0, v_s0);
 
+  int j_cur = 0, j_next = 0;
+  uint32_t mw_cur[NKB], mw_next[NKB];
+  if (ntiles > 0) {
+    j_cur = tile_j(0);
+    load_kv(j_cur, k_s0, v_s0);
+    load_masks(0, mw_cur);
+    if (ntiles > 1) j_next = tile_j(1);
+  }
   bf16x8 qf[DS], df[DS];
   load_row_frags<D>(qf, rq, q_row_off, g);
   load_row_frags<D>(df, rdo, q_row_off, g);
@@ -273,79 +316,141 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_dq[db] = f32x16{};
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
-    __bf16* ks = st ? k_s1 : k_s0;
-    __bf16* vs = st ? v_s1 : v_s0;
-    const int j = tile_j(t);
-    uint32_t mw[NKB];
-    if (t < np) {
-      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
-#pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk] >> (4 * g);
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) mw[kk] = 0xFFFFFFFFu;
+  int t = 0;
+  auto step = [&](auto stage) __attribute__((always_inline)) {
+    const auto nx = flip(stage);
+    const __bf16* ks = kbuf(stage);
+    const __bf16* vs = vbuf(stage);
+    const bool more = t + 1 < ntiles;
+    if (more) {
+      load_kv(j_next, kbuf(nx), vbuf(nx));
+      load_masks(t + 1, mw_next);
     }
-    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's tile loads have landed
-    __syncthreads();                 // ... and everyone's
-    if (t + 1 < ntiles) load_kv(t + 1, st ? k_s0 : k_s1, st ? v_s0 : v_s1);
-
+    const int j2 = t + 2 < ntiles ? tile_j(t + 2) : 0;
     // S^T = K Q^T and dP^T = V dO^T: lane holds Q row lq, K rows 8(v/4)+4g+v%4
     f32x16 s_acc[NKB], dp_acc[NKB];
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) s_acc[kk] = dp_acc[kk] = f32x16{};
+    // operand rows read from LDS one k-step ahead of the MFMAs using them
+    bf16x8 ak[2][NKB], av[2][NKB];
 #pragma unroll
-    for (int s = 0; s < DS; ++s)
+    for (int kk = 0; kk < NKB; ++kk) {
+      ak[0][kk] = lds_chunk<D>(ks, 32 * kk + lq, g);
+      av[0][kk] = lds_chunk<D>(vs, 32 * kk + lq, g);
+    }
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const int c = s & 1;
+      if (s + 1 < DS) {
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) {
+          ak[c ^ 1][kk] = lds_chunk<D>(ks, 32 * kk + lq, 2 * (s + 1) + g);
+          av[c ^ 1][kk] = lds_chunk<D>(vs, 32 * kk + lq, 2 * (s + 1) + g);
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) {
-        const bf16x8 a = lds_chunk<D>(ks, 32 * kk + lq, 2 * s + g);
-        const bf16x8 b = lds_chunk<D>(vs, 32 * kk + lq, 2 * s + g);
-        s_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], s_acc[kk], 0, 0, 0);
-        dp_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, df[s], dp_acc[kk], 0, 0, 0);
+        s_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[c][kk], qf[s], s_acc[kk], 0, 0, 0);
+        dp_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c][kk], df[s], dp_acc[kk], 0, 0, 0);
       }
+    }
+    __builtin_amdgcn_s_setprio(0);
     // dS^T in the B operand order of the next product
     bf16x8 dsb[NKB][2];
-    const float kq0 = (float)(j * TKV + 4 * g - qloc);
+    const float kq0 = (float)(j_cur * TKV + 4 * g - qloc);
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk)
+    for (int kk = 0; kk < NKB; ++kk) {
+      const uint32_t mw = mw_cur[kk] >> (4 * g);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int pos = 8 * (v / 4) + v % 4;
-        const bool keep = (mw[kk] >> pos) & 1u;
+        const bool keep = (mw >> pos) & 1u;
         float P, dS;
         weight_and_ds<MOD>(s_acc[kk][v], dp_acc[kk][v], kq0 + (float)(32 * kk + pos), keep, lse2,
                            dqv, p, slope, P, dS);
         dsb[kk][v / 8][v % 8] = (__bf16)dS;
       }
-    // dQ^T += K^T dS^T
+    }
+    // dQ^T += K^T dS^T, transposed operands read one step ahead; consecutive
+    // MFMAs update different accumulators
+    constexpr int NS = 2 * NKB * DB;
+    bf16x8 fk[2];
+    fk[0] = lds_tr_frag<D>(ks, 0, 0, lane);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int x = 0; x < NS; ++x) {
+      const int c = x & 1, db = x % DB, km = x / DB, kk = km / 2, m = km % 2;
+      if (x + 1 < NS) {
+        const int db1 = (x + 1) % DB, km1 = (x + 1) / DB;
+        fk[c ^ 1] = lds_tr_frag<D>(ks, 32 * (km1 / 2) + 16 * (km1 % 2), db1, lane);
+      }
+      acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], dsb[kk][m], acc_dq[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (more) {
 #pragma unroll
-      for (int kk = 0; kk < NKB; ++kk)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-          acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_tr_frag<D>(ks, 32 * kk + 16 * m, db, lane), dsb[kk][m], acc_dq[db], 0, 0, 0);
+      for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
+      j_cur = j_next;
+      j_next = j2;
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next tile have landed
+    __syncthreads();                 // ... and everyone's; this tile's reads are done
+    ++t;
+  };
+  if (ntiles > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    while (t + 1 < ntiles) {
+      step(S0{});
+      step(S1{});
+    }
+    if (t < ntiles) step(S0{});
   }
   store_rows<D>(rdq, q_row_off, acc_dq, p.scale, g);
 }
 
 // ------------------------------------------------------------------ dK, dV
 
+// One workgroup per (KV head, K plan row): wavefront w takes K block
+// w % NKW (32 K rows) and Q half w / NKW of every Q tile, so dK and dV of a K
+// block are summed by two wavefronts and added through LDS at the end.  The
+// Q tiles of all heads of the group (partial list, then full list, per head)
+// stream through a double buffer: item n + 1 (Q, dO, LSE and Dq rows) is
+// fetched straight into LDS while item n is computed.
 template <int D, int TQ, int TKV, int MOD>
-__global__ __launch_bounds__(TKV * 2) void attn_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NWK = TKV / 32, NQB = TQ / 32, DS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 q_s[TQ * D];
-  __shared__ __attribute__((aligned(16))) __bf16 do_s[TQ * D];
-  __shared__ float lse_s[TQ];
-  __shared__ float dq_s[TQ];
+__global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
+  constexpr int NKW = TKV / 32, NW = 2 * NKW, NQB = TQ / 32, QBW = NQB / 2;
+  constexpr int DS = D / 16, DB = D / 32;
+  static_assert(NQB % 2 == 0, "Q tile must split into two halves of whole 32-row blocks");
+  __shared__ __attribute__((aligned(16))) __bf16 q_s0[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 q_s1[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s0[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s1[TQ * D];
+  __shared__ __attribute__((aligned(16))) float lse_s0[TQ];
+  __shared__ __attribute__((aligned(16))) float lse_s1[TQ];
+  __shared__ __attribute__((aligned(16))) float dd_s0[TQ];
+  __shared__ __attribute__((aligned(16))) float dd_s1[TQ];
+  auto qbuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return q_s0; else return q_s1;
+  };
+  auto dobuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return do_s0; else return do_s1;
+  };
+  auto lsebuf = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return lse_s0; else return lse_s1;
+  };
+  auto ddbuf = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return dd_s0; else return dd_s1;
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lq = lane & 31;
+  const int kb = wave % NKW, qh = wave / NKW;
 
-  const int item = blockIdx.x;
-  const int kvh = item / p.krows_total;
-  const int kr = item - kvh * p.krows_total;
+  // K rows in the plan's launch order (heaviest first), all KV heads of a
+  // K row next to each other
+  const int kvh = blockIdx.x % p.heads_k;
+  const int kr = __builtin_amdgcn_readfirstlane(p.k_order[blockIdx.x / p.heads_k]);
   // sample of the K row (largest b with cu_krows[b] <= kr)
   int lo = 0, hi = p.batch - 1;
   while (lo < hi) {
@@ -368,8 +473,76 @@ __global__ __launch_bounds__(TKV * 2) void attn_bwd_dkdv_kernel(BwdParams p) {
   const rsrc_t rdk = make_rsrc((char*)p.dk + kh, (uint32_t)k_len * kv_rs);
   const rsrc_t rdv = make_rsrc((char*)p.dv + kh, (uint32_t)k_len * kv_rs);
 
-  const int kloc = j * TKV + 32 * wave + lq;   // this lane's sample-local K row
+  // Items: (head of the group, Q tile) pairs, per head its partial list then
+  // its full list.  pair >= 0 is the partial pair's payload index.
+  struct Item { int h, i, pair; };
+  auto lists = [&](int hh, int& pb, int& np, int& fb, int& nf) {
+    const int h = kvh * p.group + hh;
+    const int64_t flat = (int64_t)(p.mask_heads == 1 ? 0 : h) * p.krows_total + kr;
+    pb = __builtin_amdgcn_readfirstlane(p.k_p_off[flat]);
+    np = __builtin_amdgcn_readfirstlane(p.k_p_off[flat + 1]) - pb;
+    fb = __builtin_amdgcn_readfirstlane(p.k_f_off[flat]);
+    nf = __builtin_amdgcn_readfirstlane(p.k_f_off[flat + 1]) - fb;
+  };
+  int n_items = 0;
+  for (int hh = 0; hh < p.group; ++hh) {
+    int pb, np, fb, nf;
+    lists(hh, pb, np, fb, nf);
+    n_items += np + nf;
+  }
+  auto item_at = [&](int n) -> Item {
+    for (int hh = 0; hh < p.group; ++hh) {
+      int pb, np, fb, nf;
+      lists(hh, pb, np, fb, nf);
+      const int h = kvh * p.group + hh;
+      if (n < np) return Item{h, __builtin_amdgcn_readfirstlane(p.k_p_idx[pb + n]), pb + n};
+      n -= np;
+      if (n < nf) return Item{h, __builtin_amdgcn_readfirstlane(p.k_f_idx[fb + n]), -1};
+      n -= nf;
+    }
+    return Item{0, 0, -1};
+  };
+  // Q, dO, LSE and Dq rows of an item into one stage (rows past q_len land as
+  // zeros and are never kept: their predicate bits are 0 and tail Q tiles
+  // are never full).
+  auto load_item = [&](const Item& it, __bf16* qd, __bf16* dod, float* ld, float* dd) {
+    const int64_t qh64 = (int64_t)q_off * q_rs + (int64_t)it.h * D * 2;
+    const rsrc_t rq = make_rsrc((const char*)p.q + qh64, (uint32_t)q_len * q_rs);
+    const rsrc_t rdo = make_rsrc((const char*)p.dout + qh64, (uint32_t)q_len * q_rs);
+    const uint32_t off = (uint32_t)it.i * TQ * q_rs;
+    dma_tile<D, TQ, NW>(qd, rq, off, q_rs, wave, lane);
+    dma_tile<D, TQ, NW>(dod, rdo, off, q_rs, wave, lane);
+    const int64_t st = (int64_t)it.h * p.total_q + q_off;
+    if (wave < TQ / 64) {
+      const rsrc_t rl = make_rsrc(p.lse + st, (uint32_t)q_len * 4);
+      const rsrc_t rd = make_rsrc(p.dvec + st, (uint32_t)q_len * 4);
+      const int q = it.i * TQ + 64 * wave + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_vptr)&ld[64 * wave], 4, q * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_vptr)&dd[64 * wave], 4, q * 4, 0, 0, 0);
+    }
+  };
+  auto load_masks = [&](const Item& it, uint32_t (&mw)[QBW]) {
+    if (it.pair >= 0) {
+      const uint32_t* src =
+          p.k_masks + ((int64_t)it.pair * TKV + 32 * kb + lq) * NQB + qh * QBW;
+#pragma unroll
+      for (int w = 0; w < QBW; ++w) mw[w] = src[w];
+    } else {
+#pragma unroll
+      for (int w = 0; w < QBW; ++w) mw[w] = 0xFFFFFFFFu;
+    }
+  };
+
+  const int kloc = j * TKV + 32 * kb + lq;   // this lane's sample-local K row
   const uint32_t k_row_off = (uint32_t)kloc * kv_rs;
+  Item cur = Item{0, 0, -1}, nxt = Item{0, 0, -1};
+  uint32_t mw_cur[QBW], mw_next[QBW];
+  if (n_items > 0) {
+    cur = item_at(0);
+    load_item(cur, q_s0, do_s0, lse_s0, dd_s0);
+    load_masks(cur, mw_cur);
+    if (n_items > 1) nxt = item_at(1);
+  }
   bf16x8 kf[DS], vf[DS];
   load_row_frags<D>(kf, rk, k_row_off, g);
   load_row_frags<D>(vf, rv, k_row_off, g);
@@ -378,82 +551,122 @@ __global__ __launch_bounds__(TKV * 2) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc_dk[db] = acc_dv[db] = f32x16{};
 
-  for (int hh = 0; hh < p.group; ++hh) {
-    const int h = kvh * p.group + hh;
-    const int hm = p.mask_heads == 1 ? 0 : h;
-    const int64_t flat = (int64_t)hm * p.krows_total + kr;
-    const int pb = __builtin_amdgcn_readfirstlane(p.k_p_off[flat]);
-    const int np = __builtin_amdgcn_readfirstlane(p.k_p_off[flat + 1]) - pb;
-    const int fb = __builtin_amdgcn_readfirstlane(p.k_f_off[flat]);
-    const int ntiles = np + __builtin_amdgcn_readfirstlane(p.k_f_off[flat + 1]) - fb;
-    const int64_t qh = (int64_t)q_off * q_rs + (int64_t)h * D * 2;
-    const rsrc_t rq = make_rsrc((const char*)p.q + qh, (uint32_t)q_len * q_rs);
-    const rsrc_t rdo = make_rsrc((const char*)p.dout + qh, (uint32_t)q_len * q_rs);
-    const float slope = head_slope<MOD>(p, h);
-    const int64_t stat = (int64_t)h * p.total_q + q_off;
-
-    for (int t = 0; t < ntiles; ++t) {
-      const int i = __builtin_amdgcn_readfirstlane(t < np ? p.k_p_idx[pb + t]
-                                                          : p.k_f_idx[fb + t - np]);
-      __syncthreads();   // the previous tile's LDS reads are done
-      dma_tile<D, TQ, NWK>(q_s, rq, (uint32_t)i * TQ * q_rs, q_rs, wave, lane);
-      dma_tile<D, TQ, NWK>(do_s, rdo, (uint32_t)i * TQ * q_rs, q_rs, wave, lane);
-      for (int r = tid; r < TQ; r += TKV * 2) {
-        const int q = i * TQ + r;
-        lse_s[r] = q < q_len ? lse_log2(p.lse[stat + q]) : kPosInf;
-        dq_s[r] = q < q_len ? p.dvec[stat + q] : 0.0f;
-      }
-      uint32_t mw[NQB];
-      if (t < np) {
-        const uint32_t* src = p.k_masks + ((int64_t)(pb + t) * TKV + 32 * wave + lq) * NQB;
-#pragma unroll
-        for (int w = 0; w < NQB; ++w) mw[w] = src[w] >> (4 * g);
-      } else {
-#pragma unroll
-        for (int w = 0; w < NQB; ++w) mw[w] = 0xFFFFFFFFu;
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-
-      const float kq0 = (float)(kloc - i * TQ - 4 * g);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        // S = Q K^T and dP = dO V^T: lane holds K row lq, Q rows 32qb+8(v/4)+4g+v%4
-        f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_chunk<D>(q_s, 32 * qb + lq, 2 * s + g),
-                                                          kf[s], s_acc, 0, 0, 0);
-          dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              lds_chunk<D>(do_s, 32 * qb + lq, 2 * s + g), vf[s], dp_acc, 0, 0, 0);
-        }
-        bf16x8 pb8[2], dsb[2];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int pos = 8 * (v / 4) + v % 4;
-          const int qr = 32 * qb + pos + 4 * g;   // tile-local Q row
-          const bool keep = (mw[qb] >> pos) & 1u;
-          float P, dS;
-          weight_and_ds<MOD>(s_acc[v], dp_acc[v], kq0 - (float)(32 * qb + pos), keep, lse_s[qr],
-                             dq_s[qr], p, slope, P, dS);
-          pb8[v / 8][v % 8] = (__bf16)P;
-          dsb[v / 8][v % 8] = (__bf16)dS;
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                lds_tr_frag<D>(do_s, 32 * qb + 16 * m, db, lane), pb8[m], acc_dv[db], 0, 0, 0);
-            acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                lds_tr_frag<D>(q_s, 32 * qb + 16 * m, db, lane), dsb[m], acc_dk[db], 0, 0, 0);
-          }
-      }
+  int n = 0;
+  auto step = [&](auto stage) __attribute__((always_inline)) {
+    const auto nx = flip(stage);
+    const __bf16* qs = qbuf(stage);
+    const __bf16* dos = dobuf(stage);
+    const float* ls = lsebuf(stage);
+    const float* ds = ddbuf(stage);
+    const bool more = n + 1 < n_items;
+    if (more) {
+      load_item(nxt, qbuf(nx), dobuf(nx), lsebuf(nx), ddbuf(nx));
+      load_masks(nxt, mw_next);
     }
+    const float slope = head_slope<MOD>(p, cur.h);
+    const float kq0 = (float)(kloc - cur.i * TQ - 4 * g);
+#pragma unroll
+    for (int w = 0; w < QBW; ++w) {
+      const int qb = qh * QBW + w;
+      // S = Q K^T and dP = dO V^T: lane holds K row lq, Q rows 32qb+8(v/4)+4g+v%4
+      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      // operand rows read from LDS one k-step ahead of the MFMAs using them
+      bf16x8 aq[2], ad[2];
+      aq[0] = lds_chunk<D>(qs, 32 * qb + lq, g);
+      ad[0] = lds_chunk<D>(dos, 32 * qb + lq, g);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const int c = s & 1;
+        if (s + 1 < DS) {
+          aq[c ^ 1] = lds_chunk<D>(qs, 32 * qb + lq, 2 * (s + 1) + g);
+          ad[c ^ 1] = lds_chunk<D>(dos, 32 * qb + lq, 2 * (s + 1) + g);
+        }
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[c], kf[s], s_acc, 0, 0, 0);
+        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[c], vf[s], dp_acc, 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const uint32_t mw = mw_cur[w] >> (4 * g);
+      bf16x8 pb8[2], dsb[2];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int pos = 8 * (v / 4) + v % 4;
+        const int qr = 32 * qb + pos + 4 * g;   // tile-local Q row
+        const bool keep = (mw >> pos) & 1u;
+        float P, dS;
+        weight_and_ds<MOD>(s_acc[v], dp_acc[v], kq0 - (float)(32 * qb + pos), keep,
+                           lse_log2(ls[qr]), ds[qr], p, slope, P, dS);
+        pb8[v / 8][v % 8] = (__bf16)P;
+        dsb[v / 8][v % 8] = (__bf16)dS;
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS, transposed operands read one
+      // step ahead; consecutive MFMAs update different accumulators
+      constexpr int NS = 2 * DB;
+      bf16x8 fd[2], fq[2];
+      fd[0] = lds_tr_frag<D>(dos, 32 * qb, 0, lane);
+      fq[0] = lds_tr_frag<D>(qs, 32 * qb, 0, lane);
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int x = 0; x < NS; ++x) {
+        const int c = x & 1, m = x / DB, db = x % DB;
+        if (x + 1 < NS) {
+          const int m1 = (x + 1) / DB, db1 = (x + 1) % DB;
+          fd[c ^ 1] = lds_tr_frag<D>(dos, 32 * qb + 16 * m1, db1, lane);
+          fq[c ^ 1] = lds_tr_frag<D>(qs, 32 * qb + 16 * m1, db1, lane);
+        }
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], pb8[m], acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], dsb[m], acc_dk[db], 0, 0, 0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    if (more) {
+#pragma unroll
+      for (int w = 0; w < QBW; ++w) mw_cur[w] = mw_next[w];
+      cur = nxt;
+      if (n + 2 < n_items) nxt = item_at(n + 2);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next item have landed
+    __syncthreads();                 // ... and everyone's; this item's reads are done
+    ++n;
+  };
+  if (n_items > 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    while (n + 1 < n_items) {
+      step(S0{});
+      step(S1{});
+    }
+    if (n < n_items) step(S0{});
   }
-  store_rows<D>(rdk, k_row_off, acc_dk, p.scale, g);
-  store_rows<D>(rdv, k_row_off, acc_dv, 1.0f, g);
+
+  // The two Q halves of each K block: the upper half's wavefronts hand their
+  // sums over through LDS (the Q buffers, free now), the lower half adds and
+  // stores.
+  // K block kb uses stage kb's Q buffer for dK and its dO buffer for dV.
+  static_assert(NKW <= 2 && DB * 16 * 64 * 4 <= TQ * D * 2, "reduction buffer");
+  float* red = reinterpret_cast<float*>(kb == 0 ? q_s0 : q_s1);
+  float* red_v = reinterpret_cast<float*>(kb == 0 ? do_s0 : do_s1);
+  if (qh == 1) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        red[(db * 16 + v) * 64 + lane] = acc_dk[db][v];
+        red_v[(db * 16 + v) * 64 + lane] = acc_dv[db][v];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc_dk[db][v] += red[(db * 16 + v) * 64 + lane];
+        acc_dv[db][v] += red_v[(db * 16 + v) * 64 + lane];
+      }
+    store_rows<D>(rdk, k_row_off, acc_dk, p.scale, g);
+    store_rows<D>(rdv, k_row_off, acc_dv, 1.0f, g);
+  }
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -468,7 +681,7 @@ hipError_t launch_bwd_mod(int num_tasks, const BwdParams& p, hipStream_t s) {
   const int64_t items = (int64_t)p.heads_k * p.krows_total;
   if (items > 0)
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, TQ, TKV, MOD>), dim3((unsigned)items),
-                       dim3(TKV * 2), 0, s, p);
+                       dim3(TKV * 4), 0, s, p);
   return hipGetLastError();
 }
 

@@ -96,6 +96,7 @@ struct K2QDev {
   int32_t* p_idx;      // sample-local Q tiles, ascending per K row
   int32_t* f_idx;
   uint32_t* p_masks;   // [pnnz][tile_k][tile_q/32]
+  int32_t* order;      // [krows] K rows by descending cost over mask heads (launch order)
 };
 struct K2QWork {
   int32_t* pcnt;       // [Hmask][B][nk_max] (padded by sample)
@@ -104,7 +105,12 @@ struct K2QWork {
   int32_t* p_off;      // [Hmask*B*nk_max+1] compact exclusive offsets
   int32_t* f_off;
   int32_t* info;       // [4]: K rows total, partial nnz, full nnz, 0
+  int32_t* order;      // [B*nk_max] launch order staged for the plan
+  int32_t max_cost;    // upper bound of a K row's cost (mask heads x Q tiles of a sample)
 };
+// Costs up to this bound are sorted in LDS; above it the K rows keep their
+// natural order (any permutation is a valid launch order).
+constexpr int kK2QOrderBuckets = 4096;
 constexpr int kHeaderSeq2 = 9;   // host slot index of the K2Q header's sequence number
 
 // ---- planner launchers (plan_kernels.hip) ----
@@ -206,6 +212,7 @@ struct BwdParams {
   const int32_t* k_p_idx;
   const int32_t* k_f_idx;
   const uint32_t* k_masks;
+  const int32_t* k_order;    // K2Q launch order of the K rows
   const float* slopes;
   int32_t batch, heads_q, heads_k, group, mask_heads, total_q, krows_total;
   float scale;

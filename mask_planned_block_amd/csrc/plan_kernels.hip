@@ -1270,6 +1270,7 @@ __global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev 
   __shared__ int s_last;
   __shared__ int s_wp[4], s_wf[4];
   __shared__ int s_cu[1025];
+  __shared__ int s_hist[kK2QOrderBuckets];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t items = (int64_t)g.mask_heads * g.batch * g.words_k;
   const int64_t item = (int64_t)blockIdx.x * 4 + wv;
@@ -1383,6 +1384,58 @@ __global__ __launch_bounds__(256) void plan_k2q_count_kernel(PlanGeo g, PlanDev 
   });
   carry_p = tot_p;
   carry_f = tot_f;
+
+  // Launch order of the K rows for a backward consumer: descending cost
+  // summed over mask heads (partial + full Q tiles), ties by K row, by a
+  // counting sort (histogram in LDS, then one wavefront places the rows in
+  // order, ranking equal keys by one ballot per key bit).  Heavy K rows then
+  // start first instead of forming the tail of the grid.
+  auto cost = [&](int k) -> int {
+    int b2 = sample_of_row(cu, g.batch, k);
+    const int jj = k - cu[b2];
+    int c = 0;
+    for (int hm = 0; hm < g.mask_heads; ++hm) {
+      const int64_t src = ((int64_t)hm * g.batch + b2) * g.nk_max + jj;
+      c += kw.pcnt[src] + kw.fcnt[src];
+    }
+    return c;
+  };
+  const int maxc = kw.max_cost;
+  if (maxc < kK2QOrderBuckets) {
+    for (int x = tid; x <= maxc; x += 256) s_hist[x] = 0;
+    __syncthreads();
+    for (int k = tid; k < krows; k += 256) atomicAdd(&s_hist[maxc - min(cost(k), maxc)], 1);
+    __syncthreads();
+    if (wv == 0) {
+      int run = 0;
+      for (int x0 = 0; x0 <= maxc; x0 += 64) {
+        const int x = x0 + lane;
+        const int v = x <= maxc ? s_hist[x] : 0;
+        const int inc = wave_incl_scan(v, lane);
+        if (x <= maxc) s_hist[x] = run + inc - v;
+        run += __builtin_amdgcn_readlane(inc, 63);
+      }
+      const uint64_t below = lanes_below(lane);
+      for (int k0 = 0; k0 < krows; k0 += 64) {
+        const int k = k0 + lane;
+        const bool valid = k < krows;
+        const int key = valid ? maxc - min(cost(k), maxc) : 0;
+        uint64_t same = __ballot(valid);
+        for (int bit = 0; (1 << bit) <= maxc; ++bit) {
+          const uint64_t ones = __ballot(valid && ((key >> bit) & 1));
+          same &= ((key >> bit) & 1) ? ones : ~ones;
+        }
+        const int pos = valid ? s_hist[key] + __popcll(same & below) : 0;
+        const bool leader = valid && (same & below) == 0;
+        if (valid) kw.order[pos] = k;
+        __builtin_amdgcn_wave_barrier();
+        if (leader) s_hist[key] += __popcll(same);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+  } else {
+    for (int k = tid; k < krows; k += 256) kw.order[k] = k;
+  }
   if (tid == 0) {
     kw.p_off[n] = carry_p;
     kw.f_off[n] = carry_f;
@@ -1477,6 +1530,7 @@ __global__ __launch_bounds__(256) void plan_k2q_materialize_kernel(
       kd.f_off[n] = kw.f_off[n];
     }
   }
+  if (item < krows_total && threadIdx.x == 0) kd.order[item] = kw.order[item];
   if (item >= n) return;
   const int hm = item / krows_total, kr = item - hm * krows_total;
   int b, j;

@@ -349,7 +349,7 @@ T* at(void* base, size_t off) {
 // header is known).
 struct BlockLayout {
   size_t header, seqdesc, cu_rows, cu_q, cu_k, work_desc, sec, rec, p_off, f_off, p_idx, f_idx,
-      masks, k_cu, k_p_off, k_f_off, k_p_idx, k_f_idx, k_masks, bytes;
+      masks, k_cu, k_p_off, k_f_off, k_p_idx, k_f_idx, k_masks, k_order, bytes;
 };
 // Counts of the backward K2Q view (all zero: none).
 struct K2QCounts {
@@ -384,8 +384,9 @@ BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int
     L.k_p_idx = c.take<int32_t>(kc.pnnz);
     L.k_f_idx = c.take<int32_t>(kc.fnnz);
     L.k_masks = c.take<uint32_t>(kc.pnnz * tk * (tq / 32));
+    L.k_order = c.take<int32_t>(kc.krows);
   } else {
-    L.k_cu = L.k_p_off = L.k_f_off = L.k_p_idx = L.k_f_idx = L.k_masks = 0;
+    L.k_cu = L.k_p_off = L.k_f_off = L.k_p_idx = L.k_f_idx = L.k_masks = L.k_order = 0;
   }
   L.bytes = c.off;
   return L;
@@ -400,6 +401,7 @@ K2QDev bind_k2q(void* block, const BlockLayout& L, bool on) {
   k.p_idx = at<int32_t>(block, L.k_p_idx);
   k.f_idx = at<int32_t>(block, L.k_f_idx);
   k.p_masks = at<uint32_t>(block, L.k_masks);
+  k.order = at<int32_t>(block, L.k_order);
   return k;
 }
 PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
@@ -623,6 +625,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const size_t o_kpo = cw.take<int32_t>(bwd ? kpad + 1 : 0);
   const size_t o_kfo = cw.take<int32_t>(bwd ? kpad + 1 : 0);
   const size_t o_kin = cw.take<int32_t>(4);
+  const size_t o_kord = cw.take<int32_t>(bwd ? (int64_t)p.batch * nk_max : 0);
   Arena& arena = slot->arena[dev];
   if ((e = arena_acquire(arena, cw.off, s)) != hipSuccess)
     return device_status(e, "planner workspace");
@@ -660,6 +663,13 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   kw.p_off = at<int32_t>(wb, o_kpo);
   kw.f_off = at<int32_t>(wb, o_kfo);
   kw.info = at<int32_t>(wb, o_kin);
+  kw.order = at<int32_t>(wb, o_kord);
+  {
+    // a K row's cost is at most mask_heads x the Q tiles of its sample
+    const int64_t rps_max = ((int64_t)p.seqlen_q + tq - 1) / tq;
+    const int64_t mc = (int64_t)p.mask_heads * rps_max;
+    kw.max_cost = (int32_t)(mc < (int64_t)kK2QOrderBuckets ? mc : (int64_t)kK2QOrderBuckets);
+  }
 
   const int32_t* cq = p.layout == MPB_LAYOUT_THD ? cu_seqlens_q : nullptr;
   const int32_t* ck = p.layout == MPB_LAYOUT_THD ? cu_seqlens_k : nullptr;
@@ -929,6 +939,20 @@ mpb_status mask_plan_export_k2q(const mpb_plan* plan, int32_t* cu_krows, int32_t
   return ok();
 }
 
+mpb_status mask_plan_export_k2q_order(const mpb_plan* plan, int32_t* order) {
+  if (!plan || !order) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or order is NULL");
+  if (!plan->has_k2q) return fail(MPB_ERR_INVALID_ARGUMENT, "the plan has no K2Q view");
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != plan->device) hipSetDevice(plan->device);
+  hipError_t e = hipStreamSynchronize(plan->stream);
+  if (e == hipSuccess && plan->header[4] > 0)
+    e = hipMemcpy(order, plan->kdev.order, (size_t)plan->header[4] * 4, hipMemcpyDeviceToHost);
+  if (cur != plan->device) hipSetDevice(cur);
+  if (e != hipSuccess) return device_status(e, "K2Q order export");
+  return ok();
+}
+
 mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us) {
   if (!plan || !us) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or us is NULL");
   const StageEvents& t = plan->tev;
@@ -1141,6 +1165,7 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
   prm.k_p_idx = plan->kdev.p_idx;
   prm.k_f_idx = plan->kdev.f_idx;
   prm.k_masks = plan->kdev.p_masks;
+  prm.k_order = plan->kdev.order;
   prm.slopes = al ? mod->alibi_slopes : nullptr;
   prm.batch = b.batch;
   prm.heads_q = b.heads_q;

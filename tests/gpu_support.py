@@ -184,3 +184,20 @@ def compare_k2q(gk, ok):
         assert a.shape == b.shape and np.array_equal(a, b), key
     assert gk["p_masks"].shape == ok.p_masks.shape
     assert np.array_equal(gk["p_masks"], ok.p_masks), "K2Q payload words differ"
+
+
+def check_k2q_order(gk, mask_heads):
+    """The K2Q launch order: a permutation of the K rows with non-increasing
+    cost (partial + full Q tiles summed over mask heads), ties by K row."""
+    krows = int(gk["header"][4])
+    order = np.asarray(gk["order"], np.int64)
+    assert order.shape == (krows,) and np.array_equal(np.sort(order), np.arange(krows))
+    po, fo = np.asarray(gk["p_off"], np.int64), np.asarray(gk["f_off"], np.int64)
+    cost = np.zeros(krows, np.int64)
+    for hm in range(mask_heads):
+        sl = slice(hm * krows, (hm + 1) * krows + 1)
+        cost += np.diff(po[sl]) + np.diff(fo[sl])
+    c = cost[order]
+    assert np.all(c[:-1] >= c[1:]), "order not by descending cost"
+    ties = c[:-1] == c[1:]
+    assert np.all(order[:-1][ties] < order[1:][ties]), "ties not by K row"

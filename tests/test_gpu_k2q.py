@@ -34,7 +34,9 @@ def _check_both_views(w, d, tq, tk):
     plan = G.build_plan(w, d, tq, tk, build_backward=True)
     gp = plan.export()
     G.compare_plan(gp, oracle.build_plan(w, tq, tk), with_k2q=True)
-    G.compare_k2q(plan.export_k2q(), oracle.build_k2q(w, tq, tk))
+    gk = plan.export_k2q()
+    G.compare_k2q(gk, oracle.build_k2q(w, tq, tk))
+    G.check_k2q_order(gk, w.mask_heads)
     return plan
 
 
