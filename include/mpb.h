@@ -284,8 +284,9 @@ mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* probl
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t force_partial);
 
-/* Bytes of caller-provided device workspace flex_attn_bwd needs: one fp32
- * per (Q row, head) for dO . O, rounded up to 256. */
+/* Bytes of caller-provided device workspace flex_attn_bwd needs: two fp32
+ * per (Q row, head), dO . O and the LSE in log2 units, each vector rounded
+ * up to 256 bytes. */
 size_t flex_attn_bwd_workspace_size(const mpb_plan* plan);
 
 /* flex_attn_bwd [MPD §6.3, §8; FLEX Eq. 1 and its automatic backward]:

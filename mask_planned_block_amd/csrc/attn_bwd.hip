@@ -184,13 +184,17 @@ __device__ inline float head_slope(const BwdParams& p, int h) {
 // (its weights are then exactly 0) and for rows past the sample.
 __device__ inline float lse_log2(float lse) { return lse == -kPosInf ? kPosInf : lse * kLog2e; }
 
-// Weight and dS of one score element.
-template <int MOD>
-__device__ inline void weight_and_ds(float s, float dp, float kq, bool keep, float lse2, float dq,
-                                     const BwdParams& p, float slope, float& P, float& dS) {
+// Weight and dS of one score element; lse2 is the row's LSE in log2 units
+// (+inf for a row that sees nothing).  Full tiles (MASKED = false) keep
+// every element.
+template <int MOD, bool MASKED>
+__device__ inline void weight_and_ds(float s, float dp, float kq, uint32_t mw, int pos,
+                                     float lse2, float dq, const BwdParams& p, float slope,
+                                     float& P, float& dS) {
   float grad;
   const float t = mod_fwd_bwd<MOD>(s, kq, p, slope, grad);
-  P = keep ? exp2_fast(t - lse2) : 0.0f;
+  P = exp2_fast(t - lse2);
+  if constexpr (MASKED) P = ((mw >> pos) & 1u) ? P : 0.0f;
   dS = P * (dp - dq) * grad;
 }
 
@@ -198,7 +202,9 @@ __device__ inline void weight_and_ds(float s, float dp, float kq, bool keep, flo
 
 // ------------------------------------------------------------------ Dq
 
-// Dq[h][t] = dO[t][h] . O[t][h] in fp32; D / 8 lanes per (token, head) row.
+// Dq[h][t] = dO[t][h] . O[t][h] in fp32, and the row's LSE in log2 units
+// (+inf for a row that sees nothing, whose weights are then exactly 0);
+// D / 8 lanes per (token, head) row.
 template <int D>
 __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(BwdParams p) {
   constexpr int L = D / 8;
@@ -218,7 +224,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(BwdParams p) {
   if (row < rows && part == 0) {
     const int64_t t = row / p.heads_q;
     const int h = (int)(row % p.heads_q);
-    p.dvec[(int64_t)h * p.total_q + t] = s;
+    const int64_t x = (int64_t)h * p.total_q + t;
+    p.dvec[x] = s;
+    p.lse2[x] = lse_log2(p.lse[x]);
   }
 }
 
@@ -236,7 +244,8 @@ __device__ constexpr auto flip(St) {
 }
 
 template <int D, int TQ, int TKV, int MOD>
-__global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(TQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dq_kernel(BwdParams p) {
   constexpr int NW = TQ / 32, NKB = TKV / 32, DS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) __bf16 k_s0[TKV * D];
   __shared__ __attribute__((aligned(16))) __bf16 k_s1[TKV * D];
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
   load_row_frags<D>(df, rdo, q_row_off, g);
   const bool row_in = qloc < q_len;
   const int64_t stat = (int64_t)h * p.total_q + q_off + qloc;
-  const float lse2 = row_in ? lse_log2(p.lse[stat]) : kPosInf;
+  const float lse2 = row_in ? p.lse2[stat] : kPosInf;
   const float dqv = row_in ? p.dvec[stat] : 0.0f;
   const float slope = head_slope<MOD>(p, h);
 
@@ -317,7 +326,11 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < DB; ++db) acc_dq[db] = f32x16{};
 
   int t = 0;
-  auto step = [&](auto stage) __attribute__((always_inline)) {
+  // One K tile: per 32-row K block kk, S^T = K Q^T and dP^T = V dO^T on MFMA
+  // (lane holds Q row lq, K rows 32kk+8(v/4)+4g+v%4), the weights and dS^T
+  // on the VALU, then dQ^T += K^T dS^T (K^T read transposed from LDS).
+  auto step = [&](auto masked, auto stage) __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked)::value;
     const auto nx = flip(stage);
     const __bf16* ks = kbuf(stage);
     const __bf16* vs = vbuf(stage);
@@ -327,67 +340,45 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
       load_masks(t + 1, mw_next);
     }
     const int j2 = t + 2 < ntiles ? tile_j(t + 2) : 0;
-    // S^T = K Q^T and dP^T = V dO^T: lane holds Q row lq, K rows 8(v/4)+4g+v%4
-    f32x16 s_acc[NKB], dp_acc[NKB];
-#pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) s_acc[kk] = dp_acc[kk] = f32x16{};
-    // operand rows read from LDS one k-step ahead of the MFMAs using them
-    bf16x8 ak[2][NKB], av[2][NKB];
-#pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) {
-      ak[0][kk] = lds_chunk<D>(ks, 32 * kk + lq, g);
-      av[0][kk] = lds_chunk<D>(vs, 32 * kk + lq, g);
-    }
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      const int c = s & 1;
-      if (s + 1 < DS) {
-#pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) {
-          ak[c ^ 1][kk] = lds_chunk<D>(ks, 32 * kk + lq, 2 * (s + 1) + g);
-          av[c ^ 1][kk] = lds_chunk<D>(vs, 32 * kk + lq, 2 * (s + 1) + g);
-        }
-      }
-#pragma unroll
-      for (int kk = 0; kk < NKB; ++kk) {
-        s_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[c][kk], qf[s], s_acc[kk], 0, 0, 0);
-        dp_acc[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c][kk], df[s], dp_acc[kk], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // dS^T in the B operand order of the next product
-    bf16x8 dsb[NKB][2];
     const float kq0 = (float)(j_cur * TKV + 4 * g - qloc);
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
+      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      // operand rows read from LDS one k-step ahead of the MFMAs using them
+      bf16x8 ak[2], av[2];
+      ak[0] = lds_chunk<D>(ks, 32 * kk + lq, g);
+      av[0] = lds_chunk<D>(vs, 32 * kk + lq, g);
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const int c = s & 1;
+        if (s + 1 < DS) {
+          ak[c ^ 1] = lds_chunk<D>(ks, 32 * kk + lq, 2 * (s + 1) + g);
+          av[c ^ 1] = lds_chunk<D>(vs, 32 * kk + lq, 2 * (s + 1) + g);
+        }
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[c], qf[s], s_acc, 0, 0, 0);
+        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c], df[s], dp_acc, 0, 0, 0);
+      }
       const uint32_t mw = mw_cur[kk] >> (4 * g);
+      bf16x8 dsb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int pos = 8 * (v / 4) + v % 4;
-        const bool keep = (mw >> pos) & 1u;
         float P, dS;
-        weight_and_ds<MOD>(s_acc[kk][v], dp_acc[kk][v], kq0 + (float)(32 * kk + pos), keep, lse2,
-                           dqv, p, slope, P, dS);
-        dsb[kk][v / 8][v % 8] = (__bf16)dS;
+        weight_and_ds<MOD, kMasked>(s_acc[v], dp_acc[v], kq0 + (float)(32 * kk + pos), mw, pos,
+                                    lse2, dqv, p, slope, P, dS);
+        dsb[v / 8][v % 8] = (__bf16)dS;
       }
-    }
-    // dQ^T += K^T dS^T, transposed operands read one step ahead; consecutive
-    // MFMAs update different accumulators
-    constexpr int NS = 2 * NKB * DB;
-    bf16x8 fk[2];
-    fk[0] = lds_tr_frag<D>(ks, 0, 0, lane);
-    __builtin_amdgcn_s_setprio(1);
+      // dQ^T += K^T dS^T, transposed operands read one step ahead
+      bf16x8 fk[2];
+      fk[0] = lds_tr_frag<D>(ks, 32 * kk, 0, lane);
 #pragma unroll
-    for (int x = 0; x < NS; ++x) {
-      const int c = x & 1, db = x % DB, km = x / DB, kk = km / 2, m = km % 2;
-      if (x + 1 < NS) {
-        const int db1 = (x + 1) % DB, km1 = (x + 1) / DB;
-        fk[c ^ 1] = lds_tr_frag<D>(ks, 32 * (km1 / 2) + 16 * (km1 % 2), db1, lane);
+      for (int x = 0; x < 2 * DB; ++x) {
+        const int c = x & 1, db = x % DB, m = x / DB;
+        if (x + 1 < 2 * DB)
+          fk[c ^ 1] = lds_tr_frag<D>(ks, 32 * kk + 16 * ((x + 1) / DB), (x + 1) % DB, lane);
+        acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], dsb[m], acc_dq[db], 0, 0, 0);
       }
-      acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], dsb[kk][m], acc_dq[db], 0, 0, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
     if (more) {
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
@@ -398,14 +389,20 @@ __global__ __launch_bounds__(TQ * 2) void attn_bwd_dq_kernel(BwdParams p) {
     __syncthreads();                 // ... and everyone's; this tile's reads are done
     ++t;
   };
+  // partial tiles with their predicate, then full tiles without (§6.3)
+  auto run = [&](auto masked, int t_end) __attribute__((always_inline)) {
+    if (t < t_end && (t & 1)) step(masked, S1{});
+    while (t + 1 < t_end) {
+      step(masked, S0{});
+      step(masked, S1{});
+    }
+    if (t < t_end) step(masked, S0{});
+  };
   if (ntiles > 0) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    while (t + 1 < ntiles) {
-      step(S0{});
-      step(S1{});
-    }
-    if (t < ntiles) step(S0{});
+    run(std::true_type{}, np);
+    run(std::false_type{}, ntiles);
   }
   store_rows<D>(rdq, q_row_off, acc_dq, p.scale, g);
 }
@@ -514,7 +511,7 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
     dma_tile<D, TQ, NW>(dod, rdo, off, q_rs, wave, lane);
     const int64_t st = (int64_t)it.h * p.total_q + q_off;
     if (wave < TQ / 64) {
-      const rsrc_t rl = make_rsrc(p.lse + st, (uint32_t)q_len * 4);
+      const rsrc_t rl = make_rsrc(p.lse2 + st, (uint32_t)q_len * 4);
       const rsrc_t rd = make_rsrc(p.dvec + st, (uint32_t)q_len * 4);
       const int q = it.i * TQ + 64 * wave + lane;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_vptr)&ld[64 * wave], 4, q * 4, 0, 0, 0);
@@ -565,16 +562,21 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
     }
     const float slope = head_slope<MOD>(p, cur.h);
     const float kq0 = (float)(kloc - cur.i * TQ - 4 * g);
-#pragma unroll
-    for (int w = 0; w < QBW; ++w) {
+    // Phases per 32-row Q block qb: S = Q K^T and dP = dO V^T on MFMA (lane
+    // holds K row lq, Q rows 32qb+8(v/4)+4g+v%4), the weights and dS on the
+    // VALU, then dV^T += dO^T P and dK^T += Q^T dS on MFMA.  With two blocks
+    // per wavefront they are issued as S(0) S(1) W(0) V(0) W(1) V(1): the
+    // VALU work of one block sits between MFMAs of the other.
+    f32x16 s_acc[QBW], dp_acc[QBW];
+    bf16x8 pb8[QBW][2], dsb[QBW][2];
+    auto scores = [&](int w) __attribute__((always_inline)) {
       const int qb = qh * QBW + w;
-      // S = Q K^T and dP = dO V^T: lane holds K row lq, Q rows 32qb+8(v/4)+4g+v%4
-      f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
+      s_acc[w] = f32x16{};
+      dp_acc[w] = f32x16{};
       // operand rows read from LDS one k-step ahead of the MFMAs using them
       bf16x8 aq[2], ad[2];
       aq[0] = lds_chunk<D>(qs, 32 * qb + lq, g);
       ad[0] = lds_chunk<D>(dos, 32 * qb + lq, g);
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int s = 0; s < DS; ++s) {
         const int c = s & 1;
@@ -582,30 +584,40 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
           aq[c ^ 1] = lds_chunk<D>(qs, 32 * qb + lq, 2 * (s + 1) + g);
           ad[c ^ 1] = lds_chunk<D>(dos, 32 * qb + lq, 2 * (s + 1) + g);
         }
-        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[c], kf[s], s_acc, 0, 0, 0);
-        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[c], vf[s], dp_acc, 0, 0, 0);
+        s_acc[w] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[c], kf[s], s_acc[w], 0, 0, 0);
+        dp_acc[w] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad[c], vf[s], dp_acc[w], 0, 0, 0);
       }
-      __builtin_amdgcn_s_setprio(0);
+    };
+    auto weights = [&](int w, auto masked) __attribute__((always_inline)) {
+      constexpr bool kMasked = decltype(masked)::value;
+      const int qb = qh * QBW + w;
       const uint32_t mw = mw_cur[w] >> (4 * g);
-      bf16x8 pb8[2], dsb[2];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int pos = 8 * (v / 4) + v % 4;
-        const int qr = 32 * qb + pos + 4 * g;   // tile-local Q row
-        const bool keep = (mw >> pos) & 1u;
-        float P, dS;
-        weight_and_ds<MOD>(s_acc[v], dp_acc[v], kq0 - (float)(32 * qb + pos), keep,
-                           lse_log2(ls[qr]), ds[qr], p, slope, P, dS);
-        pb8[v / 8][v % 8] = (__bf16)P;
-        dsb[v / 8][v % 8] = (__bf16)dS;
+      for (int a = 0; a < 4; ++a) {
+        // rows 32qb + 8a + 4g + 0..3 of the LSE and Dq vectors: one 16-byte read each
+        const int q4 = 32 * qb + 8 * a + 4 * g;
+        const float4 l4 = *(const float4*)&ls[q4];
+        const float4 d4 = *(const float4*)&ds[q4];
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int v = 4 * a + c, pos = 8 * a + c;
+          float P, dS;
+          weight_and_ds<MOD, kMasked>(s_acc[w][v], dp_acc[w][v], kq0 - (float)(32 * qb + pos), mw,
+                                      pos, lv[c], dv[c], p, slope, P, dS);
+          pb8[w][v / 8][v % 8] = (__bf16)P;
+          dsb[w][v / 8][v % 8] = (__bf16)dS;
+        }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS, transposed operands read one
-      // step ahead; consecutive MFMAs update different accumulators
+    };
+    auto grads = [&](int w) __attribute__((always_inline)) {
+      const int qb = qh * QBW + w;
+      // transposed operands read one step ahead; consecutive MFMAs update
+      // different accumulators
       constexpr int NS = 2 * DB;
       bf16x8 fd[2], fq[2];
       fd[0] = lds_tr_frag<D>(dos, 32 * qb, 0, lane);
       fq[0] = lds_tr_frag<D>(qs, 32 * qb, 0, lane);
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int x = 0; x < NS; ++x) {
         const int c = x & 1, m = x / DB, db = x % DB;
@@ -614,11 +626,30 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
           fd[c ^ 1] = lds_tr_frag<D>(dos, 32 * qb + 16 * m1, db1, lane);
           fq[c ^ 1] = lds_tr_frag<D>(qs, 32 * qb + 16 * m1, db1, lane);
         }
-        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], pb8[m], acc_dv[db], 0, 0, 0);
-        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], dsb[m], acc_dk[db], 0, 0, 0);
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], pb8[w][m], acc_dv[db], 0, 0, 0);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], dsb[w][m], acc_dk[db], 0, 0, 0);
       }
-      __builtin_amdgcn_s_setprio(0);
-    }
+    };
+    auto item = [&](auto masked) __attribute__((always_inline)) {
+      if constexpr (QBW == 2) {
+        scores(0);
+        scores(1);
+        weights(0, masked);
+        grads(0);
+        weights(1, masked);
+        grads(1);
+      } else {
+#pragma unroll
+        for (int w = 0; w < QBW; ++w) {
+          scores(w);
+          weights(w, masked);
+          grads(w);
+        }
+      }
+    };
+    // (one code path: a full pair's predicate words are all ones; two paths
+    // would not fit the register file together)
+    item(std::true_type{});
     if (more) {
 #pragma unroll
       for (int w = 0; w < QBW; ++w) mw_cur[w] = mw_next[w];

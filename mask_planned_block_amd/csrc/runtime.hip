@@ -1085,10 +1085,15 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   return ok();
 }
 
-size_t flex_attn_bwd_workspace_size(const mpb_plan* plan) {
-  if (!plan) return 0;
+// Two fp32 vectors per (head, Q row): dO . O and the LSE in log2 units.
+static size_t bwd_vec_bytes(const mpb_plan* plan) {
   const size_t bytes = (size_t)plan->prob.heads_q * plan->prob.total_q * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
+}
+
+size_t flex_attn_bwd_workspace_size(const mpb_plan* plan) {
+  if (!plan) return 0;
+  return 2 * bwd_vec_bytes(plan);
 }
 
 mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
@@ -1154,6 +1159,7 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
   prm.dv = dv;
   prm.lse = lse;
   prm.dvec = static_cast<float*>(workspace);
+  prm.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_vec_bytes(plan));
   prm.seqdesc = plan->dev.seqdesc;
   prm.task_rec = plan->dev.task_rec;
   prm.p_idx = plan->dev.p_idx;
