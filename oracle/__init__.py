@@ -75,6 +75,13 @@ def _load():
                                       ctypes.c_double, ctypes.c_int, vp, ctypes.c_int,
                                       ctypes.c_int64, vp, vp, vp, ctypes.c_int]
         lib.orc_attention.restype = None
+        lib.orc_attention_part.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_double,
+                                           ctypes.c_int, ctypes.c_double, ctypes.c_int, vp,
+                                           ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, vp, vp, vp, ctypes.c_int]
+        lib.orc_attention_part.restype = None
+        lib.orc_merge.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
+        lib.orc_merge.restype = None
         lib.orc_attention_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_double,
                                           ctypes.c_int, ctypes.c_double, ctypes.c_int, vp,
                                           ctypes.c_int, vp, vp, vp, ctypes.c_int]
@@ -229,6 +236,19 @@ def attention(w, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = No
     LSE [Hq, total_q].  rows = int array [n, 2] of (token, head): returns O [n, d]
     and LSE [n].
     """
+    return _attention(w, None, rows, nthreads)
+
+
+def attention_part(w, k_lo: int, k_hi: int, rows: Optional[np.ndarray] = None,
+                   nthreads: Optional[int] = None):
+    """Split-K partial state: the attention of attention() with every row's
+    visible keys cut to the sample-local range [k_lo, k_hi) (O normalized over
+    those keys, their LSE; O = 0, LSE = -inf where none is left).  Same
+    return layouts as attention()."""
+    return _attention(w, (int(k_lo), int(k_hi)), rows, nthreads)
+
+
+def _attention(w, krange, rows, nthreads):
     lib = _load()
     p = _problem(w)
     mf, cq, ck = _i32(w.mask_func), _i32(w.cu_seqlens_q), _i32(w.cu_seqlens_k)
@@ -245,10 +265,27 @@ def attention(w, rows: Optional[np.ndarray] = None, nthreads: Optional[int] = No
         n = rp.shape[0]
         o = np.zeros((n, w.head_dim), np.float64)
         lse = np.zeros(n, np.float64)
-    lib.orc_attention(ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck), _ptr(q), _ptr(k), _ptr(v),
-                      float(w.scale), int(w.softcap > 0), float(w.softcap),
-                      int(slopes is not None), _ptr(slopes), int(bool(w.alibi_before_softcap)),
-                      n, _ptr(rp), _ptr(o), _ptr(lse), nthreads or default_threads())
+    common = (ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck), _ptr(q), _ptr(k), _ptr(v),
+              float(w.scale), int(w.softcap > 0), float(w.softcap), int(slopes is not None),
+              _ptr(slopes), int(bool(w.alibi_before_softcap)))
+    tail = (n, _ptr(rp), _ptr(o), _ptr(lse), nthreads or default_threads())
+    if krange is None:
+        lib.orc_attention(*common, *tail)
+    else:
+        lib.orc_attention_part(*common, krange[0], krange[1], *tail)
+    return o, lse
+
+
+def merge(o_parts: np.ndarray, lse_parts: np.ndarray):
+    """Merge of Split-K partial states (orc_merge): o_parts [P, n, d] (each
+    normalized over its keys), lse_parts [P, n] -> (O [n, d], LSE [n])."""
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    P, n, d = o_parts.shape
+    assert lse_parts.shape == (P, n)
+    o = np.zeros((n, d), np.float64)
+    lse = np.zeros(n, np.float64)
+    _load().orc_merge(P, n, d, _ptr(o_parts), _ptr(lse_parts), _ptr(o), _ptr(lse))
     return o, lse
 
 

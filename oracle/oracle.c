@@ -30,6 +30,10 @@
  *                 rows with nothing visible give O = 0 and LSE = -inf (mask
  *                 plan design §6.1).  LSE is the natural log of the sum of
  *                 exp(score) over visible keys, scores after score_mod.
+ *   - Split-K   : Tessera page, "Split-K" (Figure 5): attention restricted to
+ *                 a K range gives a partial state (normalized O and LSE of the
+ *                 keys in the range); partial states merge by rescaling to a
+ *                 common maximum (orc_attention_part, orc_merge).
  *   - K2Q view  : §4.4 / §4.7, the same pair classes read K-major, with a
  *                 K-major predicate per partial pair (see orc_k2q_build).
  *   - score_mod : softcap c*tanh(s/c) then ALiBi + slope_h*(k-q) with
@@ -553,6 +557,7 @@ typedef struct {
   double scale;
   const orc_mod* mod;
   const int64_t* rows;   /* pairs (token, head); NULL = all rows */
+  int64_t k_lo, k_hi;    /* only keys with k_lo <= k < k_hi (sample-local) count */
   int64_t begin, end;
   double* o;             /* [n][d] for selected rows; [total_q][Hq][d] for all */
   double* lse;           /* [n] ; [Hq][total_q] for all */
@@ -588,7 +593,7 @@ static void* attn_worker(void* arg) {
     double m = -INFINITY;
     int any = 0;
     for (int64_t kk = 0; kk < k_len; ++kk) {
-      if (!vis[kk]) continue;
+      if (!vis[kk] || kk < J->k_lo || kk >= J->k_hi) continue;
       const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
       double dot = 0.0;
       for (int i = 0; i < d; ++i) dot += (double)qrow[i] * (double)krow[i];
@@ -606,7 +611,7 @@ static void* attn_worker(void* arg) {
     double l = 0.0;
     for (int i = 0; i < d; ++i) acc[i] = 0.0;
     for (int64_t kk = 0; kk < k_len; ++kk) {
-      if (!vis[kk]) continue;
+      if (!vis[kk] || kk < J->k_lo || kk >= J->k_hi) continue;
       double w = exp(s[kk] - m);
       l += w;
       const float* vrow = J->v + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
@@ -621,6 +626,26 @@ static void* attn_worker(void* arg) {
   return NULL;
 }
 
+static void attention_range(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                            const int32_t* cu_k, const float* q, const float* k, const float* v,
+                            double scale, const orc_mod* mod, int64_t k_lo, int64_t k_hi,
+                            int64_t n, const int64_t* rows, double* o, double* lse,
+                            int nthreads) {
+  int64_t total = rows ? n : (int64_t)p->total_q * p->heads_q;
+  if (nthreads < 1) nthreads = 1;
+  if (total < nthreads) nthreads = total > 0 ? (int)total : 1;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  attn_job* jobs = (attn_job*)malloc(sizeof(attn_job) * nthreads);
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = (attn_job){p, mf, cu_q, cu_k, q, k, v, scale, mod, rows, k_lo, k_hi,
+                         total * t / nthreads, total * (t + 1) / nthreads, o, lse};
+    pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+  }
+  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+  free(th);
+  free(jobs);
+}
+
 /* Attention for selected rows (rows = n pairs (token, head)) or for every row
  * (rows = NULL, n ignored).  Inputs are float32 arrays holding the exact input
  * values ([tokens][heads][d]); everything is computed in double. */
@@ -630,19 +655,59 @@ void orc_attention(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
                    const float* slopes, int alibi_first, int64_t n, const int64_t* rows,
                    double* o, double* lse, int nthreads) {
   orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
-  int64_t total = rows ? n : (int64_t)p->total_q * p->heads_q;
-  if (nthreads < 1) nthreads = 1;
-  if (total < nthreads) nthreads = total > 0 ? (int)total : 1;
-  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
-  attn_job* jobs = (attn_job*)malloc(sizeof(attn_job) * nthreads);
-  for (int t = 0; t < nthreads; ++t) {
-    jobs[t] = (attn_job){p, mf, cu_q, cu_k, q, k, v, scale, &mod, rows,
-                         total * t / nthreads, total * (t + 1) / nthreads, o, lse};
-    pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+  attention_range(p, mf, cu_q, cu_k, q, k, v, scale, &mod, 0, INT64_MAX, n, rows, o, lse,
+                  nthreads);
+}
+
+/* Split-K partial state (Tessera page, "Split-K"): the same attention with the
+ * visible set of every row cut to the sample-local keys k_lo <= k < k_hi.
+ * O is normalized over those keys and LSE is the log of their sum of
+ * exp(score); a row with none of its visible keys in the range gets O = 0 and
+ * LSE = -inf.  Layouts as orc_attention. */
+void orc_attention_part(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                        const int32_t* cu_k, const float* q, const float* k, const float* v,
+                        double scale, int softcap_on, double softcap, int alibi_on,
+                        const float* slopes, int alibi_first, int64_t k_lo, int64_t k_hi,
+                        int64_t n, const int64_t* rows, double* o, double* lse, int nthreads) {
+  orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
+  attention_range(p, mf, cu_q, cu_k, q, k, v, scale, &mod, k_lo, k_hi, n, rows, o, lse,
+                  nthreads);
+}
+
+/* Merge of Split-K partial states (Tessera page, "Split-K": partial states are
+ * rescaled to a common maximum, summed and normalized).  Part s of row r has
+ * O_s = o_parts[(s*nrows + r)*d ...] (normalized over its keys) and
+ * L_s = lse_parts[s*nrows + r].  With M = max_s L_s:
+ *   LSE = M + log(sum_s exp(L_s - M)),  O = sum_s exp(L_s - LSE) * O_s.
+ * A part with L_s = -inf holds no keys and is not read; if every part is
+ * empty the row gets O = 0 and LSE = -inf. */
+void orc_merge(int nparts, int64_t nrows, int d, const double* o_parts,
+               const double* lse_parts, double* o, double* lse) {
+  for (int64_t r = 0; r < nrows; ++r) {
+    double m = -INFINITY;
+    for (int s = 0; s < nparts; ++s)
+      if (lse_parts[s * nrows + r] > m) m = lse_parts[s * nrows + r];
+    double* out = o + r * d;
+    for (int i = 0; i < d; ++i) out[i] = 0.0;
+    if (m == -INFINITY) {
+      lse[r] = -INFINITY;
+      continue;
+    }
+    double l = 0.0;
+    for (int s = 0; s < nparts; ++s) {
+      double ls = lse_parts[s * nrows + r];
+      if (ls != -INFINITY) l += exp(ls - m);
+    }
+    double L = m + log(l);
+    for (int s = 0; s < nparts; ++s) {
+      double ls = lse_parts[s * nrows + r];
+      if (ls == -INFINITY) continue;
+      double w = exp(ls - L);
+      const double* os = o_parts + (s * nrows + r) * d;
+      for (int i = 0; i < d; ++i) out[i] += w * os[i];
+    }
+    lse[r] = L;
   }
-  for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
-  free(th);
-  free(jobs);
 }
 
 /* ------------------------------------------------------------ backward */
