@@ -190,6 +190,54 @@ def load_traffic(expected_digest):
         return None
 
 
+def run_splitk(args, mpb, W, torch, np):
+    """Split-K forward on the long-K chunk shape (512 query tokens against a
+    32768-token prefix, 32 Q heads on 8 K/V heads): 128 tasks, fewer than the
+    GPU's resident workgroups.  HIP events around back-to-back launches of the
+    unsplit forward, of the library's split count and of a sweep; effective
+    TFLOP/s = 4*d per visible pair."""
+    w = W.make("chunk_long_kv")
+    d = W.to_device(w)
+    stream = torch.cuda.current_stream()
+    prob = mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                            w.total_k, w.heads_q, w.heads_k, w.head_dim, w.mask_heads, w.nfunc,
+                            0, 0)
+    plan = mpb.mask_plan_build(prob, d["mask_func"], None, None, stream=stream)
+    st = plan_stats(w, plan)
+    eff = 4.0 * w.head_dim * st["visible_pairs"]
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
+    auto = mpb.flex_attn_fwd_num_splits(plan)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(sp):
+        ws = None
+        if sp is not None:
+            ws = torch.empty(max(mpb.flex_attn_fwd_splitk_workspace_size(plan, sp), 256),
+                             dtype=torch.uint8, device="cuda")
+        call = lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], scale=w.scale, out=out,
+                                         lse=lse, workspace=ws, stream=stream, num_splits=sp)
+        for _ in range(3):
+            call()
+        e0.record(stream)
+        for _ in range(args.splitk_iters):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / args.splitk_iters
+        return {"us": round(us, 2), "effective_tflops": round(eff / us / 1e6, 2)}
+
+    res = {"workload": "chunk_long_kv", "tasks": st["tasks"], "library_splits": auto,
+           "unsplit": timed(None), "library_choice": timed(0),
+           "sweep": {str(sp): timed(sp) for sp in (2, 4, 8, 16, 32)},
+           "effective_gflop": round(eff / 1e9, 3),
+           "basis": "HIP events around %d back-to-back launches (split launch + merge)"
+                    % args.splitk_iters}
+    res["speedup_library_choice"] = round(res["unsplit"]["us"] / res["library_choice"]["us"], 3)
+    plan.close()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +257,12 @@ def main():
     ap.add_argument("--bwd-iters", type=int, default=20,
                     help="back-to-back backward launches timed on a plan with the K2Q view "
                          "(bf16 workloads; 0 = skip)")
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="run the step's forward as the Split-K forward with this many parts "
+                         "(0 = the library's choice)")
+    ap.add_argument("--splitk-iters", type=int, default=20,
+                    help="back-to-back launches per Split-K configuration timed on the long-K "
+                         "chunk shape (0 = skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="end with plain device copies of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
@@ -244,6 +298,12 @@ def main():
     kw = dict(scale=w.scale, softcap=w.softcap if w.softcap > 0 else None,
               alibi_slopes=d["slopes"], alibi_before_softcap=w.alibi_before_softcap,
               out=out, lse=lse, workspace=ws, stream=stream)
+    if args.num_splits is not None:
+        p0 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        kw["num_splits"] = args.num_splits
+        kw["workspace"] = torch.empty(max(mpb.flex_attn_fwd_splitk_workspace_size(
+            p0, args.num_splits), 256), dtype=torch.uint8, device="cuda")
+        p0.close()
 
     def step():
         plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
@@ -417,6 +477,8 @@ def main():
                               "recompute S and dP in both the dQ and the dK/dV launch"}
         pbw.close()
 
+    splitk = run_splitk(args, mpb, W, torch, np) if args.splitk_iters > 0 else None
+
     if args.copy_calibration_mb > 0:
         # streaming calibration: reads and writes exactly copy_calibration_mb MiB
         src = torch.ones((args.copy_calibration_mb << 20) // 4, dtype=torch.float32, device="cuda")
@@ -477,6 +539,7 @@ def main():
                  **stats},
         "plan_k2q": plan_k2q,
         "bwd": bwd,
+        "splitk": splitk,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }

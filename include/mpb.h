@@ -284,6 +284,56 @@ mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* probl
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t force_partial);
 
+/* Split-K forward [TESS "Split-K", Figure 5; MPD §6.1]: for plans with too
+ * few tasks to fill the GPU (short Q against a long K, few heads or
+ * samples), every task's tile list (partial tiles, then full tiles, n of
+ * them) is cut into num_splits contiguous parts; part s covers list
+ * positions [s*n/S, (s+1)*n/S) and runs in its own workgroup, writing the
+ * softmax output normalized over its tiles (fp32) and their log-sum-exp to
+ * the workspace; a merge kernel then rescales the parts to a common maximum,
+ * sums and normalizes them into o and lse (flex_attn_fwd_merge).  Results
+ * equal flex_attn_fwd's up to fp32 rounding order; o is rounded to its
+ * dtype once, after the merge.
+ *
+ * flex_attn_fwd_num_splits: the library's choice for a plan: 1 when the
+ * plan has at least as many tasks as the GPU holds resident workgroups,
+ * else enough parts to fill it, with at least four tiles per part on
+ * average, at most 64.
+ * flex_attn_fwd_splitk_workspace_size: bytes needed for num_splits parts
+ * (0 = the library's choice): per part, fp32 O [total_q][heads_q][head_dim]
+ * and fp32 LSE [heads_q][total_q], each area rounded up to 256 bytes; 0 when
+ * the resolved split count is 1.
+ * flex_attn_fwd_splitk: arguments as flex_attn_fwd, plus num_splits in
+ * [0, 64] (0 = library's choice; 1 = flex_attn_fwd itself).  With more than
+ * one part the workspace must be 256-byte aligned and o 16-byte aligned.
+ * Enqueues the split launch and the merge launch on `stream`; the
+ * workspace is in use until the merge has run.  Errors as flex_attn_fwd,
+ * MPB_ERR_INVALID_ARGUMENT for num_splits out of range. */
+int32_t flex_attn_fwd_num_splits(const mpb_plan* plan);
+size_t flex_attn_fwd_splitk_workspace_size(const mpb_plan* plan, int32_t num_splits);
+mpb_status flex_attn_fwd_splitk(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                                const void* k, const void* v, void* o, float* lse, float scale,
+                                const mpb_score_mod* mod, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/* flex_attn_fwd_merge [TESS "Split-K"]: merges num_parts partial attention
+ * states of the same rows, e.g. the parts of a Split-K forward or the
+ * outputs of attention over disjoint key ranges.  Row r = token*heads_q + h.
+ *   o_parts   device fp32 [num_parts][total_q][heads_q][head_dim], part s's
+ *             output normalized over its own keys (16-byte aligned).
+ *   lse_parts device fp32 [num_parts][heads_q][total_q], part s's natural
+ *             log-sum-exp; -inf = the part holds no key of the row (its O
+ *             is then not read).  Finite or -inf values only.
+ *   o         device [total_q][heads_q][head_dim] in dtype (bf16 or fp32),
+ *             16-byte aligned:  O = sum_s exp(L_s - LSE) O_s.
+ *   lse       device fp32 [heads_q][total_q]:  LSE = M + ln sum_s exp(L_s - M),
+ *             M = max_s L_s.  A row whose parts are all empty gets O = 0,
+ *             LSE = -inf.
+ * head_dim 64 or 128 (else MPB_ERR_UNSUPPORTED).  Enqueue only. */
+mpb_status flex_attn_fwd_merge(int32_t num_parts, int32_t total_q, int32_t heads_q,
+                               int32_t head_dim, int32_t dtype, const float* o_parts,
+                               const float* lse_parts, void* o, float* lse, void* stream);
+
 /* Bytes of caller-provided device workspace flex_attn_bwd needs: two fp32
  * per (Q row, head), dO . O and the LSE in log2 units, each vector rounded
  * up to 256 bytes. */

@@ -20,7 +20,9 @@ import torch
 __all__ = [
     "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "MPBError", "Problem", "MaskPlan",
     "make_problem", "mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
-    "flex_attn_fwd", "flex_attn_fwd_workspace_size", "library_path", "TASK_REC_FIELDS",
+    "flex_attn_fwd", "flex_attn_fwd_workspace_size", "flex_attn_fwd_num_splits",
+    "flex_attn_fwd_splitk_workspace_size", "flex_attn_fwd_merge", "flex_attn_bwd",
+    "flex_attn_bwd_workspace_size", "library_path", "TASK_REC_FIELDS",
 ]
 
 LAYOUT_BSHD = 0
@@ -103,6 +105,12 @@ def _load():
                 ctypes.c_size_t, vp]
     lib.flex_attn_fwd.argtypes = fwd_args
     lib.flex_attn_fwd_ablation.argtypes = fwd_args + [ctypes.c_int32]
+    lib.flex_attn_fwd_num_splits.argtypes = [vp]
+    lib.flex_attn_fwd_num_splits.restype = ctypes.c_int32
+    lib.flex_attn_fwd_splitk_workspace_size.argtypes = [vp, ctypes.c_int32]
+    lib.flex_attn_fwd_splitk_workspace_size.restype = ctypes.c_size_t
+    lib.flex_attn_fwd_splitk.argtypes = fwd_args[:9] + [ctypes.c_int32] + fwd_args[9:]
+    lib.flex_attn_fwd_merge.argtypes = [ctypes.c_int32] * 5 + [vp] * 5
     lib.flex_attn_bwd_workspace_size.argtypes = [vp]
     lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
@@ -114,7 +122,8 @@ def _load():
     for name in ("mask_plan_build", "mask_plan_build_ex", "mask_plan_destroy", "mask_plan_info",
                  "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times", "mask_plan_export_k2q_order",
                  "mask_plan_export_launch_order",
-                 "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_bwd"):
+                 "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_fwd_splitk",
+                 "flex_attn_fwd_merge", "flex_attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -336,23 +345,37 @@ def _call_problem(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor) -> Problem:
                    p.mask_heads, p.nfunc, 0, 0)
 
 
+def flex_attn_fwd_num_splits(plan: MaskPlan) -> int:
+    """The library's Split-K part count for this plan (1 = no split)."""
+    return int(_lib.flex_attn_fwd_num_splits(plan.handle))
+
+
+def flex_attn_fwd_splitk_workspace_size(plan: MaskPlan, num_splits: int = 0) -> int:
+    return int(_lib.flex_attn_fwd_splitk_workspace_size(plan.handle, int(num_splits)))
+
+
 def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                   scale: Optional[float] = None, softcap: Optional[float] = None,
                   alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None,
-                  force_partial: bool = False):
+                  force_partial: bool = False, num_splits: Optional[int] = None):
     """Block-sparse attention forward over a plan.  Returns (O, LSE[Hq, total_q]).
 
-    Allocates O/LSE/workspace with torch when not given (device memory only)."""
+    num_splits=None runs flex_attn_fwd; an int runs flex_attn_fwd_splitk with
+    that many parts (0 = the library's choice).  Allocates O/LSE/workspace
+    with torch when not given (device memory only)."""
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
+    if force_partial and num_splits is not None:
+        raise ValueError("force_partial and num_splits are separate entry points")
     prob = _call_problem(plan, q, k)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
-    need = plan.workspace_bytes
+    need = plan.workspace_bytes if num_splits is None else \
+        flex_attn_fwd_splitk_workspace_size(plan, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     mod = None
@@ -362,15 +385,45 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
                        _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
                        1 if alibi_before_softcap else 0)
     sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
-    args = (plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
-            _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
-            ctypes.byref(mod) if mod is not None else None, _dev_ptr(workspace, "workspace"),
+    head = (plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype),
+            _dev_ptr(v, "v", q.dtype), _dev_ptr(out, "out", q.dtype),
+            _dev_ptr(lse, "lse", torch.float32), sc,
+            ctypes.byref(mod) if mod is not None else None)
+    tail = (_dev_ptr(workspace, "workspace"),
             0 if workspace is None else workspace.numel() * workspace.element_size(),
             _stream_handle(stream))
-    if force_partial:
-        _check(_lib.flex_attn_fwd_ablation(*args, 1))
+    if num_splits is not None:
+        _check(_lib.flex_attn_fwd_splitk(*head, int(num_splits), *tail))
+    elif force_partial:
+        _check(_lib.flex_attn_fwd_ablation(*head, *tail, 1))
     else:
-        _check(_lib.flex_attn_fwd(*args))
+        _check(_lib.flex_attn_fwd(*head, *tail))
+    return out, lse
+
+
+def flex_attn_fwd_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        out_dtype=torch.bfloat16, stream=None):
+    """Merges partial attention states (see include/mpb.h, flex_attn_fwd_merge).
+
+    o_parts: fp32 [P, total_q, Hq, D] (each part normalized over its keys);
+    lse_parts: fp32 [P, Hq, total_q].  Returns (O [total_q, Hq, D] in
+    out_dtype, LSE [Hq, total_q])."""
+    if o_parts.dim() != 4 or lse_parts.dim() != 3:
+        raise ValueError("o_parts must be [P, T, H, D] and lse_parts [P, H, T]")
+    P, T, H, D = o_parts.shape
+    if tuple(lse_parts.shape) != (P, H, T):
+        raise ValueError("lse_parts must be [P, H, T] = %s" % ((P, H, T),))
+    if out is None:
+        out = torch.empty((T, H, D), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=o_parts.device)
+    dt = DTYPE_BF16 if out.dtype == torch.bfloat16 else (DTYPE_FP32 if out.dtype == torch.float32
+                                                        else -1)
+    _check(_lib.flex_attn_fwd_merge(P, T, H, D, dt, _dev_ptr(o_parts, "o_parts", torch.float32),
+                                    _dev_ptr(lse_parts, "lse_parts", torch.float32),
+                                    _dev_ptr(out, "out"), _dev_ptr(lse, "lse", torch.float32),
+                                    _stream_handle(stream)))
     return out, lse
 
 

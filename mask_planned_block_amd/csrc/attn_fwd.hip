@@ -506,8 +506,29 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
   __builtin_amdgcn_s_setprio(0);
 }
 
+// Normalized fp32 O of one 32-row block (a Split-K partial state): lane
+// stores four consecutive columns per 32-column group, as store_o does.
+template <int D>
+__device__ inline void store_o_f32(rsrc_t ro, uint32_t row_off, const f32x16 (&o)[D / 32],
+                                   float inv, int b2) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      f32x4 v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = o[db][4 * a + c] * inv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro,
+                                             (int)(row_off + (db * 32 + 8 * a + 4 * b2) * 4), 0,
+                                             0);
+    }
+}
+
 // One workgroup per task, in the plan's launch order (record blockIdx.x).
-template <class Ops, int MOD>
+// SPLIT: one workgroup per (split, task), the splits of the Tessera page's
+// Split-K: workgroup i runs split i / tasks_padded of task i % tasks_padded
+// over a contiguous part of the task's tile list and writes its partial state.
+template <class Ops, int MOD, bool SPLIT>
 __global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(Ops::WPE, Ops::WPE)))
 void attn_fwd_kernel(AttnParams p) {
   constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
@@ -544,19 +565,39 @@ void attn_fwd_kernel(AttnParams p) {
   const int b2 = lane >> 5;
   const int lq = lane & 31;
 
-  const int32_t* rec = p.task_rec + (int64_t)blockIdx.x * kTaskRecInts;
+  int task = blockIdx.x, split = 0;
+  if constexpr (SPLIT) {
+    split = blockIdx.x / p.tasks_padded;
+    task = blockIdx.x - split * p.tasks_padded;
+    if (task >= p.num_tasks) return;   // padding of the last task row (whole workgroup)
+  }
+  const int32_t* rec = p.task_rec + (int64_t)task * kTaskRecInts;
   const int m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);
   const int h = __builtin_amdgcn_readfirstlane(rec[kRecHead]);
   const int q_off = __builtin_amdgcn_readfirstlane(rec[kRecQOff]);
   const int k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
   const int q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
   const int k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
-  const int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
-  const int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
-  const int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
-  const int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
-  const int j_first = __builtin_amdgcn_readfirstlane(rec[kRecFirstTile]);
+  int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
+  int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
+  int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
+  int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
+  int j_first = __builtin_amdgcn_readfirstlane(rec[kRecFirstTile]);
   const int g = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
+  if constexpr (SPLIT) {
+    // positions [t0, t1) of the list: partial positions [t0, min(t1, np)),
+    // full positions [max(t0, np), t1)
+    const int t0 = split * ntiles / p.num_splits;
+    const int t1 = (split + 1) * ntiles / p.num_splits;
+    const int f0 = t0 > np ? t0 : np;
+    const int np_s = (t1 < np ? t1 : np) - t0;
+    p_beg += t0;
+    f_beg += f0 - np;
+    np = np_s > 0 ? np_s : 0;
+    ntiles = t1 - t0;
+    j_first = __builtin_amdgcn_readfirstlane(
+        ntiles == 0 ? -1 : (np > 0 ? p.p_idx[p_beg] : p.f_idx[f_beg]));
+  }
 
   const uint32_t q_rs = (uint32_t)p.heads_q * D * ESZ;   // bytes per Q/O token row
   const uint32_t kv_rs = (uint32_t)p.heads_k * D * ESZ;  // bytes per K/V token row
@@ -691,30 +732,95 @@ void attn_fwd_kernel(AttnParams p) {
   }
 
   // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf.
-  // Rows past q_len are dropped by the O descriptor's range check.
+  // Rows past q_len are dropped by the O descriptor's range check.  A split
+  // writes the same for its tiles, in fp32, into its partial-state slice.
+  rsrc_t rout = ro;
+  float* lse_out = p.lse;
+  if constexpr (SPLIT) {
+    const int64_t fq_rs = (int64_t)p.heads_q * D;   // floats per token row
+    float* ob = p.o_part + (int64_t)split * p.total_q * fq_rs + (int64_t)q_off * fq_rs +
+                (int64_t)h * D;
+    rout = make_rsrc(ob, (uint32_t)(q_len * fq_rs * 4));
+    lse_out = p.lse_part + (int64_t)split * p.heads_q * p.total_q;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum(rs[qb].l);
     const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
-    Ops::store_o(ro, q_row_off[qb], o[qb], inv, b2);
+    if constexpr (SPLIT)
+      store_o_f32<D>(rout, (uint32_t)qloc[qb] * p.heads_q * D * 4, o[qb], inv, b2);
+    else
+      Ops::store_o(rout, q_row_off[qb], o[qb], inv, b2);
     if (b2 == 0 && qloc[qb] < q_len) {
-      p.lse[(int64_t)h * p.total_q + q_off + qloc[qb]] =
+      lse_out[(int64_t)h * p.total_q + q_off + qloc[qb]] =
           l_tot > 0.0f ? (rs[qb].m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
     }
   }
 }
 
+// Merge of Split-K partial states (Tessera page, "Split-K"): per (token, head)
+// row, LSE = M + ln sum_s exp(L_s - M) with M = max_s L_s, and
+// O = sum_s exp(L_s - LSE) O_s; parts with L_s = -inf are not read; a row
+// with every part empty gets O = 0, LSE = -inf.  D/8 lanes per row, eight
+// columns each (two 16-byte loads per part); HBM-bound.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  if (row >= p.rows) return;
+  const int64_t tok = row / p.heads_q;
+  const int h = (int)(row - tok * p.heads_q);
+  const int64_t lstride = (int64_t)p.heads_q * p.total_q;
+  const float* lp = p.lse_part + (int64_t)h * p.total_q + tok;
+  float m = kNegInf;
+  for (int s = 0; s < p.parts; ++s) m = fmaxf(m, lp[s * lstride]);
+  float acc[8] = {};
+  float lsum = 0.0f;
+  if (m != kNegInf) {
+    const int64_t ostride = p.rows * D;
+    const float* op = p.o_part + row * D + c * 8;
+    for (int s = 0; s < p.parts; ++s) {
+      const float ls = lp[s * lstride];
+      if (ls == kNegInf) continue;
+      const float w = exp2_fast((ls - m) * kLog2e);
+      lsum += w;
+      const f32x4 x0 = *(const f32x4*)(op + s * ostride);
+      const f32x4 x1 = *(const f32x4*)(op + s * ostride + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(w, x0[e], acc[e]);
+        acc[4 + e] = fmaf(w, x1[e], acc[4 + e]);
+      }
+    }
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  }
+  OutT* out = (OutT*)p.o + row * D + c * 8;
+  if constexpr (std::is_same_v<OutT, float>) {
+    *(f32x4*)out = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *(f32x4*)(out + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  } else {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)acc[e];
+    *(bf16x8*)out = v;
+  }
+  if (c == 0) p.lse[(int64_t)h * p.total_q + tok] = m == kNegInf ? kNegInf : m + logf(lsum);
+}
+
 // ----------------------------------------------------------------- dispatch
 
-template <class Ops>
-hipError_t launch_ops(int mod, int num_tasks, const AttnParams& p, hipStream_t s) {
-  const dim3 g(num_tasks), blk(Ops::NT);
+template <class Ops, bool SPLIT>
+hipError_t launch_ops(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
+  const dim3 g(num_blocks), blk(Ops::NT);
   switch (mod) {
-    case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone>), g, blk, 0, s, p); break;
-    case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap>), g, blk, 0, s, p); break;
-    case kModAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibi>), g, blk, 0, s, p); break;
-    case kModSoftcapAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcapAlibi>), g, blk, 0, s, p); break;
-    case kModAlibiSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibiSoftcap>), g, blk, 0, s, p); break;
+    case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone, SPLIT>), g, blk, 0, s, p); break;
+    case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap, SPLIT>), g, blk, 0, s, p); break;
+    case kModAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibi, SPLIT>), g, blk, 0, s, p); break;
+    case kModSoftcapAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcapAlibi, SPLIT>), g, blk, 0, s, p); break;
+    case kModAlibiSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibiSoftcap, SPLIT>), g, blk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -746,10 +852,42 @@ hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int3
                            int32_t mod_kind, int32_t num_tasks, const AttnParams& p,
                            hipStream_t s) {
 #define X(DT, HD, TQ_, TK_, ...) \
-  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return launch_ops<__VA_ARGS__>(mod_kind, num_tasks, p, s);
+  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return launch_ops<__VA_ARGS__, false>(mod_kind, num_tasks, p, s);
   MPB_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_split(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
+                                 int32_t mod_kind, const AttnParams& p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.num_splits * p.tasks_padded;
+  if (p.num_splits < 1 || p.tasks_padded < p.num_tasks || blocks > 0x7FFFFFFF)
+    return hipErrorInvalidValue;
+#define X(DT, HD, TQ_, TK_, ...) \
+  if (dtype == DT && head_dim == HD && tile_q == TQ_ && tile_k == TK_) return launch_ops<__VA_ARGS__, true>(mod_kind, (int)blocks, p, s);
+  MPB_VARIANTS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_merge(int32_t dtype, int32_t head_dim, const MergeParams& p,
+                             hipStream_t s) {
+  if (p.rows == 0) return hipSuccess;
+  const int rpb = 256 / (head_dim / 8);
+  const int64_t blocks = (p.rows + rpb - 1) / rpb;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const dim3 g((unsigned)blocks), blk(256);
+  if (dtype == MPB_DTYPE_BF16 && head_dim == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<128, __bf16>), g, blk, 0, s, p);
+  else if (dtype == MPB_DTYPE_BF16 && head_dim == 64)
+    hipLaunchKernelGGL((attn_merge_kernel<64, __bf16>), g, blk, 0, s, p);
+  else if (dtype == MPB_DTYPE_FP32 && head_dim == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<128, float>), g, blk, 0, s, p);
+  else if (dtype == MPB_DTYPE_FP32 && head_dim == 64)
+    hipLaunchKernelGGL((attn_merge_kernel<64, float>), g, blk, 0, s, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace mpb

@@ -186,6 +186,24 @@ struct AttnParams {
   float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
   float softcap_c2;         // c * log2(e)
   float alibi_k;            // ALiBi-first: 2*log2(e)/c multiplier of slope*(k-q)
+  // Split-K (launch_attn_fwd_split only): workgroup i runs split i / tasks_padded
+  // of task i % tasks_padded; split s covers positions [s*n/S, (s+1)*n/S) of
+  // the task's tile list (partial tiles, then full tiles, n of them) and
+  // writes O normalized over those tiles into o_part [S][total_q][heads_q][D]
+  // (fp32) and its LSE into lse_part [S][heads_q][total_q].
+  int32_t num_tasks, num_splits, tasks_padded;
+  float* o_part;
+  float* lse_part;
+};
+
+// Merge of Split-K partial states into O (input dtype) and LSE.
+struct MergeParams {
+  const float* o_part;       // [parts][rows][D], rows = total_q * heads_q (token-major)
+  const float* lse_part;     // [parts][heads_q][total_q]
+  void* o;                   // [rows][D]
+  float* lse;                // [heads_q][total_q]
+  int64_t rows;
+  int32_t parts, heads_q, total_q;
 };
 
 // Backward: Q2K launch records and payload (dQ), K2Q lists and payload
@@ -230,5 +248,12 @@ bool attn_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_
 hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
                            int32_t mod_kind, int32_t num_tasks, const AttnParams& p,
                            hipStream_t s);
+// Split-K forward: p.num_splits * p.tasks_padded workgroups writing partial
+// states (p.o_part, p.lse_part); the merge follows with launch_attn_merge.
+hipError_t launch_attn_fwd_split(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
+                                 int32_t mod_kind, const AttnParams& p, hipStream_t s);
+// Merge kernel for head_dim 64 or 128, output bf16 (dtype 0) or fp32 (1).
+hipError_t launch_attn_merge(int32_t dtype, int32_t head_dim, const MergeParams& p,
+                             hipStream_t s);
 
 }  // namespace mpb

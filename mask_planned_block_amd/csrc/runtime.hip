@@ -995,10 +995,53 @@ size_t flex_attn_fwd_workspace_size(const mpb_plan* plan) {
   return 0;  // the forward launches one workgroup per task: no scheduler state
 }
 
+// ---- Split-K ----
+constexpr int32_t kMaxSplits = 64;
+
+static int device_cus(int dev) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  cache[dev] = n;
+  return n;
+}
+
+// Splits per task when the caller leaves the choice to the library: enough
+// workgroups to give every CU its resident share (two 4-wavefront or four
+// 2-wavefront workgroups) when the plan has fewer tasks, but no split shorter
+// than four tiles on average (each split pays its own Q load, prologue and
+// partial-state write).
+static int32_t choose_splits(const mpb_plan* plan) {
+  const mpb_problem& b = plan->prob;
+  if (plan->num_tasks <= 0) return 1;
+  const int64_t wg_per_cu = b.tile_q >= 128 ? 2 : 4;
+  const int64_t slots = (int64_t)device_cus(plan->device) * wg_per_cu;
+  if (plan->num_tasks >= slots) return 1;
+  const int64_t tiles = (plan->header[1] + plan->header[2]) * (b.heads_q / b.mask_heads);
+  const int64_t avg = tiles / plan->num_tasks;
+  int64_t sp = (slots + plan->num_tasks - 1) / plan->num_tasks;
+  sp = std::min<int64_t>(sp, avg / 4);
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(sp, kMaxSplits));
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+static size_t splitk_o_bytes(const mpb_plan* plan, int32_t sp) {
+  return round256((size_t)sp * plan->prob.total_q * plan->prob.heads_q * plan->prob.head_dim *
+                  sizeof(float));
+}
+static size_t splitk_lse_bytes(const mpb_plan* plan, int32_t sp) {
+  return round256((size_t)sp * plan->prob.heads_q * plan->prob.total_q * sizeof(float));
+}
+
 static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
                               const void* k, const void* v, void* o, float* lse, float scale,
                               const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
-                              void* stream, int32_t force_partial) {
+                              void* stream, int32_t force_partial, int32_t num_splits) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
   int dev = 0;
@@ -1027,10 +1070,14 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
                                             "this forward consumer");
   if (plan->num_tasks > 0 && (!q || !k || !v || !o || !lse))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
-  if (workspace_bytes < flex_attn_fwd_workspace_size(plan) ||
-      (workspace_bytes > 0 && !workspace))
-    return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed",
-                flex_attn_fwd_workspace_size(plan));
+  const size_t ws_need = num_splits > 1 ? flex_attn_fwd_splitk_workspace_size(plan, num_splits)
+                                        : flex_attn_fwd_workspace_size(plan);
+  if (workspace_bytes < ws_need || (ws_need > 0 && !workspace))
+    return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed", ws_need);
+  if (num_splits > 1 && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(MPB_ERR_WORKSPACE, "split-K workspace must be 256-byte aligned");
+  if (num_splits > 1 && (reinterpret_cast<uintptr_t>(o) & 15))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "split-K output o must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.0f))
     return fail(MPB_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   // The kernel addresses one sample's rows of one head through 32-bit buffer
@@ -1040,6 +1087,10 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   const int64_t kspan = ((int64_t)b.seqlen_k + b.tile_k) * b.heads_k * b.head_dim * esz;
   if (qspan >= ((int64_t)1 << 31) || kspan >= ((int64_t)1 << 31))
     return fail(MPB_ERR_UNSUPPORTED, "one sample spans >= 2 GiB of Q/K/V; not supported");
+  // partial states are fp32 rows addressed like O
+  if (num_splits > 1 && ((int64_t)b.seqlen_q + b.tile_q) * b.heads_q * b.head_dim * 4 >=
+                            ((int64_t)1 << 31))
+    return fail(MPB_ERR_UNSUPPORTED, "one sample's fp32 partial output spans >= 2 GiB");
   const bool sc = mod && mod->softcap_enabled;
   const bool al = mod && mod->alibi_enabled;
   if (sc && !(std::isfinite(mod->softcap) && mod->softcap > 0.0f))
@@ -1050,7 +1101,7 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   else if (sc) kind = kModSoftcap;
   else if (al) kind = kModAlibi;
 
-  AttnParams prm;
+  AttnParams prm = {};
   prm.q = q;
   prm.k = k;
   prm.v = v;
@@ -1079,9 +1130,87 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
   if (plan->num_tasks == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks, prm,
-                           s)) != hipSuccess)
-    return device_status(e, "attention launch");
+  if (num_splits <= 1) {
+    if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks,
+                             prm, s)) != hipSuccess)
+      return device_status(e, "attention launch");
+    return ok();
+  }
+  // Split-K: the splits of a task are tasks_padded workgroups apart; with
+  // tasks_padded a multiple of the 8 XCDs every split of a task runs on the
+  // XCD its launch slot maps to (the plan's section for that slot).
+  prm.num_tasks = plan->num_tasks;
+  prm.num_splits = num_splits;
+  prm.tasks_padded = (plan->num_tasks + kNumSections - 1) / kNumSections * kNumSections;
+  prm.o_part = static_cast<float*>(workspace);
+  prm.lse_part =
+      reinterpret_cast<float*>(static_cast<char*>(workspace) + splitk_o_bytes(plan, num_splits));
+  if ((e = launch_attn_fwd_split(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, prm, s)) !=
+      hipSuccess)
+    return device_status(e, "split-K attention launch");
+  MergeParams mp;
+  mp.o_part = prm.o_part;
+  mp.lse_part = prm.lse_part;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = (int64_t)b.total_q * b.heads_q;
+  mp.parts = num_splits;
+  mp.heads_q = b.heads_q;
+  mp.total_q = b.total_q;
+  if ((e = launch_attn_merge(b.dtype, b.head_dim, mp, s)) != hipSuccess)
+    return device_status(e, "split-K merge launch");
+  return ok();
+}
+
+int32_t flex_attn_fwd_num_splits(const mpb_plan* plan) {
+  return plan ? choose_splits(plan) : 1;
+}
+
+size_t flex_attn_fwd_splitk_workspace_size(const mpb_plan* plan, int32_t num_splits) {
+  if (!plan || num_splits < 0 || num_splits > kMaxSplits) return 0;
+  const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
+  if (sp <= 1) return flex_attn_fwd_workspace_size(plan);
+  return splitk_o_bytes(plan, sp) + splitk_lse_bytes(plan, sp);
+}
+
+mpb_status flex_attn_fwd_splitk(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                                const void* k, const void* v, void* o, float* lse, float scale,
+                                const mpb_score_mod* mod, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "num_splits must be in [0, %d]", kMaxSplits);
+  const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
+  return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
+                     stream, 0, sp);
+}
+
+mpb_status flex_attn_fwd_merge(int32_t num_parts, int32_t total_q, int32_t heads_q,
+                               int32_t head_dim, int32_t dtype, const float* o_parts,
+                               const float* lse_parts, void* o, float* lse, void* stream) {
+  if (num_parts < 1 || total_q < 0 || heads_q < 1)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "need num_parts >= 1, total_q >= 0, heads_q >= 1");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(MPB_ERR_UNSUPPORTED, "merge supports head_dim 64 and 128, got %d", head_dim);
+  if (dtype != MPB_DTYPE_BF16 && dtype != MPB_DTYPE_FP32)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "dtype must be MPB_DTYPE_BF16 or MPB_DTYPE_FP32");
+  const int64_t rows = (int64_t)total_q * heads_q;
+  if (rows == 0) return ok();
+  if (!o_parts || !lse_parts || !o || !lse)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "o_parts, lse_parts, o and lse must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(o_parts) & 15) || (reinterpret_cast<uintptr_t>(o) & 15))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "o_parts and o must be 16-byte aligned");
+  MergeParams mp;
+  mp.o_part = o_parts;
+  mp.lse_part = lse_parts;
+  mp.o = o;
+  mp.lse = lse;
+  mp.rows = rows;
+  mp.parts = num_parts;
+  mp.heads_q = heads_q;
+  mp.total_q = total_q;
+  const hipError_t e = launch_attn_merge(dtype, head_dim, mp, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return device_status(e, "merge launch");
   return ok();
 }
 
@@ -1198,7 +1327,7 @@ mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const
                          const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
                          void* stream) {
   return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
-                     stream, 0);
+                     stream, 0, 1);
 }
 
 mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
@@ -1207,7 +1336,7 @@ mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* probl
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t force_partial) {
   return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
-                     stream, force_partial);
+                     stream, force_partial, 1);
 }
 
 }  // extern "C"

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     for name in ("mask_plan_build", "flex_attn_fwd", "mask_plan_destroy", "mask_plan_info",
                  "mask_plan_export", "flex_attn_fwd_workspace_size", "mpb_status_string",
                  "mpb_last_error_detail", "mask_plan_build_ex", "mask_plan_export_k2q",
-                 "mask_plan_stage_times"):
+                 "mask_plan_stage_times", "flex_attn_fwd_splitk", "flex_attn_fwd_merge",
+                 "flex_attn_fwd_num_splits", "flex_attn_fwd_splitk_workspace_size"):
         assert name in fns
 
 
@@ -146,3 +147,31 @@ def test_build_options_and_k2q_export_refusals(lib):
     lib.mask_plan_stage_times.restype = ctypes.c_int
     lib.mask_plan_stage_times.argtypes = [ctypes.c_void_p] * 2
     assert lib.mask_plan_stage_times(None, None) == INVALID
+
+
+def test_splitk_and_merge_host_refusals(lib):
+    """Split-K and merge refusals are decided on the host, before any device
+    call; a merge of zero rows is a no-op."""
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.flex_attn_fwd_splitk.restype = ctypes.c_int
+    lib.flex_attn_fwd_splitk.argtypes = [vp] * 7 + [ctypes.c_float, vp, i32, vp, ctypes.c_size_t,
+                                                    vp]
+    assert lib.flex_attn_fwd_splitk(None, None, None, None, None, None, None, 1.0, None, 2, None,
+                                    0, None) == INVALID
+    lib.flex_attn_fwd_num_splits.restype = i32
+    lib.flex_attn_fwd_num_splits.argtypes = [vp]
+    assert lib.flex_attn_fwd_num_splits(None) == 1
+    lib.flex_attn_fwd_splitk_workspace_size.restype = ctypes.c_size_t
+    lib.flex_attn_fwd_splitk_workspace_size.argtypes = [vp, i32]
+    assert lib.flex_attn_fwd_splitk_workspace_size(None, 4) == 0
+    lib.flex_attn_fwd_merge.restype = ctypes.c_int
+    lib.flex_attn_fwd_merge.argtypes = [i32] * 5 + [vp] * 5
+    p = ctypes.c_void_p(256)
+    assert lib.flex_attn_fwd_merge(0, 4, 2, 128, 0, p, p, p, p, None) == INVALID   # no parts
+    assert lib.flex_attn_fwd_merge(2, -1, 2, 128, 0, p, p, p, p, None) == INVALID
+    assert lib.flex_attn_fwd_merge(2, 4, 2, 96, 0, p, p, p, p, None) == UNSUPPORTED
+    assert lib.flex_attn_fwd_merge(2, 4, 2, 128, 7, p, p, p, p, None) == INVALID   # dtype
+    assert lib.flex_attn_fwd_merge(2, 4, 2, 128, 0, None, p, p, p, None) == INVALID
+    assert lib.flex_attn_fwd_merge(2, 4, 2, 128, 0, ctypes.c_void_p(264), p, p, p,
+                                   None) == INVALID                              # alignment
+    assert lib.flex_attn_fwd_merge(2, 0, 2, 128, 0, None, None, None, None, None) == 0

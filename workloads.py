@@ -24,6 +24,12 @@ sample-local K positions):
                    score = 30*tanh(s*scale/30) + slope_h*(k-q),
                    slope_h = 2^(-8(h+1)/H)
 
+A sixth shape, for the Split-K forward (few tasks, long K lists):
+
+  chunk_long_kv    B=1, Hq=32, Hk=8 (grouped K/V heads), Sq=512, Sk=32768,
+                   d=128, bf16: the last 512 tokens of a 32768-token causal
+                   sequence attend to the whole prefix, F0 = Sk - Sq + q + 1
+
 Random draws use numpy's PCG64 generator seeded with ``seed``, in the order
 structure, then Q, K, V.  bf16 cases draw fp32 N(0,1) values and round them to
 bf16 (round to nearest, ties to even); the rounded values are kept as exact
@@ -265,6 +271,18 @@ def prefix_softcap(seed=0, batch=4, heads=32, seqlen=4096, head_dim=128, prefix=
                     alibi_slopes=alibi_slopes(heads), seed=seed, extra={"prefix": prefix})
 
 
+def chunk_long_kv(seed=0, batch=1, heads_q=32, heads_k=8, seqlen_q=512, seqlen_k=32768,
+                  head_dim=128, dtype=DTYPE_BF16, with_values=True) -> Workload:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ql = np.arange(seqlen_q, dtype=np.int64)
+    mf = _tile_bsh(causal_endpoints(ql + (seqlen_k - seqlen_q)), batch)[None]
+    total_q, total_k = batch * seqlen_q, batch * seqlen_k
+    q, k, v = _draw_qkv(rng, total_q, total_k, heads_q, heads_k, head_dim, dtype, with_values)
+    return Workload("chunk_long_kv", LAYOUT_BSHD, dtype, batch, seqlen_q, seqlen_k, total_q,
+                    total_k, heads_q, heads_k, head_dim, 1, 1, np.ascontiguousarray(mf), None,
+                    None, q, k, v, 1.0 / math.sqrt(head_dim), seed=seed)
+
+
 FULL_CONFIGS = {
     "tiny_causal": tiny_causal,
     "window_sink": window_sink,
@@ -287,8 +305,16 @@ SMALL_CONFIGS = {
 }
 
 
+# Shapes outside the five benchmark cases (Split-K: few tasks, long K lists).
+EXTRA_FULL = {"chunk_long_kv": chunk_long_kv}
+EXTRA_SMALL = {
+    "chunk_long_kv": lambda seed=0, **kw: chunk_long_kv(seed=seed, batch=2, heads_q=4, heads_k=2,
+                                                        seqlen_q=200, seqlen_k=3000, **kw),
+}
+
+
 def make(name: str, seed: int = 0, small: bool = False, **kw) -> Workload:
-    table = SMALL_CONFIGS if small else FULL_CONFIGS
+    table = dict(SMALL_CONFIGS, **EXTRA_SMALL) if small else dict(FULL_CONFIGS, **EXTRA_FULL)
     return table[name](seed=seed, **kw)
 
 
