@@ -67,8 +67,14 @@ enum { MPB_DEVERR_SEQLENS = 1, MPB_DEVERR_RANGE = 2, MPB_DEVERR_ORDER = 4 };
  *   mask_heads (Hmask) is 1 (one mask shared by all Q heads) or heads_q
  *   [MPD §2].  nfunc is odd, 1 <= nfunc <= 4095.  heads_q % heads_k == 0; the
  *   K/V head of Q head h is h / (heads_q / heads_k).  tile_q/tile_k are the
- *   physical tile (0 = library default), chosen independently of any logical
- *   block size [TESS "logical blocks and physical tiles"]. */
+ *   physical tile, chosen independently of any logical block size [TESS
+ *   "logical blocks and physical tiles"].  0 = the library's choice: tile_q
+ *   128 (bf16) or 64 (fp32); tile_k for bf16 head_dim 128 with 128-row
+ *   tiles is 32 when the plan has at least 3 tasks (Q tiles x heads_q; THD:
+ *   total_q/128 rows) per compute unit of the current device, else 64 (the
+ *   32-wide kernel keeps three workgroups per CU and executes fewer masked
+ *   entries, the 64-wide one is faster per workgroup); otherwise 64 (fp32
+ *   head_dim 128: 32).  mask_plan_info reports the resolved tile. */
 typedef struct mpb_problem {
   int32_t layout;
   int32_t dtype;

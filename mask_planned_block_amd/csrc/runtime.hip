@@ -428,9 +428,43 @@ PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
 // each other with no host round trip and no staging copy.
 constexpr size_t kInPlaceBlockBytes = (size_t)32 << 20;
 
+int device_cus(int dev) {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  cache[dev] = n;
+  return n;
+}
+
 int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 128 : 64; }
-int default_tile_k(const mpb_problem& p) {
-  return (p.dtype == MPB_DTYPE_FP32 && p.head_dim > 64) ? 32 : 64;
+
+// Physical K-tile width when the caller leaves it to the library ([TESS]:
+// the physical tile is chosen for the hardware, independently of the mask's
+// logical blocks).  For bf16 d = 128 with 128-row tiles both 64- and 32-wide
+// K tiles exist: the 32-wide kernel holds three workgroups per CU (two for
+// the 64-wide one) and halves the tile granularity, so it executes fewer
+// masked score entries, but it pays a barrier and an index read per 32
+// columns.  Measured on MI355X over the benchmark shapes, it is faster once
+// the plan has at least as many tasks (Q tiles x heads) as the GPU holds
+// resident 32-wide workgroups (3 per CU), and slower below that, where each
+// workgroup's own speed decides.  The task count is known from the geometry
+// (for THD, total_q / 128 rows, the lower bound).
+int default_tile_k(const mpb_problem& p, int tq) {
+  if (p.dtype == MPB_DTYPE_FP32) return p.head_dim > 64 ? 32 : 64;
+  if (p.head_dim == 128 && tq == 128) {
+    const int64_t rows = p.layout == MPB_LAYOUT_BSHD
+                             ? (int64_t)p.batch * ((p.seqlen_q + tq - 1) / tq)
+                             : (int64_t)p.total_q / tq;
+    int dev = 0;
+    const int cus = hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : 256;
+    return rows * p.heads_q >= 3 * (int64_t)cus ? 32 : 64;
+  }
+  return 64;
 }
 
 mpb_signature consumer_signature(const mpb_problem& p, int tq, int tk) {
@@ -477,10 +511,13 @@ mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out) {
   if (p->nfunc < 1 || (p->nfunc % 2) == 0)
     return fail(MPB_ERR_INVALID_ARGUMENT, "nfunc %d is not a positive odd integer", p->nfunc);
   if (p->nfunc > 4095) return fail(MPB_ERR_UNSUPPORTED, "nfunc %d > 4095", p->nfunc);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(MPB_ERR_UNSUPPORTED, "head_dim %d: gfx950 consumers exist for 64 and 128",
+                p->head_dim);
   const int tq = p->tile_q ? p->tile_q : default_tile_q(*p);
-  const int tk = p->tile_k ? p->tile_k : default_tile_k(*p);
   if (tq != 32 && tq != 64 && tq != 128 && tq != 256)
     return fail(MPB_ERR_UNSUPPORTED, "tile_q %d not in {32,64,128,256}", tq);
+  const int tk = p->tile_k ? p->tile_k : default_tile_k(*p, tq);
   if (tk < 32 || tk % 32 != 0 || tk > 256)
     return fail(MPB_ERR_UNSUPPORTED, "tile_k %d is not a multiple of 32 in [32,256]", tk);
   if (!attn_variant_exists(p->dtype, p->head_dim, tq, tk))
@@ -997,19 +1034,6 @@ size_t flex_attn_fwd_workspace_size(const mpb_plan* plan) {
 
 // ---- Split-K ----
 constexpr int32_t kMaxSplits = 64;
-
-static int device_cus(int dev) {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-    n = 256;
-  cache[dev] = n;
-  return n;
-}
 
 // Splits per task when the caller leaves the choice to the library: enough
 // workgroups to give every CU its resident share (two 4-wavefront or four

@@ -168,11 +168,11 @@ def test_k2q_no_k_rows():
 def test_stage_times(name, small, in_place):
     import mask_planned_block_amd as mpb
     w = W.make(name, small=small, with_values=False)
-    tq, tk = default_tiles(w)
     _case("stage_times", name=name, small=small)
     d = G.device_inputs(w)
     for bwd in (False, True):
         plan = G.build_plan(w, d, build_backward=bwd, time_stages=True)
+        tq, tk = plan.problem.tile_q, plan.problem.tile_k
         t = plan.stage_times()
         assert t["classify"] > 0 and t["schedule"] > 0, t
         assert (t["materialize"] == -1) == in_place, t

@@ -29,7 +29,16 @@ def require_gpu():
 
 
 def default_tiles(w):
-    return (128, 64) if w.dtype == W.DTYPE_BF16 else (64, 64)
+    """The library's tile for a workload whose plan leaves it open: 128x32 for
+    bf16 d=128 once the plan has at least 3 tasks per CU, else 128x64; fp32
+    64x64 (d=64)."""
+    if w.dtype != W.DTYPE_BF16:
+        return (64, 64) if w.head_dim == 64 else (64, 32)
+    if w.head_dim != 128:
+        return (128, 64)
+    rows = w.batch * -(-w.seqlen_q // 128) if w.layout == W.LAYOUT_BSHD else w.total_q // 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (128, 32) if rows * w.heads_q >= 3 * cus else (128, 64)
 
 
 def _print_case(case, **kw):
@@ -60,6 +69,7 @@ def test_plan_bit_exact_full(name):
     _print_case("plan_full", name=name, tq=tq, tk=tk)
     d = G.device_inputs(w)
     plan = G.build_plan(w, d)
+    assert (plan.problem.tile_q, plan.problem.tile_k) == (tq, tk), "library tile choice"
     gp = plan.export()
     op = oracle.build_plan(w, tq, tk)
     G.compare_plan(gp, op)
@@ -93,7 +103,7 @@ def test_attention_full_sampled_rows(name):
     # properties at full size: every row of these workloads sees >= 1 key
     assert np.isfinite(lse_np).all()
     assert not torch.isnan(o.float()).any().item()
-    rows = G.sample_rows(w, tile_q=default_tiles(w)[0])
+    rows = G.sample_rows(w, tile_q=plan.problem.tile_q)
     O, L = oracle.attention(w, rows=rows)
     og = G.flat_o(w, o)[rows[:, 0], rows[:, 1]]
     lg = lse_np[rows[:, 1], rows[:, 0]]
@@ -162,7 +172,8 @@ def test_empty_samples_empty_rows_gqa_hmask():
     _print_case("edge_thd")
     d = G.device_inputs(w)
     plan = G.build_plan(w, d)
-    G.compare_plan(plan.export(), oracle.build_plan(w, 128, 64))
+    pl = plan.problem
+    G.compare_plan(plan.export(), oracle.build_plan(w, pl.tile_q, pl.tile_k))
     G.check_schedule(w, plan.export(), 128)
     G.check_launch_order(w, plan.export(), 128)
     o, lse = G.run_attention(w, d, plan)
@@ -181,7 +192,8 @@ def test_ragged_fixed_length_fp32():
     _print_case("ragged_fp32")
     d = G.device_inputs(w)
     plan = G.build_plan(w, d)
-    G.compare_plan(plan.export(), oracle.build_plan(w, 64, 64))
+    pl = plan.problem
+    G.compare_plan(plan.export(), oracle.build_plan(w, pl.tile_q, pl.tile_k))
     o, lse = G.run_attention(w, d, plan)
     torch.cuda.synchronize()
     O, L = oracle.attention(w)
@@ -297,3 +309,19 @@ def test_signature_and_workspace_errors():
     assert mpb.flex_attn_fwd_workspace_size(plan) == 0
     _expect("MPB_ERR_INVALID_ARGUMENT", lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"],
                                                                    scale=-1.0))
+
+
+def test_library_tile_choice():
+    """tile 0x0 resolves from the task count: bf16 d=128 plans with at least
+    three tasks per CU get 128x32 tiles, smaller ones 128x64; an explicit
+    tile is kept."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for heads, want in ((3 * cus // 16, (128, 32)), (3 * cus // 16 - 1, (128, 64))):
+        w = W.custom(np.full((1, 1, 2048), 2048, np.int32), batch=1, seqlen_q=2048,
+                     seqlen_k=2048, heads_q=heads, head_dim=128, dtype=W.DTYPE_BF16,
+                     with_values=False)
+        _print_case("tile_choice", heads=heads)
+        plan = G.build_plan(w, G.device_inputs(w))
+        assert (plan.problem.tile_q, plan.problem.tile_k) == want, (heads, want)
+        plan = G.build_plan(w, G.device_inputs(w), 64, 64)
+        assert (plan.problem.tile_q, plan.problem.tile_k) == (64, 64)
