@@ -87,20 +87,49 @@ def _median_stages(runs):
     return {k: round(float(np.median([r[k] for r in runs])), 2) for k in runs[0]}
 
 
-def cpu_baseline(w, min_seconds=10.0):
+def cpu_baseline(w, tile_q, tile_k, min_seconds=10.0):
     """The oracle, as it is, on the host cores: whole-workload passes of the
-    fp64 attention (plus the plan) until min_seconds have elapsed."""
+    fp64 plan (expand + classify + pack) and attention until min_seconds
+    have elapsed.  Returns (total s, passes, threads, plan s, attention s)."""
     import oracle
     threads = oracle.default_threads()
     t0 = time.perf_counter()
     passes = 0
+    t_plan = t_attn = 0.0
     while True:
-        oracle.build_plan(w, 128 if w.dtype == 0 else 64, 64, nthreads=threads)
+        a = time.perf_counter()
+        oracle.build_plan(w, tile_q, tile_k, nthreads=threads)
+        b = time.perf_counter()
         oracle.attention(w, nthreads=threads)
+        c = time.perf_counter()
+        t_plan += b - a
+        t_attn += c - b
         passes += 1
-        if time.perf_counter() - t0 >= min_seconds:
+        if c - t0 >= min_seconds:
             break
-    return time.perf_counter() - t0, passes, threads
+    return time.perf_counter() - t0, passes, threads, t_plan, t_attn
+
+
+def mfma_peak(mpb, torch, iters=4000):
+    """Dense bf16 MFMA rate the device sustains: the library's MFMA probe
+    (independent v_mfma_f32_32x32x16_bf16 chains on register operands) on
+    8 workgroups per CU, timed with HIP events; median of 5 launches."""
+    import numpy as np
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = 8 * cus
+    out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    flops = mpb.mfma_probe(wg, 200, out, stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    rates = []
+    for _ in range(5):
+        e0.record(stream)
+        flops = mpb.mfma_probe(wg, iters, out, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"tflops": round(float(np.median(rates)), 1), "workgroups": wg,
+            "pct_of_published": round(100 * float(np.median(rates)) / PEAK_BF16_TFLOPS, 1)}
 
 
 ATTN_SOURCE = os.path.join(ROOT, "mask_planned_block_amd", "csrc", "attn_fwd.hip")
@@ -263,6 +292,10 @@ def main():
     ap.add_argument("--splitk-iters", type=int, default=20,
                     help="back-to-back launches per Split-K configuration timed on the long-K "
                          "chunk shape (0 = skip)")
+    ap.add_argument("--cold-iters", type=int, default=5,
+                    help="forwards timed after writing 512 MiB through HBM (0 = skip)")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the MFMA throughput probe")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="end with plain device copies of this many MiB (counter calibration)")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
@@ -479,6 +512,21 @@ def main():
 
     splitk = run_splitk(args, mpb, W, torch, np) if args.splitk_iters > 0 else None
 
+    # cold forward: 512 MiB written through HBM first (more than the 256 MiB
+    # MALL), then one forward, HIP events around it; median of 5
+    cold = []
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.cold_iters else None
+    for _ in range(args.cold_iters):
+        scratch.fill_(1)
+        e0.record(stream)
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    fwd_cold_us = float(np.median(cold)) if cold else None
+    mfma = None if args.no_mfma_probe else mfma_peak(mpb, torch)
+
     if args.copy_calibration_mb > 0:
         # streaming calibration: reads and writes exactly copy_calibration_mb MiB
         src = torch.ones((args.copy_calibration_mb << 20) // 4, dtype=torch.float32, device="cuda")
@@ -519,7 +567,8 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic,
                      "kernel": "attn_fwd_kernel", "achieved_basis": "effective flops per launch / "
                      "average launch duration (HIP events around %d back-to-back launches on "
-                     "the launch stream)" % args.fwd_iters},
+                     "the launch stream)" % args.fwd_iters,
+                     "measured_mfma_peak": mfma},
         "fwd": {
             "us_in_step": round(fwd_in_step_us, 2),
             "us_steady": round(fwd_ss_us, 2),
@@ -532,6 +581,7 @@ def main():
             "dense_gflop": round(dense / 1e9, 4),
             "force_partial_us": None if abl is None else round(abl, 2),
             "us_in_step_median": round(fwd_in_step_med_us, 2),
+            "us_cold": None if fwd_cold_us is None else round(fwd_cold_us, 2),
             "dense_all_visible": dense_ref,
         },
         "plan": {"build_us_host": round(plan_us, 1), "stages_us": plan_stages,
@@ -544,12 +594,14 @@ def main():
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }
     if not args.no_cpu_baseline:
-        secs, passes, threads = cpu_baseline(w, args.cpu_seconds)
+        secs, passes, threads, t_plan, t_attn = cpu_baseline(w, tq, tk, args.cpu_seconds)
         res["cpu_baseline"] = {
             "value": round(eff * passes / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": "%d whole-workload pass(es) of the fp64 oracle (plan + attention, every "
-                      "row) in %.1f s" % (passes, secs)}
+                      "row) in %.1f s" % (passes, secs),
+            "plan_s_per_pass": round(t_plan / passes, 4),
+            "attention_s_per_pass": round(t_attn / passes, 4)}
     print(json.dumps(res))
 
 

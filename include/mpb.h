@@ -371,6 +371,16 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
                          const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Measurement helper (not part of the attention path): launches
+ * `workgroups` workgroups of four wavefronts, each wavefront issuing
+ * iters * 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each) on
+ * register operands, and writes one float per thread to `out` (device,
+ * workgroups * 256 floats).  Flops per launch: workgroups * 4 * iters * 8 *
+ * 32768; the caller times the launch on `stream` to measure the dense bf16
+ * MFMA rate the device sustains.  MPB_ERR_INVALID_ARGUMENT for a
+ * non-positive count or NULL out.  Enqueue only. */
+mpb_status mpb_mfma_probe(int32_t workgroups, int32_t iters, float* out, void* stream);
+
 const char* mpb_status_string(mpb_status status);
 const char* mpb_last_error_detail(void);
 

@@ -115,6 +115,8 @@ def _load():
     lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
                                                               ctypes.c_size_t, vp]
+    lib.mpb_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.mpb_mfma_probe.restype = ctypes.c_int
     lib.mpb_status_string.restype = ctypes.c_char_p
     lib.mpb_status_string.argtypes = [ctypes.c_int]
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
@@ -425,6 +427,16 @@ def flex_attn_fwd_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
                                     _dev_ptr(out, "out"), _dev_ptr(lse, "lse", torch.float32),
                                     _stream_handle(stream)))
     return out, lse
+
+
+def mfma_probe(workgroups: int, iters: int, out: torch.Tensor, stream=None) -> int:
+    """Launches the bf16 MFMA throughput probe (measurement only); returns
+    the flops of the launch.  out: fp32 device tensor of workgroups*256."""
+    if out.numel() < workgroups * 256:
+        raise ValueError("out needs workgroups*256 floats")
+    _check(_lib.mpb_mfma_probe(int(workgroups), int(iters),
+                               _dev_ptr(out, "out", torch.float32), _stream_handle(stream)))
+    return workgroups * 4 * iters * 8 * 32768
 
 
 def flex_attn_bwd_workspace_size(plan: MaskPlan) -> int:
