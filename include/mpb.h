@@ -340,6 +340,38 @@ mpb_status flex_attn_fwd_merge(int32_t num_parts, int32_t total_q, int32_t heads
                                int32_t head_dim, int32_t dtype, const float* o_parts,
                                const float* lse_parts, void* o, float* lse, void* stream);
 
+/* Paged K/V forward [FLEX paged attention: the page table is folded into
+ * the block indices, physical = page_table[batch][logical]; MPD §6.1]:
+ * flex_attn_fwd (or, with num_splits != 1, flex_attn_fwd_splitk) with K and
+ * V read from page pools instead of contiguous BSHD/THD tensors.
+ *   k_pages, v_pages  device pools of token rows, [num_pages * page_size]
+ *             [heads_k][head_dim] in the plan's dtype: logical K position
+ *             kk of sample b lives in pool row
+ *             page_table[b][kk / page_size] * page_size + kk % page_size.
+ *   page_table device int32 [batch][pages_per_seq]; entries must lie in
+ *             [0, num_pages) for every page a sample's k_len reaches (an
+ *             entry outside it is read as zeros, never dereferenced).
+ *   page_size a positive multiple of the plan's tile_k (a K tile never
+ *             straddles pages), else MPB_ERR_UNSUPPORTED.
+ *   pages_per_seq * page_size >= seqlen_k (the longest sample).
+ *   q, o, lse, problem, scale, mod: as flex_attn_fwd (problem describes the
+ *             logical K: seqlen_k / total_k / cu_seqlens as for the plan).
+ *   num_splits as flex_attn_fwd_splitk (1 = one workgroup per task).
+ *   workspace >= flex_attn_fwd_paged_workspace_size(plan, num_splits) bytes,
+ *             256-byte aligned: the pool tile of every listed K tile (a
+ *             remap launch writes it first), then the Split-K area.
+ * Pool rows past a sample's k_len are never read (loads there return
+ * zero), so unused pool rows may hold anything.  Results are identical to
+ * flex_attn_fwd (or flex_attn_fwd_splitk) on the same logical K/V.  bf16
+ * plans only (fp32: MPB_ERR_UNSUPPORTED). */
+size_t flex_attn_fwd_paged_workspace_size(const mpb_plan* plan, int32_t num_splits);
+mpb_status flex_attn_fwd_paged(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, int32_t page_size,
+                               int32_t pages_per_seq, int32_t num_pages, void* o, float* lse,
+                               float scale, const mpb_score_mod* mod, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of caller-provided device workspace flex_attn_bwd needs: two fp32
  * per (Q row, head), dO . O and the LSE in log2 units, each vector rounded
  * up to 256 bytes. */

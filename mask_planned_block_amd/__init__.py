@@ -21,7 +21,8 @@ __all__ = [
     "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "MPBError", "Problem", "MaskPlan",
     "make_problem", "mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
     "flex_attn_fwd", "flex_attn_fwd_workspace_size", "flex_attn_fwd_num_splits",
-    "flex_attn_fwd_splitk_workspace_size", "flex_attn_fwd_merge", "flex_attn_bwd",
+    "flex_attn_fwd_splitk_workspace_size", "flex_attn_fwd_merge", "flex_attn_fwd_paged",
+    "flex_attn_fwd_paged_workspace_size", "flex_attn_bwd",
     "flex_attn_bwd_workspace_size", "library_path", "TASK_REC_FIELDS",
 ]
 
@@ -111,6 +112,10 @@ def _load():
     lib.flex_attn_fwd_splitk_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_fwd_splitk.argtypes = fwd_args[:9] + [ctypes.c_int32] + fwd_args[9:]
     lib.flex_attn_fwd_merge.argtypes = [ctypes.c_int32] * 5 + [vp] * 5
+    lib.flex_attn_fwd_paged_workspace_size.argtypes = [vp, ctypes.c_int32]
+    lib.flex_attn_fwd_paged_workspace_size.restype = ctypes.c_size_t
+    lib.flex_attn_fwd_paged.argtypes = [vp, P(Problem), vp, vp, vp, vp] + [ctypes.c_int32] * 3 + \
+        [vp, vp, ctypes.c_float, P(ScoreMod), ctypes.c_int32, vp, ctypes.c_size_t, vp]
     lib.flex_attn_bwd_workspace_size.argtypes = [vp]
     lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
@@ -125,7 +130,7 @@ def _load():
                  "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times", "mask_plan_export_k2q_order",
                  "mask_plan_export_launch_order",
                  "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_fwd_splitk",
-                 "flex_attn_fwd_merge", "flex_attn_bwd"):
+                 "flex_attn_fwd_merge", "flex_attn_fwd_paged", "flex_attn_bwd"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -400,6 +405,65 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         _check(_lib.flex_attn_fwd_ablation(*head, *tail, 1))
     else:
         _check(_lib.flex_attn_fwd(*head, *tail))
+    return out, lse
+
+
+def flex_attn_fwd_paged_workspace_size(plan: MaskPlan, num_splits: int = 1) -> int:
+    return int(_lib.flex_attn_fwd_paged_workspace_size(plan.handle, int(num_splits)))
+
+
+def flex_attn_fwd_paged(plan: MaskPlan, q: torch.Tensor, k_pages: torch.Tensor,
+                        v_pages: torch.Tensor, page_table: torch.Tensor, page_size: int,
+                        scale: Optional[float] = None, softcap: Optional[float] = None,
+                        alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None,
+                        num_splits: int = 1):
+    """Forward with K/V in page pools (see include/mpb.h, flex_attn_fwd_paged).
+
+    k_pages/v_pages: [num_pages, page_size, Hk, D] (or [num_pages*page_size,
+    Hk, D]); page_table: int32 [batch, pages_per_seq].  Returns (O, LSE)."""
+    p = plan._bound
+    if k_pages.shape != v_pages.shape or k_pages.dtype != q.dtype:
+        raise ValueError("k_pages and v_pages must match each other and q's dtype")
+    if page_table.dim() != 2 or page_table.shape[0] != p.batch:
+        raise ValueError("page_table must be [batch, pages_per_seq]")
+    Hk, D = k_pages.shape[-2], k_pages.shape[-1]
+    rows = k_pages.numel() // (Hk * D)
+    if rows % page_size:
+        raise ValueError("pool rows are not a multiple of page_size")
+    dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else (DTYPE_FP32 if q.dtype == torch.float32
+                                                     else -1)
+    if p.layout == LAYOUT_BSHD:
+        B, Sq, Hq, Dq = q.shape
+        prob = Problem(LAYOUT_BSHD, dt, B, Sq, p.seqlen_k, B * Sq, p.total_k, Hq, Hk, Dq,
+                       p.mask_heads, p.nfunc, 0, 0)
+    else:
+        Tq, Hq, Dq = q.shape
+        prob = Problem(LAYOUT_THD, dt, p.batch, p.seqlen_q, p.seqlen_k, Tq, p.total_k, Hq, Hk,
+                       Dq, p.mask_heads, p.nfunc, 0, 0)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(flex_attn_fwd_paged_workspace_size(plan, num_splits), 256),
+                                dtype=torch.uint8, device=q.device)
+    mod = None
+    if softcap or alibi_slopes is not None:
+        mod = ScoreMod(1 if softcap else 0, float(softcap or 0.0),
+                       1 if alibi_slopes is not None else 0,
+                       _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
+                       1 if alibi_before_softcap else 0)
+    sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
+    _check(_lib.flex_attn_fwd_paged(
+        plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k_pages, "k_pages", q.dtype),
+        _dev_ptr(v_pages, "v_pages", q.dtype), _dev_ptr(page_table, "page_table", torch.int32),
+        int(page_size), int(page_table.shape[1]), rows // page_size,
+        _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
+        ctypes.byref(mod) if mod is not None else None, int(num_splits),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream)))
     return out, lse
 
 

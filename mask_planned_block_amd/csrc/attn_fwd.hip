@@ -528,7 +528,8 @@ __device__ inline void store_o_f32(rsrc_t ro, uint32_t row_off, const f32x16 (&o
 // SPLIT: one workgroup per (split, task), the splits of the Tessera page's
 // Split-K: workgroup i runs split i / tasks_padded of task i % tasks_padded
 // over a contiguous part of the task's tile list and writes its partial state.
-template <class Ops, int MOD, bool SPLIT>
+// PAGED: K and V are page pools addressed through the remapped tile lists.
+template <class Ops, int MOD, bool SPLIT, bool PAGED>
 __global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(Ops::WPE, Ops::WPE)))
 void attn_fwd_kernel(AttnParams p) {
   constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
@@ -611,6 +612,17 @@ void attn_fwd_kernel(AttnParams p) {
   const rsrc_t ro = make_rsrc(obase, (uint32_t)q_len * q_rs);
   const rsrc_t rk = make_rsrc(kbase, (uint32_t)k_len * kv_rs);
   const rsrc_t rv = make_rsrc(vbase, (uint32_t)k_len * kv_rs);
+  // Paged K/V: tile t's rows live in pool tile phys (tile_k rows of the pool,
+  // starting at row phys * TKV); its descriptors cover only the rows below
+  // the sample's k_len, so loads past it read zero as in the contiguous case.
+  // An unmapped entry (phys < 0) gets empty descriptors: its rows read zero.
+  const char* kpool = (const char*)p.k + (int64_t)g * D * ESZ;
+  const char* vpool = (const char*)p.v + (int64_t)g * D * ESZ;
+  auto tile_rsrc = [&](const char* pool, int j, int phys) {
+    const int rows = k_len - j * TKV;
+    const uint32_t n = phys < 0 ? 0u : (uint32_t)(rows < TKV ? rows : TKV) * kv_rs;
+    return make_rsrc(pool + (int64_t)(phys < 0 ? 0 : phys) * TKV * kv_rs, n);
+  };
 
   // Sample-local Q row of this lane in each of the wavefront's blocks.
   int qloc[QB];
@@ -624,6 +636,10 @@ void attn_fwd_kernel(AttnParams p) {
   // tile t of the task: partial list first, then full list (§6.1)
   auto tile_j = [&](int t) {
     return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
+  };
+  auto tile_phys = [&](int t) {
+    return __builtin_amdgcn_readfirstlane(t < np ? p.phys_p[p_beg + t]
+                                                 : p.phys_f[f_beg + t - np]);
   };
   auto load_masks = [&](int t, uint32_t (&mw)[QB][NKB]) {
 #pragma unroll
@@ -645,11 +661,20 @@ void attn_fwd_kernel(AttnParams p) {
   int j_cur = j_first;
   // K-tile index of tile t+1, read one tile ahead of its use so that no
   // tile waits on the index load before issuing its prefetch.
-  int j_ahead = 0;
+  int j_ahead = 0, ph_ahead = 0;
   if (ntiles > 0) {
-    Ops::load(st, k_s0, v_s0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
+    if constexpr (PAGED) {
+      const int ph = tile_phys(0);
+      Ops::load(st, k_s0, v_s0, tile_rsrc(kpool, j_cur, ph), tile_rsrc(vpool, j_cur, ph), 0u,
+                kv_rs, tid);
+    } else {
+      Ops::load(st, k_s0, v_s0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
+    }
     load_masks(0, mw_cur);
-    if (ntiles > 1) j_ahead = tile_j(1);
+    if (ntiles > 1) {
+      j_ahead = tile_j(1);
+      if constexpr (PAGED) ph_ahead = tile_phys(1);
+    }
   }
   typename Ops::QFrag qf;
   Ops::load_q(qf, rq, q_row_off, b2);
@@ -674,16 +699,26 @@ void attn_fwd_kernel(AttnParams p) {
   // step (the loops step two tiles at a time).
   int t = 0;
   int j_pending = 0;   // index of tile t+2, in flight during tile t
+  int ph_pending = 0;  // its pool tile (paged K/V)
   auto step = [&](auto masked, auto stage) __attribute__((always_inline)) {
     constexpr bool kMasked = decltype(masked)::value;
     const auto next = flip(stage);
     const bool more = t + 1 < ntiles;
     const int j_next = j_ahead;
     if (more) {
-      Ops::load(st, kbuf(next), vbuf(next), rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs, tid);
+      if constexpr (PAGED)
+        Ops::load(st, kbuf(next), vbuf(next), tile_rsrc(kpool, j_next, ph_ahead),
+                  tile_rsrc(vpool, j_next, ph_ahead), 0u, kv_rs, tid);
+      else
+        Ops::load(st, kbuf(next), vbuf(next), rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs,
+                  tid);
       load_masks(t + 1, mw_next);
     }
-    if (t + 2 < ntiles) j_pending = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
+    if (t + 2 < ntiles) {
+      j_pending = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
+      if constexpr (PAGED)
+        ph_pending = t + 2 < np ? p.phys_p[p_beg + t + 2] : p.phys_f[f_beg + t + 2 - np];
+    }
     float kq0[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) kq0[qb] = (float)(j_cur * TKV + 4 * b2 - qloc[qb]);
@@ -699,7 +734,10 @@ void attn_fwd_kernel(AttnParams p) {
     // this wavefront's loads straight into LDS have landed; the barrier
     // publishes them and the stores above to the whole workgroup
     __builtin_amdgcn_s_waitcnt(0);
-    if (t + 2 < ntiles) j_ahead = __builtin_amdgcn_readfirstlane(j_pending);
+    if (t + 2 < ntiles) {
+      j_ahead = __builtin_amdgcn_readfirstlane(j_pending);
+      if constexpr (PAGED) ph_ahead = __builtin_amdgcn_readfirstlane(ph_pending);
+    }
     __syncthreads();
     ++t;
   };
@@ -758,6 +796,37 @@ void attn_fwd_kernel(AttnParams p) {
   }
 }
 
+// Page-table remap of the plan's K-tile lists (FlexAttention page, paged
+// attention: the page table is folded into the block indices, physical =
+// page_table[batch][logical]): one wavefront per flat mask row finds the
+// row's sample, then its lanes map every listed K tile j to the pool tile
+// page * (page_size / tile_k) + (j * tile_k mod page_size) / tile_k, or -1
+// when the page entry is outside [0, num_pages).
+__global__ __launch_bounds__(256) void page_remap_kernel(RemapParams p) {
+  const int flat = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (flat >= p.rows_flat) return;
+  const int r = flat % p.rows_total;
+  // sample b with cu_rows[b] <= r < cu_rows[b+1] (largest such b)
+  int lo = 0, hi = p.batch;              // invariant: cu_rows[lo] <= r < cu_rows[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (p.cu_rows[mid] <= r) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int tiles_per_page = p.page_size / p.tile_k;
+  const int32_t* pt = p.page_table + (int64_t)b * p.pages_per_seq;
+  auto map = [&](int j) {
+    const int lp = j / tiles_per_page;
+    if (lp >= p.pages_per_seq) return -1;
+    const int pg = pt[lp];
+    if (pg < 0 || pg >= p.num_pages) return -1;
+    return pg * tiles_per_page + (j - lp * tiles_per_page);
+  };
+  for (int e = p.p_off[flat] + lane; e < p.p_off[flat + 1]; e += 64) p.phys_p[e] = map(p.p_idx[e]);
+  for (int e = p.f_off[flat] + lane; e < p.f_off[flat + 1]; e += 64) p.phys_f[e] = map(p.f_idx[e]);
+}
+
 // Merge of Split-K partial states (Tessera page, "Split-K"): per (token, head)
 // row, LSE = M + ln sum_s exp(L_s - M) with M = max_s L_s, and
 // O = sum_s exp(L_s - LSE) O_s; parts with L_s = -inf are not read; a row
@@ -812,18 +881,30 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
 
 // ----------------------------------------------------------------- dispatch
 
-template <class Ops, bool SPLIT>
-hipError_t launch_ops(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
+template <class Ops, bool SPLIT, bool PAGED>
+hipError_t launch_mods(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
   const dim3 g(num_blocks), blk(Ops::NT);
   switch (mod) {
-    case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone, SPLIT>), g, blk, 0, s, p); break;
-    case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap, SPLIT>), g, blk, 0, s, p); break;
-    case kModAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibi, SPLIT>), g, blk, 0, s, p); break;
-    case kModSoftcapAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcapAlibi, SPLIT>), g, blk, 0, s, p); break;
-    case kModAlibiSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibiSoftcap, SPLIT>), g, blk, 0, s, p); break;
+    case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone, SPLIT, PAGED>), g, blk, 0, s, p); break;
+    case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap, SPLIT, PAGED>), g, blk, 0, s, p); break;
+    case kModAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibi, SPLIT, PAGED>), g, blk, 0, s, p); break;
+    case kModSoftcapAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcapAlibi, SPLIT, PAGED>), g, blk, 0, s, p); break;
+    case kModAlibiSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibiSoftcap, SPLIT, PAGED>), g, blk, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Paged K/V kernels exist for the bf16 consumers only.
+template <class Ops, bool SPLIT>
+hipError_t launch_ops(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
+  if (p.paged) {
+    if constexpr (std::is_same_v<typename Ops::T, __bf16>)
+      return launch_mods<Ops, SPLIT, true>(mod, num_blocks, p, s);
+    else
+      return hipErrorInvalidValue;
+  }
+  return launch_mods<Ops, SPLIT, false>(mod, num_blocks, p, s);
 }
 
 // The consumer table: (dtype, head_dim, tile_q, tile_k) -> kernel family.
@@ -868,6 +949,12 @@ hipError_t launch_attn_fwd_split(int32_t dtype, int32_t head_dim, int32_t tile_q
   MPB_VARIANTS(X)
 #undef X
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_page_remap(const RemapParams& p, hipStream_t s) {
+  if (p.rows_flat == 0) return hipSuccess;
+  hipLaunchKernelGGL(page_remap_kernel, dim3((p.rows_flat + 3) / 4), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_merge(int32_t dtype, int32_t head_dim, const MergeParams& p,

@@ -194,6 +194,25 @@ struct AttnParams {
   int32_t num_tasks, num_splits, tasks_padded;
   float* o_part;
   float* lse_part;
+  // Paged K/V: k and v are pools of token rows ([pool rows][heads_k][D]);
+  // phys_p / phys_f hold, beside p_idx / f_idx, the pool tile (tile_k rows)
+  // of every listed K tile, -1 for an entry whose page is out of range.
+  int32_t paged;
+  const int32_t* phys_p;
+  const int32_t* phys_f;
+};
+
+// Page remap of a plan's K-tile lists (the forward's paged mode).
+struct RemapParams {
+  const int32_t* cu_rows;    // [batch+1]
+  const int32_t* p_off;      // [rows_flat+1]
+  const int32_t* f_off;
+  const int32_t* p_idx;
+  const int32_t* f_idx;
+  const int32_t* page_table; // [batch][pages_per_seq]
+  int32_t* phys_p;
+  int32_t* phys_f;
+  int32_t rows_total, rows_flat, batch, tile_k, page_size, pages_per_seq, num_pages;
 };
 
 // Merge of Split-K partial states into O (input dtype) and LSE.
@@ -252,6 +271,8 @@ hipError_t launch_attn_fwd(int32_t dtype, int32_t head_dim, int32_t tile_q, int3
 // states (p.o_part, p.lse_part); the merge follows with launch_attn_merge.
 hipError_t launch_attn_fwd_split(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k,
                                  int32_t mod_kind, const AttnParams& p, hipStream_t s);
+// Physical pool tiles of every listed K tile (one wavefront per flat row).
+hipError_t launch_page_remap(const RemapParams& p, hipStream_t s);
 // Merge kernel for head_dim 64 or 128, output bf16 (dtype 0) or fp32 (1).
 hipError_t launch_attn_merge(int32_t dtype, int32_t head_dim, const MergeParams& p,
                              hipStream_t s);

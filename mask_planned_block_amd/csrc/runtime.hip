@@ -1062,10 +1062,23 @@ static size_t splitk_lse_bytes(const mpb_plan* plan, int32_t sp) {
   return round256((size_t)sp * plan->prob.heads_q * plan->prob.total_q * sizeof(float));
 }
 
+// Paged K/V arguments of flex_attn_fwd_paged.
+struct PagedArgs {
+  const int32_t* page_table;
+  int32_t page_size, pages_per_seq, num_pages;
+};
+
+// Workspace of the paged forward: the pool tile of every listed K tile,
+// partial list then full list, each area rounded to 256 bytes.
+static size_t paged_remap_bytes(const mpb_plan* plan) {
+  return round256((size_t)plan->header[1] * 4) + round256((size_t)plan->header[2] * 4);
+}
+
 static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
                               const void* k, const void* v, void* o, float* lse, float scale,
                               const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
-                              void* stream, int32_t force_partial, int32_t num_splits) {
+                              void* stream, int32_t force_partial, int32_t num_splits,
+                              const PagedArgs* paged = nullptr) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
   int dev = 0;
@@ -1094,12 +1107,31 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
                                             "this forward consumer");
   if (plan->num_tasks > 0 && (!q || !k || !v || !o || !lse))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
-  const size_t ws_need = num_splits > 1 ? flex_attn_fwd_splitk_workspace_size(plan, num_splits)
-                                        : flex_attn_fwd_workspace_size(plan);
+  const size_t remap_bytes = paged ? paged_remap_bytes(plan) : 0;
+  const size_t ws_need =
+      remap_bytes + (num_splits > 1 ? flex_attn_fwd_splitk_workspace_size(plan, num_splits)
+                                    : flex_attn_fwd_workspace_size(plan));
   if (workspace_bytes < ws_need || (ws_need > 0 && !workspace))
     return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed", ws_need);
-  if (num_splits > 1 && (reinterpret_cast<uintptr_t>(workspace) & 255))
-    return fail(MPB_ERR_WORKSPACE, "split-K workspace must be 256-byte aligned");
+  if ((num_splits > 1 || paged) && (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return fail(MPB_ERR_WORKSPACE, "split-K and paged workspaces must be 256-byte aligned");
+  if (paged) {
+    if (b.dtype != MPB_DTYPE_BF16)
+      return fail(MPB_ERR_UNSUPPORTED, "paged K/V is implemented for bf16 plans only");
+    if (!paged->page_table)
+      return fail(MPB_ERR_INVALID_ARGUMENT, "page_table is NULL");
+    if (paged->page_size < b.tile_k || paged->page_size % b.tile_k != 0)
+      return fail(MPB_ERR_UNSUPPORTED, "page_size %d must be a positive multiple of the plan's "
+                  "tile_k %d", paged->page_size, b.tile_k);
+    if (paged->pages_per_seq < 1 || paged->num_pages < 1)
+      return fail(MPB_ERR_INVALID_ARGUMENT, "pages_per_seq and num_pages must be >= 1");
+    if ((int64_t)paged->pages_per_seq * paged->page_size < b.seqlen_k)
+      return fail(MPB_ERR_INVALID_ARGUMENT, "pages_per_seq * page_size = %lld < seqlen_k %d",
+                  (long long)paged->pages_per_seq * paged->page_size, b.seqlen_k);
+    if ((int64_t)paged->num_pages * (paged->page_size / b.tile_k) >= ((int64_t)1 << 31) ||
+        (int64_t)b.batch * paged->pages_per_seq >= ((int64_t)1 << 31))
+      return fail(MPB_ERR_UNSUPPORTED, "page pool or page table too large");
+  }
   if (num_splits > 1 && (reinterpret_cast<uintptr_t>(o) & 15))
     return fail(MPB_ERR_INVALID_ARGUMENT, "split-K output o must be 16-byte aligned");
   if (!std::isfinite(scale) || !(scale > 0.0f))
@@ -1108,7 +1140,7 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   // offsets (including one tile of overshoot past the sample end).
   const int64_t esz = b.dtype == MPB_DTYPE_BF16 ? 2 : 4;
   const int64_t qspan = ((int64_t)b.seqlen_q + b.tile_q) * b.heads_q * b.head_dim * esz;
-  const int64_t kspan = ((int64_t)b.seqlen_k + b.tile_k) * b.heads_k * b.head_dim * esz;
+  const int64_t kspan = paged ? 0 : ((int64_t)b.seqlen_k + b.tile_k) * b.heads_k * b.head_dim * esz;
   if (qspan >= ((int64_t)1 << 31) || kspan >= ((int64_t)1 << 31))
     return fail(MPB_ERR_UNSUPPORTED, "one sample spans >= 2 GiB of Q/K/V; not supported");
   // partial states are fp32 rows addressed like O
@@ -1154,6 +1186,30 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
   if (plan->num_tasks == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (paged) {
+    RemapParams rp;
+    rp.cu_rows = plan->dev.cu_rows;
+    rp.p_off = plan->dev.p_off;
+    rp.f_off = plan->dev.f_off;
+    rp.p_idx = plan->dev.p_idx;
+    rp.f_idx = plan->dev.f_idx;
+    rp.page_table = paged->page_table;
+    rp.phys_p = static_cast<int32_t*>(workspace);
+    rp.phys_f = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                           round256((size_t)plan->header[1] * 4));
+    rp.rows_total = plan->rows_total;
+    rp.rows_flat = b.mask_heads * plan->rows_total;
+    rp.batch = b.batch;
+    rp.tile_k = b.tile_k;
+    rp.page_size = paged->page_size;
+    rp.pages_per_seq = paged->pages_per_seq;
+    rp.num_pages = paged->num_pages;
+    if ((e = launch_page_remap(rp, s)) != hipSuccess) return device_status(e, "page remap launch");
+    prm.paged = 1;
+    prm.phys_p = rp.phys_p;
+    prm.phys_f = rp.phys_f;
+    workspace = static_cast<char*>(workspace) + remap_bytes;
+  }
   if (num_splits <= 1) {
     if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks,
                              prm, s)) != hipSuccess)
@@ -1207,6 +1263,28 @@ mpb_status flex_attn_fwd_splitk(const mpb_plan* plan, const mpb_problem* problem
   const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
   return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
                      stream, 0, sp);
+}
+
+size_t flex_attn_fwd_paged_workspace_size(const mpb_plan* plan, int32_t num_splits) {
+  if (!plan || num_splits < 0 || num_splits > kMaxSplits) return 0;
+  const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
+  return paged_remap_bytes(plan) +
+         (sp > 1 ? splitk_o_bytes(plan, sp) + splitk_lse_bytes(plan, sp) : 0);
+}
+
+mpb_status flex_attn_fwd_paged(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                               const void* k_pages, const void* v_pages,
+                               const int32_t* page_table, int32_t page_size,
+                               int32_t pages_per_seq, int32_t num_pages, void* o, float* lse,
+                               float scale, const mpb_score_mod* mod, int32_t num_splits,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "num_splits must be in [0, %d]", kMaxSplits);
+  const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
+  const PagedArgs pg = {page_table, page_size, pages_per_seq, num_pages};
+  return attn_common(plan, problem, q, k_pages, v_pages, o, lse, scale, mod, workspace,
+                     workspace_bytes, stream, 0, sp, &pg);
 }
 
 mpb_status flex_attn_fwd_merge(int32_t num_parts, int32_t total_q, int32_t heads_q,
