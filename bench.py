@@ -267,6 +267,71 @@ def run_splitk(args, mpb, W, torch, np):
     return res
 
 
+def run_paged(args, w, d, plan, kw, mpb, torch, np):
+    """Paged K/V overhead: the main workload's K/V scattered into a page pool
+    (pages of 2 * tile_k tokens, random page order) and the paged forward
+    (remap launch + forward) timed against the contiguous forward on the same
+    plan; HIP events around back-to-back launches."""
+    p = plan.problem
+    ps = 2 * p.tile_k
+    g = torch.Generator().manual_seed(0)
+    need = [-(-w.sample_bounds(b)[3] // ps) for b in range(w.batch)]
+    pps = max(max(need), -(-w.seqlen_k // ps), 1)
+    num_pages = sum(need)
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.full((w.batch, pps), -1, dtype=torch.int32)
+    src, dst = [], []
+    nxt = 0
+    for b in range(w.batch):
+        _, _, k_off, k_len = w.sample_bounds(b)
+        for lp in range(need[b]):
+            table[b, lp] = int(perm[nxt])
+            nxt += 1
+        kk = torch.arange(k_len)
+        src.append(k_off + kk)
+        dst.append(table[b, kk // ps].long() * ps + kk % ps)
+    src, dst = torch.cat(src).cuda(), torch.cat(dst).cuda()
+    kflat = d["k"].reshape(-1, w.heads_k, w.head_dim)
+    vflat = d["v"].reshape(-1, w.heads_k, w.head_dim)
+    kp = torch.zeros((num_pages * ps, w.heads_k, w.head_dim), dtype=kflat.dtype, device="cuda")
+    vp = torch.zeros_like(kp)
+    kp[dst] = kflat[src]
+    vp[dst] = vflat[src]
+    table = table.cuda()
+    stream = kw["stream"]
+    ws = torch.empty(max(mpb.flex_attn_fwd_paged_workspace_size(plan, 1), 256),
+                     dtype=torch.uint8, device="cuda")
+    kw_p = {k: v for k, v in kw.items() if k not in ("workspace", "num_splits")}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        e0.record(stream)
+        for _ in range(args.fwd_iters):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.fwd_iters
+
+    us_p = timed(lambda: mpb.flex_attn_fwd_paged(plan, d["q"], kp, vp, table, ps, workspace=ws,
+                                                 **kw_p))
+    us_r = timed(lambda: mpb.flex_attn_fwd_paged(plan, d["q"], kp, vp, table, ps, workspace=ws,
+                                                 remap=False, **kw_p))
+    us_c = timed(lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw_p))
+    o_p = kw_p["out"].clone()
+    mpb.flex_attn_fwd_paged(plan, d["q"], kp, vp, table, ps, workspace=ws, **kw_p)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(o_p, kw_p["out"]))
+    return {"page_size": ps, "num_pages": num_pages, "us_with_remap": round(us_p, 2),
+            "us_reusing_remap": round(us_r, 2), "contiguous_us": round(us_c, 2),
+            "overhead_pct_with_remap": round(100 * (us_p / us_c - 1), 2),
+            "overhead_pct_reusing_remap": round(100 * (us_r / us_c - 1), 2),
+            "identical_output": same,
+            "basis": "HIP events around %d back-to-back calls (remap launch + forward, or the "
+                     "forward alone on lists remapped once)" % args.fwd_iters}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +357,8 @@ def main():
     ap.add_argument("--splitk-iters", type=int, default=20,
                     help="back-to-back launches per Split-K configuration timed on the long-K "
                          "chunk shape (0 = skip)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged K/V overhead leg")
     ap.add_argument("--cold-iters", type=int, default=5,
                     help="forwards timed after writing 512 MiB through HBM (0 = skip)")
     ap.add_argument("--no-mfma-probe", action="store_true",
@@ -511,6 +578,9 @@ def main():
         pbw.close()
 
     splitk = run_splitk(args, mpb, W, torch, np) if args.splitk_iters > 0 else None
+    paged = None
+    if not args.no_paged and w.dtype == W.DTYPE_BF16 and args.num_splits is None:
+        paged = run_paged(args, w, d, plan, kw, mpb, torch, np)
 
     # cold forward: 512 MiB written through HBM first (more than the 256 MiB
     # MALL), then one forward, HIP events around it; median of 5
@@ -590,6 +660,7 @@ def main():
         "plan_k2q": plan_k2q,
         "bwd": bwd,
         "splitk": splitk,
+        "paged": paged,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
     }

@@ -357,9 +357,13 @@ mpb_status flex_attn_fwd_merge(int32_t num_parts, int32_t total_q, int32_t heads
  *   q, o, lse, problem, scale, mod: as flex_attn_fwd (problem describes the
  *             logical K: seqlen_k / total_k / cu_seqlens as for the plan).
  *   num_splits as flex_attn_fwd_splitk (1 = one workgroup per task).
+ *   remap     1: a remap launch first writes the pool tile of every listed K
+ *             tile into the workspace; 0: the workspace already holds them
+ *             from an earlier call with remap = 1 on the same plan, page
+ *             table contents and page_size, and they are reused (e.g. the
+ *             layers of one model step share one page table).
  *   workspace >= flex_attn_fwd_paged_workspace_size(plan, num_splits) bytes,
- *             256-byte aligned: the pool tile of every listed K tile (a
- *             remap launch writes it first), then the Split-K area.
+ *             256-byte aligned: the remapped lists, then the Split-K area.
  * Pool rows past a sample's k_len are never read (loads there return
  * zero), so unused pool rows may hold anything.  Results are identical to
  * flex_attn_fwd (or flex_attn_fwd_splitk) on the same logical K/V.  bf16
@@ -370,7 +374,8 @@ mpb_status flex_attn_fwd_paged(const mpb_plan* plan, const mpb_problem* problem,
                                const int32_t* page_table, int32_t page_size,
                                int32_t pages_per_seq, int32_t num_pages, void* o, float* lse,
                                float scale, const mpb_score_mod* mod, int32_t num_splits,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               int32_t remap, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Bytes of caller-provided device workspace flex_attn_bwd needs: two fp32
  * per (Q row, head), dO . O and the LSE in log2 units, each vector rounded

@@ -115,7 +115,8 @@ def _load():
     lib.flex_attn_fwd_paged_workspace_size.argtypes = [vp, ctypes.c_int32]
     lib.flex_attn_fwd_paged_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_fwd_paged.argtypes = [vp, P(Problem), vp, vp, vp, vp] + [ctypes.c_int32] * 3 + \
-        [vp, vp, ctypes.c_float, P(ScoreMod), ctypes.c_int32, vp, ctypes.c_size_t, vp]
+        [vp, vp, ctypes.c_float, P(ScoreMod), ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t,
+         vp]
     lib.flex_attn_bwd_workspace_size.argtypes = [vp]
     lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
@@ -418,8 +419,10 @@ def flex_attn_fwd_paged(plan: MaskPlan, q: torch.Tensor, k_pages: torch.Tensor,
                         alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         workspace: Optional[torch.Tensor] = None, stream=None,
-                        num_splits: int = 1):
+                        num_splits: int = 1, remap: bool = True):
     """Forward with K/V in page pools (see include/mpb.h, flex_attn_fwd_paged).
+    remap=False reuses the remapped tile lists an earlier call left in the
+    same workspace (same plan, page table and page size).
 
     k_pages/v_pages: [num_pages, page_size, Hk, D] (or [num_pages*page_size,
     Hk, D]); page_table: int32 [batch, pages_per_seq].  Returns (O, LSE)."""
@@ -461,7 +464,7 @@ def flex_attn_fwd_paged(plan: MaskPlan, q: torch.Tensor, k_pages: torch.Tensor,
         _dev_ptr(v_pages, "v_pages", q.dtype), _dev_ptr(page_table, "page_table", torch.int32),
         int(page_size), int(page_table.shape[1]), rows // page_size,
         _dev_ptr(out, "out", q.dtype), _dev_ptr(lse, "lse", torch.float32), sc,
-        ctypes.byref(mod) if mod is not None else None, int(num_splits),
+        ctypes.byref(mod) if mod is not None else None, int(num_splits), 1 if remap else 0,
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream)))
     return out, lse

@@ -1066,6 +1066,7 @@ static size_t splitk_lse_bytes(const mpb_plan* plan, int32_t sp) {
 struct PagedArgs {
   const int32_t* page_table;
   int32_t page_size, pages_per_seq, num_pages;
+  int32_t remap;   // 0: the workspace already holds this plan's remapped lists
 };
 
 // Workspace of the paged forward: the pool tile of every listed K tile,
@@ -1204,7 +1205,8 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
     rp.page_size = paged->page_size;
     rp.pages_per_seq = paged->pages_per_seq;
     rp.num_pages = paged->num_pages;
-    if ((e = launch_page_remap(rp, s)) != hipSuccess) return device_status(e, "page remap launch");
+    if (paged->remap && (e = launch_page_remap(rp, s)) != hipSuccess)
+      return device_status(e, "page remap launch");
     prm.paged = 1;
     prm.phys_p = rp.phys_p;
     prm.phys_f = rp.phys_f;
@@ -1277,12 +1279,14 @@ mpb_status flex_attn_fwd_paged(const mpb_plan* plan, const mpb_problem* problem,
                                const int32_t* page_table, int32_t page_size,
                                int32_t pages_per_seq, int32_t num_pages, void* o, float* lse,
                                float scale, const mpb_score_mod* mod, int32_t num_splits,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               int32_t remap, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(MPB_ERR_INVALID_ARGUMENT, "num_splits must be in [0, %d]", kMaxSplits);
+  if (remap != 0 && remap != 1) return fail(MPB_ERR_INVALID_ARGUMENT, "remap must be 0 or 1");
   const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
-  const PagedArgs pg = {page_table, page_size, pages_per_seq, num_pages};
+  const PagedArgs pg = {page_table, page_size, pages_per_seq, num_pages, remap};
   return attn_common(plan, problem, q, k_pages, v_pages, o, lse, scale, mod, workspace,
                      workspace_bytes, stream, 0, sp, &pg);
 }

@@ -78,10 +78,17 @@ def test_paged_equals_contiguous_and_oracle(name, pages_per_tile):
     ps = plan.problem.tile_k * pages_per_tile
     _case("paged", name=name, page_size=ps)
     pool = make_pool(w, ps, seed=pages_per_tile)
-    o, lse = run_paged(w, d, plan, pool, ps)
+    import mask_planned_block_amd as mpb
+    ws = torch.empty(mpb.flex_attn_fwd_paged_workspace_size(plan, 1) + 256, dtype=torch.uint8,
+                     device="cuda")
+    o, lse = run_paged(w, d, plan, pool, ps, workspace=ws)
     o_ref, l_ref = G.run_attention(w, d, plan)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), "paged != contiguous"
+    # a second call reuses the lists the first one remapped into the workspace
+    o2, l2 = run_paged(w, d, plan, pool, ps, workspace=ws, remap=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o_ref) and torch.equal(l2, l_ref), "reused remap differs"
     O, L = oracle.attention(w)
     G.compare_attention(w, O, L, G.flat_o(w, o), lse.cpu().numpy().astype(np.float64), name)
 
