@@ -206,10 +206,11 @@ __device__ inline uint32_t range_bits(int lo, int hi) {
   return upto & ~((1u << lo) - 1u);
 }
 
-// OR tiles [t0, t1) into a 128-tile window starting at tile tg.
-__device__ inline void set_tiles(uint32_t (&m)[4], int t0, int t1, int tg) {
+// OR tiles [t0, t1) into the window of WW 32-bit words starting at tile tg.
+template <int WW>
+__device__ inline void set_tiles(uint32_t (&m)[WW], int t0, int t1, int tg) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
+  for (int x = 0; x < WW; ++x) {
     const int w0 = tg + 32 * x;
     const int lo = max(t0, w0), hi = min(t1, w0 + 32);
     if (hi > lo) m[x] |= range_bits(lo - w0, hi - w0);
@@ -240,16 +241,20 @@ __device__ inline uint32_t wave_and(uint32_t x) {
 }
 
 // Classification of one (mask head, Q plan row): one wavefront, lanes own rows
-// lane + 64t.  Tiles are handled in windows of 128 (four 32-bit words): for
-// each window a lane walks its row's intervals (read 8 at a time, coalesced
-// across lanes), merges touching intervals into runs, and ORs the tiles each
-// run touches ("any") or fully covers ("full") into its words.  Across the
-// wavefront the "any" words are OR-ed and the "full" words AND-ed: a tile is
-// visible if any row sees part of it and full if every one of the T_Q rows
-// covers it, which needs every row in bounds (rows past q_len contribute
-// nothing) and the tile inside k_len (no run extends past k_len).  §2 order
-// and bounds of every endpoint are checked on the way.
-template <int RPL>
+// lane + 64t.  Tiles are handled in windows of 32*WW (WW 32-bit words; 4 when
+// a sample has at most 128 K tiles, else 8, so the 256 tiles of an 8192-key
+// sample at 32-wide tiles take one pass over the endpoints): for
+// each window a lane walks its rows' intervals, 64/RPL at a time with the
+// loads of all its rows issued together (coalesced across lanes, so a row's
+// intervals cost one memory round trip per batch), merges touching
+// intervals into runs, and ORs the tiles each run touches ("any") or fully
+// covers ("full") into its words.  Across the wavefront the "any" words are
+// OR-ed and the "full" words AND-ed: a tile is visible if any row sees part
+// of it and full if every one of the T_Q rows covers it, which needs every
+// row in bounds (rows past q_len contribute nothing) and the tile inside
+// k_len (no run extends past k_len).  §2 order and bounds of every endpoint
+// are checked on the way.
+template <int RPL, int WW>
 __device__ inline void classify_row(const PlanGeo& g, const int32_t* __restrict__ mf,
                                     const PlanDev& d, const PlanWork& w, int hm, int row,
                                     int lane) {
@@ -272,70 +277,83 @@ __device__ inline void classify_row(const PlanGeo& g, const int32_t* __restrict_
   uint32_t err = 0;
   int pc = 0, fc = 0, first_p = -1, first_f = -1;
   const int64_t wbase = ((int64_t)hm * g.upper_rows + row) * g.words_k;
-  for (int tg = 0; tg < nk; tg += 128) {
-    uint32_t any_m[4] = {0u, 0u, 0u, 0u};
-    uint32_t full_m[4] = {~0u, ~0u, ~0u, ~0u};   // AND identity
+  for (int tg = 0; tg < nk; tg += 32 * WW) {
+    uint32_t any_m[WW], rf[RPL][WW];
 #pragma unroll
-    for (int t = 0; t < RPL; ++t) {
-      if (!exists[t]) continue;                    // not a row of the tile
-      uint32_t rf[4] = {0u, 0u, 0u, 0u};
-      if (valid[t]) {
-        // A run [a, b) touches tiles a/T .. (b-1)/T and fully covers
-        // ceil(a/T) .. b/T - 1 (clamped to [0, nk] for malformed input).
-        auto flush = [&](int a, int b) {
-          if (b <= a) return;
-          const int t0 = min(max(a / T, 0), nk), t1 = min(max((b - 1) / T + 1, 0), nk);
-          set_tiles(any_m, t0, t1, tg);
-          const int f0 = min(max((a + T - 1) / T, 0), nk), f1 = min(max(b / T, 0), nk);
-          set_tiles(rf, f0, f1, tg);
-        };
-        int run_a = 0, run_b = 0;  // open run, empty when run_b <= run_a
-        int prev = 0;
-        constexpr int kBatch = 8;
-        for (int p0 = 0; p0 < nint; p0 += kBatch) {
-          int sv[kBatch], ev[kBatch];
+    for (int x = 0; x < WW; ++x) {
+      any_m[x] = 0u;
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            const int p = p0 + u;
-            sv[u] = 0;
-            ev[u] = 0;
-            if (p < nint) {
-              if (p > 0) sv[u] = col[t][(int64_t)(2 * p - 1) * g.total_q];
-              ev[u] = col[t][(int64_t)(2 * p) * g.total_q];
-            }
-          }
+      for (int t = 0; t < RPL; ++t) rf[t][x] = 0u;
+    }
+    // open run per row, empty when run_b <= run_a; last endpoint seen
+    int run_a[RPL], run_b[RPL], prev[RPL];
 #pragma unroll
-          for (int u = 0; u < kBatch; ++u) {
-            const int p = p0 + u;
-            if (p >= nint) break;
-            const int s = sv[u], e = ev[u];
-            if (tg == 0) {
-              if (p > 0) {
-                if (s < prev) err |= MPB_DEVERR_ORDER;
-                if (s < 0 || s > rg.k_len) err |= MPB_DEVERR_RANGE;
-              }
-              if (e < s) err |= MPB_DEVERR_ORDER;
-              if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
-            }
-            prev = e;
-            if (e <= s) continue;                 // empty interval
-            if (run_b > run_a && s == run_b) {
-              run_b = e;                          // touching: extend the run
-            } else {
-              flush(run_a, run_b);
-              run_a = s;
-              run_b = e;
-            }
+    for (int t = 0; t < RPL; ++t) run_a[t] = run_b[t] = prev[t] = 0;
+    // A run [a, b) touches tiles a/T .. (b-1)/T and fully covers
+    // ceil(a/T) .. b/T - 1 (clamped to [0, nk] for malformed input).
+    auto flush = [&](int t, int a, int b) {
+      if (b <= a) return;
+      const int t0 = min(max(a / T, 0), nk), t1 = min(max((b - 1) / T + 1, 0), nk);
+      set_tiles(any_m, t0, t1, tg);
+      const int f0 = min(max((a + T - 1) / T, 0), nk), f1 = min(max(b / T, 0), nk);
+      set_tiles(rf[t], f0, f1, tg);
+    };
+    constexpr int kBatch = 16 / RPL;   // intervals per lane in flight
+    for (int p0 = 0; p0 < nint; p0 += kBatch) {
+      int sv[RPL][kBatch], ev[RPL][kBatch];
+#pragma unroll
+      for (int t = 0; t < RPL; ++t)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int p = p0 + u;
+          sv[t][u] = 0;
+          ev[t][u] = 0;
+          if (valid[t] && p < nint) {
+            if (p > 0) sv[t][u] = col[t][(int64_t)(2 * p - 1) * g.total_q];
+            ev[t][u] = col[t][(int64_t)(2 * p) * g.total_q];
           }
         }
-        flush(run_a, run_b);
+#pragma unroll
+      for (int t = 0; t < RPL; ++t) {
+        if (!valid[t]) continue;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int p = p0 + u;
+          if (p >= nint) break;
+          const int s = sv[t][u], e = ev[t][u];
+          if (tg == 0) {
+            if (p > 0) {
+              if (s < prev[t]) err |= MPB_DEVERR_ORDER;
+              if (s < 0 || s > rg.k_len) err |= MPB_DEVERR_RANGE;
+            }
+            if (e < s) err |= MPB_DEVERR_ORDER;
+            if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
+          }
+          prev[t] = e;
+          if (e <= s) continue;                 // empty interval
+          if (run_b[t] > run_a[t] && s == run_b[t]) {
+            run_b[t] = e;                       // touching: extend the run
+          } else {
+            flush(t, run_a[t], run_b[t]);
+            run_a[t] = s;
+            run_b[t] = e;
+          }
+        }
       }
-#pragma unroll
-      for (int x = 0; x < 4; ++x) full_m[x] &= rf[x];
     }
-    uint32_t vis_w[4], full_w[4];
+    uint32_t full_m[WW];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < WW; ++x) full_m[x] = ~0u;   // AND identity
+#pragma unroll
+    for (int t = 0; t < RPL; ++t) {
+      if (!exists[t]) continue;                 // not a row of the tile
+      if (valid[t]) flush(t, run_a[t], run_b[t]);
+#pragma unroll
+      for (int x = 0; x < WW; ++x) full_m[x] &= rf[t][x];
+    }
+    uint32_t vis_w[WW], full_w[WW];
+#pragma unroll
+    for (int x = 0; x < WW; ++x) {
       vis_w[x] = wave_or(any_m[x]);
       full_w[x] = wave_and(full_m[x]);
       const int w0 = tg + 32 * x;
@@ -348,13 +366,16 @@ __device__ inline void classify_row(const PlanGeo& g, const int32_t* __restrict_
       if (first_p < 0 && part) first_p = w0 + __ffs(part) - 1;
       if (first_f < 0 && full_w[x]) first_f = w0 + __ffs(full_w[x]) - 1;
     }
-    if (lane < 4) {
-      const int x = lane;
-      const int w0 = tg + 32 * x;
-      if (w0 < nk) {
-        w.vis_bits[wbase + (w0 >> 5)] = x == 0 ? vis_w[0] : x == 1 ? vis_w[1] : x == 2 ? vis_w[2] : vis_w[3];
-        w.full_bits[wbase + (w0 >> 5)] = x == 0 ? full_w[0] : x == 1 ? full_w[1] : x == 2 ? full_w[2] : full_w[3];
-      }
+    // lane x < WW stores word x of the window (values are uniform)
+    uint32_t my_vis = 0, my_full = 0;
+#pragma unroll
+    for (int x = 0; x < WW; ++x) {
+      my_vis = lane == x ? vis_w[x] : my_vis;
+      my_full = lane == x ? full_w[x] : my_full;
+    }
+    if (lane < WW && tg + 32 * lane < nk) {
+      w.vis_bits[wbase + ((tg + 32 * lane) >> 5)] = my_vis;
+      w.full_bits[wbase + ((tg + 32 * lane) >> 5)] = my_full;
     }
   }
   const uint64_t er = __ballot((err & MPB_DEVERR_RANGE) != 0);
@@ -460,7 +481,7 @@ __device__ inline void publish_offsets(const PlanGeo& g, const PlanDev& d, const
 // `arrive`; the one that draws the last ticket resets the counter, sees
 // every other workgroup's results and runs publish_offsets.  No workgroup
 // waits for another, so the grid always drains.
-template <int RPL>
+template <int RPL, int WW>
 __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
                                                             const int32_t* __restrict__ mf,
                                                             PlanDev d, PlanWork w, int32_t* arrive,
@@ -474,7 +495,7 @@ __global__ __launch_bounds__(256) void plan_classify_kernel(PlanGeo g,
     const int hm = item / g.upper_rows;
     const int row = item - hm * g.upper_rows;
     if (hm < g.mask_heads && row < rows_total_of(g, d))
-      classify_row<RPL>(g, mf, d, w, hm, row, lane);
+      classify_row<RPL, WW>(g, mf, d, w, hm, row, lane);
   }
 
   // Every wavefront waits for its stores to complete; the workgroup's ticket
@@ -1657,12 +1678,17 @@ hipError_t launch_plan_classify(const PlanGeo& g, const int32_t* mask_func, cons
   const int64_t items = (int64_t)g.mask_heads * g.upper_rows;
   // At least one workgroup, so the header is always published.
   const dim3 grid((unsigned)(items > 0 ? (items + 3) / 4 : 1)), block(256);
+  // 128-tile windows when every sample fits in one, else 256-tile windows
+  const bool wide = g.nk_max > 128;
+#define MPB_CLASSIFY(R, WW_) \
+  hipLaunchKernelGGL((plan_classify_kernel<R, WW_>), grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq)
   switch (rows_per_lane(g.tile_q)) {
-    case 1: hipLaunchKernelGGL(plan_classify_kernel<1>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
-    case 2: hipLaunchKernelGGL(plan_classify_kernel<2>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
-    case 4: hipLaunchKernelGGL(plan_classify_kernel<4>, grid, block, 0, s, g, mask_func, d, w, arrive, host_slot, seq); break;
+    case 1: if (wide) MPB_CLASSIFY(1, 8); else MPB_CLASSIFY(1, 4); break;
+    case 2: if (wide) MPB_CLASSIFY(2, 8); else MPB_CLASSIFY(2, 4); break;
+    case 4: if (wide) MPB_CLASSIFY(4, 8); else MPB_CLASSIFY(4, 4); break;
     default: return hipErrorInvalidValue;
   }
+#undef MPB_CLASSIFY
   return hipGetLastError();
 }
 
