@@ -262,7 +262,8 @@ size_t flex_attn_fwd_workspace_size(const mpb_plan* plan);
  *   problem   geometry of q/k/v/o as the caller sees it; must equal the plan's
  *             binding field by field (tile_q/tile_k may be 0) and the current
  *             device must be the plan's, else MPB_ERR_SIGNATURE_MISMATCH.
- *   q,k,v     device, layout per `problem` (bf16 or fp32 per dtype).
+ *   q,k,v     device, layout per `problem` (bf16 or fp32 per dtype); k and
+ *             v may be NULL when total_k is 0 (nothing is then read).
  *   o         device, same layout and dtype as q.
  *   lse       device float32 [heads_q][total_q], natural log of the sum of
  *             exp(score) over visible keys (scores after score_mod).  A row

@@ -1106,7 +1106,8 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
       !attn_variant_exists(b.dtype, b.head_dim, b.tile_q, b.tile_k))
     return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan payload/scheduler signature does not match "
                                             "this forward consumer");
-  if (plan->num_tasks > 0 && (!q || !k || !v || !o || !lse))
+  // k and v are never read when there are no keys (every row is then empty)
+  if (plan->num_tasks > 0 && (!q || !o || !lse || (b.total_k > 0 && (!k || !v))))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
   const size_t remap_bytes = paged ? paged_remap_bytes(plan) : 0;
   const size_t ws_need =
