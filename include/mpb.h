@@ -390,6 +390,8 @@ size_t flex_attn_bwd_workspace_size(const mpb_plan* plan);
  *             device and tile checked as for flex_attn_fwd.  bf16 only, at
  *             the forward's bf16 tile geometries (else MPB_ERR_UNSUPPORTED).
  *   q,k,v     device bf16, the forward's inputs, layout per `problem`.
+ *             Tensors of an empty side may be NULL: q, o, lse, dout, dq when
+ *             total_q is 0; k, v, dk, dv when total_k is 0.
  *   o, lse    the forward's outputs for these inputs (flex_attn_fwd).
  *   dout      device bf16, layout of o: the gradient of the loss w.r.t. O.
  *   dq        device bf16, layout of q (overwritten).

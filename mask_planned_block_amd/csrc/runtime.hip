@@ -1363,9 +1363,13 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
   if (!attn_bwd_variant_exists(b.dtype, b.head_dim, b.tile_q, b.tile_k))
     return fail(MPB_ERR_UNSUPPORTED, "no gfx950 backward consumer for dtype %d, head_dim %d, "
                 "tile %dx%d", b.dtype, b.head_dim, b.tile_q, b.tile_k);
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv)
+  // tensors of an empty side are never touched (no Q rows: dK = dV = 0 only;
+  // no keys: dQ = 0 only)
+  if ((b.total_q > 0 && (!q || !o || !lse || !dout || !dq)) ||
+      (b.total_k > 0 && (!k || !v || !dk || !dv)))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL");
-  if (workspace_bytes < flex_attn_bwd_workspace_size(plan) || !workspace)
+  if (workspace_bytes < flex_attn_bwd_workspace_size(plan) ||
+      (flex_attn_bwd_workspace_size(plan) > 0 && !workspace))
     return fail(MPB_ERR_WORKSPACE, "workspace of %zu bytes needed",
                 flex_attn_bwd_workspace_size(plan));
   if (!std::isfinite(scale) || !(scale > 0.0f))

@@ -104,3 +104,22 @@ def test_zero_length_sequences():
         assert torch.all(o == 0).item() and torch.all(lse == -float("inf")).item()
         G.compare_attention(w, O, L, G.flat_o(w, o), lse.cpu().numpy().astype(np.float64),
                             "Sk=0 S=%s" % sp)
+
+
+def test_backward_zero_length_sides():
+    """Backward with no Q rows: every K row sees nothing, dK = dV = 0; with
+    no keys: every row is empty, dQ = 0."""
+    import mask_planned_block_amd as mpb
+    for sq, sk in ((0, 300), (150, 0)):
+        nf = np.zeros((1, 1, 2 * sq), np.int32)
+        w = W.custom(nf, batch=2, seqlen_q=sq, seqlen_k=sk, heads_q=2, head_dim=128,
+                     dtype=W.DTYPE_BF16, seed=45)
+        _case("bwd_empty_side", sq=sq, sk=sk)
+        d = G.device_inputs(w)
+        plan = G.build_plan(w, d, build_backward=True)
+        o, lse = G.run_attention(w, d, plan)
+        dout = torch.from_numpy(W.grad_output(w)).to(torch.bfloat16).reshape(d["q"].shape).cuda()
+        dq, dk, dv = mpb.flex_attn_bwd(plan, d["q"], d["k"], d["v"], o, lse, dout, scale=w.scale)
+        torch.cuda.synchronize()
+        for t in (dq, dk, dv):
+            assert torch.all(t == 0).item()
