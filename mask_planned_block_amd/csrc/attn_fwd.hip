@@ -54,6 +54,12 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kNegInf = -__builtin_huge_valf();
 // Lazy rescale threshold in log2 units: P values stay <= 2^8.
 constexpr float kRescaleSlack = 8.0f;
+// A weight exp2(u - m) with u more than this far below the reference max m
+// is exactly 0 in fp32 (anything below 2^-149 underflows past the smallest
+// denormal), so a tile whose scores all lie that far below it adds nothing to
+// O or to the row sum and leaves the max alone: skipping it changes no bit of
+// the result.
+constexpr float kNegligibleLog2 = 200.0f;
 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
@@ -421,9 +427,11 @@ struct RowState {
 
 // Softmax of one 32-row Q block over one K tile: score_mod and (MASKED) the
 // predicate, online max with lazy rescale of the block's O, exponentials,
-// P in the MFMA operand type and the row sum.
+// P in the MFMA operand type and the row sum.  Returns false, with P zero and
+// the state untouched, when every weight of the block would be exactly 0
+// (all scores kNegligibleLog2 below the reference max, or all masked).
 template <class Ops, int MOD, bool MASKED>
-__device__ __attribute__((always_inline)) inline void softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
+__device__ __attribute__((always_inline)) inline bool softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
                                      const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
                                      f32x16 (&o)[Ops::D / 32], RowState& rs,
                                      typename Ops::PBlock& pb) {
@@ -453,6 +461,20 @@ __device__ __attribute__((always_inline)) inline void softmax_block(const AttnPa
       }
     mt = pair_max(mt);
   }
+  // Only a predicate (a fully masked 32-row block) or an ALiBi bias (keys far
+  // from the row) makes a whole block negligible often; elsewhere the check
+  // is compiled out.
+  constexpr bool kCheck = MASKED || MOD == kModAlibi || MOD == kModSoftcapAlibi ||
+                          MOD == kModAlibiSoftcap;
+  if constexpr (kCheck) {
+    const bool negligible = mt == kNegInf || mt < rs.m - kNegligibleLog2;
+    if (__builtin_amdgcn_ballot_w64(!negligible) == 0) {
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) acc[kk] = f32x16{};
+      Ops::to_p(pb, acc);
+      return false;
+    }
+  }
   // Lazy rescale: the reference max only moves when the row max grows by more
   // than kRescaleSlack, and the wavefront skips the O rescale if no lane
   // moved.  Both lanes of a row see the same mt, so they stay in step.
@@ -478,10 +500,14 @@ __device__ __attribute__((always_inline)) inline void softmax_block(const AttnPa
   }
   Ops::to_p(pb, acc);
   rs.l += Ops::row_sum(pb, acc);
+  return true;
 }
 
 // One K tile for the wavefront's QB Q blocks: scores on MFMA, softmax per
-// block, P.V on MFMA.
+// block, P.V on MFMA.  Tiles whose weights are all exactly 0 for this
+// wavefront's rows are skipped: after the scores (any score_mod), or before
+// them when the score_mod bounds the scores (softcap, then ALiBi: a score is
+// at most the cap plus the tile's largest ALiBi bias).
 template <class Ops, int MOD, bool MASKED>
 __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
                                  const typename Ops::T* kst, const typename Ops::T* vst,
@@ -489,7 +515,17 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
                                  const uint32_t (&mw)[Ops::QB][Ops::NKB],
                                  const float (&kq0)[Ops::QB], float slope,
                                  f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
-  constexpr int QB = Ops::QB, NKB = Ops::NKB;
+  constexpr int QB = Ops::QB, NKB = Ops::NKB, TKV = Ops::TKV;
+  if constexpr (MOD == kModSoftcapAlibi) {
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // the lane's row spans k - q in [kq0 - 4, kq0 + TKV) over this tile
+      const float bias = fmaxf(slope * (kq0[qb] - 4.0f), slope * (kq0[qb] + (float)TKV));
+      need |= !(p.softcap_c2 + bias < rs[qb].m - kNegligibleLog2);
+    }
+    if (__builtin_amdgcn_ballot_w64(need) == 0) return;
+  }
   f32x16 acc[QB][NKB];
   // Wavefront priority: high while issuing MFMAs, low during the softmax, so
   // that of the wavefronts sharing a SIMD the one with matrix work issues
@@ -498,9 +534,12 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
   Ops::qk(acc, qf, kst, lane);
   __builtin_amdgcn_s_setprio(0);
   typename Ops::PFrag pf;
+  bool any = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
-    softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb], pf.p[qb]);
+    any |= softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb],
+                                           pf.p[qb]);
+  if (!any) return;
   __builtin_amdgcn_s_setprio(1);
   Ops::pv(o, pf, vst, lane);
   __builtin_amdgcn_s_setprio(0);
