@@ -505,9 +505,10 @@ __device__ __attribute__((always_inline)) inline bool softmax_block(const AttnPa
 
 // One K tile for the wavefront's QB Q blocks: scores on MFMA, softmax per
 // block, P.V on MFMA.  Tiles whose weights are all exactly 0 for this
-// wavefront's rows are skipped: after the scores (any score_mod), or before
-// them when the score_mod bounds the scores (softcap, then ALiBi: a score is
-// at most the cap plus the tile's largest ALiBi bias).
+// wavefront's rows are skipped: before the scores when the predicate hides
+// the whole tile from them or the score_mod bounds the scores (softcap, then
+// ALiBi: a score is at most the cap plus the tile's largest ALiBi bias), else
+// after the scores.
 template <class Ops, int MOD, bool MASKED>
 __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
                                  const typename Ops::T* kst, const typename Ops::T* vst,
@@ -516,6 +517,15 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
                                  const float (&kq0)[Ops::QB], float slope,
                                  f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
   constexpr int QB = Ops::QB, NKB = Ops::NKB, TKV = Ops::TKV;
+  if constexpr (MASKED) {
+    // no predicate bit set for any of this wavefront's rows: nothing visible
+    uint32_t any_bit = 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < NKB; ++kk) any_bit |= mw[qb][kk];
+    if (__builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
+  }
   if constexpr (MOD == kModSoftcapAlibi) {
     bool need = false;
 #pragma unroll
