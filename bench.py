@@ -513,7 +513,8 @@ def main():
     kb = k2q_bytes(w, pk)
     kmat = k2q_stages["k2q_materialize"]
     kh = pk.info.header
-    plan_k2q = {"build_us_host": round(float(np.median(tbk)) * 1e6, 1), "stages_us": k2q_stages,
+    plan_k2q = {"tile": "%dx%d" % (pk.problem.tile_q, pk.problem.tile_k),
+                "build_us_host": round(float(np.median(tbk)) * 1e6, 1), "stages_us": k2q_stages,
                 "k_rows": int(kh[4]), "partial": int(kh[5]), "full": int(kh[6]),
                 "materialize_algorithmic_bytes": kb,
                 "materialize_gbs": round(kb / (kmat * 1e-6) / 1e9, 1) if kmat > 0 else None,
@@ -570,7 +571,8 @@ def main():
         # algorithmic work: five products per visible pair (S, dP, dV, dQ, dK)
         eff_b = 10.0 * w.head_dim * stats["visible_pairs"]
         dense_b = 10.0 * w.head_dim * stats["dense_pairs"]
-        bwd = {"us": round(bwd_us, 2), "effective_tflops": round(eff_b / bwd_us / 1e6, 3),
+        bwd = {"tile": "%dx%d" % (pbw.problem.tile_q, pbw.problem.tile_k),
+               "us": round(bwd_us, 2), "effective_tflops": round(eff_b / bwd_us / 1e6, 3),
                "dense_equiv_tflops": round(dense_b / bwd_us / 1e6, 3),
                "pct_peak_dense_equiv": round(100 * dense_b / bwd_us / 1e6 / PEAK_BF16_TFLOPS, 2),
                "flops_basis": "10*d per visible pair (S, dP, dV, dQ, dK); the kernels also "

@@ -71,10 +71,12 @@ enum { MPB_DEVERR_SEQLENS = 1, MPB_DEVERR_RANGE = 2, MPB_DEVERR_ORDER = 4 };
  *   "logical blocks and physical tiles"].  0 = the library's choice: tile_q
  *   128 (bf16) or 64 (fp32); tile_k for bf16 head_dim 128 with 128-row
  *   tiles is 32 when the plan has at least 3 tasks (Q tiles x heads_q; THD:
- *   total_q/128 rows) per compute unit of the current device, else 64 (the
- *   32-wide kernel keeps three workgroups per CU and executes fewer masked
- *   entries, the 64-wide one is faster per workgroup); otherwise 64 (fp32
- *   head_dim 128: 32).  mask_plan_info reports the resolved tile. */
+ *   total_q/128 rows) per compute unit of the current device and is built
+ *   without the backward view, else 64 (the 32-wide forward kernel keeps
+ *   three workgroups per CU and executes fewer masked entries, the 64-wide
+ *   one is faster per workgroup, and the backward's dK/dV consumer reads
+ *   every Q and dO tile once per K tile); otherwise 64 (fp32 head_dim 128:
+ *   32).  mask_plan_info reports the resolved tile. */
 typedef struct mpb_problem {
   int32_t layout;
   int32_t dtype;

@@ -343,6 +343,10 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const float kq0 = (float)(j_cur * TKV + 4 * g - qloc);
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
+      // a 32-row K block that the predicate hides from all of this
+      // wavefront's Q rows contributes nothing (every weight is exactly 0)
+      if constexpr (kMasked)
+        if (__builtin_amdgcn_ballot_w64(mw_cur[kk] != 0) == 0) continue;
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       // operand rows read from LDS one k-step ahead of the MFMAs using them
       bf16x8 ak[2], av[2];
@@ -631,6 +635,12 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
       }
     };
     auto item = [&](auto masked) __attribute__((always_inline)) {
+      // a pair whose predicate hides the wavefront's Q half from all of its
+      // K rows contributes nothing (every weight is exactly 0)
+      uint32_t any_bit = 0;
+#pragma unroll
+      for (int w = 0; w < QBW; ++w) any_bit |= mw_cur[w];
+      if (__builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
       if constexpr (QBW == 2) {
         scores(0);
         scores(1);

@@ -453,10 +453,13 @@ int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 12
 // the plan has at least as many tasks (Q tiles x heads) as the GPU holds
 // resident 32-wide workgroups (3 per CU), and slower below that, where each
 // workgroup's own speed decides.  The task count is known from the geometry
-// (for THD, total_q / 128 rows, the lower bound).
-int default_tile_k(const mpb_problem& p, int tq) {
+// (for THD, total_q / 128 rows, the lower bound).  A plan built for the
+// backward keeps 64-wide tiles: its dK/dV consumer streams the Q and dO tiles
+// of every pair once per K tile, so 32-wide K tiles double that traffic and
+// cost far more in the backward than they save in the forward.
+int default_tile_k(const mpb_problem& p, int tq, bool backward) {
   if (p.dtype == MPB_DTYPE_FP32) return p.head_dim > 64 ? 32 : 64;
-  if (p.head_dim == 128 && tq == 128) {
+  if (p.head_dim == 128 && tq == 128 && !backward) {
     const int64_t rows = p.layout == MPB_LAYOUT_BSHD
                              ? (int64_t)p.batch * ((p.seqlen_q + tq - 1) / tq)
                              : (int64_t)p.total_q / tq;
@@ -482,7 +485,8 @@ mpb_signature consumer_signature(const mpb_problem& p, int tq, int tk) {
 }
 
 // §4.1: structural validation only (no element is read on the host).
-mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out) {
+mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out,
+                            bool backward = false) {
   if (!p) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
   if (p->layout != MPB_LAYOUT_BSHD && p->layout != MPB_LAYOUT_THD)
     return fail(MPB_ERR_INVALID_ARGUMENT, "layout %d is neither BSHD (0) nor THD (1)", p->layout);
@@ -517,7 +521,7 @@ mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out) {
   const int tq = p->tile_q ? p->tile_q : default_tile_q(*p);
   if (tq != 32 && tq != 64 && tq != 128 && tq != 256)
     return fail(MPB_ERR_UNSUPPORTED, "tile_q %d not in {32,64,128,256}", tq);
-  const int tk = p->tile_k ? p->tile_k : default_tile_k(*p, tq);
+  const int tk = p->tile_k ? p->tile_k : default_tile_k(*p, tq, backward);
   if (tk < 32 || tk % 32 != 0 || tk > 256)
     return fail(MPB_ERR_UNSUPPORTED, "tile_k %d is not a multiple of 32 in [32,256]", tk);
   if (!attn_variant_exists(p->dtype, p->head_dim, tq, tk))
@@ -579,7 +583,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     return fail(MPB_ERR_INVALID_ARGUMENT, "time_stages must be 0 or 1");
   const bool time_stages = options && options->time_stages;
   int tq = 0, tk = 0;
-  mpb_status st = validate_problem(problem, &tq, &tk);
+  mpb_status st = validate_problem(problem, &tq, &tk, bwd);
   if (st != MPB_OK) return st;
   const mpb_problem& p = *problem;
   if (!mask_func && p.total_q > 0) return fail(MPB_ERR_INVALID_ARGUMENT, "mask_func is NULL");

@@ -110,8 +110,8 @@ def test_forward_unchanged_by_k2q_view():
     w = W.make("varlen_doc", small=True)
     _case("k2q_forward_unchanged")
     d = G.device_inputs(w)
-    p0 = G.build_plan(w, d)
     p1 = G.build_plan(w, d, build_backward=True)
+    p0 = G.build_plan(w, d, p1.problem.tile_q, p1.problem.tile_k)
     o0, l0 = G.run_attention(w, d, p0)
     o1, l1 = G.run_attention(w, d, p1)
     torch.cuda.synchronize()

@@ -313,8 +313,8 @@ def test_signature_and_workspace_errors():
 
 def test_library_tile_choice():
     """tile 0x0 resolves from the task count: bf16 d=128 plans with at least
-    three tasks per CU get 128x32 tiles, smaller ones 128x64; an explicit
-    tile is kept."""
+    three tasks per CU get 128x32 tiles, smaller ones 128x64, and plans with
+    the backward view 128x64; an explicit tile is kept."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for heads, want in ((3 * cus // 16, (128, 32)), (3 * cus // 16 - 1, (128, 64))):
         w = W.custom(np.full((1, 1, 2048), 2048, np.int32), batch=1, seqlen_q=2048,
@@ -325,6 +325,9 @@ def test_library_tile_choice():
         assert (plan.problem.tile_q, plan.problem.tile_k) == want, (heads, want)
         plan = G.build_plan(w, G.device_inputs(w), 64, 64)
         assert (plan.problem.tile_q, plan.problem.tile_k) == (64, 64)
+        # a plan with the backward view keeps 64-wide K tiles
+        plan = G.build_plan(w, G.device_inputs(w), build_backward=True)
+        assert (plan.problem.tile_q, plan.problem.tile_k) == (128, 64)
 
 
 @pytest.mark.parametrize("dtype", [W.DTYPE_FP32, W.DTYPE_BF16])
