@@ -184,6 +184,20 @@ __device__ inline float head_slope(const BwdParams& p, int h) {
 // (its weights are then exactly 0) and for rows past the sample.
 __device__ inline float lse_log2(float lse) { return lse == -kPosInf ? kPosInf : lse * kLog2e; }
 
+// A weight exp2(t - lse2) with t - lse2 below -200 is exactly 0 in fp32 (the
+// smallest denormal is 2^-149), and so is its dS.  With the softcap applied
+// before ALiBi, t <= c2 + slope * (k - q) (c2 = the cap in log2 units), so a
+// block whose every element has that bound 200 below its row's LSE adds
+// nothing to dQ, dK or dV and is skipped before its scores.
+constexpr float kNegligibleLog2 = 200.0f;
+
+// Upper bound of t over the K - Q offsets [k_lo, k_lo + 27] a lane holds in
+// one 32 x 32 block; fmaf rounds the bound the way t itself is rounded, and
+// monotonically, so t never exceeds it.
+__device__ inline float softcap_alibi_bound(float c2, float slope, float k_lo) {
+  return fmaxf(fmaf(slope, k_lo, c2), fmaf(slope, k_lo + 27.0f, c2));
+}
+
 // Weight and dS of one score element; lse2 is the row's LSE in log2 units
 // (+inf for a row that sees nothing).  Full tiles (MASKED = false) keep
 // every element.
@@ -257,6 +271,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
   auto vbuf = [&](auto st) -> __bf16* {
     if constexpr (decltype(st)::value == 0) return v_s0; else return v_s1;
   };
+  __shared__ float s_min[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, lq = lane & 31;
 
@@ -267,11 +282,55 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const int k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
   const int q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
   const int k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
-  const int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
-  const int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
-  const int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
-  const int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
+  int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
+  int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
+  int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
+  int nf = __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
   const int kvh = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
+  const int qloc = m_block * TQ + 32 * wave + lq;   // this lane's sample-local Q row
+  const bool row_in = qloc < q_len;
+  const int64_t stat = (int64_t)h * p.total_q + q_off + qloc;
+  const float lse2 = row_in ? p.lse2[stat] : kPosInf;
+  if constexpr (MOD == kModSoftcapAlibi) {
+    // The tile's least LSE; the K tiles whose every weight in this tile is
+    // negligible (softcap_alibi_bound below the least LSE by 200) are cut
+    // from the ends of both ascending lists before anything is loaded.  With
+    // slope >= 0 the bound grows with the K tile, so such tiles lead the
+    // lists (trail them for slope < 0); only whole leading and trailing runs
+    // are cut.
+    float v = lse2;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fminf(v, __shfl_xor(v, off));
+    if (lane == 0) s_min[wave] = v;
+    __syncthreads();
+    float tm = s_min[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tm = fminf(tm, s_min[w]);
+    const float slope = head_slope<MOD>(p, h);
+    const float thr = tm - kNegligibleLog2;
+    const int q0 = m_block * TQ;
+    auto negligible = [&](int j) {
+      const float lo = (float)(j * TKV - (q0 + TQ - 1)), hi = (float)(j * TKV + TKV - 1 - q0);
+      return fmaxf(fmaf(slope, lo, p.softcap_c2), fmaf(slope, hi, p.softcap_c2)) < thr;
+    };
+    auto trim = [&](const int32_t* idx, int& beg, int& cnt) {
+      for (int front = 1; front >= 0; --front)
+        while (cnt > 0) {
+          bool f = false;
+          if (lane < cnt) f = negligible(idx[front ? beg + lane : beg + cnt - 1 - lane]);
+          const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+          const int run = ~m == 0 ? 64 : __builtin_ctzll(~m);
+          if (front) beg += run;
+          cnt -= run;
+          if (run < 64) break;
+        }
+      beg = __builtin_amdgcn_readfirstlane(beg);
+      cnt = __builtin_amdgcn_readfirstlane(cnt);
+    };
+    trim(p.p_idx, p_beg, np);
+    trim(p.f_idx, f_beg, nf);
+  }
+  const int ntiles = np + nf;
 
   const uint32_t q_rs = (uint32_t)p.heads_q * D * 2;
   const uint32_t kv_rs = (uint32_t)p.heads_k * D * 2;
@@ -283,7 +342,6 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const rsrc_t rk = make_rsrc((const char*)p.k + kh, (uint32_t)k_len * kv_rs);
   const rsrc_t rv = make_rsrc((const char*)p.v + kh, (uint32_t)k_len * kv_rs);
 
-  const int qloc = m_block * TQ + 32 * wave + lq;   // this lane's sample-local Q row
   const uint32_t q_row_off = (uint32_t)qloc * q_rs;
   auto tile_j = [&](int t) {
     return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
@@ -315,9 +373,6 @@ void attn_bwd_dq_kernel(BwdParams p) {
   bf16x8 qf[DS], df[DS];
   load_row_frags<D>(qf, rq, q_row_off, g);
   load_row_frags<D>(df, rdo, q_row_off, g);
-  const bool row_in = qloc < q_len;
-  const int64_t stat = (int64_t)h * p.total_q + q_off + qloc;
-  const float lse2 = row_in ? p.lse2[stat] : kPosInf;
   const float dqv = row_in ? p.dvec[stat] : 0.0f;
   const float slope = head_slope<MOD>(p, h);
 
@@ -347,6 +402,11 @@ void attn_bwd_dq_kernel(BwdParams p) {
       // wavefront's Q rows contributes nothing (every weight is exactly 0)
       if constexpr (kMasked)
         if (__builtin_amdgcn_ballot_w64(mw_cur[kk] != 0) == 0) continue;
+      // ... and so does one whose weights are all negligible
+      if constexpr (MOD == kModSoftcapAlibi) {
+        const float bound = softcap_alibi_bound(p.softcap_c2, slope, kq0 + (float)(32 * kk));
+        if (__builtin_amdgcn_ballot_w64(!(bound < lse2 - kNegligibleLog2)) == 0) continue;
+      }
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       // operand rows read from LDS one k-step ahead of the MFMAs using them
       bf16x8 ak[2], av[2];
@@ -503,6 +563,7 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
     }
     return Item{0, 0, -1};
   };
+
   // Q, dO, LSE and Dq rows of an item into one stage (rows past q_len land as
   // zeros and are never kept: their predicate bits are 0 and tail Q tiles
   // are never full).
@@ -641,6 +702,25 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int w = 0; w < QBW; ++w) any_bit |= mw_cur[w];
       if (__builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
+      // ... and so does one whose weights are all negligible: the bound over
+      // the lane's 16 elements of each block against its 16 rows' least LSE
+      if constexpr (MOD == kModSoftcapAlibi) {
+        bool need = false;
+#pragma unroll
+        for (int w = 0; w < QBW; ++w) {
+          const int qb = qh * QBW + w;
+          float lmin = kPosInf;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const float4 l4 = *(const float4*)&ls[32 * qb + 8 * a + 4 * g];
+            lmin = fminf(lmin, fminf(fminf(l4.x, l4.y), fminf(l4.z, l4.w)));
+          }
+          const float bound =
+              softcap_alibi_bound(p.softcap_c2, slope, kq0 - (float)(32 * qb + 27));
+          need |= !(bound < lmin - kNegligibleLog2);
+        }
+        if (__builtin_amdgcn_ballot_w64(need) == 0) return;
+      }
       if constexpr (QBW == 2) {
         scores(0);
         scores(1);

@@ -208,3 +208,23 @@ def test_backward_full_sampled_and_sums(name):
             if w.softcap == 0 and w.alibi_slopes is None:
                 ksum = dk[ko:ko + kl, g].sum(axis=0)
                 assert np.all(np.abs(ksum) <= 1e-2 * np.abs(dk[ko:ko + kl, g]).sum(axis=0) + 1e-6)
+
+
+@pytest.mark.parametrize("alibi_before_softcap", [False, True])
+def test_backward_steep_alibi_negligible_blocks(alibi_before_softcap):
+    """Steep ALiBi slopes after a softcap bound every score of most blocks far
+    below the row's LSE: their weights and dS are exactly zero in fp32, and
+    the dQ and dK/dV kernels skip them before the scores.  The gradients must
+    still match the oracle, fully masked rows included (ALiBi inside the cap
+    bounds nothing and skips nothing: the same case as a control)."""
+    B, S, H = 2, 700, 4
+    q_local = np.tile(np.arange(S), B)
+    mf = np.stack([np.minimum(q_local + 1, 16), np.minimum(q_local + 1, 16), q_local + 1])
+    mf[:, :3] = 0                       # three fully masked rows
+    w = W.custom(mf[None].astype(np.int32), batch=B, seqlen_q=S, seqlen_k=S, heads_q=H,
+                 head_dim=128, dtype=W.DTYPE_BF16, seed=47, softcap=20.0,
+                 alibi=np.array([8.0, 2.0, 0.5, 0.01], np.float32),
+                 alibi_before_softcap=alibi_before_softcap)
+    _case("bwd_steep_alibi", alibi_before_softcap=alibi_before_softcap)
+    ref, got = _check(w)
+    assert np.all(got[0][:3] == 0.0)     # dQ of the fully masked rows
