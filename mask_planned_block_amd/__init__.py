@@ -332,9 +332,23 @@ def flex_attn_fwd_workspace_size(plan: MaskPlan) -> int:
     return int(_lib.flex_attn_fwd_workspace_size(plan.handle))
 
 
+_CALL_PROBLEMS = {}
+
+
 def _call_problem(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor) -> Problem:
     """Geometry of the call as the tensors show it (checked against the plan
-    binding by the library)."""
+    binding by the library).  Problems are reused across calls and plans with
+    the same binding, shapes and dtype (the library only reads them)."""
+    key = (bytes(plan._bound), q.shape, k.shape, q.dtype)
+    prob = _CALL_PROBLEMS.get(key)
+    if prob is None:
+        if len(_CALL_PROBLEMS) >= 64:
+            _CALL_PROBLEMS.clear()
+        prob = _CALL_PROBLEMS[key] = _make_call_problem(plan, q, k)
+    return prob
+
+
+def _make_call_problem(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor) -> Problem:
     p = plan._bound
     dt = DTYPE_BF16 if q.dtype == torch.bfloat16 else (DTYPE_FP32 if q.dtype == torch.float32
                                                      else -1)
@@ -382,10 +396,11 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[-2], prob.total_q), dtype=torch.float32, device=q.device)
-    need = plan.workspace_bytes if num_splits is None else \
-        flex_attn_fwd_splitk_workspace_size(plan, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # a given workspace is checked by the library
+        need = plan.workspace_bytes if num_splits is None else \
+            flex_attn_fwd_splitk_workspace_size(plan, num_splits)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     mod = None
     if softcap or alibi_slopes is not None:
         mod = ScoreMod(1 if softcap else 0, float(softcap or 0.0),
