@@ -134,6 +134,22 @@ struct Bf16Ops {
   }
 
   static __device__ inline void store(const Stage&, T*, T*, int) {}
+  // Loads of one operand (K: kv = 0, V: kv = 1) of a tile by NW wavefronts,
+  // with the tile's offset folded into the descriptor (built on the scalar
+  // unit) so the per-lane offsets stay loop invariant: lane_off(kv, c, ...)
+  // is the lane's byte offset within the tile for load instruction c of
+  // wavefront `wave`.
+  static __device__ inline uint32_t lane_off(int kv, int c, int wave, int lane, uint32_t rs) {
+    const int r = (c * NW + wave) * RPI + lane / CH;
+    return (uint32_t)r * rs + (uint32_t)(((lane % CH) ^ (kv ? vswz(r) : kswz(r))) * 16);
+  }
+  static __device__ inline void load_op(T* dst, rsrc_t r, const uint32_t (&voff)[KI], int wave) {
+#pragma unroll
+    for (int c = 0; c < KI; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)&dst[(c * NW + wave) * RPI * D], 16,
+          (int)voff[c], 0, 0, 0);
+  }
 
   static __device__ inline void load_q(QFrag& qf, rsrc_t rq, const uint32_t (&row_off)[QB],
                                        int b2) {
@@ -145,7 +161,7 @@ struct Bf16Ops {
             __builtin_bit_cast(bf16x8, bload16(rq, row_off[qb] + (16 * s + 8 * b2) * ESZ));
   }
 
-  // K fragments are read from LDS one k-step ahead of the MFMAs using them.
+  // K fragments are read from LDS two k-steps ahead of the MFMAs using them.
   static __device__ inline void qk(f32x16 (&acc)[QB][NKB], const QFrag& qf, const T* kst,
                                    int lane) {
     // row kk*32 + lane%32, logical chunk 2s + lane/32, at chunk (2s) ^ x
@@ -155,24 +171,25 @@ struct Bf16Ops {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) acc[qb][kk] = f32x16{};
-    bf16x8 a[2][NKB];
+    // ring of PF + 1 K-steps: step s + PF is requested while step s computes
+    constexpr int PF = 2, NS = D / 16;
+    bf16x8 a[PF + 1][NKB];
+    auto fetch = [&](int s, bf16x8 (&dst)[NKB]) {
+      const int off = ((2 * s) ^ x) * 8;
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) a[0][kk] = *(const bf16x8*)(kb + kk * 32 * D + x * 8);
+      for (int kk = 0; kk < NKB; ++kk) dst[kk] = *(const bf16x8*)(kb + kk * 32 * D + off);
+    };
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < D / 16) {
-        const int off = ((2 * (s + 1)) ^ x) * 8;
+    for (int s = 0; s < PF; ++s) fetch(s, a[s]);
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk)
-          a[cur ^ 1][kk] = *(const bf16x8*)(kb + kk * 32 * D + off);
-      }
+    for (int s = 0; s < NS; ++s) {
+      if (s + PF < NS) fetch(s + PF, a[(s + PF) % (PF + 1)]);
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          acc[qb][kk] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][kk], qf.q[qb][s], acc[qb][kk], 0, 0, 0);
+          acc[qb][kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s % (PF + 1)][kk], qf.q[qb][s],
+                                                                acc[qb][kk], 0, 0, 0);
     }
   }
 
@@ -210,7 +227,7 @@ struct Bf16Ops {
   // columns 32 db + 16 ((lane/16) % 2) + 4 (r % 4), so lane L receives
   // V[kb + 4 kg + j][32 db + L % 32] for j = 0..3: the 4 K slots of one
   // MFMA operand half, in the K order of the P registers (kb = 32 kk +
-  // 16 m, then + 8 for slots 4..7).  Reads run one MFMA ahead.
+  // 16 m, then + 8 for slots 4..7).  Reads run three MFMAs ahead.
   static __device__ inline void pv(f32x16 (&o)[QB][D / 32], const PFrag& pf, const T* vst,
                                    int lane) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -234,16 +251,18 @@ struct Bf16Ops {
       const v4i16 both[2] = {lo, hi};
       return __builtin_bit_cast(bf16x8, both);
     };
-    bf16x8 a[2];
-    a[0] = frag(0);
+    constexpr int PF = 3;
+    bf16x8 a[PF + 1];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) a[i] = frag(i);
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int cur = i & 1;
-      if (i + 1 < NS) a[cur ^ 1] = frag(i + 1);
+      if (i + PF < NS) a[(i + PF) % (PF + 1)] = frag(i + PF);
       const int db = i / (NKB * 2), kk = (i / 2) % NKB, m = i % 2;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur], pf.p[qb][kk][m], o[qb][db], 0, 0, 0);
+        o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i % (PF + 1)], pf.p[qb][kk][m],
+                                                            o[qb][db], 0, 0, 0);
     }
   }
 
@@ -280,6 +299,7 @@ struct F32Ops {
 
   static constexpr int KELEMS = TKV * KP, VELEMS = TKV * VP;   // LDS elements per stage
   static constexpr bool kDirectLds = false;  // tiles pass through registers
+  static constexpr int KI = 1;               // (lane offsets of direct LDS loads: unused)
   struct QFrag { float q[QB][D / 2]; };
   struct Stage { u32x4 k[KCH]; u32x4 v[KCH]; };
   typedef f32x16 PBlock[NKB];
@@ -573,6 +593,102 @@ __device__ inline void store_o_f32(rsrc_t ro, uint32_t row_off, const f32x16 (&o
     }
 }
 
+// One task of the plan's launch order (or one Split-K part of it): the
+// geometry and tile-list ranges of its record, scalar in every lane.
+struct TaskCtx {
+  int m_block, h, g, q_off, k_off, q_len, k_len;
+  int p_beg, np, f_beg, ntiles, j_first;
+  int split;
+};
+
+// Reads record blockIdx.x (SPLIT: record blockIdx.x % tasks_padded, part
+// blockIdx.x / tasks_padded, cut to positions [s*n/S, (s+1)*n/S) of the
+// list).  Returns false for the padding workgroups of a Split-K launch.
+template <bool SPLIT>
+__device__ inline bool read_task(const AttnParams& p, TaskCtx& c) {
+  int task = blockIdx.x;
+  c.split = 0;
+  if constexpr (SPLIT) {
+    c.split = blockIdx.x / p.tasks_padded;
+    task = blockIdx.x - c.split * p.tasks_padded;
+    if (task >= p.num_tasks) return false;   // padding of the last task row (whole workgroup)
+  }
+  const int32_t* rec = p.task_rec + (int64_t)task * kTaskRecInts;
+  c.m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);
+  c.h = __builtin_amdgcn_readfirstlane(rec[kRecHead]);
+  c.q_off = __builtin_amdgcn_readfirstlane(rec[kRecQOff]);
+  c.k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
+  c.q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
+  c.k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
+  c.p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
+  c.np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
+  c.f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
+  c.ntiles = c.np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
+  c.j_first = __builtin_amdgcn_readfirstlane(rec[kRecFirstTile]);
+  c.g = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
+  if constexpr (SPLIT) {
+    // positions [t0, t1) of the list: partial positions [t0, min(t1, np)),
+    // full positions [max(t0, np), t1)
+    const int t0 = c.split * c.ntiles / p.num_splits;
+    const int t1 = (c.split + 1) * c.ntiles / p.num_splits;
+    const int f0 = t0 > c.np ? t0 : c.np;
+    const int np_s = (t1 < c.np ? t1 : c.np) - t0;
+    c.p_beg += t0;
+    c.f_beg += f0 - c.np;
+    c.np = np_s > 0 ? np_s : 0;
+    c.ntiles = t1 - t0;
+    c.j_first = __builtin_amdgcn_readfirstlane(
+        c.ntiles == 0 ? -1 : (c.np > 0 ? p.p_idx[c.p_beg] : p.f_idx[c.f_beg]));
+  }
+  return true;
+}
+
+// Buffer descriptor of pool tile `phys` holding logical K tile j of a paged
+// sample: it covers only the rows below the sample's k_len, so loads past it
+// read zero as in the contiguous case; an unmapped entry (phys < 0) gets an
+// empty descriptor, its rows read zero.
+template <int TKV>
+__device__ inline rsrc_t paged_tile_rsrc(const char* pool, int j, int phys, int k_len,
+                                         uint32_t kv_rs) {
+  const int rows = k_len - j * TKV;
+  const uint32_t n = phys < 0 ? 0u : (uint32_t)(rows < TKV ? rows : TKV) * kv_rs;
+  return make_rsrc(pool + (int64_t)(phys < 0 ? 0 : phys) * TKV * kv_rs, n);
+}
+
+// Epilogue of a task: O = acc / l, LSE = m + ln l (natural log); empty rows
+// get 0 / -inf.  Rows past q_len are dropped by the O descriptor's range
+// check.  A Split-K part writes the same for its tiles, in fp32, into its
+// partial-state slice.
+template <class Ops, bool SPLIT>
+__device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t ro,
+                                  const uint32_t (&q_row_off)[Ops::QB], const int (&qloc)[Ops::QB],
+                                  const f32x16 (&o)[Ops::QB][Ops::D / 32],
+                                  const RowState (&rs)[Ops::QB], int b2) {
+  constexpr int D = Ops::D;
+  rsrc_t rout = ro;
+  float* lse_out = p.lse;
+  if constexpr (SPLIT) {
+    const int64_t fq_rs = (int64_t)p.heads_q * D;   // floats per token row
+    float* ob = p.o_part + (int64_t)c.split * p.total_q * fq_rs + (int64_t)c.q_off * fq_rs +
+                (int64_t)c.h * D;
+    rout = make_rsrc(ob, (uint32_t)(c.q_len * fq_rs * 4));
+    lse_out = p.lse_part + (int64_t)c.split * p.heads_q * p.total_q;
+  }
+#pragma unroll
+  for (int qb = 0; qb < Ops::QB; ++qb) {
+    const float l_tot = pair_sum(rs[qb].l);
+    const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
+    if constexpr (SPLIT)
+      store_o_f32<D>(rout, (uint32_t)qloc[qb] * p.heads_q * D * 4, o[qb], inv, b2);
+    else
+      Ops::store_o(rout, q_row_off[qb], o[qb], inv, b2);
+    if (b2 == 0 && qloc[qb] < c.q_len) {
+      lse_out[(int64_t)c.h * p.total_q + c.q_off + qloc[qb]] =
+          l_tot > 0.0f ? (rs[qb].m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
+    }
+  }
+}
+
 // One workgroup per task, in the plan's launch order (record blockIdx.x).
 // SPLIT: one workgroup per (split, task), the splits of the Tessera page's
 // Split-K: workgroup i runs split i / tasks_padded of task i % tasks_padded
@@ -615,39 +731,12 @@ void attn_fwd_kernel(AttnParams p) {
   const int b2 = lane >> 5;
   const int lq = lane & 31;
 
-  int task = blockIdx.x, split = 0;
-  if constexpr (SPLIT) {
-    split = blockIdx.x / p.tasks_padded;
-    task = blockIdx.x - split * p.tasks_padded;
-    if (task >= p.num_tasks) return;   // padding of the last task row (whole workgroup)
-  }
-  const int32_t* rec = p.task_rec + (int64_t)task * kTaskRecInts;
-  const int m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);
-  const int h = __builtin_amdgcn_readfirstlane(rec[kRecHead]);
-  const int q_off = __builtin_amdgcn_readfirstlane(rec[kRecQOff]);
-  const int k_off = __builtin_amdgcn_readfirstlane(rec[kRecKOff]);
-  const int q_len = __builtin_amdgcn_readfirstlane(rec[kRecQLen]);
-  const int k_len = __builtin_amdgcn_readfirstlane(rec[kRecKLen]);
-  int p_beg = __builtin_amdgcn_readfirstlane(rec[kRecPBeg]);
-  int np = __builtin_amdgcn_readfirstlane(rec[kRecPCnt]);
-  int f_beg = __builtin_amdgcn_readfirstlane(rec[kRecFBeg]);
-  int ntiles = np + __builtin_amdgcn_readfirstlane(rec[kRecFCnt]);
-  int j_first = __builtin_amdgcn_readfirstlane(rec[kRecFirstTile]);
-  const int g = __builtin_amdgcn_readfirstlane(rec[kRecKvHead]);
-  if constexpr (SPLIT) {
-    // positions [t0, t1) of the list: partial positions [t0, min(t1, np)),
-    // full positions [max(t0, np), t1)
-    const int t0 = split * ntiles / p.num_splits;
-    const int t1 = (split + 1) * ntiles / p.num_splits;
-    const int f0 = t0 > np ? t0 : np;
-    const int np_s = (t1 < np ? t1 : np) - t0;
-    p_beg += t0;
-    f_beg += f0 - np;
-    np = np_s > 0 ? np_s : 0;
-    ntiles = t1 - t0;
-    j_first = __builtin_amdgcn_readfirstlane(
-        ntiles == 0 ? -1 : (np > 0 ? p.p_idx[p_beg] : p.f_idx[f_beg]));
-  }
+  TaskCtx c;
+  if (!read_task<SPLIT>(p, c)) return;
+  const int m_block = c.m_block, h = c.h, g = c.g, q_off = c.q_off, k_off = c.k_off;
+  const int q_len = c.q_len, k_len = c.k_len;
+  const int p_beg = c.p_beg, np = c.np, f_beg = c.f_beg, ntiles = c.ntiles;
+  const int j_first = c.j_first;
 
   const uint32_t q_rs = (uint32_t)p.heads_q * D * ESZ;   // bytes per Q/O token row
   const uint32_t kv_rs = (uint32_t)p.heads_k * D * ESZ;  // bytes per K/V token row
@@ -662,15 +751,38 @@ void attn_fwd_kernel(AttnParams p) {
   const rsrc_t rk = make_rsrc(kbase, (uint32_t)k_len * kv_rs);
   const rsrc_t rv = make_rsrc(vbase, (uint32_t)k_len * kv_rs);
   // Paged K/V: tile t's rows live in pool tile phys (tile_k rows of the pool,
-  // starting at row phys * TKV); its descriptors cover only the rows below
-  // the sample's k_len, so loads past it read zero as in the contiguous case.
-  // An unmapped entry (phys < 0) gets empty descriptors: its rows read zero.
+  // starting at row phys * TKV).
   const char* kpool = (const char*)p.k + (int64_t)g * D * ESZ;
   const char* vpool = (const char*)p.v + (int64_t)g * D * ESZ;
   auto tile_rsrc = [&](const char* pool, int j, int phys) {
-    const int rows = k_len - j * TKV;
-    const uint32_t n = phys < 0 ? 0u : (uint32_t)(rows < TKV ? rows : TKV) * kv_rs;
-    return make_rsrc(pool + (int64_t)(phys < 0 ? 0 : phys) * TKV * kv_rs, n);
+    return paged_tile_rsrc<TKV>(pool, j, phys, k_len, kv_rs);
+  };
+  // bf16 tiles go straight to LDS: each lane's offsets within a tile are
+  // fixed for the task and the tile's own offset is folded into a
+  // descriptor built on the scalar unit (listed tiles start below k_len)
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t kv_bytes = (uint32_t)k_len * kv_rs;
+  uint32_t koff[Ops::KI], voff[Ops::KI];
+  if constexpr (Ops::kDirectLds) {
+#pragma unroll
+    for (int i = 0; i < Ops::KI; ++i) {
+      koff[i] = Ops::lane_off(0, i, wave_u, tid & 63, kv_rs);
+      voff[i] = Ops::lane_off(1, i, wave_u, tid & 63, kv_rs);
+    }
+  }
+  auto load_tile = [&](typename Ops::Stage& stg, T* kd, T* vd, int j, int phys)
+      __attribute__((always_inline)) {
+    if constexpr (Ops::kDirectLds) {
+      const uint32_t off = (uint32_t)j * TKV * kv_rs;
+      const rsrc_t a = PAGED ? tile_rsrc(kpool, j, phys) : make_rsrc(kbase + off, kv_bytes - off);
+      const rsrc_t b = PAGED ? tile_rsrc(vpool, j, phys) : make_rsrc(vbase + off, kv_bytes - off);
+      Ops::load_op(kd, a, koff, wave_u);
+      Ops::load_op(vd, b, voff, wave_u);
+    } else if constexpr (PAGED) {
+      Ops::load(stg, kd, vd, tile_rsrc(kpool, j, phys), tile_rsrc(vpool, j, phys), 0u, kv_rs, tid);
+    } else {
+      Ops::load(stg, kd, vd, rk, rv, (uint32_t)j * TKV * kv_rs, kv_rs, tid);
+    }
   };
 
   // Sample-local Q row of this lane in each of the wavefront's blocks.
@@ -712,13 +824,7 @@ void attn_fwd_kernel(AttnParams p) {
   // tile waits on the index load before issuing its prefetch.
   int j_ahead = 0, ph_ahead = 0;
   if (ntiles > 0) {
-    if constexpr (PAGED) {
-      const int ph = tile_phys(0);
-      Ops::load(st, k_s0, v_s0, tile_rsrc(kpool, j_cur, ph), tile_rsrc(vpool, j_cur, ph), 0u,
-                kv_rs, tid);
-    } else {
-      Ops::load(st, k_s0, v_s0, rk, rv, (uint32_t)j_cur * TKV * kv_rs, kv_rs, tid);
-    }
+    load_tile(st, k_s0, v_s0, j_cur, PAGED ? tile_phys(0) : 0);
     load_masks(0, mw_cur);
     if (ntiles > 1) {
       j_ahead = tile_j(1);
@@ -755,12 +861,7 @@ void attn_fwd_kernel(AttnParams p) {
     const bool more = t + 1 < ntiles;
     const int j_next = j_ahead;
     if (more) {
-      if constexpr (PAGED)
-        Ops::load(st, kbuf(next), vbuf(next), tile_rsrc(kpool, j_next, ph_ahead),
-                  tile_rsrc(vpool, j_next, ph_ahead), 0u, kv_rs, tid);
-      else
-        Ops::load(st, kbuf(next), vbuf(next), rk, rv, (uint32_t)j_next * TKV * kv_rs, kv_rs,
-                  tid);
+      load_tile(st, kbuf(next), vbuf(next), j_next, ph_ahead);
       load_masks(t + 1, mw_next);
     }
     if (t + 2 < ntiles) {
@@ -818,31 +919,7 @@ void attn_fwd_kernel(AttnParams p) {
     run(std::false_type{}, ntiles);
   }
 
-  // epilogue: O = acc / l, LSE = m + ln l (natural log); empty rows 0 / -inf.
-  // Rows past q_len are dropped by the O descriptor's range check.  A split
-  // writes the same for its tiles, in fp32, into its partial-state slice.
-  rsrc_t rout = ro;
-  float* lse_out = p.lse;
-  if constexpr (SPLIT) {
-    const int64_t fq_rs = (int64_t)p.heads_q * D;   // floats per token row
-    float* ob = p.o_part + (int64_t)split * p.total_q * fq_rs + (int64_t)q_off * fq_rs +
-                (int64_t)h * D;
-    rout = make_rsrc(ob, (uint32_t)(q_len * fq_rs * 4));
-    lse_out = p.lse_part + (int64_t)split * p.heads_q * p.total_q;
-  }
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = pair_sum(rs[qb].l);
-    const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
-    if constexpr (SPLIT)
-      store_o_f32<D>(rout, (uint32_t)qloc[qb] * p.heads_q * D * 4, o[qb], inv, b2);
-    else
-      Ops::store_o(rout, q_row_off[qb], o[qb], inv, b2);
-    if (b2 == 0 && qloc[qb] < q_len) {
-      lse_out[(int64_t)h * p.total_q + q_off + qloc[qb]] =
-          l_tot > 0.0f ? (rs[qb].m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
-    }
-  }
+  write_rows<Ops, SPLIT>(p, c, ro, q_row_off, qloc, o, rs, b2);
 }
 
 // Page-table remap of the plan's K-tile lists (FlexAttention page, paged
@@ -933,15 +1010,18 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(MergeParams p) {
 template <class Ops, bool SPLIT, bool PAGED>
 hipError_t launch_mods(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
   const dim3 g(num_blocks), blk(Ops::NT);
+  auto go = [&](auto m) {
+    hipLaunchKernelGGL((attn_fwd_kernel<Ops, decltype(m)::value, SPLIT, PAGED>), g, blk, 0, s, p);
+    return hipGetLastError();
+  };
   switch (mod) {
-    case kModNone: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModNone, SPLIT, PAGED>), g, blk, 0, s, p); break;
-    case kModSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcap, SPLIT, PAGED>), g, blk, 0, s, p); break;
-    case kModAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibi, SPLIT, PAGED>), g, blk, 0, s, p); break;
-    case kModSoftcapAlibi: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModSoftcapAlibi, SPLIT, PAGED>), g, blk, 0, s, p); break;
-    case kModAlibiSoftcap: hipLaunchKernelGGL((attn_fwd_kernel<Ops, kModAlibiSoftcap, SPLIT, PAGED>), g, blk, 0, s, p); break;
+    case kModNone: return go(std::integral_constant<int, kModNone>{});
+    case kModSoftcap: return go(std::integral_constant<int, kModSoftcap>{});
+    case kModAlibi: return go(std::integral_constant<int, kModAlibi>{});
+    case kModSoftcapAlibi: return go(std::integral_constant<int, kModSoftcapAlibi>{});
+    case kModAlibiSoftcap: return go(std::integral_constant<int, kModAlibiSoftcap>{});
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 // Paged K/V kernels exist for the bf16 consumers only.
