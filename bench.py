@@ -110,21 +110,41 @@ def cpu_baseline(w, tile_q, tile_k, min_seconds=10.0):
     return time.perf_counter() - t0, passes, threads, t_plan, t_attn
 
 
-def mfma_peak(mpb, torch, iters=4000):
-    """Dense bf16 MFMA rate the device sustains: the library's MFMA probe
-    (independent v_mfma_f32_32x32x16_bf16 chains on register operands) on
-    8 workgroups per CU, timed with HIP events; median of 5 launches."""
+PROBE_LIB = os.path.join(ROOT, "mask_planned_block_amd", "libmpb_probe.so")
+
+
+def mfma_probe(workgroups, iters, out, stream):
+    """Launches the MFMA throughput probe of libmpb_probe.so (include/mpb_probe.h,
+    a measurement helper beside the library); returns the launch's flops."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.mpb_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.mpb_mfma_probe.restype = ctypes.c_int
+    if out.numel() < workgroups * 256:
+        raise ValueError("out needs workgroups*256 floats")
+    st = lib.mpb_mfma_probe(int(workgroups), int(iters), ctypes.c_void_p(out.data_ptr()),
+                            ctypes.c_void_p(stream.cuda_stream))
+    if st != 0:
+        raise RuntimeError("mpb_mfma_probe failed with status %d" % st)
+    return workgroups * 4 * iters * 8 * 32768
+
+
+def mfma_peak(torch, iters=4000):
+    """Dense bf16 MFMA rate the device sustains: the MFMA probe (independent
+    v_mfma_f32_32x32x16_bf16 chains on register operands) on 8 workgroups
+    per CU, timed with HIP events; median of 5 launches."""
     import numpy as np
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     wg = 8 * cus
     out = torch.empty(wg * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-    flops = mpb.mfma_probe(wg, 200, out, stream)
+    flops = mfma_probe(wg, 200, out, stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     rates = []
     for _ in range(5):
         e0.record(stream)
-        flops = mpb.mfma_probe(wg, iters, out, stream)
+        flops = mfma_probe(wg, iters, out, stream)
         e1.record(stream)
         torch.cuda.synchronize()
         rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
@@ -597,7 +617,7 @@ def main():
         cold.append(e0.elapsed_time(e1) * 1e3)
     del scratch
     fwd_cold_us = float(np.median(cold)) if cold else None
-    mfma = None if args.no_mfma_probe else mfma_peak(mpb, torch)
+    mfma = None if args.no_mfma_probe else mfma_peak(torch)
 
     if args.copy_calibration_mb > 0:
         # streaming calibration: reads and writes exactly copy_calibration_mb MiB

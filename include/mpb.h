@@ -283,15 +283,25 @@ mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const
                          const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Ablation hook: same contract as flex_attn_fwd.  With force_partial = 1
- * every full tile runs through the partial-tile code path with an all-ones
- * predicate, which measures what the full-tile fast path saves ([FLEX] "full
- * block optimization"; [MPD §6.1]).  Results equal flex_attn_fwd's. */
+/* Ablation hooks: same contracts as flex_attn_fwd / flex_attn_bwd, with
+ * flags selecting slower paths whose results are identical bit for bit:
+ *   MPB_ABLATE_FULL_AS_PARTIAL (forward only): every full tile runs through
+ *     the partial-tile code path with an all-ones predicate, which measures
+ *     what the full-tile fast path saves ([FLEX] "full block optimization";
+ *     [MPD §6.1]);
+ *   MPB_ABLATE_NO_SKIP: the kernels compute every listed tile and block,
+ *     including those they otherwise skip because every weight in them is
+ *     exactly zero in fp32 (a predicate that hides a block from all of a
+ *     wavefront's rows; scores bounded 200 log2 units below the running max
+ *     or the row's LSE), which checks that those skips change nothing (given
+ *     finite V: a skipped 0 * inf would have been NaN).
+ * Unknown flag bits return MPB_ERR_INVALID_ARGUMENT. */
+enum { MPB_ABLATE_FULL_AS_PARTIAL = 1, MPB_ABLATE_NO_SKIP = 2 };
 mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
                                   const void* q, const void* k, const void* v, void* o,
                                   float* lse, float scale, const mpb_score_mod* mod,
                                   void* workspace, size_t workspace_bytes, void* stream,
-                                  int32_t force_partial);
+                                  int32_t flags);
 
 /* Split-K forward [TESS "Split-K", Figure 5; MPD §6.1]: for plans with too
  * few tasks to fill the GPU (short Q against a long K, few heads or
@@ -413,15 +423,14 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
                          const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Measurement helper (not part of the attention path): launches
- * `workgroups` workgroups of four wavefronts, each wavefront issuing
- * iters * 8 independent v_mfma_f32_32x32x16_bf16 (32768 flops each) on
- * register operands, and writes one float per thread to `out` (device,
- * workgroups * 256 floats).  Flops per launch: workgroups * 4 * iters * 8 *
- * 32768; the caller times the launch on `stream` to measure the dense bf16
- * MFMA rate the device sustains.  MPB_ERR_INVALID_ARGUMENT for a
- * non-positive count or NULL out.  Enqueue only. */
-mpb_status mpb_mfma_probe(int32_t workgroups, int32_t iters, float* out, void* stream);
+/* flex_attn_bwd with ablation flags (see flex_attn_fwd_ablation; only
+ * MPB_ABLATE_NO_SKIP applies to the backward). */
+mpb_status flex_attn_bwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
+                                  const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, float scale, const mpb_score_mod* mod,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t flags);
 
 const char* mpb_status_string(mpb_status status);
 const char* mpb_last_error_detail(void);

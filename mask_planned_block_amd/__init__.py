@@ -121,8 +121,7 @@ def _load():
     lib.flex_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_bwd.argtypes = [vp, P(Problem)] + [vp] * 9 + [ctypes.c_float, P(ScoreMod), vp,
                                                               ctypes.c_size_t, vp]
-    lib.mpb_mfma_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
-    lib.mpb_mfma_probe.restype = ctypes.c_int
+    lib.flex_attn_bwd_ablation.argtypes = lib.flex_attn_bwd.argtypes + [ctypes.c_int32]
     lib.mpb_status_string.restype = ctypes.c_char_p
     lib.mpb_status_string.argtypes = [ctypes.c_int]
     lib.mpb_last_error_detail.restype = ctypes.c_char_p
@@ -131,7 +130,8 @@ def _load():
                  "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times", "mask_plan_export_k2q_order",
                  "mask_plan_export_launch_order",
                  "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_fwd_splitk",
-                 "flex_attn_fwd_merge", "flex_attn_fwd_paged", "flex_attn_bwd"):
+                 "flex_attn_fwd_merge", "flex_attn_fwd_paged", "flex_attn_bwd",
+                 "flex_attn_bwd_ablation"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -160,6 +160,24 @@ def _dev_ptr(t: Optional[torch.Tensor], what: str, dtype=None):
                          % (what, "" if dtype is None else " of " + str(dtype), t.device,
                             t.dtype, t.is_contiguous()))
     return t.data_ptr()
+
+
+def _require_shape(t: Optional[torch.Tensor], what: str, shape):
+    """Caller-supplied outputs and per-head arrays must have the size the
+    kernels write or read: the library only sees bare pointers, so an
+    undersized tensor would become an out-of-bounds device access."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (what, tuple(shape), tuple(t.shape)))
+
+
+def _check_slopes(alibi_slopes: Optional[torch.Tensor], heads_q: int):
+    if alibi_slopes is not None and alibi_slopes.numel() < heads_q:
+        raise ValueError("alibi_slopes needs one value per Q head (%d), got %d"
+                         % (heads_q, alibi_slopes.numel()))
+
+
+ABLATE_FULL_AS_PARTIAL = 1
+ABLATE_NO_SKIP = 2
 
 
 def make_problem(layout, dtype, batch, seqlen_q, seqlen_k, total_q, total_k, heads_q, heads_k,
@@ -381,17 +399,24 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
                   alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None,
-                  force_partial: bool = False, num_splits: Optional[int] = None):
+                  force_partial: bool = False, num_splits: Optional[int] = None,
+                  no_skip: bool = False):
     """Block-sparse attention forward over a plan.  Returns (O, LSE[Hq, total_q]).
 
     num_splits=None runs flex_attn_fwd; an int runs flex_attn_fwd_splitk with
-    that many parts (0 = the library's choice).  Allocates O/LSE/workspace
-    with torch when not given (device memory only)."""
+    that many parts (0 = the library's choice).  force_partial / no_skip run
+    flex_attn_fwd_ablation (identical results through slower paths).
+    Allocates O/LSE/workspace with torch when not given (device memory
+    only)."""
     if k.shape != v.shape:
         raise ValueError("k and v must have the same shape")
-    if force_partial and num_splits is not None:
-        raise ValueError("force_partial and num_splits are separate entry points")
+    flags = (ABLATE_FULL_AS_PARTIAL if force_partial else 0) | (ABLATE_NO_SKIP if no_skip else 0)
+    if flags and num_splits is not None:
+        raise ValueError("the ablation flags and num_splits are separate entry points")
     prob = _call_problem(plan, q, k)
+    _require_shape(out, "out", q.shape)
+    _require_shape(lse, "lse", (q.shape[-2], prob.total_q))
+    _check_slopes(alibi_slopes, q.shape[-2])
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -417,8 +442,8 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
             _stream_handle(stream))
     if num_splits is not None:
         _check(_lib.flex_attn_fwd_splitk(*head, int(num_splits), *tail))
-    elif force_partial:
-        _check(_lib.flex_attn_fwd_ablation(*head, *tail, 1))
+    elif flags:
+        _check(_lib.flex_attn_fwd_ablation(*head, *tail, flags))
     else:
         _check(_lib.flex_attn_fwd(*head, *tail))
     return out, lse
@@ -460,6 +485,9 @@ def flex_attn_fwd_paged(plan: MaskPlan, q: torch.Tensor, k_pages: torch.Tensor,
         Tq, Hq, Dq = q.shape
         prob = Problem(LAYOUT_THD, dt, p.batch, p.seqlen_q, p.seqlen_k, Tq, p.total_k, Hq, Hk,
                        Dq, p.mask_heads, p.nfunc, 0, 0)
+    _require_shape(out, "out", q.shape)
+    _require_shape(lse, "lse", (q.shape[-2], prob.total_q))
+    _check_slopes(alibi_slopes, q.shape[-2])
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -498,6 +526,8 @@ def flex_attn_fwd_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
     P, T, H, D = o_parts.shape
     if tuple(lse_parts.shape) != (P, H, T):
         raise ValueError("lse_parts must be [P, H, T] = %s" % ((P, H, T),))
+    _require_shape(out, "out", (T, H, D))
+    _require_shape(lse, "lse", (H, T))
     if out is None:
         out = torch.empty((T, H, D), dtype=out_dtype, device=o_parts.device)
     if lse is None:
@@ -511,16 +541,6 @@ def flex_attn_fwd_merge(o_parts: torch.Tensor, lse_parts: torch.Tensor,
     return out, lse
 
 
-def mfma_probe(workgroups: int, iters: int, out: torch.Tensor, stream=None) -> int:
-    """Launches the bf16 MFMA throughput probe (measurement only); returns
-    the flops of the launch.  out: fp32 device tensor of workgroups*256."""
-    if out.numel() < workgroups * 256:
-        raise ValueError("out needs workgroups*256 floats")
-    _check(_lib.mpb_mfma_probe(int(workgroups), int(iters),
-                               _dev_ptr(out, "out", torch.float32), _stream_handle(stream)))
-    return workgroups * 4 * iters * 8 * 32768
-
-
 def flex_attn_bwd_workspace_size(plan: MaskPlan) -> int:
     return int(_lib.flex_attn_bwd_workspace_size(plan.handle))
 
@@ -531,14 +551,21 @@ def flex_attn_bwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
                   alibi_slopes: Optional[torch.Tensor] = None, alibi_before_softcap=False,
                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                   dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                  stream=None):
+                  stream=None, no_skip: bool = False):
     """Backward of flex_attn_fwd over a plan built with build_backward=True:
     returns (dQ, dK, dV) for the incoming gradient dout (see include/mpb.h).
+    no_skip runs flex_attn_bwd_ablation (identical results, no zero-weight
+    skips).
 
     Allocates the outputs and the workspace with torch when not given."""
     if k.shape != v.shape or dout.shape != q.shape or o.shape != q.shape:
         raise ValueError("k/v, and q/o/dout must have matching shapes")
     prob = _call_problem(plan, q, k)
+    _require_shape(dq, "dq", q.shape)
+    _require_shape(dk, "dk", k.shape)
+    _require_shape(dv, "dv", v.shape)
+    _require_shape(lse, "lse", (q.shape[-2], prob.total_q))
+    _check_slopes(alibi_slopes, q.shape[-2])
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -552,11 +579,14 @@ def flex_attn_bwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
                        _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
                        1 if alibi_before_softcap else 0)
     sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
-    _check(_lib.flex_attn_bwd(
-        plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype),
-        _dev_ptr(v, "v", q.dtype), _dev_ptr(o, "o", q.dtype), _dev_ptr(lse, "lse", torch.float32),
-        _dev_ptr(dout, "dout", q.dtype), _dev_ptr(dq, "dq", q.dtype), _dev_ptr(dk, "dk", q.dtype),
-        _dev_ptr(dv, "dv", q.dtype), sc, ctypes.byref(mod) if mod is not None else None,
-        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream_handle(stream)))
+    args = (plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype),
+            _dev_ptr(v, "v", q.dtype), _dev_ptr(o, "o", q.dtype),
+            _dev_ptr(lse, "lse", torch.float32), _dev_ptr(dout, "dout", q.dtype),
+            _dev_ptr(dq, "dq", q.dtype), _dev_ptr(dk, "dk", q.dtype), _dev_ptr(dv, "dv", q.dtype),
+            sc, ctypes.byref(mod) if mod is not None else None, _dev_ptr(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if no_skip:
+        _check(_lib.flex_attn_bwd_ablation(*args, ABLATE_NO_SKIP))
+    else:
+        _check(_lib.flex_attn_bwd(*args))
     return dq, dk, dv

@@ -1,8 +1,10 @@
 """Builds libmpb.so (HIP, gfx950) in-tree with hipcc.
 
-Every .hip source under csrc/ is compiled to an object in _build/ and linked
-into mask_planned_block_amd/libmpb.so.  Usable as a module
-(``build_library()``) or as a script.
+Every .hip source directly under csrc/ is compiled to an object in _build/ and
+linked into mask_planned_block_amd/libmpb.so; csrc/probe/ holds the MFMA
+throughput probe, linked on its own into libmpb_probe.so (a measurement
+helper for the benchmark, not part of the attention path).  Usable as a
+module (``build_library()``) or as a script.
 """
 from __future__ import annotations
 
@@ -16,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmpb.so")
+PROBE_LIB = os.path.join(PKG, "libmpb_probe.so")
+PROBE_SRC = os.path.join(CSRC, "probe", "mfma_probe.hip")
 ARCH = "gfx950"
 
 COMMON = [
@@ -47,19 +51,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build_library(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build_library(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources() + [PROBE_SRC]
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 5)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -291,7 +291,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const bool row_in = qloc < q_len;
   const int64_t stat = (int64_t)h * p.total_q + q_off + qloc;
   const float lse2 = row_in ? p.lse2[stat] : kPosInf;
-  if constexpr (MOD == kModSoftcapAlibi) {
+  if (MOD == kModSoftcapAlibi && !p.no_skip) {
     // The tile's least LSE; the K tiles whose every weight in this tile is
     // negligible (softcap_alibi_bound below the least LSE by 200) are cut
     // from the ends of both ascending lists before anything is loaded.  With
@@ -401,11 +401,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
       // a 32-row K block that the predicate hides from all of this
       // wavefront's Q rows contributes nothing (every weight is exactly 0)
       if constexpr (kMasked)
-        if (__builtin_amdgcn_ballot_w64(mw_cur[kk] != 0) == 0) continue;
+        if (!p.no_skip && __builtin_amdgcn_ballot_w64(mw_cur[kk] != 0) == 0) continue;
       // ... and so does one whose weights are all negligible
       if constexpr (MOD == kModSoftcapAlibi) {
         const float bound = softcap_alibi_bound(p.softcap_c2, slope, kq0 + (float)(32 * kk));
-        if (__builtin_amdgcn_ballot_w64(!(bound < lse2 - kNegligibleLog2)) == 0) continue;
+        if (!p.no_skip && __builtin_amdgcn_ballot_w64(!(bound < lse2 - kNegligibleLog2)) == 0)
+          continue;
       }
       f32x16 s_acc = f32x16{}, dp_acc = f32x16{};
       // operand rows read from LDS one k-step ahead of the MFMAs using them
@@ -701,11 +702,11 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
       uint32_t any_bit = 0;
 #pragma unroll
       for (int w = 0; w < QBW; ++w) any_bit |= mw_cur[w];
-      if (__builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
+      if (!p.no_skip && __builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
       // ... and so does one whose weights are all negligible: the bound over
       // the lane's 16 elements of each block against its 16 rows' least LSE
       if constexpr (MOD == kModSoftcapAlibi) {
-        bool need = false;
+        bool need = p.no_skip != 0;
 #pragma unroll
         for (int w = 0; w < QBW; ++w) {
           const int qb = qh * QBW + w;

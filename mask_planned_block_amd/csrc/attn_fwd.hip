@@ -488,7 +488,7 @@ __device__ __attribute__((always_inline)) inline bool softmax_block(const AttnPa
                           MOD == kModAlibiSoftcap;
   if constexpr (kCheck) {
     const bool negligible = mt == kNegInf || mt < rs.m - kNegligibleLog2;
-    if (__builtin_amdgcn_ballot_w64(!negligible) == 0) {
+    if (!p.no_skip && __builtin_amdgcn_ballot_w64(!negligible) == 0) {
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) acc[kk] = f32x16{};
       Ops::to_p(pb, acc);
@@ -544,10 +544,10 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) any_bit |= mw[qb][kk];
-    if (__builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
+    if (!p.no_skip && __builtin_amdgcn_ballot_w64(any_bit != 0) == 0) return;
   }
   if constexpr (MOD == kModSoftcapAlibi) {
-    bool need = false;
+    bool need = p.no_skip != 0;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // the lane's row spans k - q in [kq0 - 4, kq0 + TKV) over this tile

@@ -181,7 +181,8 @@ struct AttnParams {
   const int32_t* task_rec;  // [num_tasks][kTaskRecInts]
   const float* slopes;
   int32_t heads_q, heads_k, group, mask_heads, rows_total, total_q;
-  int32_t force_partial;
+  int32_t force_partial;     // full tiles through the predicate path (ablation)
+  int32_t no_skip;           // compute tiles and blocks whose weights are all exactly 0 (ablation)
   float scale_log2;         // scale * log2(e)
   float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
   float softcap_c2;         // c * log2(e)
@@ -255,6 +256,7 @@ struct BwdParams {
   int32_t batch, heads_q, heads_k, group, mask_heads, total_q, krows_total;
   float scale;
   float scale_log2, softcap_k, softcap_c2, alibi_k;   // as in AttnParams
+  int32_t no_skip;           // compute blocks whose weights are all exactly 0 (ablation)
 };
 
 bool attn_bwd_variant_exists(int32_t dtype, int32_t head_dim, int32_t tile_q, int32_t tile_k);

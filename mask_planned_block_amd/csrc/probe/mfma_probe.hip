@@ -1,4 +1,5 @@
-// Measurement helper: a bf16 MFMA throughput probe for gfx950.
+// Measurement helper (libmpb_probe.so, not part of the attention path): a
+// bf16 MFMA throughput probe for gfx950.
 //
 // Every wavefront issues `iters` rounds of eight independent
 // v_mfma_f32_32x32x16_bf16 (the instruction the attention kernels use) on
@@ -8,7 +9,7 @@
 // published peak that the attention roofline is quoted against.
 #include <hip/hip_runtime.h>
 
-#include "../../include/mpb.h"
+#include "../../../include/mpb_probe.h"
 
 namespace {
 

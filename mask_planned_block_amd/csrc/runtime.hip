@@ -1082,7 +1082,7 @@ static size_t paged_remap_bytes(const mpb_plan* plan) {
 static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
                               const void* k, const void* v, void* o, float* lse, float scale,
                               const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
-                              void* stream, int32_t force_partial, int32_t num_splits,
+                              void* stream, int32_t ablate, int32_t num_splits,
                               const PagedArgs* paged = nullptr) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
@@ -1184,7 +1184,8 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.mask_heads = b.mask_heads;
   prm.rows_total = plan->rows_total;
   prm.total_q = b.total_q;
-  prm.force_partial = force_partial ? 1 : 0;
+  prm.force_partial = (ablate & MPB_ABLATE_FULL_AS_PARTIAL) ? 1 : 0;
+  prm.no_skip = (ablate & MPB_ABLATE_NO_SKIP) ? 1 : 0;
   const float log2e = 1.4426950408889634f;
   prm.scale_log2 = scale * log2e;
   prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
@@ -1336,11 +1337,11 @@ size_t flex_attn_bwd_workspace_size(const mpb_plan* plan) {
   return 2 * bwd_vec_bytes(plan);
 }
 
-mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
-                         const void* k, const void* v, const void* o, const float* lse,
-                         const void* dout, void* dq, void* dk, void* dv, float scale,
-                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+static mpb_status bwd_common(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                             const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, float scale,
+                             const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                             void* stream, int32_t ablate) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (!problem) return fail(MPB_ERR_INVALID_ARGUMENT, "problem is NULL");
   int dev = 0;
@@ -1430,11 +1431,34 @@ mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const
   prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
   prm.softcap_c2 = sc ? mod->softcap * log2e : 0.0f;
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
+  prm.no_skip = (ablate & MPB_ABLATE_NO_SKIP) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((e = launch_attn_bwd(b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks, prm, s)) !=
       hipSuccess)
     return device_status(e, "backward launch");
   return ok();
+}
+
+mpb_status flex_attn_bwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
+                         const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float scale,
+                         const mpb_score_mod* mod, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return bwd_common(plan, problem, q, k, v, o, lse, dout, dq, dk, dv, scale, mod, workspace,
+                    workspace_bytes, stream, 0);
+}
+
+mpb_status flex_attn_bwd_ablation(const mpb_plan* plan, const mpb_problem* problem,
+                                  const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout, void* dq, void* dk,
+                                  void* dv, float scale, const mpb_score_mod* mod,
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t flags) {
+  if (flags & ~MPB_ABLATE_NO_SKIP)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "backward ablation flags must be 0 or %d",
+                MPB_ABLATE_NO_SKIP);
+  return bwd_common(plan, problem, q, k, v, o, lse, dout, dq, dk, dv, scale, mod, workspace,
+                    workspace_bytes, stream, flags);
 }
 
 mpb_status flex_attn_fwd(const mpb_plan* plan, const mpb_problem* problem, const void* q,
@@ -1449,9 +1473,11 @@ mpb_status flex_attn_fwd_ablation(const mpb_plan* plan, const mpb_problem* probl
                                   const void* q, const void* k, const void* v, void* o,
                                   float* lse, float scale, const mpb_score_mod* mod,
                                   void* workspace, size_t workspace_bytes, void* stream,
-                                  int32_t force_partial) {
+                                  int32_t flags) {
+  if (flags & ~(MPB_ABLATE_FULL_AS_PARTIAL | MPB_ABLATE_NO_SKIP))
+    return fail(MPB_ERR_INVALID_ARGUMENT, "unknown ablation flags 0x%x", flags);
   return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
-                     stream, force_partial, 1);
+                     stream, flags, 1);
 }
 
 }  // extern "C"

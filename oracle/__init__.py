@@ -19,7 +19,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MPB_ORACLE_LIB selects another build of the same source (the sanitizer
+# test loads an AddressSanitizer/UBSan build through it)
+_LIB_PATH = os.environ.get("MPB_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 ERR_SEQLENS = 1
 ERR_RANGE = 2
@@ -91,6 +93,12 @@ def _load():
                                                   vp, ctypes.c_int, ctypes.c_int64, vp, vp,
                                                   ctypes.c_int]
         lib.orc_attention_bwd_dq_rows.restype = None
+        lib.orc_attention_bwd_dkdv_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, vp,
+                                                    ctypes.c_double, ctypes.c_int,
+                                                    ctypes.c_double, ctypes.c_int, vp,
+                                                    ctypes.c_int, ctypes.c_int64, vp, vp, vp,
+                                                    ctypes.c_int]
+        lib.orc_attention_bwd_dkdv_rows.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -334,3 +342,32 @@ def attention_bwd_dq_rows(w, dout: np.ndarray, rows: np.ndarray,
                                   _ptr(slopes), int(bool(w.alibi_before_softcap)),
                                   rp.shape[0], _ptr(rp), _ptr(dq), nthreads or default_threads())
     return dq
+
+
+def attention_bwd_dkdv_rows(w, dout: np.ndarray, rows: np.ndarray,
+                            nthreads: Optional[int] = None):
+    """dK and dV [n, d] of the selected (K token, KV head) rows (same chain
+    rule as attention_bwd; each Q row that sees the key is recomputed from
+    that row alone).  The cost grows with the (sample, KV head) pairs the
+    rows fall in, not with their number."""
+    lib = _load()
+    p = _problem(w)
+    mf, cq, ck = _i32(w.mask_func), _i32(w.cu_seqlens_q), _i32(w.cu_seqlens_k)
+    q = np.ascontiguousarray(w.q, dtype=np.float32)
+    k = np.ascontiguousarray(w.k, dtype=np.float32)
+    v = np.ascontiguousarray(w.v, dtype=np.float32)
+    do = np.ascontiguousarray(dout, dtype=np.float32)
+    rp = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+    slopes = None if w.alibi_slopes is None else np.ascontiguousarray(w.alibi_slopes, np.float32)
+    n = rp.shape[0]
+    dk = np.zeros((max(n, 1), w.head_dim), np.float64)
+    dv = np.zeros((max(n, 1), w.head_dim), np.float64)
+    rc = lib.orc_attention_bwd_dkdv_rows(ctypes.byref(p), _ptr(mf), _ptr(cq), _ptr(ck), _ptr(q),
+                                         _ptr(k), _ptr(v), _ptr(do), float(w.scale),
+                                         int(w.softcap > 0), float(w.softcap),
+                                         int(slopes is not None), _ptr(slopes),
+                                         int(bool(w.alibi_before_softcap)), n, _ptr(rp),
+                                         _ptr(dk), _ptr(dv), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("a selected K token lies outside every sample")
+    return dk[:n], dv[:n]

@@ -949,3 +949,153 @@ void orc_attention_bwd_dq_rows(const orc_problem* p, const int32_t* mf, const in
   free(th);
   free(jobs);
 }
+
+/* dK and dV of selected K rows: rows = n pairs (K token, KV head g).  The
+ * same chain rule as bwd_worker, restricted to the keys asked for: for every
+ * Q head h of g's group and every Q row q of the key's sample (in that
+ * order, as bwd_worker adds them), the row's scores, log-sum-exp and
+ * sum_j P_j dP_j are recomputed from that row alone, and a row that sees the
+ * key adds scale * dX_qk * Q_q to its dK and P_qk * dO_q to its dV. */
+typedef struct {
+  const orc_problem* p;
+  const int32_t* mf;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const float *q, *k, *v, *dout;
+  double scale;
+  const orc_mod* mod;
+  const int64_t* rows;      /* pairs (k token, kv head) */
+  const int64_t* item_of;   /* [n] item (sample * Hk + kv head) of each row */
+  const int64_t* items;     /* distinct items, this job's share: items[begin..end) */
+  int64_t n, begin, end;
+  double *dk, *dv;          /* [n][d] */
+} dkdv_rows_job;
+
+static int owner_of_k_token(const orc_problem* p, const int32_t* cu_k, int64_t t) {
+  if (p->layout == ORC_BSHD)
+    return t >= 0 && t < (int64_t)p->batch * p->seqlen_k ? (int)(t / p->seqlen_k) : -1;
+  for (int b = 0; b < p->batch; ++b)
+    if (t >= cu_k[b] && t < cu_k[b + 1]) return b;
+  return -1;
+}
+
+static void* dkdv_rows_worker(void* arg) {
+  dkdv_rows_job* J = (dkdv_rows_job*)arg;
+  const orc_problem* p = J->p;
+  int d = p->head_dim;
+  int group = p->heads_q / p->heads_k;
+  int64_t kmax = p->seqlen_k > 0 ? p->seqlen_k : 1;
+  uint8_t* vis = (uint8_t*)malloc((size_t)kmax);
+  double* x = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* t = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* P = (double*)malloc(sizeof(double) * (size_t)kmax);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)kmax);
+  for (int64_t it = J->begin; it < J->end; ++it) {
+    int64_t item = J->items[it];
+    int b = (int)(item / p->heads_k);
+    int g = (int)(item % p->heads_k);
+    int64_t q_off, q_len, k_off, k_len;
+    sample_of(p, J->cu_q, J->cu_k, b, &q_off, &q_len, &k_off, &k_len);
+    for (int h = g * group; h < (g + 1) * group; ++h) {
+      int hm = p->mask_heads == 1 ? 0 : h;
+      for (int64_t ql = 0; ql < q_len; ++ql) {
+        int64_t tok = q_off + ql;
+        const int32_t* F = J->mf + (int64_t)hm * p->nfunc * p->total_q + tok;
+        orc_expand_row(F, p->total_q, p->nfunc, k_len, vis);
+        const float* qrow = J->q + (tok * p->heads_q + h) * (int64_t)d;
+        const float* dorow = J->dout + (tok * p->heads_q + h) * (int64_t)d;
+        double m = -INFINITY;
+        int any = 0;
+        for (int64_t kk = 0; kk < k_len; ++kk) {
+          if (!vis[kk]) continue;
+          const float* krow = J->k + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += (double)qrow[i] * (double)krow[i];
+          x[kk] = J->scale * dot;
+          t[kk] = apply_mod(J->mod, x[kk], h, ql, kk);
+          if (!any || t[kk] > m) m = t[kk];
+          any = 1;
+        }
+        if (!any) continue;   /* nothing visible: no gradient flows */
+        double l = 0.0;
+        for (int64_t kk = 0; kk < k_len; ++kk)
+          if (vis[kk]) l += exp(t[kk] - m);
+        double lse = m + log(l);
+        double Dsum = 0.0;
+        for (int64_t kk = 0; kk < k_len; ++kk) {
+          if (!vis[kk]) continue;
+          const float* vrow = J->v + ((k_off + kk) * p->heads_k + g) * (int64_t)d;
+          P[kk] = exp(t[kk] - lse);
+          double dot = 0.0;
+          for (int i = 0; i < d; ++i) dot += (double)dorow[i] * (double)vrow[i];
+          dP[kk] = dot;
+          Dsum += P[kk] * dP[kk];
+        }
+        for (int64_t r = 0; r < J->n; ++r) {
+          if (J->item_of[r] != item) continue;
+          int64_t kk = J->rows[2 * r] - k_off;
+          if (!vis[kk]) continue;
+          double dT = P[kk] * (dP[kk] - Dsum);
+          double dX = dT * mod_slope(J->mod, x[kk], h, ql, kk);
+          double* dkrow = J->dk + r * d;
+          double* dvrow = J->dv + r * d;
+          for (int i = 0; i < d; ++i) {
+            dkrow[i] += J->scale * dX * (double)qrow[i];
+            dvrow[i] += P[kk] * (double)dorow[i];
+          }
+        }
+      }
+    }
+  }
+  free(vis);
+  free(x);
+  free(t);
+  free(P);
+  free(dP);
+  return NULL;
+}
+
+/* dK, dV [n][d] of the n selected (K token, KV head) rows.  Returns 0, or -1
+ * for a K token outside every sample. */
+int orc_attention_bwd_dkdv_rows(const orc_problem* p, const int32_t* mf, const int32_t* cu_q,
+                                const int32_t* cu_k, const float* q, const float* k,
+                                const float* v, const float* dout, double scale, int softcap_on,
+                                double softcap, int alibi_on, const float* slopes,
+                                int alibi_first, int64_t n, const int64_t* rows, double* dk,
+                                double* dv, int nthreads) {
+  orc_mod mod = {softcap_on, softcap, alibi_on, slopes, alibi_first};
+  int d = p->head_dim;
+  memset(dk, 0, sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+  memset(dv, 0, sizeof(double) * (size_t)(n > 0 ? n : 1) * d);
+  if (n <= 0) return 0;
+  int64_t* item_of = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t* items = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+  int64_t nitems = 0;
+  for (int64_t r = 0; r < n; ++r) {
+    int b = owner_of_k_token(p, cu_k, rows[2 * r]);
+    if (b < 0 || rows[2 * r + 1] < 0 || rows[2 * r + 1] >= p->heads_k) {
+      free(item_of);
+      free(items);
+      return -1;
+    }
+    item_of[r] = (int64_t)b * p->heads_k + rows[2 * r + 1];
+    int seen = 0;
+    for (int64_t i = 0; i < nitems; ++i) seen |= items[i] == item_of[r];
+    if (!seen) items[nitems++] = item_of[r];
+  }
+  if (nthreads < 1) nthreads = 1;
+  if (nitems < nthreads) nthreads = (int)nitems;
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nthreads);
+  dkdv_rows_job* jobs = (dkdv_rows_job*)malloc(sizeof(dkdv_rows_job) * nthreads);
+  for (int i = 0; i < nthreads; ++i) {
+    jobs[i] = (dkdv_rows_job){p, mf, cu_q, cu_k, q, k, v, dout, scale, &mod, rows, item_of, items,
+                              n, nitems * i / nthreads, nitems * (i + 1) / nthreads, dk, dv};
+    pthread_create(&th[i], NULL, dkdv_rows_worker, &jobs[i]);
+  }
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  free(th);
+  free(jobs);
+  free(item_of);
+  free(items);
+  return 0;
+}

@@ -176,6 +176,27 @@ def sample_rows(w, n_random=1500, seed=0, tile_q=128):
     return np.asarray(sorted(rows), dtype=np.int64)
 
 
+def sample_krows(w, items, n_random=100, seed=0, tile_k=64):
+    """(K token, KV head) pairs inside the given (sample, KV head) items:
+    random keys plus the sample's edges, both sides of K-tile boundaries,
+    the first tile's keys (a sink) and the middle key."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b, g in items:
+        _, _, ko, kl = w.sample_bounds(b)
+        if kl == 0:
+            continue
+        for _ in range(n_random):
+            rows.add((ko + int(rng.integers(0, kl)), g))
+        cand = [0, 1, 2, 31, 32, 63, kl - 1, kl - 2, kl // 2]
+        for j in range(1, kl // tile_k + 1, max(1, kl // tile_k // 6)):
+            cand += [j * tile_k - 1, j * tile_k]
+        for k in cand:
+            if 0 <= k < kl:
+                rows.add((ko + k, g))
+    return np.asarray(sorted(rows), dtype=np.int64)
+
+
 def compare_k2q(gk, ok):
     """Bit-exact comparison of a GPU K2Q export with the oracle's K2Q view."""
     assert list(gk["header"][3:7]) == [int(x) for x in ok.header], (gk["header"], ok.header)

@@ -15,18 +15,28 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mpb.h")
 LIB = os.path.join(ROOT, "mask_planned_block_amd", "libmpb.so")
+PROBE_HEADER = os.path.join(ROOT, "include", "mpb_probe.h")
+PROBE_LIB = os.path.join(ROOT, "mask_planned_block_amd", "libmpb_probe.so")
+# every header under include/ and the library that must export what it declares
+HEADER_LIBS = {HEADER: LIB, PROBE_HEADER: PROBE_LIB}
 
 
 def _ensure_built():
-    if not os.path.exists(LIB):
+    if not (os.path.exists(LIB) and os.path.exists(PROBE_LIB)):
         subprocess.check_call(["python", os.path.join(ROOT, "mask_planned_block_amd", "build.py")])
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if not n.startswith("__")))
+
+
+def exported_symbols(lib_path):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path], capture_output=True,
+                         text=True).stdout
+    return set(line.split()[-1] for line in out.splitlines() if line.strip())
 
 
 @pytest.fixture(scope="module")
@@ -46,12 +56,26 @@ def test_header_declares_the_boundary():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    missing = [n for n in declared_functions() if not hasattr(lib, n)]
-    assert not missing, missing
-    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
-    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
-    for n in declared_functions():
-        assert n in exported, n
+    _ensure_built()
+    headers = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                     if f.endswith(".h"))
+    assert set(headers) == set(HEADER_LIBS), headers
+    for header, lib_path in HEADER_LIBS.items():
+        handle = ctypes.CDLL(lib_path)
+        missing = [n for n in declared_functions(header) if not hasattr(handle, n)]
+        assert not missing, (header, missing)
+        exported = exported_symbols(lib_path)
+        for n in declared_functions(header):
+            assert n in exported, (header, n)
+
+
+def test_probe_is_outside_the_attention_library():
+    """The MFMA throughput probe is a measurement helper: it lives in its own
+    library and header, and libmpb.so does not export it."""
+    _ensure_built()
+    assert "mpb_mfma_probe" in declared_functions(PROBE_HEADER)
+    assert "mpb_mfma_probe" not in declared_functions(HEADER)
+    assert "mpb_mfma_probe" not in exported_symbols(LIB)
 
 
 class Problem(ctypes.Structure):

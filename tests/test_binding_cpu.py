@@ -54,3 +54,29 @@ def test_call_problem_cache_is_bounded():
         k = torch.empty(1, s, 1, 64, dtype=torch.bfloat16)
         assert mpb._call_problem(_Plan(), q, k).seqlen_k == s
     assert len(mpb._CALL_PROBLEMS) <= 64
+
+
+def test_outputs_and_slopes_are_size_checked_before_any_call():
+    """The library sees bare pointers, so the binding refuses an output or a
+    slope array whose size differs from what the kernels write or read
+    (ValueError before any library call; CPU tensors never reach it)."""
+    import pytest
+    plan = _Plan(heads_q=4, heads_k=4, batch=1, seqlen_q=64, seqlen_k=64, total_q=64,
+                 total_k=64)
+    q = torch.empty(1, 64, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="out"):
+        mpb.flex_attn_fwd(plan, q, q, q, out=torch.empty(1, 63, 4, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="lse"):
+        mpb.flex_attn_fwd(plan, q, q, q, lse=torch.empty(4, 63))
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        mpb.flex_attn_fwd(plan, q, q, q, alibi_slopes=torch.empty(3))
+    lse = torch.empty(4, 64)
+    with pytest.raises(ValueError, match="dq"):
+        mpb.flex_attn_bwd(plan, q, q, q, q, lse, q, dq=torch.empty(1, 64, 4, 64))
+    with pytest.raises(ValueError, match="dk"):
+        mpb.flex_attn_bwd(plan, q, q, q, q, lse, q, dk=torch.empty(2, 64, 4, 128))
+    with pytest.raises(ValueError, match="lse"):
+        mpb.flex_attn_bwd(plan, q, q, q, q, torch.empty(64, 4), q)
+    parts = torch.empty(2, 64, 4, 128)
+    with pytest.raises(ValueError, match="lse"):
+        mpb.flex_attn_fwd_merge(parts, torch.empty(2, 4, 64), lse=torch.empty(4, 65))

@@ -32,14 +32,14 @@ def _case(case, **kw):
     print("CASE", case, kw, flush=True)
 
 
-def run_backward(w, d, plan, do_np):
+def run_backward(w, d, plan, do_np, no_skip=False):
     import mask_planned_block_amd as mpb
     o, lse = G.run_attention(w, d, plan)
     dout = torch.from_numpy(do_np).to(torch.bfloat16).reshape(d["q"].shape).cuda()
     dq, dk, dv = mpb.flex_attn_bwd(plan, d["q"], d["k"], d["v"], o, lse, dout, scale=w.scale,
                                    softcap=w.softcap if w.softcap > 0 else None,
                                    alibi_slopes=d["slopes"],
-                                   alibi_before_softcap=w.alibi_before_softcap)
+                                   alibi_before_softcap=w.alibi_before_softcap, no_skip=no_skip)
     torch.cuda.synchronize()
     f = lambda x, T, H: x.float().reshape(T, H, w.head_dim).cpu().numpy().astype(np.float64)
     return (f(dq, w.total_q, w.heads_q), f(dk, w.total_k, w.heads_k),
@@ -168,14 +168,26 @@ def test_backward_full_window_sink():
     _check(w)
 
 
+# (sample, KV head) pairs whose keys are compared one by one at full size:
+# first and last samples and heads (for the ALiBi workload the steepest and
+# the flattest slope), and one in the middle
+FULL_DKDV_ITEMS = {
+    "varlen_doc": [(0, 0), (3, 7), (5, 10), (7, 15)],
+    "block_sparse": [(0, 0), (0, 11), (0, 23)],
+    "prefix_softcap": [(0, 0), (1, 31), (3, 16)],
+}
+
+
 @pytest.mark.parametrize("name", ["varlen_doc", "block_sparse", "prefix_softcap"])
 def test_backward_full_sampled_and_sums(name):
     """Full benchmark shapes: dQ on sampled rows (random rows plus sample and
-    tile edges) against the oracle; dK and dV through identities that hold
-    at any size: summed over a sample's keys, dV of KV head g equals the sum
-    of dO over the sample's rows (of g's Q heads) that see anything (each
-    row's weights sum to 1), and without a score_mod dK sums to zero (each
-    row's softmax gradient sums to zero)."""
+    tile edges) and dK/dV on sampled keys (random keys plus sample edges,
+    K-tile boundaries and the first tile's keys, in a few (sample, KV head)
+    pairs) against the oracle, element by element; dK and dV also through
+    identities that hold at any size: summed over a sample's keys, dV of KV
+    head g equals the sum of dO over the sample's rows (of g's Q heads) that
+    see anything (each row's weights sum to 1), and without a score_mod dK
+    sums to zero (each row's softmax gradient sums to zero)."""
     w = W.make(name)
     _case("bwd_full", name=name)
     d = G.device_inputs(w)
@@ -190,6 +202,16 @@ def test_backward_full_sampled_and_sums(name):
     err = float(np.max(np.abs(ref - got)))
     print("  %s dQ sampled max|err|/max|ref| = %.3g" % (name, err / scale), flush=True)
     assert err <= NORM_TOL * scale
+    krows = G.sample_krows(w, FULL_DKDV_ITEMS[name], n_random=100, seed=2,
+                           tile_k=plan.problem.tile_k)
+    rk, rv = oracle.attention_bwd_dkdv_rows(w, do, krows)
+    for what, ref, got in (("dK", rk, dk[krows[:, 0], krows[:, 1]]),
+                           ("dV", rv, dv[krows[:, 0], krows[:, 1]])):
+        scale = float(np.max(np.abs(ref)))
+        err = float(np.max(np.abs(ref - got)))
+        print("  %s %s sampled (%d keys) max|err|/max|ref| = %.3g"
+              % (name, what, len(krows), err / scale), flush=True)
+        assert err <= NORM_TOL * scale
     # rows that see anything: those with a finite LSE in the forward
     _, lse = G.run_attention(w, d, plan)
     torch.cuda.synchronize()
@@ -210,21 +232,47 @@ def test_backward_full_sampled_and_sums(name):
                 assert np.all(np.abs(ksum) <= 1e-2 * np.abs(dk[ko:ko + kl, g]).sum(axis=0) + 1e-6)
 
 
+@pytest.mark.parametrize("sign", [1.0, -1.0])
 @pytest.mark.parametrize("alibi_before_softcap", [False, True])
-def test_backward_steep_alibi_negligible_blocks(alibi_before_softcap):
+def test_backward_steep_alibi_negligible_blocks(alibi_before_softcap, sign):
     """Steep ALiBi slopes after a softcap bound every score of most blocks far
     below the row's LSE: their weights and dS are exactly zero in fp32, and
-    the dQ and dK/dV kernels skip them before the scores.  The gradients must
-    still match the oracle, fully masked rows included (ALiBi inside the cap
-    bounds nothing and skips nothing: the same case as a control)."""
+    the dQ and dK/dV kernels skip them before the scores (the dQ launch cuts
+    leading runs of such K tiles from its lists for positive slopes, trailing
+    runs for negative ones).  The gradients must still match the oracle,
+    fully masked rows included, and equal bit for bit the ablation run that
+    skips nothing (ALiBi inside the cap bounds nothing and skips nothing: the
+    same case as a control)."""
     B, S, H = 2, 700, 4
     q_local = np.tile(np.arange(S), B)
     mf = np.stack([np.minimum(q_local + 1, 16), np.minimum(q_local + 1, 16), q_local + 1])
     mf[:, :3] = 0                       # three fully masked rows
     w = W.custom(mf[None].astype(np.int32), batch=B, seqlen_q=S, seqlen_k=S, heads_q=H,
                  head_dim=128, dtype=W.DTYPE_BF16, seed=47, softcap=20.0,
-                 alibi=np.array([8.0, 2.0, 0.5, 0.01], np.float32),
+                 alibi=sign * np.array([8.0, 2.0, 0.5, 0.01], np.float32),
                  alibi_before_softcap=alibi_before_softcap)
-    _case("bwd_steep_alibi", alibi_before_softcap=alibi_before_softcap)
-    ref, got = _check(w)
+    _case("bwd_steep_alibi", alibi_before_softcap=alibi_before_softcap, sign=sign)
+    d = G.device_inputs(w)
+    plan = G.build_plan(w, d, build_backward=True)
+    do = W.grad_output(w)
+    got = run_backward(w, d, plan, do)
+    full = run_backward(w, d, plan, do, no_skip=True)
+    for a, b in zip(got, full):
+        assert np.array_equal(a, b), "a skipped block had nonzero weight or gradient"
+    compare_grads(w, oracle.attention_bwd(w, do), got, w.name)
     assert np.all(got[0][:3] == 0.0)     # dQ of the fully masked rows
+
+
+@pytest.mark.parametrize("name", ["block_sparse", "window_sink", "prefix_softcap"])
+def test_backward_skips_change_nothing(name):
+    """dQ, dK and dV equal bit for bit those of the ablation run that computes
+    every listed pair and block (no exact-zero skips)."""
+    w = W.make(name, small=True)
+    _case("bwd_no_skip", name=name)
+    d = G.device_inputs(w)
+    plan = G.build_plan(w, d, build_backward=True)
+    do = W.grad_output(w)
+    got = run_backward(w, d, plan, do)
+    full = run_backward(w, d, plan, do, no_skip=True)
+    for a, b in zip(got, full):
+        assert np.array_equal(a, b)

@@ -330,26 +330,48 @@ def test_library_tile_choice():
         assert (plan.problem.tile_q, plan.problem.tile_k) == (128, 64)
 
 
+@pytest.mark.parametrize("sign", [1.0, -1.0])
 @pytest.mark.parametrize("dtype", [W.DTYPE_FP32, W.DTYPE_BF16])
 @pytest.mark.parametrize("softcap", [0.0, 20.0])
-def test_steep_alibi_negligible_tiles(dtype, softcap):
+def test_steep_alibi_negligible_tiles(dtype, softcap, sign):
     """Steep ALiBi slopes put most K tiles far below each row's max: their
     softmax weights are exactly zero in fp32 and the kernel skips them (after
-    the scores, or before them when a softcap bounds the scores); the result
-    must still match the oracle, fully masked rows included."""
+    the scores, or before them when a softcap bounds the scores).  With
+    positive slopes the far keys vanish, with negative ones the near keys
+    (the row max sits at key 0).  The result must match the oracle, fully
+    masked rows included, and equal bit for bit the ablation run that skips
+    nothing (and the one that runs full tiles through the predicate path)."""
     B, S, H = 2, 700, 4
     q_local = np.tile(np.arange(S), B)
     mf = np.stack([np.minimum(q_local + 1, 16), np.minimum(q_local + 1, 16), q_local + 1])
     mf[:, :3] = 0                       # three fully masked rows
     w = W.custom(mf[None].astype(np.int32), batch=B, seqlen_q=S, seqlen_k=S, heads_q=H,
                  head_dim=64 if dtype == W.DTYPE_FP32 else 128, dtype=dtype, seed=46,
-                 softcap=softcap, alibi=np.array([8.0, 2.0, 0.5, 0.01], np.float32))
-    _print_case("steep_alibi", dtype=dtype, softcap=softcap)
+                 softcap=softcap, alibi=sign * np.array([8.0, 2.0, 0.5, 0.01], np.float32))
+    _print_case("steep_alibi", dtype=dtype, softcap=softcap, sign=sign)
     d = G.device_inputs(w)
     plan = G.build_plan(w, d)
     o, lse = G.run_attention(w, d, plan)
     o2, l2 = G.run_attention(w, d, plan, force_partial=True)
+    o3, l3 = G.run_attention(w, d, plan, no_skip=True)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(lse, l2)
+    assert torch.equal(o, o3) and torch.equal(lse, l3), "a skipped block had nonzero weight"
     O, L = oracle.attention(w)
     G.compare_attention(w, O, L, G.flat_o(w, o), lse.cpu().numpy().astype(np.float64), "steep")
+
+
+@pytest.mark.parametrize("name", ["block_sparse", "window_sink", "prefix_softcap"])
+def test_skips_change_nothing(name):
+    """The exact-zero skips (predicate words all zero for a wavefront's rows,
+    negligible blocks) leave O and LSE unchanged bit for bit: the ablation
+    run that computes every listed tile and block gives the same bytes."""
+    w = W.make(name, small=True)
+    _print_case("no_skip", name=name)
+    d = G.device_inputs(w)
+    for tq, tk in ((0, 0), (128, 64), (64, 32)):
+        plan = G.build_plan(w, d, tq, tk)
+        o, lse = G.run_attention(w, d, plan)
+        o3, l3 = G.run_attention(w, d, plan, no_skip=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o3) and torch.equal(lse, l3), (tq, tk)

@@ -171,3 +171,34 @@ def test_selected_dq_rows_match_full_backward(variant):
     got = oracle.attention_bwd_dq_rows(w, do, rows, nthreads=3)
     for n, (t, h) in enumerate(rows):
         assert np.array_equal(got[n], dq[t, h])
+
+
+@pytest.mark.parametrize("variant", ["none", "softcap", "alibi", "both", "both_first"])
+def test_selected_dkdv_rows_match_full_backward(variant):
+    """dK/dV of selected K rows (recomputing each Q row that sees the key)
+    equal the full backward's rows bit for bit, for every key of a varlen
+    case with empty, fully masked and single-key rows, in any row order."""
+    w, do = _tiny(variant)
+    _, dk, dv = oracle.attention_bwd(w, do, nthreads=1)
+    rows = np.array([[t, g] for t in range(w.total_k) for g in range(w.heads_k)])[::-1]
+    gk, gv = oracle.attention_bwd_dkdv_rows(w, do, rows, nthreads=3)
+    for n, (t, g) in enumerate(rows):
+        assert np.array_equal(gk[n], dk[t, g]) and np.array_equal(gv[n], dv[t, g]), (t, g)
+
+
+def test_selected_dkdv_rows_gqa_bshd():
+    """The same on a fixed-length GQA case (four Q heads on two K/V heads,
+    per-head masks) with the rows sampled unevenly over samples and heads."""
+    B, S, Sk, Hq, Hk = 2, 30, 26, 4, 2
+    rng = np.random.default_rng(21)
+    mf = np.sort(rng.integers(0, Sk + 1, size=(Hq, 5, B * S)), axis=1).astype(np.int32)
+    w = W.custom(mf, batch=B, seqlen_q=S, seqlen_k=Sk, heads_q=Hq, heads_k=Hk, head_dim=8,
+                 dtype=W.DTYPE_FP32, seed=13, softcap=3.0, alibi=True)
+    do = W.grad_output(w)
+    _, dk, dv = oracle.attention_bwd(w, do)
+    rows = np.array([[0, 0], [25, 1], [26, 1], [51, 0], [13, 1], [13, 0], [40, 1]])
+    gk, gv = oracle.attention_bwd_dkdv_rows(w, do, rows)
+    for n, (t, g) in enumerate(rows):
+        assert np.array_equal(gk[n], dk[t, g]) and np.array_equal(gv[n], dv[t, g]), (t, g)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_dkdv_rows(w, do, np.array([[B * Sk, 0]]))

@@ -231,6 +231,44 @@ def test_classify_pack_brute_force_varlen():
                  with_values=False)
     P = _check_plan_against_brute_force(w, 32, 32)
     assert P.cu_rows.tolist() == [0, 2, 2, 6, 8]
+    # per-sample descriptor {q_off, k_off, q_len, k_len, row_begin, rows, k_tiles, 0},
+    # written out by hand from the prefix: rows = ceil(q_len/32), k_tiles = ceil(k_len/32)
+    assert P.seqdesc.tolist() == [[0, 0, 40, 40, 0, 2, 2, 0],
+                                  [40, 40, 0, 0, 2, 0, 0, 0],
+                                  [40, 40, 97, 97, 2, 4, 4, 0],
+                                  [137, 137, 33, 33, 6, 2, 2, 0]]
+
+
+def test_seqdesc_closed_form():
+    """The per-sample descriptor for Q and K split differently (THD, an
+    empty Q side, an empty K side, ragged lengths, tile_q != tile_k) and for
+    fixed-length BSHD, against values written out by hand: offsets from the
+    prefixes, row_begin the running sum of ceil(q_len / T_Q), rows =
+    ceil(q_len / T_Q), k_tiles = ceil(k_len / T_KV)."""
+    rng = np.random.default_rng(4)
+    cq = np.array([0, 5, 75, 75], np.int32)
+    ck = np.array([0, 64, 64, 97], np.int32)
+    klen = [64, 0, 33]
+    mf = np.zeros((1, 3, 75), np.int32)
+    for b in range(3):
+        for t in range(cq[b], cq[b + 1]):
+            mf[0, :, t] = np.sort(rng.integers(0, klen[b] + 1, size=3))
+    w = W.custom(mf, layout=W.LAYOUT_THD, cu_seqlens_q=cq, cu_seqlens_k=ck, head_dim=32,
+                 with_values=False)
+    P = oracle.build_plan(w, 64, 32, nthreads=2)
+    assert P.err == 0
+    assert P.seqdesc.tolist() == [[0, 0, 5, 64, 0, 1, 2, 0],
+                                  [5, 64, 70, 0, 1, 2, 0, 0],
+                                  [75, 64, 0, 33, 3, 0, 2, 0]]
+    assert P.cu_rows.tolist() == [0, 1, 3, 3]
+    # fixed length: B=3, Sq=50, Sk=70 at 32x32
+    mfb = np.sort(rng.integers(0, 71, size=(1, 3, 150)), axis=1).astype(np.int32)
+    wb = W.custom(mfb, batch=3, seqlen_q=50, seqlen_k=70, head_dim=32, with_values=False)
+    Pb = oracle.build_plan(wb, 32, 32, nthreads=2)
+    assert Pb.seqdesc.tolist() == [[0, 0, 50, 70, 0, 2, 3, 0],
+                                   [50, 70, 50, 70, 2, 2, 3, 0],
+                                   [100, 140, 50, 70, 4, 2, 3, 0]]
+    assert Pb.cu_rows.tolist() == [0, 2, 4, 6]
 
 
 def test_causal_closed_form():
