@@ -82,6 +82,170 @@ def k2q_bytes(w, plan):
     return read + write
 
 
+def attn_bytes(w, plan):
+    """Algorithmic bytes of one forward launch: Q, K, V and O once each, the
+    LSE (4 bytes per row and head), the predicate payload (T_Q*T_KV/8 bytes
+    per partial tile) and 4 bytes per listed tile index."""
+    h = plan.info.header
+    p = plan.problem
+    esz = 2 if w.dtype == 0 else 4
+    qo = 2 * w.total_q * w.heads_q * w.head_dim * esz
+    kv = 2 * w.total_k * w.heads_k * w.head_dim * esz
+    pn, fn = int(h[1]), int(h[2])
+    return qo + kv + 4 * w.heads_q * w.total_q + pn * p.tile_q * p.tile_k // 8 + 4 * (pn + fn)
+
+
+def roofline(flops, nbytes, seconds, peak_tflops):
+    """The roof that binds: the larger of the MFMA time (flops at the dense
+    peak) and the HBM time (algorithmic bytes at 8 TB/s).  `achieved`/`frac`
+    are against that roof; both fractions are reported."""
+    t_mfma = flops / (peak_tflops * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    mfma_frac = flops / seconds / 1e12 / peak_tflops
+    hbm_frac = nbytes / seconds / 1e9 / PEAK_HBM_GBS
+    if t_hbm > t_mfma:
+        r = {"bound": "hbm", "achieved": round(nbytes / seconds / 1e9, 2), "peak": PEAK_HBM_GBS,
+             "unit": "GB/s", "frac": round(hbm_frac, 5)}
+    else:
+        r = {"bound": "mfma", "achieved": round(flops / seconds / 1e12, 3), "peak": peak_tflops,
+             "unit": "TFLOP/s", "frac": round(mfma_frac, 5)}
+    r.update({"mfma_frac": round(mfma_frac, 5), "hbm_frac": round(hbm_frac, 5),
+              "roof_us": {"mfma": round(t_mfma * 1e6, 3), "hbm": round(t_hbm * 1e6, 3)},
+              "intensity_flop_per_byte": round(flops / nbytes, 2),
+              "ridge_flop_per_byte": round(peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9), 2)})
+    return r
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+CONFIG_WORKLOADS = ("tiny_causal", "window_sink", "varlen_doc", "block_sparse",
+                    "prefix_softcap")
+
+
+def oracle_sample_rate(w, seconds):
+    """The oracle's attention on a bounded random sample of (token, head)
+    rows (about `seconds` of CPU work on all host threads): effective
+    TFLOP/s = 4*d per visible pair of the sampled rows / time.  Visible
+    pairs are counted from the endpoints (bookkeeping, not attention)."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(7)
+    # visible keys per (mask head, token): [0,F0) plus [F1,F2), [F3,F4), ...
+    mf = w.mask_func.astype(np.int64)
+    vis = mf[:, 0, :] + (mf[:, 2::2, :] - mf[:, 1::2, :]).sum(axis=1)
+    n = 64
+    t_total, flops, rows_done = 0.0, 0.0, 0
+    while t_total < seconds and rows_done < w.total_q * w.heads_q:
+        rows = np.stack([rng.integers(0, w.total_q, n), rng.integers(0, w.heads_q, n)], axis=1)
+        a = time.perf_counter()
+        oracle.attention(w, rows=rows)
+        t_total += time.perf_counter() - a
+        hm = rows[:, 1] if w.mask_heads > 1 else np.zeros(n, np.int64)
+        flops += 4.0 * w.head_dim * float(vis[hm, rows[:, 0]].sum())
+        rows_done += n
+        n = min(n * 2, 4096)
+    return flops / t_total / 1e12, rows_done, t_total
+
+
+def measure_config(name, args, mpb, W, torch, np):
+    """One workload at its full size: the library's tile, steady-state
+    forward (HIP events around back-to-back launches), the forward inside a
+    plan+forward step, plan build (host clock, and GPU stage events), the
+    roofline against the binding roof, and the oracle on a bounded sample."""
+    w = W.make(name)
+    d = W.to_device(w)
+    stream = torch.cuda.current_stream()
+    prob = mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                            w.total_k, w.heads_q, w.heads_k, w.head_dim, w.mask_heads, w.nfunc,
+                            0, 0)
+    kw = dict(scale=w.scale, softcap=w.softcap if w.softcap > 0 else None,
+              alibi_slopes=d["slopes"], alibi_before_softcap=w.alibi_before_softcap,
+              stream=stream)
+    plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+    out, lse = mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+    kw.update(out=out, lse=lse)
+    st = plan_stats(w, plan)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+    e0.record(stream)
+    for _ in range(args.config_iters):
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_us = e0.elapsed_time(e1) * 1e3 / args.config_iters
+    # whole steps (build + forward), host clock around them
+    torch.cuda.synchronize()
+    keep = []
+    a = time.perf_counter()
+    for _ in range(args.config_iters):
+        p2 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        mpb.flex_attn_fwd(p2, d["q"], d["k"], d["v"], **kw)
+        keep.append(p2)
+        if len(keep) > 2:
+            keep.pop(0).close()
+    torch.cuda.synchronize()
+    step_us = (time.perf_counter() - a) * 1e6 / args.config_iters
+    for p2 in keep:
+        p2.close()
+    builds = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        p3 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        torch.cuda.synchronize()
+        builds.append((time.perf_counter() - a) * 1e6)
+        p3.close()
+    runs = []
+    for _ in range(5):
+        p4 = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream,
+                                 time_stages=True)
+        runs.append(p4.stage_times())
+        p4.close()
+    stages = _median_stages(runs)
+    gpu_us = sum(v for k, v in stages.items() if k != "span" and v > 0)
+    pb = plan_bytes(w, plan)
+    eff = 4.0 * w.head_dim * st["visible_pairs"]
+    exe = 4.0 * w.head_dim * st["executed_pairs"]
+    dense = 4.0 * w.head_dim * st["dense_pairs"]
+    peak = PEAK_BF16_TFLOPS if w.dtype == W.DTYPE_BF16 else PEAK_FP32_MFMA_TFLOPS
+    t = fwd_us * 1e-6
+    res = {"workload": name, "dtype": "bf16" if w.dtype == W.DTYPE_BF16 else "f32",
+           "tile": "%dx%d" % (plan.problem.tile_q, plan.problem.tile_k),
+           "tasks": st["tasks"], "partial_tiles": st["partial_tiles"],
+           "full_tiles": st["full_tiles"],
+           "fwd_us": round(fwd_us, 2), "step_us": round(step_us, 2),
+           "effective_gflop": round(eff / 1e9, 3), "executed_gflop": round(exe / 1e9, 3),
+           "dense_gflop": round(dense / 1e9, 3),
+           "effective_tflops": round(eff / t / 1e12, 2), "executed_tflops": round(exe / t / 1e12, 2),
+           "pct_peak_effective": round(100 * eff / t / 1e12 / peak, 2),
+           "pct_peak_executed": round(100 * exe / t / 1e12 / peak, 2),
+           "pct_peak_dense_equiv": round(100 * dense / t / 1e12 / peak, 2),
+           "roofline": roofline(eff, attn_bytes(w, plan), t, peak),
+           "plan_build_us_host": round(float(np.median(builds)), 1), "plan_stages_us": stages,
+           "plan_algorithmic_bytes": pb,
+           "planner_gbs_over_stages": round(pb / (gpu_us * 1e-6) / 1e9, 1) if gpu_us > 0 else None}
+    if not args.no_cpu_baseline:
+        rate, rows, secs = oracle_sample_rate(w, args.config_cpu_seconds)
+        import oracle
+        res["cpu_baseline"] = {"value": round(rate, 6), "unit": "TFLOP/s",
+                               "cores": oracle.default_threads(), "kind": "oracle",
+                               "sample": "%d random (token, head) rows of fp64 oracle attention in "
+                                         "%.1f s" % (rows, secs)}
+    plan.close()
+    del d
+    torch.cuda.empty_cache()
+    return res
+
+
 def _median_stages(runs):
     import numpy as np
     return {k: round(float(np.median([r[k] for r in runs])), 2) for k in runs[0]}
@@ -385,6 +549,10 @@ def main():
                     help="skip the MFMA throughput probe")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="end with plain device copies of this many MiB (counter calibration)")
+    ap.add_argument("--config-iters", type=int, default=20,
+                    help="launches per workload in the per-config table (0 = skip the table)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="oracle seconds per workload in the per-config table")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
                     help="print a summary of rocprofv3 csv output under comma-separated DIRS "
                          "(KIND: stats or pmc) and exit")
@@ -635,8 +803,12 @@ def main():
     # roofline: the kernel's average launch duration from the back-to-back
     # launches on one plan (HIP events on the launch stream); the per-step
     # event spans also hold the host's launch latency
-    achieved = eff / (fwd_ss_us * 1e-6) / 1e12
+    roof = roofline(eff, attn_bytes(w, plan), fwd_ss_us * 1e-6, peak)
     traffic = load_traffic(source_digest()) if args.workload == "window_sink" else None
+    configs = None
+    if args.config_iters > 0:
+        configs = {name: measure_config(name, args, mpb, W, torch, np)
+                   for name in CONFIG_WORKLOADS}
 
     res = {
         "metric": METRIC,
@@ -655,12 +827,13 @@ def main():
                    "heads_k": w.heads_k, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
                    "head_dim": w.head_dim, "mask_heads": w.mask_heads, "nfunc": w.nfunc,
                    "tile": "%dx%d" % (tq, tk), "step": "mask_plan_build + flex_attn_fwd"},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 5), "traffic": traffic,
-                     "kernel": "attn_fwd_kernel", "achieved_basis": "effective flops per launch / "
-                     "average launch duration (HIP events around %d back-to-back launches on "
-                     "the launch stream)" % args.fwd_iters,
-                     "measured_mfma_peak": mfma},
+        "roofline": dict(roof, traffic=traffic, kernel="attn_fwd_kernel",
+                         algorithmic_bytes=attn_bytes(w, plan),
+                         achieved_basis="algorithmic bytes (hbm) or effective flops (mfma) per "
+                         "launch / average launch duration (HIP events around %d back-to-back "
+                         "launches on the launch stream); the binding roof is the larger of "
+                         "flops / MFMA peak and bytes / 8 TB/s" % args.fwd_iters,
+                         measured_mfma_peak=mfma),
         "fwd": {
             "us_in_step": round(fwd_in_step_us, 2),
             "us_steady": round(fwd_ss_us, 2),
@@ -685,12 +858,13 @@ def main():
         "paged": paged,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},
+        "configs": configs,
     }
     if not args.no_cpu_baseline:
         secs, passes, threads, t_plan, t_attn = cpu_baseline(w, tq, tk, args.cpu_seconds)
         res["cpu_baseline"] = {
             "value": round(eff * passes / secs / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d whole-workload pass(es) of the fp64 oracle (plan + attention, every "
                       "row) in %.1f s" % (passes, secs),
             "plan_s_per_pass": round(t_plan / passes, 4),
