@@ -335,6 +335,23 @@ mpb_status flex_attn_fwd_splitk(const mpb_plan* plan, const mpb_problem* problem
                                 const mpb_score_mod* mod, int32_t num_splits, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* flex_attn_fwd_splitk without allocation, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and errors as flex_attn_fwd_splitk minus the workspace: the partial states
+ * live in a static device array of the library (64 MiB, one per GPU the
+ * library runs on, held until the process ends), so a call whose resolved
+ * parts need more than that (flex_attn_fwd_splitk_workspace_size) returns
+ * MPB_ERR_WORKSPACE before any launch.  No device or host memory is
+ * allocated.  Every call overwrites the partial states it reads (nothing
+ * needs clearing), and all calls on one GPU share the array: calls that
+ * overlap on one GPU (several streams or host threads) race and must be
+ * ordered by the caller.  A resolved split count of 1 runs flex_attn_fwd. */
+mpb_status flex_attn_fwd_splitk_noalloc(const mpb_plan* plan, const mpb_problem* problem,
+                                        const void* q, const void* k, const void* v, void* o,
+                                        float* lse, float scale, const mpb_score_mod* mod,
+                                        int32_t num_splits, void* stream);
+
 /* flex_attn_fwd_merge [TESS "Split-K"]: merges num_parts partial attention
  * states of the same rows, e.g. the parts of a Split-K forward or the
  * outputs of attention over disjoint key ranges.  Row r = token*heads_q + h.

@@ -22,6 +22,7 @@ __all__ = [
     "make_problem", "mask_plan_build", "mask_plan_destroy", "mask_plan_info", "mask_plan_export",
     "flex_attn_fwd", "flex_attn_fwd_workspace_size", "flex_attn_fwd_num_splits",
     "flex_attn_fwd_splitk_workspace_size", "flex_attn_fwd_merge", "flex_attn_fwd_paged",
+    "flex_attn_fwd_splitk_noalloc",
     "flex_attn_fwd_paged_workspace_size", "flex_attn_bwd",
     "flex_attn_bwd_workspace_size", "library_path", "TASK_REC_FIELDS",
 ]
@@ -111,6 +112,7 @@ def _load():
     lib.flex_attn_fwd_splitk_workspace_size.argtypes = [vp, ctypes.c_int32]
     lib.flex_attn_fwd_splitk_workspace_size.restype = ctypes.c_size_t
     lib.flex_attn_fwd_splitk.argtypes = fwd_args[:9] + [ctypes.c_int32] + fwd_args[9:]
+    lib.flex_attn_fwd_splitk_noalloc.argtypes = fwd_args[:9] + [ctypes.c_int32, vp]
     lib.flex_attn_fwd_merge.argtypes = [ctypes.c_int32] * 5 + [vp] * 5
     lib.flex_attn_fwd_paged_workspace_size.argtypes = [vp, ctypes.c_int32]
     lib.flex_attn_fwd_paged_workspace_size.restype = ctypes.c_size_t
@@ -130,6 +132,7 @@ def _load():
                  "mask_plan_export", "mask_plan_export_k2q", "mask_plan_stage_times", "mask_plan_export_k2q_order",
                  "mask_plan_export_launch_order",
                  "flex_attn_fwd", "flex_attn_fwd_ablation", "flex_attn_fwd_splitk",
+                 "flex_attn_fwd_splitk_noalloc",
                  "flex_attn_fwd_merge", "flex_attn_fwd_paged", "flex_attn_bwd",
                  "flex_attn_bwd_ablation"):
         getattr(lib, name).restype = ctypes.c_int
@@ -446,6 +449,35 @@ def flex_attn_fwd(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         _check(_lib.flex_attn_fwd_ablation(*head, *tail, flags))
     else:
         _check(_lib.flex_attn_fwd(*head, *tail))
+    return out, lse
+
+
+def flex_attn_fwd_splitk_noalloc(plan: MaskPlan, q: torch.Tensor, k: torch.Tensor,
+                                 v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                                 scale: Optional[float] = None, softcap: Optional[float] = None,
+                                 alibi_slopes: Optional[torch.Tensor] = None,
+                                 alibi_before_softcap=False, num_splits: int = 0, stream=None):
+    """Split-K forward whose partial states live in the library's static
+    scratch (see include/mpb.h): nothing is allocated, so out and lse must be
+    given.  Calls that overlap on one GPU share the scratch and race."""
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    prob = _call_problem(plan, q, k)
+    _require_shape(out, "out", q.shape)
+    _require_shape(lse, "lse", (q.shape[-2], prob.total_q))
+    _check_slopes(alibi_slopes, q.shape[-2])
+    mod = None
+    if softcap or alibi_slopes is not None:
+        mod = ScoreMod(1 if softcap else 0, float(softcap or 0.0),
+                       1 if alibi_slopes is not None else 0,
+                       _dev_ptr(alibi_slopes, "alibi_slopes", torch.float32),
+                       1 if alibi_before_softcap else 0)
+    sc = float(scale) if scale is not None else 1.0 / float(q.shape[-1]) ** 0.5
+    _check(_lib.flex_attn_fwd_splitk_noalloc(
+        plan.handle, ctypes.byref(prob), _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype),
+        _dev_ptr(v, "v", q.dtype), _dev_ptr(out, "out", q.dtype),
+        _dev_ptr(lse, "lse", torch.float32), sc, ctypes.byref(mod) if mod is not None else None,
+        int(num_splits), _stream_handle(stream)))
     return out, lse
 
 

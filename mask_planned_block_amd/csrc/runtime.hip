@@ -429,15 +429,17 @@ PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
 constexpr size_t kInPlaceBlockBytes = (size_t)32 << 20;
 
 int device_cus(int dev) {
-  static std::mutex mu;
-  static std::map<int, int> cache;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = cache.find(dev);
-  if (it != cache.end()) return it->second;
+  // fixed-size cache (no allocation on any call path)
+  constexpr int kDevices = 64;
+  static std::atomic<int> cache[kDevices];
+  if (dev >= 0 && dev < kDevices) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
     n = 256;
-  cache[dev] = n;
+  if (dev >= 0 && dev < kDevices) cache[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
@@ -1271,6 +1273,65 @@ mpb_status flex_attn_fwd_splitk(const mpb_plan* plan, const mpb_problem* problem
   const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
   return attn_common(plan, problem, q, k, v, o, lse, scale, mod, workspace, workspace_bytes,
                      stream, 0, sp);
+}
+
+}  // extern "C"
+
+// Scratch of flex_attn_fwd_splitk_noalloc: the Split-K partial states live
+// in this file-scope device array instead of a caller workspace.  Every GPU
+// the library runs on holds its own copy until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress returns for the
+// current device (the array's name is a host-side stand-in).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+// Device address of this device's scratch, looked up once per device with
+// that device current.
+mpb_status scratch_address(int dev, void** out) {
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(MPB_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kScratchDevices - 1);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return device_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MPB_OK;
+}
+}  // namespace
+
+extern "C" {
+
+mpb_status flex_attn_fwd_splitk_noalloc(const mpb_plan* plan, const mpb_problem* problem,
+                                        const void* q, const void* k, const void* v, void* o,
+                                        float* lse, float scale, const mpb_score_mod* mod,
+                                        int32_t num_splits, void* stream) {
+  if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "num_splits must be in [0, %d]", kMaxSplits);
+  const int32_t sp = num_splits == 0 ? choose_splits(plan) : num_splits;
+  const size_t need = sp > 1 ? splitk_o_bytes(plan, sp) + splitk_lse_bytes(plan, sp) : 0;
+  if (need > kNoAllocScratchBytes)
+    return fail(MPB_ERR_WORKSPACE, "%d parts need %zu bytes of partial states; the static "
+                "scratch holds %zu (use flex_attn_fwd_splitk with a workspace)", sp, need,
+                kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    const mpb_status st = scratch_address(dev, &ws);
+    if (st != MPB_OK) return st;
+  }
+  return attn_common(plan, problem, q, k, v, o, lse, scale, mod, ws, need, stream, 0, sp);
 }
 
 size_t flex_attn_fwd_paged_workspace_size(const mpb_plan* plan, int32_t num_splits) {
