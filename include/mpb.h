@@ -113,7 +113,14 @@ typedef struct mpb_plan_info {
   mpb_problem problem;
   mpb_signature signature;
   int64_t device_bytes;    /* bytes of device memory the plan holds */
+  int32_t build_mode;      /* how the plan was built: MPB_BUILD_EXACT (header read back, then the
+                            * exact block and the materialisation), MPB_BUILD_IN_PLACE (small
+                            * plans: the upper-bound block, schedule and materialisation in one
+                            * launch) or MPB_BUILD_SINGLE_PASS (forward plans: one pass over the
+                            * endpoints, block cut to its exact size after the header) */
+  int32_t reserved;
 } mpb_plan_info;
+enum { MPB_BUILD_EXACT = 0, MPB_BUILD_IN_PLACE = 1, MPB_BUILD_SINGLE_PASS = 2 };
 
 /* score_mod of [FLEX] Eq. 1, applied to t = scale * (q . k):
  *   softcap:  t <- softcap * tanh(t / softcap)

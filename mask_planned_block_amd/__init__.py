@@ -31,6 +31,7 @@ LAYOUT_BSHD = 0
 LAYOUT_THD = 1
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
+BUILD_EXACT, BUILD_IN_PLACE, BUILD_SINGLE_PASS = 0, 1, 2   # PlanInfo.build_mode
 NUM_QUEUES = 9
 TASK_REC_INTS = 16
 TASK_REC_FIELDS = ("m_block", "head", "batch", "q_valid_rows", "q_offset", "k_offset", "q_len",
@@ -73,7 +74,8 @@ class PlanInfo(ctypes.Structure):
                 ("nk_max", ctypes.c_int32), ("words_per_row", ctypes.c_int32),
                 ("num_tasks", ctypes.c_int32), ("num_sections", ctypes.c_int32),
                 ("device", ctypes.c_int32), ("problem", Problem), ("signature", Signature),
-                ("device_bytes", ctypes.c_int64)]
+                ("device_bytes", ctypes.c_int64), ("build_mode", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class BuildOptions(ctypes.Structure):

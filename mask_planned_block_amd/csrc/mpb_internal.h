@@ -144,6 +144,36 @@ hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const 
 // Whether that launch's LDS fits (count matrix in LDS or not, its chunks).
 bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks);
 
+// Single-pass builds (forward plans whose block at the upper bound of every
+// count fits the library's cap): classification, offsets by decoupled
+// look-back, lists and payload in one launch, then the schedule and the
+// placement of the lists in a second one.
+struct SinglePass {
+  uint64_t* lb;          // [Hmask * upper_rows][4] look-back words {aggregate, inclusive
+                         // partial, inclusive full, done}, each (tag << 32) | value
+  uint32_t tag;          // this build's tag (nonzero; words of earlier builds differ)
+  int32_t* ticket;       // item counter: 0 on entry, left 0
+  int32_t* host_slot;    // host-mapped header slot
+  int32_t seq;           // the build's sequence number (published last)
+  int32_t* p_list;       // [Hmask * upper_rows * nk_max] partial lists, flat CSR order
+  int32_t* f_list;       // full lists
+  int32_t stage;         // endpoints: 0 read from HBM; staged in LDS as int32 (1 through
+                         // registers, 2 loaded straight into LDS) or int16 (3)
+};
+// Longest sample (seqlen_k) whose endpoints a single-pass build stages as
+// int16: every column it compares, up to seqlen_k plus a tile and a word,
+// stays below the int16 sentinel 32767.
+constexpr int kShortEpMaxLen = 32000;
+// Header error bit of a single-pass build whose look-back wait ran out.
+constexpr uint32_t kDevErrLookback = 1u << 8;
+// rows_total < 0: THD, rows counted on the device (the grid covers the upper
+// bound).
+hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                                   const PlanWork& w, const SinglePass& sp, int32_t rows_total,
+                                   hipStream_t s);
+hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                        const SinglePass& sp, int64_t tiles_upper, hipStream_t s);
+
 // Backward K2Q view (same tile geometry as the forward plan): count from the
 // classifier's bitsets, then (last workgroup) offsets and header values 3..6
 // published with `seq` at kHeaderSeq2; materialize lists and K-major payload

@@ -229,6 +229,15 @@ __device__ inline uint32_t wave_or(uint32_t x) {
   v |= __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);
   return (uint32_t)__builtin_amdgcn_readlane(v, 63);
 }
+__device__ inline int wave_min(int v) {
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x111, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x112, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x114, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x118, 0xf, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x142, 0xa, 0xf, false));
+  v = min(v, __builtin_amdgcn_update_dpp(INT_MAX, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
 __device__ inline uint32_t wave_and(uint32_t x) {
   int v = (int)x;
   v &= __builtin_amdgcn_update_dpp(-1, v, 0x111, 0xf, 0xf, false);
@@ -693,6 +702,56 @@ __device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int*
 
 }  // namespace
 
+namespace {
+
+// §4.8 step 3: tasks t = t0, t0 + stride, ... (t < rows_total * Hq) to the
+// section-major schedule and, as launch records, to their interleaved launch
+// slots.  P, F: the rows' CSR offsets; FT: first listed K tile per
+// (hm * upper_rows + row); rbase: first in-queue position of each row's
+// tasks; so: queue offsets; cu: an LDS copy of cu_rows or nullptr.
+template <class PP, class RP>
+__device__ __attribute__((always_inline)) inline void write_tasks(
+    const PlanGeo& g, const PlanDev& d, PP P, PP F, PP FT, RP rbase, const int* cu,
+    const int (&so)[kNumQueues + 1], int rows_total, int t0, int stride) {
+  const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
+  const int ntasks = rows_total * Hq;
+  for (int t = t0; t < ntasks; t += stride) {
+    int i, h;
+    if (g.mask_heads == 1) {
+      i = t / Hq;
+      h = t - i * Hq;
+    } else {
+      i = t;
+      h = t / rows_total;
+    }
+    const int hm = g.mask_heads == 1 ? 0 : h;
+    const int row = i - hm * rows_total;
+    const SampleGeo sg = sample_geo(g, d, cu, row);
+    const int p_beg = P[i], np = P[i + 1] - p_beg;
+    const int f_beg = F[i], nf = F[i + 1] - f_beg;
+    int s, rank;
+    if (np + nf == 0) {
+      s = kNumSections;
+      rank = g.mask_heads == 1 ? h : 0;
+    } else {
+      const int hk = h / group;
+      s = section_of(sg.b, g.heads_k, hk);
+      if (g.mask_heads == 1) {
+        int r;
+        kv_heads_in_section(sg.b, g.heads_k, s, &r);
+        rank = ((hk - r) / kNumSections) * group + (h - hk * group);
+      } else {
+        rank = 0;
+      }
+    }
+    write_task(g, d, so, sg, row - sg.row_begin, h, hm, s,
+               rbase[(int64_t)i * kNumQueues + s] + rank, p_beg, np, f_beg, nf,
+               FT[(int64_t)hm * g.upper_rows + row]);
+  }
+}
+
+}  // namespace
+
 // The schedule, run by one workgroup of 1024 threads; `dyn` is its dynamic
 // LDS.  CNT_LDS: the count matrix is in LDS; ROWS: 0 row data read from the
 // workspace, 1 in LDS, 2 their first positions in LDS too.  (Compile-time, so
@@ -745,13 +804,8 @@ __device__ __attribute__((always_inline)) inline void schedule_block(
   if (hdr_err != 0) return;  // the build failed: no plan is made
   const int rows_total = hdr_rows;
   const int n = g.mask_heads * rows_total;
-  const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
   const int nc = (n + 63) >> 6;
   const int64_t cnt_len = (int64_t)(g.nk_max + 1) * nc;
-  auto first_of = [&](int i) -> int {
-    const int hm = i / rows_total;
-    return FT[(int64_t)hm * g.upper_rows + (i - hm * rows_total)];
-  };
   auto cost_of = [&](int i) -> int { return (P[i + 1] - P[i]) + (F[i + 1] - F[i]); };
 
   const int* cu = nullptr;
@@ -903,57 +957,29 @@ __device__ __attribute__((always_inline)) inline void schedule_block(
       if (lane == 63) sh.vec[wv][s] = incl;
     }
     __syncthreads();
-    if (pos < n) {
-#pragma unroll
-      for (int s = 0; s < kNumQueues; ++s) {
-        int pre = sh.run[s];
-        for (int x = 0; x < wv; ++x) pre += sh.vec[x][s];
-        rbase[(int64_t)i * kNumQueues + s] = pre + first_pos[s];
+    if (tid < kNumQueues) {   // queue tid: exclusive prefix of the wavefront totals
+      int run = sh.run[tid];
+      for (int x = 0; x < 16; ++x) {
+        const int t = sh.vec[x][tid];
+        sh.vec[x][tid] = run;
+        run += t;
       }
+      sh.run[tid] = run;
     }
     __syncthreads();
-    if (tid < kNumQueues)
-      for (int x = 0; x < 16; ++x) sh.run[tid] += sh.vec[x][tid];
-    __syncthreads();
+    if (pos < n) {
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s)
+        rbase[(int64_t)i * kNumQueues + s] = sh.vec[wv][s] + first_pos[s];
+    }
+    __syncthreads();   // sh.vec is reused
   }
 
   // 3. every task, one per thread
   int so[kNumQueues + 1];
 #pragma unroll
   for (int s = 0; s <= kNumQueues; ++s) so[s] = sh.secoff[s];
-  const int ntasks = rows_total * Hq;
-  for (int t = tid; t < ntasks; t += 1024) {
-    int i, h;
-    if (g.mask_heads == 1) {
-      i = t / Hq;
-      h = t - i * Hq;
-    } else {
-      i = t;
-      h = t / rows_total;
-    }
-    const int hm = g.mask_heads == 1 ? 0 : h;
-    const int row = i - hm * rows_total;
-    const SampleGeo sg = sample_geo(g, d, cu, row);
-    const int p_beg = P[i], np = P[i + 1] - p_beg;
-    const int f_beg = F[i], nf = F[i + 1] - f_beg;
-    int s, rank;
-    if (np + nf == 0) {
-      s = kNumSections;
-      rank = g.mask_heads == 1 ? h : 0;
-    } else {
-      const int hk = h / group;
-      s = section_of(sg.b, g.heads_k, hk);
-      if (g.mask_heads == 1) {
-        int r;
-        kv_heads_in_section(sg.b, g.heads_k, s, &r);
-        rank = ((hk - r) / kNumSections) * group + (h - hk * group);
-      } else {
-        rank = 0;
-      }
-    }
-    write_task(g, d, so, sg, row - sg.row_begin, h, hm, s,
-               rbase[(int64_t)i * kNumQueues + s] + rank, p_beg, np, f_beg, nf, first_of(i));
-  }
+  write_tasks(g, d, P, F, FT, rbase, cu, so, rows_total, tid, 1024);
 }
 
 __device__ __attribute__((always_inline)) inline void schedule_any(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
@@ -988,29 +1014,44 @@ __global__ __launch_bounds__(1024) void plan_schedule_kernel(PlanGeo g, PlanDev 
 // [nfunc][T_Q]; else read from HBM through `col`.  (One instance per source
 // keeps LDS reads ds_read: a pointer that may point to either memory would
 // become a flat load.)
-template <bool STAGED>
-__device__ __attribute__((always_inline)) inline void row_payload(
-    const PlanGeo& g, const int* tiles, int np, const int* ep, const int32_t* col, int rho,
-    bool valid, bool is_row, uint32_t* p_masks, int p_begin) {
-  auto E = [&](int f) -> int {
-    if (f >= g.nfunc) return INT_MAX;
-    if constexpr (STAGED) return ep[f * g.tile_q + rho];
-    else return col[(int64_t)f * g.total_q];
-  };
+// E(f): the row's endpoint f, INT_MAX past the last.
+template <class EF>
+__device__ __attribute__((always_inline)) inline void row_payload_e(
+    const PlanGeo& g, const int* tiles, int np, EF&& E, int rho, bool valid, bool is_row,
+    uint32_t* p_masks, int p_begin) {
+  // e0..e3: endpoints ptr..ptr+3, each loaded three steps before it is
+  // needed, so the walk does not wait on one load per endpoint
   int ptr = 0;
-  int nxt = valid ? E(0) : INT_MAX;
+  int e0 = valid ? E(0) : INT_MAX, e1 = valid ? E(1) : INT_MAX;
+  int e2 = valid ? E(2) : INT_MAX, e3 = valid ? E(3) : INT_MAX;
+  auto advance = [&]() {
+    ++ptr;
+    e0 = e1;
+    e1 = e2;
+    e2 = e3;
+    e3 = E(ptr + 3);
+  };
   auto word_at = [&](int c) -> uint32_t {
     if (!valid) return 0u;
-    while (nxt < c) nxt = E(++ptr);
+    while (e3 < c) {   // all four below c: skip them with one round of loads
+      ptr += 4;
+      e0 = E(ptr);
+      e1 = E(ptr + 1);
+      e2 = E(ptr + 2);
+      e3 = E(ptr + 3);
+    }
+    while (e0 < c) advance();
     uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
-    while (nxt < c + 32) {
-      word ^= 0xFFFFFFFFu << (nxt - c);
-      nxt = E(++ptr);
+    while (e0 < c + 32) {
+      word ^= 0xFFFFFFFFu << (e0 - c);
+      advance();
     }
     return word;
   };
+  int t_next = np > 0 ? tiles[0] : 0;   // the list is read one tile ahead
   for (int k = 0; k < np; ++k) {
-    const int c0 = tiles[k] * g.tile_k;
+    const int c0 = t_next * g.tile_k;
+    if (k + 1 < np) t_next = tiles[k + 1];
     uint32_t* dst = p_masks + ((int64_t)(p_begin + k) * g.tile_q + rho) * g.words_tile;
     if (g.words_tile == 2) {
       const uint32_t w0 = word_at(c0);
@@ -1023,6 +1064,51 @@ __device__ __attribute__((always_inline)) inline void row_payload(
       }
     }
   }
+}
+
+// The payload walk of a staged row, kept to a few instructions per word: the
+// tile's column is uniform (read once for the wavefront), the words go out
+// by buffer stores whose per-tile offset is a scalar add, and a word with no
+// endpoint inside costs two compares.  E(f) must hold a sentinel above every
+// column at f = nfunc.  Rows past q_len write 0.
+template <class EF>
+__device__ __attribute__((always_inline)) inline void row_payload_tight(
+    const PlanGeo& g, const int* tiles, int np, EF&& E, int rho, bool valid, bool is_row,
+    uint32_t* p_masks, int p_begin) {
+  const int W = g.words_tile;
+  const int64_t cap = (int64_t)g.mask_heads * g.upper_rows * g.nk_max * g.tile_q * W * 4;
+  const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      p_masks, (short)0, (int)(cap < 0x7FFFFFFF ? cap : 0x7FFFFFFF), 0x00020000);
+  const uint32_t step = (uint32_t)g.tile_q * W * 4;
+  uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(p_begin) * step;   // uniform
+  const uint32_t voff = (uint32_t)rho * W * 4;
+  int ptr = valid ? 0 : 1;   // a row past q_len: invisible everywhere
+  int e0 = valid ? E(0) : INT_MAX;
+  for (int k = 0; k < np; ++k, soff += step) {
+    const int c0 = __builtin_amdgcn_readfirstlane(tiles[k]) * g.tile_k;
+    for (int x = 0; x < W; ++x) {
+      const int c = c0 + 32 * x;
+      while (e0 < c) e0 = E(++ptr);
+      uint32_t word = (ptr & 1) ? 0u : 0xFFFFFFFFu;
+      while (e0 < c + 32) {
+        word ^= 0xFFFFFFFFu << (e0 - c);
+        e0 = E(++ptr);
+      }
+      if (is_row) __builtin_amdgcn_raw_buffer_store_b32(word, rm, (int)(voff + 4 * x), (int)soff, 0);
+    }
+  }
+}
+
+template <bool STAGED>
+__device__ __attribute__((always_inline)) inline void row_payload(
+    const PlanGeo& g, const int* tiles, int np, const int* ep, const int32_t* col, int rho,
+    bool valid, bool is_row, uint32_t* p_masks, int p_begin) {
+  auto E = [&](int f) -> int {
+    if (f >= g.nfunc) return INT_MAX;
+    if constexpr (STAGED) return ep[f * g.tile_q + rho];
+    else return col[(int64_t)f * g.total_q];
+  };
+  row_payload_e(g, tiles, np, E, rho, valid, is_row, p_masks, p_begin);
 }
 
 // One workgroup per (mask head, Q plan row), one thread per Q row of the
@@ -1241,6 +1327,491 @@ __global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
     row_payload<true>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
   else
     row_payload<false>(g, tiles, np, ep, col, rho, valid, is_row, d.p_masks, p_begin);
+}
+
+
+// ---------------------------------------------------------------- single pass
+//
+// Forward plans whose block at the upper bound of every count fits the
+// library's cap are built in one pass over the endpoints: one workgroup per
+// (mask head, Q plan row) item classifies its row (§4.3), takes the exact CSR
+// offsets of its lists by decoupled look-back over the items before it
+// (§4.5), and writes its lists and payload (§4.6, §5) while its endpoints are
+// still in LDS, so the endpoints are read from HBM once.
+//  * Items go out by ticket in flat head-major order: the workgroup that draws
+//    ticket t handles item t, so every item it waits for belongs to a
+//    workgroup that started before it and never waits for a later one.
+//  * Look-back words are tagged with the build's sequence number, so nothing
+//    has to be cleared between builds: a word is valid when its tag is this
+//    build's.  Item t publishes its aggregate (tile counts) as soon as it is
+//    classified, then its inclusive prefix and a "done" word with its error
+//    bits once its look-back ends.  A wavefront reads 64 predecessors at a
+//    time and stops at the nearest inclusive prefix.  Every wait is bounded
+//    (kLookbackSpins polls); a wait that runs out marks the build failed
+//    (kDevErrLookback).
+//  * The item that ends the flat order publishes the header after every
+//    item's "done" word has landed, with the OR of their error bits.
+//  * The lists go to workspace arrays in flat CSR order; the tail launch
+//    (schedule plus list placement) copies them behind the payload once the
+//    total partial count fixes their place in the exact block.
+namespace {
+
+constexpr uint32_t kLookbackSpins = 1u << 20;
+// Sentinel rows after a staged row's endpoints (the walks read up to
+// nfunc + 5) and the int16 sentinel: above every column of a sample short
+// enough for int16 endpoints (seqlen_k <= kShortEpMaxLen).
+constexpr int kEpPad = 6;
+constexpr short kEpSentinel16 = 32767;
+
+__device__ inline uint64_t lb_word(uint32_t tag, uint32_t v) { return ((uint64_t)tag << 32) | v; }
+
+__device__ inline uint64_t lb_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void lb_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Header of a finished single-pass build, to the plan and the host slot
+// (values first, then the sequence number with release semantics).
+__device__ inline void sp_publish(const PlanDev& d, const SinglePass& sp, int rows_total,
+                                  int pnnz, int fnnz, uint32_t err) {
+  const int32_t hdr[8] = {rows_total, pnnz, fnnz, 0, 0, 0, 0, (int32_t)err};
+  for (int i = 0; i < 8; ++i) {
+    d.header[i] = hdr[i];
+    __hip_atomic_store(&sp.host_slot[i], hdr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+  __hip_atomic_store(&sp.host_slot[kHeaderSeq], sp.seq, __ATOMIC_RELEASE,
+                     __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Exclusive prefix over the workgroup's threads of (a, b); totals in ta, tb.
+__device__ inline void block_scan2(int a, int b, int* pa, int* pb, int* ta, int* tb, int* s_a,
+                                   int* s_b) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int ia = wave_incl_scan(a, lane), ib = wave_incl_scan(b, lane);
+  if (lane == 63) {
+    s_a[wv] = ia;
+    s_b[wv] = ib;
+  }
+  __syncthreads();
+  int ra = 0, rb = 0, sa = 0, sb = 0;
+  for (int x = 0; x < nw; ++x) {
+    if (x < wv) {
+      ra += s_a[x];
+      rb += s_b[x];
+    }
+    sa += s_a[x];
+    sb += s_b[x];
+  }
+  *pa = ra + ia - a;
+  *pb = rb + ib - b;
+  *ta = sa;
+  *tb = sb;
+}
+
+}  // namespace
+
+// One workgroup of max(64, T_Q) threads per item, thread rho owning Q row rho
+// of the tile.  EPM, where the item's endpoints [nfunc][T_Q] are read from:
+// 1 LDS as int32 (sp.stage 2: loaded straight into LDS, whole wavefronts of
+// rows; 1: through registers), 2 LDS as int16 (every sample has k_len below
+// 2^15; loaded through registers and checked at full width on the way, half
+// the LDS, so twice the workgroups fit a CU), 0 HBM in both passes.
+template <int EPM>
+__global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
+                                                               const int32_t* __restrict__ mf,
+                                                               PlanDev d, PlanWork w,
+                                                               SinglePass sp) {
+  extern __shared__ int lds[];
+  __shared__ int s_item, s_err, s_err2, s_pbeg, s_fbeg, s_ffirst;
+  __shared__ int s_a[4], s_b[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nw = blockDim.x >> 6;
+  if (tid == 0) {
+    const int t = __hip_atomic_fetch_add(sp.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the last ticket of the grid resets the counter for the next build
+    if (t == (int)gridDim.x - 1)
+      __hip_atomic_store(sp.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_item = t;
+    s_err = 0;
+    s_ffirst = -1;
+    s_err2 = 0;
+  }
+  __syncthreads();
+  const int item = s_item;
+  const int rows_total = rows_total_of(g, d);
+  const int n = g.mask_heads * rows_total;
+  if (item >= n) {
+    // no rows at all (empty THD batch or a failed prefix check): ticket 0
+    // publishes the empty header
+    if (item == 0 && tid == 0) {
+      d.p_off[0] = 0;
+      d.f_off[0] = 0;
+      const uint32_t err = g.layout == MPB_LAYOUT_THD ? (uint32_t)w.geo_err[0] : 0u;
+      sp_publish(d, sp, rows_total, 0, 0, err);
+    }
+    return;
+  }
+  const int hm = item / rows_total;
+  const int row = item - hm * rows_total;
+  const RowGeo rg = row_geometry(g, d, row);
+  const int rho = tid;
+  const bool is_row = rho < g.tile_q;
+  const bool valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
+  const int32_t* col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off +
+                       (int64_t)rg.i * g.tile_q + (valid ? rho : 0);
+  // [nfunc + kEpPad][T_Q] when staged; the pad rows hold a sentinel above
+  // every column, so reads past the last endpoint need no bound check
+  const int ep_rows = g.nfunc + kEpPad;
+  int* ep = lds;
+  short* ep16 = reinterpret_cast<short*>(lds);
+  const int ep_ints = EPM == 1 ? ep_rows * g.tile_q : EPM == 2 ? (ep_rows * g.tile_q + 1) / 2 : 0;
+  uint32_t* s_any = reinterpret_cast<uint32_t*>(lds + ep_ints);
+  uint32_t* s_nfull = s_any + nw * g.words_k;              // [nw][words_k] each
+  int* ptiles = reinterpret_cast<int*>(s_nfull + nw * g.words_k);   // [nk_max]
+
+  // §2 order and bounds of every endpoint of the row (EPM 2: while staging)
+  uint32_t err = 0;
+  if constexpr (EPM == 2) {
+    int prev = 0;
+    for (int f0 = 0; f0 < g.nfunc; f0 += 32) {
+      int v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        v[u] = valid && f0 + u < g.nfunc ? col[(int64_t)(f0 + u) * g.total_q] : 0;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        if (!valid || f0 + u >= g.nfunc) break;
+        const int e = v[u];
+        if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
+        if (f0 + u > 0 && e < prev) err |= MPB_DEVERR_ORDER;
+        prev = e;
+        ep16[(f0 + u) * g.tile_q + rho] = (short)e;
+      }
+    }
+    if (is_row)
+      for (int f = g.nfunc; f < ep_rows; ++f) ep16[f * g.tile_q + rho] = kEpSentinel16;
+    __syncthreads();
+  } else if constexpr (EPM == 1) {
+    if (sp.stage == 2) {
+      // lane l of wavefront v loads row 64v + l of every endpoint column
+      // (rows past q_len load values nobody reads)
+      const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<int32_t*>(mf + (int64_t)hm * g.nfunc * g.total_q), (short)0,
+          (int)((int64_t)g.nfunc * g.total_q * 4), 0x00020000);
+      const uint32_t base = (uint32_t)(rg.q_off + rg.i * g.tile_q + 64 * wv + lane) * 4u;
+      for (int f = 0; f < g.nfunc; ++f)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rm, (__attribute__((address_space(3))) void*)&ep[f * g.tile_q + 64 * wv], 4,
+            (int)(base + (uint32_t)f * (uint32_t)g.total_q * 4u), 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+    } else if (valid) {
+      for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
+    }
+    if (is_row)
+      for (int f = g.nfunc; f < ep_rows; ++f) ep[f * g.tile_q + rho] = INT_MAX;
+    __syncthreads();
+  }
+  // E(f): endpoint f of the row, a value above every column past the last
+  // (staged: f < nfunc + kEpPad without a check)
+  auto E = [&](int f) -> int {
+    if constexpr (EPM == 2) return (int)ep16[f * g.tile_q + rho];
+    else if constexpr (EPM == 1) return ep[f * g.tile_q + rho];
+    else return f >= g.nfunc ? INT_MAX : col[(int64_t)f * g.total_q];
+  };
+
+  if (EPM != 2 && valid) {
+    int prev = 0;
+    for (int f = 0; f < g.nfunc; ++f) {
+      const int e = E(f);
+      if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
+      if (f > 0 && e < prev) err |= MPB_DEVERR_ORDER;
+      prev = e;
+    }
+  }
+
+  // Pass 1 (§4.3), in windows of 256 K tiles (eight 32-bit words per lane):
+  // each lane merges its row's touching intervals into runs and ORs the
+  // tiles each run touches into its "any" words and the tiles it fully covers
+  // into its "full" words, eight words at a time with no branch per tile.
+  // Across the wavefront "any" is OR-ed and "full" AND-ed: a tile is visible
+  // if some row sees part of it and full if every one of the T_Q rows covers
+  // it, which needs every row in bounds (rows past q_len cover nothing; lanes
+  // past T_Q are not rows) and the tile inside k_len (no run passes k_len).
+  const int nk = rg.nk, T = g.tile_k;
+  const int wk = (nk + 31) >> 5;
+  {
+    const int nint = (g.nfunc + 1) >> 1;
+    for (int tg = 0; tg < nk; tg += 256) {
+      uint32_t am[8], fm[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) am[x] = fm[x] = 0u;
+      // tiles [lo, hi) of the window into m; a range inside one word (most
+      // runs) costs one mask and a select per word
+      auto set_range = [&](uint32_t (&m)[8], int lo, int hi) {
+        lo = max(lo, 0);
+        hi = min(hi, 256);
+        if (hi <= lo) return;
+        const int w0 = lo >> 5;
+        if (w0 == ((hi - 1) >> 5)) {
+          const uint32_t bits = range_bits(lo - 32 * w0, hi - 32 * w0);
+#pragma unroll
+          for (int x = 0; x < 8; ++x) m[x] |= x == w0 ? bits : 0u;
+          return;
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int l = min(max(lo - 32 * x, 0), 32), h = min(max(hi - 32 * x, 0), 32);
+          const uint32_t from_l = l >= 32 ? 0u : (0xFFFFFFFFu << l);
+          const uint32_t from_h = h >= 32 ? 0u : (0xFFFFFFFFu << h);
+          m[x] |= from_l & ~from_h;
+        }
+      };
+      const int w_lo = tg * T, w_hi = (tg + 256) * T;
+      auto flush = [&](int a, int b) {
+        if (b <= a || b <= w_lo || a >= w_hi) return;
+        set_range(am, a / T - tg, (b - 1) / T + 1 - tg);
+        const int f0 = (a + T - 1) / T - tg, f1 = b / T - tg;
+        if (f1 > f0) set_range(fm, f0, f1);
+      };
+      if (valid) {
+        int ra = 0, rb = 0;   // open run [ra, rb), empty while rb <= ra
+        for (int p0 = 0; p0 < nint; p0 += 4) {
+          int sv[4], ev[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int p = p0 + u;
+            sv[u] = p > 0 ? E(2 * p - 1) : 0;
+            ev[u] = E(2 * p);   // INT_MAX past the last interval
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (p0 + u >= nint) break;
+            if (ev[u] <= sv[u]) continue;             // empty interval
+            if (rb > ra && sv[u] == rb) {
+              rb = ev[u];                             // touching: extend the run
+            } else {
+              flush(ra, rb);
+              ra = sv[u];
+              rb = ev[u];
+            }
+          }
+        }
+        flush(ra, rb);
+      }
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int wd = (tg >> 5) + x;
+        if (wd < wk) {
+          const uint32_t va = wave_or(am[x]);
+          const uint32_t vf = wave_and(is_row ? fm[x] : 0xFFFFFFFFu);
+          if (lane == 0) {
+            s_any[wv * g.words_k + wd] = va;
+            s_nfull[wv * g.words_k + wd] = ~vf;
+          }
+        }
+      }
+    }
+  }
+  {
+    const uint64_t er = __ballot((err & MPB_DEVERR_RANGE) != 0);
+    const uint64_t eo = __ballot((err & MPB_DEVERR_ORDER) != 0);
+    if (lane == 0 && (er | eo))
+      atomicOr(&s_err, (er ? MPB_DEVERR_RANGE : 0) | (eo ? MPB_DEVERR_ORDER : 0));
+  }
+  __syncthreads();
+
+  // Words of the item: visible = OR over the wavefronts, full = visible and
+  // no wavefront has a row that misses a bit.  Thread tid takes words
+  // [per*tid, per*tid + per).
+  const int per = (wk + (int)blockDim.x - 1) / (int)blockDim.x;   // at most 4
+  const int x0 = per * tid;
+  uint32_t pw[4], fw[4];
+  int cp = 0, cf = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pw[u] = fw[u] = 0u;
+    const int x = x0 + u;
+    if (u < per && x < wk) {
+      uint32_t vis = 0u, nfull = 0u;
+      for (int v = 0; v < nw; ++v) {
+        vis |= s_any[v * g.words_k + x];
+        nfull |= s_nfull[v * g.words_k + x];
+      }
+      vis &= nk - 32 * x >= 32 ? 0xFFFFFFFFu : ((1u << (nk - 32 * x)) - 1u);   // tiles < nk
+      fw[u] = vis & ~nfull;
+      pw[u] = vis & ~fw[u];
+      cp += __popc(pw[u]);
+      cf += __popc(fw[u]);
+    }
+  }
+  int pp, pf, pc, fc;
+  block_scan2(cp, cf, &pp, &pf, &pc, &fc, s_a, s_b);
+  // the ascending partial list into LDS (the payload loop reads it); the
+  // first full tile for the schedule
+  {
+    int k = pp;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t m = pw[u];
+      while (m) {
+        ptiles[k++] = 32 * (x0 + u) + __ffs(m) - 1;
+        m &= m - 1u;
+      }
+    }
+    if (cf > 0 && pf == 0) {
+#pragma unroll
+      for (int u = 3; u >= 0; --u)
+        if (fw[u]) s_ffirst = 32 * (x0 + u) + __ffs(fw[u]) - 1;
+    }
+  }
+
+  // §4.5 offsets by decoupled look-back (wavefront 0).  Only relaxed atomics:
+  // every word carries its whole value, so no other memory has to be made
+  // visible with it (a release or acquire at agent scope would write back or
+  // invalidate the L2 on every publish).
+  if (wv == 0) {
+    const uint32_t tag = sp.tag;
+    uint64_t* lb = sp.lb;
+    if (lane == 0) lb_store(&lb[4 * (int64_t)item], lb_word(tag, ((uint32_t)pc << 16) | (uint32_t)fc));
+    int acc_p = 0, acc_f = 0;
+    int base = item - 1;
+    uint32_t spins = 0;
+    bool timeout = false;
+    while (true) {
+      const int j = base - lane;
+      int st = 2, vp = 0, vf = 0;   // before item 0: an inclusive prefix of 0
+      if (j >= 0) {
+        const uint64_t ip = lb_load(&lb[4 * (int64_t)j + 1]);
+        const uint64_t iq = lb_load(&lb[4 * (int64_t)j + 2]);
+        if ((uint32_t)(ip >> 32) == tag && (uint32_t)(iq >> 32) == tag) {
+          vp = (int)(uint32_t)ip;
+          vf = (int)(uint32_t)iq;
+        } else {
+          const uint64_t ag = lb_load(&lb[4 * (int64_t)j]);
+          if ((uint32_t)(ag >> 32) == tag) {
+            st = 1;
+            vp = (int)((uint32_t)ag >> 16);
+            vf = (int)((uint32_t)ag & 0xFFFFu);
+          } else {
+            st = 0;
+          }
+        }
+      }
+      const uint64_t m2 = __ballot(st == 2);
+      const int L = m2 ? (int)__ffsll((unsigned long long)m2) - 1 : 64;
+      const uint64_t upto = L >= 63 ? ~0ull : ((2ull << L) - 1ull);   // lanes 0..L
+      if (__ballot(st == 0) & upto) {   // a needed predecessor has not published
+        if (++spins > kLookbackSpins) {
+          timeout = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      const bool take = lane <= L;
+      acc_p += wave_sum(take ? vp : 0);
+      acc_f += wave_sum(take ? vf : 0);
+      if (L < 64) break;
+      base -= 64;
+    }
+    if (lane == 0) {
+      lb_store(&lb[4 * (int64_t)item + 1], lb_word(tag, (uint32_t)(acc_p + pc)));
+      lb_store(&lb[4 * (int64_t)item + 2], lb_word(tag, (uint32_t)(acc_f + fc)));
+      // offsets fixed: this item's error bits (and a wait that ran out)
+      lb_store(&lb[4 * (int64_t)item + 3],
+               lb_word(tag, (uint32_t)s_err | (timeout ? kDevErrLookback : 0u)));
+      s_pbeg = acc_p;
+      s_fbeg = acc_f;
+    }
+  }
+  __syncthreads();
+  const int p_begin = s_pbeg, f_begin = s_fbeg;
+  if (tid == 0) {
+    d.p_off[item] = p_begin;
+    d.f_off[item] = f_begin;
+    w.first_tile[(int64_t)hm * g.upper_rows + row] = pc > 0 ? ptiles[0] : s_ffirst;
+  }
+  if (item == n - 1) {
+    // The header waits until every item has fixed its offsets (each did so
+    // from its predecessors' words alone, so these waits end), and carries
+    // the OR of their error bits.
+    const uint32_t tag = sp.tag;
+    uint32_t err_all = 0;
+    for (int j0 = 0; j0 < n; j0 += blockDim.x) {
+      const int j = j0 + tid;
+      if (j >= n) break;
+      uint32_t spins = 0;
+      uint64_t v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+      while ((uint32_t)(v >> 32) != tag) {
+        if (++spins > kLookbackSpins) {
+          v = lb_word(tag, kDevErrLookback);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+      }
+      err_all |= (uint32_t)v;
+    }
+    if (err_all) atomicOr(&s_err2, err_all);
+    __syncthreads();
+    if (tid == 0) {
+      d.p_off[n] = p_begin + pc;
+      d.f_off[n] = f_begin + fc;
+      uint32_t e = (uint32_t)s_err2;
+      if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
+      sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
+    }
+  }
+  // §4.6 lists, flat CSR order, to the workspace
+  for (int k = tid; k < pc; k += blockDim.x) sp.p_list[p_begin + k] = ptiles[k];
+  {
+    int k = f_begin + pf;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t m = fw[u];
+      while (m) {
+        sp.f_list[k++] = 32 * (x0 + u) + __ffs(m) - 1;
+        m &= m - 1u;
+      }
+    }
+  }
+  // §5 payload of every partial tile
+  if (pc > 0) {
+    if constexpr (EPM != 0) row_payload_tight(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
+    else row_payload_e(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
+  }
+}
+
+// The tail of a single-pass build: workgroup 0 runs the schedule (§4.8) on
+// the finished offsets; the others place the partial and full lists behind
+// the payload, where the exact block has them: the payload holds
+// pnnz * T_Q * words_tile words, then come pnnz partial and fnnz full
+// indices, each array starting on a 256-byte boundary (the host binds the
+// same places once it has read the header).
+__global__ __launch_bounds__(1024) void plan_single_pass_tail_kernel(PlanGeo g, PlanDev d,
+                                                                     PlanWork w, SinglePass sp,
+                                                                     int cnt_in_lds,
+                                                                     int rows_in_lds) {
+  extern __shared__ int dyn[];
+  if (blockIdx.x == 0) {
+    schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn);
+    return;
+  }
+  if (d.header[7] != 0) return;   // failed build: nothing to place
+  const int64_t pn = d.header[1], fn = d.header[2];
+  auto padded = [](int64_t bytes) -> int64_t { return (bytes + 255) & ~(int64_t)255; };
+  const int64_t mask_words = pn * g.tile_q * g.words_tile;
+  const int64_t mask_bytes = padded((mask_words > 0 ? mask_words : 1) * 4);
+  int32_t* p_dst = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d.p_masks) + mask_bytes);
+  int32_t* f_dst = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p_dst) +
+                                              padded((pn > 0 ? pn : 1) * 4));
+  const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
+  for (int64_t x = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; x < pn + fn; x += stride) {
+    if (x < pn) p_dst[x] = sp.p_list[x];
+    else f_dst[x - pn] = sp.f_list[x - pn];
+  }
 }
 
 
@@ -1788,6 +2359,44 @@ hipError_t launch_plan_finish(const PlanGeo& g, const int32_t* mask_func, const 
   return hipGetLastError();
 }
 
+
+hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
+                                   const PlanWork& w, const SinglePass& sp, int32_t rows_total,
+                                   hipStream_t s) {
+  const int64_t items = (int64_t)g.mask_heads * (rows_total >= 0 ? rows_total : g.upper_rows);
+  const int threads = g.tile_q < 64 ? 64 : g.tile_q;
+  const int nw = threads / 64;
+  const size_t ep_rows = (size_t)g.nfunc + kEpPad;
+  const size_t ep_ints = sp.stage == 3   ? (ep_rows * g.tile_q + 1) / 2
+                         : sp.stage != 0 ? ep_rows * g.tile_q
+                                         : 0;
+  const size_t lds = ep_ints * 4 + (size_t)2 * nw * g.words_k * 4 + (size_t)g.nk_max * 4;
+  // at least one workgroup, so the header is always published
+  const dim3 grid((unsigned)(items > 0 ? items : 1)), block(threads);
+  if (sp.stage == 3)
+    hipLaunchKernelGGL(plan_single_pass_kernel<2>, grid, block, lds, s, g, mask_func, d, w, sp);
+  else if (sp.stage != 0)
+    hipLaunchKernelGGL(plan_single_pass_kernel<1>, grid, block, lds, s, g, mask_func, d, w, sp);
+  else
+    hipLaunchKernelGGL(plan_single_pass_kernel<0>, grid, block, lds, s, g, mask_func, d, w, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
+                                        const SinglePass& sp, int64_t tiles_upper,
+                                        hipStream_t s) {
+  const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
+  const size_t cnt_bytes = w.chunk_cnt ? 0 : (size_t)(g.nk_max + 1) * w.nchunks * 4;
+  const int rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  const size_t row_bytes =
+      rows_in_lds ? (size_t)(4 * rows + 2 + (rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4 : 0;
+  // list placement: up to 256 workgroups of 1024 threads, four indices each
+  int64_t copy_wgs = (2 * tiles_upper + 4095) / 4096;
+  copy_wgs = copy_wgs < 1 ? 1 : (copy_wgs > 256 ? 256 : copy_wgs);
+  hipLaunchKernelGGL(plan_single_pass_tail_kernel, dim3((unsigned)(1 + copy_wgs)), dim3(1024),
+                     cnt_bytes + row_bytes, s, g, d, w, sp, w.chunk_cnt ? 0 : 1, rows_in_lds);
+  return hipGetLastError();
+}
 
 hipError_t launch_plan_k2q_count(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
                                  const K2QWork& kw, int32_t* arrive, int32_t* host_slot,

@@ -88,7 +88,7 @@ struct mpb_plan {
   size_t blk_off;
   hipStream_t stream;
   StageEvents tev;         // build stage events (time_stages)
-  bool fused_finish;       // in-place build: schedule and materialize in one launch
+  int build_mode;          // kBuildExact, kBuildInPlace or kBuildSinglePass
 };
 
 namespace {
@@ -250,8 +250,9 @@ struct ThreadSlot {
   int32_t* pinned = nullptr;
   int32_t* pinned_dev = nullptr;
   uint32_t seq = 0;
-  int32_t* arrive[64] = {};
+  int32_t* arrive[64] = {};   // [64] counters: classify, K2Q count, single-pass ticket
   Arena arena[64];
+  Arena lookback[64];         // look-back words of single-pass builds
 };
 thread_local ThreadSlot g_slot;
 
@@ -296,6 +297,29 @@ hipError_t arena_acquire(Arena& a, size_t bytes, hipStream_t stream) {
     if ((e = hipMalloc(&a.ptr, want)) != hipSuccess) return e;
     a.bytes = want;
   }
+  a.last = stream;
+  a.used = true;
+  return hipSuccess;
+}
+
+// Look-back words of single-pass builds, per (thread, device).  The buffer
+// holds nothing else and is zeroed when allocated, so every word in it
+// carries the tag of an earlier build of this thread, or 0.  `clear`: zero it
+// again (the sequence numbers wrapped round).
+hipError_t lookback_acquire(Arena& a, size_t bytes, hipStream_t stream, bool clear) {
+  hipError_t e = hipSuccess;
+  if (a.used && a.last != stream && (e = hipStreamSynchronize(a.last)) != hipSuccess) return e;
+  if (a.bytes < bytes) {
+    if (a.ptr && ((e = hipDeviceSynchronize()) != hipSuccess || (e = hipFree(a.ptr)) != hipSuccess))
+      return e;
+    a.ptr = nullptr;
+    a.bytes = 0;
+    const size_t want = std::max(bytes + bytes / 2, (size_t)1 << 16);
+    if ((e = hipMalloc(&a.ptr, want)) != hipSuccess) return e;
+    a.bytes = want;
+    clear = true;
+  }
+  if (clear && (e = hipMemsetAsync(a.ptr, 0, a.bytes, stream)) != hipSuccess) return e;
   a.last = stream;
   a.used = true;
   return hipSuccess;
@@ -356,8 +380,12 @@ struct K2QCounts {
   int64_t krows = 0, pnnz = 0, fnnz = 0;
   bool on = false;
 };
+// lists_last (single-pass builds): the payload comes before the two index
+// lists, so its place does not depend on the counts and the block can be
+// allocated at the upper bound and cut back to the exact size.
 BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int64_t pnnz,
-                         int64_t fnnz, const K2QCounts& kc = K2QCounts()) {
+                         int64_t fnnz, const K2QCounts& kc = K2QCounts(),
+                         bool lists_last = false) {
   const int64_t n_off = p.mask_heads * rows + 1;
   const int64_t tasks = rows * p.heads_q;
   const bool thd = p.layout == MPB_LAYOUT_THD;
@@ -373,9 +401,15 @@ BlockLayout block_layout(const mpb_problem& p, int tq, int tk, int64_t rows, int
   L.rec = c.take<int32_t>(kTaskRecInts * tasks);
   L.p_off = c.take<int32_t>(n_off);
   L.f_off = c.take<int32_t>(n_off);
-  L.p_idx = c.take<int32_t>(pnnz);
-  L.f_idx = c.take<int32_t>(fnnz);
-  L.masks = c.take<uint32_t>(pnnz * tq * (tk / 32));
+  if (lists_last) {
+    L.masks = c.take<uint32_t>(pnnz * tq * (tk / 32));
+    L.p_idx = c.take<int32_t>(pnnz);
+    L.f_idx = c.take<int32_t>(fnnz);
+  } else {
+    L.p_idx = c.take<int32_t>(pnnz);
+    L.f_idx = c.take<int32_t>(fnnz);
+    L.masks = c.take<uint32_t>(pnnz * tq * (tk / 32));
+  }
   if (kc.on) {
     const int64_t nk_off = p.mask_heads * kc.krows + 1;
     L.k_cu = c.take<int32_t>(p.batch + 1);
@@ -427,6 +461,20 @@ PlanDev bind_block(void* block, const BlockLayout& L, bool thd) {
 // and every planner kernel writes its part in place, so the launches follow
 // each other with no host round trip and no staging copy.
 constexpr size_t kInPlaceBlockBytes = (size_t)32 << 20;
+
+// Forward plans whose block at the upper bound of every count, plus the list
+// workspace at that bound, stays under this size are built in a single pass
+// (plan_single_pass_kernel): the block is allocated at the upper bound, every
+// array is written in place, and once the header is back the block is cut to
+// its exact size (the payload and the lists end it), so the plan keeps no
+// padding of its lists or payload.
+constexpr size_t kSinglePassBytes = (size_t)2 << 30;
+
+enum BuildMode {
+  kBuildExact = MPB_BUILD_EXACT,
+  kBuildInPlace = MPB_BUILD_IN_PLACE,
+  kBuildSinglePass = MPB_BUILD_SINGLE_PASS
+};
 
 int device_cus(int dev) {
   // fixed-size cache (no allocation on any call path)
@@ -638,6 +686,12 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const int64_t cnt_len = (nk_max + 1) * nchunks;
   // The schedule's [cost][chunk] count matrix lives in LDS when it fits.
   const bool cnt_in_lds = cnt_len * 4 <= 60 * 1024;
+  const int64_t tiles_upper = items_upper * nk_max;
+  // Single pass: forward plans whose upper-bound block (lists last) and list
+  // workspace fit kSinglePassBytes.
+  const BlockLayout L_sp = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper, K2QCounts(),
+                                        true);
+  const bool single = !bwd && L_sp.bytes + (size_t)tiles_upper * 8 <= kSinglePassBytes;
   Carver cw;
   const size_t o_vis = cw.take<uint32_t>(items_upper * words_k);
   const size_t o_full = cw.take<uint32_t>(items_upper * words_k);
@@ -669,6 +723,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const size_t o_kfo = cw.take<int32_t>(bwd ? kpad + 1 : 0);
   const size_t o_kin = cw.take<int32_t>(4);
   const size_t o_kord = cw.take<int32_t>(bwd ? (int64_t)p.batch * nk_max : 0);
+  const size_t o_plist = cw.take<int32_t>(single ? tiles_upper : 0);
+  const size_t o_flist = cw.take<int32_t>(single ? tiles_upper : 0);
   Arena& arena = slot->arena[dev];
   if ((e = arena_acquire(arena, cw.off, s)) != hipSuccess)
     return device_status(e, "planner workspace");
@@ -731,7 +787,6 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   // In place (small plans): the block at the upper bound of every count,
   // allocated now; every kernel writes the plan directly and the header is
   // read back only to report errors and the exact counts.
-  const int64_t tiles_upper = items_upper * nk_max;
   K2QCounts kc_up;
   kc_up.on = bwd;
   if (bwd) {
@@ -739,7 +794,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     kc_up.pnnz = kc_up.fnnz = tiles_upper;
   }
   const BlockLayout L_up = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper, kc_up);
-  const bool in_place = L_up.bytes <= kInPlaceBlockBytes && plan_finish_fits(g, cnt_in_lds, nchunks);
+  const bool in_place =
+      !single && L_up.bytes <= kInPlaceBlockBytes && plan_finish_fits(g, cnt_in_lds, nchunks);
   void* block = nullptr;
   int blk_chunk = 0;
   size_t blk_off = 0, blk_bytes = 0;
@@ -747,7 +803,47 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   std::memset(&d, 0, sizeof(d));
   K2QDev kd;
   std::memset(&kd, 0, sizeof(kd));
-  if (in_place) {
+  if (single) {
+    if ((e = lookback_acquire(slot->lookback[dev], (size_t)items_upper * 32, s, seq == 1)) !=
+        hipSuccess)
+      return device_status(e, "look-back words");
+    if ((e = heap->alloc(L_sp.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
+      return device_status(e, "plan allocation");
+    blk_bytes = L_sp.bytes;
+    d = bind_block(block, L_sp, thd);
+    SinglePass sp;
+    sp.lb = static_cast<uint64_t*>(slot->lookback[dev].ptr);
+    sp.tag = seq;
+    sp.ticket = slot->arrive[dev] + 32;
+    sp.host_slot = slot->pinned_dev;
+    sp.seq = (int32_t)seq;
+    sp.p_list = at<int32_t>(wb, o_plist);
+    sp.f_list = at<int32_t>(wb, o_flist);
+    // endpoints staged in LDS when [nfunc + 6][T_Q] takes at most 48 KiB: as
+    // int16 when the longest sample (seqlen_k) has at most kShortEpMaxLen
+    // keys, else as int32, loaded straight into LDS for whole wavefronts of
+    // rows and 32-bit offsets
+    const bool short_ep = p.seqlen_k <= kShortEpMaxLen;
+    const bool stage_ep = ((int64_t)p.nfunc + 6) * tq * (short_ep ? 2 : 4) <= 48 * 1024;
+    sp.stage = !stage_ep ? 0
+               : short_ep ? 3
+               : (tq >= 64 && (int64_t)p.nfunc * p.total_q * 4 < ((int64_t)1 << 31)) ? 2
+                                                                                      : 1;
+    PlanWork ws = w;   // the schedule reads the plan's own offsets
+    ws.p_off_tmp = d.p_off;
+    ws.f_off_tmp = d.f_off;
+    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, d, w, s); })) !=
+            hipSuccess ||
+        (e = tev.timed(1, s, [&] {
+           return launch_plan_single_pass(g, mask_func, d, w, sp, thd ? -1 : (int32_t)upper, s);
+         })) != hipSuccess ||
+        (e = tev.timed(2, s, [&] {
+           return launch_plan_single_pass_tail(g, d, ws, sp, tiles_upper, s);
+         })) != hipSuccess) {
+      heap->release(blk_chunk, blk_off, blk_bytes, s);
+      return device_status(e, "planner launch");
+    }
+  } else if (in_place) {
     if ((e = heap->alloc(L_up.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
       return device_status(e, "plan allocation");
     blk_bytes = L_up.bytes;
@@ -816,6 +912,9 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const uint32_t err = (uint32_t)header[7];
   if (err) {
     drop_block();
+    if (err & kDevErrLookback)
+      return fail(MPB_ERR_DEVICE, "a single-pass planner workgroup waited too long for the "
+                                  "offsets of the rows before it");
     if (err & MPB_DEVERR_SEQLENS)
       return fail(MPB_ERR_SEQLENS,
                   "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
@@ -845,7 +944,22 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     }
   }
 
-  if (!in_place) {
+  if (single) {
+    // The exact layout keeps every place but those of the two lists (which the
+    // tail launch has written behind the payload); the rest of the block goes
+    // back to the heap in stream order.
+    const BlockLayout L = block_layout(p, tq, tk, upper, pnnz, fnnz, K2QCounts(), true);
+    d.p_idx = at<int32_t>(block, L.p_idx);
+    d.f_idx = at<int32_t>(block, L.f_idx);
+    if (L.bytes < blk_bytes) {
+      if ((e = heap->release(blk_chunk, blk_off + L.bytes, blk_bytes - L.bytes, s)) !=
+          hipSuccess) {
+        drop_block();
+        return device_status(e, "plan trim");
+      }
+      blk_bytes = L.bytes;
+    }
+  } else if (!in_place) {
     // Exact allocation: every retained array sized by the header, no
     // capacity padding (§4.5); one block per plan.
     const BlockLayout L = block_layout(p, tq, tk, rows_total, pnnz, fnnz, kc);
@@ -888,7 +1002,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   plan->blk_off = blk_off;
   plan->stream = s;
   plan->tev = tev;
-  plan->fused_finish = in_place;
+  plan->build_mode = single ? kBuildSinglePass : in_place ? kBuildInPlace : kBuildExact;
   tev_guard.t = nullptr;   // the plan owns the events now
   *out = plan;
   return ok();
@@ -919,6 +1033,8 @@ mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info) {
   info->problem = plan->prob;
   info->signature = plan->sig;
   info->device_bytes = (int64_t)plan->bytes;
+  info->build_mode = plan->build_mode;
+  info->reserved = 0;
   return ok();
 }
 

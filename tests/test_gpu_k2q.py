@@ -163,9 +163,8 @@ def test_k2q_no_k_rows():
     assert int(plan.info.header[4]) == 0
 
 
-@pytest.mark.parametrize("name,small,in_place", [("window_sink", True, True),
-                                                 ("block_sparse", False, False)])
-def test_stage_times(name, small, in_place):
+@pytest.mark.parametrize("name,small", [("window_sink", True), ("block_sparse", False)])
+def test_stage_times(name, small):
     import mask_planned_block_amd as mpb
     w = W.make(name, small=small, with_values=False)
     _case("stage_times", name=name, small=small)
@@ -175,7 +174,12 @@ def test_stage_times(name, small, in_place):
         tq, tk = plan.problem.tile_q, plan.problem.tile_k
         t = plan.stage_times()
         assert t["classify"] > 0 and t["schedule"] > 0, t
-        assert (t["materialize"] == -1) == in_place, t
+        # forward plans are built in a single pass, backward ones in place
+        # (small) or with the exact block allocated after the header
+        mode = plan.info.build_mode
+        assert mode == (mpb.BUILD_SINGLE_PASS if not bwd else
+                        mpb.BUILD_IN_PLACE if small else mpb.BUILD_EXACT), (bwd, mode)
+        assert (t["materialize"] == -1) == (mode != mpb.BUILD_EXACT), t
         for k in ("k2q_count", "k2q_materialize"):
             assert (t[k] > 0) if bwd else (t[k] == -1), t
         assert t["span"] >= max(t[k] for k in mpb.STAGE_NAMES[:-1]), t
