@@ -1683,13 +1683,14 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
       const int j = base - lane;
       int st = 2, vp = 0, vf = 0;   // before item 0: an inclusive prefix of 0
       if (j >= 0) {
+        // the three words in one round of loads
+        const uint64_t ag = lb_load(&lb[4 * (int64_t)j]);
         const uint64_t ip = lb_load(&lb[4 * (int64_t)j + 1]);
         const uint64_t iq = lb_load(&lb[4 * (int64_t)j + 2]);
         if ((uint32_t)(ip >> 32) == tag && (uint32_t)(iq >> 32) == tag) {
           vp = (int)(uint32_t)ip;
           vf = (int)(uint32_t)iq;
         } else {
-          const uint64_t ag = lb_load(&lb[4 * (int64_t)j]);
           if ((uint32_t)(ag >> 32) == tag) {
             st = 1;
             vp = (int)((uint32_t)ag >> 16);

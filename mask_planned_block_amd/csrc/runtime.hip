@@ -819,12 +819,14 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     sp.seq = (int32_t)seq;
     sp.p_list = at<int32_t>(wb, o_plist);
     sp.f_list = at<int32_t>(wb, o_flist);
-    // endpoints staged in LDS when [nfunc + 6][T_Q] takes at most 48 KiB: as
-    // int16 when the longest sample (seqlen_k) has at most kShortEpMaxLen
-    // keys, else as int32, loaded straight into LDS for whole wavefronts of
-    // rows and 32-bit offsets
-    const bool short_ep = p.seqlen_k <= kShortEpMaxLen;
-    const bool stage_ep = ((int64_t)p.nfunc + 6) * tq * (short_ep ? 2 : 4) <= 48 * 1024;
+    // endpoints staged in LDS when [nfunc + 6][T_Q] takes at most 48 KiB:
+    // as int32 loaded straight into LDS (whole wavefronts of rows, 32-bit
+    // offsets) while that takes at most 16 KiB, else as int16 when the
+    // longest sample (seqlen_k) has at most kShortEpMaxLen keys (half the
+    // LDS, so twice the items fit a CU, for loads through registers)
+    const int64_t ep32_bytes = ((int64_t)p.nfunc + 6) * tq * 4;
+    const bool short_ep = p.seqlen_k <= kShortEpMaxLen && ep32_bytes > 16 * 1024;
+    const bool stage_ep = (short_ep ? ep32_bytes / 2 : ep32_bytes) <= 48 * 1024;
     sp.stage = !stage_ep ? 0
                : short_ep ? 3
                : (tq >= 64 && (int64_t)p.nfunc * p.total_q * 4 < ((int64_t)1 << 31)) ? 2
