@@ -646,10 +646,9 @@ __device__ inline int launch_slot(const int* secoff, int s, int r) {
 //     record, at its section-interleaved launch slot (slot 8r+x holds the r-th
 //     task of section x while every section still has tasks).
 // Up to kSchedLdsRows rows, the row data (offsets, first tiles, the sorted
-// order) live in LDS, and up to kSchedLdsBaseRows rows their nine first
-// positions too; past that in the build workspace.
+// order) live in LDS, and their nine first positions too while they fit
+// (sched_rows_in_lds); past that in the build workspace.
 constexpr int kSchedLdsRows = 4096;
-constexpr int kSchedLdsBaseRows = 1024;   // rows whose first positions also fit in LDS
 
 namespace {
 
@@ -767,9 +766,14 @@ struct SchedShared {
   int cu[1025];
 };
 
+// rank / nranks: several workgroups may run the schedule together, each
+// sorting the rows itself (the sort only writes LDS: CNT_LDS and ROWS == 2)
+// and writing every nranks-th block of 1024 tasks; rank 0 also writes the
+// section offsets and the fixed-length geometry.
 template <bool CNT_LDS, int ROWS>
 __device__ __attribute__((always_inline)) inline void schedule_block(
-    const PlanGeo& g, const PlanDev& d, const PlanWork& w, int* dyn, SchedShared& sh) {
+    const PlanGeo& g, const PlanDev& d, const PlanWork& w, int* dyn, SchedShared& sh, int rank,
+    int nranks) {
   constexpr bool cnt_in_lds = CNT_LDS;
   constexpr int rows_in_lds = ROWS;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -812,13 +816,13 @@ __device__ __attribute__((always_inline)) inline void schedule_block(
   if (g.layout == MPB_LAYOUT_BSHD) {
     // Fixed-length geometry in closed form (§4.2: rectangular upper bound).
     const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
-    for (int b = tid; b < g.batch; b += 1024) {
+    for (int b = tid; b < g.batch && rank == 0; b += 1024) {
       int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
       sd[0] = make_int4(b * g.seqlen_q, b * g.seqlen_k, g.seqlen_q, g.seqlen_k);
       sd[1] = make_int4(b * rps, rps, (g.seqlen_k + g.tile_k - 1) / g.tile_k, 0);
       d.cu_rows[b + 1] = (b + 1) * rps;
     }
-    if (tid == 0) d.cu_rows[0] = 0;
+    if (tid == 0 && rank == 0) d.cu_rows[0] = 0;
   } else if (g.batch < 1025) {
     for (int b = tid; b <= g.batch; b += 1024) sh.cu[b] = d.cu_rows[b];
     cu = sh.cu;
@@ -917,7 +921,8 @@ __device__ __attribute__((always_inline)) inline void schedule_block(
   if (tid == 0) {
     sh.secoff[0] = 0;
     for (int s = 0; s < kNumQueues; ++s) sh.secoff[s + 1] = sh.secoff[s] + sh.tot[s];
-    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = sh.secoff[s];
+    if (rank == 0)
+      for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = sh.secoff[s];
   }
   __syncthreads();
 
@@ -979,20 +984,21 @@ __device__ __attribute__((always_inline)) inline void schedule_block(
   int so[kNumQueues + 1];
 #pragma unroll
   for (int s = 0; s <= kNumQueues; ++s) so[s] = sh.secoff[s];
-  write_tasks(g, d, P, F, FT, rbase, cu, so, rows_total, tid, 1024);
+  write_tasks(g, d, P, F, FT, rbase, cu, so, rows_total, tid + 1024 * rank, 1024 * nranks);
 }
 
-__device__ __attribute__((always_inline)) inline void schedule_any(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                    int cnt_in_lds, int rows_in_lds, int* dyn) {
+__device__ __attribute__((always_inline)) inline void schedule_any(
+    const PlanGeo& g, const PlanDev& d, const PlanWork& w, int cnt_in_lds, int rows_in_lds,
+    int* dyn, int rank = 0, int nranks = 1) {
   __shared__ SchedShared sh;
   if (cnt_in_lds) {
-    if (rows_in_lds == 2) schedule_block<true, 2>(g, d, w, dyn, sh);
-    else if (rows_in_lds == 1) schedule_block<true, 1>(g, d, w, dyn, sh);
-    else schedule_block<true, 0>(g, d, w, dyn, sh);
+    if (rows_in_lds == 2) schedule_block<true, 2>(g, d, w, dyn, sh, rank, nranks);
+    else if (rows_in_lds == 1) schedule_block<true, 1>(g, d, w, dyn, sh, 0, 1);
+    else schedule_block<true, 0>(g, d, w, dyn, sh, 0, 1);
   } else {
-    if (rows_in_lds == 2) schedule_block<false, 2>(g, d, w, dyn, sh);
-    else if (rows_in_lds == 1) schedule_block<false, 1>(g, d, w, dyn, sh);
-    else schedule_block<false, 0>(g, d, w, dyn, sh);
+    if (rows_in_lds == 2) schedule_block<false, 2>(g, d, w, dyn, sh, 0, 1);
+    else if (rows_in_lds == 1) schedule_block<false, 1>(g, d, w, dyn, sh, 0, 1);
+    else schedule_block<false, 0>(g, d, w, dyn, sh, 0, 1);
   }
 }
 
@@ -1796,7 +1802,10 @@ __global__ __launch_bounds__(1024) void plan_single_pass_tail_kernel(PlanGeo g, 
                                                                      int cnt_in_lds,
                                                                      int rows_in_lds) {
   extern __shared__ int dyn[];
-  if (blockIdx.x == 0) {
+  // With the sort in LDS every workgroup sorts and writes its share of the
+  // tasks (after its share of the lists); else workgroup 0 alone schedules.
+  const bool shared_sort = cnt_in_lds && rows_in_lds == 2;
+  if (blockIdx.x == 0 && !shared_sort) {
     schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn);
     return;
   }
@@ -1808,11 +1817,14 @@ __global__ __launch_bounds__(1024) void plan_single_pass_tail_kernel(PlanGeo g, 
   int32_t* p_dst = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(d.p_masks) + mask_bytes);
   int32_t* f_dst = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(p_dst) +
                                               padded((pn > 0 ? pn : 1) * 4));
-  const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
-  for (int64_t x = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; x < pn + fn; x += stride) {
+  const int copiers = shared_sort ? (int)gridDim.x : (int)gridDim.x - 1;
+  const int me = shared_sort ? (int)blockIdx.x : (int)blockIdx.x - 1;
+  const int64_t stride = (int64_t)copiers * blockDim.x;
+  for (int64_t x = (int64_t)me * blockDim.x + threadIdx.x; x < pn + fn; x += stride) {
     if (x < pn) p_dst[x] = sp.p_list[x];
     else f_dst[x - pn] = sp.f_list[x - pn];
   }
+  if (shared_sort) schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn, blockIdx.x, gridDim.x);
 }
 
 
@@ -2237,6 +2249,17 @@ __global__ __launch_bounds__(256) void plan_k2q_materialize_kernel(
 
 static inline int rows_per_lane(int tile_q) { return tile_q <= 64 ? 1 : tile_q / 64; }
 
+// Where the schedule keeps its row data: 2 offsets, first tiles, order and
+// first positions in LDS, 1 all but the first positions, 0 none -- as much
+// as fits 120 KiB beside the count matrix (cnt_bytes of LDS, 0 when it is in
+// the workspace); at most kSchedLdsRows rows either way.
+static inline int sched_rows_in_lds(int64_t rows, size_t cnt_bytes) {
+  if (rows > kSchedLdsRows) return 0;
+  const size_t two = cnt_bytes + (size_t)(4 * rows + 2 + kNumQueues * rows) * 4;
+  const size_t one = cnt_bytes + (size_t)(4 * rows + 2) * 4;
+  return two <= 120 * 1024 ? 2 : one <= 120 * 1024 ? 1 : 0;
+}
+
 hipError_t launch_plan_geometry(const PlanGeo& g, const int32_t* cu_q_in, const int32_t* cu_k_in,
                                 const PlanDev& d, const PlanWork& w, hipStream_t s) {
   if (g.layout != MPB_LAYOUT_THD) return hipSuccess;
@@ -2269,7 +2292,7 @@ hipError_t launch_plan_schedule(const PlanGeo& g, const PlanDev& d, const PlanWo
   const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
   const size_t cnt_bytes = w.chunk_cnt ? 0 : (size_t)(g.nk_max + 1) * w.nchunks * 4;
   // 0: row data in the workspace; 1: in LDS; 2: their first positions too
-  const int rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  const int rows_in_lds = sched_rows_in_lds(rows, cnt_bytes);
   const size_t row_bytes =
       rows_in_lds ? (size_t)(4 * rows + 2 + (rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4 : 0;
   hipLaunchKernelGGL(plan_schedule_kernel, dim3(1), dim3(1024), cnt_bytes + row_bytes, s, g, d,
@@ -2327,7 +2350,7 @@ FinishShape finish_shape(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks) {
   FinishShape f;
   const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
   const size_t cnt_bytes = cnt_in_lds ? (size_t)(g.nk_max + 1) * nchunks * 4 : 0;
-  f.rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  f.rows_in_lds = sched_rows_in_lds(rows, cnt_bytes);
   const size_t row_bytes =
       f.rows_in_lds ? (size_t)(4 * rows + 2 + (f.rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4
                     : 0;
@@ -2388,11 +2411,14 @@ hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, cons
                                         hipStream_t s) {
   const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
   const size_t cnt_bytes = w.chunk_cnt ? 0 : (size_t)(g.nk_max + 1) * w.nchunks * 4;
-  const int rows_in_lds = rows <= kSchedLdsBaseRows ? 2 : rows <= kSchedLdsRows ? 1 : 0;
+  const int rows_in_lds = sched_rows_in_lds(rows, cnt_bytes);
   const size_t row_bytes =
       rows_in_lds ? (size_t)(4 * rows + 2 + (rows_in_lds == 2 ? kNumQueues * rows : 0)) * 4 : 0;
-  // list placement: up to 256 workgroups of 1024 threads, four indices each
+  // list placement (four indices per thread) and, with the sort in LDS,
+  // tasks (one per thread): up to 256 more workgroups of 1024 threads
+  const int64_t tasks = (int64_t)g.upper_rows * g.heads_q;
   int64_t copy_wgs = (2 * tiles_upper + 4095) / 4096;
+  if (!w.chunk_cnt && rows_in_lds == 2) copy_wgs = std::max(copy_wgs, (tasks + 1023) / 1024 - 1);
   copy_wgs = copy_wgs < 1 ? 1 : (copy_wgs > 256 ? 256 : copy_wgs);
   hipLaunchKernelGGL(plan_single_pass_tail_kernel, dim3((unsigned)(1 + copy_wgs)), dim3(1024),
                      cnt_bytes + row_bytes, s, g, d, w, sp, w.chunk_cnt ? 0 : 1, rows_in_lds);
