@@ -141,11 +141,21 @@ typedef struct mpb_score_mod {
  * (§4.5), the forward schedule (§4.8), one 8-value header read-back (the
  * call waits on the host until the header has landed in host-mapped memory,
  * not for the stream to drain), allocation, and Q2K materialisation of the
- * partial/full CSR and the packed predicates (§4.6, §5).  Allocation is
- * exact (sized by the header) unless the plan's block at the upper bound of
- * every count is at most 32 MiB: then that block is allocated before the
- * launches, every stage writes the plan in place and the schedule and the
- * materialisation run in one launch (mask_plan_info reports the bytes held).
+ * partial/full CSR and the packed predicates (§4.6, §5).  Three build
+ * modes (mask_plan_info's build_mode):
+ *   single pass  forward plans (no backward view) whose block at the upper
+ *                bound of every count, with the list workspace, is at most
+ *                2 GiB: that block is allocated before the launches; one
+ *                launch classifies every (mask head, Q row), takes its CSR
+ *                offsets by decoupled look-back and writes its lists and
+ *                payload (the endpoints are read once), a second runs the
+ *                schedule and places the lists; after the header the block is
+ *                cut to its exact size (nothing padded is kept).
+ *   in place     backward plans whose upper-bound block is at most 32 MiB:
+ *                that block is allocated first and kept; schedule and
+ *                materialisation run in one launch.
+ *   exact        the rest: the block is allocated after the header, sized by
+ *                it, and the materialisation runs after that.
  *
  *   mask_func    device int32 [mask_heads][nfunc][total_q]; column t holds the
  *                endpoints F0..F(nfunc-1) of Q token t, sample-local K
@@ -252,12 +262,14 @@ mpb_status mask_plan_export_k2q_order(const mpb_plan* plan, int32_t* order);
 
 /* GPU time of each planner stage of a build made with time_stages = 1, in
  * microseconds, from the HIP events around its launches [MPD §4.2-§4.7
- * stages]; us must hold 7 floats: us[0] THD geometry (an empty span for
- * BSHD), us[1] classify, us[2] schedule (for a plan built in place, schedule
- * and materialization in one launch), us[3] materialization (-1 when fused),
- * us[4] K2Q count, us[5] K2Q materialization (-1 without the view), us[6]
- * first event to last (when the plan is not built in place this includes the
- * host's header wait).  Waits for the build's last event.
+ * stages]; us must hold 7 floats, -1 for a stage the build did not launch:
+ * us[0] THD geometry (none for BSHD), us[1] classify (a single-pass build:
+ * classification, offsets, lists and payload in one launch), us[2] schedule
+ * (in place: schedule and materialization in one launch; single pass:
+ * schedule and list placement), us[3] materialization (exact builds only),
+ * us[4] K2Q count, us[5] K2Q materialization (backward view only), us[6]
+ * first event to last (for an exact build this includes the host's header
+ * wait).  Waits for the build's last event.
  * MPB_ERR_INVALID_ARGUMENT if the plan was built without time_stages. */
 mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us);
 

@@ -40,6 +40,7 @@ struct StageEvents {
   static constexpr int kStages = 6;   // geometry, classify, schedule, materialize, K2Q x2
   hipEvent_t ev[2 * kStages] = {};
   bool used[kStages] = {};
+  int first = -1;                     // stage launched first
   int last = -1;                      // stage launched last
   bool on = false;
   hipError_t create() {
@@ -65,6 +66,7 @@ struct StageEvents {
     if (r == hipSuccess && on) {
       r = hipEventRecord(ev[2 * stage + 1], s);
       used[stage] = true;
+      if (first < 0) first = stage;
       last = stage;
     }
     return r;
@@ -325,6 +327,14 @@ hipError_t lookback_acquire(Arena& a, size_t bytes, hipStream_t stream, bool cle
   return hipSuccess;
 }
 
+// The THD geometry launch, timed as stage 0; fixed-length plans have no
+// geometry launch and no stage 0.
+hipError_t geometry_stage(StageEvents& tev, const PlanGeo& g, const int32_t* cq,
+                          const int32_t* ck, const PlanDev& d, const PlanWork& w, hipStream_t s) {
+  if (g.layout != MPB_LAYOUT_THD) return hipSuccess;
+  return tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, d, w, s); });
+}
+
 // Wait until the header of build `seq` has landed in the slot.  Now and then
 // (every few hundred microseconds) the stream is queried: if all its work has
 // completed and the sequence number is still not there, the header was never
@@ -496,27 +506,21 @@ int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 12
 // Physical K-tile width when the caller leaves it to the library ([TESS]:
 // the physical tile is chosen for the hardware, independently of the mask's
 // logical blocks).  For bf16 d = 128 with 128-row tiles both 64- and 32-wide
-// K tiles exist: the 32-wide kernel holds three workgroups per CU (two for
-// the 64-wide one) and halves the tile granularity, so it executes fewer
-// masked score entries, but it pays a barrier and an index read per 32
-// columns.  Measured on MI355X over the benchmark shapes, it is faster once
-// the plan has at least as many tasks (Q tiles x heads) as the GPU holds
-// resident 32-wide workgroups (3 per CU), and slower below that, where each
-// workgroup's own speed decides.  The task count is known from the geometry
-// (for THD, total_q / 128 rows, the lower bound).  A plan built for the
-// backward keeps 64-wide tiles: its dK/dV consumer streams the Q and dO tiles
-// of every pair once per K tile, so 32-wide K tiles double that traffic and
-// cost far more in the backward than they save in the forward.
+// K tiles exist.  The 32-wide kernel halves the tile granularity, so it
+// executes fewer masked score entries where visibility changes often along a
+// row, but it pays a barrier and an index read per 32 columns.  Measured on
+// MI355X over the benchmark shapes, 32-wide tiles win only for masks made of
+// many intervals per row (the block-sparse workload, 27 intervals: 443 us
+// against 557 us) and lose where rows are one or two long intervals (causal
+// documents 206 against 188 us, prefix-LM 823 against 750 us), so the
+// library takes 32 from five endpoints (three intervals) per row on.  A plan
+// built for the backward keeps 64-wide tiles: its dK/dV consumer streams the
+// Q and dO tiles of every pair once per K tile, so 32-wide K tiles double
+// that traffic and cost far more in the backward than they save in the
+// forward.
 int default_tile_k(const mpb_problem& p, int tq, bool backward) {
   if (p.dtype == MPB_DTYPE_FP32) return p.head_dim > 64 ? 32 : 64;
-  if (p.head_dim == 128 && tq == 128 && !backward) {
-    const int64_t rows = p.layout == MPB_LAYOUT_BSHD
-                             ? (int64_t)p.batch * ((p.seqlen_q + tq - 1) / tq)
-                             : (int64_t)p.total_q / tq;
-    int dev = 0;
-    const int cus = hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : 256;
-    return rows * p.heads_q >= 3 * (int64_t)cus ? 32 : 64;
-  }
+  if (p.head_dim == 128 && tq == 128 && !backward) return p.nfunc >= 5 ? 32 : 64;
   return 64;
 }
 
@@ -834,7 +838,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     PlanWork ws = w;   // the schedule reads the plan's own offsets
     ws.p_off_tmp = d.p_off;
     ws.f_off_tmp = d.f_off;
-    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, d, w, s); })) !=
+    if ((e = geometry_stage(tev, g, cq, ck, d, w, s)) !=
             hipSuccess ||
         (e = tev.timed(1, s, [&] {
            return launch_plan_single_pass(g, mask_func, d, w, sp, thd ? -1 : (int32_t)upper, s);
@@ -851,7 +855,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     blk_bytes = L_up.bytes;
     d = bind_block(block, L_up, thd);
     kd = bind_k2q(block, L_up, bwd);
-    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, d, w, s); })) !=
+    if ((e = geometry_stage(tev, g, cq, ck, d, w, s)) !=
             hipSuccess ||
         (e = tev.timed(1, s, [&] {
            return launch_plan_classify(g, mask_func, d, w, slot->arrive[dev], slot->pinned_dev,
@@ -871,7 +875,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
       return device_status(e, "planner launch");
     }
   } else {
-    if ((e = tev.timed(0, s, [&] { return launch_plan_geometry(g, cq, ck, sg, w, s); })) !=
+    if ((e = geometry_stage(tev, g, cq, ck, sg, w, s)) !=
             hipSuccess ||
         (e = tev.timed(1, s, [&] {
            return launch_plan_classify(g, mask_func, sg, w, slot->arrive[dev], slot->pinned_dev,
@@ -1130,7 +1134,7 @@ mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us) {
       us[k] = ms * 1e3f;
   }
   float span = 0.0f;
-  if (e == hipSuccess) e = hipEventElapsedTime(&span, t.ev[0], t.ev[2 * t.last + 1]);
+  if (e == hipSuccess) e = hipEventElapsedTime(&span, t.ev[2 * t.first], t.ev[2 * t.last + 1]);
   if (e == hipSuccess) us[StageEvents::kStages] = span * 1e3f;
   if (cur != plan->device) hipSetDevice(cur);
   if (e != hipSuccess) return device_status(e, "stage times");
