@@ -1079,18 +1079,30 @@ __device__ __attribute__((always_inline)) inline void row_payload_e(
 // column at f = nfunc.  Rows past q_len write 0.
 template <class EF>
 __device__ __attribute__((always_inline)) inline void row_payload_tight(
-    const PlanGeo& g, const int* tiles, int np, EF&& E, int rho, bool valid, bool is_row,
-    uint32_t* p_masks, int p_begin) {
+    const PlanGeo& g, const int* tiles, int k_begin, int k_end, EF&& E, int rho, bool valid,
+    bool is_row, uint32_t* p_masks, int p_begin) {
   const int W = g.words_tile;
   const int64_t cap = (int64_t)g.mask_heads * g.upper_rows * g.nk_max * g.tile_q * W * 4;
   const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
       p_masks, (short)0, (int)(cap < 0x7FFFFFFF ? cap : 0x7FFFFFFF), 0x00020000);
   const uint32_t step = (uint32_t)g.tile_q * W * 4;
-  uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(p_begin) * step;   // uniform
+  uint32_t soff = (uint32_t)__builtin_amdgcn_readfirstlane(p_begin + k_begin) * step;   // uniform
   const uint32_t voff = (uint32_t)rho * W * 4;
-  int ptr = valid ? 0 : 1;   // a row past q_len: invisible everywhere
-  int e0 = valid ? E(0) : INT_MAX;
-  for (int k = 0; k < np; ++k, soff += step) {
+  // the walk starts at the first endpoint not below the first tile's column
+  // (binary search; a row past q_len is invisible everywhere)
+  int ptr = 1, e0 = INT_MAX;
+  if (valid) {
+    const int c_first = __builtin_amdgcn_readfirstlane(tiles[k_begin]) * g.tile_k;
+    int lo = 0, hi = g.nfunc;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (E(mid) < c_first) lo = mid + 1;
+      else hi = mid;
+    }
+    ptr = lo;
+    e0 = E(ptr);
+  }
+  for (int k = k_begin; k < k_end; ++k, soff += step) {
     const int c0 = __builtin_amdgcn_readfirstlane(tiles[k]) * g.tile_k;
     for (int x = 0; x < W; ++x) {
       const int c = c0 + 32 * x;
@@ -1418,14 +1430,16 @@ __device__ inline void block_scan2(int a, int b, int* pa, int* pb, int* ta, int*
 
 }  // namespace
 
-// One workgroup of max(64, T_Q) threads per item, thread rho owning Q row rho
-// of the tile.  EPM, where the item's endpoints [nfunc][T_Q] are read from:
+// One workgroup per item: one or two groups of max(64, T_Q) threads, thread
+// rho of a group owning Q row rho of the tile.  EPM, where the item's
+// endpoints [nfunc][T_Q] are read from:
 // 1 LDS as int32 (sp.stage 2: loaded straight into LDS, whole wavefronts of
 // rows; 1: through registers), 2 LDS as int16 (every sample has k_len below
 // 2^15; loaded through registers and checked at full width on the way, half
 // the LDS, so twice the workgroups fit a CU), 0 HBM in both passes.
 template <int EPM>
-__global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6)))
+void plan_single_pass_kernel(PlanGeo g,
                                                                const int32_t* __restrict__ mf,
                                                                PlanDev d, PlanWork w,
                                                                SinglePass sp) {
@@ -1433,7 +1447,14 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
   __shared__ int s_item, s_err, s_err2, s_pbeg, s_fbeg, s_ffirst;
   __shared__ int s_a[4], s_b[4];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nw = blockDim.x >> 6;
+  // ng groups of sg threads: thread rho of every group owns Q row rho of the
+  // tile; the groups split the endpoint loads, the K-tile range of the
+  // classification and the partial tiles of the payload
+  const int sg = g.tile_q < 64 ? 64 : g.tile_q;
+  const int ng = (int)blockDim.x / sg;
+  const int grp = tid / sg;
+  const int nwr = sg >> 6;            // wavefronts per group
+  const int wr = (tid - grp * sg) >> 6;   // this wavefront's 64-row block
   if (tid == 0) {
     const int t = __hip_atomic_fetch_add(sp.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // the last ticket of the grid resets the counter for the next build
@@ -1462,7 +1483,7 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
   const int hm = item / rows_total;
   const int row = item - hm * rows_total;
   const RowGeo rg = row_geometry(g, d, row);
-  const int rho = tid;
+  const int rho = tid - grp * sg;
   const bool is_row = rho < g.tile_q;
   const bool valid = is_row && rg.i * g.tile_q + rho < rg.q_len;
   const int32_t* col = mf + (int64_t)hm * g.nfunc * g.total_q + rg.q_off +
@@ -1474,29 +1495,32 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
   short* ep16 = reinterpret_cast<short*>(lds);
   const int ep_ints = EPM == 1 ? ep_rows * g.tile_q : EPM == 2 ? (ep_rows * g.tile_q + 1) / 2 : 0;
   uint32_t* s_any = reinterpret_cast<uint32_t*>(lds + ep_ints);
-  uint32_t* s_nfull = s_any + nw * g.words_k;              // [nw][words_k] each
-  int* ptiles = reinterpret_cast<int*>(s_nfull + nw * g.words_k);   // [nk_max]
+  uint32_t* s_nfull = s_any + nwr * g.words_k;              // [nwr][words_k] each
+  int* ptiles = reinterpret_cast<int*>(s_nfull + nwr * g.words_k);   // [nk_max]
 
   // §2 order and bounds of every endpoint of the row (EPM 2: while staging)
   uint32_t err = 0;
   if constexpr (EPM == 2) {
-    int prev = 0;
-    for (int f0 = 0; f0 < g.nfunc; f0 += 32) {
+    // group grp loads endpoints grp, grp + ng, ...; bounds are checked on
+    // the full int32 values, order once the whole row is staged
+    for (int f0 = grp; f0 < g.nfunc; f0 += 32 * ng) {
       int v[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        v[u] = valid && f0 + u < g.nfunc ? col[(int64_t)(f0 + u) * g.total_q] : 0;
+      for (int u = 0; u < 32; ++u) {
+        const int f = f0 + u * ng;
+        v[u] = valid && f < g.nfunc ? col[(int64_t)f * g.total_q] : 0;
+      }
 #pragma unroll
       for (int u = 0; u < 32; ++u) {
-        if (!valid || f0 + u >= g.nfunc) break;
-        const int e = v[u];
-        if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
-        if (f0 + u > 0 && e < prev) err |= MPB_DEVERR_ORDER;
-        prev = e;
-        ep16[(f0 + u) * g.tile_q + rho] = (short)e;
+        const int f = f0 + u * ng;
+        if (valid && f < g.nfunc) {
+          const int e = v[u];
+          if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
+          ep16[f * g.tile_q + rho] = (short)e;
+        }
       }
     }
-    if (is_row)
+    if (is_row && grp == 0)
       for (int f = g.nfunc; f < ep_rows; ++f) ep16[f * g.tile_q + rho] = kEpSentinel16;
     __syncthreads();
   } else if constexpr (EPM == 1) {
@@ -1506,16 +1530,16 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
       const rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<int32_t*>(mf + (int64_t)hm * g.nfunc * g.total_q), (short)0,
           (int)((int64_t)g.nfunc * g.total_q * 4), 0x00020000);
-      const uint32_t base = (uint32_t)(rg.q_off + rg.i * g.tile_q + 64 * wv + lane) * 4u;
-      for (int f = 0; f < g.nfunc; ++f)
+      const uint32_t base = (uint32_t)(rg.q_off + rg.i * g.tile_q + 64 * wr + lane) * 4u;
+      for (int f = grp; f < g.nfunc; f += ng)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rm, (__attribute__((address_space(3))) void*)&ep[f * g.tile_q + 64 * wv], 4,
+            rm, (__attribute__((address_space(3))) void*)&ep[f * g.tile_q + 64 * wr], 4,
             (int)(base + (uint32_t)f * (uint32_t)g.total_q * 4u), 0, 0, 0);
       __builtin_amdgcn_s_waitcnt(0);
     } else if (valid) {
-      for (int f = 0; f < g.nfunc; ++f) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
+      for (int f = grp; f < g.nfunc; f += ng) ep[f * g.tile_q + rho] = col[(int64_t)f * g.total_q];
     }
-    if (is_row)
+    if (is_row && grp == 0)
       for (int f = g.nfunc; f < ep_rows; ++f) ep[f * g.tile_q + rho] = INT_MAX;
     __syncthreads();
   }
@@ -1527,13 +1551,13 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
     else return f >= g.nfunc ? INT_MAX : col[(int64_t)f * g.total_q];
   };
 
-  if (EPM != 2 && valid) {
-    int prev = 0;
-    for (int f = 0; f < g.nfunc; ++f) {
+  // §2: every endpoint in [0, k_len] (EPM 2: checked while staging) and no
+  // endpoint below the one before it; group grp takes endpoints grp, grp + ng, ...
+  if (valid) {
+    for (int f = grp; f < g.nfunc; f += ng) {
       const int e = E(f);
-      if (e < 0 || e > rg.k_len) err |= MPB_DEVERR_RANGE;
-      if (f > 0 && e < prev) err |= MPB_DEVERR_ORDER;
-      prev = e;
+      if (EPM != 2 && (e < 0 || e > rg.k_len)) err |= MPB_DEVERR_RANGE;
+      if (f > 0 && e < E(f - 1)) err |= MPB_DEVERR_ORDER;
     }
   }
 
@@ -1549,7 +1573,11 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
   const int wk = (nk + 31) >> 5;
   {
     const int nint = (g.nfunc + 1) >> 1;
-    for (int tg = 0; tg < nk; tg += 256) {
+    // group grp: words [g_w0, g_w1) of the item, tiles [32 g_w0, t_end)
+    const int hw = (wk + ng - 1) / ng;
+    const int g_w0 = min(grp * hw, wk), g_w1 = min(g_w0 + hw, wk);
+    const int t_end = min(32 * g_w1, nk);
+    for (int tg = 32 * g_w0; tg < t_end; tg += 256) {
       uint32_t am[8], fm[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) am[x] = fm[x] = 0u;
@@ -1574,7 +1602,7 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
           m[x] |= from_l & ~from_h;
         }
       };
-      const int w_lo = tg * T, w_hi = (tg + 256) * T;
+      const int w_lo = tg * T, w_hi = min(tg + 256, t_end) * T;
       auto flush = [&](int a, int b) {
         if (b <= a || b <= w_lo || a >= w_hi) return;
         set_range(am, a / T - tg, (b - 1) / T + 1 - tg);
@@ -1609,12 +1637,12 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const int wd = (tg >> 5) + x;
-        if (wd < wk) {
+        if (wd < g_w1) {
           const uint32_t va = wave_or(am[x]);
           const uint32_t vf = wave_and(is_row ? fm[x] : 0xFFFFFFFFu);
           if (lane == 0) {
-            s_any[wv * g.words_k + wd] = va;
-            s_nfull[wv * g.words_k + wd] = ~vf;
+            s_any[wr * g.words_k + wd] = va;
+            s_nfull[wr * g.words_k + wd] = ~vf;
           }
         }
       }
@@ -1641,7 +1669,7 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
     const int x = x0 + u;
     if (u < per && x < wk) {
       uint32_t vis = 0u, nfull = 0u;
-      for (int v = 0; v < nw; ++v) {
+      for (int v = 0; v < nwr; ++v) {
         vis |= s_any[v * g.words_k + x];
         nfull |= s_nfull[v * g.words_k + x];
       }
@@ -1786,8 +1814,14 @@ __global__ __launch_bounds__(256) void plan_single_pass_kernel(PlanGeo g,
   }
   // §5 payload of every partial tile
   if (pc > 0) {
-    if constexpr (EPM != 0) row_payload_tight(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
-    else row_payload_e(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
+    if constexpr (EPM != 0) {
+      // group grp writes partial tiles [k0, k1)
+      const int k0 = (pc * grp) / ng, k1 = (pc * (grp + 1)) / ng;
+      if (k1 > k0)
+        row_payload_tight(g, ptiles, k0, k1, E, rho, valid, is_row, d.p_masks, p_begin);
+    } else {
+      if (grp == 0) row_payload_e(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
+    }
   }
 }
 
@@ -2388,8 +2422,11 @@ hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, c
                                    const PlanWork& w, const SinglePass& sp, int32_t rows_total,
                                    hipStream_t s) {
   const int64_t items = (int64_t)g.mask_heads * (rows_total >= 0 ? rows_total : g.upper_rows);
-  const int threads = g.tile_q < 64 ? 64 : g.tile_q;
-  const int nw = threads / 64;
+  // two groups of T_Q threads per item when the endpoints are staged and
+  // T_Q is 64 or 128 (twice the wavefronts to hide the walks' latency)
+  const int sg = g.tile_q < 64 ? 64 : g.tile_q;
+  const int threads = (sp.stage != 0 && sg <= 128) ? 2 * sg : sg;
+  const int nw = sg / 64;
   const size_t ep_rows = (size_t)g.nfunc + kEpPad;
   const size_t ep_ints = sp.stage == 3   ? (ep_rows * g.tile_q + 1) / 2
                          : sp.stage != 0 ? ep_rows * g.tile_q
