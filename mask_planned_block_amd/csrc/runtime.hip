@@ -506,21 +506,30 @@ int default_tile_q(const mpb_problem& p) { return p.dtype == MPB_DTYPE_BF16 ? 12
 // Physical K-tile width when the caller leaves it to the library ([TESS]:
 // the physical tile is chosen for the hardware, independently of the mask's
 // logical blocks).  For bf16 d = 128 with 128-row tiles both 64- and 32-wide
-// K tiles exist.  The 32-wide kernel halves the tile granularity, so it
-// executes fewer masked score entries where visibility changes often along a
-// row, but it pays a barrier and an index read per 32 columns.  Measured on
-// MI355X over the benchmark shapes, 32-wide tiles win only for masks made of
-// many intervals per row (the block-sparse workload, 27 intervals: 443 us
-// against 557 us) and lose where rows are one or two long intervals (causal
-// documents 206 against 188 us, prefix-LM 823 against 750 us), so the
-// library takes 32 from five endpoints (three intervals) per row on.  A plan
-// built for the backward keeps 64-wide tiles: its dK/dV consumer streams the
-// Q and dO tiles of every pair once per K tile, so 32-wide K tiles double
-// that traffic and cost far more in the backward than they save in the
-// forward.
+// K tiles exist: the 32-wide kernel holds three workgroups per CU (two for
+// the 64-wide one) and halves the tile granularity, so it executes fewer
+// masked score entries, but it pays a barrier and an index read per 32
+// columns.  Measured on MI355X (the two tiles' forwards interleaved, medians
+// of seven rounds), it is faster once the plan has at least as many tasks
+// (Q tiles x heads) as the GPU holds resident 32-wide workgroups (3 per CU):
+// block-sparse 362 against 467 us, causal documents 170 against 184,
+// prefix-LM 712 against 742; below that (the long-K chunk's 128 tasks) each
+// workgroup's own speed decides and the 64-wide kernel wins.  The task count
+// is known from the geometry (for THD, total_q / 128 rows, the lower bound).
+// A plan built for the backward keeps 64-wide tiles: its dK/dV consumer
+// streams the Q and dO tiles of every pair once per K tile, so 32-wide K
+// tiles double that traffic and cost far more in the backward than they save
+// in the forward.
 int default_tile_k(const mpb_problem& p, int tq, bool backward) {
   if (p.dtype == MPB_DTYPE_FP32) return p.head_dim > 64 ? 32 : 64;
-  if (p.head_dim == 128 && tq == 128 && !backward) return p.nfunc >= 5 ? 32 : 64;
+  if (p.head_dim == 128 && tq == 128 && !backward) {
+    const int64_t rows = p.layout == MPB_LAYOUT_BSHD
+                             ? (int64_t)p.batch * ((p.seqlen_q + tq - 1) / tq)
+                             : (int64_t)p.total_q / tq;
+    int dev = 0;
+    const int cus = hipGetDevice(&dev) == hipSuccess ? device_cus(dev) : 256;
+    return rows * p.heads_q >= 3 * (int64_t)cus ? 32 : 64;
+  }
   return 64;
 }
 

@@ -29,14 +29,16 @@ def require_gpu():
 
 
 def default_tiles(w):
-    """The library's tile for a workload whose plan leaves it open: for bf16
-    d=128, 128x32 when rows have at least five endpoints (three intervals),
-    else 128x64; fp32 64x64 (d=64) or 64x32 (d=128)."""
+    """The library's tile for a workload whose plan leaves it open: 128x32 for
+    bf16 d=128 once the plan has at least 3 tasks per CU, else 128x64; fp32
+    64x64 (d=64)."""
     if w.dtype != W.DTYPE_BF16:
         return (64, 64) if w.head_dim == 64 else (64, 32)
     if w.head_dim != 128:
         return (128, 64)
-    return (128, 32) if w.nfunc >= 5 else (128, 64)
+    rows = w.batch * -(-w.seqlen_q // 128) if w.layout == W.LAYOUT_BSHD else w.total_q // 128
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return (128, 32) if rows * w.heads_q >= 3 * cus else (128, 64)
 
 
 def _print_case(case, **kw):
@@ -310,15 +312,15 @@ def test_signature_and_workspace_errors():
 
 
 def test_library_tile_choice():
-    """tile 0x0 resolves from the endpoints per row: bf16 d=128 plans whose
-    rows have at least five endpoints (three intervals) get 128x32 tiles,
-    others 128x64, and plans with the backward view 128x64; an explicit tile
-    is kept."""
-    for nfunc, want in ((5, (128, 32)), (3, (128, 64)), (1, (128, 64))):
-        mf = np.full((1, nfunc, 2048), 2048, np.int32)
-        w = W.custom(mf, batch=1, seqlen_q=2048, seqlen_k=2048, heads_q=4, head_dim=128,
-                     dtype=W.DTYPE_BF16, with_values=False)
-        _print_case("tile_choice", nfunc=nfunc)
+    """tile 0x0 resolves from the task count: bf16 d=128 plans with at least
+    three tasks per CU get 128x32 tiles, smaller ones 128x64, and plans with
+    the backward view 128x64; an explicit tile is kept."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for heads, want in ((3 * cus // 16, (128, 32)), (3 * cus // 16 - 1, (128, 64))):
+        w = W.custom(np.full((1, 1, 2048), 2048, np.int32), batch=1, seqlen_q=2048,
+                     seqlen_k=2048, heads_q=heads, head_dim=128, dtype=W.DTYPE_BF16,
+                     with_values=False)
+        _print_case("tile_choice", heads=heads)
         plan = G.build_plan(w, G.device_inputs(w))
         assert (plan.problem.tile_q, plan.problem.tile_k) == want, (heads, want)
         plan = G.build_plan(w, G.device_inputs(w), 64, 64)
