@@ -190,3 +190,37 @@ def test_stage_times(name, small):
     with pytest.raises(mpb.MPBError) as ei:
         G.build_plan(w, d).stage_times()
     assert ei.value.name == "MPB_ERR_INVALID_ARGUMENT"
+
+
+def _exact_single_pass_bytes(w, tq, tk, header):
+    """Bytes of a single-pass plan's block after the cut: every array rounded
+    to 256 bytes (an empty one still takes 256), the per-row metadata at the
+    rows' upper bound, then the payload and the two index lists at their
+    exact sizes."""
+    def take(count):
+        return -(-max(count, 1) * 4 // 256) * 256
+    thd = w.layout == W.LAYOUT_THD
+    upper = w.batch * -(-w.seqlen_q // tq) if not thd else (w.total_q + w.batch * (tq - 1)) // tq
+    tasks = upper * w.heads_q
+    n_off = w.mask_heads * upper + 1
+    pn, fn = int(header[1]), int(header[2])
+    return (take(8) + take(8 * w.batch) + take(w.batch + 1) +
+            2 * take(w.batch + 1 if thd else 0) + take(4 * tasks) + take(10) + take(16 * tasks) +
+            2 * take(n_off) + take(pn * tq * tk // 32) + take(pn) + take(fn))
+
+
+@pytest.mark.parametrize("name", ["window_sink", "varlen_doc", "block_sparse"])
+def test_single_pass_block_is_cut_to_exact_size(name):
+    """A forward plan built in one pass holds exactly its arrays: the block
+    allocated at the upper bound of every count is cut after the header, so
+    no padded list or payload is kept (only the per-row metadata is sized by
+    the rows' upper bound, which is exact for BSHD)."""
+    import mask_planned_block_amd as mpb
+    w = W.make(name, small=True, with_values=False)
+    _case("single_pass_exact", name=name)
+    plan = G.build_plan(w, G.device_inputs(w))
+    info = plan.info
+    assert info.build_mode == mpb.BUILD_SINGLE_PASS
+    tq, tk = plan.problem.tile_q, plan.problem.tile_k
+    assert info.device_bytes == _exact_single_pass_bytes(w, tq, tk, info.header)
+    G.compare_plan(plan.export(), oracle.build_plan(w, tq, tk))
