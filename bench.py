@@ -18,7 +18,7 @@ counter summary, when that summary was taken on the current kernel source.
 The CPU oracle is timed on the host cores as "cpu_baseline" (a reported
 baseline, not a target).
 
-  --summarize stats|pmc DIRS  digests rocprofv3 csv output instead.
+  --summarize stats|pmc|counters DIRS  digests rocprofv3 csv output instead.
 """
 from __future__ import annotations
 
@@ -346,6 +346,9 @@ def summarize(kind, dirs, copy_mb=0):
     import csv
     import glob
     paths = lambda pat: sorted(p for d in dirs.split(",") for p in glob.glob(os.path.join(d, pat)))
+    if kind == "counters":
+        summarize_counters(paths)
+        return
     if kind == "stats":
         for path in paths("*kernel_stats.csv"):
             print("# %s" % os.path.basename(path))
@@ -389,6 +392,46 @@ def summarize(kind, dirs, copy_mb=0):
     if complete:
         print("attn_source_sha256_16=%s" % source_digest())
         print("traffic_bytes_per_launch=%.0f" % total)
+
+
+def summarize_counters(paths):
+    """Per-kernel averages of every counter in the counter_collection csv
+    files (one pass per directory; at most 8 SQ counters fit one pass), then
+    ratios for the attention forward and the planner kernels: VALU and LDS
+    instructions per MFMA instruction, the share of MFMA-busy cycles in which
+    a VALU instruction issued beside it (SQ_VALU_MFMA_COEXEC_CYCLES over
+    SQ_VALU_MFMA_BUSY_CYCLES), and the share of wavefront cycles spent
+    waiting on a dependency (SQ_WAIT_INST_ANY over SQ_WAVE_CYCLES) or for
+    anything (SQ_WAIT_ANY)."""
+    import csv
+    per = {}
+    for path in paths("*counter_collection.csv"):
+        for r in csv.DictReader(open(path)):
+            g = _kernel_group(r["Kernel_Name"])
+            if g is not None:
+                per.setdefault(g, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    for g in sorted(per):
+        avg = {c: sum(v) / len(v) for c, v in per[g].items()}
+        print("# %s" % g)
+        for c in sorted(avg):
+            print("%-44s %-28s dispatches=%d avg=%.4g" % (g, c, len(per[g][c]), avg[c]))
+        ratios = []
+        mf = avg.get("SQ_INSTS_MFMA")
+        if mf:
+            for c, label in (("SQ_INSTS_VALU", "valu_per_mfma"), ("SQ_INSTS_LDS", "lds_per_mfma")):
+                if c in avg:
+                    ratios.append((label, avg[c] / mf))
+        if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+            ratios.append(("coexec_share_of_mfma_busy",
+                           avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]))
+        if avg.get("SQ_WAVE_CYCLES"):
+            for c, label in (("SQ_WAIT_INST_ANY", "wait_dependency_share"),
+                             ("SQ_WAIT_ANY", "wait_any_share")):
+                if c in avg:
+                    ratios.append((label, avg[c] / avg["SQ_WAVE_CYCLES"]))
+        for label, v in ratios:
+            print("%-44s %-28s %.4f" % (g, label, v))
 
 
 def load_traffic(expected_digest):
@@ -556,7 +599,7 @@ def main():
                     help="oracle seconds per workload in the per-config table")
     ap.add_argument("--summarize", nargs=2, metavar=("KIND", "DIRS"),
                     help="print a summary of rocprofv3 csv output under comma-separated DIRS "
-                         "(KIND: stats or pmc) and exit")
+                         "(KIND: stats, pmc or counters) and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize[0], args.summarize[1], args.copy_calibration_mb)
