@@ -38,18 +38,25 @@ PEAK_FP32_MFMA_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+def plan_rows_tokens(plan):
+    """Tokens per plan row: the tile's rows, or tile_q / G for a PackGQA plan
+    (whose tile rows are its G heads of tile_q / G tokens)."""
+    return plan.problem.tile_q // plan.info.signature.pack_gqa
+
+
 def plan_stats(w, plan):
     """Algorithmic counts from the plan (no oracle): visible pairs |E|,
     executed tiles, dense-equivalent pairs."""
     import numpy as np
     ex = plan.export()
     p = plan.problem
+    tq = plan_rows_tokens(plan)
     pop = int(np.unpackbits(ex["p_masks"].view(np.uint8)).sum()) if ex["p_masks"].size else 0
     pnnz, fnnz = int(ex["header"][1]), int(ex["header"][2])
-    per_mask_head = pop + fnnz * p.tile_q * p.tile_k
+    per_mask_head = pop + fnnz * tq * p.tile_k
     rep = w.heads_q // w.mask_heads
     visible = per_mask_head * rep
-    executed = (pnnz + fnnz) * p.tile_q * p.tile_k * rep
+    executed = (pnnz + fnnz) * tq * p.tile_k * rep
     dense = sum(w.sample_bounds(b)[1] * w.sample_bounds(b)[3] for b in range(w.batch)) * w.heads_q
     return {"visible_pairs": visible, "executed_pairs": executed, "dense_pairs": dense,
             "partial_tiles": pnnz, "full_tiles": fnnz, "rows": int(ex["header"][0]),
@@ -64,8 +71,8 @@ def plan_bytes(w, plan):
     p = plan.problem
     rows, pn, fn = int(h[0]), int(h[1]), int(h[2])
     read = 4 * w.mask_heads * w.nfunc * w.total_q
-    write = 4 * (pn + fn) + pn * p.tile_q * p.tile_k // 8 + 8 * (w.mask_heads * rows + 1) + \
-        16 * int(plan.info.num_tasks)
+    write = 4 * (pn + fn) + pn * plan_rows_tokens(plan) * p.tile_k // 8 + \
+        8 * (w.mask_heads * rows + 1) + 16 * int(plan.info.num_tasks)
     return read + write
 
 
@@ -92,7 +99,8 @@ def attn_bytes(w, plan):
     qo = 2 * w.total_q * w.heads_q * w.head_dim * esz
     kv = 2 * w.total_k * w.heads_k * w.head_dim * esz
     pn, fn = int(h[1]), int(h[2])
-    return qo + kv + 4 * w.heads_q * w.total_q + pn * p.tile_q * p.tile_k // 8 + 4 * (pn + fn)
+    return qo + kv + 4 * w.heads_q * w.total_q + pn * plan_rows_tokens(plan) * p.tile_k // 8 + \
+        4 * (pn + fn)
 
 
 def roofline(flops, nbytes, seconds, peak_tflops):
@@ -495,6 +503,63 @@ def run_splitk(args, mpb, W, torch, np):
     return res
 
 
+PACKGQA_SHAPES = {
+    # 16-token chunks (decoding a few tokens per sample) against 8192 cached
+    # keys, 32 Q heads on 8 K/V heads
+    "decode16_g4": dict(batch=8, heads_q=32, heads_k=8, seqlen_q=16, seqlen_k=8192),
+    # the long-K chunk: 512 queries against a 32768-token prefix
+    "chunk512_g4": dict(),
+}
+
+
+def run_packgqa(args, mpb, W, torch, np):
+    """PackGQA against one head per tile on GQA shapes (causal chunks at the
+    end of a long prefix): HIP events around back-to-back forwards with the
+    library's Split-K choice for each plan; effective TFLOP/s = 4*d per
+    visible pair, GB/s = algorithmic forward bytes per launch."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = {}
+    for name, shape in PACKGQA_SHAPES.items():
+        w = W.chunk_long_kv(**shape)
+        d = W.to_device(w)
+        prob = mpb.make_problem(w.layout, w.dtype, w.batch, w.seqlen_q, w.seqlen_k, w.total_q,
+                                w.total_k, w.heads_q, w.heads_k, w.head_dim, w.mask_heads,
+                                w.nfunc, 0, 0)
+        o = torch.empty_like(d["q"])
+        lse = torch.empty((w.heads_q, w.total_q), dtype=torch.float32, device="cuda")
+        row = {"batch": w.batch, "heads_q": w.heads_q, "heads_k": w.heads_k,
+               "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k}
+        for label, pack in (("unpacked", False), ("packed", True)):
+            plan = mpb.mask_plan_build(prob, d["mask_func"], None, None, stream=stream,
+                                       pack_gqa=pack)
+            st = plan_stats(w, plan)
+            eff = 4.0 * w.head_dim * st["visible_pairs"]
+            sp = mpb.flex_attn_fwd_num_splits(plan)
+            ws = torch.empty(max(mpb.flex_attn_fwd_splitk_workspace_size(plan, 0), 256),
+                             dtype=torch.uint8, device="cuda")
+            call = lambda: mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], scale=w.scale,
+                                             out=o, lse=lse, workspace=ws, stream=stream,
+                                             num_splits=0 if sp > 1 else None)
+            for _ in range(3):
+                call()
+            e0.record(stream)
+            for _ in range(args.packgqa_iters):
+                call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.packgqa_iters
+            row[label] = {"us": round(us, 2), "tasks": st["tasks"], "splits": sp,
+                          "effective_tflops": round(eff / us / 1e6, 2),
+                          "gbs": round(attn_bytes(w, plan) / us / 1e3, 1)}
+            plan.close()
+        row["speedup"] = round(row["unpacked"]["us"] / row["packed"]["us"], 3)
+        out[name] = row
+    out["basis"] = ("HIP events around %d back-to-back forwards (split launch + merge where "
+                    "the library splits)" % args.packgqa_iters)
+    return out
+
+
 def run_paged(args, w, d, plan, kw, mpb, torch, np):
     """Paged K/V overhead: the main workload's K/V scattered into a page pool
     (pages of 2 * tile_k tokens, random page order) and the paged forward
@@ -585,6 +650,8 @@ def main():
     ap.add_argument("--splitk-iters", type=int, default=20,
                     help="back-to-back launches per Split-K configuration timed on the long-K "
                          "chunk shape (0 = skip)")
+    ap.add_argument("--packgqa-iters", type=int, default=20,
+                    help="back-to-back forwards per plan in the PackGQA leg (0 = skip)")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged K/V overhead leg")
     ap.add_argument("--cold-iters", type=int, default=5,
@@ -812,6 +879,7 @@ def main():
         pbw.close()
 
     splitk = run_splitk(args, mpb, W, torch, np) if args.splitk_iters > 0 else None
+    packgqa = run_packgqa(args, mpb, W, torch, np) if args.packgqa_iters > 0 else None
     paged = None
     if not args.no_paged and w.dtype == W.DTYPE_BF16 and args.num_splits is None:
         paged = run_paged(args, w, d, plan, kw, mpb, torch, np)
@@ -899,6 +967,7 @@ def main():
         "plan_k2q": plan_k2q,
         "bwd": bwd,
         "splitk": splitk,
+        "packgqa": packgqa,
         "paged": paged,
         "host": {"build_call_us": round(host_build / args.steps * 1e6, 1),
                  "fwd_call_us": round(host_fwd / args.steps * 1e6, 1)},

@@ -99,6 +99,8 @@ typedef struct mpb_signature {
   int32_t tile_q, tile_k, head_dim, dtype;
   int32_t payload_layout;  /* 1 = row-major, 32-column uint32 words (see below) */
   int32_t scheduler;       /* 2 = one workgroup per task, section-interleaved launch order */
+  int32_t pack_gqa;        /* Q heads per plan row in the consumer tile: 1, or heads_q/heads_k
+                            * when the plan is packed (PackGQA, see mpb_build_options) */
 } mpb_signature;
 
 typedef struct mpb_plan_info {
@@ -107,7 +109,7 @@ typedef struct mpb_plan_info {
   int32_t rows_total;      /* Q plan rows over all samples */
   int32_t nk_max;          /* K tiles of the longest sample */
   int32_t words_per_row;   /* tile_k / 32 */
-  int32_t num_tasks;       /* rows_total * heads_q */
+  int32_t num_tasks;       /* rows_total * heads_q (packed: rows_total * heads_k) */
   int32_t num_sections;    /* schedule sections (8 XCD sections + the zero-cost tail) */
   int32_t device;
   mpb_problem problem;
@@ -177,11 +179,12 @@ typedef struct mpb_score_mod {
  * MPB_ERR_ENDPOINT_ORDER (first set bit in that order).
  *
  * Plan layout (device, read with mask_plan_export):
- *   rows are Q tiles of T_Q tokens per sample; row r of sample b is global row
+ *   rows are Q tiles of T_Q tokens per sample (a packed plan: T_Q/G tokens,
+ *   G = signature.pack_gqa; see mpb_build_options); row r of sample b is global row
  *   cu_rows[b] + r; CSR rows are flattened head-major, flat = hm*rows_total +
  *   row.  p_off/f_off [mask_heads*rows_total + 1] are exclusive offsets into
  *   p_idx/f_idx (sample-local K-tile indices, ascending).  Partial tile n
- *   owns payload words p_masks[n][T_Q][tile_k/32]: bit c%32 of word
+ *   owns payload words p_masks[n][T_Q/G][tile_k/32]: bit c%32 of word
  *   [r][c/32] is 1 iff score (row r, column c) of the tile is visible and in
  *   bounds [MPD §5].  In the attention kernel each lane owns one Q row and 16
  *   K columns of every 32-column block, all in one such word, so it reads its
@@ -202,8 +205,10 @@ mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info);
  * be NULL.  Sizes: cu_rows [batch+1], seqdesc [batch][8] = {q_offset,
  * k_offset, q_len, k_len, row_begin, row_count, k_tiles, 0}, p_off/f_off
  * [mask_heads*rows_total+1], p_idx [header[1]], f_idx [header[2]], p_masks
- * [header[1]*tile_q*tile_k/32], work_desc [num_tasks][4] = {m_block, head,
- * batch, q_valid_rows} in schedule order, section_off [num_sections+1].
+ * [header[1]*(tile_q/pack_gqa)*tile_k/32], work_desc [num_tasks][4] =
+ * {m_block, head, batch, q_valid_rows} in schedule order (a packed plan's
+ * tasks are (row, K/V head): head is the K/V head and q_valid_rows counts
+ * tokens of the row), section_off [num_sections+1].
  * Synchronises the plan's build stream. */
 mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seqdesc,
                             int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
@@ -237,6 +242,19 @@ typedef struct {
   int32_t time_stages;     /* 0 or 1: record HIP events around each planner launch
                             * (mask_plan_stage_times); adds event records to the
                             * build stream, for measurement only */
+  int32_t pack_gqa;        /* PackGQA [MPD §4.1 consumer resolution, §6.2]: 0 = the
+                            * library's choice, 1 = off, 2 = on.  A packed forward tile
+                            * holds T_Q/G tokens x the G = heads_q/heads_k Q heads that
+                            * share one K/V head (tile row r: token r/G of the row, Q
+                            * head G*kv_head + r%G), so one K/V tile load serves all G
+                            * heads and the payload keeps one word row per token (T_Q/G
+                            * payload rows: the same block relation and predicate as an
+                            * unpacked plan with T_Q/G-token rows).  Needs mask_heads = 1
+                            * (every Q head of a group sees the same mask), G a power of
+                            * two with T_Q/G >= 16, and no backward view; 2 with any of
+                            * these unmet is MPB_ERR_UNSUPPORTED.  The library packs
+                            * whenever it may (measured faster on every shape tried:
+                            * short query chunks most, by filling the tile's rows). */
 } mpb_build_options;
 
 /* mask_plan_build with options; same arguments, errors and lifetime rules. */

@@ -66,7 +66,7 @@ class Problem(ctypes.Structure):
 class Signature(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "arch", "direction", "kernel_family", "tile_q", "tile_k", "head_dim", "dtype",
-        "payload_layout", "scheduler")]
+        "payload_layout", "scheduler", "pack_gqa")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -79,7 +79,8 @@ class PlanInfo(ctypes.Structure):
 
 
 class BuildOptions(ctypes.Structure):
-    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32)]
+    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32),
+                ("pack_gqa", ctypes.c_int32)]
 
 
 class ScoreMod(ctypes.Structure):
@@ -249,17 +250,20 @@ class MaskPlan:
 def mask_plan_build(problem: Problem, mask_func: torch.Tensor,
                     cu_seqlens_q: Optional[torch.Tensor] = None,
                     cu_seqlens_k: Optional[torch.Tensor] = None, stream=None,
-                    build_backward: bool = False, time_stages: bool = False) -> MaskPlan:
+                    build_backward: bool = False, time_stages: bool = False,
+                    pack_gqa: Optional[bool] = None) -> MaskPlan:
     """Builds a MaskPlan on the GPU (one header read-back; see include/mpb.h);
     build_backward adds the K2Q view, time_stages records HIP events around the
-    planner launches (both through mask_plan_build_ex)."""
+    planner launches, pack_gqa forces PackGQA on (True) or off (False), None
+    leaves it to the library (all through mask_plan_build_ex)."""
     mf = _dev_ptr(mask_func, "mask_func", torch.int32)
     cq = _dev_ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     ck = _dev_ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32)
     s = _stream_handle(stream)
     out = ctypes.c_void_p()
-    if build_backward or time_stages:
-        opt = BuildOptions(int(build_backward), int(time_stages))
+    pack = 0 if pack_gqa is None else (2 if pack_gqa else 1)
+    if build_backward or time_stages or pack:
+        opt = BuildOptions(int(build_backward), int(time_stages), pack)
         _check(_lib.mask_plan_build_ex(ctypes.byref(problem), ctypes.byref(opt), mf, cq, ck, s,
                                        ctypes.byref(out)))
     else:
@@ -284,12 +288,13 @@ def mask_plan_export(plan: MaskPlan) -> dict:
     n_off = p.mask_heads * info.rows_total + 1
     pnnz, fnnz = int(info.header[1]), int(info.header[2])
     W = p.tile_k // 32
+    tq = p.tile_q // info.signature.pack_gqa   # payload word rows per partial tile
     a = {
         "cu_rows": np.zeros(p.batch + 1, np.int32),
         "seqdesc": np.zeros((p.batch, 8), np.int32),
         "p_off": np.zeros(n_off, np.int32),
         "p_idx": np.zeros(max(pnnz, 1), np.int32),
-        "p_masks": np.zeros(max(pnnz * p.tile_q * W, 1), np.uint32),
+        "p_masks": np.zeros(max(pnnz * tq * W, 1), np.uint32),
         "f_off": np.zeros(n_off, np.int32),
         "f_idx": np.zeros(max(fnnz, 1), np.int32),
         "work_desc": np.zeros((max(info.num_tasks, 1), 4), np.int32),
@@ -301,7 +306,7 @@ def mask_plan_export(plan: MaskPlan) -> dict:
     _check(_lib.mask_plan_export(plan.handle, *ptrs))
     a["p_idx"] = a["p_idx"][:pnnz]
     a["f_idx"] = a["f_idx"][:fnnz]
-    a["p_masks"] = a["p_masks"][:pnnz * p.tile_q * W].reshape(pnnz, p.tile_q, W)
+    a["p_masks"] = a["p_masks"][:pnnz * tq * W].reshape(pnnz, tq, W)
     a["work_desc"] = a["work_desc"][:info.num_tasks]
     a["header"] = np.asarray(list(info.header), np.int64)
     rec = np.zeros((max(info.num_tasks, 1), TASK_REC_INTS), np.int32)

@@ -534,7 +534,7 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
                                  const typename Ops::T* kst, const typename Ops::T* vst,
                                  int lane,
                                  const uint32_t (&mw)[Ops::QB][Ops::NKB],
-                                 const float (&kq0)[Ops::QB], float slope,
+                                 const float (&kq0)[Ops::QB], const float (&slope)[Ops::QB],
                                  f32x16 (&o)[Ops::QB][Ops::D / 32], RowState (&rs)[Ops::QB]) {
   constexpr int QB = Ops::QB, NKB = Ops::NKB, TKV = Ops::TKV;
   if constexpr (MASKED) {
@@ -551,7 +551,8 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // the lane's row spans k - q in [kq0 - 4, kq0 + TKV) over this tile
-      const float bias = fmaxf(slope * (kq0[qb] - 4.0f), slope * (kq0[qb] + (float)TKV));
+      const float bias =
+          fmaxf(slope[qb] * (kq0[qb] - 4.0f), slope[qb] * (kq0[qb] + (float)TKV));
       need |= !(p.softcap_c2 + bias < rs[qb].m - kNegligibleLog2);
     }
     if (__builtin_amdgcn_ballot_w64(need) == 0) return;
@@ -567,7 +568,7 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
   bool any = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
-    any |= softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope, o[qb], rs[qb],
+    any |= softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope[qb], o[qb], rs[qb],
                                            pf.p[qb]);
   if (!any) return;
   __builtin_amdgcn_s_setprio(1);
@@ -659,9 +660,12 @@ __device__ inline rsrc_t paged_tile_rsrc(const char* pool, int j, int phys, int 
 // get 0 / -inf.  Rows past q_len are dropped by the O descriptor's range
 // check.  A Split-K part writes the same for its tiles, in fp32, into its
 // partial-state slice.
+// hq0 is the task's first Q head, hs the lane's head within the task
+// (PackGQA; 0 when unpacked).
 template <class Ops, bool SPLIT>
-__device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t ro,
+__device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t ro, int hq0,
                                   const uint32_t (&q_row_off)[Ops::QB], const int (&qloc)[Ops::QB],
+                                  const int (&hs)[Ops::QB],
                                   const f32x16 (&o)[Ops::QB][Ops::D / 32],
                                   const RowState (&rs)[Ops::QB], int b2) {
   constexpr int D = Ops::D;
@@ -670,7 +674,7 @@ __device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t 
   if constexpr (SPLIT) {
     const int64_t fq_rs = (int64_t)p.heads_q * D;   // floats per token row
     float* ob = p.o_part + (int64_t)c.split * p.total_q * fq_rs + (int64_t)c.q_off * fq_rs +
-                (int64_t)c.h * D;
+                (int64_t)hq0 * D;
     rout = make_rsrc(ob, (uint32_t)(c.q_len * fq_rs * 4));
     lse_out = p.lse_part + (int64_t)c.split * p.heads_q * p.total_q;
   }
@@ -679,11 +683,11 @@ __device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t 
     const float l_tot = pair_sum(rs[qb].l);
     const float inv = l_tot > 0.0f ? rcp_fast(l_tot) : 0.0f;
     if constexpr (SPLIT)
-      store_o_f32<D>(rout, (uint32_t)qloc[qb] * p.heads_q * D * 4, o[qb], inv, b2);
+      store_o_f32<D>(rout, ((uint32_t)qloc[qb] * p.heads_q + hs[qb]) * D * 4, o[qb], inv, b2);
     else
       Ops::store_o(rout, q_row_off[qb], o[qb], inv, b2);
     if (b2 == 0 && qloc[qb] < c.q_len) {
-      lse_out[(int64_t)c.h * p.total_q + c.q_off + qloc[qb]] =
+      lse_out[(int64_t)(hq0 + hs[qb]) * p.total_q + c.q_off + qloc[qb]] =
           l_tot > 0.0f ? (rs[qb].m + __builtin_amdgcn_logf(l_tot)) * kLn2 : kNegInf;
     }
   }
@@ -737,13 +741,18 @@ void attn_fwd_kernel(AttnParams p) {
   const int q_len = c.q_len, k_len = c.k_len;
   const int p_beg = c.p_beg, np = c.np, f_beg = c.f_beg, ntiles = c.ntiles;
   const int j_first = c.j_first;
+  // PackGQA: the task covers Q heads [hq0, hq0 + 2^psh) (the task head is
+  // the K/V head) and TQ >> psh tokens; tile row r is token r >> psh, head
+  // hq0 + (r & (2^psh - 1)).  Unpacked: psh = 0, hq0 = h.
+  const int psh = p.pack_shift;
+  const int hq0 = h << psh;
 
   const uint32_t q_rs = (uint32_t)p.heads_q * D * ESZ;   // bytes per Q/O token row
   const uint32_t kv_rs = (uint32_t)p.heads_k * D * ESZ;  // bytes per K/V token row
-  // Sample-bounded views: [q_off, q_off+q_len) rows of head h in Q and O,
-  // [k_off, k_off+k_len) rows of K/V head g.
-  const char* qbase = (const char*)p.q + (int64_t)q_off * q_rs + (int64_t)h * D * ESZ;
-  char* obase = (char*)p.o + (int64_t)q_off * q_rs + (int64_t)h * D * ESZ;
+  // Sample-bounded views: [q_off, q_off+q_len) rows from head hq0 on in Q
+  // and O, [k_off, k_off+k_len) rows of K/V head g.
+  const char* qbase = (const char*)p.q + (int64_t)q_off * q_rs + (int64_t)hq0 * D * ESZ;
+  char* obase = (char*)p.o + (int64_t)q_off * q_rs + (int64_t)hq0 * D * ESZ;
   const char* kbase = (const char*)p.k + (int64_t)k_off * kv_rs + (int64_t)g * D * ESZ;
   const char* vbase = (const char*)p.v + (int64_t)k_off * kv_rs + (int64_t)g * D * ESZ;
   const rsrc_t rq = make_rsrc(qbase, (uint32_t)q_len * q_rs);
@@ -785,14 +794,19 @@ void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // Sample-local Q row of this lane in each of the wavefront's blocks.
-  int qloc[QB];
+  // Sample-local Q token (qloc), head within the task (hs) and payload word
+  // row (prow) of this lane's tile row in each of the wavefront's blocks.
+  int qloc[QB], hs[QB], prow[QB];
   uint32_t q_row_off[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    qloc[qb] = m_block * TQ + 32 * (QB * wave + qb) + lq;
-    q_row_off[qb] = (uint32_t)qloc[qb] * q_rs;
+    const int r = 32 * (QB * wave + qb) + lq;
+    prow[qb] = r >> psh;
+    hs[qb] = r & ((1 << psh) - 1);
+    qloc[qb] = m_block * (TQ >> psh) + prow[qb];
+    q_row_off[qb] = (uint32_t)qloc[qb] * q_rs + (uint32_t)hs[qb] * D * ESZ;
   }
+  const int tq_plan = TQ >> psh;   // payload word rows per partial tile
 
   // tile t of the task: partial list first, then full list (§6.1)
   auto tile_j = [&](int t) {
@@ -806,8 +820,7 @@ void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (t < np) {
-        const uint32_t* src =
-            p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * (QB * wave + qb) + lq) * NKB;
+        const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * tq_plan + prow[qb]) * NKB;
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = src[kk];
       } else {
@@ -834,9 +847,14 @@ void attn_fwd_kernel(AttnParams p) {
   typename Ops::QFrag qf;
   Ops::load_q(qf, rq, q_row_off, b2);
 
-  float slope = 0.0f;
-  if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) slope = p.slopes[h] * kLog2e;
-  if constexpr (MOD == kModAlibiSoftcap) slope = p.slopes[h] * p.alibi_k;
+  float slope[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    slope[qb] = 0.0f;
+    if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi)
+      slope[qb] = p.slopes[hq0 + hs[qb]] * kLog2e;
+    if constexpr (MOD == kModAlibiSoftcap) slope[qb] = p.slopes[hq0 + hs[qb]] * p.alibi_k;
+  }
 
   f32x16 o[QB][D / 32];
   RowState rs[QB];
@@ -919,7 +937,7 @@ void attn_fwd_kernel(AttnParams p) {
     run(std::false_type{}, ntiles);
   }
 
-  write_rows<Ops, SPLIT>(p, c, ro, q_row_off, qloc, o, rs, b2);
+  write_rows<Ops, SPLIT>(p, c, ro, hq0, q_row_off, qloc, hs, o, rs, b2);
 }
 
 // Page-table remap of the plan's K-tile lists (FlexAttention page, paged

@@ -213,6 +213,10 @@ struct AttnParams {
   int32_t heads_q, heads_k, group, mask_heads, rows_total, total_q;
   int32_t force_partial;     // full tiles through the predicate path (ablation)
   int32_t no_skip;           // compute tiles and blocks whose weights are all exactly 0 (ablation)
+  // PackGQA: a task's tile row r is token r >> pack_shift of its plan row and
+  // Q head (task head) * 2^pack_shift + (r & (2^pack_shift - 1)); 0 = unpacked
+  // (the task head is then the Q head).
+  int32_t pack_shift;
   float scale_log2;         // scale * log2(e)
   float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
   float softcap_c2;         // c * log2(e)

@@ -146,7 +146,8 @@ def test_fwd_refuses_null_plan_and_workspace_size(lib):
 
 
 class BuildOptions(ctypes.Structure):
-    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32)]
+    _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32),
+                ("pack_gqa", ctypes.c_int32)]
 
 
 def test_build_options_and_k2q_export_refusals(lib):
@@ -155,7 +156,8 @@ def test_build_options_and_k2q_export_refusals(lib):
         [ctypes.c_void_p] * 4 + [ctypes.POINTER(ctypes.c_void_p)]
     out = ctypes.c_void_p(12345)
     prob = _good()
-    for opt in (BuildOptions(2, 0), BuildOptions(0, -1)):
+    for opt in (BuildOptions(2, 0), BuildOptions(0, -1), BuildOptions(0, 0, 3),
+                BuildOptions(0, 0, -1)):
         out = ctypes.c_void_p(12345)
         st = lib.mask_plan_build_ex(ctypes.byref(prob), ctypes.byref(opt),
                                     ctypes.c_void_p(1), None, None, None, ctypes.byref(out))
@@ -171,6 +173,28 @@ def test_build_options_and_k2q_export_refusals(lib):
     lib.mask_plan_stage_times.restype = ctypes.c_int
     lib.mask_plan_stage_times.argtypes = [ctypes.c_void_p] * 2
     assert lib.mask_plan_stage_times(None, None) == INVALID
+
+
+@pytest.mark.parametrize("kw,bwd", [
+    (dict(), 0),                                     # heads_q == heads_k: nothing to pack
+    (dict(heads_q=8, heads_k=2, mask_heads=8), 0),   # per-head masks differ inside a group
+    (dict(heads_q=6, heads_k=2), 0),                 # group of 3: not a power of two
+    (dict(heads_q=32, heads_k=2, tile_q=128), 0),    # 128 / 16 = 8 tokens per plan row
+    (dict(heads_q=8, heads_k=2), 1),                 # no backward view over packed tiles
+])
+def test_pack_gqa_refusals(lib, kw, bwd):
+    """PackGQA forced on (pack_gqa = 2) where it cannot run is refused on the
+    host, before any launch, with the rule named."""
+    lib.mask_plan_build_ex.restype = ctypes.c_int
+    lib.mask_plan_build_ex.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(BuildOptions)] + \
+        [ctypes.c_void_p] * 4 + [ctypes.POINTER(ctypes.c_void_p)]
+    prob = _good(tile_k=64, **kw)
+    out = ctypes.c_void_p(12345)
+    st = lib.mask_plan_build_ex(ctypes.byref(prob), ctypes.byref(BuildOptions(bwd, 0, 2)),
+                                ctypes.c_void_p(1), None, None, None, ctypes.byref(out))
+    assert st == UNSUPPORTED and out.value is None
+    lib.mpb_last_error_detail.restype = ctypes.c_char_p
+    assert b"PackGQA" in lib.mpb_last_error_detail()
 
 
 def test_splitk_and_merge_host_refusals(lib):

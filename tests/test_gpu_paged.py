@@ -93,13 +93,14 @@ def test_paged_equals_contiguous_and_oracle(name, pages_per_tile):
     G.compare_attention(w, O, L, G.flat_o(w, o), lse.cpu().numpy().astype(np.float64), name)
 
 
+@pytest.mark.parametrize("pack", [None, False])   # the library's choice (packed), unpacked
 @pytest.mark.parametrize("tq,tk", [(64, 64), (128, 32), (64, 32)])
-def test_paged_other_tiles_and_splitk(tq, tk):
+def test_paged_other_tiles_and_splitk(tq, tk, pack):
     w = W.make("chunk_long_kv", small=True)
     d = G.device_inputs(w)
-    plan = G.build_plan(w, d, tq, tk)
+    plan = G.build_plan(w, d, tq, tk, pack_gqa=pack)
     ps = 2 * tk
-    _case("paged_tiles_split", tq=tq, tk=tk)
+    _case("paged_tiles_split", tq=tq, tk=tk, pack=pack)
     pool = make_pool(w, ps, seed=7)
     for sp in (1, 3):
         o, lse = run_paged(w, d, plan, pool, ps, num_splits=sp)

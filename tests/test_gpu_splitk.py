@@ -50,12 +50,13 @@ def test_splitk_small_all_rows(name, num_splits):
                         "%s S=%d" % (name, num_splits))
 
 
+@pytest.mark.parametrize("pack", [None, False])   # the library's choice (packed), unpacked
 @pytest.mark.parametrize("tq,tk", [(64, 64), (128, 32), (64, 32)])
-def test_splitk_other_tiles(tq, tk):
+def test_splitk_other_tiles(tq, tk, pack):
     w = W.make("chunk_long_kv", small=True)
-    _case("splitk_tiles", tq=tq, tk=tk)
+    _case("splitk_tiles", tq=tq, tk=tk, pack=pack)
     d = G.device_inputs(w)
-    plan = G.build_plan(w, d, tq, tk)
+    plan = G.build_plan(w, d, tq, tk, pack_gqa=pack)
     o, lse = _run_split(w, d, plan, 5)
     torch.cuda.synchronize()
     O, L = oracle.attention(w)

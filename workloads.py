@@ -201,14 +201,15 @@ def tiny_causal(seed=0, batch=1, heads=2, seqlen=256, head_dim=64,
 
 
 def window_sink(seed=0, batch=2, heads=16, seqlen=2048, head_dim=128, sink=64, window=256,
-                dtype=DTYPE_BF16, with_values=True) -> Workload:
+                dtype=DTYPE_BF16, with_values=True, heads_k=None) -> Workload:
+    heads_k = heads if heads_k is None else heads_k
     rng = np.random.Generator(np.random.PCG64(seed))
     ql = np.arange(seqlen, dtype=np.int64)
     mf = _tile_bsh(window_sink_endpoints(ql, sink, window), batch)[None]
     total = batch * seqlen
-    q, k, v = _draw_qkv(rng, total, total, heads, heads, head_dim, dtype, with_values)
+    q, k, v = _draw_qkv(rng, total, total, heads, heads_k, head_dim, dtype, with_values)
     return Workload("window_sink", LAYOUT_BSHD, dtype, batch, seqlen, seqlen, total, total,
-                    heads, heads, head_dim, 1, 3, np.ascontiguousarray(mf), None, None,
+                    heads, heads_k, head_dim, 1, 3, np.ascontiguousarray(mf), None, None,
                     q, k, v, 1.0 / math.sqrt(head_dim), seed=seed,
                     extra={"sink": sink, "window": window})
 
@@ -220,7 +221,8 @@ def varlen_lengths(rng, total: int, nseq: int, min_len: int) -> np.ndarray:
 
 
 def varlen_doc(seed=0, total=16384, nseq=8, min_len=256, heads=16, head_dim=128,
-               dtype=DTYPE_BF16, with_values=True, lengths=None) -> Workload:
+               dtype=DTYPE_BF16, with_values=True, lengths=None, heads_k=None) -> Workload:
+    heads_k = heads if heads_k is None else heads_k
     rng = np.random.Generator(np.random.PCG64(seed))
     lens = np.asarray(lengths, dtype=np.int64) if lengths is not None else \
         varlen_lengths(rng, total, nseq, min_len)
@@ -233,9 +235,9 @@ def varlen_doc(seed=0, total=16384, nseq=8, min_len=256, heads=16, head_dim=128,
         ql = np.arange(int(lens[b]), dtype=np.int64)
         mf[0, :, cu[b]:cu[b + 1]] = causal_endpoints(ql)
     maxlen = int(lens.max()) if nseq else 0
-    q, k, v = _draw_qkv(rng, total, total, heads, heads, head_dim, dtype, with_values)
+    q, k, v = _draw_qkv(rng, total, total, heads, heads_k, head_dim, dtype, with_values)
     return Workload("varlen_doc", LAYOUT_THD, dtype, nseq, maxlen, maxlen, total, total,
-                    heads, heads, head_dim, 1, 1, mf, cu, cu.copy(), q, k, v,
+                    heads, heads_k, head_dim, 1, 1, mf, cu, cu.copy(), q, k, v,
                     1.0 / math.sqrt(head_dim), seed=seed, extra={"lengths": lens.tolist()})
 
 
@@ -259,14 +261,15 @@ def block_sparse(seed=0, batch=1, heads=24, seqlen=8190, head_dim=128, block_q=9
 
 
 def prefix_softcap(seed=0, batch=4, heads=32, seqlen=4096, head_dim=128, prefix=1024,
-                   softcap=30.0, dtype=DTYPE_BF16, with_values=True) -> Workload:
+                   softcap=30.0, dtype=DTYPE_BF16, with_values=True, heads_k=None) -> Workload:
+    heads_k = heads if heads_k is None else heads_k
     rng = np.random.Generator(np.random.PCG64(seed))
     ql = np.arange(seqlen, dtype=np.int64)
     mf = _tile_bsh(prefix_lm_endpoints(ql, prefix, seqlen), batch)[None]
     total = batch * seqlen
-    q, k, v = _draw_qkv(rng, total, total, heads, heads, head_dim, dtype, with_values)
+    q, k, v = _draw_qkv(rng, total, total, heads, heads_k, head_dim, dtype, with_values)
     return Workload("prefix_softcap", LAYOUT_BSHD, dtype, batch, seqlen, seqlen, total, total,
-                    heads, heads, head_dim, 1, 1, np.ascontiguousarray(mf), None, None,
+                    heads, heads_k, head_dim, 1, 1, np.ascontiguousarray(mf), None, None,
                     q, k, v, 1.0 / math.sqrt(head_dim), softcap=softcap,
                     alibi_slopes=alibi_slopes(heads), seed=seed, extra={"prefix": prefix})
 
