@@ -650,6 +650,10 @@ def main():
     ap.add_argument("--splitk-iters", type=int, default=20,
                     help="back-to-back launches per Split-K configuration timed on the long-K "
                          "chunk shape (0 = skip)")
+    ap.add_argument("--sync-build", action="store_true",
+                    help="time the step with the header read back inside mask_plan_build "
+                         "(default: defer_header, the build returns once its launches are "
+                         "enqueued)")
     ap.add_argument("--packgqa-iters", type=int, default=20,
                     help="back-to-back forwards per plan in the PackGQA leg (0 = skip)")
     ap.add_argument("--no-paged", action="store_true",
@@ -704,8 +708,14 @@ def main():
             p0, args.num_splits), 256), dtype=torch.uint8, device="cuda")
         p0.close()
 
+    defer = not args.sync_build
+
+    def build(deferred=defer):
+        return mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream,
+                                   defer_header=deferred)
+
     def step():
-        plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        plan = build()
         mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
         return plan
 
@@ -723,25 +733,49 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ta = time.perf_counter()
-        plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        plan = build()
         tb = time.perf_counter()
         mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
         tc = time.perf_counter()
         host_build += tb - ta
         host_fwd += tc - tb
-        keep.append(plan)          # released once no longer in flight
+        keep.append(plan)          # released in stream order once no longer needed
         if len(keep) > 2:
             keep.pop(0).close()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_s = (t1 - t0) / args.steps
+    # a deferred plan's GPU checks are read here, after the timed region: the
+    # last step's plan must have passed them and its forward's output must be
+    # the one a plan built with the header read-back gives
+    if defer:
+        assert keep[-1].info.build_mode == mpb.BUILD_SINGLE_PASS_DEFERRED
+        o_def, l_def = out.clone(), lse.clone()
+        p_chk = build(False)
+        mpb.flex_attn_fwd(p_chk, d["q"], d["k"], d["v"], **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, o_def) and torch.equal(lse, l_def), "deferred != read-back"
+        p_chk.close()
+
+    # the same steps with the header read back inside the build (the host
+    # waits for it before it enqueues the forward)
+    torch.cuda.synchronize()
+    t0s = time.perf_counter()
+    for i in range(args.steps):
+        plan = build(False)
+        mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
+        keep.append(plan)
+        if len(keep) > 2:
+            keep.pop(0).close()
+    torch.cuda.synchronize()
+    step_sync_s = (time.perf_counter() - t0s) / args.steps
 
     # the same steps again, each forward bracketed by HIP events (the event
     # markers perturb the step, so this loop is not the timed one)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     for i in range(args.steps):
-        plan = mpb.mask_plan_build(prob, d["mask_func"], d["cu_q"], d["cu_k"], stream=stream)
+        plan = build()
         ev[i][0].record(stream)
         mpb.flex_attn_fwd(plan, d["q"], d["k"], d["v"], **kw)
         ev[i][1].record(stream)
@@ -930,6 +964,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step_header_read_back": round(step_sync_s * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -938,7 +973,11 @@ def main():
         "config": {"workload": args.workload, "batch": w.batch, "heads_q": w.heads_q,
                    "heads_k": w.heads_k, "seqlen_q": w.seqlen_q, "seqlen_k": w.seqlen_k,
                    "head_dim": w.head_dim, "mask_heads": w.mask_heads, "nfunc": w.nfunc,
-                   "tile": "%dx%d" % (tq, tk), "step": "mask_plan_build + flex_attn_fwd"},
+                   "tile": "%dx%d" % (tq, tk),
+                   "step": "mask_plan_build (%s) + flex_attn_fwd"
+                           % ("header read back in the build" if not defer
+                              else "defer_header: the first header read follows the timed "
+                                   "steps")},
         "roofline": dict(roof, traffic=traffic, kernel="attn_fwd_kernel",
                          algorithmic_bytes=attn_bytes(w, plan),
                          achieved_basis="algorithmic bytes (hbm) or effective flops (mfma) per "

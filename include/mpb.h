@@ -122,7 +122,12 @@ typedef struct mpb_plan_info {
                             * endpoints, block cut to its exact size after the header) */
   int32_t reserved;
 } mpb_plan_info;
-enum { MPB_BUILD_EXACT = 0, MPB_BUILD_IN_PLACE = 1, MPB_BUILD_SINGLE_PASS = 2 };
+enum {
+  MPB_BUILD_EXACT = 0,
+  MPB_BUILD_IN_PLACE = 1,
+  MPB_BUILD_SINGLE_PASS = 2,
+  MPB_BUILD_SINGLE_PASS_DEFERRED = 3   /* single pass, header read lazily (defer_header) */
+};
 
 /* score_mod of [FLEX] Eq. 1, applied to t = scale * (q . k):
  *   softcap:  t <- softcap * tanh(t / softcap)
@@ -198,7 +203,11 @@ mpb_status mask_plan_build(const mpb_problem* problem, const int32_t* mask_func,
  * call (e.g. synchronise them).  NULL is accepted. */
 mpb_status mask_plan_destroy(mpb_plan* plan);
 
-/* Header, geometry and signature of a plan (host struct, no device access). */
+/* Header, geometry and signature of a plan (host struct).  No device access,
+ * except for a plan built with defer_header whose header has not been read
+ * yet: the call then waits for the build stream, reads the header and returns
+ * the build's error (MPB_ERR_SEQLENS, MPB_ERR_ENDPOINT_RANGE, ...) if the
+ * GPU checks failed, else fills *info. */
 mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info);
 
 /* Copies plan arrays to host memory [MPD §8 debug_snapshot]; any pointer may
@@ -255,6 +264,20 @@ typedef struct {
                             * these unmet is MPB_ERR_UNSUPPORTED.  The library packs
                             * whenever it may (measured faster on every shape tried:
                             * short query chunks most, by filling the tile's rows). */
+  int32_t defer_header;    /* 0 or 1.  1: a single-pass build returns as soon as its
+                            * launches are enqueued, without the header read-back
+                            * (other builds ignore the flag and read it back as usual).
+                            * The block keeps its upper-bound layout (the lists are
+                            * written into it directly; nothing is cut off), and the
+                            * endpoint / prefix checks done on the GPU are reported by
+                            * the first call that reads the header: mask_plan_info, the
+                            * exports, flex_attn_fwd_num_splits and the Split-K and
+                            * paged forwards read it (waiting for the build stream) and
+                            * return the build's error if it failed.  flex_attn_fwd and
+                            * flex_attn_fwd_ablation do not wait: they launch the upper
+                            * bound of workgroups, which read the task count and the
+                            * error word on the device; on a plan that failed its checks
+                            * they write nothing (O and LSE keep their contents). */
 } mpb_build_options;
 
 /* mask_plan_build with options; same arguments, errors and lifetime rules. */

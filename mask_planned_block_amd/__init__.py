@@ -31,7 +31,7 @@ LAYOUT_BSHD = 0
 LAYOUT_THD = 1
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
-BUILD_EXACT, BUILD_IN_PLACE, BUILD_SINGLE_PASS = 0, 1, 2   # PlanInfo.build_mode
+BUILD_EXACT, BUILD_IN_PLACE, BUILD_SINGLE_PASS, BUILD_SINGLE_PASS_DEFERRED = 0, 1, 2, 3   # PlanInfo.build_mode
 NUM_QUEUES = 9
 TASK_REC_INTS = 16
 TASK_REC_FIELDS = ("m_block", "head", "batch", "q_valid_rows", "q_offset", "k_offset", "q_len",
@@ -80,7 +80,7 @@ class PlanInfo(ctypes.Structure):
 
 class BuildOptions(ctypes.Structure):
     _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32),
-                ("pack_gqa", ctypes.c_int32)]
+                ("pack_gqa", ctypes.c_int32), ("defer_header", ctypes.c_int32)]
 
 
 class ScoreMod(ctypes.Structure):
@@ -251,19 +251,21 @@ def mask_plan_build(problem: Problem, mask_func: torch.Tensor,
                     cu_seqlens_q: Optional[torch.Tensor] = None,
                     cu_seqlens_k: Optional[torch.Tensor] = None, stream=None,
                     build_backward: bool = False, time_stages: bool = False,
-                    pack_gqa: Optional[bool] = None) -> MaskPlan:
+                    pack_gqa: Optional[bool] = None, defer_header: bool = False) -> MaskPlan:
     """Builds a MaskPlan on the GPU (one header read-back; see include/mpb.h);
     build_backward adds the K2Q view, time_stages records HIP events around the
     planner launches, pack_gqa forces PackGQA on (True) or off (False), None
-    leaves it to the library (all through mask_plan_build_ex)."""
+    leaves it to the library, defer_header returns without the header
+    read-back (the first call that needs the header reads it and reports the
+    build's errors) (all through mask_plan_build_ex)."""
     mf = _dev_ptr(mask_func, "mask_func", torch.int32)
     cq = _dev_ptr(cu_seqlens_q, "cu_seqlens_q", torch.int32)
     ck = _dev_ptr(cu_seqlens_k, "cu_seqlens_k", torch.int32)
     s = _stream_handle(stream)
     out = ctypes.c_void_p()
     pack = 0 if pack_gqa is None else (2 if pack_gqa else 1)
-    if build_backward or time_stages or pack:
-        opt = BuildOptions(int(build_backward), int(time_stages), pack)
+    if build_backward or time_stages or pack or defer_header:
+        opt = BuildOptions(int(build_backward), int(time_stages), pack, int(defer_header))
         _check(_lib.mask_plan_build_ex(ctypes.byref(problem), ctypes.byref(opt), mf, cq, ck, s,
                                        ctypes.byref(out)))
     else:

@@ -613,6 +613,12 @@ __device__ inline bool read_task(const AttnParams& p, TaskCtx& c) {
     c.split = blockIdx.x / p.tasks_padded;
     task = blockIdx.x - c.split * p.tasks_padded;
     if (task >= p.num_tasks) return false;   // padding of the last task row (whole workgroup)
+  } else {
+    if (p.dev_header) {   // deferred header: the plan's task count is on the device
+      const int rows = __builtin_amdgcn_readfirstlane(p.dev_header[0]);
+      const int err = __builtin_amdgcn_readfirstlane(p.dev_header[7]);
+      if (err != 0 || task >= rows * p.task_heads) return false;
+    }
   }
   const int32_t* rec = p.task_rec + (int64_t)task * kTaskRecInts;
   c.m_block = __builtin_amdgcn_readfirstlane(rec[kRecMBlock]);

@@ -171,8 +171,11 @@ constexpr uint32_t kDevErrLookback = 1u << 8;
 hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, const PlanDev& d,
                                    const PlanWork& w, const SinglePass& sp, int32_t rows_total,
                                    hipStream_t s);
+// place_lists: copy the lists from the workspace behind the payload (exact
+// layout); false when the single pass wrote them into the block itself.
 hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
-                                        const SinglePass& sp, int64_t tiles_upper, hipStream_t s);
+                                        const SinglePass& sp, int64_t tiles_upper,
+                                        bool place_lists, hipStream_t s);
 
 // Backward K2Q view (same tile geometry as the forward plan): count from the
 // classifier's bitsets, then (last workgroup) offsets and header values 3..6
@@ -217,6 +220,12 @@ struct AttnParams {
   // Q head (task head) * 2^pack_shift + (r & (2^pack_shift - 1)); 0 = unpacked
   // (the task head is then the Q head).
   int32_t pack_shift;
+  // A plan whose header the host has not read (deferred build): the launch
+  // covers the upper bound of tasks and workgroup i runs only while
+  // i < dev_header[0] * task_heads and dev_header[7] (device error bits) is
+  // 0.  nullptr: the launch covers exactly the plan's tasks.
+  const int32_t* dev_header;
+  int32_t task_heads;
   float scale_log2;         // scale * log2(e)
   float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
   float softcap_c2;         // c * log2(e)

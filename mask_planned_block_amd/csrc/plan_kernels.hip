@@ -1834,7 +1834,8 @@ void plan_single_pass_kernel(PlanGeo g,
 __global__ __launch_bounds__(1024) void plan_single_pass_tail_kernel(PlanGeo g, PlanDev d,
                                                                      PlanWork w, SinglePass sp,
                                                                      int cnt_in_lds,
-                                                                     int rows_in_lds) {
+                                                                     int rows_in_lds,
+                                                                     int place_lists) {
   extern __shared__ int dyn[];
   // With the sort in LDS every workgroup sorts and writes its share of the
   // tasks (after its share of the lists); else workgroup 0 alone schedules.
@@ -1844,6 +1845,10 @@ __global__ __launch_bounds__(1024) void plan_single_pass_tail_kernel(PlanGeo g, 
     return;
   }
   if (d.header[7] != 0) return;   // failed build: nothing to place
+  if (!place_lists) {   // the lists are in place already: schedule only
+    schedule_any(g, d, w, cnt_in_lds, rows_in_lds, dyn, blockIdx.x, gridDim.x);
+    return;
+  }
   const int64_t pn = d.header[1], fn = d.header[2];
   auto padded = [](int64_t bytes) -> int64_t { return (bytes + 255) & ~(int64_t)255; };
   const int64_t mask_words = pn * g.tile_q * g.words_tile;
@@ -2445,7 +2450,7 @@ hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, c
 
 hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, const PlanWork& w,
                                         const SinglePass& sp, int64_t tiles_upper,
-                                        hipStream_t s) {
+                                        bool place_lists, hipStream_t s) {
   const int64_t rows = (int64_t)g.mask_heads * g.upper_rows;
   const size_t cnt_bytes = w.chunk_cnt ? 0 : (size_t)(g.nk_max + 1) * w.nchunks * 4;
   const int rows_in_lds = sched_rows_in_lds(rows, cnt_bytes);
@@ -2454,11 +2459,16 @@ hipError_t launch_plan_single_pass_tail(const PlanGeo& g, const PlanDev& d, cons
   // list placement (four indices per thread) and, with the sort in LDS,
   // tasks (one per thread): up to 256 more workgroups of 1024 threads
   const int64_t tasks = (int64_t)g.upper_rows * g.heads_q;
-  int64_t copy_wgs = (2 * tiles_upper + 4095) / 4096;
-  if (!w.chunk_cnt && rows_in_lds == 2) copy_wgs = std::max(copy_wgs, (tasks + 1023) / 1024 - 1);
-  copy_wgs = copy_wgs < 1 ? 1 : (copy_wgs > 256 ? 256 : copy_wgs);
+  const bool shared_sort = !w.chunk_cnt && rows_in_lds == 2;
+  int64_t copy_wgs = place_lists ? (2 * tiles_upper + 4095) / 4096 : 0;
+  if (shared_sort) copy_wgs = std::max(copy_wgs, (tasks + 1023) / 1024 - 1);
+  copy_wgs = copy_wgs < (place_lists ? 1 : 0) ? 1 : (copy_wgs > 256 ? 256 : copy_wgs);
+  // without list placement and without the shared sort, workgroup 0 alone
+  // schedules (the kernel then returns from every other workgroup at once)
+  if (!place_lists && !shared_sort) copy_wgs = 0;
   hipLaunchKernelGGL(plan_single_pass_tail_kernel, dim3((unsigned)(1 + copy_wgs)), dim3(1024),
-                     cnt_bytes + row_bytes, s, g, d, w, sp, w.chunk_cnt ? 0 : 1, rows_in_lds);
+                     cnt_bytes + row_bytes, s, g, d, w, sp, w.chunk_cnt ? 0 : 1, rows_in_lds,
+                     place_lists ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -92,6 +92,19 @@ struct mpb_plan {
   StageEvents tev;         // build stage events (time_stages)
   int build_mode;          // kBuildExact, kBuildInPlace or kBuildSinglePass
   int32_t pack;            // PackGQA: Q heads per plan row (1 = unpacked)
+  // Deferred header (mpb_build_options.defer_header): the build returned
+  // without reading the header back.  Until the first call that needs it
+  // reads it from the plan block (resolve_header), header, rows_total and
+  // num_tasks are unknown, the block keeps its upper-bound layout and a
+  // forward covers tasks_upper workgroups that read the task count on the
+  // device.
+  std::atomic<bool> pending{false};
+  std::mutex resolve_mu;
+  mpb_status resolve_status = MPB_OK;
+  std::string resolve_detail;
+  int64_t rows_upper = 0;
+  int64_t tiles_upper = 0;
+  int32_t tasks_upper = 0;
 };
 
 namespace {
@@ -484,7 +497,8 @@ constexpr size_t kSinglePassBytes = (size_t)2 << 30;
 enum BuildMode {
   kBuildExact = MPB_BUILD_EXACT,
   kBuildInPlace = MPB_BUILD_IN_PLACE,
-  kBuildSinglePass = MPB_BUILD_SINGLE_PASS
+  kBuildSinglePass = MPB_BUILD_SINGLE_PASS,
+  kBuildSinglePassDeferred = MPB_BUILD_SINGLE_PASS_DEFERRED
 };
 
 int device_cus(int dev) {
@@ -579,6 +593,30 @@ const char* pack_gqa_refusal(const mpb_problem& p, int tq, bool backward) {
 // 165, prefix-LM + softcap + ALiBi 749 against 708.
 bool pack_gqa_default(const mpb_problem&, int) { return true; }
 
+// §4.5: what a planner header says about the build: the device error bits
+// (first set of: look-back time-out, prefixes, endpoint range, endpoint
+// order) or counts outside their upper bounds.
+mpb_status header_status(const int64_t (&header)[8], int64_t rows_upper, int64_t tiles_upper) {
+  const uint32_t err = (uint32_t)header[7];
+  if (err) {
+    if (err & kDevErrLookback)
+      return fail(MPB_ERR_DEVICE, "a single-pass planner workgroup waited too long for the "
+                                  "offsets of the rows before it");
+    if (err & MPB_DEVERR_SEQLENS)
+      return fail(MPB_ERR_SEQLENS,
+                  "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
+                  "respect max_seqlen");
+    if (err & MPB_DEVERR_RANGE)
+      return fail(MPB_ERR_ENDPOINT_RANGE, "an endpoint is < 0 or > its sample's k_len");
+    return fail(MPB_ERR_ENDPOINT_ORDER, "endpoints of some row are not nondecreasing");
+  }
+  const int64_t rows_total = header[0], pnnz = header[1], fnnz = header[2];
+  if (rows_total < 0 || rows_total > rows_upper || pnnz < 0 || fnnz < 0 ||
+      pnnz > tiles_upper || fnnz > tiles_upper)
+    return fail(MPB_ERR_DEVICE, "inconsistent plan header");
+  return MPB_OK;
+}
+
 // §4.1: structural validation only (no element is read on the host).
 mpb_status validate_problem(const mpb_problem* p, int* tq_out, int* tk_out,
                             bool backward = false) {
@@ -636,6 +674,46 @@ mpb_status device_status(hipError_t e, const char* what) {
   return fail(MPB_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// The header of a deferred plan, read from its block by the first call that
+// needs it (after the build stream has drained); the outcome, the counts or
+// the build's error, is kept and returned to every later call.  A plan built
+// with its header read back returns MPB_OK at once.
+mpb_status resolve_header(const mpb_plan* cplan) {
+  mpb_plan* plan = const_cast<mpb_plan*>(cplan);
+  if (plan->pending.load(std::memory_order_acquire)) {
+    std::lock_guard<std::mutex> lk(plan->resolve_mu);
+    if (plan->pending.load(std::memory_order_relaxed)) {
+      int cur = 0;
+      hipGetDevice(&cur);
+      if (cur != plan->device) hipSetDevice(plan->device);
+      int32_t h32[8] = {};
+      hipError_t e = hipStreamSynchronize(plan->stream);
+      if (e == hipSuccess)
+        e = hipMemcpy(h32, plan->dev.header, sizeof(h32), hipMemcpyDeviceToHost);
+      if (cur != plan->device) hipSetDevice(cur);
+      mpb_status st;
+      if (e != hipSuccess) {
+        st = device_status(e, "deferred header read-back");
+      } else {
+        int64_t header[8];
+        for (int i = 0; i < 8; ++i) header[i] = (i >= 3 && i < 7) ? 0 : h32[i];
+        st = header_status(header, plan->rows_upper, plan->tiles_upper);
+        if (st == MPB_OK) {
+          for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
+          plan->rows_total = (int32_t)header[0];
+          plan->num_tasks = (int32_t)(header[0] * (plan->prob.heads_q / plan->pack));
+        }
+      }
+      plan->resolve_status = st;
+      plan->resolve_detail = st == MPB_OK ? std::string() : g_detail;
+      plan->pending.store(false, std::memory_order_release);
+    }
+  }
+  if (plan->resolve_status != MPB_OK)
+    return fail(plan->resolve_status, "%s", plan->resolve_detail.c_str());
+  return MPB_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -680,6 +758,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const int pack_opt = options ? options->pack_gqa : 0;
   if (pack_opt < 0 || pack_opt > 2)
     return fail(MPB_ERR_INVALID_ARGUMENT, "pack_gqa must be 0 (library's choice), 1 or 2");
+  if (options && options->defer_header != 0 && options->defer_header != 1)
+    return fail(MPB_ERR_INVALID_ARGUMENT, "defer_header must be 0 or 1");
   int tq = 0, tk = 0;
   mpb_status st = validate_problem(problem, &tq, &tk, bwd);
   if (st != MPB_OK) return st;
@@ -755,6 +835,9 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   const BlockLayout L_sp = block_layout(p, tq, tk, upper, tiles_upper, tiles_upper, K2QCounts(),
                                         true);
   const bool single = !bwd && L_sp.bytes + (size_t)tiles_upper * 8 <= kSinglePassBytes;
+  // Deferred header: single-pass builds only; the single pass then writes the
+  // lists straight into the block (upper-bound layout, kept as it is).
+  const bool defer = single && options && options->defer_header;
   Carver cw;
   const size_t o_vis = cw.take<uint32_t>(items_upper * words_k);
   const size_t o_full = cw.take<uint32_t>(items_upper * words_k);
@@ -880,8 +963,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     sp.ticket = slot->arrive[dev] + 32;
     sp.host_slot = slot->pinned_dev;
     sp.seq = (int32_t)seq;
-    sp.p_list = at<int32_t>(wb, o_plist);
-    sp.f_list = at<int32_t>(wb, o_flist);
+    sp.p_list = defer ? d.p_idx : at<int32_t>(wb, o_plist);
+    sp.f_list = defer ? d.f_idx : at<int32_t>(wb, o_flist);
     // endpoints staged in LDS when [nfunc + 6][T_Q] takes at most 48 KiB:
     // as int32 loaded straight into LDS (whole wavefronts of rows, 32-bit
     // offsets) while that takes at most 16 KiB, else as int16 when the
@@ -903,7 +986,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
            return launch_plan_single_pass(g, mask_func, d, w, sp, thd ? -1 : (int32_t)upper, s);
          })) != hipSuccess ||
         (e = tev.timed(2, s, [&] {
-           return launch_plan_single_pass_tail(g, d, ws, sp, tiles_upper, s);
+           return launch_plan_single_pass_tail(g, d, ws, sp, tiles_upper, !defer, s);
          })) != hipSuccess) {
       heap->release(blk_chunk, blk_off, blk_bytes, s);
       return device_status(e, "planner launch");
@@ -950,6 +1033,46 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   auto drop_block = [&]() {
     if (block) heap->release(blk_chunk, blk_off, blk_bytes, s);
   };
+  auto new_plan = [&]() -> mpb_plan* {
+    mpb_plan* plan = new (std::nothrow) mpb_plan;
+    if (!plan) return nullptr;
+    plan->device = dev;
+    plan->prob = *problem;
+    plan->prob.tile_q = tq_tile;
+    plan->prob.tile_k = tk;
+    plan->sig = consumer_signature(*problem, tq_tile, tk, pack);
+    plan->pack = pack;
+    plan->geo = g;
+    plan->dev = d;
+    plan->kdev = kd;
+    plan->has_k2q = bwd;
+    plan->block = block;
+    plan->bytes = blk_bytes;
+    plan->blk_chunk = blk_chunk;
+    plan->blk_off = blk_off;
+    plan->stream = s;
+    plan->tev = tev;
+    plan->rows_upper = upper;
+    plan->tiles_upper = tiles_upper;
+    plan->tasks_upper = (int32_t)tasks_upper;
+    plan->build_mode = single ? kBuildSinglePass : in_place ? kBuildInPlace : kBuildExact;
+    return plan;
+  };
+  if (defer) {
+    mpb_plan* plan = new_plan();
+    if (!plan) {
+      drop_block();
+      return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
+    }
+    plan->rows_total = 0;
+    plan->num_tasks = 0;
+    for (int i = 0; i < 8; ++i) plan->header[i] = 0;
+    plan->build_mode = kBuildSinglePassDeferred;
+    plan->pending.store(true, std::memory_order_release);
+    tev_guard.t = nullptr;   // the plan owns the events now
+    *out = plan;
+    return ok();
+  }
   // §4.5: the single header read-back of the build.
   bool published = false;
   if ((e = wait_header(slot, s, seq, &published)) != hipSuccess) {
@@ -974,26 +1097,11 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   for (int i = 0; i < 8; ++i) header[i] = ((volatile int32_t*)slot->pinned)[i];
   if (!bwd)
     for (int i = 3; i < 7; ++i) header[i] = 0;
-  const uint32_t err = (uint32_t)header[7];
-  if (err) {
+  if ((st = header_status(header, upper, tiles_upper)) != MPB_OK) {
     drop_block();
-    if (err & kDevErrLookback)
-      return fail(MPB_ERR_DEVICE, "a single-pass planner workgroup waited too long for the "
-                                  "offsets of the rows before it");
-    if (err & MPB_DEVERR_SEQLENS)
-      return fail(MPB_ERR_SEQLENS,
-                  "cu_seqlens must start at 0, end at total_q/total_k, be nondecreasing and "
-                  "respect max_seqlen");
-    if (err & MPB_DEVERR_RANGE)
-      return fail(MPB_ERR_ENDPOINT_RANGE, "an endpoint is < 0 or > its sample's k_len");
-    return fail(MPB_ERR_ENDPOINT_ORDER, "endpoints of some row are not nondecreasing");
+    return st;
   }
   const int64_t rows_total = header[0], pnnz = header[1], fnnz = header[2];
-  if (rows_total < 0 || rows_total > upper || pnnz < 0 || fnnz < 0 || pnnz > tiles_upper ||
-      fnnz > tiles_upper) {
-    drop_block();
-    return fail(MPB_ERR_DEVICE, "inconsistent plan header");
-  }
   const int64_t tasks = rows_total * p.heads_q;
   K2QCounts kc;
   kc.on = bwd;
@@ -1044,31 +1152,14 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     }
   }
 
-  mpb_plan* plan = new (std::nothrow) mpb_plan;
+  mpb_plan* plan = new_plan();
   if (!plan) {
     drop_block();
     return fail(MPB_ERR_OUT_OF_MEMORY, "host allocation of the plan");
   }
-  plan->device = dev;
-  plan->prob = *problem;
-  plan->prob.tile_q = tq_tile;
-  plan->prob.tile_k = tk;
-  plan->sig = consumer_signature(*problem, tq_tile, tk, pack);
-  plan->pack = pack;
-  plan->geo = g;
-  plan->dev = d;
-  plan->kdev = kd;
-  plan->has_k2q = bwd;
   plan->rows_total = (int32_t)rows_total;
   plan->num_tasks = (int32_t)tasks;
   for (int i = 0; i < 8; ++i) plan->header[i] = header[i];
-  plan->block = block;
-  plan->bytes = blk_bytes;
-  plan->blk_chunk = blk_chunk;
-  plan->blk_off = blk_off;
-  plan->stream = s;
-  plan->tev = tev;
-  plan->build_mode = single ? kBuildSinglePass : in_place ? kBuildInPlace : kBuildExact;
   tev_guard.t = nullptr;   // the plan owns the events now
   *out = plan;
   return ok();
@@ -1089,6 +1180,8 @@ mpb_status mask_plan_destroy(mpb_plan* plan) {
 
 mpb_status mask_plan_info(const mpb_plan* plan, mpb_plan_info* info) {
   if (!plan || !info) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or info is NULL");
+  const mpb_status rs = resolve_header(plan);
+  if (rs != MPB_OK) return rs;
   for (int i = 0; i < 8; ++i) info->header[i] = plan->header[i];
   info->rows_total = plan->rows_total;
   info->nk_max = plan->geo.nk_max;
@@ -1108,6 +1201,8 @@ mpb_status mask_plan_export(const mpb_plan* plan, int32_t* cu_rows, int32_t* seq
                             int32_t* p_off, int32_t* p_idx, uint32_t* p_masks, int32_t* f_off,
                             int32_t* f_idx, int32_t* work_desc, int32_t* section_off) {
   if (!plan) return fail(MPB_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const mpb_status rs = resolve_header(plan);
+  if (rs != MPB_OK) return rs;
   int cur = 0;
   hipGetDevice(&cur);
   if (cur != plan->device) hipSetDevice(plan->device);
@@ -1204,6 +1299,8 @@ mpb_status mask_plan_stage_times(const mpb_plan* plan, float* us) {
 
 mpb_status mask_plan_export_launch_order(const mpb_plan* plan, int32_t* records) {
   if (!plan || !records) return fail(MPB_ERR_INVALID_ARGUMENT, "plan or records is NULL");
+  const mpb_status rs = resolve_header(plan);
+  if (rs != MPB_OK) return rs;
   int cur = 0;
   hipGetDevice(&cur);
   if (cur != plan->device) hipSetDevice(plan->device);
@@ -1231,7 +1328,7 @@ constexpr int32_t kMaxSplits = 64;
 // partial-state write).
 static int32_t choose_splits(const mpb_plan* plan) {
   const mpb_problem& b = plan->prob;
-  if (plan->num_tasks <= 0) return 1;
+  if (resolve_header(plan) != MPB_OK || plan->num_tasks <= 0) return 1;
   const int64_t wg_per_cu = b.tile_q >= 128 ? 2 : 4;
   const int64_t slots = (int64_t)device_cus(plan->device) * wg_per_cu;
   if (plan->num_tasks >= slots) return 1;
@@ -1262,6 +1359,7 @@ struct PagedArgs {
 // Workspace of the paged forward: the pool tile of every listed K tile,
 // partial list then full list, each area rounded to 256 bytes.
 static size_t paged_remap_bytes(const mpb_plan* plan) {
+  if (resolve_header(plan) != MPB_OK) return 0;
   return round256((size_t)plan->header[1] * 4) + round256((size_t)plan->header[2] * 4);
 }
 
@@ -1278,6 +1376,15 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   if (dev != plan->device)
     return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan built on device %d used on device %d",
                 plan->device, dev);
+  // A deferred plan's header is read here unless the launch can take the task
+  // count on the device (the plain forward); Split-K and paged forwards size
+  // their work from the counts on the host.
+  const bool lazy = plan->pending.load(std::memory_order_acquire) && num_splits <= 1 && !paged;
+  if (!lazy) {
+    const mpb_status rs = resolve_header(plan);
+    if (rs != MPB_OK) return rs;
+  }
+  const int32_t ntasks = lazy ? plan->tasks_upper : plan->num_tasks;
   // §7 / §8: the call's geometry must equal the plan binding field by field.
   const mpb_problem& a = *problem;
   const mpb_problem& b = plan->prob;
@@ -1297,7 +1404,7 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
     return fail(MPB_ERR_SIGNATURE_MISMATCH, "plan payload/scheduler signature does not match "
                                             "this forward consumer");
   // k and v are never read when there are no keys (every row is then empty)
-  if (plan->num_tasks > 0 && (!q || !o || !lse || (b.total_k > 0 && (!k || !v))))
+  if (ntasks > 0 && (!q || !o || !lse || (b.total_k > 0 && (!k || !v))))
     return fail(MPB_ERR_INVALID_ARGUMENT, "q, k, v, o and lse must be non-NULL");
   const size_t remap_bytes = paged ? paged_remap_bytes(plan) : 0;
   const size_t ws_need =
@@ -1373,12 +1480,14 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.force_partial = (ablate & MPB_ABLATE_FULL_AS_PARTIAL) ? 1 : 0;
   prm.no_skip = (ablate & MPB_ABLATE_NO_SKIP) ? 1 : 0;
   prm.pack_shift = __builtin_ctz((unsigned)plan->pack);
+  prm.dev_header = lazy ? plan->dev.header : nullptr;
+  prm.task_heads = b.heads_q / plan->pack;
   const float log2e = 1.4426950408889634f;
   prm.scale_log2 = scale * log2e;
   prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
   prm.softcap_c2 = sc ? mod->softcap * log2e : 0.0f;
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
-  if (plan->num_tasks == 0) return ok();
+  if (ntasks == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (paged) {
     RemapParams rp;
@@ -1406,8 +1515,8 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
     workspace = static_cast<char*>(workspace) + remap_bytes;
   }
   if (num_splits <= 1) {
-    if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, plan->num_tasks,
-                             prm, s)) != hipSuccess)
+    if ((e = launch_attn_fwd(b.dtype, b.head_dim, b.tile_q, b.tile_k, kind, ntasks, prm, s)) !=
+        hipSuccess)
       return device_status(e, "attention launch");
     return ok();
   }

@@ -26,10 +26,11 @@ def problem(w, tile_q=0, tile_k=0):
 
 
 def build_plan(w, d, tile_q=0, tile_k=0, stream=None, build_backward=False, time_stages=False,
-               pack_gqa=None):
+               pack_gqa=None, defer_header=False):
     return mpb.mask_plan_build(problem(w, tile_q, tile_k), d["mask_func"], d["cu_q"], d["cu_k"],
                                stream=stream, build_backward=build_backward,
-                               time_stages=time_stages, pack_gqa=pack_gqa)
+                               time_stages=time_stages, pack_gqa=pack_gqa,
+                               defer_header=defer_header)
 
 
 def run_attention(w, d, plan, **kw):

@@ -147,7 +147,7 @@ def test_fwd_refuses_null_plan_and_workspace_size(lib):
 
 class BuildOptions(ctypes.Structure):
     _fields_ = [("build_backward", ctypes.c_int32), ("time_stages", ctypes.c_int32),
-                ("pack_gqa", ctypes.c_int32)]
+                ("pack_gqa", ctypes.c_int32), ("defer_header", ctypes.c_int32)]
 
 
 def test_build_options_and_k2q_export_refusals(lib):
@@ -157,7 +157,7 @@ def test_build_options_and_k2q_export_refusals(lib):
     out = ctypes.c_void_p(12345)
     prob = _good()
     for opt in (BuildOptions(2, 0), BuildOptions(0, -1), BuildOptions(0, 0, 3),
-                BuildOptions(0, 0, -1)):
+                BuildOptions(0, 0, -1), BuildOptions(0, 0, 0, 2)):
         out = ctypes.c_void_p(12345)
         st = lib.mask_plan_build_ex(ctypes.byref(prob), ctypes.byref(opt),
                                     ctypes.c_void_p(1), None, None, None, ctypes.byref(out))
