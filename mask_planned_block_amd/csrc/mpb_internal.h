@@ -154,8 +154,11 @@ struct SinglePass {
   uint32_t tag;          // this build's tag (nonzero; words of earlier builds differ)
   int32_t* ticket;       // item counter: 0 on entry, left 0
   int32_t* host_slot;    // host-mapped header slot
+  int32_t deferred;      // 1: deferred read-back: the header goes to the plan block only,
+                         // after the last item's own lists and payload
   int32_t seq;           // the build's sequence number (published last)
   int32_t* p_list;       // [Hmask * upper_rows * nk_max] partial lists, flat CSR order
+                         // (workspace, or the plan block's own lists when deferred)
   int32_t* f_list;       // full lists
   int32_t stage;         // endpoints: 0 read from HBM; staged in LDS as int32 (1 through
                          // registers, 2 loaded straight into LDS) or int16 (3)

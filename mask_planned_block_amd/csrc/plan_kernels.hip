@@ -1395,10 +1395,10 @@ __device__ inline void lb_store(uint64_t* p, uint64_t v) {
 __device__ inline void sp_publish(const PlanDev& d, const SinglePass& sp, int rows_total,
                                   int pnnz, int fnnz, uint32_t err) {
   const int32_t hdr[8] = {rows_total, pnnz, fnnz, 0, 0, 0, 0, (int32_t)err};
-  for (int i = 0; i < 8; ++i) {
-    d.header[i] = hdr[i];
+  for (int i = 0; i < 8; ++i) d.header[i] = hdr[i];
+  if (sp.deferred) return;   // the host reads d.header later
+  for (int i = 0; i < 8; ++i)
     __hip_atomic_store(&sp.host_slot[i], hdr[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
   __hip_atomic_store(&sp.host_slot[kHeaderSeq], sp.seq, __ATOMIC_RELEASE,
                      __HIP_MEMORY_SCOPE_SYSTEM);
 }
@@ -1768,37 +1768,44 @@ void plan_single_pass_kernel(PlanGeo g,
     d.f_off[item] = f_begin;
     w.first_tile[(int64_t)hm * g.upper_rows + row] = pc > 0 ? ptiles[0] : s_ffirst;
   }
-  if (item == n - 1) {
-    // The header waits until every item has fixed its offsets (each did so
-    // from its predecessors' words alone, so these waits end), and carries
-    // the OR of their error bits.
-    const uint32_t tag = sp.tag;
-    uint32_t err_all = 0;
-    for (int j0 = 0; j0 < n; j0 += blockDim.x) {
-      const int j = j0 + tid;
-      if (j >= n) break;
-      uint32_t spins = 0;
-      uint64_t v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
-      while ((uint32_t)(v >> 32) != tag) {
-        if (++spins > kLookbackSpins) {
-          v = lb_word(tag, kDevErrLookback);
-          break;
+  // §4.5 header: with a host read-back it goes out before this item's own
+  // lists and payload (the host waits for it); deferred, after them (only
+  // the kernel's end matters then).
+  auto publish = [&]() __attribute__((always_inline)) {
+    if (item == n - 1) {
+      // The header waits until every item has fixed its offsets (each did so
+      // from its predecessors' words alone, so these waits end), and carries
+      // the OR of their error bits.
+      const uint32_t tag = sp.tag;
+      uint32_t err_all = 0;
+      for (int j0 = 0; j0 < n; j0 += blockDim.x) {
+        const int j = j0 + tid;
+        if (j >= n) break;
+        uint32_t spins = 0;
+        uint64_t v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+        while ((uint32_t)(v >> 32) != tag) {
+          if (++spins > kLookbackSpins) {
+            v = lb_word(tag, kDevErrLookback);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+          v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
         }
-        __builtin_amdgcn_s_sleep(1);
-        v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+        err_all |= (uint32_t)v;
       }
-      err_all |= (uint32_t)v;
+      if (err_all) atomicOr(&s_err2, err_all);
+      __syncthreads();
+      if (tid == 0) {
+        d.p_off[n] = p_begin + pc;
+        d.f_off[n] = f_begin + fc;
+        uint32_t e = (uint32_t)s_err2;
+        if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
+        sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
+      }
     }
-    if (err_all) atomicOr(&s_err2, err_all);
-    __syncthreads();
-    if (tid == 0) {
-      d.p_off[n] = p_begin + pc;
-      d.f_off[n] = f_begin + fc;
-      uint32_t e = (uint32_t)s_err2;
-      if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
-      sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
-    }
-  }
+  };
+  const bool deferred = sp.deferred != 0;
+  if (!deferred) publish();
   // §4.6 lists, flat CSR order, to the workspace
   for (int k = tid; k < pc; k += blockDim.x) sp.p_list[p_begin + k] = ptiles[k];
   {
@@ -1823,6 +1830,7 @@ void plan_single_pass_kernel(PlanGeo g,
       if (grp == 0) row_payload_e(g, ptiles, pc, E, rho, valid, is_row, d.p_masks, p_begin);
     }
   }
+  if (deferred) publish();
 }
 
 // The tail of a single-pass build: workgroup 0 runs the schedule (§4.8) on

@@ -962,6 +962,7 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     sp.tag = seq;
     sp.ticket = slot->arrive[dev] + 32;
     sp.host_slot = slot->pinned_dev;
+    sp.deferred = defer ? 1 : 0;   // deferred: the header goes to the block only
     sp.seq = (int32_t)seq;
     sp.p_list = defer ? d.p_idx : at<int32_t>(wb, o_plist);
     sp.f_list = defer ? d.f_idx : at<int32_t>(wb, o_flist);
