@@ -266,6 +266,9 @@ typedef struct {
                             * short query chunks most, by filling the tile's rows). */
   int32_t defer_header;    /* 0 or 1.  1: a single-pass build returns as soon as its
                             * launches are enqueued, without the header read-back
+                            * (and with at most 256 (mask head, Q row) items at the upper
+                            * bound, the single pass also runs the schedule in the
+                            * workgroup that publishes the header: one launch in all)
                             * (other builds ignore the flag and read it back as usual).
                             * The block keeps its upper-bound layout (the lists are
                             * written into it directly; nothing is cut off), and the
@@ -307,7 +310,9 @@ mpb_status mask_plan_export_k2q_order(const mpb_plan* plan, int32_t* order);
  * us[0] THD geometry (none for BSHD), us[1] classify (a single-pass build:
  * classification, offsets, lists and payload in one launch), us[2] schedule
  * (in place: schedule and materialization in one launch; single pass:
- * schedule and list placement), us[3] materialization (exact builds only),
+ * schedule and list placement; -1 for a deferred build of at most 256
+ * (mask head, Q row) items, whose single pass schedules in its last item),
+ * us[3] materialization (exact builds only),
  * us[4] K2Q count, us[5] K2Q materialization (backward view only), us[6]
  * first event to last (for an exact build this includes the host's header
  * wait).  Waits for the build's last event.

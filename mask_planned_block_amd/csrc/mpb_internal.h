@@ -149,8 +149,9 @@ bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks);
 // look-back, lists and payload in one launch, then the schedule and the
 // placement of the lists in a second one.
 struct SinglePass {
-  uint64_t* lb;          // [Hmask * upper_rows][4] look-back words {aggregate, inclusive
-                         // partial, inclusive full, done}, each (tag << 32) | value
+  uint64_t* lb;          // [Hmask * upper_rows][kLbWords] look-back words {aggregate,
+                         // inclusive partial, inclusive full, done, first listed tile + 1
+                         // (fused builds)}, each (tag << 32) | value
   uint32_t tag;          // this build's tag (nonzero; words of earlier builds differ)
   int32_t* ticket;       // item counter: 0 on entry, left 0
   int32_t* host_slot;    // host-mapped header slot
@@ -162,7 +163,19 @@ struct SinglePass {
   int32_t* f_list;       // full lists
   int32_t stage;         // endpoints: 0 read from HBM; staged in LDS as int32 (1 through
                          // registers, 2 loaded straight into LDS) or int16 (3)
+  int32_t fused;         // 1 (deferred builds of at most kFusedMaxItems upper-bound items):
+                         // the last item also runs the schedule, and there is no tail launch
 };
+// Look-back words per item.
+constexpr int kLbWords = 8;
+// Largest Hmask * upper_rows whose schedule a fused single-pass build runs in
+// the last item's workgroup.
+constexpr int kFusedMaxItems = 256;
+// Dynamic LDS bytes of that schedule for `items_upper` items and a workgroup
+// of `threads` threads.
+constexpr size_t fused_schedule_lds_bytes(int64_t items_upper, int threads) {
+  return (size_t)(14 * items_upper + 2 + (threads / 64 + 3) * 9 + 10) * 4;
+}
 // Longest sample (seqlen_k) whose endpoints a single-pass build stages as
 // int16: every column it compares, up to seqlen_k plus a tile and a word,
 // stays below the int16 sentinel 32767.

@@ -1403,6 +1403,107 @@ __device__ inline void sp_publish(const PlanDev& d, const SinglePass& sp, int ro
                      __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// §4.8 schedule of a fused single-pass build, run by the workgroup of the
+// item that ends the flat order once the header is out.  Its inputs come from
+// the look-back words the items wrote as tagged atomics (gathered into LDS by
+// publish_fused): exclusive offsets lp / lf [n + 1] over the flat items,
+// first listed tiles lt [Hmask * upper_rows] (at hm * upper_rows + row) and
+// costs [n].  The order is the one schedule_block produces: items by
+// descending cost, ties by flat index (each item ranks itself against all
+// others: at most kFusedMaxItems of them), then the per-queue first positions
+// by a scan over the sorted items, then every task to its section-major slot
+// and its interleaved launch slot.
+__device__ __attribute__((always_inline)) inline void schedule_fused(const PlanGeo& g,
+                                                                    const PlanDev& d, int n,
+                                                                    int rows_total, int* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nt = (int)blockDim.x, nw = nt >> 6;
+  const int n_up = g.mask_heads * g.upper_rows;
+  int* lp = lds;
+  int* lf = lp + n_up + 1;
+  int* lt = lf + n_up + 1;
+  int* cost = lt + n_up;
+  int* order = cost + n_up;
+  int* rbase = order + n_up;
+  int* s_vec = rbase + kNumQueues * n_up;   // [nw][kNumQueues]
+  int* s_run = s_vec + nw * kNumQueues;     // [kNumQueues]
+  int* s_sec = s_run + kNumQueues;          // [kNumQueues + 1]
+  // 1. rank of every item: the items of higher cost, or of equal cost and a
+  // lower flat index, come first
+  for (int i = tid; i < n; i += nt) {
+    const int c = cost[i];
+    int r = 0;
+    for (int j = 0; j < n; ++j) {
+      const int cj = cost[j];
+      r += (cj > c || (cj == c && j < i)) ? 1 : 0;
+    }
+    order[r] = i;
+  }
+  if (tid < kNumQueues) s_run[tid] = 0;
+  __syncthreads();
+  // 2. first in-queue position of each item's tasks: exclusive scans over the
+  // sorted items of their per-queue task counts
+  for (int base = 0; base < n; base += nt) {
+    const int pos = base + tid;
+    int v[kNumQueues];
+    int i = 0;
+    if (pos < n) {
+      i = order[pos];
+      const int hm = i / rows_total;
+      row_queue_counts(g, sample_geo(g, d, nullptr, i - hm * rows_total).b, hm, cost[i], v);
+    } else {
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s) v[s] = 0;
+    }
+    int first_pos[kNumQueues];
+#pragma unroll
+    for (int s = 0; s < kNumQueues; ++s) {
+      const int incl = wave_incl_scan(v[s], lane);
+      first_pos[s] = incl - v[s];
+      if (lane == 63) s_vec[wv * kNumQueues + s] = incl;
+    }
+    __syncthreads();
+    if (tid < kNumQueues) {   // queue tid: exclusive prefix of the wavefront totals
+      int run = s_run[tid];
+      for (int x = 0; x < nw; ++x) {
+        const int tw = s_vec[x * kNumQueues + tid];
+        s_vec[x * kNumQueues + tid] = run;
+        run += tw;
+      }
+      s_run[tid] = run;
+    }
+    __syncthreads();
+    if (pos < n) {
+#pragma unroll
+      for (int s = 0; s < kNumQueues; ++s)
+        rbase[i * kNumQueues + s] = s_vec[wv * kNumQueues + s] + first_pos[s];
+    }
+    __syncthreads();   // s_vec is reused
+  }
+  if (tid == 0) {
+    s_sec[0] = 0;
+    for (int s = 0; s < kNumQueues; ++s) s_sec[s + 1] = s_sec[s] + s_run[s];
+    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_sec[s];
+  }
+  if (g.layout == MPB_LAYOUT_BSHD) {   // fixed-length geometry in closed form (§4.2)
+    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+    for (int b = tid; b < g.batch; b += nt) {
+      int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
+      sd[0] = make_int4(b * g.seqlen_q, b * g.seqlen_k, g.seqlen_q, g.seqlen_k);
+      sd[1] = make_int4(b * rps, rps, (g.seqlen_k + g.tile_k - 1) / g.tile_k, 0);
+      d.cu_rows[b + 1] = (b + 1) * rps;
+    }
+    if (tid == 0) d.cu_rows[0] = 0;
+  }
+  __syncthreads();
+  // 3. every task
+  int so[kNumQueues + 1];
+#pragma unroll
+  for (int s = 0; s <= kNumQueues; ++s) so[s] = s_sec[s];
+  write_tasks(g, d, (const int*)lp, (const int*)lf, (const int*)lt, (const int*)rbase, nullptr,
+              so, rows_total, tid, nt);
+}
+
 // Exclusive prefix over the workgroup's threads of (a, b); totals in ta, tb.
 __device__ inline void block_scan2(int a, int b, int* pa, int* pb, int* ta, int* tb, int* s_a,
                                    int* s_b) {
@@ -1708,7 +1809,7 @@ void plan_single_pass_kernel(PlanGeo g,
   if (wv == 0) {
     const uint32_t tag = sp.tag;
     uint64_t* lb = sp.lb;
-    if (lane == 0) lb_store(&lb[4 * (int64_t)item], lb_word(tag, ((uint32_t)pc << 16) | (uint32_t)fc));
+    if (lane == 0) lb_store(&lb[kLbWords * (int64_t)item], lb_word(tag, ((uint32_t)pc << 16) | (uint32_t)fc));
     int acc_p = 0, acc_f = 0;
     int base = item - 1;
     uint32_t spins = 0;
@@ -1718,9 +1819,9 @@ void plan_single_pass_kernel(PlanGeo g,
       int st = 2, vp = 0, vf = 0;   // before item 0: an inclusive prefix of 0
       if (j >= 0) {
         // the three words in one round of loads
-        const uint64_t ag = lb_load(&lb[4 * (int64_t)j]);
-        const uint64_t ip = lb_load(&lb[4 * (int64_t)j + 1]);
-        const uint64_t iq = lb_load(&lb[4 * (int64_t)j + 2]);
+        const uint64_t ag = lb_load(&lb[kLbWords * (int64_t)j]);
+        const uint64_t ip = lb_load(&lb[kLbWords * (int64_t)j + 1]);
+        const uint64_t iq = lb_load(&lb[kLbWords * (int64_t)j + 2]);
         if ((uint32_t)(ip >> 32) == tag && (uint32_t)(iq >> 32) == tag) {
           vp = (int)(uint32_t)ip;
           vf = (int)(uint32_t)iq;
@@ -1752,10 +1853,10 @@ void plan_single_pass_kernel(PlanGeo g,
       base -= 64;
     }
     if (lane == 0) {
-      lb_store(&lb[4 * (int64_t)item + 1], lb_word(tag, (uint32_t)(acc_p + pc)));
-      lb_store(&lb[4 * (int64_t)item + 2], lb_word(tag, (uint32_t)(acc_f + fc)));
+      lb_store(&lb[kLbWords * (int64_t)item + 1], lb_word(tag, (uint32_t)(acc_p + pc)));
+      lb_store(&lb[kLbWords * (int64_t)item + 2], lb_word(tag, (uint32_t)(acc_f + fc)));
       // offsets fixed: this item's error bits (and a wait that ran out)
-      lb_store(&lb[4 * (int64_t)item + 3],
+      lb_store(&lb[kLbWords * (int64_t)item + 3],
                lb_word(tag, (uint32_t)s_err | (timeout ? kDevErrLookback : 0u)));
       s_pbeg = acc_p;
       s_fbeg = acc_f;
@@ -1764,47 +1865,89 @@ void plan_single_pass_kernel(PlanGeo g,
   __syncthreads();
   const int p_begin = s_pbeg, f_begin = s_fbeg;
   if (tid == 0) {
+    const int first = pc > 0 ? ptiles[0] : s_ffirst;
     d.p_off[item] = p_begin;
     d.f_off[item] = f_begin;
-    w.first_tile[(int64_t)hm * g.upper_rows + row] = pc > 0 ? ptiles[0] : s_ffirst;
+    w.first_tile[(int64_t)hm * g.upper_rows + row] = first;
+    // fused builds: the first tile for the schedule in the last item's workgroup
+    if (sp.fused)
+      lb_store(&sp.lb[kLbWords * (int64_t)item + 4], lb_word(sp.tag, (uint32_t)(first + 1)));
   }
   // §4.5 header: with a host read-back it goes out before this item's own
   // lists and payload (the host waits for it); deferred, after them (only
   // the kernel's end matters then).
+  const bool deferred = sp.deferred != 0;
   auto publish = [&]() __attribute__((always_inline)) {
     if (item == n - 1) {
       // The header waits until every item has fixed its offsets (each did so
       // from its predecessors' words alone, so these waits end), and carries
-      // the OR of their error bits.
+      // the OR of their error bits.  A fused build (deferred, so this item's
+      // own lists and payload are done and its LDS is free) also gathers every
+      // item's offsets, cost and first tile from its words for the schedule.
       const uint32_t tag = sp.tag;
+      const bool fuse = sp.fused != 0 && deferred;
+      const int n_up = g.mask_heads * g.upper_rows;
+      int* f_lp = lds;
+      int* f_lf = f_lp + n_up + 1;
+      int* f_lt = f_lf + n_up + 1;
+      int* f_cost = f_lt + n_up;
+      if (fuse) __syncthreads();
       uint32_t err_all = 0;
       for (int j0 = 0; j0 < n; j0 += blockDim.x) {
         const int j = j0 + tid;
         if (j >= n) break;
+        const uint64_t* wj = sp.lb + kLbWords * (int64_t)j;
         uint32_t spins = 0;
-        uint64_t v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+        uint64_t v = lb_load(wj + 3);
         while ((uint32_t)(v >> 32) != tag) {
           if (++spins > kLookbackSpins) {
             v = lb_word(tag, kDevErrLookback);
             break;
           }
           __builtin_amdgcn_s_sleep(1);
-          v = lb_load(&sp.lb[4 * (int64_t)j + 3]);
+          v = lb_load(wj + 3);
         }
         err_all |= (uint32_t)v;
+        if (fuse) {
+          uint64_t ag = lb_load(wj), ip = lb_load(wj + 1), iq = lb_load(wj + 2);
+          uint64_t ft = lb_load(wj + 4);
+          spins = 0;
+          while ((uint32_t)(ag >> 32) != tag || (uint32_t)(ip >> 32) != tag ||
+                 (uint32_t)(iq >> 32) != tag || (uint32_t)(ft >> 32) != tag) {
+            if (++spins > kLookbackSpins) {
+              err_all |= kDevErrLookback;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            ag = lb_load(wj);
+            ip = lb_load(wj + 1);
+            iq = lb_load(wj + 2);
+            ft = lb_load(wj + 4);
+          }
+          const int pcj = (int)((uint32_t)ag >> 16), fcj = (int)((uint32_t)ag & 0xFFFFu);
+          f_lp[j] = (int)(uint32_t)ip - pcj;
+          f_lf[j] = (int)(uint32_t)iq - fcj;
+          f_cost[j] = pcj + fcj;
+          const int hmj = j / rows_total;
+          f_lt[hmj * g.upper_rows + (j - hmj * rows_total)] = (int)(uint32_t)ft - 1;
+          if (j == n - 1) {
+            f_lp[n] = (int)(uint32_t)ip;
+            f_lf[n] = (int)(uint32_t)iq;
+          }
+        }
       }
       if (err_all) atomicOr(&s_err2, err_all);
       __syncthreads();
+      uint32_t e = (uint32_t)s_err2;
+      if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
       if (tid == 0) {
         d.p_off[n] = p_begin + pc;
         d.f_off[n] = f_begin + fc;
-        uint32_t e = (uint32_t)s_err2;
-        if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
         sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
       }
+      if (fuse && e == 0) schedule_fused(g, d, n, rows_total, lds);
     }
   };
-  const bool deferred = sp.deferred != 0;
   if (!deferred) publish();
   // §4.6 lists, flat CSR order, to the workspace
   for (int k = tid; k < pc; k += blockDim.x) sp.p_list[p_begin + k] = ptiles[k];
@@ -2444,7 +2587,10 @@ hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, c
   const size_t ep_ints = sp.stage == 3   ? (ep_rows * g.tile_q + 1) / 2
                          : sp.stage != 0 ? ep_rows * g.tile_q
                                          : 0;
-  const size_t lds = ep_ints * 4 + (size_t)2 * nw * g.words_k * 4 + (size_t)g.nk_max * 4;
+  size_t lds = ep_ints * 4 + (size_t)2 * nw * g.words_k * 4 + (size_t)g.nk_max * 4;
+  // a fused build's last item reuses its LDS for the schedule
+  if (sp.fused)
+    lds = std::max(lds, fused_schedule_lds_bytes((int64_t)g.mask_heads * g.upper_rows, threads));
   // at least one workgroup, so the header is always published
   const dim3 grid((unsigned)(items > 0 ? items : 1)), block(threads);
   if (sp.stage == 3)

@@ -950,7 +950,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
   K2QDev kd;
   std::memset(&kd, 0, sizeof(kd));
   if (single) {
-    if ((e = lookback_acquire(slot->lookback[dev], (size_t)items_upper * 32, s, seq == 1)) !=
+    if ((e = lookback_acquire(slot->lookback[dev], (size_t)items_upper * kLbWords * 8, s,
+                              seq == 1)) !=
         hipSuccess)
       return device_status(e, "look-back words");
     if ((e = heap->alloc(L_sp.bytes, &block, &blk_chunk, &blk_off)) != hipSuccess)
@@ -963,6 +964,8 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     sp.ticket = slot->arrive[dev] + 32;
     sp.host_slot = slot->pinned_dev;
     sp.deferred = defer ? 1 : 0;   // deferred: the header goes to the block only
+    // small deferred builds: the last item schedules too (no tail launch)
+    sp.fused = defer && items_upper <= kFusedMaxItems ? 1 : 0;
     sp.seq = (int32_t)seq;
     sp.p_list = defer ? d.p_idx : at<int32_t>(wb, o_plist);
     sp.f_list = defer ? d.f_idx : at<int32_t>(wb, o_flist);
@@ -986,9 +989,9 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
         (e = tev.timed(1, s, [&] {
            return launch_plan_single_pass(g, mask_func, d, w, sp, thd ? -1 : (int32_t)upper, s);
          })) != hipSuccess ||
-        (e = tev.timed(2, s, [&] {
+        (!sp.fused && (e = tev.timed(2, s, [&] {
            return launch_plan_single_pass_tail(g, d, ws, sp, tiles_upper, !defer, s);
-         })) != hipSuccess) {
+         })) != hipSuccess)) {
       heap->release(blk_chunk, blk_off, blk_bytes, s);
       return device_status(e, "planner launch");
     }

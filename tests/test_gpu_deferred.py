@@ -65,6 +65,23 @@ def test_deferred_forward_equals_waited(name):
     G.compare_plan(ge, op)
 
 
+def test_deferred_large_plan_schedules_in_its_own_launch():
+    """Past the fused schedule's size (block-sparse: 24 x 64 items) a deferred
+    build keeps its schedule launch; its plan and forward equal those of the
+    build that read the header back."""
+    w = W.make("block_sparse")
+    _case("deferred_large")
+    d = G.device_inputs(w)
+    lazy = G.build_plan(w, d, defer_header=True)
+    o_lazy, l_lazy = G.run_attention(w, d, lazy)
+    ref = G.build_plan(w, d)
+    o_ref, l_ref = G.run_attention(w, d, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lazy, o_ref) and torch.equal(l_lazy, l_ref)
+    assert lazy.info.build_mode == mpb.BUILD_SINGLE_PASS_DEFERRED
+    _same_exports(lazy.export(), ref.export())
+
+
 def test_back_to_back_deferred_builds():
     """Several deferred builds of one host thread in a row, each followed by
     its forward, before any header is read: every build reuses the thread's
