@@ -445,17 +445,129 @@ struct RowState {
   float l;   // this lane's partial sum of the weights
 };
 
+// Softmax of one 32-row Q block over one K tile under a softcap score_mod,
+// with the reference max taken from a bound instead of the scores: every
+// softcapped score is at most c (log2 units: c2), plus, for softcap then
+// ALiBi, the largest bias slope * (k - q) over the row's visible keys of the
+// tile.  The row sees the key of that largest bias, whose score is at least
+// -c2 plus the bias, so the row's true maximum is within 2 c2 of the bound,
+// and with 2 c2 + kRescaleSlack <= 100 (cap_bounded) no weight that matters
+// leaves the normal range.  Per score this leaves the cap's exponential and
+// reciprocal, one FMA for the bias and one for the exponent, and the weight's
+// exponential (MASKED: and the predicate's select): no maximum, no
+// subtraction.  A full tile's bound comes from its last (or, for a negative
+// slope, first) column; a partial tile's from the row's last (first) visible
+// column, found from its predicate words -- the same column and the same
+// arithmetic when the predicate is all ones, so a full tile run through the
+// predicate path gives the same bits.  Lazy rescale and the exact zero skip
+// work on the bound as on the maximum.
+template <class Ops, int MOD, bool MASKED>
+__device__ __attribute__((always_inline)) inline bool softmax_block_capped(
+    const AttnParams& p, f32x16 (&acc)[Ops::NKB], const uint32_t (&mw)[Ops::NKB], float kq0,
+    float slope, f32x16 (&o)[Ops::D / 32], RowState& rs, typename Ops::PBlock& pb) {
+  constexpr int NKB = Ops::NKB, D = Ops::D;
+  const float c2 = p.softcap_c2;
+  float bound = c2;
+  if constexpr (MOD == kModSoftcapAlibi) {
+    // the lane's column of element v of block kk is kk*32 + 8(v/4) + v%4 past
+    // kq0; its predicate bit sits at the same position of word kk
+    int col;                                    // the lane's extreme visible column, or -1
+    if constexpr (MASKED) {
+      col = -1;
+      if (slope > 0.0f) {
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) {
+          const uint32_t m = mw[kk] & 0x0F0F0F0Fu;
+          if (m) col = kk * 32 + 31 - __builtin_clz(m);
+        }
+      } else {
+#pragma unroll
+        for (int kk = NKB - 1; kk >= 0; --kk) {
+          const uint32_t m = mw[kk] & 0x0F0F0F0Fu;
+          if (m) col = kk * 32 + __builtin_ctz(m);
+        }
+      }
+    } else {
+      col = slope > 0.0f ? (NKB - 1) * 32 + 27 : 0;
+    }
+    const float bias = col < 0 ? kNegInf : slope * (kq0 + (float)col);
+    bound = c2 + pair_max(bias);                // the row's two lanes agree
+  }
+  if (!p.no_skip && __builtin_amdgcn_ballot_w64(!(bound < rs.m - kNegligibleLog2)) == 0) {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk) acc[kk] = f32x16{};
+    Ops::to_p(pb, acc);
+    return false;
+  }
+  const bool bump = bound > rs.m + kRescaleSlack;
+  if (__builtin_amdgcn_ballot_w64(bump)) {
+    const float alpha = bump ? exp2_fast(rs.m - bound) : 1.0f;
+    rs.m = bump ? bound : rs.m;
+    rs.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+  }
+  const float m2 = -2.0f * c2;
+  if constexpr (MOD == kModSoftcap) {
+    const float x = c2 - rs.m;
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float e = exp2_fast(acc[kk][v] * p.softcap_k);
+        acc[kk][v] = exp2_fast(fmaf(m2, rcp_fast(1.0f + e), x));
+      }
+  } else if constexpr (MOD == kModSoftcapAlibi) {
+    const float base = fmaf(slope, kq0, c2 - rs.m);
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float x = fmaf(slope, (float)(kk * 32 + 8 * (v / 4) + (v % 4)), base);
+        const float e = exp2_fast(acc[kk][v] * p.softcap_k);
+        acc[kk][v] = exp2_fast(fmaf(m2, rcp_fast(1.0f + e), x));
+      }
+  } else {   // ALiBi inside the cap: tanh of (s*scale + slope_h*(k-q)) / c
+    const float x = c2 - rs.m, sb = slope * kq0;
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float t = fmaf(slope, (float)(kk * 32 + 8 * (v / 4) + (v % 4)), sb);
+        const float e = exp2_fast(fmaf(acc[kk][v], p.softcap_k, t));
+        acc[kk][v] = exp2_fast(fmaf(m2, rcp_fast(1.0f + e), x));
+      }
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int kk = 0; kk < NKB; ++kk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t keep =
+            (uint32_t)__builtin_amdgcn_sbfe((int)mw[kk], 8 * (v / 4) + v % 4, 1);
+        acc[kk][v] = __uint_as_float(__float_as_uint(acc[kk][v]) & keep);
+      }
+  }
+  Ops::to_p(pb, acc);
+  rs.l += Ops::row_sum(pb, acc);
+  return true;
+}
+
 // Softmax of one 32-row Q block over one K tile: score_mod and (MASKED) the
 // predicate, online max with lazy rescale of the block's O, exponentials,
 // P in the MFMA operand type and the row sum.  Returns false, with P zero and
 // the state untouched, when every weight of the block would be exactly 0
 // (all scores kNegligibleLog2 below the reference max, or all masked).
-template <class Ops, int MOD, bool MASKED>
+// CAPPED: a softcap score_mod's kernel takes its reference max from the
+// scores' bound (softmax_block_capped).
+template <class Ops, int MOD, bool MASKED, bool CAPPED>
 __device__ __attribute__((always_inline)) inline bool softmax_block(const AttnParams& p, f32x16 (&acc)[Ops::NKB],
                                      const uint32_t (&mw)[Ops::NKB], float kq0, float slope,
                                      f32x16 (&o)[Ops::D / 32], RowState& rs,
                                      typename Ops::PBlock& pb) {
   constexpr int NKB = Ops::NKB, D = Ops::D;
+  if constexpr (CAPPED)
+    return softmax_block_capped<Ops, MOD, MASKED>(p, acc, mw, kq0, slope, o, rs, pb);
   // Without a score_mod the max is taken on the raw dot products (scale > 0)
   // and scaled once; the exponent is then one FMA per element.
   float mt = kNegInf;
@@ -529,7 +641,7 @@ __device__ __attribute__((always_inline)) inline bool softmax_block(const AttnPa
 // the whole tile from them or the score_mod bounds the scores (softcap, then
 // ALiBi: a score is at most the cap plus the tile's largest ALiBi bias), else
 // after the scores.
-template <class Ops, int MOD, bool MASKED>
+template <class Ops, int MOD, bool MASKED, bool CAPPED>
 __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams& p, const typename Ops::QFrag& qf,
                                  const typename Ops::T* kst, const typename Ops::T* vst,
                                  int lane,
@@ -568,8 +680,8 @@ __device__ __attribute__((always_inline)) inline void tile_step(const AttnParams
   bool any = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
-    any |= softmax_block<Ops, MOD, MASKED>(p, acc[qb], mw[qb], kq0[qb], slope[qb], o[qb], rs[qb],
-                                           pf.p[qb]);
+    any |= softmax_block<Ops, MOD, MASKED, CAPPED>(p, acc[qb], mw[qb], kq0[qb], slope[qb], o[qb],
+                                                   rs[qb], pf.p[qb]);
   if (!any) return;
   __builtin_amdgcn_s_setprio(1);
   Ops::pv(o, pf, vst, lane);
@@ -704,7 +816,7 @@ __device__ inline void write_rows(const AttnParams& p, const TaskCtx& c, rsrc_t 
 // Split-K: workgroup i runs split i / tasks_padded of task i % tasks_padded
 // over a contiguous part of the task's tile list and writes its partial state.
 // PAGED: K and V are page pools addressed through the remapped tile lists.
-template <class Ops, int MOD, bool SPLIT, bool PAGED>
+template <class Ops, int MOD, bool SPLIT, bool PAGED, bool CAPPED>
 __global__ __launch_bounds__(Ops::NT) __attribute__((amdgpu_waves_per_eu(Ops::WPE, Ops::WPE)))
 void attn_fwd_kernel(AttnParams p) {
   constexpr int D = Ops::D, TQ = Ops::TQ, TKV = Ops::TKV, NKB = Ops::NKB, ESZ = Ops::ESZ;
@@ -896,7 +1008,8 @@ void attn_fwd_kernel(AttnParams p) {
     float kq0[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) kq0[qb] = (float)(j_cur * TKV + 4 * b2 - qloc[qb]);
-    tile_step<Ops, MOD, kMasked>(p, qf, kbuf(stage), vbuf(stage), lane, mw_cur, kq0, slope, o, rs);
+    tile_step<Ops, MOD, kMasked, CAPPED>(p, qf, kbuf(stage), vbuf(stage), lane, mw_cur, kq0, slope,
+                                         o, rs);
     if (more) {
       Ops::store(st, kbuf(next), vbuf(next), tid);
 #pragma unroll
@@ -1035,15 +1148,23 @@ template <class Ops, bool SPLIT, bool PAGED>
 hipError_t launch_mods(int mod, int num_blocks, const AttnParams& p, hipStream_t s) {
   const dim3 g(num_blocks), blk(Ops::NT);
   auto go = [&](auto m) {
-    hipLaunchKernelGGL((attn_fwd_kernel<Ops, decltype(m)::value, SPLIT, PAGED>), g, blk, 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<Ops, decltype(m)::value, SPLIT, PAGED, false>), g, blk, 0,
+                       s, p);
+    return hipGetLastError();
+  };
+  // softcap score_mods: the bound-max kernel where the cap allows it
+  auto go_cap = [&](auto m) {
+    if (!p.cap_bounded) return go(m);
+    hipLaunchKernelGGL((attn_fwd_kernel<Ops, decltype(m)::value, SPLIT, PAGED, true>), g, blk, 0,
+                       s, p);
     return hipGetLastError();
   };
   switch (mod) {
     case kModNone: return go(std::integral_constant<int, kModNone>{});
-    case kModSoftcap: return go(std::integral_constant<int, kModSoftcap>{});
+    case kModSoftcap: return go_cap(std::integral_constant<int, kModSoftcap>{});
     case kModAlibi: return go(std::integral_constant<int, kModAlibi>{});
-    case kModSoftcapAlibi: return go(std::integral_constant<int, kModSoftcapAlibi>{});
-    case kModAlibiSoftcap: return go(std::integral_constant<int, kModAlibiSoftcap>{});
+    case kModSoftcapAlibi: return go_cap(std::integral_constant<int, kModSoftcapAlibi>{});
+    case kModAlibiSoftcap: return go_cap(std::integral_constant<int, kModAlibiSoftcap>{});
     default: return hipErrorInvalidValue;
   }
 }

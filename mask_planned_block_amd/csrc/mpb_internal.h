@@ -242,6 +242,11 @@ struct AttnParams {
   // 0.  nullptr: the launch covers exactly the plan's tasks.
   const int32_t* dev_header;
   int32_t task_heads;
+  // Softcap score_mods: full tiles take the reference max from the closed-form
+  // bound of their scores (c plus the tile's largest ALiBi bias) instead of the
+  // scores' maximum; set when 2c*log2(e) plus the rescale slack stays under
+  // 100, so weights within 2c of the bound stay normal floats.
+  int32_t cap_bounded;
   float scale_log2;         // scale * log2(e)
   float softcap_k;          // 2*scale*log2(e)/c  (exp2 argument factor of tanh)
   float softcap_c2;         // c * log2(e)

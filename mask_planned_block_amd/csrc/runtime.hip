@@ -1491,6 +1491,9 @@ static mpb_status attn_common(const mpb_plan* plan, const mpb_problem* problem, 
   prm.softcap_k = sc ? 2.0f * scale * log2e / mod->softcap : 0.0f;
   prm.softcap_c2 = sc ? mod->softcap * log2e : 0.0f;
   prm.alibi_k = sc ? 2.0f * log2e / mod->softcap : 0.0f;
+  // the bound of full tiles' softcapped scores serves as their reference max
+  // while weights within 2c of it stay far from underflow (c <= 31.8)
+  prm.cap_bounded = sc && 2.0f * prm.softcap_c2 + 8.0f <= 100.0f ? 1 : 0;
   if (ntasks == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (paged) {
