@@ -153,7 +153,6 @@ struct SinglePass {
                          // inclusive partial, inclusive full, done, first listed tile + 1
                          // (fused builds)}, each (tag << 32) | value
   uint32_t tag;          // this build's tag (nonzero; words of earlier builds differ)
-  int32_t* ticket;       // item counter: 0 on entry, left 0
   int32_t* host_slot;    // host-mapped header slot
   int32_t deferred;      // 1: deferred read-back: the header goes to the plan block only,
                          // after the last item's own lists and payload

@@ -1356,9 +1356,14 @@ __global__ __launch_bounds__(1024) void plan_finish_kernel(PlanGeo g,
 // offsets of its lists by decoupled look-back over the items before it
 // (§4.5), and writes its lists and payload (§4.6, §5) while its endpoints are
 // still in LDS, so the endpoints are read from HBM once.
-//  * Items go out by ticket in flat head-major order: the workgroup that draws
-//    ticket t handles item t, so every item it waits for belongs to a
-//    workgroup that started before it and never waits for a later one.
+//  * Workgroup t handles item t of the flat head-major order and waits only
+//    for items before it.  Workgroups go to the XCDs round-robin and each XCD
+//    starts its own in index order, so the lowest unfinished item either runs
+//    (everything it waits for is done) or waits for a slot on its XCD that
+//    only finished or foreign work holds: the waits end.  (A ticket counter
+//    drawn by every workgroup gave the same guarantee without the dispatch
+//    order, but its atomics on one address serialized the starts: 19 us for
+//    1536 items.)
 //  * Look-back words are tagged with the build's sequence number, so nothing
 //    has to be cleared between builds: a word is valid when its tag is this
 //    build's.  Item t publishes its aggregate (tile counts) as soon as it is
@@ -1557,11 +1562,7 @@ void plan_single_pass_kernel(PlanGeo g,
   const int nwr = sg >> 6;            // wavefronts per group
   const int wr = (tid - grp * sg) >> 6;   // this wavefront's 64-row block
   if (tid == 0) {
-    const int t = __hip_atomic_fetch_add(sp.ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // the last ticket of the grid resets the counter for the next build
-    if (t == (int)gridDim.x - 1)
-      __hip_atomic_store(sp.ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_item = t;
+    s_item = blockIdx.x;
     s_err = 0;
     s_ffirst = -1;
     s_err2 = 0;
@@ -1571,7 +1572,7 @@ void plan_single_pass_kernel(PlanGeo g,
   const int rows_total = rows_total_of(g, d);
   const int n = g.mask_heads * rows_total;
   if (item >= n) {
-    // no rows at all (empty THD batch or a failed prefix check): ticket 0
+    // no rows at all (empty THD batch or a failed prefix check): item 0
     // publishes the empty header
     if (item == 0 && tid == 0) {
       d.p_off[0] = 0;
@@ -1662,88 +1663,143 @@ void plan_single_pass_kernel(PlanGeo g,
     }
   }
 
-  // Pass 1 (§4.3), in windows of 256 K tiles (eight 32-bit words per lane):
-  // each lane merges its row's touching intervals into runs and ORs the
-  // tiles each run touches into its "any" words and the tiles it fully covers
-  // into its "full" words, eight words at a time with no branch per tile.
-  // Across the wavefront "any" is OR-ed and "full" AND-ed: a tile is visible
-  // if some row sees part of it and full if every one of the T_Q rows covers
-  // it, which needs every row in bounds (rows past q_len cover nothing; lanes
-  // past T_Q are not rows) and the tile inside k_len (no run passes k_len).
+  // Pass 1 (§4.3): each lane merges its row's touching intervals into runs
+  // and ORs the tiles each run touches into an "any" word and the tiles it
+  // fully covers into a "full" word, one 32-tile word at a time.  Across the
+  // wavefront "any" is OR-ed and "full" AND-ed: a tile is visible if some row
+  // sees part of it and full if every one of the T_Q rows covers it, which
+  // needs every row in bounds (rows past q_len cover nothing; lanes past T_Q
+  // are not rows) and the tile inside k_len (no run passes k_len).
   const int nk = rg.nk, T = g.tile_k;
   const int wk = (nk + 31) >> 5;
-  {
+  if constexpr (EPM != 0) {
+    // Endpoints in LDS: the lane walks its runs along the words, so a run
+    // costs one mask per word it touches.  [ra, rb) is the lane's current
+    // run ([INT_MAX, INT_MAX) once they are used up).
     const int nint = (g.nfunc + 1) >> 1;
-    // group grp: words [g_w0, g_w1) of the item, tiles [32 g_w0, t_end)
     const int hw = (wk + ng - 1) / ng;
     const int g_w0 = min(grp * hw, wk), g_w1 = min(g_w0 + hw, wk);
-    const int t_end = min(32 * g_w1, nk);
-    for (int tg = 32 * g_w0; tg < t_end; tg += 256) {
-      uint32_t am[8], fm[8];
+    const int sh = 31 - __builtin_clz((uint32_t)T);   // T is a power of two
+    int p = 0, ra = INT_MAX, rb = INT_MAX;
+    auto advance = [&]() __attribute__((always_inline)) {
+      int a = INT_MAX, b = INT_MAX;
+      while (p < nint) {   // the next nonempty interval
+        const int s = p > 0 ? E(2 * p - 1) : 0, e = E(2 * p);
+        ++p;
+        if (e > s) {
+          a = s;
+          b = e;
+          break;
+        }
+      }
+      while (p < nint && b != INT_MAX) {   // intervals touching it: one run
+        const int s = E(2 * p - 1), e = E(2 * p);
+        if (s != b) break;
+        b = e;
+        ++p;
+      }
+      ra = a;
+      rb = b;
+    };
+    if (valid) advance();
+    for (int x = g_w0; x < g_w1; ++x) {
+      const int t_lo = 32 * x;
+      const int k_lo = t_lo << sh, k_hi = (t_lo + 32) << sh;
+      uint32_t any = 0u, full = 0u;
+      while (rb <= k_lo) advance();   // runs that end before this word
+      while (ra < k_hi) {
+        const int t0 = max(ra >> sh, t_lo) - t_lo;
+        const int t1 = min(((rb - 1) >> sh) + 1, t_lo + 32) - t_lo;
+        any |= range_bits(t0, t1);
+        const int f0 = max((ra + T - 1) >> sh, t_lo) - t_lo;
+        const int f1 = min(rb >> sh, t_lo + 32) - t_lo;
+        if (f1 > f0) full |= range_bits(f0, f1);
+        if (rb > k_hi) break;         // the run goes on into the next word
+        advance();
+      }
+      const uint32_t va = wave_or(any);
+      const uint32_t vf = wave_and(is_row ? full : 0xFFFFFFFFu);
+      if (lane == 0) {
+        s_any[wr * g.words_k + x] = va;
+        s_nfull[wr * g.words_k + x] = ~vf;
+      }
+    }
+  } else {
+    // Endpoints read from HBM: runs in windows of 256 tiles (eight words per
+    // lane), the endpoints loaded four intervals at a time.
+    {
+      const int nint = (g.nfunc + 1) >> 1;
+      // group grp: words [g_w0, g_w1) of the item, tiles [32 g_w0, t_end)
+      const int hw = (wk + ng - 1) / ng;
+      const int g_w0 = min(grp * hw, wk), g_w1 = min(g_w0 + hw, wk);
+      const int t_end = min(32 * g_w1, nk);
+      for (int tg = 32 * g_w0; tg < t_end; tg += 256) {
+        uint32_t am[8], fm[8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) am[x] = fm[x] = 0u;
-      // tiles [lo, hi) of the window into m; a range inside one word (most
-      // runs) costs one mask and a select per word
-      auto set_range = [&](uint32_t (&m)[8], int lo, int hi) {
-        lo = max(lo, 0);
-        hi = min(hi, 256);
-        if (hi <= lo) return;
-        const int w0 = lo >> 5;
-        if (w0 == ((hi - 1) >> 5)) {
-          const uint32_t bits = range_bits(lo - 32 * w0, hi - 32 * w0);
+        for (int x = 0; x < 8; ++x) am[x] = fm[x] = 0u;
+        // tiles [lo, hi) of the window into m; a range inside one word (most
+        // runs) costs one mask and a select per word
+        auto set_range = [&](uint32_t (&m)[8], int lo, int hi) {
+          lo = max(lo, 0);
+          hi = min(hi, 256);
+          if (hi <= lo) return;
+          const int w0 = lo >> 5;
+          if (w0 == ((hi - 1) >> 5)) {
+            const uint32_t bits = range_bits(lo - 32 * w0, hi - 32 * w0);
 #pragma unroll
-          for (int x = 0; x < 8; ++x) m[x] |= x == w0 ? bits : 0u;
-          return;
+            for (int x = 0; x < 8; ++x) m[x] |= x == w0 ? bits : 0u;
+            return;
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int l = min(max(lo - 32 * x, 0), 32), h = min(max(hi - 32 * x, 0), 32);
+            const uint32_t from_l = l >= 32 ? 0u : (0xFFFFFFFFu << l);
+            const uint32_t from_h = h >= 32 ? 0u : (0xFFFFFFFFu << h);
+            m[x] |= from_l & ~from_h;
+          }
+        };
+        const int w_lo = tg * T, w_hi = min(tg + 256, t_end) * T;
+        auto flush = [&](int a, int b) {
+          if (b <= a || b <= w_lo || a >= w_hi) return;
+          set_range(am, a / T - tg, (b - 1) / T + 1 - tg);
+          const int f0 = (a + T - 1) / T - tg, f1 = b / T - tg;
+          if (f1 > f0) set_range(fm, f0, f1);
+        };
+        if (valid) {
+          int ra = 0, rb = 0;   // open run [ra, rb), empty while rb <= ra
+          for (int p0 = 0; p0 < nint; p0 += 4) {
+            int sv[4], ev[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int p = p0 + u;
+              sv[u] = p > 0 ? E(2 * p - 1) : 0;
+              ev[u] = E(2 * p);   // INT_MAX past the last interval
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              if (p0 + u >= nint) break;
+              if (ev[u] <= sv[u]) continue;             // empty interval
+              if (rb > ra && sv[u] == rb) {
+                rb = ev[u];                             // touching: extend the run
+              } else {
+                flush(ra, rb);
+                ra = sv[u];
+                rb = ev[u];
+              }
+            }
+          }
+          flush(ra, rb);
         }
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
-          const int l = min(max(lo - 32 * x, 0), 32), h = min(max(hi - 32 * x, 0), 32);
-          const uint32_t from_l = l >= 32 ? 0u : (0xFFFFFFFFu << l);
-          const uint32_t from_h = h >= 32 ? 0u : (0xFFFFFFFFu << h);
-          m[x] |= from_l & ~from_h;
-        }
-      };
-      const int w_lo = tg * T, w_hi = min(tg + 256, t_end) * T;
-      auto flush = [&](int a, int b) {
-        if (b <= a || b <= w_lo || a >= w_hi) return;
-        set_range(am, a / T - tg, (b - 1) / T + 1 - tg);
-        const int f0 = (a + T - 1) / T - tg, f1 = b / T - tg;
-        if (f1 > f0) set_range(fm, f0, f1);
-      };
-      if (valid) {
-        int ra = 0, rb = 0;   // open run [ra, rb), empty while rb <= ra
-        for (int p0 = 0; p0 < nint; p0 += 4) {
-          int sv[4], ev[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int p = p0 + u;
-            sv[u] = p > 0 ? E(2 * p - 1) : 0;
-            ev[u] = E(2 * p);   // INT_MAX past the last interval
-          }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (p0 + u >= nint) break;
-            if (ev[u] <= sv[u]) continue;             // empty interval
-            if (rb > ra && sv[u] == rb) {
-              rb = ev[u];                             // touching: extend the run
-            } else {
-              flush(ra, rb);
-              ra = sv[u];
-              rb = ev[u];
+          const int wd = (tg >> 5) + x;
+          if (wd < g_w1) {
+            const uint32_t va = wave_or(am[x]);
+            const uint32_t vf = wave_and(is_row ? fm[x] : 0xFFFFFFFFu);
+            if (lane == 0) {
+              s_any[wr * g.words_k + wd] = va;
+              s_nfull[wr * g.words_k + wd] = ~vf;
             }
-          }
-        }
-        flush(ra, rb);
-      }
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int wd = (tg >> 5) + x;
-        if (wd < g_w1) {
-          const uint32_t va = wave_or(am[x]);
-          const uint32_t vf = wave_and(is_row ? fm[x] : 0xFFFFFFFFu);
-          if (lane == 0) {
-            s_any[wr * g.words_k + wd] = va;
-            s_nfull[wr * g.words_k + wd] = ~vf;
           }
         }
       }

@@ -266,7 +266,7 @@ struct ThreadSlot {
   int32_t* pinned = nullptr;
   int32_t* pinned_dev = nullptr;
   uint32_t seq = 0;
-  int32_t* arrive[64] = {};   // [64] counters: classify, K2Q count, single-pass ticket
+  int32_t* arrive[64] = {};   // [64] counters: classify, K2Q count, (spare)
   Arena arena[64];
   Arena lookback[64];         // look-back words of single-pass builds
 };
@@ -961,7 +961,6 @@ mpb_status mask_plan_build_ex(const mpb_problem* problem, const mpb_build_option
     SinglePass sp;
     sp.lb = static_cast<uint64_t*>(slot->lookback[dev].ptr);
     sp.tag = seq;
-    sp.ticket = slot->arrive[dev] + 32;
     sp.host_slot = slot->pinned_dev;
     sp.deferred = defer ? 1 : 0;   // deferred: the header goes to the block only
     // small deferred builds: the last item schedules too (no tail launch)
