@@ -1701,7 +1701,20 @@ void plan_single_pass_kernel(PlanGeo g,
       ra = a;
       rb = b;
     };
-    if (valid) advance();
+    if (valid && g_w0 < g_w1) {
+      // enter at the first interval that ends past the group's first key
+      // (binary search; a run that started before it is clipped to the word
+      // anyway, so its earlier intervals are not needed)
+      const int k0 = (32 * g_w0) << sh;
+      int lo = 0, hi = nint;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (E(2 * mid) > k0) hi = mid;
+        else lo = mid + 1;
+      }
+      p = lo;
+      advance();
+    }
     for (int x = g_w0; x < g_w1; ++x) {
       const int t_lo = 32 * x;
       const int k_lo = t_lo << sh, k_hi = (t_lo + 32) << sh;
