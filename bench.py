@@ -337,7 +337,8 @@ def _kernel_group(name):
     for key in ("attn_fwd_kernel", "plan_single_pass_tail_kernel", "plan_single_pass_kernel",
                 "plan_classify_kernel", "plan_schedule_kernel",
                 "plan_materialize_kernel", "plan_geometry_kernel", "plan_finish_kernel",
-                "plan_k2q_count_kernel", "plan_k2q_materialize_kernel", "elementwise"):
+                "plan_k2q_count_kernel", "plan_k2q_materialize_kernel", "attn_bwd_dkdv",
+                "attn_bwd_dq_kernel", "attn_bwd_dot_kernel", "elementwise"):
         if key in name:
             return key
     return None

@@ -14,7 +14,7 @@
 //   dQ = scale * sum_k dS K,  dK = scale * sum_q dS Q,  dV = sum_q P dO.
 //
 // Three launches:
-//  * attn_bwd_dot_kernel: Dq per (row, head), fp32 [Hq][total_q].
+//  * attn_bwd_dot_kernel: -Dq per (row, head), fp32 [Hq][total_q].
 //  * attn_bwd_dq_kernel: one workgroup per task of the plan's launch order
 //    (as the forward), a wavefront per 32 Q rows.  S^T = K Q^T and
 //    dP^T = V dO^T put one Q row in each lane (its LSE and Dq are scalars),
@@ -199,24 +199,24 @@ __device__ inline float softcap_alibi_bound(float c2, float slope, float k_lo) {
 }
 
 // Weight and dS of one score element; lse2 is the row's LSE in log2 units
-// (+inf for a row that sees nothing).  Full tiles (MASKED = false) keep
-// every element.
+// (+inf for a row that sees nothing), ndq is -Dq of the row.  Full tiles
+// (MASKED = false) keep every element.
 template <int MOD, bool MASKED>
 __device__ inline void weight_and_ds(float s, float dp, float kq, uint32_t mw, int pos,
-                                     float lse2, float dq, const BwdParams& p, float slope,
+                                     float lse2, float ndq, const BwdParams& p, float slope,
                                      float& P, float& dS) {
   float grad;
   const float t = mod_fwd_bwd<MOD>(s, kq, p, slope, grad);
   P = exp2_fast(t - lse2);
   if constexpr (MASKED) P = ((mw >> pos) & 1u) ? P : 0.0f;
-  dS = P * (dp - dq) * grad;
+  dS = P * (dp + ndq) * grad;
 }
 
 }  // namespace
 
 // ------------------------------------------------------------------ Dq
 
-// Dq[h][t] = dO[t][h] . O[t][h] in fp32, and the row's LSE in log2 units
+// -Dq[h][t] = -(dO[t][h] . O[t][h]) in fp32, and the row's LSE in log2 units
 // (+inf for a row that sees nothing, whose weights are then exactly 0);
 // D / 8 lanes per (token, head) row.
 template <int D>
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(BwdParams p) {
     const int64_t t = row / p.heads_q;
     const int h = (int)(row % p.heads_q);
     const int64_t x = (int64_t)h * p.total_q + t;
-    p.dvec[x] = s;
+    p.dvec[x] = -s;
     p.lse2[x] = lse_log2(p.lse[x]);
   }
 }
@@ -373,7 +373,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
   bf16x8 qf[DS], df[DS];
   load_row_frags<D>(qf, rq, q_row_off, g);
   load_row_frags<D>(df, rdo, q_row_off, g);
-  const float dqv = row_in ? p.dvec[stat] : 0.0f;
+  const float ndq = row_in ? p.dvec[stat] : 0.0f;   // -Dq
   const float slope = head_slope<MOD>(p, h);
 
   f32x16 acc_dq[DB];
@@ -430,7 +430,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
         const int pos = 8 * (v / 4) + v % 4;
         float P, dS;
         weight_and_ds<MOD, kMasked>(s_acc[v], dp_acc[v], kq0 + (float)(32 * kk + pos), mw, pos,
-                                    lse2, dqv, p, slope, P, dS);
+                                    lse2, ndq, p, slope, P, dS);
         dsb[v / 8][v % 8] = (__bf16)dS;
       }
       // dQ^T += K^T dS^T, transposed operands read one step ahead
@@ -791,6 +791,445 @@ __global__ __launch_bounds__(TKV * 4) void attn_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// Inclusive prefix sum over the wavefront's lanes.
+__device__ inline int wave_prefix_sum(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Byte offsets inside a swizzled tile for the split kernel's fixed reads,
+// each an XOR and an immediate away from a per-lane base: with swz even,
+// chunk 2 s + g of row r sits at row_base(r, g) ^ 32 s, and the transposed
+// fragment (rows 16 m + 8 p + the lane's row, columns 32 db + the lane's) at
+// (tr_base ^ 64 db) + (16 m + 8 p) 2 D for rows that start a multiple of 8.
+template <int D>
+__device__ inline int row_base(int row, int g) {
+  constexpr int CH = D / 8, RP = 256 / (2 * D);
+  return row * 2 * D + 16 * g + 32 * ((row / RP) % (CH / 2));
+}
+template <int D>
+__device__ inline int tr_base(int lane) {
+  const int r = lane & 15, g2 = (lane >> 4) & 1, kg = lane >> 5;
+  const int row = 4 * kg + (r >> 2);
+  const int dcol = 16 * g2 + 4 * (r & 3);
+  return row * 2 * D + (((dcol >> 3) ^ swz<D>(row)) << 4) + 2 * (dcol & 7);
+}
+__device__ inline bf16x8 lds_at(const __bf16* tile, int off) {
+  return *(const bf16x8*)((const char*)tile + off);
+}
+// the A operand of lds_tr_frag from the byte offset of its first four rows
+template <int D>
+__device__ inline bf16x8 lds_tr_at(const __bf16* tile, int off) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const char* b = (const char*)tile + off;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)b);
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(b + 8 * 2 * D));
+  const v4i16 both[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, both);
+}
+
+// dK and dV with one wavefront per 32 x 32 block of a (K plan row, Q tile)
+// pair: for 128-row Q tiles and 64-row K tiles, eight wavefronts, two per
+// SIMD, so one wavefront's weights (VALU) run beside the other's products
+// (MFMA).  Wavefront w takes K block w % 2 and Q block w / 2 of every item;
+// V stays in its registers (a lane per K row), K sits in LDS for the whole
+// workgroup, and Q, dO, LSE and Dq stream through the double buffer of the
+// kernel above.  The four wavefronts of a K block add their sums through LDS
+// at the end (two rounds).  Softcap weights use r (1 - r) for the derivative
+// 4 r (1 - r) and dK's scale takes the factor 4 (exact in bf16).
+template <int D, int TQ, int TKV, int MOD>
+__global__ __launch_bounds__(TQ * TKV / 16) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_split_kernel(BwdParams p) {
+  constexpr int NKW = TKV / 32, NQB = TQ / 32, NW = NKW * NQB;
+  constexpr int DS = D / 16, DB = D / 32;
+  static_assert(NW == 8 && NQB == 4, "eight wavefronts: two K blocks by four Q blocks");
+  __shared__ __attribute__((aligned(16))) __bf16 q_s0[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 q_s1[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s0[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 do_s1[TQ * D];
+  __shared__ __attribute__((aligned(16))) __bf16 k_s[TKV * D];
+  __shared__ __attribute__((aligned(16))) float lse_s0[TQ];
+  __shared__ __attribute__((aligned(16))) float lse_s1[TQ];
+  __shared__ __attribute__((aligned(16))) float dd_s0[TQ];
+  __shared__ __attribute__((aligned(16))) float dd_s1[TQ];
+  __shared__ int s_lists[4][64];   // per head of the group: partial begin, count, full begin, running total
+  auto qbuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return q_s0; else return q_s1;
+  };
+  auto dobuf = [&](auto st) -> __bf16* {
+    if constexpr (decltype(st)::value == 0) return do_s0; else return do_s1;
+  };
+  auto lsebuf = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return lse_s0; else return lse_s1;
+  };
+  auto ddbuf = [&](auto st) -> float* {
+    if constexpr (decltype(st)::value == 0) return dd_s0; else return dd_s1;
+  };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, lq = lane & 31;
+  const int kb = wave % NKW, qb = wave / NKW;
+  constexpr bool kSoftcap =
+      MOD == kModSoftcap || MOD == kModSoftcapAlibi || MOD == kModAlibiSoftcap;
+
+  // KV head: workgroup i runs on XCD i % 8, so with Hk a multiple of 8 the
+  // heads r, r + 8, r + 16, ... would share an XCD; dealing the heads out in
+  // snake order (0..7, then 15..8, ...) mixes the steep and flat ALiBi slopes
+  // (whose exact zero skips leave very different work) on every XCD
+  int kvh = blockIdx.x % p.heads_k;
+  if (p.heads_k % 8 == 0 && ((kvh >> 3) & 1)) kvh ^= 7;
+  const int kr = __builtin_amdgcn_readfirstlane(p.k_order[blockIdx.x / p.heads_k]);
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.k_cu[mid] <= kr) lo = mid; else hi = mid - 1;
+  }
+  const int b = __builtin_amdgcn_readfirstlane(lo);
+  const int j = kr - p.k_cu[b];
+  const int32_t* sd = p.seqdesc + 8 * b;
+  const int q_off = __builtin_amdgcn_readfirstlane(sd[0]);
+  const int k_off = __builtin_amdgcn_readfirstlane(sd[1]);
+  const int q_len = __builtin_amdgcn_readfirstlane(sd[2]);
+  const int k_len = __builtin_amdgcn_readfirstlane(sd[3]);
+
+  const uint32_t q_rs = (uint32_t)p.heads_q * D * 2;
+  const uint32_t kv_rs = (uint32_t)p.heads_k * D * 2;
+  const int64_t kh = (int64_t)k_off * kv_rs + (int64_t)kvh * D * 2;
+  const rsrc_t rk = make_rsrc((const char*)p.k + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rv = make_rsrc((const char*)p.v + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rdk = make_rsrc((char*)p.dk + kh, (uint32_t)k_len * kv_rs);
+  const rsrc_t rdv = make_rsrc((char*)p.dv + kh, (uint32_t)k_len * kv_rs);
+
+  // Items: (head of the group, Q tile) pairs, per head its partial list then
+  // its full list.  Lane hh < group holds head hh's list bounds and the
+  // running item count, so locating item n needs no memory access; only its
+  // Q tile index is read (pair >= 0: the partial pair's payload index).
+  struct Item { int h, i, pair; };
+  int l_pb = 0, l_np = 0, l_fb = 0, l_nf = 0;
+  if (lane < p.group) {
+    const int64_t flat =
+        (int64_t)(p.mask_heads == 1 ? 0 : kvh * p.group + lane) * p.krows_total + kr;
+    l_pb = p.k_p_off[flat];
+    l_np = p.k_p_off[flat + 1] - l_pb;
+    l_fb = p.k_f_off[flat];
+    l_nf = p.k_f_off[flat + 1] - l_fb;
+  }
+  const int l_cum = wave_prefix_sum(l_np + l_nf, lane);
+  const int n_items = __builtin_amdgcn_readlane(l_cum, 63);
+  // head, list slot and payload index of item n (n < n_items), from the
+  // lanes' registers (first items) or from their copy in LDS (the loop)
+  auto locate = [&](int n, int& h, const int32_t*& src, int& pair) {
+    const int hh = __popcll(__builtin_amdgcn_ballot_w64(lane < p.group && l_cum <= n));
+    const int r = n - (hh ? __builtin_amdgcn_readlane(l_cum, hh - 1) : 0);
+    const int np = __builtin_amdgcn_readlane(l_np, hh);
+    h = kvh * p.group + hh;
+    if (r < np) {
+      pair = __builtin_amdgcn_readlane(l_pb, hh) + r;
+      src = p.k_p_idx + pair;
+    } else {
+      pair = -1;
+      src = p.k_f_idx + __builtin_amdgcn_readlane(l_fb, hh) + (r - np);
+    }
+  };
+  auto locate_lds = [&](int n, int& h, const int32_t*& src, int& pair) {
+    const int cum = lane < p.group ? s_lists[3][lane] : n + 1;
+    const int hh = __popcll(__builtin_amdgcn_ballot_w64(cum <= n));
+    const int r = n - (hh ? __builtin_amdgcn_readfirstlane(s_lists[3][hh - 1]) : 0);
+    const int np = __builtin_amdgcn_readfirstlane(s_lists[1][hh]);
+    h = kvh * p.group + hh;
+    if (r < np) {
+      pair = __builtin_amdgcn_readfirstlane(s_lists[0][hh]) + r;
+      src = p.k_p_idx + pair;
+    } else {
+      pair = -1;
+      src = p.k_f_idx + __builtin_amdgcn_readfirstlane(s_lists[2][hh]) + (r - np);
+    }
+  };
+  if (wave == 0) {
+    s_lists[0][lane] = l_pb;
+    s_lists[1][lane] = l_np;
+    s_lists[2][lane] = l_fb;
+    s_lists[3][lane] = l_cum;
+  }
+  auto slope_of = [&](int h) -> float {
+    if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi || MOD == kModAlibiSoftcap)
+      return p.slopes[h];
+    else
+      return 0.0f;
+  };
+  // the raw slope in the units the weights use
+  auto slope_units = [&](float s) -> float {
+    if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi) return s * kLog2e;
+    else if constexpr (MOD == kModAlibiSoftcap) return s * p.alibi_k;
+    else return 0.0f;
+  };
+  auto load_item = [&](const Item& it, __bf16* qd, __bf16* dod, float* ld, float* dd) {
+    const int64_t qh64 = (int64_t)q_off * q_rs + (int64_t)it.h * D * 2;
+    const rsrc_t rq = make_rsrc((const char*)p.q + qh64, (uint32_t)q_len * q_rs);
+    const rsrc_t rdo = make_rsrc((const char*)p.dout + qh64, (uint32_t)q_len * q_rs);
+    const uint32_t off = (uint32_t)it.i * TQ * q_rs;
+    dma_tile<D, TQ, NW>(qd, rq, off, q_rs, wave, lane);
+    dma_tile<D, TQ, NW>(dod, rdo, off, q_rs, wave, lane);
+    const int64_t st = (int64_t)it.h * p.total_q + q_off;
+    if (wave < TQ / 64) {
+      const rsrc_t rl = make_rsrc(p.lse2 + st, (uint32_t)q_len * 4);
+      const rsrc_t rd = make_rsrc(p.dvec + st, (uint32_t)q_len * 4);
+      const int q = it.i * TQ + 64 * wave + lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_vptr)&ld[64 * wave], 4, q * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_vptr)&dd[64 * wave], 4, q * 4, 0, 0, 0);
+    }
+  };
+  // this lane's predicate word: K row 32 kb + lq against the 32 rows of Q block qb
+  auto load_mask = [&](const Item& it) -> uint32_t {
+    return it.pair >= 0 ? p.k_masks[((int64_t)it.pair * TKV + 32 * kb + lq) * NQB + qb]
+                        : 0xFFFFFFFFu;
+  };
+
+  const int kloc = j * TKV + 32 * kb + lq;   // this lane's sample-local K row
+  const uint32_t k_row_off = (uint32_t)kloc * kv_rs;
+  const int qa0 = row_base<D>(32 * qb + lq, g), ka0 = row_base<D>(32 * kb + lq, g);
+  const int ta0 = tr_base<D>(lane) + 32 * qb * 2 * D;
+  Item cur = Item{0, 0, -1}, nxt = Item{0, 0, -1};
+  uint32_t mw_cur = 0, mw_next = 0;
+  float slope_cur = 0.0f;
+  if (n_items > 0) {   // the first two items' Q tiles, read before any fill
+    const int32_t* src;
+    int i0 = 0, i1 = 0;
+    locate(0, cur.h, src, cur.pair);
+    i0 = *src;
+    if (n_items > 1) {
+      locate(1, nxt.h, src, nxt.pair);
+      i1 = *src;
+    }
+    const float s0 = slope_of(cur.h);
+    cur.i = __builtin_amdgcn_readfirstlane(i0);
+    nxt.i = __builtin_amdgcn_readfirstlane(i1);
+    slope_cur = slope_units(s0);
+  }
+  dma_tile<D, TKV, NW>(k_s, rk, (uint32_t)j * TKV * kv_rs, kv_rs, wave, lane);
+  if (n_items > 0) {
+    load_item(cur, q_s0, do_s0, lse_s0, dd_s0);
+    mw_cur = load_mask(cur);
+  }
+  bf16x8 vf[DS];
+  load_row_frags<D>(vf, rv, k_row_off, g);
+
+  f32x16 acc_dk[DB], acc_dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) acc_dk[db] = acc_dv[db] = f32x16{};
+
+  int n = 0;
+  auto step = [&](auto stage) __attribute__((always_inline)) {
+    const auto nx = flip(stage);
+    const __bf16* qs = qbuf(stage);
+    const __bf16* dos = dobuf(stage);
+    const float* ls = lsebuf(stage);
+    const float* ds = ddbuf(stage);
+    const bool more = n + 1 < n_items;
+    // the Q tile of the item after next and the next item's slope, read
+    // before the next item's fill so that waiting for them (after this
+    // item's block) does not wait for the fill
+    Item after = Item{0, 0, -1};
+    int after_i = 0;
+    float slope_nxt = 0.0f;
+    if (n + 2 < n_items) {
+      const int32_t* src;
+      locate_lds(n + 2, after.h, src, after.pair);
+      after_i = *src;
+    }
+    if (more) {
+      slope_nxt = slope_of(nxt.h);
+      load_item(nxt, qbuf(nx), dobuf(nx), lsebuf(nx), ddbuf(nx));
+      mw_next = load_mask(nxt);
+    }
+    // read bases, opaque per item so that the addresses derived from them
+    // are formed inside the item rather than held across the loop
+    int qa = qa0, ka = ka0, ta = ta0;
+    asm volatile("" : "+v"(qa), "+v"(ka), "+v"(ta));
+    const float slope = slope_cur;
+    // k - q of this lane's K row and the block's Q row 4 g (element offsets
+    // 8 (v / 4) + v % 4 are subtracted per element)
+    const float kq0 = (float)(kloc - cur.i * TQ - 32 * qb - 4 * g);
+    auto block = [&]() __attribute__((always_inline)) {
+      // S = Q K^T and dP = dO V^T (lane: K row lq; element v: Q row
+      // 8 (v / 4) + 4 g + v % 4 of the block); dP starts from the rows' -Dq,
+      // so its accumulator ends as dP - Dq
+      f32x16 s_acc = f32x16{}, dp_acc;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const float4 d4 = *(const float4*)&ds[32 * qb + 8 * a + 4 * g];
+        dp_acc[4 * a] = d4.x;
+        dp_acc[4 * a + 1] = d4.y;
+        dp_acc[4 * a + 2] = d4.z;
+        dp_acc[4 * a + 3] = d4.w;
+      }
+      // (operands are not read ahead: the registers are full, and a spill
+      // reloaded after the next item's fill would wait for the whole fill)
+#pragma unroll
+      for (int s = 0; s < DS; ++s) {
+        const bf16x8 aq = lds_at(qs, qa ^ (32 * s));
+        const bf16x8 ad = lds_at(dos, qa ^ (32 * s));
+        const bf16x8 ak = lds_at(k_s, ka ^ (32 * s));
+        s_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, ak, s_acc, 0, 0, 0);
+        dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ad, vf[s], dp_acc, 0, 0, 0);
+      }
+      // weights and dS, rounded to bf16 as the B operands of the gradients
+      bf16x8 pb8[2], dsb[2];
+      const uint32_t mw = mw_cur >> (4 * g);
+      float base;   // per-lane part of the exponent that does not depend on the element
+      if constexpr (MOD == kModAlibi) base = slope * kq0;
+      else if constexpr (MOD == kModSoftcapAlibi) base = fmaf(slope, kq0, p.softcap_c2);
+      else if constexpr (MOD == kModSoftcap) base = p.softcap_c2;
+      else base = 0.0f;
+      auto elem = [&](int v) __attribute__((always_inline)) {
+        const int pos = 8 * (v / 4) + v % 4;
+        const float s = s_acc[v];
+        const float lse = ls[32 * qb + 4 * g + pos];
+        float t, grad = 1.0f;
+        if constexpr (MOD == kModNone) {
+          t = fmaf(s, p.scale_log2, -lse);
+        } else if constexpr (MOD == kModAlibi) {
+          t = fmaf(s, p.scale_log2, fmaf(-slope, (float)pos, base)) - lse;
+        } else if constexpr (MOD == kModAlibiSoftcap) {
+          const float r =
+              rcp_fast(1.0f + exp2_fast(fmaf(s, p.softcap_k, slope * (kq0 - (float)pos))));
+          grad = fmaf(-r, r, r);
+          t = fmaf(-2.0f * p.softcap_c2, r, p.softcap_c2) - lse;
+        } else {   // softcap, then ALiBi for kModSoftcapAlibi (in base)
+          const float r = rcp_fast(1.0f + exp2_fast(s * p.softcap_k));
+          grad = fmaf(-r, r, r);
+          float u = fmaf(-2.0f * p.softcap_c2, r, base);
+          if constexpr (MOD == kModSoftcapAlibi) u = fmaf(-slope, (float)pos, u);
+          t = u - lse;
+        }
+        // the predicate bit sign-extended to an all-ones or all-zeros mask
+        int keep;
+        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(mw), "i"(pos));
+        const float P = __int_as_float(__float_as_int(exp2_fast(t)) & keep);
+        float dS = P * dp_acc[v];
+        if constexpr (kSoftcap) dS *= grad;
+        pb8[v / 8][v % 8] = (__bf16)P;
+        dsb[v / 8][v % 8] = (__bf16)dS;
+      };
+      // dV^T += dO^T P and dK^T += Q^T dS over the block's Q rows 16 m ..
+      // 16 m + 15: the products of rows 0..15 run while the weights of rows
+      // 16..31 are formed
+      // transposed operands of product x (rows 16 (x / DB), columns block x % DB)
+      bf16x8 fd[2], fq[2];
+      auto tr_read = [&](int x, int c) __attribute__((always_inline)) {
+        const int off = (ta ^ (64 * (x % DB))) + 16 * (x / DB) * 2 * D;
+        fd[c] = lds_tr_at<D>(dos, off);
+        fq[c] = lds_tr_at<D>(qs, off);
+      };
+#pragma unroll
+      for (int v = 0; v < 8; ++v) elem(v);
+#pragma unroll
+      for (int x = 0; x < 2 * DB; ++x) {
+        const int c = x & 1, m = x / DB, db = x % DB;
+        tr_read(x, c);
+        acc_dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd[c], pb8[m], acc_dv[db], 0, 0, 0);
+        if (m == 0) elem(8 + 2 * db);
+        acc_dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[c], dsb[m], acc_dk[db], 0, 0, 0);
+        if (m == 0) elem(9 + 2 * db);
+        if (x == DB - 1) {
+#pragma unroll
+          for (int v = 8 + 2 * DB; v < 16; ++v) elem(v);
+        }
+      }
+    };
+    // a block whose predicate hides all of its Q rows from all of the
+    // wavefront's K rows contributes nothing (every weight is exactly 0) ...
+    bool need = p.no_skip != 0 || __builtin_amdgcn_ballot_w64(mw_cur != 0) != 0;
+    // ... and so does one whose weights are all negligible: the bound of
+    // every exponent over the lane's 16 elements against its rows' least LSE
+    // (the 200 margin covers the rounding of the exponent's terms)
+    if constexpr (MOD == kModSoftcapAlibi) {
+      if (need && !p.no_skip) {
+        float lmin = kPosInf;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const float4 l4 = *(const float4*)&ls[32 * qb + 8 * a + 4 * g];
+          lmin = fminf(lmin, fminf(fminf(l4.x, l4.y), fminf(l4.z, l4.w)));
+        }
+        const float bound = softcap_alibi_bound(p.softcap_c2, slope, kq0 - 27.0f);
+        need = __builtin_amdgcn_ballot_w64(!(bound < lmin - kNegligibleLog2)) != 0;
+      }
+    }
+    // (one code path: a full pair's predicate words are all ones; two paths
+    // would not fit the register file together)
+    if (need) block();
+    asm volatile("" : "+v"(after_i), "+v"(slope_nxt));   // used from here on only
+    if (more) {
+      mw_cur = mw_next;
+      cur = nxt;
+      slope_cur = slope_units(slope_nxt);
+      after.i = __builtin_amdgcn_readfirstlane(after_i);
+      nxt = after;
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next item have landed
+    __syncthreads();                 // ... and everyone's; this item's reads are done
+    ++n;
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (n_items > 0) {
+    while (n + 1 < n_items) {
+      step(S0{});
+      step(S1{});
+    }
+    if (n < n_items) step(S0{});
+  }
+
+  // The four Q blocks of each K block add their sums in two rounds through
+  // the Q and dO buffers (free now): blocks 2 and 3 hand over to 0 and 1,
+  // then 1 to 0, which stores.
+  static_assert(2 * DB * 16 * 64 * 4 <= TQ * D * 2, "reduction slot");
+  auto slot = [&](int i) -> float* {
+    __bf16* s = i == 0 ? q_s0 : i == 1 ? q_s1 : i == 2 ? do_s0 : do_s1;
+    return reinterpret_cast<float*>(s);
+  };
+  auto put = [&](float* r) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const float4 a = {acc_dk[db][4 * v4], acc_dk[db][4 * v4 + 1], acc_dk[db][4 * v4 + 2],
+                          acc_dk[db][4 * v4 + 3]};
+        const float4 c = {acc_dv[db][4 * v4], acc_dv[db][4 * v4 + 1], acc_dv[db][4 * v4 + 2],
+                          acc_dv[db][4 * v4 + 3]};
+        *(float4*)&r[((db * 4 + v4) * 64 + lane) * 4] = a;
+        *(float4*)&r[((DB * 4 + db * 4 + v4) * 64 + lane) * 4] = c;
+      }
+  };
+  auto take = [&](const float* r) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        const float4 a = *(const float4*)&r[((db * 4 + v4) * 64 + lane) * 4];
+        const float4 c = *(const float4*)&r[((DB * 4 + db * 4 + v4) * 64 + lane) * 4];
+        acc_dk[db][4 * v4] += a.x; acc_dk[db][4 * v4 + 1] += a.y;
+        acc_dk[db][4 * v4 + 2] += a.z; acc_dk[db][4 * v4 + 3] += a.w;
+        acc_dv[db][4 * v4] += c.x; acc_dv[db][4 * v4 + 1] += c.y;
+        acc_dv[db][4 * v4 + 2] += c.z; acc_dv[db][4 * v4 + 3] += c.w;
+      }
+  };
+  if (qb >= 2) put(slot((qb - 2) * NKW + kb));
+  __syncthreads();
+  if (qb < 2) take(slot(qb * NKW + kb));
+  __syncthreads();
+  if (qb == 1) put(slot(kb));
+  __syncthreads();
+  if (qb == 0) {
+    take(slot(kb));
+    store_rows<D>(rdk, k_row_off, acc_dk, kSoftcap ? 4.0f * p.scale : p.scale, g);
+    store_rows<D>(rdv, k_row_off, acc_dv, 1.0f, g);
+  }
+}
+
 // ------------------------------------------------------------------ dispatch
 
 namespace {
@@ -801,9 +1240,18 @@ hipError_t launch_bwd_mod(int num_tasks, const BwdParams& p, hipStream_t s) {
     hipLaunchKernelGGL((attn_bwd_dq_kernel<D, TQ, TKV, MOD>), dim3(num_tasks), dim3(TQ * 2), 0, s,
                        p);
   const int64_t items = (int64_t)p.heads_k * p.krows_total;
-  if (items > 0)
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, TQ, TKV, MOD>), dim3((unsigned)items),
-                       dim3(TKV * 4), 0, s, p);
+  if (items > 0) {
+    bool split = false;
+    if constexpr (TQ / 32 * (TKV / 32) == 8) {   // eight 32 x 32 blocks per pair
+      split = p.group <= 64;   // the split kernel keeps a group's lists in one wavefront
+      if (split)
+        hipLaunchKernelGGL((attn_bwd_dkdv_split_kernel<D, TQ, TKV, MOD>),
+                           dim3((unsigned)items), dim3(TQ * TKV / 16), 0, s, p);
+    }
+    if (!split)
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, TQ, TKV, MOD>), dim3((unsigned)items),
+                         dim3(TKV * 4), 0, s, p);
+  }
   return hipGetLastError();
 }
 

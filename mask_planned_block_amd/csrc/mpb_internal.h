@@ -301,7 +301,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   const float* lse;          // [heads_q][total_q], natural log
-  float* dvec;               // workspace [heads_q][total_q]: dO . O per row
+  float* dvec;               // workspace [heads_q][total_q]: -(dO . O) per row
   float* lse2;               // workspace [heads_q][total_q]: LSE in log2 units, +inf if empty
   const int32_t* seqdesc;
   const int32_t* task_rec;
