@@ -390,11 +390,14 @@ void attn_bwd_dq_kernel(BwdParams p) {
     const __bf16* ks = kbuf(stage);
     const __bf16* vs = vbuf(stage);
     const bool more = t + 1 < ntiles;
+    // the K tile after next, read before the next tile's fill so that
+    // waiting for it (after this tile's products) does not wait for the fill
+    int j2 = 0;
+    if (t + 2 < ntiles) j2 = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
     if (more) {
       load_kv(j_next, kbuf(nx), vbuf(nx));
       load_masks(t + 1, mw_next);
     }
-    const int j2 = t + 2 < ntiles ? tile_j(t + 2) : 0;
     const float kq0 = (float)(j_cur * TKV + 4 * g - qloc);
 #pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
@@ -444,11 +447,12 @@ void attn_bwd_dq_kernel(BwdParams p) {
         acc_dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk[c], dsb[m], acc_dq[db], 0, 0, 0);
       }
     }
+    asm volatile("" : "+v"(j2));   // used from here on only
     if (more) {
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) mw_cur[kk] = mw_next[kk];
       j_cur = j_next;
-      j_next = j2;
+      j_next = __builtin_amdgcn_readfirstlane(j2);
     }
     __builtin_amdgcn_s_waitcnt(0);   // this wavefront's loads of the next tile have landed
     __syncthreads();                 // ... and everyone's; this tile's reads are done
