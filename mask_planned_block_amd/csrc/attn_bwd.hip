@@ -886,18 +886,50 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
   int kvh = blockIdx.x % p.heads_k;
   if (p.heads_k % 8 == 0 && ((kvh >> 3) & 1)) kvh ^= 7;
   const int kr = __builtin_amdgcn_readfirstlane(p.k_order[blockIdx.x / p.heads_k]);
-  int lo = 0, hi = p.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.k_cu[mid] <= kr) lo = mid; else hi = mid - 1;
+  // Everything the K row's setup reads is issued at once: the group's list
+  // bounds (lane hh: head hh) and, for up to 64 samples, every sample's K
+  // row start and descriptor (lane b: sample b), so the setup waits for one
+  // round of reads instead of a chain of them.
+  // (the reads land in plain registers, used only after all are issued)
+  int p0 = 0, p1 = 0, f0 = 0, f1 = 0;
+  if (lane < p.group) {
+    const int64_t flat =
+        (int64_t)(p.mask_heads == 1 ? 0 : kvh * p.group + lane) * p.krows_total + kr;
+    p0 = p.k_p_off[flat];
+    p1 = p.k_p_off[flat + 1];
+    f0 = p.k_f_off[flat];
+    f1 = p.k_f_off[flat + 1];
   }
-  const int b = __builtin_amdgcn_readfirstlane(lo);
-  const int j = kr - p.k_cu[b];
-  const int32_t* sd = p.seqdesc + 8 * b;
-  const int q_off = __builtin_amdgcn_readfirstlane(sd[0]);
-  const int k_off = __builtin_amdgcn_readfirstlane(sd[1]);
-  const int q_len = __builtin_amdgcn_readfirstlane(sd[2]);
-  const int k_len = __builtin_amdgcn_readfirstlane(sd[3]);
+  int cu = 0;
+  int4 sdl = int4{0, 0, 0, 0};
+  if (p.batch <= 64 && lane < p.batch) {
+    cu = p.k_cu[lane];
+    sdl = *(const int4*)(p.seqdesc + 8 * lane);   // 32-byte records, 256-byte aligned array
+  }
+  const int l_pb = p0, l_np = p1 - p0, l_fb = f0, l_nf = f1 - f0;
+  int b, j, q_off, k_off, q_len, k_len;
+  if (p.batch <= 64) {
+    // the largest b with cu_krows[b] <= kr (the starts ascend)
+    b = __popcll(__builtin_amdgcn_ballot_w64(lane < p.batch && cu <= kr)) - 1;
+    j = kr - __builtin_amdgcn_readlane(cu, b);
+    q_off = __builtin_amdgcn_readlane(sdl.x, b);
+    k_off = __builtin_amdgcn_readlane(sdl.y, b);
+    q_len = __builtin_amdgcn_readlane(sdl.z, b);
+    k_len = __builtin_amdgcn_readlane(sdl.w, b);
+  } else {
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.k_cu[mid] <= kr) lo = mid; else hi = mid - 1;
+    }
+    b = __builtin_amdgcn_readfirstlane(lo);
+    j = kr - p.k_cu[b];
+    const int32_t* sd = p.seqdesc + 8 * b;
+    q_off = __builtin_amdgcn_readfirstlane(sd[0]);
+    k_off = __builtin_amdgcn_readfirstlane(sd[1]);
+    q_len = __builtin_amdgcn_readfirstlane(sd[2]);
+    k_len = __builtin_amdgcn_readfirstlane(sd[3]);
+  }
 
   const uint32_t q_rs = (uint32_t)p.heads_q * D * 2;
   const uint32_t kv_rs = (uint32_t)p.heads_k * D * 2;
@@ -912,15 +944,6 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
   // running item count, so locating item n needs no memory access; only its
   // Q tile index is read (pair >= 0: the partial pair's payload index).
   struct Item { int h, i, pair; };
-  int l_pb = 0, l_np = 0, l_fb = 0, l_nf = 0;
-  if (lane < p.group) {
-    const int64_t flat =
-        (int64_t)(p.mask_heads == 1 ? 0 : kvh * p.group + lane) * p.krows_total + kr;
-    l_pb = p.k_p_off[flat];
-    l_np = p.k_p_off[flat + 1] - l_pb;
-    l_fb = p.k_f_off[flat];
-    l_nf = p.k_f_off[flat + 1] - l_fb;
-  }
   const int l_cum = wave_prefix_sum(l_np + l_nf, lane);
   const int n_items = __builtin_amdgcn_readlane(l_cum, 63);
   // head, list slot and payload index of item n (n < n_items), from the
