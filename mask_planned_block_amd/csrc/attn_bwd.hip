@@ -427,13 +427,44 @@ void attn_bwd_dq_kernel(BwdParams p) {
         dp_acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[c], df[s], dp_acc, 0, 0, 0);
       }
       const uint32_t mw = mw_cur[kk] >> (4 * g);
+      // per-lane part of the exponent (element offsets pos are added per
+      // element); softcap derivatives as r (1 - r), the factor 4 in dQ's scale
+      const float kqb = kq0 + (float)(32 * kk);
+      float base;
+      if constexpr (MOD == kModAlibi || MOD == kModAlibiSoftcap) base = slope * kqb;
+      else if constexpr (MOD == kModSoftcapAlibi) base = fmaf(slope, kqb, p.softcap_c2);
+      else if constexpr (MOD == kModSoftcap) base = p.softcap_c2;
+      else base = 0.0f;
       bf16x8 dsb[2];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int pos = 8 * (v / 4) + v % 4;
-        float P, dS;
-        weight_and_ds<MOD, kMasked>(s_acc[v], dp_acc[v], kq0 + (float)(32 * kk + pos), mw, pos,
-                                    lse2, ndq, p, slope, P, dS);
+        const float s = s_acc[v];
+        float tt, grad = 1.0f;
+        if constexpr (MOD == kModNone) {
+          tt = fmaf(s, p.scale_log2, -lse2);
+        } else if constexpr (MOD == kModAlibi) {
+          tt = fmaf(s, p.scale_log2, fmaf(slope, (float)pos, base)) - lse2;
+        } else if constexpr (MOD == kModAlibiSoftcap) {
+          const float r =
+              rcp_fast(1.0f + exp2_fast(fmaf(s, p.softcap_k, fmaf(slope, (float)pos, base))));
+          grad = fmaf(-r, r, r);
+          tt = fmaf(-2.0f * p.softcap_c2, r, p.softcap_c2) - lse2;
+        } else {   // softcap, then ALiBi for kModSoftcapAlibi (in base)
+          const float r = rcp_fast(1.0f + exp2_fast(s * p.softcap_k));
+          grad = fmaf(-r, r, r);
+          float u = fmaf(-2.0f * p.softcap_c2, r, base);
+          if constexpr (MOD == kModSoftcapAlibi) u = fmaf(slope, (float)pos, u);
+          tt = u - lse2;
+        }
+        float P = exp2_fast(tt);
+        if constexpr (kMasked) {
+          int keep;   // the predicate bit sign-extended to an all-ones or all-zeros mask
+          asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(keep) : "v"(mw), "i"(pos));
+          P = __int_as_float(__float_as_int(P) & keep);
+        }
+        float dS = P * (dp_acc[v] + ndq);
+        if constexpr (MOD != kModNone && MOD != kModAlibi) dS *= grad;
         dsb[v / 8][v % 8] = (__bf16)dS;
       }
       // dQ^T += K^T dS^T, transposed operands read one step ahead
@@ -473,7 +504,9 @@ void attn_bwd_dq_kernel(BwdParams p) {
     run(std::true_type{}, np);
     run(std::false_type{}, ntiles);
   }
-  store_rows<D>(rdq, q_row_off, acc_dq, p.scale, g);
+  constexpr bool kSoftcap =
+      MOD == kModSoftcap || MOD == kModSoftcapAlibi || MOD == kModAlibiSoftcap;
+  store_rows<D>(rdq, q_row_off, acc_dq, kSoftcap ? 4.0f * p.scale : p.scale, g);
 }
 
 // ------------------------------------------------------------------ dK, dV
