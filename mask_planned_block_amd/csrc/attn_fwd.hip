@@ -926,19 +926,32 @@ void attn_fwd_kernel(AttnParams p) {
   }
   const int tq_plan = TQ >> psh;   // payload word rows per partial tile
 
-  // tile t of the task: partial list first, then full list (§6.1)
+  // Tile t of the task: the partial list first, then the full list (§6.1);
+  // without ALiBi (whose bias peaks where the partial tiles are) the full
+  // list first, so that the tasks of a (sample, head) begin on the tiles they
+  // share (window + sink: the sink tile, an L2 hit) rather than on a tile of
+  // their own.  Split-K parts keep the plan's order (their ranges are cut
+  // from it).
+  constexpr bool kFullFirst = !SPLIT && (MOD == kModNone || MOD == kModSoftcap);
+  const int nf = ntiles - np;
+  auto is_partial = [&](int t) { return kFullFirst ? t >= nf : t < np; };
+  auto list_pos = [&](int t) {   // position in the partial or the full list
+    return kFullFirst ? (t < nf ? f_beg + t : p_beg + t - nf)
+                      : (t < np ? p_beg + t : f_beg + t - np);
+  };
   auto tile_j = [&](int t) {
-    return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
+    return __builtin_amdgcn_readfirstlane(is_partial(t) ? p.p_idx[list_pos(t)]
+                                                        : p.f_idx[list_pos(t)]);
   };
   auto tile_phys = [&](int t) {
-    return __builtin_amdgcn_readfirstlane(t < np ? p.phys_p[p_beg + t]
-                                                 : p.phys_f[f_beg + t - np]);
+    return __builtin_amdgcn_readfirstlane(is_partial(t) ? p.phys_p[list_pos(t)]
+                                                        : p.phys_f[list_pos(t)]);
   };
   auto load_masks = [&](int t, uint32_t (&mw)[QB][NKB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (t < np) {
-        const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * tq_plan + prow[qb]) * NKB;
+      if (is_partial(t)) {
+        const uint32_t* src = p.p_masks + ((int64_t)list_pos(t) * tq_plan + prow[qb]) * NKB;
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) mw[qb][kk] = src[kk];
       } else {
@@ -950,7 +963,8 @@ void attn_fwd_kernel(AttnParams p) {
 
   typename Ops::Stage st;
   uint32_t mw_cur[QB][NKB], mw_next[QB][NKB];
-  int j_cur = j_first;
+  // (the record's first tile is the first listed one, partial first)
+  int j_cur = kFullFirst && ntiles > 0 && nf > 0 && np > 0 ? tile_j(0) : j_first;
   // K-tile index of tile t+1, read one tile ahead of its use so that no
   // tile waits on the index load before issuing its prefetch.
   int j_ahead = 0, ph_ahead = 0;
@@ -1001,9 +1015,9 @@ void attn_fwd_kernel(AttnParams p) {
       load_masks(t + 1, mw_next);
     }
     if (t + 2 < ntiles) {
-      j_pending = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
+      j_pending = is_partial(t + 2) ? p.p_idx[list_pos(t + 2)] : p.f_idx[list_pos(t + 2)];
       if constexpr (PAGED)
-        ph_pending = t + 2 < np ? p.phys_p[p_beg + t + 2] : p.phys_f[f_beg + t + 2 - np];
+        ph_pending = is_partial(t + 2) ? p.phys_p[list_pos(t + 2)] : p.phys_f[list_pos(t + 2)];
     }
     float kq0[QB];
 #pragma unroll
@@ -1052,8 +1066,17 @@ void attn_fwd_kernel(AttnParams p) {
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) mw_cur[qb][kk] >>= 4 * b2;
-    run(std::true_type{}, p.force_partial ? ntiles : np);
-    run(std::false_type{}, ntiles);
+    if constexpr (kFullFirst) {
+      if (p.force_partial) {
+        run(std::true_type{}, ntiles);
+      } else {
+        run(std::false_type{}, nf);
+        run(std::true_type{}, ntiles);
+      }
+    } else {
+      run(std::true_type{}, p.force_partial ? ntiles : np);
+      run(std::false_type{}, ntiles);
+    }
   }
 
   write_rows<Ops, SPLIT>(p, c, ro, hq0, q_row_off, qloc, hs, o, rs, b2);
