@@ -343,12 +343,23 @@ void attn_bwd_dq_kernel(BwdParams p) {
   const rsrc_t rv = make_rsrc((const char*)p.v + kh, (uint32_t)k_len * kv_rs);
 
   const uint32_t q_row_off = (uint32_t)qloc * q_rs;
+  // Tile t of the row: the partial list, then the full list; without ALiBi
+  // the full list first, as in the forward (the tasks of a head begin on the
+  // tiles they share)
+  constexpr bool kFullFirst = MOD == kModNone || MOD == kModSoftcap;
+  const int nfl = ntiles - np;
+  auto is_partial = [&](int t) { return kFullFirst ? t >= nfl : t < np; };
+  auto list_pos = [&](int t) {
+    return kFullFirst ? (t < nfl ? f_beg + t : p_beg + t - nfl)
+                      : (t < np ? p_beg + t : f_beg + t - np);
+  };
+  auto tile_raw = [&](int t) { return is_partial(t) ? p.p_idx[list_pos(t)] : p.f_idx[list_pos(t)]; };
   auto tile_j = [&](int t) {
-    return __builtin_amdgcn_readfirstlane(t < np ? p.p_idx[p_beg + t] : p.f_idx[f_beg + t - np]);
+    return __builtin_amdgcn_readfirstlane(tile_raw(t));
   };
   auto load_masks = [&](int t, uint32_t (&mw)[NKB]) {
-    if (t < np) {
-      const uint32_t* src = p.p_masks + ((int64_t)(p_beg + t) * TQ + 32 * wave + lq) * NKB;
+    if (is_partial(t)) {
+      const uint32_t* src = p.p_masks + ((int64_t)list_pos(t) * TQ + 32 * wave + lq) * NKB;
 #pragma unroll
       for (int kk = 0; kk < NKB; ++kk) mw[kk] = src[kk];
     } else {
@@ -393,7 +404,7 @@ void attn_bwd_dq_kernel(BwdParams p) {
     // the K tile after next, read before the next tile's fill so that
     // waiting for it (after this tile's products) does not wait for the fill
     int j2 = 0;
-    if (t + 2 < ntiles) j2 = t + 2 < np ? p.p_idx[p_beg + t + 2] : p.f_idx[f_beg + t + 2 - np];
+    if (t + 2 < ntiles) j2 = tile_raw(t + 2);
     if (more) {
       load_kv(j_next, kbuf(nx), vbuf(nx));
       load_masks(t + 1, mw_next);
@@ -501,8 +512,13 @@ void attn_bwd_dq_kernel(BwdParams p) {
   if (ntiles > 0) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    run(std::true_type{}, np);
-    run(std::false_type{}, ntiles);
+    if constexpr (kFullFirst) {
+      run(std::false_type{}, nfl);
+      run(std::true_type{}, ntiles);
+    } else {
+      run(std::true_type{}, np);
+      run(std::false_type{}, ntiles);
+    }
   }
   constexpr bool kSoftcap =
       MOD == kModSoftcap || MOD == kModSoftcapAlibi || MOD == kModAlibiSoftcap;
