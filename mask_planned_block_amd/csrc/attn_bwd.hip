@@ -909,7 +909,7 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float lse_s1[TQ];
   __shared__ __attribute__((aligned(16))) float dd_s0[TQ];
   __shared__ __attribute__((aligned(16))) float dd_s1[TQ];
-  __shared__ int s_lists[4][64];   // per head of the group: partial begin, count, full begin, running total
+  __shared__ int s_lists[5][64];   // per head of the group: partial begin, count, full begin, running total, full count
   auto qbuf = [&](auto st) -> __bf16* {
     if constexpr (decltype(st)::value == 0) return q_s0; else return q_s1;
   };
@@ -989,10 +989,12 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
   const rsrc_t rdv = make_rsrc((char*)p.dv + kh, (uint32_t)k_len * kv_rs);
 
   // Items: (head of the group, Q tile) pairs, per head its partial list then
-  // its full list.  Lane hh < group holds head hh's list bounds and the
-  // running item count, so locating item n needs no memory access; only its
-  // Q tile index is read (pair >= 0: the partial pair's payload index).
+  // its full list (without ALiBi the full list first, as in the forward).
+  // Lane hh < group holds head hh's list bounds and the running item count,
+  // so locating item n needs no memory access; only its Q tile index is read
+  // (pair >= 0: the partial pair's payload index).
   struct Item { int h, i, pair; };
+  constexpr bool kFullFirst = MOD == kModNone || MOD == kModSoftcap;
   const int l_cum = wave_prefix_sum(l_np + l_nf, lane);
   const int n_items = __builtin_amdgcn_readlane(l_cum, 63);
   // head, list slot and payload index of item n (n < n_items), from the
@@ -1000,14 +1002,14 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
   auto locate = [&](int n, int& h, const int32_t*& src, int& pair) {
     const int hh = __popcll(__builtin_amdgcn_ballot_w64(lane < p.group && l_cum <= n));
     const int r = n - (hh ? __builtin_amdgcn_readlane(l_cum, hh - 1) : 0);
-    const int np = __builtin_amdgcn_readlane(l_np, hh);
+    const int np = __builtin_amdgcn_readlane(l_np, hh), nf = __builtin_amdgcn_readlane(l_nf, hh);
     h = kvh * p.group + hh;
-    if (r < np) {
-      pair = __builtin_amdgcn_readlane(l_pb, hh) + r;
+    if (kFullFirst ? r >= nf : r < np) {
+      pair = __builtin_amdgcn_readlane(l_pb, hh) + (kFullFirst ? r - nf : r);
       src = p.k_p_idx + pair;
     } else {
       pair = -1;
-      src = p.k_f_idx + __builtin_amdgcn_readlane(l_fb, hh) + (r - np);
+      src = p.k_f_idx + __builtin_amdgcn_readlane(l_fb, hh) + (kFullFirst ? r : r - np);
     }
   };
   auto locate_lds = [&](int n, int& h, const int32_t*& src, int& pair) {
@@ -1015,13 +1017,14 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
     const int hh = __popcll(__builtin_amdgcn_ballot_w64(cum <= n));
     const int r = n - (hh ? __builtin_amdgcn_readfirstlane(s_lists[3][hh - 1]) : 0);
     const int np = __builtin_amdgcn_readfirstlane(s_lists[1][hh]);
+    const int nf = __builtin_amdgcn_readfirstlane(s_lists[4][hh]);
     h = kvh * p.group + hh;
-    if (r < np) {
-      pair = __builtin_amdgcn_readfirstlane(s_lists[0][hh]) + r;
+    if (kFullFirst ? r >= nf : r < np) {
+      pair = __builtin_amdgcn_readfirstlane(s_lists[0][hh]) + (kFullFirst ? r - nf : r);
       src = p.k_p_idx + pair;
     } else {
       pair = -1;
-      src = p.k_f_idx + __builtin_amdgcn_readfirstlane(s_lists[2][hh]) + (r - np);
+      src = p.k_f_idx + __builtin_amdgcn_readfirstlane(s_lists[2][hh]) + (kFullFirst ? r : r - np);
     }
   };
   if (wave == 0) {
@@ -1029,6 +1032,7 @@ void attn_bwd_dkdv_split_kernel(BwdParams p) {
     s_lists[1][lane] = l_np;
     s_lists[2][lane] = l_fb;
     s_lists[3][lane] = l_cum;
+    s_lists[4][lane] = l_nf;
   }
   auto slope_of = [&](int h) -> float {
     if constexpr (MOD == kModAlibi || MOD == kModSoftcapAlibi || MOD == kModAlibiSoftcap)
