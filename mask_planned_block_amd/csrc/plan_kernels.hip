@@ -599,18 +599,32 @@ __device__ inline int row_cost(const PlanWork& w, int i) {
   return (w.p_off_tmp[i + 1] - w.p_off_tmp[i]) + (w.f_off_tmp[i + 1] - w.f_off_tmp[i]);
 }
 
-// Number of KV heads hk in [0, Hk) with (b*Hk + hk) % 8 == s; they are
-// r, r+8, ... with r = (s - b*Hk) mod 8.
-// Section of KV head hk of sample b: (b*Hk + hk) mod 8, from the low bits
-// (unsigned arithmetic, exact modulo 8 whatever the product's size).
-__device__ inline int section_of(int b, int heads_k, int hk) {
-  return (int)(((uint32_t)b * (uint32_t)heads_k + (uint32_t)hk) & (kNumSections - 1));
+// Sections deal the (sample, KV head) pairs to the eight XCDs in snake
+// order: with x = b*Hk + hk, block x / 8 goes 0..7 when even and 7..0 when
+// odd, so consecutive heads (whose ALiBi slopes, and with them the work the
+// exact-zero skips leave, fall with the head index) spread over all XCDs.
+// The pattern repeats every 16, so only x mod 16 matters: x0 = (b*Hk) mod 16
+// from the low bits (unsigned arithmetic, exact whatever the product's size).
+__device__ inline int snake_section(uint32_t x) {
+  const int lo = (int)(x & (kNumSections - 1));
+  return (x >> 3) & 1u ? kNumSections - 1 - lo : lo;
 }
-
-__device__ inline int kv_heads_in_section(int b, int heads_k, int s, int* r_out) {
-  const int r = (int)(((uint32_t)s - (uint32_t)b * (uint32_t)heads_k) & (kNumSections - 1));
-  *r_out = r;
-  return r < heads_k ? (heads_k - 1 - r) / kNumSections + 1 : 0;
+__device__ inline int section_of(int b, int heads_k, int hk) {
+  return snake_section(((uint32_t)b * (uint32_t)heads_k & 15u) + (uint32_t)hk);
+}
+// Targets of section s up to X (X >= -1): blocks 2k and 2k+1 hold it at 16k + s
+// and 16k + 15 - s.
+__device__ inline int section_targets_upto(int s, int X) {
+  const int n = X + 1, m = n & 15;
+  return 2 * (n >> 4) + (m > s ? 1 : 0) + (m > kNumSections * 2 - 1 - s ? 1 : 0);
+}
+// Number of KV heads hk in [0, Hk) of section s for sample b, and (rank_hk
+// >= 0) the number of those below rank_hk.
+__device__ inline int kv_heads_in_section(int b, int heads_k, int s, int rank_hk = -1) {
+  const int x0 = (int)((uint32_t)b * (uint32_t)heads_k & 15u);
+  const int below = section_targets_upto(s, x0 - 1);
+  const int end = rank_hk >= 0 ? x0 + rank_hk : x0 + heads_k;
+  return section_targets_upto(s, end - 1) - below;
 }
 
 // Launch slot of the r-th task of section s: sections interleaved while they
@@ -662,10 +676,7 @@ __device__ inline void row_queue_counts(const PlanGeo& g, int b, int hm, int cos
     v[kNumSections] = g.mask_heads == 1 ? g.heads_q : 1;
   } else if (g.mask_heads == 1) {
 #pragma unroll
-    for (int s = 0; s < kNumSections; ++s) {
-      int r;
-      v[s] = group * kv_heads_in_section(b, g.heads_k, s, &r);
-    }
+    for (int s = 0; s < kNumSections; ++s) v[s] = group * kv_heads_in_section(b, g.heads_k, s);
   } else {
     const int sec = section_of(b, g.heads_k, hm / group);
 #pragma unroll
@@ -678,10 +689,7 @@ __device__ inline int row_queue_count(const PlanGeo& g, int b, int hm, int cost,
   const int group = g.heads_q / g.heads_k;
   if (cost == 0) return q == kNumSections ? (g.mask_heads == 1 ? g.heads_q : 1) : 0;
   if (q == kNumSections) return 0;
-  if (g.mask_heads == 1) {
-    int r;
-    return group * kv_heads_in_section(b, g.heads_k, q, &r);
-  }
+  if (g.mask_heads == 1) return group * kv_heads_in_section(b, g.heads_k, q);
   return q == section_of(b, g.heads_k, hm / group) ? 1 : 0;
 }
 
@@ -736,9 +744,7 @@ __device__ __attribute__((always_inline)) inline void write_tasks(
       const int hk = h / group;
       s = section_of(sg.b, g.heads_k, hk);
       if (g.mask_heads == 1) {
-        int r;
-        kv_heads_in_section(sg.b, g.heads_k, s, &r);
-        rank = ((hk - r) / kNumSections) * group + (h - hk * group);
+        rank = kv_heads_in_section(sg.b, g.heads_k, s, hk) * group + (h - hk * group);
       } else {
         rank = 0;
       }

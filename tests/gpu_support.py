@@ -60,11 +60,19 @@ def compare_plan(gp, op, with_k2q=False):
     assert np.array_equal(gp["p_masks"], op.p_masks), "payload words differ"
 
 
+def snake_section(x, num_sections=8):
+    """Section of flat (sample, KV head) index x = b*Hk + hk: blocks of
+    num_sections go 0..7 when even and 7..0 when odd."""
+    lo = x % num_sections
+    return num_sections - 1 - lo if (x // num_sections) % 2 else lo
+
+
 def check_schedule(w, gp, tile_q, num_sections=8):
     """The forward schedule is a permutation of all (row, head) tasks with the
     right q_valid_rows; positive-cost tasks sit in their (batch, kv-head)
-    section in descending cost, ties by flat mask row (head-major) and then
-    head; zero-cost tasks last, in the same tie order."""
+    section (snake order over the flat index b*Hk + hk) in descending cost,
+    ties by flat mask row (head-major) and then head; zero-cost tasks last,
+    in the same tie order."""
     wd, so = gp["work_desc"], gp["section_off"]
     cu_rows, sd = gp["cu_rows"], gp["seqdesc"]
     rows_total = int(cu_rows[-1])
@@ -91,7 +99,7 @@ def check_schedule(w, gp, tile_q, num_sections=8):
             c = cost(b, h, i)
             tie = (b, i, h) if w.mask_heads == 1 else (h, b, i)
             if s < num_sections:
-                assert c > 0 and (b * w.heads_k + h // group) % num_sections == s
+                assert c > 0 and snake_section(b * w.heads_k + h // group, num_sections) == s
                 key = (-c,) + tie
             else:
                 assert c == 0
