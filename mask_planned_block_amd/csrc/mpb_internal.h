@@ -168,12 +168,12 @@ struct SinglePass {
 // Look-back words per item.
 constexpr int kLbWords = 8;
 // Largest Hmask * upper_rows whose schedule a fused single-pass build runs in
-// the last item's workgroup.
+// its items' workgroups (each item writes its own row's tasks).
 constexpr int kFusedMaxItems = 256;
 // Dynamic LDS bytes of that schedule for `items_upper` items and a workgroup
 // of `threads` threads.
 constexpr size_t fused_schedule_lds_bytes(int64_t items_upper, int threads) {
-  return (size_t)(14 * items_upper + 2 + (threads / 64 + 3) * 9 + 10) * 4;
+  return (size_t)(14 * items_upper + 2 + (2 * (threads / 64) + 2) * 9 + 10) * 4;
 }
 // Longest sample (seqlen_k) whose endpoints a single-pass build stages as
 // int16: every column it compares, up to seqlen_k plus a tile and a word,

@@ -719,9 +719,9 @@ namespace {
 template <class PP, class RP>
 __device__ __attribute__((always_inline)) inline void write_tasks(
     const PlanGeo& g, const PlanDev& d, PP P, PP F, PP FT, RP rbase, const int* cu,
-    const int (&so)[kNumQueues + 1], int rows_total, int t0, int stride) {
+    const int (&so)[kNumQueues + 1], int rows_total, int t0, int stride, int t_end = -1) {
   const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
-  const int ntasks = rows_total * Hq;
+  const int ntasks = t_end >= 0 ? t_end : rows_total * Hq;
   for (int t = t0; t < ntasks; t += stride) {
     int i, h;
     if (g.mask_heads == 1) {
@@ -1414,19 +1414,20 @@ __device__ inline void sp_publish(const PlanDev& d, const SinglePass& sp, int ro
                      __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// §4.8 schedule of a fused single-pass build, run by the workgroup of the
-// item that ends the flat order once the header is out.  Its inputs come from
-// the look-back words the items wrote as tagged atomics (gathered into LDS by
-// publish_fused): exclusive offsets lp / lf [n + 1] over the flat items,
-// first listed tiles lt [Hmask * upper_rows] (at hm * upper_rows + row) and
-// costs [n].  The order is the one schedule_block produces: items by
-// descending cost, ties by flat index (each item ranks itself against all
-// others: at most kFusedMaxItems of them), then the per-queue first positions
-// by a scan over the sorted items, then every task to its section-major slot
-// and its interleaved launch slot.
+// §4.8 schedule of a fused single-pass build, run by every item's workgroup
+// after its own lists and payload, for its own mask row.  Its inputs come
+// from the look-back words the items wrote as tagged atomics (gathered into
+// LDS): exclusive offsets lp / lf [n + 1] over the flat items, first listed
+// tiles lt [Hmask * upper_rows] (at hm * upper_rows + row) and costs [n].  The
+// order is the one schedule_block produces (items by descending cost, ties by
+// flat index): the row's first position in each queue is the task count of
+// the rows ranked before it, so no item sorts; its tasks then go to their
+// section-major slots and interleaved launch slots.  The writer (the last
+// item) also stores the queue starts and the fixed-length geometry.
 __device__ __attribute__((always_inline)) inline void schedule_fused(const PlanGeo& g,
                                                                     const PlanDev& d, int n,
-                                                                    int rows_total, int* lds) {
+                                                                    int rows_total, int* lds,
+                                                                    int item, bool writer) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nt = (int)blockDim.x, nw = nt >> 6;
   const int n_up = g.mask_heads * g.upper_rows;
@@ -1434,69 +1435,53 @@ __device__ __attribute__((always_inline)) inline void schedule_fused(const PlanG
   int* lf = lp + n_up + 1;
   int* lt = lf + n_up + 1;
   int* cost = lt + n_up;
-  int* order = cost + n_up;
-  int* rbase = order + n_up;
-  int* s_vec = rbase + kNumQueues * n_up;   // [nw][kNumQueues]
-  int* s_run = s_vec + nw * kNumQueues;     // [kNumQueues]
-  int* s_sec = s_run + kNumQueues;          // [kNumQueues + 1]
-  // 1. rank of every item: the items of higher cost, or of equal cost and a
-  // lower flat index, come first
-  for (int i = tid; i < n; i += nt) {
-    const int c = cost[i];
-    int r = 0;
-    for (int j = 0; j < n; ++j) {
-      const int cj = cost[j];
-      r += (cj > c || (cj == c && j < i)) ? 1 : 0;
-    }
-    order[r] = i;
-  }
-  if (tid < kNumQueues) s_run[tid] = 0;
-  __syncthreads();
-  // 2. first in-queue position of each item's tasks: exclusive scans over the
-  // sorted items of their per-queue task counts
-  for (int base = 0; base < n; base += nt) {
-    const int pos = base + tid;
-    int v[kNumQueues];
-    int i = 0;
-    if (pos < n) {
-      i = order[pos];
-      const int hm = i / rows_total;
-      row_queue_counts(g, sample_geo(g, d, nullptr, i - hm * rows_total).b, hm, cost[i], v);
-    } else {
+  int* rbase = cost + 2 * n_up;              // (n_up ints after the costs unused)
+  int* s_vec = rbase + kNumQueues * n_up;    // [nw][2 * kNumQueues]
+  int* s_red = s_vec + 2 * nw * kNumQueues;  // [2 * kNumQueues]
+  int* s_sec = s_red + 2 * kNumQueues;       // [kNumQueues + 1]
+  // 1. In-queue position of this item's row: the tasks, per queue, of the
+  // rows ranked before it (higher cost, or equal cost and a lower flat
+  // index), and the queue totals; one pass over the rows and one reduction,
+  // no sort (each item needs only its own row's position).
+  const int ci = cost[item];
+  int vb[kNumQueues], vt[kNumQueues];
 #pragma unroll
-      for (int s = 0; s < kNumQueues; ++s) v[s] = 0;
-    }
-    int first_pos[kNumQueues];
+  for (int s = 0; s < kNumQueues; ++s) vb[s] = vt[s] = 0;
+  for (int j = tid; j < n; j += nt) {
+    const int c = cost[j];
+    const int hm = j / rows_total;
+    int v[kNumQueues];
+    row_queue_counts(g, sample_geo(g, d, nullptr, j - hm * rows_total).b, hm, c, v);
+    const bool before = c > ci || (c == ci && j < item);
 #pragma unroll
     for (int s = 0; s < kNumQueues; ++s) {
-      const int incl = wave_incl_scan(v[s], lane);
-      first_pos[s] = incl - v[s];
-      if (lane == 63) s_vec[wv * kNumQueues + s] = incl;
+      vt[s] += v[s];
+      vb[s] += before ? v[s] : 0;
     }
-    __syncthreads();
-    if (tid < kNumQueues) {   // queue tid: exclusive prefix of the wavefront totals
-      int run = s_run[tid];
-      for (int x = 0; x < nw; ++x) {
-        const int tw = s_vec[x * kNumQueues + tid];
-        s_vec[x * kNumQueues + tid] = run;
-        run += tw;
-      }
-      s_run[tid] = run;
-    }
-    __syncthreads();
-    if (pos < n) {
+  }
 #pragma unroll
-      for (int s = 0; s < kNumQueues; ++s)
-        rbase[i * kNumQueues + s] = s_vec[wv * kNumQueues + s] + first_pos[s];
+  for (int s = 0; s < kNumQueues; ++s) {
+    const int b = wave_sum(vb[s]), a = wave_sum(vt[s]);
+    if (lane == 0) {
+      s_vec[wv * 2 * kNumQueues + s] = b;
+      s_vec[wv * 2 * kNumQueues + kNumQueues + s] = a;
     }
-    __syncthreads();   // s_vec is reused
   }
-  if (tid == 0) {
+  __syncthreads();
+  if (tid < 2 * kNumQueues) {
+    int sum = 0;
+    for (int x = 0; x < nw; ++x) sum += s_vec[x * 2 * kNumQueues + tid];
+    s_red[tid] = sum;
+  }
+  __syncthreads();
+  if (tid < kNumQueues) rbase[item * kNumQueues + tid] = s_red[tid];
+  if (tid == 0) {   // 2. queue starts
     s_sec[0] = 0;
-    for (int s = 0; s < kNumQueues; ++s) s_sec[s + 1] = s_sec[s] + s_run[s];
-    for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_sec[s];
+    for (int s = 0; s < kNumQueues; ++s) s_sec[s + 1] = s_sec[s] + s_red[kNumQueues + s];
+    if (writer)
+      for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_sec[s];
   }
-  if (g.layout == MPB_LAYOUT_BSHD) {   // fixed-length geometry in closed form (§4.2)
+  if (writer && g.layout == MPB_LAYOUT_BSHD) {   // fixed-length geometry in closed form (§4.2)
     const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
     for (int b = tid; b < g.batch; b += nt) {
       int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
@@ -1507,12 +1492,15 @@ __device__ __attribute__((always_inline)) inline void schedule_fused(const PlanG
     if (tid == 0) d.cu_rows[0] = 0;
   }
   __syncthreads();
-  // 3. every task
   int so[kNumQueues + 1];
 #pragma unroll
   for (int s = 0; s <= kNumQueues; ++s) so[s] = s_sec[s];
+  // 3. the tasks of this item's mask row (one per Q head, or the one task of
+  // a per-head mask row)
+  const int t_lo = g.mask_heads == 1 ? item * g.heads_q : item;
+  const int t_hi = g.mask_heads == 1 ? t_lo + g.heads_q : t_lo + 1;
   write_tasks(g, d, (const int*)lp, (const int*)lf, (const int*)lt, (const int*)rbase, nullptr,
-              so, rows_total, tid, nt);
+              so, rows_total, t_lo + tid, nt, t_hi);
 }
 
 // Exclusive prefix over the workgroup's threads of (a, b); totals in ta, tb.
@@ -1953,14 +1941,16 @@ void plan_single_pass_kernel(PlanGeo g,
   // the kernel's end matters then).
   const bool deferred = sp.deferred != 0;
   auto publish = [&]() __attribute__((always_inline)) {
-    if (item == n - 1) {
+    const bool fuse = sp.fused != 0 && deferred;
+    if (item == n - 1 || fuse) {
       // The header waits until every item has fixed its offsets (each did so
       // from its predecessors' words alone, so these waits end), and carries
-      // the OR of their error bits.  A fused build (deferred, so this item's
-      // own lists and payload are done and its LDS is free) also gathers every
-      // item's offsets, cost and first tile from its words for the schedule.
+      // the OR of their error bits.  In a fused build (deferred, so this
+      // item's own lists and payload are done and its LDS is free) every item
+      // gathers every item's offsets, cost and first tile from their words,
+      // ranks the rows and writes its own row's tasks; the last item also
+      // publishes the header and the section offsets.
       const uint32_t tag = sp.tag;
-      const bool fuse = sp.fused != 0 && deferred;
       const int n_up = g.mask_heads * g.upper_rows;
       int* f_lp = lds;
       int* f_lf = f_lp + n_up + 1;
@@ -2015,12 +2005,12 @@ void plan_single_pass_kernel(PlanGeo g,
       __syncthreads();
       uint32_t e = (uint32_t)s_err2;
       if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
-      if (tid == 0) {
+      if (item == n - 1 && tid == 0) {
         d.p_off[n] = p_begin + pc;
         d.f_off[n] = f_begin + fc;
         sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
       }
-      if (fuse && e == 0) schedule_fused(g, d, n, rows_total, lds);
+      if (fuse && e == 0) schedule_fused(g, d, n, rows_total, lds, item, item == n - 1);
     }
   };
   if (!deferred) publish();
