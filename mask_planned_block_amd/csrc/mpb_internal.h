@@ -163,17 +163,21 @@ struct SinglePass {
   int32_t stage;         // endpoints: 0 read from HBM; staged in LDS as int32 (1 through
                          // registers, 2 loaded straight into LDS) or int16 (3)
   int32_t fused;         // 1 (deferred builds of at most kFusedMaxItems upper-bound items):
-                         // the last item also runs the schedule, and there is no tail launch
+                         // every item also writes its row's tasks, and there is no tail launch
 };
 // Look-back words per item.
 constexpr int kLbWords = 8;
 // Largest Hmask * upper_rows whose schedule a fused single-pass build runs in
 // its items' workgroups (each item writes its own row's tasks).
 constexpr int kFusedMaxItems = 256;
+// Row keys of that schedule: a row's tasks per queue depend on its key alone
+// (16 layouts of a sample's KV heads over the sections, and empty rows).
+constexpr int kKeys = 17;
 // Dynamic LDS bytes of that schedule for `items_upper` items and a workgroup
 // of `threads` threads.
 constexpr size_t fused_schedule_lds_bytes(int64_t items_upper, int threads) {
-  return (size_t)(14 * items_upper + 2 + (2 * (threads / 64) + 2) * 9 + 10) * 4;
+  return (size_t)(14 * items_upper + 2 + 2 * kKeys * (threads / 64) + 2 * kNumQueues +
+                  kNumQueues + 1) * 4;
 }
 // Longest sample (seqlen_k) whose endpoints a single-pass build stages as
 // int16: every column it compares, up to seqlen_k plus a tile and a word,

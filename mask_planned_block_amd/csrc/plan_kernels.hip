@@ -618,13 +618,18 @@ __device__ inline int section_targets_upto(int s, int X) {
   const int n = X + 1, m = n & 15;
   return 2 * (n >> 4) + (m > s ? 1 : 0) + (m > kNumSections * 2 - 1 - s ? 1 : 0);
 }
-// Number of KV heads hk in [0, Hk) of section s for sample b, and (rank_hk
-// >= 0) the number of those below rank_hk.
-__device__ inline int kv_heads_in_section(int b, int heads_k, int s, int rank_hk = -1) {
-  const int x0 = (int)((uint32_t)b * (uint32_t)heads_k & 15u);
+// Number of KV heads hk in [0, Hk) of section s for a sample whose first KV
+// head has snake index x0, and (rank_hk >= 0) the number of those below
+// rank_hk.
+__device__ inline int kv_heads_in_section_at(int x0, int heads_k, int s, int rank_hk = -1) {
   const int below = section_targets_upto(s, x0 - 1);
   const int end = rank_hk >= 0 ? x0 + rank_hk : x0 + heads_k;
   return section_targets_upto(s, end - 1) - below;
+}
+// The same for sample b: its first KV head takes snake index (b * Hk) mod 16.
+__device__ inline int kv_heads_in_section(int b, int heads_k, int s, int rank_hk = -1) {
+  return kv_heads_in_section_at((int)((uint32_t)b * (uint32_t)heads_k & 15u), heads_k, s,
+                                rank_hk);
 }
 
 // Launch slot of the r-th task of section s: sections interleaved while they
@@ -1436,42 +1441,71 @@ __device__ __attribute__((always_inline)) inline void schedule_fused(const PlanG
   int* lt = lf + n_up + 1;
   int* cost = lt + n_up;
   int* rbase = cost + 2 * n_up;              // (n_up ints after the costs unused)
-  int* s_vec = rbase + kNumQueues * n_up;    // [nw][2 * kNumQueues]
-  int* s_red = s_vec + 2 * nw * kNumQueues;  // [2 * kNumQueues]
+  int* s_cnt = rbase + kNumQueues * n_up;    // [nw][2 * kKeys]
+  int* s_red = s_cnt + 2 * nw * kKeys;       // [2 * kNumQueues]
   int* s_sec = s_red + 2 * kNumQueues;       // [kNumQueues + 1]
   // 1. In-queue position of this item's row: the tasks, per queue, of the
   // rows ranked before it (higher cost, or equal cost and a lower flat
-  // index), and the queue totals; one pass over the rows and one reduction,
-  // no sort (each item needs only its own row's position).
+  // index), and the queue totals.  A row's tasks per queue follow from a key
+  // alone: kKeys - 1 for an empty row (all its tasks in the empty queue);
+  // else, for one mask row shared by the Q heads, (b * Hk) mod 16, which
+  // fixes how its sample's KV heads fall on the sections, or, for a per-head
+  // mask row, the section of its KV head.  So each wavefront counts its rows
+  // per key by ballots (lane k keeps key k), and the queue counts are sums
+  // over the keys, weighted by the tasks a row of that key puts in the queue.
+  // No sort: each item needs only its own row's positions.
+  const int group = g.heads_q / g.heads_k;
   const int ci = cost[item];
-  int vb[kNumQueues], vt[kNumQueues];
+  int cb = 0, ct = 0;
+  for (int j0 = wv * 64; j0 < n; j0 += nt) {   // wavefront-uniform
+    const int j = j0 + lane;
+    int key = -1;
+    bool before = false;
+    if (j < n) {
+      const int c = cost[j];
+      const int hm = j / rows_total;
+      const int b = sample_geo(g, d, nullptr, j - hm * rows_total).b;
+      key = c == 0 ? kKeys - 1
+            : g.mask_heads == 1 ? (int)((uint32_t)b * (uint32_t)g.heads_k & 15u)
+                                : section_of(b, g.heads_k, hm / group);
+      before = c > ci || (c == ci && j < item);
+    }
 #pragma unroll
-  for (int s = 0; s < kNumQueues; ++s) vb[s] = vt[s] = 0;
-  for (int j = tid; j < n; j += nt) {
-    const int c = cost[j];
-    const int hm = j / rows_total;
-    int v[kNumQueues];
-    row_queue_counts(g, sample_geo(g, d, nullptr, j - hm * rows_total).b, hm, c, v);
-    const bool before = c > ci || (c == ci && j < item);
-#pragma unroll
-    for (int s = 0; s < kNumQueues; ++s) {
-      vt[s] += v[s];
-      vb[s] += before ? v[s] : 0;
+    for (int k = 0; k < kKeys; ++k) {
+      const int na = __popcll(__ballot(key == k));
+      const int nb = __popcll(__ballot(key == k && before));
+      if (lane == k) {
+        ct += na;
+        cb += nb;
+      }
     }
   }
-#pragma unroll
-  for (int s = 0; s < kNumQueues; ++s) {
-    const int b = wave_sum(vb[s]), a = wave_sum(vt[s]);
-    if (lane == 0) {
-      s_vec[wv * 2 * kNumQueues + s] = b;
-      s_vec[wv * 2 * kNumQueues + kNumQueues + s] = a;
-    }
+  if (lane < kKeys) {
+    s_cnt[wv * 2 * kKeys + lane] = cb;
+    s_cnt[wv * 2 * kKeys + kKeys + lane] = ct;
   }
+  if (tid < 2 * kNumQueues) s_red[tid] = 0;
   __syncthreads();
-  if (tid < 2 * kNumQueues) {
-    int sum = 0;
-    for (int x = 0; x < nw; ++x) sum += s_vec[x * 2 * kNumQueues + tid];
-    s_red[tid] = sum;
+  for (int x = tid; x < kKeys * kNumQueues; x += nt) {
+    const int k = x % kKeys, s = x / kKeys;
+    int wt;   // tasks a row of key k puts in queue s
+    if (k == kKeys - 1)
+      wt = s == kNumSections ? (g.mask_heads == 1 ? g.heads_q : 1) : 0;
+    else if (s == kNumSections)
+      wt = 0;
+    else if (g.mask_heads == 1)
+      wt = group * kv_heads_in_section_at(k, g.heads_k, s);
+    else
+      wt = k == s ? 1 : 0;
+    if (wt != 0) {
+      int nb = 0, na = 0;
+      for (int v = 0; v < nw; ++v) {
+        nb += s_cnt[v * 2 * kKeys + k];
+        na += s_cnt[v * 2 * kKeys + kKeys + k];
+      }
+      if (nb) atomicAdd(&s_red[s], wt * nb);
+      if (na) atomicAdd(&s_red[kNumQueues + s], wt * na);
+    }
   }
   __syncthreads();
   if (tid < kNumQueues) rbase[item * kNumQueues + tid] = s_red[tid];
