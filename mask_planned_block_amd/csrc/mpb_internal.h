@@ -150,8 +150,7 @@ bool plan_finish_fits(const PlanGeo& g, bool cnt_in_lds, int64_t nchunks);
 // placement of the lists in a second one.
 struct SinglePass {
   uint64_t* lb;          // [Hmask * upper_rows][kLbWords] look-back words {aggregate,
-                         // inclusive partial, inclusive full, done, first listed tile + 1
-                         // (fused builds)}, each (tag << 32) | value
+                         // inclusive partial, inclusive full, done}, each (tag << 32) | value
   uint32_t tag;          // this build's tag (nonzero; words of earlier builds differ)
   int32_t* host_slot;    // host-mapped header slot
   int32_t deferred;      // 1: deferred read-back: the header goes to the plan block only,
@@ -163,22 +162,18 @@ struct SinglePass {
   int32_t stage;         // endpoints: 0 read from HBM; staged in LDS as int32 (1 through
                          // registers, 2 loaded straight into LDS) or int16 (3)
   int32_t fused;         // 1 (deferred builds of at most kFusedMaxItems upper-bound items):
-                         // every item also writes its row's tasks, and there is no tail launch
+                         // every item also ranks its row and writes its tasks, and there is
+                         // no tail launch
 };
 // Look-back words per item.
 constexpr int kLbWords = 8;
-// Largest Hmask * upper_rows whose schedule a fused single-pass build runs in
-// its items' workgroups (each item writes its own row's tasks).
+// Largest Hmask * upper_rows for which a deferred single-pass build also runs
+// the schedule: every item reads every item's cost, so all of them must be
+// resident at once, and each item's ranking pass grows with their number.
 constexpr int kFusedMaxItems = 256;
 // Row keys of that schedule: a row's tasks per queue depend on its key alone
 // (16 layouts of a sample's KV heads over the sections, and empty rows).
 constexpr int kKeys = 17;
-// Dynamic LDS bytes of that schedule for `items_upper` items and a workgroup
-// of `threads` threads.
-constexpr size_t fused_schedule_lds_bytes(int64_t items_upper, int threads) {
-  return (size_t)(14 * items_upper + 2 + 2 * kKeys * (threads / 64) + 2 * kNumQueues +
-                  kNumQueues + 1) * 4;
-}
 // Longest sample (seqlen_k) whose endpoints a single-pass build stages as
 // int16: every column it compares, up to seqlen_k plus a tile and a word,
 // stays below the int16 sentinel 32767.

@@ -716,6 +716,35 @@ __device__ inline void write_task(const PlanGeo& g, const PlanDev& d, const int*
 
 namespace {
 
+// Records of task (row i, Q head h): its queue and its rank among the row's
+// tasks in that queue give its section-major slot and its launch slot.  rb:
+// the row's first in-queue position per queue; so: queue offsets; cu: an LDS
+// copy of cu_rows or nullptr.
+template <class RP>
+__device__ __attribute__((always_inline)) inline void place_task(
+    const PlanGeo& g, const PlanDev& d, RP rb, const int* cu,
+    const int (&so)[kNumQueues + 1], int rows_total, int i, int h, int p_beg, int np, int f_beg,
+    int nf, int first) {
+  const int group = g.heads_q / g.heads_k;
+  const int hm = g.mask_heads == 1 ? 0 : h;
+  const int row = i - hm * rows_total;
+  const SampleGeo sg = sample_geo(g, d, cu, row);
+  int s, rank;
+  if (np + nf == 0) {
+    s = kNumSections;
+    rank = g.mask_heads == 1 ? h : 0;
+  } else {
+    const int hk = h / group;
+    s = section_of(sg.b, g.heads_k, hk);
+    if (g.mask_heads == 1) {
+      rank = kv_heads_in_section(sg.b, g.heads_k, s, hk) * group + (h - hk * group);
+    } else {
+      rank = 0;
+    }
+  }
+  write_task(g, d, so, sg, row - sg.row_begin, h, hm, s, rb[s] + rank, p_beg, np, f_beg, nf,
+             first);
+}
 // §4.8 step 3: tasks t = t0, t0 + stride, ... (t < rows_total * Hq) to the
 // section-major schedule and, as launch records, to their interleaved launch
 // slots.  P, F: the rows' CSR offsets; FT: first listed K tile per
@@ -724,9 +753,9 @@ namespace {
 template <class PP, class RP>
 __device__ __attribute__((always_inline)) inline void write_tasks(
     const PlanGeo& g, const PlanDev& d, PP P, PP F, PP FT, RP rbase, const int* cu,
-    const int (&so)[kNumQueues + 1], int rows_total, int t0, int stride, int t_end = -1) {
-  const int Hq = g.heads_q, group = g.heads_q / g.heads_k;
-  const int ntasks = t_end >= 0 ? t_end : rows_total * Hq;
+    const int (&so)[kNumQueues + 1], int rows_total, int t0, int stride) {
+  const int Hq = g.heads_q;
+  const int ntasks = rows_total * Hq;
   for (int t = t0; t < ntasks; t += stride) {
     int i, h;
     if (g.mask_heads == 1) {
@@ -738,25 +767,9 @@ __device__ __attribute__((always_inline)) inline void write_tasks(
     }
     const int hm = g.mask_heads == 1 ? 0 : h;
     const int row = i - hm * rows_total;
-    const SampleGeo sg = sample_geo(g, d, cu, row);
-    const int p_beg = P[i], np = P[i + 1] - p_beg;
-    const int f_beg = F[i], nf = F[i + 1] - f_beg;
-    int s, rank;
-    if (np + nf == 0) {
-      s = kNumSections;
-      rank = g.mask_heads == 1 ? h : 0;
-    } else {
-      const int hk = h / group;
-      s = section_of(sg.b, g.heads_k, hk);
-      if (g.mask_heads == 1) {
-        rank = kv_heads_in_section(sg.b, g.heads_k, s, hk) * group + (h - hk * group);
-      } else {
-        rank = 0;
-      }
-    }
-    write_task(g, d, so, sg, row - sg.row_begin, h, hm, s,
-               rbase[(int64_t)i * kNumQueues + s] + rank, p_beg, np, f_beg, nf,
-               FT[(int64_t)hm * g.upper_rows + row]);
+    const int p_beg = P[i], f_beg = F[i];
+    place_task(g, d, rbase + (int64_t)i * kNumQueues, cu, so, rows_total, i, h, p_beg,
+               P[i + 1] - p_beg, f_beg, F[i + 1] - f_beg, FT[(int64_t)hm * g.upper_rows + row]);
   }
 }
 
@@ -1419,122 +1432,93 @@ __device__ inline void sp_publish(const PlanDev& d, const SinglePass& sp, int ro
                      __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
-// §4.8 schedule of a fused single-pass build, run by every item's workgroup
-// after its own lists and payload, for its own mask row.  Its inputs come
-// from the look-back words the items wrote as tagged atomics (gathered into
-// LDS): exclusive offsets lp / lf [n + 1] over the flat items, first listed
-// tiles lt [Hmask * upper_rows] (at hm * upper_rows + row) and costs [n].  The
-// order is the one schedule_block produces (items by descending cost, ties by
-// flat index): the row's first position in each queue is the task count of
-// the rows ranked before it, so no item sorts; its tasks then go to their
-// section-major slots and interleaved launch slots.  The writer (the last
-// item) also stores the queue starts and the fixed-length geometry.
-__device__ __attribute__((always_inline)) inline void schedule_fused(const PlanGeo& g,
-                                                                    const PlanDev& d, int n,
-                                                                    int rows_total, int* lds,
-                                                                    int item, bool writer) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int nt = (int)blockDim.x, nw = nt >> 6;
-  const int n_up = g.mask_heads * g.upper_rows;
-  int* lp = lds;
-  int* lf = lp + n_up + 1;
-  int* lt = lf + n_up + 1;
-  int* cost = lt + n_up;
-  int* rbase = cost + 2 * n_up;              // (n_up ints after the costs unused)
-  int* s_cnt = rbase + kNumQueues * n_up;    // [nw][2 * kKeys]
-  int* s_red = s_cnt + 2 * nw * kKeys;       // [2 * kNumQueues]
-  int* s_sec = s_red + 2 * kNumQueues;       // [kNumQueues + 1]
-  // 1. In-queue position of this item's row: the tasks, per queue, of the
-  // rows ranked before it (higher cost, or equal cost and a lower flat
-  // index), and the queue totals.  A row's tasks per queue follow from a key
-  // alone: kKeys - 1 for an empty row (all its tasks in the empty queue);
-  // else, for one mask row shared by the Q heads, (b * Hk) mod 16, which
-  // fixes how its sample's KV heads fall on the sections, or, for a per-head
-  // mask row, the section of its KV head.  So each wavefront counts its rows
-  // per key by ballots (lane k keeps key k), and the queue counts are sums
-  // over the keys, weighted by the tasks a row of that key puts in the queue.
-  // No sort: each item needs only its own row's positions.
+// §4.8 tasks that a row of key k puts in queue s, for the fused schedule
+// below.  Key kKeys - 1: an empty row, all its tasks in the empty queue;
+// keys 0..15 for one mask row shared by the Q heads: (b * Hk) mod 16, which
+// fixes how its sample's KV heads fall on the sections; for a per-head mask
+// row, the section of its KV head.
+__device__ inline int fused_queue_weight(const PlanGeo& g, int k, int s) {
+  if (k == kKeys - 1) return s == kNumSections ? (g.mask_heads == 1 ? g.heads_q : 1) : 0;
+  if (s == kNumSections) return 0;
+  if (g.mask_heads == 1)
+    return (g.heads_q / g.heads_k) * kv_heads_in_section_at(k, g.heads_k, s);
+  return k == s ? 1 : 0;
+}
+// §4.8 queue positions of one row of a fused single-pass build, computed by
+// one whole wavefront beside the look-back.  The schedule ranks the rows by
+// descending cost (partial plus full tiles), ties by flat index.  A row's
+// tasks per queue follow from its key alone (fused_queue_weight), so the
+// row's first position in each queue is a sum over the keys of (rows of that
+// key ranked before it) x (tasks such a row puts in the queue), and the queue
+// starts are the same sums over all rows; no item sorts.  The costs come from
+// the items' aggregate words, which every item publishes right after its
+// classification.  ci: this item's cost; wts[kKeys * kNumQueues]: the
+// weights.  Out: rb[kNumQueues] this row's first position per queue,
+// sec[kNumQueues + 1] the queue starts; cnt[kKeys] and red[kNumQueues] are
+// scratch.  Returns false when some item's word never came (the positions
+// are then in bounds but not meaningful).
+__device__ bool fused_row_positions(const PlanGeo& g, const PlanDev& d, const SinglePass& sp,
+                                    int n, int rows_total, int item, int ci, const int* wts,
+                                    int* cnt, int* red, int* rb, int* sec) {
+  const int lane = threadIdx.x & 63;
   const int group = g.heads_q / g.heads_k;
-  const int ci = cost[item];
-  int cb = 0, ct = 0;
-  for (int j0 = wv * 64; j0 < n; j0 += nt) {   // wavefront-uniform
-    const int j = j0 + lane;
-    int key = -1;
-    bool before = false;
-    if (j < n) {
-      const int c = cost[j];
-      const int hm = j / rows_total;
-      const int b = sample_geo(g, d, nullptr, j - hm * rows_total).b;
-      key = c == 0 ? kKeys - 1
-            : g.mask_heads == 1 ? (int)((uint32_t)b * (uint32_t)g.heads_k & 15u)
-                                : section_of(b, g.heads_k, hm / group);
-      before = c > ci || (c == ci && j < item);
+  // one wavefront: its LDS operations complete in order; the fences keep
+  // the compiler from moving them across the points between the steps
+  auto wave_sync = []() __attribute__((always_inline)) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (lane < kKeys) cnt[lane] = 0;
+  wave_sync();
+  bool late = false;
+  for (int j = lane; j < n; j += 64) {
+    int c = ci;
+    if (j != item) {
+      const uint64_t* wj = sp.lb + kLbWords * (int64_t)j;
+      uint64_t ag = lb_load(wj);
+      uint32_t spins = 0;
+      while ((uint32_t)(ag >> 32) != sp.tag) {
+        if (++spins > kLookbackSpins) {
+          late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        ag = lb_load(wj);
+      }
+      c = (int)((uint32_t)ag >> 16) + (int)((uint32_t)ag & 0xFFFFu);
     }
-#pragma unroll
+    const int hm = j / rows_total;
+    const int b = sample_geo(g, d, nullptr, j - hm * rows_total).b;
+    const int key = c == 0 ? kKeys - 1
+                    : g.mask_heads == 1 ? (int)((uint32_t)b * (uint32_t)g.heads_k & 15u)
+                                        : section_of(b, g.heads_k, hm / group);
+    const bool before = c > ci || (c == ci && j < item);
+    // rows of the key in the low half, those ranked before this one in the
+    // high half (at most kFusedMaxItems of each)
+    atomicAdd(&cnt[key], before ? 0x10001 : 1);
+  }
+  wave_sync();
+  // lanes 0..8: this row's first position per queue; 9..17: queue totals
+  if (lane < 2 * kNumQueues) {
+    const bool tot = lane >= kNumQueues;
+    const int s = tot ? lane - kNumQueues : lane;
+    int acc = 0;
     for (int k = 0; k < kKeys; ++k) {
-      const int na = __popcll(__ballot(key == k));
-      const int nb = __popcll(__ballot(key == k && before));
-      if (lane == k) {
-        ct += na;
-        cb += nb;
-      }
+      const int v = cnt[k];
+      acc += wts[k * kNumQueues + s] * (tot ? (v & 0xFFFF) : (v >> 16));
     }
-  }
-  if (lane < kKeys) {
-    s_cnt[wv * 2 * kKeys + lane] = cb;
-    s_cnt[wv * 2 * kKeys + kKeys + lane] = ct;
-  }
-  if (tid < 2 * kNumQueues) s_red[tid] = 0;
-  __syncthreads();
-  for (int x = tid; x < kKeys * kNumQueues; x += nt) {
-    const int k = x % kKeys, s = x / kKeys;
-    int wt;   // tasks a row of key k puts in queue s
-    if (k == kKeys - 1)
-      wt = s == kNumSections ? (g.mask_heads == 1 ? g.heads_q : 1) : 0;
-    else if (s == kNumSections)
-      wt = 0;
-    else if (g.mask_heads == 1)
-      wt = group * kv_heads_in_section_at(k, g.heads_k, s);
+    if (tot)
+      red[s] = acc;
     else
-      wt = k == s ? 1 : 0;
-    if (wt != 0) {
-      int nb = 0, na = 0;
-      for (int v = 0; v < nw; ++v) {
-        nb += s_cnt[v * 2 * kKeys + k];
-        na += s_cnt[v * 2 * kKeys + kKeys + k];
-      }
-      if (nb) atomicAdd(&s_red[s], wt * nb);
-      if (na) atomicAdd(&s_red[kNumQueues + s], wt * na);
-    }
+      rb[s] = acc;
   }
-  __syncthreads();
-  if (tid < kNumQueues) rbase[item * kNumQueues + tid] = s_red[tid];
-  if (tid == 0) {   // 2. queue starts
-    s_sec[0] = 0;
-    for (int s = 0; s < kNumQueues; ++s) s_sec[s + 1] = s_sec[s] + s_red[kNumQueues + s];
-    if (writer)
-      for (int s = 0; s <= kNumQueues; ++s) d.section_off[s] = s_sec[s];
+  wave_sync();
+  if (lane == 0) {
+    sec[0] = 0;
+    for (int s = 0; s < kNumQueues; ++s) sec[s + 1] = sec[s] + red[s];
   }
-  if (writer && g.layout == MPB_LAYOUT_BSHD) {   // fixed-length geometry in closed form (§4.2)
-    const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
-    for (int b = tid; b < g.batch; b += nt) {
-      int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
-      sd[0] = make_int4(b * g.seqlen_q, b * g.seqlen_k, g.seqlen_q, g.seqlen_k);
-      sd[1] = make_int4(b * rps, rps, (g.seqlen_k + g.tile_k - 1) / g.tile_k, 0);
-      d.cu_rows[b + 1] = (b + 1) * rps;
-    }
-    if (tid == 0) d.cu_rows[0] = 0;
-  }
-  __syncthreads();
-  int so[kNumQueues + 1];
-#pragma unroll
-  for (int s = 0; s <= kNumQueues; ++s) so[s] = s_sec[s];
-  // 3. the tasks of this item's mask row (one per Q head, or the one task of
-  // a per-head mask row)
-  const int t_lo = g.mask_heads == 1 ? item * g.heads_q : item;
-  const int t_hi = g.mask_heads == 1 ? t_lo + g.heads_q : t_lo + 1;
-  write_tasks(g, d, (const int*)lp, (const int*)lf, (const int*)lt, (const int*)rbase, nullptr,
-              so, rows_total, t_lo + tid, nt, t_hi);
+  return __ballot(late) == 0;
 }
 
 // Exclusive prefix over the workgroup's threads of (a, b); totals in ta, tb.
@@ -1580,6 +1564,9 @@ void plan_single_pass_kernel(PlanGeo g,
   extern __shared__ int lds[];
   __shared__ int s_item, s_err, s_err2, s_pbeg, s_fbeg, s_ffirst;
   __shared__ int s_a[4], s_b[4];
+  // fused builds: this row's queue positions, the queue starts, scratch
+  __shared__ int s_frb[kNumQueues], s_fsec[kNumQueues + 1], s_fok;
+  __shared__ int s_fcnt[kKeys], s_fred[kNumQueues], s_fwts[kKeys * kNumQueues];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   // ng groups of sg threads: thread rho of every group owns Q row rho of the
   // tile; the groups split the endpoint loads, the K-tile range of the
@@ -1878,6 +1865,10 @@ void plan_single_pass_kernel(PlanGeo g,
       cf += __popc(fw[u]);
     }
   }
+  // fused builds: the schedule's weights (the scan's barrier publishes them)
+  if (sp.fused != 0 && sp.deferred != 0)
+    for (int x = tid; x < kKeys * kNumQueues; x += blockDim.x)
+      s_fwts[x] = fused_queue_weight(g, x / kNumQueues, x % kNumQueues);
   int pp, pf, pc, fc;
   block_scan2(cp, cf, &pp, &pf, &pc, &fc, s_a, s_b);
   // the ascending partial list into LDS (the payload loop reads it); the
@@ -1959,6 +1950,14 @@ void plan_single_pass_kernel(PlanGeo g,
       s_fbeg = acc_f;
     }
   }
+  // fused builds: this row's queue positions, by the second wavefront while
+  // the first looks back (by the only one, after it)
+  const bool fuse = sp.fused != 0 && sp.deferred != 0;
+  if (fuse && wv == ((int)blockDim.x > 64 ? 1 : 0)) {
+    const bool ok = fused_row_positions(g, d, sp, n, rows_total, item, pc + fc, s_fwts, s_fcnt,
+                                        s_fred, s_frb, s_fsec);
+    if (lane == 0) s_fok = ok ? 1 : 0;
+  }
   __syncthreads();
   const int p_begin = s_pbeg, f_begin = s_fbeg;
   if (tid == 0) {
@@ -1966,35 +1965,19 @@ void plan_single_pass_kernel(PlanGeo g,
     d.p_off[item] = p_begin;
     d.f_off[item] = f_begin;
     w.first_tile[(int64_t)hm * g.upper_rows + row] = first;
-    // fused builds: the first tile for the schedule in the last item's workgroup
-    if (sp.fused)
-      lb_store(&sp.lb[kLbWords * (int64_t)item + 4], lb_word(sp.tag, (uint32_t)(first + 1)));
   }
   // §4.5 header: with a host read-back it goes out before this item's own
   // lists and payload (the host waits for it); deferred, after them (only
   // the kernel's end matters then).
   const bool deferred = sp.deferred != 0;
   auto publish = [&]() __attribute__((always_inline)) {
-    const bool fuse = sp.fused != 0 && deferred;
-    if (item == n - 1 || fuse) {
+    if (item == n - 1) {
       // The header waits until every item has fixed its offsets (each did so
       // from its predecessors' words alone, so these waits end), and carries
-      // the OR of their error bits.  In a fused build (deferred, so this
-      // item's own lists and payload are done and its LDS is free) every item
-      // gathers every item's offsets, cost and first tile from their words,
-      // ranks the rows and writes its own row's tasks; the last item also
-      // publishes the header and the section offsets.
+      // the OR of their error bits.
       const uint32_t tag = sp.tag;
-      const int n_up = g.mask_heads * g.upper_rows;
-      int* f_lp = lds;
-      int* f_lf = f_lp + n_up + 1;
-      int* f_lt = f_lf + n_up + 1;
-      int* f_cost = f_lt + n_up;
-      if (fuse) __syncthreads();
       uint32_t err_all = 0;
-      for (int j0 = 0; j0 < n; j0 += blockDim.x) {
-        const int j = j0 + tid;
-        if (j >= n) break;
+      for (int j = tid; j < n; j += blockDim.x) {
         const uint64_t* wj = sp.lb + kLbWords * (int64_t)j;
         uint32_t spins = 0;
         uint64_t v = lb_load(wj + 3);
@@ -2007,44 +1990,46 @@ void plan_single_pass_kernel(PlanGeo g,
           v = lb_load(wj + 3);
         }
         err_all |= (uint32_t)v;
-        if (fuse) {
-          uint64_t ag = lb_load(wj), ip = lb_load(wj + 1), iq = lb_load(wj + 2);
-          uint64_t ft = lb_load(wj + 4);
-          spins = 0;
-          while ((uint32_t)(ag >> 32) != tag || (uint32_t)(ip >> 32) != tag ||
-                 (uint32_t)(iq >> 32) != tag || (uint32_t)(ft >> 32) != tag) {
-            if (++spins > kLookbackSpins) {
-              err_all |= kDevErrLookback;
-              break;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            ag = lb_load(wj);
-            ip = lb_load(wj + 1);
-            iq = lb_load(wj + 2);
-            ft = lb_load(wj + 4);
-          }
-          const int pcj = (int)((uint32_t)ag >> 16), fcj = (int)((uint32_t)ag & 0xFFFFu);
-          f_lp[j] = (int)(uint32_t)ip - pcj;
-          f_lf[j] = (int)(uint32_t)iq - fcj;
-          f_cost[j] = pcj + fcj;
-          const int hmj = j / rows_total;
-          f_lt[hmj * g.upper_rows + (j - hmj * rows_total)] = (int)(uint32_t)ft - 1;
-          if (j == n - 1) {
-            f_lp[n] = (int)(uint32_t)ip;
-            f_lf[n] = (int)(uint32_t)iq;
-          }
-        }
       }
       if (err_all) atomicOr(&s_err2, err_all);
       __syncthreads();
       uint32_t e = (uint32_t)s_err2;
       if (g.layout == MPB_LAYOUT_THD) e |= (uint32_t)w.geo_err[0];
-      if (item == n - 1 && tid == 0) {
+      if (tid == 0) {
         d.p_off[n] = p_begin + pc;
         d.f_off[n] = f_begin + fc;
         sp_publish(d, sp, rows_total, p_begin + pc, f_begin + fc, e);
       }
-      if (fuse && e == 0) schedule_fused(g, d, n, rows_total, lds, item, item == n - 1);
+      // fused builds: the queue starts and the fixed-length geometry (§4.2,
+      // in closed form)
+      if (fuse && e == 0) {
+        if (tid <= kNumQueues) d.section_off[tid] = s_fsec[tid];
+        if (g.layout == MPB_LAYOUT_BSHD) {
+          const int rps = (g.seqlen_q + g.tile_q - 1) / g.tile_q;
+          for (int b = tid; b < g.batch; b += blockDim.x) {
+            int4* sd = reinterpret_cast<int4*>(d.seqdesc + 8 * b);
+            sd[0] = make_int4(b * g.seqlen_q, b * g.seqlen_k, g.seqlen_q, g.seqlen_k);
+            sd[1] = make_int4(b * rps, rps, (g.seqlen_k + g.tile_k - 1) / g.tile_k, 0);
+            d.cu_rows[b + 1] = (b + 1) * rps;
+          }
+          if (tid == 0) d.cu_rows[0] = 0;
+        }
+      }
+    }
+    // fused builds: every item writes its own row's tasks (one per Q head, or
+    // the one task of a per-head mask row).  Their slots stay in bounds
+    // whatever other items found, and a failed build's header keeps the
+    // forward from reading them.
+    if (fuse && s_fok != 0 && (g.layout != MPB_LAYOUT_THD || w.geo_err[0] == 0)) {
+      int so[kNumQueues + 1];
+#pragma unroll
+      for (int s = 0; s <= kNumQueues; ++s) so[s] = s_fsec[s];
+      const int first = pc > 0 ? ptiles[0] : s_ffirst;
+      const int h_lo = g.mask_heads == 1 ? 0 : hm;
+      const int h_hi = g.mask_heads == 1 ? g.heads_q : hm + 1;
+      for (int h = h_lo + tid; h < h_hi; h += blockDim.x)
+        place_task(g, d, (const int*)s_frb, nullptr, so, rows_total, item, h, p_begin, pc,
+                   f_begin, fc, first);
     }
   };
   if (!deferred) publish();
@@ -2687,9 +2672,6 @@ hipError_t launch_plan_single_pass(const PlanGeo& g, const int32_t* mask_func, c
                          : sp.stage != 0 ? ep_rows * g.tile_q
                                          : 0;
   size_t lds = ep_ints * 4 + (size_t)2 * nw * g.words_k * 4 + (size_t)g.nk_max * 4;
-  // a fused build's last item reuses its LDS for the schedule
-  if (sp.fused)
-    lds = std::max(lds, fused_schedule_lds_bytes((int64_t)g.mask_heads * g.upper_rows, threads));
   // at least one workgroup, so the header is always published
   const dim3 grid((unsigned)(items > 0 ? items : 1)), block(threads);
   if (sp.stage == 3)
