@@ -210,6 +210,10 @@ struct PlanHeap {
     return hipSuccess;
   }
   // Returns the block once everything enqueued on `stream` so far is done.
+  // The event only tells the host when the stream has passed this point; no
+  // memory has to become visible to the host with it, so it is recorded
+  // without the system-scope fence (a fence would write back and invalidate
+  // the caches between the work before it and the work after it).
   hipError_t release(int c, size_t off, size_t bytes, hipStream_t stream) {
     std::lock_guard<std::mutex> lk(mu);
     bytes = (bytes + 255) & ~(size_t)255;
@@ -218,7 +222,8 @@ struct PlanHeap {
       ev = idle_events.back();
       idle_events.pop_back();
     } else {
-      hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+      hipError_t e =
+          hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
       if (e != hipSuccess) return e;
     }
     hipError_t e = hipEventRecord(ev, stream);
