@@ -65,6 +65,48 @@ def test_deferred_forward_equals_waited(name):
     G.compare_plan(ge, op)
 
 
+def _gqa_workload(kind):
+    """Deferred builds small enough that every item ranks its own row (at most
+    256 mask rows) with Q heads grouped over fewer KV heads.  "shared": one
+    window+sink mask, 24 Q heads on 12 KV heads over 3 samples, so that
+    sample 1's KV heads run past 16 in the snake order of the sections
+    ((b * Hk) mod 16 = 0, 12, 8).  "per_head": a different window per Q head
+    (mask heads = Q heads), 8 Q heads on 4 KV heads."""
+    if kind == "shared":
+        return W.window_sink(seed=3, batch=3, heads=24, heads_k=12, seqlen=384, sink=32,
+                             window=100)
+    batch, seqlen, hq, hk = 3, 384, 8, 4
+    ql = np.arange(seqlen, dtype=np.int64)
+    mf = np.stack([np.tile(W.window_sink_endpoints(ql, 16, 40 + 37 * h), (1, batch))
+                   for h in range(hq)])
+    return W.custom(mf, layout=W.LAYOUT_BSHD, batch=batch, seqlen_q=seqlen, seqlen_k=seqlen,
+                    heads_q=hq, heads_k=hk, head_dim=128, dtype=W.DTYPE_BF16, seed=4,
+                    name="per_head_windows")
+
+
+@pytest.mark.parametrize("kind", ["shared", "per_head"])
+def test_deferred_ranked_schedule_gqa(kind):
+    w = _gqa_workload(kind)
+    _case("deferred gqa", kind=kind, hq=w.heads_q, hk=w.heads_k, hmask=w.mask_heads)
+    d = G.device_inputs(w)
+    lazy = G.build_plan(w, d, defer_header=True)
+    o_lazy, l_lazy = G.run_attention(w, d, lazy)
+    ref = G.build_plan(w, d)
+    o_ref, l_ref = G.run_attention(w, d, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o_lazy, o_ref) and torch.equal(l_lazy, l_ref)
+    info = lazy.info
+    assert info.build_mode == mpb.BUILD_SINGLE_PASS_DEFERRED
+    assert list(info.header) == list(ref.info.header)
+    ge = lazy.export()
+    _same_exports(ge, ref.export())
+    pl = info.problem
+    op = oracle.build_plan(w, pl.tile_q // info.signature.pack_gqa, pl.tile_k)
+    G.compare_plan(ge, op)
+    if info.signature.pack_gqa == 1:   # a packed plan's tasks follow the packed view
+        G.check_schedule(w, ge, pl.tile_q)
+
+
 def test_deferred_large_plan_schedules_in_its_own_launch():
     """Past the fused schedule's size (block-sparse: 24 x 64 items) a deferred
     build keeps its schedule launch; its plan and forward equal those of the
