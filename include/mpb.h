@@ -311,7 +311,8 @@ mpb_status mask_plan_export_k2q_order(const mpb_plan* plan, int32_t* order);
  * classification, offsets, lists and payload in one launch), us[2] schedule
  * (in place: schedule and materialization in one launch; single pass:
  * schedule and list placement; -1 for a deferred build of at most 256
- * (mask head, Q row) items, whose single pass schedules in its last item),
+ * (mask head, Q row) items, whose single pass also schedules: each item
+ * ranks and writes its own row's tasks),
  * us[3] materialization (exact builds only),
  * us[4] K2Q count, us[5] K2Q materialization (backward view only), us[6]
  * first event to last (for an exact build this includes the host's header
